@@ -1,0 +1,288 @@
+"""Pins of the oracle against what the pages and mathematics fix (CPU only).
+
+Each test names the plausible oracle mistake it would catch.  The pages print
+no worked SATA output, so exact outputs are pinned by closed forms, special
+cases that reduce to textbook/library routines, exact rational arithmetic on
+tiny inputs, and invariants.
+"""
+import collections
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def _rand_qkv(seed, lead, n, dk, dv):
+    d = si.draw_qkv(lead, n, dk, dv, seed, "f32")
+    return d.q, d.k, d.v
+
+
+# ------------------------------------------------------------ basis (O3, O4)
+
+@pytest.mark.parametrize("d", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("p", [0, 1, 2, 3, 4])
+def test_basis_count_is_binomial(oracle, d, p):
+    """Brute-force sorted-tuple groups of all d^p ordered tuples number
+    C(d+p-1, p) [hotdry, 'Core insight of symmetric tensor decomposition'].
+    Catches a wrong grouping (e.g. keeping ordered tuples, or strict i1<i2)."""
+    tup, cnt = oracle.basis_bruteforce(d, p)
+    assert len(cnt) == math.comb(d + p - 1, p)
+    assert int(cnt.sum()) == d ** p
+    # every group is a sorted tuple, listed in lexicographic order
+    for t in tup:
+        assert list(t) == sorted(t)
+    assert [tuple(t) for t in tup] == sorted(tuple(t) for t in tup)
+
+
+@pytest.mark.parametrize("d,p", [(3, 3), (4, 4), (5, 2), (2, 4)])
+def test_group_sizes_are_multinomial(oracle, d, p):
+    """Group size = p!/prod(alpha!) (textbook multinomial).  Catches a wrong
+    symmetric weight in phi."""
+    tup, cnt = oracle.basis_bruteforce(d, p)
+    for t, c in zip(tup, cnt):
+        mult = collections.Counter(t.tolist())
+        expect = math.factorial(p)
+        for a in mult.values():
+            expect //= math.factorial(a)
+        assert c == expect
+
+
+def test_page_figures_minimal_basis_and_expansion(oracle):
+    """The page's numbers: 47905 minimal-basis features at d_K=64 (read as the
+    orders 0..3 together) and more than 16 million unreduced monomials at
+    d_K=64, p=4 [hotdry, 'Core insight of symmetric tensor decomposition']."""
+    g = json.load(open(GOLDEN))
+    fig = g["minimal_basis_d64"]
+    total = sum(len(oracle.basis_bruteforce(fig["d_k"], p)[1]) for p in range(fig["P"]))
+    assert total == fig["page_value"] == oracle.cumulative_basis(64, 4)
+    full = g["full_expansion_d64_p4"]
+    _, cnt4 = oracle.basis_bruteforce(full["d_k"], full["p"])
+    assert int(cnt4.sum()) > full["lower_bound"]
+    # the single order p=4 alone is C(67,4), not the page's 47905
+    assert len(cnt4) == math.comb(67, 4) == 766480
+
+
+@pytest.mark.parametrize("d,P,expect", [(8, 3, 45), (16, 4, 969), (32, 4, 6545), (64, 4, 47905)])
+def test_cumulative_basis_at_workloads(oracle, d, P, expect):
+    total = sum(len(oracle.basis_bruteforce(d, p)[1]) for p in range(P))
+    assert total == expect == oracle.cumulative_basis(d, P)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_phi_identity_exact_on_integers(oracle, seed):
+    """sum_t count_t prod q prod k = (q.k)^p exactly for integer q, k (both sides
+    are exact integers in fp64), and phi_p(q).phi_p(k) = (q.k)^p to rounding.
+    Catches a wrong index or weight in the feature map."""
+    rng = np.random.default_rng(seed)
+    for d in range(1, 5):
+        for p in range(0, 5):
+            q = rng.integers(-3, 4, size=d).astype(np.float64)
+            k = rng.integers(-3, 4, size=d).astype(np.float64)
+            tup, cnt = oracle.basis_bruteforce(d, p)
+            lhs = 0.0
+            for t, c in zip(tup, cnt):
+                lhs += float(c) * float(np.prod(q[t])) * float(np.prod(k[t]))
+            assert lhs == float(np.dot(q, k)) ** p
+            sym = float(np.dot(oracle.phi(q, p), oracle.phi(k, p)))
+            ref = float(np.dot(q, k)) ** p
+            assert abs(sym - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+# ------------------------------------------------------------ state form (O5)
+
+@pytest.mark.parametrize("d,P", [(1, 1), (1, 4), (2, 2), (2, 3), (3, 4), (4, 4), (4, 3), (3, 1)])
+def test_recurrent_state_equals_quadratic(oracle, d, P):
+    """The constant-size state form (O5) equals the quadratic definition (O1)
+    [hotdry, 'Engineering realisation of the constant compute cost'].
+    Catches a missing 1/p!, a wrong d^(p/2), or a read-before-update."""
+    q, k, v = _rand_qkv(100 + 10 * d + P, (2,), 40, d, 3)
+    a = oracle.recurrent_attention(q, k, v, P)
+    b = oracle.taylor_attention(q, k, v, P)
+    assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
+
+
+def test_fp32_emulation_runs_close(oracle):
+    q, k, v = _rand_qkv(7, (1,), 64, 4, 4)
+    a = oracle.recurrent_attention_f32(q, k, v, 4)
+    b = oracle.taylor_attention(q, k, v, 4)
+    assert np.max(np.abs(a - b)) < 1e-5 * np.max(np.abs(b)) * 10
+
+
+# ------------------------------------------------------------ special cases (O1)
+
+def test_P1_is_causal_running_mean(oracle):
+    """P=1 keeps only the constant order: w = 1, so o_i is the mean of v_0..v_i.
+    Catches j<i (diagonal dropped) or j<=n (non-causal)."""
+    q, k, v = _rand_qkv(11, (3,), 50, 5, 6)
+    o = oracle.taylor_attention(q, k, v, 1)
+    vv = v.astype(np.float64)
+    ref = np.cumsum(vv, axis=1) / np.arange(1, 51)[None, :, None]
+    assert np.max(np.abs(o - ref)) < 1e-13
+
+
+def _torch_softmax_attention(q, k, v):
+    """Causal scaled-dot-product softmax attention via torch library routines
+    (CPU, float64) [mokono, standard attention]."""
+    qt, kt, vt = (torch.from_numpy(np.asarray(x, dtype=np.float64)) for x in (q, k, v))
+    s = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) / math.sqrt(q.shape[-1])
+    n = q.shape[-2]
+    mask = torch.ones(n, n, dtype=torch.bool).triu(1)
+    s = s.masked_fill(mask, float("-inf"))
+    return torch.matmul(torch.softmax(s, dim=-1), vt).numpy()
+
+
+def test_softmax_oracle_matches_torch(oracle):
+    q, k, v = _rand_qkv(12, (2, 2), 70, 8, 5)
+    a = oracle.softmax_attention(q, k, v)
+    b = _torch_softmax_attention(q, k, v)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_large_P_converges_to_softmax_library(oracle):
+    """With P=24 orders the truncation error of exp on |x|<=1 is below
+    e/24! ~ 4e-24 per weight, so the Taylor oracle must equal library softmax
+    attention to rounding.  Catches a wrong 1/p!, a sign error in x, a missing
+    1/sqrt(d) scale or a q/k swap."""
+    q, k, v = _rand_qkv(13, (2, 3), 90, 16, 7)
+    a = oracle.taylor_attention(q, k, v, 24)
+    b = _torch_softmax_attention(q, k, v)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+@pytest.mark.parametrize("P", [3, 4])
+def test_softmax_gap_below_truncation_bound(oracle, P):
+    """|o_taylor - o_softmax| <= 2 eps/(1-eps) * max_j |v_j - o_softmax| with
+    eps = max_{|x|<=1} |w_P(x) e^-x - 1| (Lagrange remainder; x in [-1,1] by
+    the input recipe).  The gap the page compares with fp16 precision
+    [hotdry, 'Precision/efficiency trade-off']."""
+    xs = np.linspace(-1, 1, 20001)
+    w = sum(xs ** p / math.factorial(p) for p in range(P))
+    eps = float(np.max(np.abs(w * np.exp(-xs) - 1)))
+    q, k, v = _rand_qkv(14, (2,), 200, 8, 4)
+    a = oracle.taylor_attention(q, k, v, P)
+    b = oracle.softmax_attention(q, k, v)
+    vv = v.astype(np.float64)
+    for h in range(2):
+        for i in range(200):
+            spread = np.max(np.abs(vv[h, : i + 1] - b[h, i][None, :]))
+            assert np.max(np.abs(a[h, i] - b[h, i])) <= 2 * eps / (1 - eps) * spread + 1e-13
+
+
+def test_single_token_returns_v0(oracle):
+    q, k, v = _rand_qkv(15, (4,), 1, 6, 3)
+    o = oracle.taylor_attention(q, k, v, 4)
+    assert np.max(np.abs(o - v.astype(np.float64))) <= 4e-16 * np.max(np.abs(v))
+
+
+def test_constant_v_gives_constant_output(oracle):
+    q, k, _ = _rand_qkv(16, (2,), 64, 8, 3)
+    v = np.tile(np.array([1.5, -2.25, 0.125], dtype=np.float32), (2, 64, 1))
+    o = oracle.taylor_attention(q, k, v, 4)
+    assert np.max(np.abs(o - v.astype(np.float64))) < 1e-13
+
+
+def test_affine_equivariance_in_v(oracle):
+    """v -> a v + b maps o -> a o + b (weights sum to one after normalising).
+    Catches a missing or wrong normaliser."""
+    q, k, v = _rand_qkv(17, (2,), 64, 8, 4)
+    v = (np.round(v * 64) / 64).astype(np.float32)    # dyadic grid: a*v+b stays exact
+    o = oracle.taylor_attention(q, k, v, 3)
+    a, b = np.float32(2.0), np.float32(0.5)            # exact in fp32 for these v
+    o2 = oracle.taylor_attention(q, k, v * a + b, 3)
+    ref = o * 2.0 + 0.5
+    assert np.max(np.abs(o2 - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_joint_coordinate_permutation_invariance(oracle):
+    q, k, v = _rand_qkv(18, (2,), 64, 8, 4)
+    perm = np.random.default_rng(0).permutation(8)
+    o = oracle.taylor_attention(q, k, v, 4)
+    o2 = oracle.taylor_attention(q[..., perm], k[..., perm], v, 4)
+    assert np.max(np.abs(o - o2)) < 1e-13
+
+
+def test_row_subset_matches_full(oracle):
+    q, k, v = _rand_qkv(19, (3,), 100, 8, 4)
+    rows = np.array([0, 5, 99, 42], dtype=np.int64)
+    full = oracle.taylor_attention(q, k, v, 4)
+    sub = oracle.taylor_attention(q, k, v, 4, rows=rows)
+    assert np.array_equal(full[:, rows], sub)
+
+
+def test_exact_rational_tiny_case(oracle):
+    """Brute force in exact rational arithmetic on a tiny case with d_K=4, so
+    that 1/sqrt(d_K)=1/2 is exact.  Also checks that dropping one order (P-1)
+    would be detected."""
+    d, n, P = 4, 5, 3
+    rng = np.random.default_rng(3)
+    qi = rng.integers(-4, 5, size=(n, d))
+    ki = rng.integers(-4, 5, size=(n, d))
+    vi = rng.integers(-8, 9, size=(n, 2))
+    q = (qi / 8.0).astype(np.float32)                  # exact dyadic values
+    k = (ki / 8.0).astype(np.float32)
+    v = (vi / 4.0).astype(np.float32)
+
+    def exact(PP):
+        out = []
+        for i in range(n):
+            num = [Fraction(0), Fraction(0)]
+            den = Fraction(0)
+            for j in range(i + 1):
+                x = sum(Fraction(int(qi[i, c]), 8) * Fraction(int(ki[j, c]), 8) for c in range(d)) / 2
+                w = sum(x ** p / math.factorial(p) for p in range(PP))
+                den += w
+                for c in range(2):
+                    num[c] += w * Fraction(int(vi[j, c]), 4)
+            out.append([float(num[c] / den) for c in range(2)])
+        return np.array(out)
+
+    o = oracle.taylor_attention(q, k, v, P)
+    e = exact(P)
+    assert np.max(np.abs(o - e)) < 1e-15
+    assert np.max(np.abs(oracle.taylor_attention(q, k, v, P - 1) - e)) > 1e-6
+
+
+# ------------------------------------------------------------ closed forms (O6)
+
+@pytest.mark.parametrize("d", [1, 2, 3, 5, 8, 16, 32, 64])
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+def test_state_size_and_flops_from_bruteforce_counts(oracle, d, P):
+    """State size (d_V+1)*C(d+P-1,P-1) and the per-token FLOP formula
+    (4 d_V + 2(P d + 1)/(d + 1) + 2) C(d+P-1,P-1)
+    [hotdry, 'Engineering realisation of the constant compute cost'] against
+    the brute-force per-order counts m_p: the FLOP formula equals
+    sum_p m_p (4 d_V + 2 + 2(p+1)), the orders' update, readout, normaliser
+    and two-sided expansion work."""
+    if d == 64 and P == 4:
+        counts = [1, 64, 2080, 45760]      # brute force at d=64, p=3 takes ~1 s
+        counts[3] = len(oracle.basis_bruteforce(64, 3)[1])
+    else:
+        counts = [len(oracle.basis_bruteforce(d, p)[1]) for p in range(P)]
+    dv = d
+    assert oracle.state_size(d, dv, P) == (dv + 1) * sum(counts)
+    f = oracle.flops_per_token(d, dv, P)
+    assert f.denominator == 1
+    assert f == sum(m * (4 * dv + 2 + 2 * (p + 1)) for p, m in enumerate(counts))
+
+
+def test_flops_and_state_at_d64_p4(oracle):
+    assert oracle.flops_per_token(64, 64, 4) == 12738308
+    assert oracle.state_size(64, 64, 4) == 3113825
+    kv, fl = oracle.conventional_cost(65536, 64, 64)
+    assert kv == 8388608 and fl == 16973824
+
+
+def test_page_basis_sizes_for_P3_P5_are_rejected(oracle):
+    """The trade-off section prints 29635 (P=3) and 71525 (P=5) for d_K=64;
+    neither is the cumulative basis size, so neither is used as a pin."""
+    g = json.load(open(GOLDEN))["rejected_basis_sizes"]["page_value"]
+    assert oracle.cumulative_basis(64, 3) == 2145 != g["P=3"]
+    assert oracle.cumulative_basis(64, 5) == 814385 != g["P=5"]
