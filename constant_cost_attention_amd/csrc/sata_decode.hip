@@ -1,0 +1,203 @@
+// Fused SATA decode step for gfx950.
+//
+// One new token per head.  For every feature f of every order the kernel reads
+// the state column S[:, f] once, adds the key monomial times [v, 1], writes it
+// back and, in the same pass, accumulates the query-weighted readout
+// [hotdry, "Engineering realisation of the constant compute cost": per token,
+// map k through M_p, accumulate into the fixed state, weight and sum the
+// orders' contributions].  All orders run in the same grid [hotdry, "Hardware
+// optimisation paths and current limits": the orders have no data dependence].
+//
+// Work is HBM-bound: 8 * m * (d_V + 1) bytes per head-token of state traffic
+// against 4 * m * (d_V + 1) FLOPs.  Layout of the state: [bh][d_V+1][m_pad]
+// fp32, so a wavefront's 64 lanes touch 64 * FPT consecutive features of one
+// row: fully coalesced 16-byte accesses.
+//
+// Grid: (ceil(m_pad / (256 * FPT)), B*H) workgroups of 256 lanes; lane owns FPT
+// consecutive features.  Each workgroup leaves d_V+1 partial sums; a second,
+// tiny kernel adds the partials of a head in a fixed order and normalises, so
+// results are deterministic.
+//
+//   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
+//            engineering a constant per-token cost" (2026-02-05).
+#include "sata_device.h"
+#include "sata_internal.h"
+
+namespace sata {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecFPT = 8;     // features per lane
+
+// Wave-level reduce-scatter of DV (power of two) per-lane values followed by a
+// plain reduction across the remaining lane groups: afterwards lane l holds the
+// wavefront sum of column (l % DV).
+template <int DV>
+__device__ __forceinline__ float wave_reduce_scatter(float (&a)[DV]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int half = DV / 2; half >= 1; half /= 2) {
+        const bool upper = (lane & half) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = upper ? a[i] : a[i + half];
+            const float keep = upper ? a[i + half] : a[i];
+            a[i] = keep + __shfl_xor(send, half, 64);
+        }
+    }
+    float r = a[0];
+#pragma unroll
+    for (int off = DV; off < 64; off *= 2) r += __shfl_xor(r, off, 64);
+    return r;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+template <int DV, typename TIn>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+    const uint32_t *__restrict__ tup, const float *__restrict__ coef, float *__restrict__ state,
+    int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
+    const TIn *__restrict__ v, float *__restrict__ partial) {
+    constexpr int NC = DV + 1;
+    __shared__ float sq[72], sk[72], sv[NC];
+    __shared__ float red[kDecThreads / 64][NC];
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    if (tid < dk) {
+        sq[tid] = to_f32(q[(int64_t)bh * dk + tid]);
+        sk[tid] = to_f32(k[(int64_t)bh * dk + tid]);
+    }
+    if (tid == 0) {
+        sq[dk] = 1.f; sk[dk] = 1.f; sq[dk + 1] = 0.f; sk[dk + 1] = 0.f;
+        sv[DV] = 1.f;
+    }
+    if (tid < DV) sv[tid] = to_f32(v[(int64_t)bh * DV + tid]);
+    __syncthreads();
+
+    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * kDecFPT;
+    const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
+    float phk[kDecFPT], psq[kDecFPT];
+#pragma unroll
+    for (int j = 0; j < kDecFPT; ++j) { phk[j] = 0.f; psq[j] = 0.f; }
+    if (valid) {
+#pragma unroll
+        for (int j4 = 0; j4 < kDecFPT; j4 += 4) {
+            const uint4 t4 = *reinterpret_cast<const uint4 *>(tup + f0 + j4);
+            const float4 c4 = *reinterpret_cast<const float4 *>(coef + f0 + j4);
+            const uint32_t tt[4] = {t4.x, t4.y, t4.z, t4.w};
+            const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                phk[j4 + j] = monomial(tt[j], sk, 1);
+                psq[j4 + j] = cc[j] * monomial(tt[j], sq, 1);
+            }
+        }
+    }
+
+    float acc[NC];
+    float *Sb = state + (int64_t)bh * NC * m_pad + f0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        float a = 0.f;
+        if (valid) {
+            const float vc = sv[c];
+#pragma unroll
+            for (int j4 = 0; j4 < kDecFPT; j4 += 4) {
+                f32x4 *p = reinterpret_cast<f32x4 *>(Sb + (int64_t)c * m_pad + j4);
+                f32x4 s = __builtin_nontemporal_load(p);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s[j] += phk[j4 + j] * vc;
+                __builtin_nontemporal_store(s, p);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a += psq[j4 + j] * s[j];
+            }
+        }
+        acc[c] = a;
+    }
+
+    // workgroup reduction of the d_V + 1 readout sums
+    float vals[DV];
+#pragma unroll
+    for (int c = 0; c < DV; ++c) vals[c] = acc[c];
+    const float col = wave_reduce_scatter<DV>(vals);
+    const float den = wave_sum(acc[DV]);
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane < DV) red[wave][lane] = col;
+    if (lane == 0) red[wave][DV] = den;
+    __syncthreads();
+    if (tid < NC) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecThreads / 64; ++w) s += red[w][tid];
+        partial[((int64_t)bh * gridDim.x + blockIdx.x) * NC + tid] = s;
+    }
+}
+
+// Adds a head's partial sums in block order and divides by the normaliser.
+template <int DV, typename TOut>
+__global__ __launch_bounds__(128) void decode_finish_kernel(const float *__restrict__ partial, int nblk,
+                                                            TOut *__restrict__ out) {
+    constexpr int NC = DV + 1;
+    __shared__ float y[NC];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    if (tid < NC) {
+        float s = 0.f;
+        for (int b = 0; b < nblk; ++b) s += partial[((int64_t)bh * nblk + b) * NC + tid];
+        y[tid] = s;
+    }
+    __syncthreads();
+    if (tid < DV) out[(int64_t)bh * DV + tid] = from_f32<TOut>(y[tid] / y[DV]);
+}
+
+static int64_t decode_blocks(const sata_index *idx) {
+    const int64_t per = (int64_t)kDecThreads * kDecFPT;
+    return (idx->m_pad + per - 1) / per;
+}
+
+int64_t decode_workspace_bytes(const sata_index *idx, int64_t bh) {
+    return bh * decode_blocks(idx) * (idx->dv + 1) * (int64_t)sizeof(float);
+}
+
+template <int DV, typename TIn, typename TOut>
+static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, const void *q,
+                                  const void *k, const void *v, void *out, hipStream_t stream) {
+    const int64_t bh = (int64_t)st->batch * st->heads;
+    const int nblk = (int)decode_blocks(idx);
+    float *partial = static_cast<float *>(st->d_work);
+    hipLaunchKernelGGL((decode_kernel<DV, TIn>), dim3(nblk, (unsigned)bh), dim3(kDecThreads), 0, stream,
+                       idx->d_tup, idx->d_coef, st->d_state, idx->m_pad, idx->dk,
+                       static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                       static_cast<const TIn *>(v), partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_finish_kernel<DV, TOut>), dim3((unsigned)bh), dim3(128), 0, stream,
+                       partial, nblk, static_cast<TOut *>(out));
+    return hipGetLastError();
+}
+
+template <int DV>
+static hipError_t launch_decode_dv(const sata_index *idx, const sata_state *st, const void *q,
+                                   const void *k, const void *v, void *out, sata_dtype in_dt,
+                                   sata_dtype out_dt, hipStream_t s) {
+    if (in_dt == SATA_F32 && out_dt == SATA_F32) return launch_decode_t<DV, float, float>(idx, st, q, k, v, out, s);
+    if (in_dt == SATA_F32 && out_dt == SATA_BF16) return launch_decode_t<DV, float, bf16_t>(idx, st, q, k, v, out, s);
+    if (in_dt == SATA_BF16 && out_dt == SATA_F32) return launch_decode_t<DV, bf16_t, float>(idx, st, q, k, v, out, s);
+    return launch_decode_t<DV, bf16_t, bf16_t>(idx, st, q, k, v, out, s);
+}
+
+hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void *q, const void *k,
+                         const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt,
+                         hipStream_t stream) {
+    switch (idx->dv) {
+        case 8: return launch_decode_dv<8>(idx, st, q, k, v, out, in_dt, out_dt, stream);
+        case 16: return launch_decode_dv<16>(idx, st, q, k, v, out, in_dt, out_dt, stream);
+        case 32: return launch_decode_dv<32>(idx, st, q, k, v, out, in_dt, out_dt, stream);
+        case 64: return launch_decode_dv<64>(idx, st, q, k, v, out, in_dt, out_dt, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sata

@@ -1,0 +1,382 @@
+// Host side of libsata: index construction, state management, argument
+// validation and the extern "C" entry points declared in include/sata.h.
+//
+//   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
+//            engineering a constant per-token cost" (2026-02-05).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "sata_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sata_status fail(sata_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+sata_status fail_hip(hipError_t e, const char *what) {
+    return fail(SATA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int64_t dtype_bytes(sata_dtype t) { return t == SATA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == SATA_F32 || t == SATA_BF16; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+// Sorted index tuples i_1 <= ... <= i_p over [0, d) in lexicographic order,
+// last index fastest [hotdry, "Core insight of symmetric tensor
+// decomposition": the minimal basis of the symmetric tensor of order p].
+void enumerate_order(int d, int p, std::vector<std::vector<int>> &out) {
+    std::vector<int> idx(p, 0);
+    if (p == 0) { out.push_back(idx); return; }
+    for (;;) {
+        out.push_back(idx);
+        int r = p - 1;
+        while (r >= 0 && idx[r] == d - 1) --r;
+        if (r < 0) break;
+        ++idx[r];
+        for (int s = r + 1; s < p; ++s) idx[s] = idx[r];
+    }
+}
+
+// Product of the factorials of the run lengths of a sorted tuple (alpha!).
+double alpha_factorial(const std::vector<int> &t) {
+    double prod = 1.0;
+    size_t i = 0;
+    while (i < t.size()) {
+        size_t j = i;
+        while (j < t.size() && t[j] == t[i]) ++j;
+        for (size_t a = 2; a <= j - i; ++a) prod *= (double)a;
+        i = j;
+    }
+    return prod;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+sata_status ensure_work(sata_state *st, int64_t bytes) {
+    if (bytes <= st->work_bytes) return SATA_OK;
+    if (st->d_work) {
+        hipError_t e = hipFree(st->d_work);
+        st->d_work = nullptr;
+        st->work_bytes = 0;
+        if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
+    }
+    hipError_t e = hipMalloc(&st->d_work, (size_t)bytes);
+    if (e != hipSuccess) {
+        st->d_work = nullptr;
+        (void)hipGetLastError();
+        return fail(SATA_ERR_OOM, "workspace allocation of %lld bytes failed: %s", (long long)bytes,
+                    hipGetErrorString(e));
+    }
+    st->work_bytes = bytes;
+    return SATA_OK;
+}
+
+sata_status check_index_state(const sata_index *idx, const sata_state *st) {
+    if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
+    if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
+    if (st->idx != idx) return fail(SATA_ERR_INVALID, "state was allocated for a different index");
+    return SATA_OK;
+}
+
+}  // namespace
+
+namespace sata {
+hipError_t launch_zero(float *p, int64_t count, hipStream_t stream);
+}
+
+extern "C" {
+
+const char *sata_status_string(sata_status s) {
+    switch (s) {
+        case SATA_OK: return "ok";
+        case SATA_ERR_INVALID: return "invalid argument";
+        case SATA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SATA_ERR_OOM: return "device out of memory";
+        case SATA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *sata_last_error(void) { return g_last_error.c_str(); }
+
+// Feature tables for (d_k, P): packed tuples and query-side readout weights
+// 1/(alpha! d_k^(p/2)) (the multinomial p!/alpha! of the symmetric basis times
+// the 1/p! of the Taylor term and the d_k^(-p/2) of the logit scale)
+// [hotdry, "Core insight of symmetric tensor decomposition"].
+static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector<float> &coef) {
+    const double sqd = std::sqrt((double)d_k);
+    for (int p = 0; p < P; ++p) {
+        std::vector<std::vector<int>> tuples;
+        enumerate_order(d_k, p, tuples);
+        const double dp = std::pow(sqd, (double)p);
+        for (const auto &t : tuples) {
+            uint32_t w = (uint32_t)p << 24;
+            for (int r = 0; r < sata::kMaxOrder; ++r) {
+                const uint32_t slot = r < p ? (uint32_t)t[r] : (uint32_t)d_k;   // d_k -> constant 1
+                w |= slot << (8 * r);
+            }
+            tup.push_back(w);
+            coef.push_back((float)(1.0 / (alpha_factorial(t) * dp)));
+        }
+    }
+}
+
+static sata_status check_dims(int d_k, int d_v, int P) {
+    if (d_k <= 0 || d_v <= 0) return fail(SATA_ERR_INVALID, "head dims must be positive (d_k=%d, d_v=%d)", d_k, d_v);
+    if (P < 1) return fail(SATA_ERR_INVALID, "P must be >= 1 (got %d)", P);
+    if (!supported_dim(d_k) || !supported_dim(d_v))
+        return fail(SATA_ERR_UNSUPPORTED, "head dims must be 8, 16, 32 or 64 (d_k=%d, d_v=%d)", d_k, d_v);
+    if (P > sata::kMaxOrder + 1) return fail(SATA_ERR_UNSUPPORTED, "P <= %d supported (got %d)", sata::kMaxOrder + 1, P);
+    return SATA_OK;
+}
+
+int64_t sata_describe_features(int d_k, int P, uint32_t *tuples, float *coef, int64_t cap) {
+    g_last_error.clear();
+    if (check_dims(d_k, d_k, P) != SATA_OK) return -1;
+    std::vector<uint32_t> tup;
+    std::vector<float> cf;
+    build_tables(d_k, P, tup, cf);
+    const int64_t m = (int64_t)tup.size();
+    for (int64_t f = 0; f < m && f < cap; ++f) {
+        if (tuples) tuples[f] = tup[(size_t)f];
+        if (coef) coef[f] = cf[(size_t)f];
+    }
+    return m;
+}
+
+sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
+    g_last_error.clear();
+    if (!out) return fail(SATA_ERR_INVALID, "out is NULL");
+    sata_status s = check_dims(d_k, d_v, P);
+    if (s != SATA_OK) return s;
+
+    std::vector<uint32_t> tup;
+    std::vector<float> coef;
+    build_tables(d_k, P, tup, coef);
+    sata_index *idx = new (std::nothrow) sata_index();
+    if (!idx) return fail(SATA_ERR_OOM, "host allocation failed");
+    idx->dk = d_k;
+    idx->dv = d_v;
+    idx->P = P;
+    idx->m = (int64_t)tup.size();
+    idx->m_pad = round_up(idx->m, 64);
+    idx->m_tab = round_up(idx->m, sata::kTablePad);
+    double fact = 1.0;
+    for (int p = 0; p < P; ++p) {
+        if (p) fact *= p;
+        idx->taylor[p] = (float)(1.0 / fact);
+    }
+    const uint32_t pad = (0xffu << 24) | ((uint32_t)(d_k + 1) * 0x010101u);   // slots -> constant 0
+    tup.resize((size_t)idx->m_tab, pad);
+    coef.resize((size_t)idx->m_tab, 0.f);
+    if (hipGetDevice(&idx->device) != hipSuccess) {
+        delete idx;
+        (void)hipGetLastError();
+        return fail(SATA_ERR_HIP, "no HIP device available");
+    }
+    hipError_t e = hipMalloc(&idx->d_tup, tup.size() * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMalloc(&idx->d_coef, coef.size() * sizeof(float));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        if (idx->d_tup) (void)hipFree(idx->d_tup);
+        delete idx;
+        return fail(SATA_ERR_OOM, "index allocation failed");
+    }
+    e = hipMemcpy(idx->d_tup, tup.data(), tup.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(idx->d_coef, coef.data(), coef.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(idx->d_tup);
+        (void)hipFree(idx->d_coef);
+        delete idx;
+        return fail_hip(e, "index upload");
+    }
+    *out = idx;
+    return SATA_OK;
+}
+
+void sata_index_free(sata_index *idx) {
+    if (!idx) return;
+    DeviceGuard g(idx->device);
+    if (idx->d_tup) (void)hipFree(idx->d_tup);
+    if (idx->d_coef) (void)hipFree(idx->d_coef);
+    delete idx;
+}
+
+int64_t sata_index_features(const sata_index *idx) { return idx ? idx->m : -1; }
+
+sata_status sata_index_info(const sata_index *idx, int *d_k, int *d_v, int *P, int64_t *m, int64_t *m_pad) {
+    if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
+    if (d_k) *d_k = idx->dk;
+    if (d_v) *d_v = idx->dv;
+    if (P) *P = idx->P;
+    if (m) *m = idx->m;
+    if (m_pad) *m_pad = idx->m_pad;
+    return SATA_OK;
+}
+
+sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *stream, sata_state **out) {
+    g_last_error.clear();
+    if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
+    if (!out) return fail(SATA_ERR_INVALID, "out is NULL");
+    if (batch < 1 || heads < 1) return fail(SATA_ERR_INVALID, "batch and heads must be >= 1 (%d, %d)", batch, heads);
+    const int64_t bh = (int64_t)batch * heads;
+    if (bh > 65535) return fail(SATA_ERR_UNSUPPORTED, "batch*heads <= 65535 supported (got %lld)", (long long)bh);
+    DeviceGuard g(idx->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the index's device");
+    sata_state *st = new (std::nothrow) sata_state();
+    if (!st) return fail(SATA_ERR_OOM, "host allocation failed");
+    st->idx = idx;
+    st->batch = batch;
+    st->heads = heads;
+    st->device = idx->device;
+    st->state_bytes = bh * (idx->dv + 1) * idx->m_pad * (int64_t)sizeof(float);
+    hipError_t e = hipMalloc(&st->d_state, (size_t)st->state_bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete st;
+        return fail(SATA_ERR_OOM, "state allocation of %lld bytes failed", (long long)bh * (idx->dv + 1) * idx->m_pad * 4);
+    }
+    e = sata::launch_zero(st->d_state, st->state_bytes / 4, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        (void)hipFree(st->d_state);
+        delete st;
+        return fail_hip(e, "state clear");
+    }
+    *out = st;
+    return SATA_OK;
+}
+
+sata_status sata_state_reset(sata_state *st, void *stream) {
+    g_last_error.clear();
+    if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
+    DeviceGuard g(st->device);
+    hipError_t e = sata::launch_zero(st->d_state, st->state_bytes / 4, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "state clear");
+    return SATA_OK;
+}
+
+void sata_state_free(sata_state *st) {
+    if (!st) return;
+    DeviceGuard g(st->device);
+    if (st->d_state) (void)hipFree(st->d_state);
+    if (st->d_work) (void)hipFree(st->d_work);
+    delete st;
+}
+
+sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes) {
+    if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
+    if (dev_ptr) *dev_ptr = st->d_state;
+    if (bytes) *bytes = st->state_bytes;
+    return SATA_OK;
+}
+
+sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
+                         void *out, int64_t n, int chunk, sata_dtype in_dt, sata_dtype out_dt, void *stream) {
+    g_last_error.clear();
+    sata_status s = check_index_state(idx, st);
+    if (s != SATA_OK) return s;
+    if (n < 0) return fail(SATA_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return fail(SATA_ERR_INVALID, "unknown dtype");
+    if (chunk != 0 && chunk != 64 && chunk != 128)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
+    if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
+    if (n == 0) return SATA_OK;
+    if (!q || !k || !v || !out) return fail(SATA_ERR_INVALID, "q, k, v and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(SATA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    const int64_t bh = (int64_t)st->batch * st->heads;
+    const int64_t in_b = dtype_bytes(in_dt), out_b = dtype_bytes(out_dt);
+    const int64_t nq = bh * n * idx->dk * in_b, nv = bh * n * idx->dv * in_b, no = bh * n * idx->dv * out_b;
+    if (overlaps(out, no, q, nq) || overlaps(out, no, k, nq) || overlaps(out, no, v, nv))
+        return fail(SATA_ERR_INVALID, "out overlaps q, k or v");
+    const sata::PrefillPlan plan = sata::plan_prefill(idx, bh, n, chunk, in_dt);
+    if (!plan.ok) return fail(SATA_ERR_UNSUPPORTED, "no prefill plan for this configuration");
+    DeviceGuard g(st->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    s = ensure_work(st, plan.work_bytes);
+    if (s != SATA_OK) return s;
+    hipError_t e = sata::launch_prefill(idx, st, plan, q, k, v, out, n, in_dt, out_dt, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "prefill launch");
+    return SATA_OK;
+}
+
+sata_status sata_decode_step(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
+                             void *out, sata_dtype in_dt, sata_dtype out_dt, void *stream) {
+    g_last_error.clear();
+    sata_status s = check_index_state(idx, st);
+    if (s != SATA_OK) return s;
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return fail(SATA_ERR_INVALID, "unknown dtype");
+    if (!q || !k || !v || !out) return fail(SATA_ERR_INVALID, "q, k, v and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(SATA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    const int64_t bh = (int64_t)st->batch * st->heads;
+    const int64_t in_b = dtype_bytes(in_dt), out_b = dtype_bytes(out_dt);
+    const int64_t nq = bh * idx->dk * in_b, nv = bh * idx->dv * in_b, no = bh * idx->dv * out_b;
+    if (overlaps(out, no, q, nq) || overlaps(out, no, k, nq) || overlaps(out, no, v, nv))
+        return fail(SATA_ERR_INVALID, "out overlaps q, k or v");
+    DeviceGuard g(st->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    s = ensure_work(st, sata::decode_workspace_bytes(idx, bh));
+    if (s != SATA_OK) return s;
+    hipError_t e = sata::launch_decode(idx, st, q, k, v, out, in_dt, out_dt, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "decode launch");
+    return SATA_OK;
+}
+
+sata_status sata_expand_features(const sata_index *idx, const void *x, void *out, int64_t rows, int side,
+                                 sata_dtype in_dt, void *stream) {
+    g_last_error.clear();
+    if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
+    if (rows < 0) return fail(SATA_ERR_INVALID, "rows must be >= 0");
+    if (side != 0 && side != 1) return fail(SATA_ERR_INVALID, "side must be 0 (key) or 1 (query)");
+    if (!valid_dtype(in_dt)) return fail(SATA_ERR_INVALID, "unknown dtype");
+    if (rows > 65535) return fail(SATA_ERR_UNSUPPORTED, "rows <= 65535 per call");
+    if (rows == 0) return SATA_OK;
+    if (!x || !out) return fail(SATA_ERR_INVALID, "x and out must be non-NULL");
+    if (overlaps(out, rows * idx->m_pad * 4, x, rows * idx->dk * dtype_bytes(in_dt)))
+        return fail(SATA_ERR_INVALID, "out overlaps x");
+    DeviceGuard g(idx->device);
+    hipError_t e = sata::launch_expand(idx, x, out, rows, side, in_dt, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "expand launch");
+    return SATA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host side of libsata and its kernels.
+//
+// Feature numbering and the packed tuple table
+//   Features run order by order, p = 0..P-1; within an order they are the
+//   sorted index tuples i_1 <= ... <= i_p over [0, d_K) in lexicographic order
+//   (last index fastest) [hotdry, "Core insight of symmetric tensor
+//   decomposition"; "Hardware optimisation paths and current limits" for the
+//   nested i_1 <= ... <= i_p structure].  Each feature is packed in one 32-bit
+//   word: bytes 0..2 are the tuple's indices, byte 3 its order.  Unused index
+//   slots (orders below 3) hold d_K, which the kernels map to the constant 1;
+//   padding features (f >= m) hold d_K + 1 in every slot, mapped to 0, so their
+//   monomial vanishes.  Orders up to 3 (P <= 4) fit.
+//
+//   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
+//            engineering a constant per-token cost" (2026-02-05).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sata.h"
+
+struct sata_index {
+    int dk = 0, dv = 0, P = 0;
+    int64_t m = 0;       // C(d_K+P-1, P-1)
+    int64_t m_pad = 0;   // state row stride (multiple of 64)
+    int64_t m_tab = 0;   // table length (multiple of kTablePad, covers every kernel's tail)
+    int device = 0;
+    uint32_t *d_tup = nullptr;   // [m_tab] packed tuples
+    float *d_coef = nullptr;     // [m_tab] query-side readout weight 1/(alpha! d_K^(p/2)); 0 for padding
+    float taylor[8] = {0};       // 1/p!, p < P (intra-chunk direct weights)
+};
+
+struct sata_state {
+    const sata_index *idx = nullptr;
+    int batch = 0, heads = 0;
+    int device = 0;
+    float *d_state = nullptr;    // [B*H][d_V+1][m_pad]
+    int64_t state_bytes = 0;
+    void *d_work = nullptr;      // prefill / decode partial sums (grown on demand)
+    int64_t work_bytes = 0;
+};
+
+namespace sata {
+
+constexpr int kTablePad = 2048;          // tables cover every slice up to this granularity
+constexpr int kMaxOrder = 3;             // P <= 4
+
+// ---- launchers (defined in the .hip files) --------------------------------
+
+// Decode: one token per head.  Returns hipSuccess or the launch error.
+hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void *q, const void *k,
+                         const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt,
+                         hipStream_t stream);
+int64_t decode_workspace_bytes(const sata_index *idx, int64_t bh);
+
+// Prefill plan: how the sequence is split into chunks, feature slices and
+// segments, and how large the partial-sum workspace must be.
+struct PrefillPlan {
+    int chunk = 0;          // tokens per chunk
+    int fw = 0;             // features per wave
+    int fs = 0;             // features per workgroup slice
+    int slices = 0;         // workgroups per head
+    int64_t seg_chunks = 0; // chunks per segment (bounded by the workspace cap)
+    int64_t work_bytes = 0; // workspace needed
+    bool ok = false;
+};
+PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt);
+hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
+                          const void *q, const void *k, const void *v, void *out, int64_t n,
+                          sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream);
+
+hipError_t launch_expand(const sata_index *idx, const void *x, void *out, int64_t rows, int side,
+                         sata_dtype in_dt, hipStream_t stream);
+
+}  // namespace sata

@@ -1,0 +1,173 @@
+/*
+ * sata.h -- C ABI of the MI355X (gfx950) SATA attention library, libsata.so.
+ *
+ * SATA (symmetry-aware Taylor approximation) attention is causal attention
+ * whose weight is the exp kernel truncated after P Taylor orders,
+ *     x_ij = q_i . k_j / sqrt(d_K),   w(x) = sum_{p<P} x^p / p!,
+ *     o_i  = sum_{j<=i} w(x_ij) v_j / sum_{j<=i} w(x_ij),
+ * computed without an n x n matrix: keys and queries are mapped onto the
+ * minimal basis of the symmetric tensors of order p (sorted index tuples
+ * i_1 <= ... <= i_p, the tables M_p), and a fixed-size state
+ *     S_p = sum_s phi_p(k_s) (x) [v_s, 1]
+ * of (d_V + 1) * C(d_K+P-1, P-1) values per head is accumulated and read out.
+ *
+ * Citations (page title and section):
+ *   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
+ *            engineering a constant per-token cost" (2026-02-05):
+ *            "Core insight of symmetric tensor decomposition" -- the minimal
+ *            basis C(d_K+p-1, p) and the fixed, precomputed index tables M_p;
+ *            "Engineering realisation of the constant compute cost" -- the
+ *            state size, the per-token steps (map k through M_p, accumulate,
+ *            weight and sum the orders' contributions) and the FLOP count;
+ *            "Hardware optimisation paths and current limits" -- the
+ *            hierarchical i_1 <= ... <= i_p structure, orders run in parallel.
+ *   [mokono] www.mokono.cn attention-variants survey, standard attention:
+ *            the (batch, heads, seq_len, dim) tensor layout.
+ *
+ * Conventions for every entry point
+ *   - Status codes: every call returns sata_status; no C++ exception crosses
+ *     this boundary.  Argument checks happen before any work is enqueued and
+ *     have no side effects (SATA_ERR_INVALID).  sata_last_error() returns a
+ *     thread-local message describing the last failure on this thread.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the legacy
+ *     default stream).  Calls that take a stream only enqueue work; kernel
+ *     faults surface at the caller's next synchronisation.  A state must not
+ *     be used from two streams at once.
+ *   - Memory: q, k, v, out are device pointers owned by the caller, contiguous
+ *     row-major, 16-byte aligned; `out` must not overlap q, k or v.  The
+ *     library owns index and state memory (hipMalloc) and frees it in the
+ *     *_free calls.
+ *   - Supported shapes: d_K, d_V in {8, 16, 32, 64} with d_K == d_V for
+ *     prefill; 1 <= P <= 4.  Other values return SATA_ERR_UNSUPPORTED.
+ */
+#ifndef SATA_H
+#define SATA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SATA_OK = 0,
+    SATA_ERR_INVALID = 1,      /* bad argument: null pointer, size, alignment, aliasing */
+    SATA_ERR_UNSUPPORTED = 2,  /* valid but not built: (d_K, d_V, P, dtype, chunk) */
+    SATA_ERR_OOM = 3,          /* device allocation failed */
+    SATA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} sata_status;
+
+typedef enum {
+    SATA_F32 = 0,              /* IEEE float32 */
+    SATA_BF16 = 1              /* bfloat16 (upper half of a float32) */
+} sata_dtype;
+
+/* Immutable, device-resident M_p tables and coefficients for one (d_K, d_V, P). */
+typedef struct sata_index sata_index;
+/* Fixed-size recurrent state of B x H heads plus its reusable workspace. */
+typedef struct sata_state sata_state;
+
+/* Build the index tables M_p for orders p = 0..P-1 [hotdry, "Core insight of
+ * symmetric tensor decomposition": the sorted-tuple basis is fixed and can be
+ * precomputed].  Features are numbered order by order (p = 0, 1, ..., P-1),
+ * and within an order in lexicographic order of the sorted tuple (last index
+ * fastest), so each order-(p-1) parent owns a contiguous run of children
+ * [hotdry, "Hardware optimisation paths and current limits"].  Synchronous:
+ * enumerates on the host, uploads to the current device.
+ * d_k, d_v: head dims; P: number of Taylor orders (constant term included).
+ * *out receives the handle on success and is untouched on failure. */
+sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out);
+
+/* Free an index (NULL is a no-op).  The caller must ensure no enqueued work
+ * still uses it (synchronise first). */
+void sata_index_free(sata_index *idx);
+
+/* m = C(d_K+P-1, P-1), the features per head over all orders
+ * [hotdry, "Engineering realisation of the constant compute cost"]; -1 if idx
+ * is NULL. */
+int64_t sata_index_features(const sata_index *idx);
+
+/* Shape of an index: any out-pointer may be NULL.  m_pad is the padded
+ * feature stride of the state layout (a multiple of 64, >= m). */
+sata_status sata_index_info(const sata_index *idx, int *d_k, int *d_v, int *P,
+                            int64_t *m, int64_t *m_pad);
+
+/* Allocate the zeroed state of batch x heads heads for `idx`, enqueueing the
+ * clear on `stream`.  Layout (fp32): [batch][heads][d_V + 1][m_pad], feature
+ * axis contiguous; row c < d_V holds sum_s prod_r k_s[i_r] * v_s[c], row d_V
+ * holds sum_s prod_r k_s[i_r] (the "+1" column of [hotdry, "Engineering
+ * realisation of the constant compute cost"]), features f >= m are zero.
+ * The key side carries the plain monomial; the multinomial weight
+ * p!/alpha!, the 1/p! of the Taylor term and d_K^(-p/2) are applied on the
+ * query side at readout.  The state keeps a pointer to idx: free the state
+ * before the index. */
+sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *stream,
+                             sata_state **out);
+
+/* Zero the state (start a new sequence); enqueued on `stream`. */
+sata_status sata_state_reset(sata_state *st, void *stream);
+
+/* Free a state and its workspace (NULL is a no-op).  Synchronise first. */
+void sata_state_free(sata_state *st);
+
+/* Device pointer and byte size of the state buffer (for checkpointing or
+ * inspection; the layout is given at sata_state_alloc). */
+sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes);
+
+/* Causal prefill of n tokens for every head of the state, continuing from the
+ * state's content (a zeroed state starts a fresh sequence); on return (in
+ * stream order) the state covers every token seen.
+ * q, k: [batch][heads][n][d_K]; v, out: [batch][heads][n][d_V]; in_dt is the
+ * dtype of q, k, v; out_dt that of out.  Token i attends to every earlier
+ * token and to itself.  The sequence is processed in chunks of `chunk` tokens
+ * (0 = default, 128 for d_K = 64 and 64 otherwise; supported: 64, 128):
+ * within a chunk the Taylor weights are formed directly, across chunks the
+ * orders' states are scanned and read out [hotdry, "Engineering realisation
+ * of the constant compute cost"]; results do not depend on the chunk length
+ * beyond rounding.  n = 0 is a no-op.  May grow the state's workspace
+ * (hipMalloc) on the first call at a given size. */
+sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, const void *k,
+                         const void *v, void *out, int64_t n, int chunk, sata_dtype in_dt,
+                         sata_dtype out_dt, void *stream);
+
+/* One decode step for every head: with q, k: [batch][heads][d_K] and
+ * v: [batch][heads][d_V] of the new token, add phi(k) (x) [v, 1] to every
+ * order's state, then read out and normalise into out: [batch][heads][d_V]
+ * [hotdry, "Engineering realisation of the constant compute cost": the cost
+ * per token is fixed by d_K, d_V and P].  Each head's state is streamed once
+ * (read and written), coalesced along the feature axis. */
+sata_status sata_decode_step(const sata_index *idx, sata_state *st, const void *q, const void *k,
+                             const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt,
+                             void *stream);
+
+/* Feature expansion on its own (tests and inspection): for rows x: [rows][d_K]
+ * write out: [rows][m_pad] fp32 with, per feature f = (i_1..i_p) of order p,
+ *   side 0 (key):   prod_r x[i_r]
+ *   side 1 (query): prod_r x[i_r] / (alpha_f! * d_K^(p/2))
+ * where alpha_f! is the product of the factorials of the index multiplicities,
+ * so that sum_f key(k)_f * query(q)_f * p! over the features of order p equals
+ * (q.k / sqrt(d_K))^p [hotdry, "Core insight of symmetric tensor
+ * decomposition"].  Features f >= m are zero. */
+sata_status sata_expand_features(const sata_index *idx, const void *x, void *out, int64_t rows,
+                                 int side, sata_dtype in_dt, void *stream);
+
+/* Host-only description of the feature tables sata_build_index uploads for
+ * (d_k, P), without touching a GPU (tests and inspection).  Writes up to cap
+ * entries: tuples[f] = the packed tuple word of feature f (bytes 0..2 the
+ * indices i_1..i_p, unused slots = d_k; byte 3 the order p) and coef[f] =
+ * 1/(alpha_f! d_k^(p/2)) rounded to fp32, in the feature order described at
+ * sata_build_index.  Either array may be NULL.  Returns m, or -1 for
+ * arguments sata_build_index would reject. */
+int64_t sata_describe_features(int d_k, int P, uint32_t *tuples, float *coef, int64_t cap);
+
+/* Static description of a status code. */
+const char *sata_status_string(sata_status s);
+
+/* Thread-local detail of the last failure on the calling thread ("" if none). */
+const char *sata_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATA_H */
