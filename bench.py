@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Throughput of the SATA hot path on one MI355X.
+
+One step = one causal prefill (state reset + sata_prefill) of the workload
+prefill_d64_p4_bf16: batch 1, 8 heads, n = 65536 tokens, d_K = d_V = 64,
+P = 4, bf16 q/k/v, fp32 state, chunk 128.  `value` is prefill tokens/s
+(batch * n / step time) with inputs already resident in HBM.
+
+Beside it the same JSON line carries
+  - roofline: the dominant kernel (prefill scan) against the bf16 MFMA peak,
+    its duration taken from HIP events the library records around each of
+    its launches on the launch stream;
+  - decode: workload decode_d64_p4_f32 (32 x 8 heads, state built by an
+    fp32 prefill of 8192 tokens, then 1024 timed decode steps with fresh
+    inputs), tokens/s = batch / step time, and its roofline against HBM;
+    plus per-step latency after 8192-, 32768- and 65536-token prefixes;
+  - extra: the other prefill workloads;
+  - cpu_baseline: the fp64 oracle on the host's cores on a bounded sample of
+    the prefill workload's rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Progress goes to stderr; stdout gets exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SATA tokens/sec (prefill, decode) at d_K=64 P=4; % of HBM / MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix / vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "constant_cost_attention_amd", "csrc")
+
+
+def log(msg: str):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-flatness", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    return ap.parse_args()
+
+
+def source_sha(fname: str) -> str:
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel and
+    workload, or None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel, {}).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_sha(rec["source"]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def features(d: int, P: int) -> int:
+    return math.comb(d + P - 1, P - 1)
+
+
+def prefill_flops(wl) -> float:
+    """Algorithmic FLOPs of the chunk-state and readout contractions:
+    4 m (d_V + 1) per head-token (state update and readout, normaliser column included)."""
+    return 4.0 * features(wl.d_k, wl.P) * (wl.d_v + 1) * wl.batch * wl.heads * wl.n
+
+
+def decode_bytes(wl) -> float:
+    """Algorithmic HBM bytes of one decode step: every head's fp32 state read
+    and written once, plus the token's q, k, v in and out's write."""
+    m = features(wl.d_k, wl.P)
+    return float(wl.batch * wl.heads * (8 * m * (wl.d_v + 1) + 4 * (2 * wl.d_k + 2 * wl.d_v)))
+
+
+# ------------------------------------------------------------------ prefill
+
+def upload(x):
+    import numpy as np
+    import torch
+    def one(name):
+        a = x.storage(name)
+        if x.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+    return one("q"), one("k"), one("v")
+
+
+def time_prefill(sata, wl, q, k, v, steps: int, warmup: int):
+    import torch
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    st = sata.State(idx, wl.batch, wl.heads)
+    out = torch.empty(v.shape, dtype=v.dtype, device="cuda")
+    for _ in range(warmup):
+        sata.sata_state_reset(st)
+        sata.sata_prefill(idx, st, q, k, v, out, chunk=wl.chunk)
+    torch.cuda.synchronize()
+    sata.sata_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        sata.sata_state_reset(st)
+        sata.sata_prefill(idx, st, q, k, v, out, chunk=wl.chunk)
+    e1.record()
+    torch.cuda.synchronize()
+    sata.sata_profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
+    scan_ms, scan_n = sata.sata_profile_query("prefill_scan")
+    comb_ms, comb_n = sata.sata_profile_query("prefill_combine")
+    flops = prefill_flops(wl)
+    launches_per_step = scan_n / steps
+    scan_avg = scan_ms / scan_n
+    achieved = (flops / launches_per_step) / (scan_avg * 1e-3) / 1e12
+    res = {
+        "workload": wl.name,
+        "value": wl.batch * wl.n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_step": ms,
+        "tflops_whole_call": flops / (ms * 1e-3) / 1e12,
+        "roofline": {
+            "bound": "mfma", "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS,
+            "unit": "TFLOP/s", "kernel": "prefill_scan",
+            "launches_per_step": launches_per_step, "avg_launch_ms": scan_avg,
+            "flops_per_launch": flops / launches_per_step,
+            "traffic": traffic_for("prefill_scan", wl.name),
+        },
+        "combine_ms_per_step": comb_ms / steps,
+    }
+    res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
+    st.free()
+    idx.free()
+    return res
+
+
+# ------------------------------------------------------------------ decode
+
+def build_state(sata, idx, wl, prefix: int, dtype: str, seed: int):
+    """Fresh state filled by a causal prefill of `prefix` seeded device tokens."""
+    import torch
+    import synth_inputs as si
+    st = sata.State(idx, wl.batch, wl.heads)
+    step = 8192
+    for t0 in range(0, prefix, step):
+        n = min(step, prefix - t0)
+        q, k, v = si.draw_qkv_device((wl.batch, wl.heads), n, wl.d_k, wl.d_v, seed + t0, dtype)
+        out = torch.empty(v.shape, dtype=v.dtype, device="cuda")
+        sata.sata_prefill(idx, st, q, k, v, out)
+        del q, k, v, out
+    torch.cuda.synchronize()
+    return st
+
+
+def time_decode(sata, idx, st, wl, steps: int, warmup: int, seed: int):
+    import torch
+    import synth_inputs as si
+    q, k, v = si.draw_qkv_device((wl.batch, wl.heads), steps + warmup, wl.d_k, wl.d_v, seed, "f32")
+    q, k, v = (t.permute(2, 0, 1, 3).contiguous() for t in (q, k, v))     # [steps, B, H, d]
+    out = torch.empty((steps + warmup, wl.batch, wl.heads, wl.d_v), dtype=torch.float32, device="cuda")
+    for t in range(warmup):
+        sata.sata_decode_step(idx, st, q[t], k[t], v[t], out[t])
+    torch.cuda.synchronize()
+    sata.sata_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warmup, warmup + steps):
+        sata.sata_decode_step(idx, st, q[t], k[t], v[t], out[t])
+    e1.record()
+    torch.cuda.synchronize()
+    sata.sata_profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
+    dms, dn = sata.sata_profile_query("decode_stream")
+    fms, fn = sata.sata_profile_query("decode_finish")
+    return ms, dms / dn, fms / fn
+
+
+def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    log("decode: fp32 prefill of %d tokens x %d heads" % (wl.n, wl.batch * wl.heads))
+    st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
+    ms, kern_ms, fin_ms = time_decode(sata, idx, st, wl, steps, warmup, wl.seed + 30)
+    st.free()
+    nbytes = decode_bytes(wl)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "workload": wl.name, "value": wl.batch / (ms * 1e-3), "unit": "tokens/s",
+        "ms_per_step": ms, "steps": steps, "prefix": wl.n,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "kernel": "decode_stream", "avg_launch_ms": kern_ms,
+            "bytes_per_launch": nbytes, "traffic": traffic_for("decode_stream", wl.name),
+        },
+        "finish_ms_per_step": fin_ms,
+        "gbs_whole_step": nbytes / (ms * 1e-3) / 1e9,
+    }
+    if flatness:
+        flat = {}
+        for prefix in (8192, 32768, 65536):
+            log("decode flatness: bf16 prefill of %d tokens" % prefix)
+            st = build_state(sata, idx, wl, prefix, "bf16", wl.seed + 100 + prefix)
+            fms, fk, _ = time_decode(sata, idx, st, wl, 256, 8, wl.seed + 200 + prefix)
+            st.free()
+            flat[str(prefix)] = {"ms_per_step": fms, "kernel_ms": fk}
+        base = flat["8192"]["ms_per_step"]
+        res["flatness"] = {"per_prefix": flat,
+                           "max_rel_dev": max(abs(f["ms_per_step"] / base - 1) for f in flat.values())}
+    idx.free()
+    return res
+
+
+# ------------------------------------------------------------------ oracle on the host
+
+def cpu_baseline(wl, x, budget_s: float):
+    """The oracle (fp64, all host cores) on uniformly strided rows of every head;
+    the full-prefill time is extrapolated by n / rows (the sample's average
+    context equals the full prefill's)."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    cores = oracle.num_cpus()
+
+    def run(r):
+        rows = np.unique(np.linspace(0, wl.n - 1, r).round().astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.taylor_attention(x.q, x.k, x.v, wl.P, rows=rows, threads=cores)
+        return rows, time.perf_counter() - t0
+
+    rows, t = run(16)
+    r = int(min(wl.n, max(16, 16 * budget_s / max(t, 1e-3))))
+    rows, t = run(r)
+    per_token = t / len(rows)                       # seconds per token (all heads), average context
+    return {
+        "value": 1.0 / per_token, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": "%d uniformly strided rows (positions 0..%d) of all %d heads of %s; "
+                  "full-prefill time extrapolated by n/rows; %.1f s of oracle time"
+                  % (len(rows), wl.n - 1, wl.heads, wl.name, t),
+    }
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not supported: "
+              "multi-GPU execution is not implemented" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth_inputs as si
+    from constant_cost_attention_amd import sata
+    sata.load()
+    torch.cuda.set_device(0)
+
+    wl = si.WORKLOADS["prefill_d64_p4_bf16"]
+    log("drawing %s inputs" % wl.name)
+    x = wl.draw()
+    q, k, v = upload(x)
+    log("prefill %s: %d warmup + %d timed steps" % (wl.name, args.warmup, args.steps))
+    pre = time_prefill(sata, wl, q, k, v, args.steps, args.warmup)
+    log("prefill: %.3f ms/step, %.3e tok/s, scan %.1f TFLOP/s (%.1f%% of peak)"
+        % (pre["ms_per_step"], pre["value"], pre["roofline"]["achieved"], 100 * pre["roofline"]["frac"]))
+    del q, k, v
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": pre["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.n,
+                   "d_k": wl.d_k, "d_v": wl.d_v, "P": wl.P, "chunk": wl.chunk,
+                   "inputs": "bf16 q/k/v, fp32 state", "parallelism": "single GPU"},
+        "roofline": pre["roofline"],
+        "prefill": {k2: pre[k2] for k2 in ("tflops_whole_call", "combine_ms_per_step")},
+    }
+
+    if not args.no_decode:
+        dwl = si.WORKLOADS["decode_d64_p4_f32"]
+        dec = decode_section(sata, dwl, args.decode_steps, 8, not args.no_flatness)
+        log("decode: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak)"
+            % (dec["ms_per_step"], dec["value"], dec["roofline"]["achieved"], 100 * dec["roofline"]["frac"]))
+        result["decode"] = dec
+        torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = []
+        for name in ("prefill_d32_p4_bf16", "prefill_d16x64h_p4_bf16", "prefill_d16_p4_f32"):
+            ewl = si.WORKLOADS[name]
+            eq, ek, ev = si.draw_qkv_device((ewl.batch, ewl.heads), ewl.n, ewl.d_k, ewl.d_v, ewl.seed, ewl.dtype)
+            r = time_prefill(sata, ewl, eq, ek, ev, max(3, args.steps // 2), 1)
+            log("extra %s: %.3f ms/step, %.3e tok/s, %.1f%% of peak"
+                % (name, r["ms_per_step"], r["value"], 100 * r["roofline"]["frac"]))
+            extra.append(r)
+            del eq, ek, ev
+            torch.cuda.empty_cache()
+        result["extra"] = extra
+
+    if not args.no_cpu:
+        log("cpu baseline: oracle on the host (budget %.0f s)" % args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget)
+        log("cpu baseline: %.3e tok/s on %d cores" % (result["cpu_baseline"]["value"],
+                                                      result["cpu_baseline"]["cores"]))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

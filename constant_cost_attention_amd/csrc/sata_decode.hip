@@ -167,14 +167,20 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
     const int64_t bh = (int64_t)st->batch * st->heads;
     const int nblk = (int)decode_blocks(idx);
     float *partial = static_cast<float *>(st->d_work);
-    hipLaunchKernelGGL((decode_kernel<DV, TIn>), dim3(nblk, (unsigned)bh), dim3(kDecThreads), 0, stream,
-                       idx->d_tup, idx->d_coef, st->d_state, idx->m_pad, idx->dk,
-                       static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                       static_cast<const TIn *>(v), partial);
+    {
+        ProfScope ps(kProfDecode, stream);
+        hipLaunchKernelGGL((decode_kernel<DV, TIn>), dim3(nblk, (unsigned)bh), dim3(kDecThreads), 0, stream,
+                           idx->d_tup, idx->d_coef, st->d_state, idx->m_pad, idx->dk,
+                           static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), partial);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_finish_kernel<DV, TOut>), dim3((unsigned)bh), dim3(128), 0, stream,
-                       partial, nblk, static_cast<TOut *>(out));
+    {
+        ProfScope ps(kProfDecodeFinish, stream);
+        hipLaunchKernelGGL((decode_finish_kernel<DV, TOut>), dim3((unsigned)bh), dim3(128), 0, stream,
+                           partial, nblk, static_cast<TOut *>(out));
+    }
     return hipGetLastError();
 }
 

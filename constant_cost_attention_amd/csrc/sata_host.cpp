@@ -380,3 +380,110 @@ sata_status sata_expand_features(const sata_index *idx, const void *x, void *out
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- profiling
+
+#include <mutex>
+
+namespace {
+
+struct ProfRecord {
+    int kernel;
+    hipEvent_t a, b;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+    // caller holds g_prof_mu
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return e;
+}
+
+void prof_clear_locked() {
+    for (auto &r : g_prof) {
+        g_prof_pool.push_back(r.a);
+        g_prof_pool.push_back(r.b);
+    }
+    g_prof.clear();
+}
+
+const char *const kProfNames[sata::kProfCount] = {"prefill_scan", "prefill_combine", "decode_stream",
+                                                   "decode_finish"};
+
+}  // namespace
+
+namespace sata {
+
+ProfScope::ProfScope(int k, hipStream_t s) : kernel(k), stream(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    start = prof_event();
+    if (start && hipEventRecord(start, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        g_prof_pool.push_back(start);
+        start = nullptr;
+    }
+}
+
+ProfScope::~ProfScope() {
+    if (!start) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t stop = prof_event();
+    if (!stop || hipEventRecord(stop, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        g_prof_pool.push_back(start);
+        if (stop) g_prof_pool.push_back(stop);
+        return;
+    }
+    g_prof.push_back({kernel, start, stop});
+}
+
+}  // namespace sata
+
+extern "C" {
+
+sata_status sata_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (on) prof_clear_locked();
+    g_prof_on = on != 0;
+    return SATA_OK;
+}
+
+sata_status sata_profile_query(int kernel, double *total_ms, int64_t *launches) {
+    if (kernel < 0 || kernel >= sata::kProfCount) return fail(SATA_ERR_INVALID, "unknown kernel id %d", kernel);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    double tot = 0.0;
+    int64_t cnt = 0;
+    for (auto &r : g_prof) {
+        if (r.kernel != kernel) continue;
+        hipError_t e = hipEventSynchronize(r.b);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) return fail_hip(e, "profile event");
+        tot += ms;
+        ++cnt;
+    }
+    if (total_ms) *total_ms = tot;
+    if (launches) *launches = cnt;
+    return SATA_OK;
+}
+
+const char *sata_profile_kernel_name(int kernel) {
+    if (kernel < 0 || kernel >= sata::kProfCount) return nullptr;
+    return kProfNames[kernel];
+}
+
+}  // extern "C"

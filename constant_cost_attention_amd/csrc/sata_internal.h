@@ -70,6 +70,18 @@ hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const Pre
                           const void *q, const void *k, const void *v, void *out, int64_t n,
                           sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream);
 
+// Kernel timing instrumentation (see sata_profile_enable).  A ProfScope
+// records an event before and after the launches in its lifetime when
+// profiling is on, and does nothing otherwise.
+enum ProfKernel { kProfScan = 0, kProfCombine = 1, kProfDecode = 2, kProfDecodeFinish = 3, kProfCount = 4 };
+struct ProfScope {
+    ProfScope(int kernel, hipStream_t stream);
+    ~ProfScope();
+    int kernel;
+    hipStream_t stream;
+    hipEvent_t start = nullptr;
+};
+
 hipError_t launch_expand(const sata_index *idx, const void *x, void *out, int64_t rows, int side,
                          sata_dtype in_dt, hipStream_t stream);
 

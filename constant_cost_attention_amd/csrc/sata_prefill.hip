@@ -393,17 +393,23 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     for (int64_t c0 = 0; c0 < nchunks; c0 += plan.seg_chunks) {
         const int nseg = (int)std::min<int64_t>(plan.seg_chunks, nchunks - c0);
         const int64_t tok0 = c0 * C;
-        hipLaunchKernelGGL(scan, dim3(plan.slices, (unsigned)bh), dim3(kThreads), Cfg::LDS, stream,
-                           idx->d_tup, idx->d_coef, st->d_state, idx->m_pad,
-                           static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), n, tok0, nseg, partial);
+        {
+            ProfScope ps(kProfScan, stream);
+            hipLaunchKernelGGL(scan, dim3(plan.slices, (unsigned)bh), dim3(kThreads), Cfg::LDS, stream,
+                               idx->d_tup, idx->d_coef, st->d_state, idx->m_pad,
+                               static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                               static_cast<const TIn *>(v), n, tok0, nseg, partial);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(comb, dim3(nseg, (unsigned)bh), dim3(256), comb_lds, stream,
-                           static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), static_cast<TOut *>(out), n, tok0, nseg,
-                           plan.slices, partial, 1.0f / sqrtf((float)D), idx->taylor[0],
-                           idx->taylor[1], idx->taylor[2], idx->taylor[3], idx->P);
+        {
+            ProfScope ps(kProfCombine, stream);
+            hipLaunchKernelGGL(comb, dim3(nseg, (unsigned)bh), dim3(256), comb_lds, stream,
+                               static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                               static_cast<const TIn *>(v), static_cast<TOut *>(out), n, tok0, nseg,
+                               plan.slices, partial, 1.0f / sqrtf((float)D), idx->taylor[0],
+                               idx->taylor[1], idx->taylor[2], idx->taylor[3], idx->P);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -27,6 +27,7 @@ _EXPORTS = (
     "sata_state_alloc", "sata_state_reset", "sata_state_free", "sata_state_data",
     "sata_prefill", "sata_decode_step", "sata_expand_features", "sata_describe_features",
     "sata_status_string", "sata_last_error",
+    "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
 )
 
 _lib = None
@@ -80,7 +81,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_status_string.restype = ctypes.c_char_p
     lib.sata_last_error.argtypes = []
     lib.sata_last_error.restype = ctypes.c_char_p
-    for name in ("sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_reset",
+    lib.sata_profile_enable.argtypes = [cint]
+    lib.sata_profile_query.argtypes = [cint, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.sata_profile_kernel_name.argtypes = [cint]
+    lib.sata_profile_kernel_name.restype = ctypes.c_char_p
+    for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_reset",
                  "sata_state_data", "sata_prefill", "sata_decode_step", "sata_expand_features"):
         getattr(lib, name).restype = cint
     _lib = lib
@@ -275,6 +280,26 @@ def sata_describe_features(d_k: int, P: int):
     lib.sata_describe_features(int(d_k), int(P), tup.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
                                coef.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), m)
     return tup, coef
+
+
+PROFILE_KERNELS = {"prefill_scan": 0, "prefill_combine": 1, "decode_stream": 2, "decode_finish": 3}
+
+
+def sata_profile_enable(on: bool):
+    _check(load().sata_profile_enable(1 if on else 0), "sata_profile_enable")
+
+
+def sata_profile_query(kernel) -> tuple:
+    """(summed milliseconds, launches) of one kernel's recorded event pairs."""
+    kid = PROFILE_KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(load().sata_profile_query(kid, ctypes.byref(ms), ctypes.byref(n)), "sata_profile_query")
+    return ms.value, n.value
+
+
+def sata_profile_kernel_name(kernel: int):
+    r = load().sata_profile_kernel_name(int(kernel))
+    return r.decode() if r else None
 
 
 def status_string(status: int) -> str:

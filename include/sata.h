@@ -160,6 +160,18 @@ sata_status sata_expand_features(const sata_index *idx, const void *x, void *out
  * arguments sata_build_index would reject. */
 int64_t sata_describe_features(int d_k, int P, uint32_t *tuples, float *coef, int64_t cap);
 
+/* Kernel timing instrumentation.  While enabled, every launch of the
+ * library's kernels is bracketed by a HIP event pair recorded on the stream
+ * the kernel is launched on.  sata_profile_enable(1) clears earlier records;
+ * (0) stops recording and keeps them.  sata_profile_query waits for the
+ * recorded events of one kernel and returns the summed duration (ms) and the
+ * launch count.  Kernel ids: 0 prefill scan, 1 prefill combine, 2 decode
+ * stream, 3 decode finish (names from sata_profile_kernel_name, NULL for an
+ * unknown id).  Host-thread safe; not meant to be left on in production. */
+sata_status sata_profile_enable(int on);
+sata_status sata_profile_query(int kernel, double *total_ms, int64_t *launches);
+const char *sata_profile_kernel_name(int kernel);
+
 /* Static description of a status code. */
 const char *sata_status_string(sata_status s);
 

@@ -115,9 +115,27 @@ WORKLOADS = {
     "tiny_d8_p3": Workload("tiny_d8_p3", 1, 1, 256, 8, 8, 3, "f32", 64, SEED_BASE + 0),
     "prefill_d16_p4_f32": Workload("prefill_d16_p4_f32", 1, 8, 4096, 16, 16, 4, "f32", 64, SEED_BASE + 1),
     "prefill_d32_p4_bf16": Workload("prefill_d32_p4_bf16", 2, 16, 16384, 32, 32, 4, "bf16", 64, SEED_BASE + 2),
-    "decode_d64_p4_f32": Workload("decode_d64_p4_f32", 32, 8, 8192, 64, 64, 4, "f32", 64, SEED_BASE + 3,
+    "decode_d64_p4_f32": Workload("decode_d64_p4_f32", 32, 8, 8192, 64, 64, 4, "f32", 128, SEED_BASE + 3,
                                   decode_steps=1024),
     "prefill_d64_p4_bf16": Workload("prefill_d64_p4_bf16", 1, 8, 65536, 64, 64, 4, "bf16", 128, SEED_BASE + 4),
     "prefill_d16x64h_p4_bf16": Workload("prefill_d16x64h_p4_bf16", 1, 64, 131072, 16, 16, 4, "bf16", 128,
                                         SEED_BASE + 5),
 }
+
+
+def draw_qkv_device(lead: tuple, n: int, d_k: int, d_v: int, seed: int, dtype: str = "f32",
+                    device: str = "cuda"):
+    """Same recipe drawn on the GPU with a seeded torch generator (timing-only
+    inputs: long prefixes whose values no parity check reads).  Returns torch
+    tensors (q, k, v) in float32 or bfloat16."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = []
+    for name, dd in (("q", d_k), ("k", d_k), ("v", d_v)):
+        g = torch.randn(tuple(lead) + (n, dd), generator=gen, device=device, dtype=torch.float32)
+        if name != "v":
+            g = g / g.norm(dim=-1, keepdim=True).clamp_min(1e-30) * (float(d_k) ** 0.25)
+        out.append(g.to(tdt).contiguous())
+    return tuple(out)
