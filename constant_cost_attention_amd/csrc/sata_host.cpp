@@ -159,6 +159,56 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
     }
 }
 
+// Quads for the prefill: for every sorted prefix (orders 0..P-1, in feature
+// order) the aligned blocks of four last indices that reach a sorted tuple.
+// Each valid slot z carries the same readout weight 1/(alpha! d^(p/2)) as the
+// feature it stands for [hotdry, "Core insight of symmetric tensor
+// decomposition"]; the hierarchical i1 <= i2 <= i3 structure lets a quad share
+// one pair product over four features [hotdry, "Hardware optimisation paths
+// and current limits"].
+static void build_quads(int d, int P, std::vector<sata::QuadRec> &out) {
+    const double sqd = std::sqrt((double)d);
+    int32_t next = 0;   // state index of the next valid feature
+    auto emit = [&](int i1, int i2, int b, const std::vector<int> &prefix) {
+        sata::QuadRec q{};
+        uint32_t mask = 0;
+        int first = -1;
+        for (int z = 0; z < 4; ++z) {
+            const int i3 = 4 * b + z;
+            std::vector<int> t = prefix;
+            bool ok;
+            if (b * 4 >= d) {            // order-0 quad: slot 0 is the constant feature
+                ok = z == 0;
+            } else {
+                ok = t.empty() || i3 >= t.back();
+                t.push_back(i3);
+            }
+            if (ok) {
+                mask |= 1u << z;
+                if (first < 0) first = z;
+                q.coef[z] = (float)(1.0 / (alpha_factorial(t) * std::pow(sqd, (double)t.size())));
+            } else {
+                q.coef[z] = 0.f;
+            }
+        }
+        q.w0 = (uint32_t)i1 | ((uint32_t)i2 << 8) | ((uint32_t)b << 16) | (mask << 24);
+        q.cidx = mask ? next : -1;
+        next += __builtin_popcount(mask);
+        out.push_back(q);
+    };
+    const int none = d;
+    if (P >= 1) emit(none, none, d / 4, {});
+    if (P >= 2)
+        for (int b = 0; b < d / 4; ++b) emit(none, none, b, {});
+    if (P >= 3)
+        for (int i2 = 0; i2 < d; ++i2)
+            for (int b = i2 / 4; b < d / 4; ++b) emit(none, i2, b, {i2});
+    if (P >= 4)
+        for (int i1 = 0; i1 < d; ++i1)
+            for (int i2 = i1; i2 < d; ++i2)
+                for (int b = i2 / 4; b < d / 4; ++b) emit(i1, i2, b, {i1, i2});
+}
+
 static sata_status check_dims(int d_k, int d_v, int P) {
     if (d_k <= 0 || d_v <= 0) return fail(SATA_ERR_INVALID, "head dims must be positive (d_k=%d, d_v=%d)", d_k, d_v);
     if (P < 1) return fail(SATA_ERR_INVALID, "P must be >= 1 (got %d)", P);
@@ -180,6 +230,21 @@ int64_t sata_describe_features(int d_k, int P, uint32_t *tuples, float *coef, in
         if (coef) coef[f] = cf[(size_t)f];
     }
     return m;
+}
+
+int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *coef4, int64_t cap) {
+    g_last_error.clear();
+    if (check_dims(d_k, d_k, P) != SATA_OK) return -1;
+    std::vector<sata::QuadRec> quads;
+    build_quads(d_k, P, quads);
+    const int64_t nq = (int64_t)quads.size();
+    for (int64_t i = 0; i < nq && i < cap; ++i) {
+        if (w0) w0[i] = quads[(size_t)i].w0;
+        if (cidx) cidx[i] = quads[(size_t)i].cidx;
+        if (coef4)
+            for (int z = 0; z < 4; ++z) coef4[4 * i + z] = quads[(size_t)i].coef[z];
+    }
+    return nq;
 }
 
 sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
@@ -207,25 +272,54 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     const uint32_t pad = (0xffu << 24) | ((uint32_t)(d_k + 1) * 0x010101u);   // slots -> constant 0
     tup.resize((size_t)idx->m_tab, pad);
     coef.resize((size_t)idx->m_tab, 0.f);
+    std::vector<sata::QuadRec> quads;
+    build_quads(d_k, P, quads);
+    idx->nq = (int64_t)quads.size();
+    idx->nq_tab = round_up(idx->nq, sata::kQuadPad);
+    {
+        sata::QuadRec padq{};
+        padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8);   // pair product 0
+        padq.cidx = -1;
+        quads.resize((size_t)idx->nq_tab, padq);
+    }
+    std::vector<uint32_t> qw0(quads.size());
+    std::vector<int32_t> qcidx(quads.size());
+    std::vector<float> qcoef(quads.size() * 4);
+    for (size_t i = 0; i < quads.size(); ++i) {
+        qw0[i] = quads[i].w0;
+        qcidx[i] = quads[i].cidx;
+        for (int z = 0; z < 4; ++z) qcoef[i * 4 + z] = quads[i].coef[z];
+    }
     if (hipGetDevice(&idx->device) != hipSuccess) {
         delete idx;
         (void)hipGetLastError();
         return fail(SATA_ERR_HIP, "no HIP device available");
     }
+    auto release = [&]() {
+        if (idx->d_tup) (void)hipFree(idx->d_tup);
+        if (idx->d_coef) (void)hipFree(idx->d_coef);
+        if (idx->d_qw0) (void)hipFree(idx->d_qw0);
+        if (idx->d_qcidx) (void)hipFree(idx->d_qcidx);
+        if (idx->d_qcoef) (void)hipFree(idx->d_qcoef);
+        delete idx;
+    };
     hipError_t e = hipMalloc(&idx->d_tup, tup.size() * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMalloc(&idx->d_coef, coef.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&idx->d_qw0, qw0.size() * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMalloc(&idx->d_qcidx, qcidx.size() * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&idx->d_qcoef, qcoef.size() * sizeof(float));
     if (e != hipSuccess) {
         (void)hipGetLastError();
-        if (idx->d_tup) (void)hipFree(idx->d_tup);
-        delete idx;
+        release();
         return fail(SATA_ERR_OOM, "index allocation failed");
     }
     e = hipMemcpy(idx->d_tup, tup.data(), tup.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(idx->d_coef, coef.data(), coef.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(idx->d_qw0, qw0.data(), qw0.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(idx->d_qcidx, qcidx.data(), qcidx.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(idx->d_qcoef, qcoef.data(), qcoef.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
-        (void)hipFree(idx->d_tup);
-        (void)hipFree(idx->d_coef);
-        delete idx;
+        release();
         return fail_hip(e, "index upload");
     }
     *out = idx;
@@ -237,6 +331,9 @@ void sata_index_free(sata_index *idx) {
     DeviceGuard g(idx->device);
     if (idx->d_tup) (void)hipFree(idx->d_tup);
     if (idx->d_coef) (void)hipFree(idx->d_coef);
+    if (idx->d_qw0) (void)hipFree(idx->d_qw0);
+    if (idx->d_qcidx) (void)hipFree(idx->d_qcidx);
+    if (idx->d_qcoef) (void)hipFree(idx->d_qcoef);
     delete idx;
 }
 

@@ -25,7 +25,7 @@ SATA_F32, SATA_BF16 = 0, 1
 _EXPORTS = (
     "sata_build_index", "sata_index_free", "sata_index_features", "sata_index_info",
     "sata_state_alloc", "sata_state_reset", "sata_state_free", "sata_state_data",
-    "sata_prefill", "sata_decode_step", "sata_expand_features", "sata_describe_features",
+    "sata_prefill", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
 )
@@ -77,6 +77,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_describe_features.argtypes = [cint, cint, ctypes.POINTER(ctypes.c_uint32),
                                            ctypes.POINTER(ctypes.c_float), i64]
     lib.sata_describe_features.restype = i64
+    lib.sata_describe_quads.argtypes = [cint, cint, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_float), i64]
+    lib.sata_describe_quads.restype = i64
     lib.sata_status_string.argtypes = [cint]
     lib.sata_status_string.restype = ctypes.c_char_p
     lib.sata_last_error.argtypes = []
@@ -274,7 +277,7 @@ def sata_describe_features(d_k: int, P: int):
     lib = load()
     m = lib.sata_describe_features(int(d_k), int(P), None, None, 0)
     if m < 0:
-        raise SataError(SATA_ERR_INVALID, "sata_describe_features", lib.sata_last_error().decode())
+        raise SataError(SATA_ERR_INVALID, "sata_describe_features", "sata_describe_quads", lib.sata_last_error().decode())
     tup = np.zeros(m, dtype=np.uint32)
     coef = np.zeros(m, dtype=np.float32)
     lib.sata_describe_features(int(d_k), int(P), tup.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
@@ -300,6 +303,22 @@ def sata_profile_query(kernel) -> tuple:
 def sata_profile_kernel_name(kernel: int):
     r = load().sata_profile_kernel_name(int(kernel))
     return r.decode() if r else None
+
+
+def sata_describe_quads(d_k: int, P: int):
+    """Host-only: (w0 uint32 [nq], cidx int32 [nq], coef float32 [nq, 4]) of the prefill's quads."""
+    import numpy as np
+    lib = load()
+    nq = lib.sata_describe_quads(int(d_k), int(P), None, None, None, 0)
+    if nq < 0:
+        raise SataError(SATA_ERR_INVALID, "sata_describe_quads", lib.sata_last_error().decode())
+    w0 = np.zeros(nq, dtype=np.uint32)
+    cidx = np.zeros(nq, dtype=np.int32)
+    coef = np.zeros((nq, 4), dtype=np.float32)
+    lib.sata_describe_quads(int(d_k), int(P), w0.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                            cidx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            coef.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), nq)
+    return w0, cidx, coef
 
 
 def status_string(status: int) -> str:

@@ -105,3 +105,35 @@ def test_binding_rejects_cpu_tensors():
     from constant_cost_attention_amd import sata
     with pytest.raises(ValueError):
         sata._dev_ptr(torch.zeros(4), "q")
+
+
+@pytest.mark.parametrize("d,P", [(8, 1), (8, 2), (8, 3), (16, 4), (32, 4), (64, 4)])
+def test_quads_cover_the_features_in_order(d, P):
+    """Every valid quad slot is exactly the feature (i1, i2, 4b+z) with the same
+    readout weight as the feature table; valid slots are consecutive features;
+    padding slots carry weight 0."""
+    from constant_cost_attention_amd import sata
+    tup, coef = sata.sata_describe_features(d, P)
+    w0, cidx, qc = sata.sata_describe_quads(d, P)
+    slots = np.stack([(tup >> (8 * r)) & 0xFF for r in range(3)], axis=1).astype(np.int64)
+    order = (tup >> 24).astype(np.int64)
+    f = 0
+    for q in range(len(w0)):
+        i1, i2, b, mask = int(w0[q] & 0xFF), int((w0[q] >> 8) & 0xFF), int((w0[q] >> 16) & 0xFF), int(w0[q] >> 24)
+        if mask:
+            assert cidx[q] == f
+        for z in range(4):
+            if not (mask >> z) & 1:
+                assert qc[q, z] == 0
+                continue
+            # the feature this slot stands for, with absent indices dropped
+            idx = [i for i in (i1, i2) if i < d]
+            if b * 4 < d:
+                idx.append(4 * b + z)
+            want = sorted(idx)
+            assert idx == want
+            got = [int(x) for x in slots[f, :order[f]]]
+            assert got == want, (q, z, got, want)
+            assert qc[q, z] == coef[f]
+            f += 1
+    assert f == len(tup)
