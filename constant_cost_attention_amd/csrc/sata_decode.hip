@@ -14,7 +14,7 @@
 // row: fully coalesced 16-byte accesses.
 //
 // Grid: (ceil(m_pad / (256 * FPT)), B*H) workgroups of 256 lanes; lane owns FPT
-// consecutive features.  Each workgroup leaves d_V+1 partial sums; a second,
+// = 4 consecutive features, i.e. one 16-byte word of every state row.  Each workgroup leaves d_V+1 partial sums; a second,
 // tiny kernel adds the partials of a head in a fixed order and normalises, so
 // results are deterministic.
 //
@@ -26,7 +26,7 @@
 namespace sata {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecFPT = 8;     // features per lane
+constexpr int kDecFPT = 4;     // features per lane (one 16-byte access per state row)
 
 // Wave-level reduce-scatter of DV (power of two) per-lane values followed by a
 // plain reduction across the remaining lane groups: afterwards lane l holds the
@@ -56,16 +56,36 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// The lane's column loads are issued in two batches of ~(d_V+1)/2 rows, the
+// second batch before any store of the first, so each lane keeps up to d_V+1
+// 16-byte loads in flight; one wavefront per SIMD then saturates the HBM
+// read-modify-write stream (the state is far larger than every cache).
 template <int DV, typename TIn>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(
-    const uint32_t *__restrict__ tup, const float *__restrict__ coef, float *__restrict__ state,
-    int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
-    const TIn *__restrict__ v, float *__restrict__ partial) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, float *__restrict__ state,
+                   int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
+                   const TIn *__restrict__ v, float *__restrict__ partial) {
     constexpr int NC = DV + 1;
+    constexpr int R = (NC + 1) / 2;          // rows per load batch
     __shared__ float sq[72], sk[72], sv[NC];
     __shared__ float red[kDecThreads / 64][NC];
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
+    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * kDecFPT;
+    const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
+    float *Sb = state + (int64_t)bh * NC * m_pad + f0;
+
+    // first batch of state rows goes out before anything else
+    f32x4 s0[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (valid) s0[r] = __builtin_nontemporal_load(reinterpret_cast<f32x4 *>(Sb + (int64_t)r * m_pad));
+    uint4 t4 = {0u, 0u, 0u, 0u};
+    float4 c4 = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+        t4 = *reinterpret_cast<const uint4 *>(tup + f0);
+        c4 = *reinterpret_cast<const float4 *>(coef + f0);
+    }
     if (tid < dk) {
         sq[tid] = to_f32(q[(int64_t)bh * dk + tid]);
         sk[tid] = to_f32(k[(int64_t)bh * dk + tid]);
@@ -77,45 +97,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (tid < DV) sv[tid] = to_f32(v[(int64_t)bh * DV + tid]);
     __syncthreads();
 
-    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * kDecFPT;
-    const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
     float phk[kDecFPT], psq[kDecFPT];
+    {
+        const uint32_t tt[4] = {t4.x, t4.y, t4.z, t4.w};
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-    for (int j = 0; j < kDecFPT; ++j) { phk[j] = 0.f; psq[j] = 0.f; }
-    if (valid) {
-#pragma unroll
-        for (int j4 = 0; j4 < kDecFPT; j4 += 4) {
-            const uint4 t4 = *reinterpret_cast<const uint4 *>(tup + f0 + j4);
-            const float4 c4 = *reinterpret_cast<const float4 *>(coef + f0 + j4);
-            const uint32_t tt[4] = {t4.x, t4.y, t4.z, t4.w};
-            const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                phk[j4 + j] = monomial(tt[j], sk, 1);
-                psq[j4 + j] = cc[j] * monomial(tt[j], sq, 1);
-            }
+        for (int j = 0; j < kDecFPT; ++j) {
+            phk[j] = monomial(tt[j], sk, 1);
+            psq[j] = cc[j] * monomial(tt[j], sq, 1);
         }
     }
 
+    // second batch in flight while the first is updated, stored and read out
+    f32x4 s1[NC - R];
+#pragma unroll
+    for (int r = 0; r < NC - R; ++r)
+        if (valid) s1[r] = __builtin_nontemporal_load(reinterpret_cast<f32x4 *>(Sb + (int64_t)(R + r) * m_pad));
     float acc[NC];
-    float *Sb = state + (int64_t)bh * NC * m_pad + f0;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+        f32x4 x = c < R ? s0[c] : s1[c - R];
+        const float vc = sv[c];
         float a = 0.f;
-        if (valid) {
-            const float vc = sv[c];
 #pragma unroll
-            for (int j4 = 0; j4 < kDecFPT; j4 += 4) {
-                f32x4 *p = reinterpret_cast<f32x4 *>(Sb + (int64_t)c * m_pad + j4);
-                f32x4 s = __builtin_nontemporal_load(p);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s[j] += phk[j4 + j] * vc;
-                __builtin_nontemporal_store(s, p);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) a += psq[j4 + j] * s[j];
-            }
+        for (int j = 0; j < kDecFPT; ++j) {
+            x[j] += phk[j] * vc;
+            a += psq[j] * x[j];
         }
-        acc[c] = a;
+        if (valid) __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(Sb + (int64_t)c * m_pad));
+        acc[c] = valid ? a : 0.f;
     }
 
     // workgroup reduction of the d_V + 1 readout sums
@@ -129,10 +139,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (lane == 0) red[wave][DV] = den;
     __syncthreads();
     if (tid < NC) {
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kDecThreads / 64; ++w) s += red[w][tid];
-        partial[((int64_t)bh * gridDim.x + blockIdx.x) * NC + tid] = s;
+        for (int w = 0; w < kDecThreads / 64; ++w) sum += red[w][tid];
+        partial[((int64_t)bh * gridDim.x + blockIdx.x) * NC + tid] = sum;
     }
 }
 
