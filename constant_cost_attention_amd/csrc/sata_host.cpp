@@ -161,13 +161,13 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
 
 // Quads for the prefill: for every sorted prefix (orders 0..P-1, in feature
 // order) the aligned blocks of four last indices that reach a sorted tuple.
-// Each valid slot z carries the same readout weight 1/(alpha! d^(p/2)) as the
-// feature it stands for [hotdry, "Core insight of symmetric tensor
-// decomposition"]; the hierarchical i1 <= i2 <= i3 structure lets a quad share
-// one pair product over four features [hotdry, "Hardware optimisation paths
-// and current limits"].
+// Each valid slot z carries the multinomial part 1/alpha! of its feature's
+// readout weight 1/(alpha! d^(p/2)) [hotdry, "Core insight of symmetric tensor
+// decomposition"]; the prefill applies d^(-p/2) by scaling q by 1/sqrt(d_K).
+// The hierarchical i1 <= i2 <= i3 structure lets a quad share one pair
+// product over four features [hotdry, "Hardware optimisation paths and
+// current limits"].
 static void build_quads(int d, int P, std::vector<sata::QuadRec> &out) {
-    const double sqd = std::sqrt((double)d);
     int32_t next = 0;   // state index of the next valid feature
     auto emit = [&](int i1, int i2, int b, const std::vector<int> &prefix) {
         sata::QuadRec q{};
@@ -186,7 +186,7 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out) {
             if (ok) {
                 mask |= 1u << z;
                 if (first < 0) first = z;
-                q.coef[z] = (float)(1.0 / (alpha_factorial(t) * std::pow(sqd, (double)t.size())));
+                q.coef[z] = (float)(1.0 / alpha_factorial(t));
             } else {
                 q.coef[z] = 0.f;
             }

@@ -49,13 +49,13 @@ constexpr int64_t kWorkCap = (int64_t)4 << 30;   // partial-sum workspace cap (b
 template <int D, int DV, int C, int MT, typename TIn>
 struct ScanCfg {
     static constexpr bool BF = sizeof(TIn) == 2;
-    static constexpr int NQW = 4 * MT;           // quads per wavefront
+    static constexpr int NQW = 4 * MT;           // quads per wavefront (four streams of MT)
     static constexpr int NQ = kNW * NQW;         // quads per workgroup (slice)
     static constexpr int NC = DV + 1;            // value columns + normaliser
     static constexpr int NT = (NC + 15) / 16;    // 16-column MFMA tiles
     static constexpr int NCP = NT * 16;
     static constexpr int TT = C / 16;            // 16-token tiles per chunk
-    static constexpr int TH = C < 64 ? C : 64;   // tokens per readout pass (register budget)
+    static constexpr int TH = (BF ? 64 : 32) < C ? (BF ? 64 : 32) : C;   // tokens per readout pass
     static constexpr int TTH = TH / 16;          // token tiles per pass
     static constexpr int NH = C / TH;            // passes per chunk
     static constexpr int KR = D + 4;             // K rows: d_K dims, then 1, 0, 0, 0
@@ -65,15 +65,17 @@ struct ScanCfg {
     static constexpr int ES = BF ? 2 : 4;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = OFF_K + KR * KS * 4;
-    static constexpr int OFF_V = OFF_Q + C * QS * 4;
-    static constexpr int OFF_Y = OFF_V + NCP * VS * ES;
-    static constexpr int OFF_W = OFF_Y + TT * NT * 64 * 16;      // one reduction buffer per pass
+    static constexpr int OFF_V = OFF_Q + TH * QS * 4;
+    static constexpr int OFF_Y = (OFF_V + NC * VS * ES + 15) / 16 * 16;
+    static constexpr int YB = TTH * NT * 64;     // f32x4 per wavefront readout buffer
+    static constexpr int OFF_W = OFF_Y + kNW * YB * 16;
     static constexpr int OFF_QC = OFF_W + NQ * 4;
     static constexpr int LDS = OFF_QC + NQ * 16;
     static_assert(MT % 2 == 0, "tiles per wave must be even");
     static_assert(C % 32 == 0, "chunk must be a multiple of 32");
     static_assert(D % 8 == 0, "d_K must be a multiple of 8");
-    static_assert(OFF_V % 16 == 0 && OFF_Y % 16 == 0 && OFF_QC % 16 == 0, "alignment");
+    static_assert(TTH <= kNW, "one token tile per wavefront in the reduce-scatter");
+    static_assert(OFF_V % 16 == 0 && OFF_QC % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -96,58 +98,38 @@ struct TaylorArgs {
     int P;
 };
 
-// Direct intra-chunk term for query tile qt of the chunk, key blocks handled by
-// this wavefront (every kNW-th K step), added into Z (rows = queries 4g + r,
-// column li of each 16-column tile).  Keys after a query get weight 0.
-template <class Cfg>
-__device__ __forceinline__ void intra_tile(f32x4 (&Z)[Cfg::NT], int qt, int wave, int g, int li,
-                                           const float *Kt, const float *Qs, const unsigned char *lds,
+// Direct intra-chunk term for query tile qt of chunk (t0, nvalid): Z (rows =
+// queries 4g + r, column li of each 16-column tile) receives
+// sum_{key <= query} w(q.k/sqrt d) [v, 1][key].  S^T = K Q^T is formed on MFMA
+// with q and k read straight from global memory; its accumulator rows are the
+// K-slots of the W [V|1] product, so W never leaves the registers.  [V | 1]
+// comes from LDS (operand dtype, dim-major, row stride VS).
+template <int D, int NT, int VS, typename TIn>
+__device__ __forceinline__ void intra_tile(f32x4 (&Z)[NT], int qt, int g, int li, const TIn *qh, const TIn *kh,
+                                           int64_t t0, int nvalid, const unsigned char *vt,
                                            const TaylorArgs &ta) {
-    constexpr int D = Cfg::D_, KS = Cfg::KS, QS = Cfg::QS, VS = Cfg::VS, NT = Cfg::NT;
     const int query = 16 * qt + li;
-    if constexpr (Cfg::BF) {
-        // Q^T operand for this query tile: lane (query li, dims 8g..8g+7 of each 32-dim step)
-        bf16x8 Bq[D / 32 > 0 ? D / 32 : 1];
-        const float *qrow = Qs + query * QS;
+    if constexpr (sizeof(TIn) == 2) {
+        constexpr int DS = D < 32 ? 1 : D / 32;            // 32-dim K steps (zero-padded below 32)
+        const bf16_t *Vt = reinterpret_cast<const bf16_t *>(vt);
+        auto load8 = [&](const TIn *base, int tok, int d0) -> bf16x8 {
+            uint4 u = {0u, 0u, 0u, 0u};
+            if (tok < nvalid && d0 < D) u = *reinterpret_cast<const uint4 *>(base + (t0 + tok) * D + d0);
+            return __builtin_bit_cast(bf16x8, u);
+        };
+        bf16x8 Bq[DS];
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            float t[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) t[j] = qrow[32 * s + 8 * g + j];
-            Bq[s] = pack_bf16x8(t);
-        }
-        const bf16_t *Vt = reinterpret_cast<const bf16_t *>(lds + Cfg::OFF_V);
-        const int nks = qt / 2 + 1;                              // 32-key steps up to the diagonal
-        for (int ks = wave; ks < nks; ks += kNW) {
+        for (int s = 0; s < DS; ++s) Bq[s] = load8(qh, query, 32 * s + 8 * g);
+        const int nks = qt / 2 + 1;                          // 32-key steps up to the diagonal
+        for (int ks = 0; ks < nks; ++ks) {
             f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
-            const int kA = 32 * ks + li, kB = kA + 16;           // this lane's key rows (A operand)
+            const int kA = 32 * ks + li, kB = kA + 16;        // this lane's key rows (A operand)
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-                float ta8[8], tb8[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    ta8[j] = Kt[(32 * s + 8 * g + j) * KS + kA];
-                    tb8[j] = Kt[(32 * s + 8 * g + j) * KS + kB];
-                }
-                sA = mfma_bf16(pack_bf16x8(ta8), Bq[s], sA);
-                sB = mfma_bf16(pack_bf16x8(tb8), Bq[s], sB);
+            for (int s = 0; s < DS; ++s) {
+                sA = mfma_bf16(load8(kh, kA, 32 * s + 8 * g), Bq[s], sA);
+                sB = mfma_bf16(load8(kh, kB, 32 * s + 8 * g), Bq[s], sB);
             }
-            if constexpr (D % 32) {
-                // d_K = 8 or 16: one 32-wide K step with zero padding
-                float ta8[8], tb8[8], tq[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int dd = 8 * g + j;
-                    const bool in = dd < D;
-                    ta8[j] = in ? Kt[dd * KS + kA] : 0.f;
-                    tb8[j] = in ? Kt[dd * KS + kB] : 0.f;
-                    tq[j] = in ? qrow[dd] : 0.f;
-                }
-                const bf16x8 bq = pack_bf16x8(tq);
-                sA = mfma_bf16(pack_bf16x8(ta8), bq, sA);
-                sB = mfma_bf16(pack_bf16x8(tb8), bq, sB);
-            }
-            // S^T rows are keys 4g + r (+16), column is query li -> weights W[query][key]
+            // S^T rows are keys 32ks + 4g + r (and +16), column is the query -> W[query][key]
             float w8[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -156,26 +138,29 @@ __device__ __forceinline__ void intra_tile(f32x4 (&Z)[Cfg::NT], int qt, int wave
                 w8[4 + r] = keyB <= query ? taylor_w(sB[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.P) : 0.f;
             }
             const bf16x8 A = pack_bf16x8(w8);
-            // [V | 1] operand with the same key order: keys 32ks + 4g + 0..3 and +16
+            // [V | 1] operand in the same key order: keys 32ks + 4g + 0..3 and +16
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const bf16_t *vr = Vt + (16 * nt + li) * VS + 32 * ks + 4 * g;
                 const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
                 const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
-                uint4 u = {lo.x, lo.y, hi.x, hi.y};
+                const uint4 u = {lo.x, lo.y, hi.x, hi.y};
                 Z[nt] = mfma_bf16(A, __builtin_bit_cast(bf16x8, u), Z[nt]);
             }
         }
     } else {
-        const float *Vt = reinterpret_cast<const float *>(lds + Cfg::OFF_V);
-        const int nkt = qt + 1;                                  // 16-key tiles up to the diagonal
-        for (int kt = wave; kt < nkt; kt += kNW) {
+        const float *Vt = reinterpret_cast<const float *>(vt);
+        const bool qok = query < nvalid;
+        for (int kt = 0; kt <= qt; ++kt) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
             const int key = 16 * kt + li;
+            const bool kok = key < nvalid;
 #pragma unroll
             for (int d4 = 0; d4 < D / 4; ++d4) {
                 const int dd = 4 * d4 + g;
-                s = mfma_f32(Kt[dd * KS + key], Qs[query * QS + dd], s);
+                const float a = kok ? to_f32(kh[(t0 + key) * D + dd]) : 0.f;
+                const float b = qok ? to_f32(qh[(t0 + query) * D + dd]) : 0.f;
+                s = mfma_f32(a, b, s);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -188,24 +173,57 @@ __device__ __forceinline__ void intra_tile(f32x4 (&Z)[Cfg::NT], int qt, int wave
     }
 }
 
-template <int D, int DV, int C, int MT, typename TIn>
-struct ScanCfgD : ScanCfg<D, DV, C, MT, TIn> {
-    static constexpr int D_ = D;
-};
+// Stage [V | 1] of a chunk into LDS, dim-major (row c, token t), operand dtype;
+// invalid tokens get zeros (also in the ones column), so they add nothing.
+// Writes rows 0..ROWS-1 (row DV is the ones column, rows above it zero).
+template <int DV, int C, int ROWS, int VS, typename TIn>
+__device__ __forceinline__ void stage_v(unsigned char *vt, const TIn *vh, int64_t t0, int nvalid, int tid,
+                                        int nthreads) {
+    for (int i = tid; i < C * ((ROWS + 7) / 8); i += nthreads) {
+        const int t = i % C, c8 = (i / C) * 8;     // consecutive lanes: consecutive tokens
+        float val[8];
+        if (t < nvalid && c8 < DV) {
+            const int64_t src = (t0 + t) * DV + c8;
+            if constexpr (sizeof(TIn) == 2) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(vh + src);
+                const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    val[2 * j] = __uint_as_float(uw[j] << 16);
+                    val[2 * j + 1] = __uint_as_float(uw[j] & 0xffff0000u);
+                }
+            } else {
+                const float4 a = *reinterpret_cast<const float4 *>(vh + src);
+                const float4 b = *reinterpret_cast<const float4 *>(vh + src + 4);
+                val[0] = a.x; val[1] = a.y; val[2] = a.z; val[3] = a.w;
+                val[4] = b.x; val[5] = b.y; val[6] = b.z; val[7] = b.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) val[j] = (t < nvalid && c8 + j == DV) ? 1.f : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (c8 + j >= ROWS) break;
+            if constexpr (sizeof(TIn) == 2) reinterpret_cast<bf16_t *>(vt)[(c8 + j) * VS + t] = from_f32<bf16_t>(val[j]);
+            else reinterpret_cast<float *>(vt)[(c8 + j) * VS + t] = val[j];
+        }
+    }
+}
 
 template <int D, int DV, int C, int MT, typename TIn>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
                          const float4 *__restrict__ qcoef, float *__restrict__ state, int64_t m_pad,
                          const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-                         int64_t n, int64_t tok0, int nchunk, float *__restrict__ partial, TaylorArgs ta) {
-    using Cfg = ScanCfgD<D, DV, C, MT, TIn>;
-    constexpr int NC = Cfg::NC, NT = Cfg::NT, NCP = Cfg::NCP, TT = Cfg::TT, KR = Cfg::KR;
-    constexpr int KS = Cfg::KS, QS = Cfg::QS, VS = Cfg::VS, NQ = Cfg::NQ, NQW = Cfg::NQW;
+                         int64_t n, int64_t tok0, int nchunk, float *__restrict__ partial, float qscale) {
+    using Cfg = ScanCfg<D, DV, C, MT, TIn>;
+    constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TH = Cfg::TH, TTH = Cfg::TTH;
+    constexpr int KS = Cfg::KS, QS = Cfg::QS, VS = Cfg::VS, NQ = Cfg::NQ, NQW = Cfg::NQW, YB = Cfg::YB;
     extern __shared__ __align__(16) unsigned char lds[];
-    float *Kt = reinterpret_cast<float *>(lds + Cfg::OFF_K);      // [KR][KS]  dim-major
-    float *Qs = reinterpret_cast<float *>(lds + Cfg::OFF_Q);      // [C][QS]   token-major
-    f32x4 *Yr = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_Y);      // [TT][NT][64] accumulator layout
+    float *Kt = reinterpret_cast<float *>(lds + Cfg::OFF_K);      // [KR][KS]  dim-major, whole chunk
+    float *Qs = reinterpret_cast<float *>(lds + Cfg::OFF_Q);      // [TH][QS]  one readout pass, dims scaled
+    f32x4 *Yb = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_Y);      // [kNW][TTH][NT][64] accumulator layout
     uint32_t *W0 = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_W);   // [NQ]
     float4 *QC = reinterpret_cast<float4 *>(lds + Cfg::OFF_QC);      // [NQ]
 
@@ -215,19 +233,19 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     const int g = lane >> 4, li = lane & 15;
     const int64_t qs0 = (int64_t)slice * NQ;          // first quad of the slice
     const int wq0 = wave * NQW;                       // first quad of this wave within the slice
+    // Four streams of MT consecutive quads per wave: tile j holds quad wq0 + s*MT + j in rows 4s..4s+3.
+    // This lane's accumulator rows (4g + r) are stream g; its update rows (li) are stream li/4, slot li%4.
 
     for (int i = tid; i < NQ; i += kThreads) {
         W0[i] = qw0[qs0 + i];
         QC[i] = qcoef[qs0 + i];
     }
 
-    // state slice -> accumulators.  Tile j of this wave = quads wq0 + 4j + s (rows 4s + r);
-    // this lane owns rows 4g + r, i.e. quad wq0 + 4j + g, slot r, column 16 nt + li.
     float *Sh = state + bh * NC * m_pad;
     f32x4 S[MT][NT];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-        const int64_t qd = qs0 + wq0 + 4 * j + g;
+        const int64_t qd = qs0 + wq0 + g * MT + j;
         const uint32_t w = qw0[qd];
         const int32_t c0 = qcidx[qd];
         const uint32_t mask = qd_mask(w);
@@ -243,101 +261,102 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     }
     __syncthreads();
 
-    // update-side quad of this lane's A-operand row li in tile j: quad wq0 + 4j + li/4, slot li%4
-    uint32_t myW[MT];
+    uint32_t myW[MT];                                  // update rows: stream li/4
 #pragma unroll
-    for (int j = 0; j < MT; ++j) myW[j] = W0[wq0 + 4 * j + (li >> 2)];
-    // tile j reuses tile j-1's pair products when every row keeps its pair (wave-uniform)
-    uint32_t same_prev = 0;
+    for (int j = 0; j < MT; ++j) myW[j] = W0[wq0 + (li >> 2) * MT + j];
+    uint32_t shared_pair = 0;                          // readout K step kk: quads 2kk, 2kk+1 of stream g
 #pragma unroll
-    for (int j = 1; j < MT; ++j)
-        if (__all(qd_pair(myW[j]) == qd_pair(myW[j - 1]))) same_prev |= 1u << j;
+    for (int kk = 0; kk < MT / 2; ++kk) {
+        const int qa = wq0 + g * MT + 2 * kk;
+        if (__all(qd_pair(W0[qa]) == qd_pair(W0[qa + 1]))) shared_pair |= 1u << kk;
+    }
 
     const TIn *qh = q + bh * n * D;
     const TIn *kh = k + bh * n * D;
     const TIn *vh = v + bh * n * DV;
-    const int ntiles_owned = (TT + nslices - 1 - slice) / nslices;   // query tiles qt = slice + i*nslices
 
-    for (int cc = 0; cc < nchunk; ++cc) {
-        const int64_t t0 = tok0 + (int64_t)cc * C;
-        const int nvalid = n - t0 < C ? (int)(n - t0) : C;
-        __syncthreads();
-        // ---- stage the chunk (invalid tokens: zeros, so they add nothing)
-        for (int i = tid; i < C * (D / 8); i += kThreads) {
-            const int t = i % C, d8 = (i / C) * 8;     // consecutive lanes: consecutive tokens
-            float kv[8], qv[8];
-            if (t < nvalid) {
-                const int64_t src = (t0 + t) * D + d8;
+    auto stage_q = [&](int64_t tq0, int nq_valid) {
+        for (int i = tid; i < TH * (D / 8); i += kThreads) {
+            const int t = i % TH, d8 = (i / TH) * 8;
+            float qv[8];
+            if (t < nq_valid) {
+                const int64_t src = (tq0 + t) * D + d8;
                 if constexpr (Cfg::BF) {
-                    const uint4 ku = *reinterpret_cast<const uint4 *>(kh + src);
                     const uint4 qu = *reinterpret_cast<const uint4 *>(qh + src);
-                    const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w}, qw[4] = {qu.x, qu.y, qu.z, qu.w};
+                    const uint32_t qw[4] = {qu.x, qu.y, qu.z, qu.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        kv[2 * j] = __uint_as_float(kw[j] << 16); kv[2 * j + 1] = __uint_as_float(kw[j] & 0xffff0000u);
-                        qv[2 * j] = __uint_as_float(qw[j] << 16); qv[2 * j + 1] = __uint_as_float(qw[j] & 0xffff0000u);
+                        qv[2 * j] = __uint_as_float(qw[j] << 16);
+                        qv[2 * j + 1] = __uint_as_float(qw[j] & 0xffff0000u);
                     }
                 } else {
-                    const float4 k0 = *reinterpret_cast<const float4 *>(kh + src);
-                    const float4 k1 = *reinterpret_cast<const float4 *>(kh + src + 4);
                     const float4 q0 = *reinterpret_cast<const float4 *>(qh + src);
                     const float4 q1 = *reinterpret_cast<const float4 *>(qh + src + 4);
-                    kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
-                    kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
                     qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w;
                     qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) { kv[j] = 0.f; qv[j] = 0.f; }
+                for (int j = 0; j < 8; ++j) qv[j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qv[j] *= qscale;
+            *reinterpret_cast<float4 *>(Qs + t * QS + d8) = float4{qv[0], qv[1], qv[2], qv[3]};
+            *reinterpret_cast<float4 *>(Qs + t * QS + d8 + 4) = float4{qv[4], qv[5], qv[6], qv[7]};
+        }
+        for (int t = tid; t < TH; t += kThreads)
+            *reinterpret_cast<float4 *>(Qs + t * QS + D) = float4{1.f, 0.f, 0.f, 0.f};
+    };
+
+    for (int cc = 0; cc < nchunk; ++cc) {
+        const int64_t t0 = tok0 + (int64_t)cc * C;
+        const int nvalid = n - t0 < C ? (int)(n - t0) : C;
+        __syncthreads();          // previous chunk: update done with Kt/Vt, reduce-scatter done with Yb
+        // ---- stage K (dim-major fp32), [V | 1] (operand dtype) for the chunk, Q for pass 0
+        for (int i = tid; i < C * (D / 8); i += kThreads) {
+            const int t = i % C, d8 = (i / C) * 8;     // consecutive lanes: consecutive tokens
+            float kv[8];
+            if (t < nvalid) {
+                const int64_t src = (t0 + t) * D + d8;
+                if constexpr (Cfg::BF) {
+                    const uint4 ku = *reinterpret_cast<const uint4 *>(kh + src);
+                    const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        kv[2 * j] = __uint_as_float(kw[j] << 16);
+                        kv[2 * j + 1] = __uint_as_float(kw[j] & 0xffff0000u);
+                    }
+                } else {
+                    const float4 k0 = *reinterpret_cast<const float4 *>(kh + src);
+                    const float4 k1 = *reinterpret_cast<const float4 *>(kh + src + 4);
+                    kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
+                    kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) kv[j] = 0.f;
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) Kt[(d8 + j) * KS + t] = kv[j];
-            *reinterpret_cast<float4 *>(Qs + t * QS + d8) = float4{qv[0], qv[1], qv[2], qv[3]};
-            *reinterpret_cast<float4 *>(Qs + t * QS + d8 + 4) = float4{qv[4], qv[5], qv[6], qv[7]};
         }
         for (int t = tid; t < C; t += kThreads) {
             Kt[D * KS + t] = 1.f;
             Kt[(D + 1) * KS + t] = 0.f; Kt[(D + 2) * KS + t] = 0.f; Kt[(D + 3) * KS + t] = 0.f;
-            *reinterpret_cast<float4 *>(Qs + t * QS + D) = float4{1.f, 0.f, 0.f, 0.f};
         }
-        for (int i = tid; i < C * (NCP / 8); i += kThreads) {
-            const int t = i % C, c8 = (i / C) * 8;     // consecutive lanes: consecutive tokens
-            float val[8];
-            if (t < nvalid && c8 < DV) {
-                const int64_t src = (t0 + t) * DV + c8;
-                if constexpr (Cfg::BF) {
-                    const uint4 u = *reinterpret_cast<const uint4 *>(vh + src);
-                    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        val[2 * j] = __uint_as_float(uw[j] << 16);
-                        val[2 * j + 1] = __uint_as_float(uw[j] & 0xffff0000u);
-                    }
-                } else {
-                    const float4 a = *reinterpret_cast<const float4 *>(vh + src);
-                    const float4 b = *reinterpret_cast<const float4 *>(vh + src + 4);
-                    val[0] = a.x; val[1] = a.y; val[2] = a.z; val[3] = a.w;
-                    val[4] = b.x; val[5] = b.y; val[6] = b.z; val[7] = b.w;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) val[j] = (t < nvalid && c8 + j == DV) ? 1.f : 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if constexpr (Cfg::BF) reinterpret_cast<bf16_t *>(lds + Cfg::OFF_V)[(c8 + j) * VS + t] = from_f32<bf16_t>(val[j]);
-                else reinterpret_cast<float *>(lds + Cfg::OFF_V)[(c8 + j) * VS + t] = val[j];
-            }
-        }
+        stage_v<DV, C, NC, VS, TIn>(lds + Cfg::OFF_V, vh, t0, nvalid, tid, kThreads);
+        stage_q(t0, nvalid);
         __syncthreads();
 
-        // ---- inter-chunk readout, Y = psi(Q_c)[:, slice] . S^(c-1)[slice, :], plus the direct
-        //      intra-chunk term of the query tiles this slice owns, in passes of TH tokens;
-        //      each pass's four wavefront partials are added in a fixed order in LDS
+        // ---- inter-chunk readout, Y = psi(Q_c)[:, slice] . S^(c-1)[slice, :], in passes of TH
+        //      tokens; each wave's partial goes to its own LDS buffer, then wave w adds the four
+        //      buffers' token tile w and writes it out (one barrier, no serial chain)
 #pragma unroll
         for (int hf = 0; hf < Cfg::NH; ++hf) {
-            constexpr int TTH = Cfg::TTH;
+            if (hf > 0) {
+                const int64_t tq0 = t0 + hf * TH;
+                stage_q(tq0, n - tq0 < TH ? (int)(n - tq0) : TH);
+                __syncthreads();
+            }
             f32x4 Y[TTH][NT];
 #pragma unroll
             for (int tt = 0; tt < TTH; ++tt)
@@ -345,7 +364,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
             if constexpr (Cfg::BF) {
-                // K step kk: tiles 2kk, 2kk+1; lane group g holds quads wq0+8kk+g and wq0+8kk+4+g
+                // psi = coef_z * (q_i1 q_i2) * q_(4b+z); q carries 1/sqrt(d), coef_z = 1/alpha!
 #pragma unroll
                 for (int kk = 0; kk < MT / 2; ++kk) {
                     bf16x8 B[NT];
@@ -356,17 +375,30 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                         for (int r = 0; r < 4; ++r) { b[r] = S[2 * kk][nt][r]; b[4 + r] = S[2 * kk + 1][nt][r]; }
                         B[nt] = pack_bf16x8(b);
                     }
-                    const int qa = wq0 + 8 * kk + g, qb = qa + 4;
+                    const int qa = wq0 + g * MT + 2 * kk, qb = qa + 1;
                     const uint32_t wa = W0[qa], wb = W0[qb];
                     const float4 ca = QC[qa], cb = QC[qb];
-                    const bool shared_pair = __all(qd_pair(wa) == qd_pair(wb));
+                    const bool sp = (shared_pair >> kk) & 1u;
+                    const int a1 = qd_i1(wa), a2 = qd_i2(wa), ab = 4 * qd_b(wa);
+                    const int b1 = qd_i1(wb), b2 = qd_i2(wb), bb = 4 * qd_b(wb);
+                    const float *row = Qs + li * QS;
+                    float pa1 = row[a1], pa2 = row[a2], pb1 = 0.f, pb2 = 0.f;
+                    if (!sp) { pb1 = row[b1]; pb2 = row[b2]; }
+                    float4 xa = *reinterpret_cast<const float4 *>(row + ab);
+                    float4 xb = *reinterpret_cast<const float4 *>(row + bb);
 #pragma unroll
                     for (int tt = 0; tt < TTH; ++tt) {
-                        const float *row = Qs + (16 * (hf * TTH + tt) + li) * QS;
-                        const float pa = row[qd_i1(wa)] * row[qd_i2(wa)];
-                        const float pb = shared_pair ? pa : row[qd_i1(wb)] * row[qd_i2(wb)];
-                        const float4 xa = *reinterpret_cast<const float4 *>(row + 4 * qd_b(wa));
-                        const float4 xb = *reinterpret_cast<const float4 *>(row + 4 * qd_b(wb));
+                        float npa1 = 0.f, npa2 = 0.f, npb1 = 0.f, npb2 = 0.f;
+                        float4 nxa = {0.f, 0.f, 0.f, 0.f}, nxb = {0.f, 0.f, 0.f, 0.f};
+                        if (tt + 1 < TTH) {          // next tile's loads go out before this tile's math
+                            const float *nrow = Qs + (16 * (tt + 1) + li) * QS;
+                            npa1 = nrow[a1]; npa2 = nrow[a2];
+                            if (!sp) { npb1 = nrow[b1]; npb2 = nrow[b2]; }
+                            nxa = *reinterpret_cast<const float4 *>(nrow + ab);
+                            nxb = *reinterpret_cast<const float4 *>(nrow + bb);
+                        }
+                        const float pa = pa1 * pa2;
+                        const float pb = sp ? pa : pb1 * pb2;
                         float a[8] = {ca.x * xa.x, ca.y * xa.y, ca.z * xa.z, ca.w * xa.w,
                                       cb.x * xb.x, cb.y * xb.y, cb.z * xb.z, cb.w * xb.w};
 #pragma unroll
@@ -374,13 +406,14 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                         const bf16x8 A = pack_bf16x8(a);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A, B[nt], Y[tt][nt]);
+                        pa1 = npa1; pa2 = npa2; pb1 = npb1; pb2 = npb2; xa = nxa; xb = nxb;
                     }
                 }
             } else {
-                // K step (j, r): lane group g holds slot r of quad wq0 + 4j + g
+                // K step (j, r): lane group g holds slot r of quad wq0 + g*MT + j
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
-                    const int qd = wq0 + 4 * j + g;
+                    const int qd = wq0 + g * MT + j;
                     const uint32_t w = W0[qd];
                     const float4 cq = QC[qd];
                     const float cr[4] = {cq.x, cq.y, cq.z, cq.w};
@@ -388,7 +421,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     for (int r = 0; r < 4; ++r) {
 #pragma unroll
                         for (int tt = 0; tt < TTH; ++tt) {
-                            const float *row = Qs + (16 * (hf * TTH + tt) + li) * QS;
+                            const float *row = Qs + (16 * tt + li) * QS;
                             const float a = cr[r] * row[qd_i1(w)] * row[qd_i2(w)] * row[4 * qd_b(w) + r];
 #pragma unroll
                             for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_f32(a, S[j][nt][r], Y[tt][nt]);
@@ -397,49 +430,28 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 }
             }
 
-            for (int oi = 0; oi < ntiles_owned; ++oi) {
-                const int qt = slice + oi * nslices;
-                if (qt / TTH != hf) continue;
-                f32x4 Z[NT];
+            f32x4 *mine = Yb + wave * YB;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                intra_tile<Cfg>(Z, qt, wave, g, li, Kt, Qs, lds, ta);
+            for (int tt = 0; tt < TTH; ++tt)
 #pragma unroll
-                for (int tt = 0; tt < TTH; ++tt)
-                    if (hf * TTH + tt == qt) {
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) Y[tt][nt] += Z[nt];
-                    }
-            }
-
-            f32x4 *Yh = Yr + hf * TTH * NT * 64;
-#pragma unroll
-            for (int wv = 0; wv < kNW - 1; ++wv) {
-                if (wave == wv) {
-#pragma unroll
-                    for (int tt = 0; tt < TTH; ++tt)
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            f32x4 *p = Yh + (tt * NT + nt) * 64 + lane;
-                            *p = wv == 0 ? Y[tt][nt] : *p + Y[tt][nt];
-                        }
-                }
-                __syncthreads();
-            }
-            if (wave == kNW - 1) {
+                for (int nt = 0; nt < NT; ++nt) mine[(tt * NT + nt) * 64 + lane] = Y[tt][nt];
+            __syncthreads();
+            if (wave < TTH) {
                 // partial layout per (bh, chunk, slice): [tt][c][16 tokens]; lane writes rows 4g..4g+3
                 float *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16);
+                const int tt = wave;
 #pragma unroll
-                for (int tt = 0; tt < TTH; ++tt)
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int c = 16 * nt + li;
+                    if (c < NC) {
+                        f32x4 y = Yb[(tt * NT + nt) * 64 + lane];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const int c = 16 * nt + li;
-                        if (c < NC) {
-                            const f32x4 y = Yh[(tt * NT + nt) * 64 + lane] + Y[tt][nt];
-                            *reinterpret_cast<f32x4 *>(pdst + ((int64_t)(hf * TTH + tt) * NC + c) * 16 + 4 * g) = y;
-                        }
+                        for (int w = 1; w < kNW; ++w) y += Yb[w * YB + (tt * NT + nt) * 64 + lane];
+                        *reinterpret_cast<f32x4 *>(pdst + ((int64_t)(hf * TTH + tt) * NC + c) * 16 + 4 * g) = y;
                     }
+                }
             }
+            if (hf + 1 < Cfg::NH) __syncthreads();   // Yb and Qs are rewritten by the next pass
         }
 
         // ---- chunk state: S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1]
@@ -450,13 +462,16 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 const int tb = 32 * ks + 8 * g;
                 bf16x8 B[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    B[nt] = *reinterpret_cast<const bf16x8 *>(Vt + (16 * nt + li) * VS + tb);
+                for (int nt = 0; nt < NT; ++nt) {
+                    uint4 u = {0u, 0u, 0u, 0u};
+                    if (16 * nt + li < NC) u = *reinterpret_cast<const uint4 *>(Vt + (16 * nt + li) * VS + tb);
+                    B[nt] = __builtin_bit_cast(bf16x8, u);
+                }
                 float p2[8];
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
                     const uint32_t w = myW[j];
-                    if (j == 0 || !((same_prev >> j) & 1u)) {
+                    if (j == 0 || qd_pair(w) != qd_pair(myW[j > 0 ? j - 1 : 0])) {   // per lane: new pair
                         const float4 *k1 = reinterpret_cast<const float4 *>(Kt + qd_i1(w) * KS + tb);
                         const float4 *k2 = reinterpret_cast<const float4 *>(Kt + qd_i2(w) * KS + tb);
                         const float4 a0 = k1[0], a1 = k1[1], b0 = k2[0], b1 = k2[1];
@@ -479,7 +494,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 const int tb = 4 * ks + g;
                 float B[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) B[nt] = Vt[(16 * nt + li) * VS + tb];
+                for (int nt = 0; nt < NT; ++nt) B[nt] = 16 * nt + li < NC ? Vt[(16 * nt + li) * VS + tb] : 0.f;
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
                     const uint32_t w = myW[j];
@@ -490,13 +505,12 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 }
             }
         }
-
     }
 
     // accumulators -> state slice
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-        const int64_t qd = qs0 + wq0 + 4 * j + g;
+        const int64_t qd = qs0 + wq0 + g * MT + j;
         const uint32_t w = qw0[qd];
         const int32_t c0 = qcidx[qd];
         const uint32_t mask = qd_mask(w);
@@ -511,19 +525,36 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     }
 }
 
-// Kernel 2: y = sum over slices of the partials (fixed order), o = y[:d_V] / y[d_V].
-// Partial layout per (bh, chunk, slice): [C/16][d_V+1][16 tokens] fp32.
-template <int DV, int C, typename TOut>
+// Kernel 2: y = (direct intra-chunk term) + sum over slices of the partials
+// (fixed order), o = y[:d_V] / y[d_V].  Partial layout per (bh, chunk, slice):
+// [C/16][d_V+1][16 tokens] fp32.  Every thread first adds the slices' partials
+// with 16-byte loads; then wave w < C/32 adds the intra-chunk term of query
+// tiles w and C/16-1-w (tile qt needs qt+1 key tiles, so each wave does
+// C/16+1 tiles' worth).
+template <int D, int DV, int C, typename TIn, typename TOut>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__restrict__ partial, int nslices,
                                                              int nchunk, int64_t n, int64_t tok0,
-                                                             TOut *__restrict__ out) {
-    constexpr int NC = DV + 1, TT = C / 16;
+                                                             const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                             const TIn *__restrict__ v, TOut *__restrict__ out,
+                                                             TaylorArgs ta) {
+    constexpr int NC = DV + 1, TT = C / 16, NT = (NC + 15) / 16, NCP = 16 * NT;
+    constexpr int VS = sizeof(TIn) == 2 ? C + 8 : C + 4;
     constexpr int NV = TT * NC * 4;                 // float4 per partial
     constexpr int PER = (NV + 255) / 256;
-    __shared__ float ys[TT * NC * 16];
+    constexpr int VBYTES = NCP * VS * (int)sizeof(TIn);
+    __shared__ __align__(16) unsigned char vt[VBYTES];
+    __shared__ __align__(16) float ys[TT * NC * 16];
     const int cc = blockIdx.x;
     const int64_t bh = blockIdx.y;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int64_t t0 = tok0 + (int64_t)cc * C;
+    const int nvalid = n - t0 < C ? (int)(n - t0) : C;
+    const TIn *qh = q + bh * n * D;
+    const TIn *kh = k + bh * n * D;
+    const TIn *vh = v + bh * n * DV;
+
+    // partial sums first: their loads are the long pole, issue them before the MFMA work
     const float4 *base = reinterpret_cast<const float4 *>(partial) + (bh * nchunk + cc) * (int64_t)nslices * NV;
     float4 acc[PER];
 #pragma unroll
@@ -560,9 +591,31 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
         const int i = tid + 256 * j;
         if (i < NV) reinterpret_cast<float4 *>(ys)[i] = acc[j];
     }
+
+    stage_v<DV, C, NCP, VS, TIn>(vt, vh, t0, nvalid, tid, 256);
     __syncthreads();
-    const int64_t t0 = tok0 + (int64_t)cc * C;
-    const int nvalid = n - t0 < C ? (int)(n - t0) : C;
+    static_assert(TT % 2 == 0 && TT / 2 <= 4, "query tiles pair up over the four wavefronts");
+    if (wave < TT / 2) {
+        const int qt = wave;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int qq = pass == 0 ? qt : TT - 1 - qt;    // tiles w and TT-1-w: w+1 + TT-w key tiles
+            f32x4 Z[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            intra_tile<D, NT, VS, TIn>(Z, qq, g, li, qh, kh, t0, nvalid, vt, ta);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int c = 16 * nt + li;
+                if (c < NC) {
+                    float4 *p = reinterpret_cast<float4 *>(ys + (qq * NC + c) * 16 + 4 * g);
+                    const float4 o = *p;
+                    *p = float4{o.x + Z[nt][0], o.y + Z[nt][1], o.z + Z[nt][2], o.w + Z[nt][3]};
+                }
+            }
+        }
+    }
+    __syncthreads();
     for (int i = tid; i < C * DV; i += 256) {
         const int t = i / DV, c = i - t * DV;
         if (t < nvalid) {
@@ -611,7 +664,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     using Cfg = ScanCfg<D, D, C, MT, TIn>;
     const int64_t bh = (int64_t)st->batch * st->heads;
     auto scan = prefill_scan_kernel<D, D, C, MT, TIn>;
-    auto red = prefill_reduce_kernel<D, C, TOut>;
+    auto red = prefill_reduce_kernel<D, D, C, TIn, TOut>;
     hipError_t e = hipFuncSetAttribute((const void *)scan, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
     if (e != hipSuccess) return e;
     TaylorArgs ta;
@@ -629,14 +682,15 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
                                idx->d_qw0, idx->d_qcidx, reinterpret_cast<const float4 *>(idx->d_qcoef),
                                st->d_state, idx->m_pad, static_cast<const TIn *>(q),
                                static_cast<const TIn *>(k), static_cast<const TIn *>(v), n, tok0, nseg,
-                               partial, ta);
+                               partial, ta.scale);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         {
             ProfScope ps(kProfCombine, stream);
             hipLaunchKernelGGL(red, dim3(nseg, (unsigned)bh), dim3(256), 0, stream, partial, plan.slices, nseg,
-                               n, tok0, static_cast<TOut *>(out));
+                               n, tok0, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                               static_cast<const TIn *>(v), static_cast<TOut *>(out), ta);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -165,8 +165,9 @@ int64_t sata_describe_features(int d_k, int P, uint32_t *tuples, float *coef, in
  * (i_1, i_2) (absent indices = d_k) and an aligned block of four last indices
  * i_3 = 4b + z.  w0[q] = i_1 | i_2 << 8 | b << 16 | mask << 24, where bit z of
  * mask marks slot z as a feature (else padding); cidx[q] is the feature index
- * of the first valid slot (-1 if none), and coef4[4q + z] the slot's readout
- * weight (0 for padding).  The order-0 quad has b = d_k/4 and mask 1.  The
+ * of the first valid slot (-1 if none), and coef4[4q + z] the slot's
+ * multinomial factor 1/alpha! (0 for padding); the slot's full readout weight
+ * is that factor times d_k^(-p/2), which the prefill applies by scaling q.  The order-0 quad has b = d_k/4 and mask 1.  The
  * valid slots of consecutive quads are consecutive features.  Returns the
  * number of quads, or -1 for arguments sata_build_index would reject. */
 int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *coef4, int64_t cap);

@@ -134,6 +134,7 @@ def test_quads_cover_the_features_in_order(d, P):
             assert idx == want
             got = [int(x) for x in slots[f, :order[f]]]
             assert got == want, (q, z, got, want)
-            assert qc[q, z] == coef[f]
+            # quad weight = multinomial part; the feature weight also carries d^(-p/2)
+            assert abs(qc[q, z] / math.sqrt(d) ** len(want) - coef[f]) <= 1e-6 * coef[f]
             f += 1
     assert f == len(tup)
