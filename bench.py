@@ -58,6 +58,10 @@ def parse_args():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="one launch of each timed kernel plus a 1 GiB copy, for rocprofv3 --pmc runs")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter CSVs of two --traffic-run passes into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -261,15 +265,119 @@ def cpu_baseline(wl, x, budget_s: float):
     }
 
 
+# ------------------------------------------------------------------ HBM traffic from counters
+
+COPY_BYTES = 1 << 30
+# kernel-name pattern -> (kernel, workload, source file)
+TRAFFIC_KERNELS = [
+    (r"prefill_scan_kernel<64, 64, 128, \d+, unsigned short>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
+    (r"prefill_scan_kernel<32, 32, 64, \d+, unsigned short>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
+    (r"prefill_scan_kernel<16, 16, 128, \d+, unsigned short>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
+    (r"decode_kernel<64, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
+]
+
+
+def traffic_run():
+    """One launch of every kernel whose traffic is recorded, preceded by a
+    plain 1 GiB device copy that calibrates the FETCH_SIZE / WRITE_SIZE
+    counters (bytes counted per byte actually moved)."""
+    import torch
+    import synth_inputs as si
+    from constant_cost_attention_amd import sata
+    sata.load()
+    torch.cuda.set_device(0)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for name in ("prefill_d64_p4_bf16", "prefill_d32_p4_bf16", "prefill_d16x64h_p4_bf16"):
+        wl = si.WORKLOADS[name]
+        q, k, v = si.draw_qkv_device((wl.batch, wl.heads), wl.n, wl.d_k, wl.d_v, wl.seed, wl.dtype)
+        idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+        st = sata.State(idx, wl.batch, wl.heads)
+        out = torch.empty(v.shape, dtype=v.dtype, device="cuda")
+        sata.sata_prefill(idx, st, q, k, v, out, chunk=wl.chunk)
+        torch.cuda.synchronize()
+        log("traffic run: prefill %s done" % name)
+        st.free()
+        idx.free()
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    wl = si.WORKLOADS["decode_d64_p4_f32"]
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
+    time_decode(sata, idx, st, wl, 2, 0, wl.seed + 30)
+    log("traffic run: decode done")
+    st.free()
+    idx.free()
+
+
+def _counter_means(path: str, counter: str):
+    """Per-dispatch counter values (KiB) from a rocprofv3 counter_collection CSV,
+    summed over the counter's instances, grouped by kernel name."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            key = (row["Dispatch_Id"], row["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    by_name = {}
+    for (_, name), val in per.items():
+        by_name.setdefault(name, []).append(val)
+    return by_name
+
+
+def write_traffic(fetch_csv: str, write_csv: str):
+    import re
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    copies = [n for n in fetch if "copy" in n.lower() and "sata::" not in n]
+    if not copies:
+        raise SystemExit("no copy kernel among: %s" % sorted(fetch))
+    copy_name = max(copies, key=lambda n: max(fetch[n]))
+    kib = COPY_BYTES / 1024.0
+    f_fetch = kib / max(fetch[copy_name])
+    f_write = kib / max(write[copy_name])
+    out = {"_calibration": {"copy_kernel": copy_name, "copy_bytes_each_way": COPY_BYTES,
+                            "fetch_kib_read": max(fetch[copy_name]), "write_kib_read": max(write[copy_name]),
+                            "fetch_factor": f_fetch, "write_factor": f_write}}
+    for pat, kernel, workload, source in TRAFFIC_KERNELS:
+        names = [n for n in fetch if re.search(pat, n)]
+        if len(names) != 1:
+            raise SystemExit("pattern %s matched %s" % (pat, names))
+        n = names[0]
+        fk = sum(fetch[n]) / len(fetch[n])
+        wk = sum(write[n]) / len(write[n])
+        out.setdefault(kernel, {})[workload] = {
+            "source": source, "source_sha256": source_sha(source), "kernel_name": n,
+            "dispatches": len(fetch[n]), "fetch_kib": fk, "write_kib": wk,
+            "bytes_per_launch": (fk * f_fetch + wk * f_write) * 1024.0,
+        }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
     args = parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not supported: "
               "multi-GPU execution is not implemented" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+    if args.traffic_run:
+        traffic_run()
+        return
     import torch
     import synth_inputs as si
     from constant_cost_attention_amd import sata
