@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <new>
 #include <string>
 #include <vector>
@@ -159,54 +160,95 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
     }
 }
 
-// Quads for the prefill: for every sorted prefix (orders 0..P-1, in feature
-// order) the aligned blocks of four last indices that reach a sorted tuple.
-// Each valid slot z carries the multinomial part 1/alpha! of its feature's
-// readout weight 1/(alpha! d^(p/2)) [hotdry, "Core insight of symmetric tensor
-// decomposition"]; the prefill applies d^(-p/2) by scaling q by 1/sqrt(d_K).
-// The hierarchical i1 <= i2 <= i3 structure lets a quad share one pair
-// product over four features [hotdry, "Hardware optimisation paths and
-// current limits"].
-static void build_quads(int d, int P, std::vector<sata::QuadRec> &out) {
-    int32_t next = 0;   // state index of the next valid feature
-    auto emit = [&](int i1, int i2, int b, const std::vector<int> &prefix) {
+// Quads for the prefill, in the order the scan kernel walks them.  A quad is a
+// pair prefix (i1, i2) (either may be absent) and an aligned block of four last
+// indices i3 = 4b + z; slot z is a feature when (i1, i2, 4b+z) is sorted.  Quads
+// come in "positions" of four, one per stream, whose pairs have the same block
+// range: every pair with i2 in [4a, 4a+4) (order 3: i1 <= i2; order 2: i1
+// absent; for a = 0 also the order-1 pair with both absent) sweeps the blocks
+// b = a .. d/4-1, and four such pairs sweep them side by side.  So within a
+// position the block b is common, and only the first block of a group (the
+// one holding i3 = i2) has slots below i2 (invalid) or a diagonal slot whose
+// multiplicity differs from the rest.  Each valid slot carries the multinomial
+// part 1/alpha! of its feature's readout weight 1/(alpha! d^(p/2))
+// [hotdry, "Core insight of symmetric tensor decomposition"]; the prefill
+// applies d^(-p/2) by scaling q by 1/sqrt(d_K).  The pair product is shared by
+// the four slots of a quad and by all blocks of its group [hotdry, "Hardware
+// optimisation paths and current limits": the hierarchical index structure].
+// Order 0 is a position of its own (block d/4: the constant-1 slot).  Unused
+// streams are padding quads (pair product 0).  flags[pos]: bit 0 = some quad
+// of the position has slots with different weights (or invalid slots), bit 1 =
+// the position starts a new group of pairs.
+static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags) {
+    std::map<std::vector<int>, int32_t> index;   // sorted tuple -> feature index
+    {
+        int32_t f = 0;
+        for (int p = 0; p < P; ++p) {
+            std::vector<std::vector<int>> tuples;
+            enumerate_order(d, p, tuples);
+            for (const auto &t : tuples) index[t] = f++;
+        }
+    }
+    const int none = d, pad = d + 1;
+    auto make = [&](int i1, int i2, int b, bool order0, uint32_t &nonuni) {
         sata::QuadRec q{};
+        q.w0 = (uint32_t)pad | ((uint32_t)pad << 8) | ((uint32_t)b << 16);
+        q.cidx = -1;
+        if (i1 == pad) return q;
+        std::vector<int> prefix;
+        if (i1 != none) prefix.push_back(i1);
+        if (i2 != none) prefix.push_back(i2);
         uint32_t mask = 0;
         int first = -1;
         for (int z = 0; z < 4; ++z) {
-            const int i3 = 4 * b + z;
             std::vector<int> t = prefix;
             bool ok;
-            if (b * 4 >= d) {            // order-0 quad: slot 0 is the constant feature
+            if (order0) {
                 ok = z == 0;
             } else {
+                const int i3 = 4 * b + z;
                 ok = t.empty() || i3 >= t.back();
                 t.push_back(i3);
             }
-            if (ok) {
-                mask |= 1u << z;
-                if (first < 0) first = z;
-                q.coef[z] = (float)(1.0 / alpha_factorial(t));
-            } else {
-                q.coef[z] = 0.f;
+            q.coef[z] = 0.f;
+            if (!ok) continue;
+            mask |= 1u << z;
+            if (first < 0) {
+                first = z;
+                q.cidx = index.at(t);
             }
+            q.coef[z] = (float)(1.0 / alpha_factorial(t));
         }
         q.w0 = (uint32_t)i1 | ((uint32_t)i2 << 8) | ((uint32_t)b << 16) | (mask << 24);
-        q.cidx = mask ? next : -1;
-        next += __builtin_popcount(mask);
-        out.push_back(q);
+        if (mask != 0xfu || q.coef[0] != q.coef[1] || q.coef[0] != q.coef[2] || q.coef[0] != q.coef[3]) nonuni = 1;
+        return q;
     };
-    const int none = d;
-    if (P >= 1) emit(none, none, d / 4, {});
-    if (P >= 2)
-        for (int b = 0; b < d / 4; ++b) emit(none, none, b, {});
-    if (P >= 3)
-        for (int i2 = 0; i2 < d; ++i2)
-            for (int b = i2 / 4; b < d / 4; ++b) emit(none, i2, b, {i2});
-    if (P >= 4)
-        for (int i1 = 0; i1 < d; ++i1)
-            for (int i2 = i1; i2 < d; ++i2)
-                for (int b = i2 / 4; b < d / 4; ++b) emit(i1, i2, b, {i1, i2});
+    for (int a = 0; a < d / 4; ++a) {
+        std::vector<std::pair<int, int>> pairs;
+        if (P >= 2 && a == 0) pairs.push_back({none, none});
+        for (int i2 = 4 * a; i2 < 4 * a + 4; ++i2) {
+            if (P >= 4)
+                for (int i1 = 0; i1 <= i2; ++i1) pairs.push_back({i1, i2});
+            if (P >= 3) pairs.push_back({none, i2});
+        }
+        for (size_t g = 0; g < pairs.size(); g += 4) {
+            for (int b = a; b < d / 4; ++b) {
+                uint32_t nonuni = 0;
+                for (size_t s = 0; s < 4; ++s) {
+                    const bool have = g + s < pairs.size();
+                    out.push_back(make(have ? pairs[g + s].first : pad, have ? pairs[g + s].second : pad, b,
+                                       false, nonuni));
+                }
+                flags.push_back(nonuni | (b == a ? 2u : 0u));
+            }
+        }
+    }
+    {
+        uint32_t nonuni = 0;
+        out.push_back(make(none, none, d / 4, true, nonuni));
+        for (int s = 1; s < 4; ++s) out.push_back(make(pad, pad, d / 4, false, nonuni));
+        flags.push_back(nonuni | 2u);
+    }
 }
 
 static sata_status check_dims(int d_k, int d_v, int P) {
@@ -236,7 +278,8 @@ int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *
     g_last_error.clear();
     if (check_dims(d_k, d_k, P) != SATA_OK) return -1;
     std::vector<sata::QuadRec> quads;
-    build_quads(d_k, P, quads);
+    std::vector<uint32_t> flags;
+    build_quads(d_k, P, quads, flags);
     const int64_t nq = (int64_t)quads.size();
     for (int64_t i = 0; i < nq && i < cap; ++i) {
         if (w0) w0[i] = quads[(size_t)i].w0;
@@ -273,7 +316,8 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     tup.resize((size_t)idx->m_tab, pad);
     coef.resize((size_t)idx->m_tab, 0.f);
     std::vector<sata::QuadRec> quads;
-    build_quads(d_k, P, quads);
+    std::vector<uint32_t> qflags;
+    build_quads(d_k, P, quads, qflags);
     idx->nq = (int64_t)quads.size();
     idx->nq_tab = round_up(idx->nq, sata::kQuadPad);
     {
@@ -281,6 +325,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
         padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8);   // pair product 0
         padq.cidx = -1;
         quads.resize((size_t)idx->nq_tab, padq);
+        qflags.resize((size_t)(idx->nq_tab / 4), 2u);
     }
     std::vector<uint32_t> qw0(quads.size());
     std::vector<int32_t> qcidx(quads.size());
@@ -301,6 +346,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
         if (idx->d_qw0) (void)hipFree(idx->d_qw0);
         if (idx->d_qcidx) (void)hipFree(idx->d_qcidx);
         if (idx->d_qcoef) (void)hipFree(idx->d_qcoef);
+        if (idx->d_qflags) (void)hipFree(idx->d_qflags);
         delete idx;
     };
     hipError_t e = hipMalloc(&idx->d_tup, tup.size() * sizeof(uint32_t));
@@ -308,6 +354,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     if (e == hipSuccess) e = hipMalloc(&idx->d_qw0, qw0.size() * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMalloc(&idx->d_qcidx, qcidx.size() * sizeof(int32_t));
     if (e == hipSuccess) e = hipMalloc(&idx->d_qcoef, qcoef.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&idx->d_qflags, qflags.size() * sizeof(uint32_t));
     if (e != hipSuccess) {
         (void)hipGetLastError();
         release();
@@ -318,6 +365,8 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     if (e == hipSuccess) e = hipMemcpy(idx->d_qw0, qw0.data(), qw0.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(idx->d_qcidx, qcidx.data(), qcidx.size() * sizeof(int32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(idx->d_qcoef, qcoef.data(), qcoef.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(idx->d_qflags, qflags.data(), qflags.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         release();
         return fail_hip(e, "index upload");
@@ -334,6 +383,7 @@ void sata_index_free(sata_index *idx) {
     if (idx->d_qw0) (void)hipFree(idx->d_qw0);
     if (idx->d_qcidx) (void)hipFree(idx->d_qcidx);
     if (idx->d_qcoef) (void)hipFree(idx->d_qcoef);
+    if (idx->d_qflags) (void)hipFree(idx->d_qflags);
     delete idx;
 }
 

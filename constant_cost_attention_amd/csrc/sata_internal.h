@@ -30,11 +30,13 @@ struct sata_index {
     float *d_coef = nullptr;     // [m_tab] query-side readout weight 1/(alpha! d_K^(p/2)); 0 for padding
     float taylor[8] = {0};       // 1/p!, p < P (intra-chunk direct weights)
     // Prefill-side "pair-quad" view of the same features (see build_quads):
-    int64_t nq = 0;              // quads
+    // quads come in positions of four (one per stream), position-major.
+    int64_t nq = 0;              // quads (4 per position)
     int64_t nq_tab = 0;          // quad table length (padded)
     uint32_t *d_qw0 = nullptr;   // [nq_tab] i1 | i2 << 8 | b << 16 | mask << 24
     int32_t *d_qcidx = nullptr;  // [nq_tab] state index of the first valid slot (-1: none)
     float *d_qcoef = nullptr;    // [nq_tab][4] query-side weights per slot (0: invalid)
+    uint32_t *d_qflags = nullptr;   // [nq_tab / 4] per position: bit 0 mixed weights, bit 1 new pair group
 };
 
 struct sata_state {
@@ -55,11 +57,11 @@ constexpr int kQuadPad = 1024;           // quad tables cover every prefill slic
 // Prefill feature view.  The features of orders 0..P-1 are grouped into
 // "quads": a pair prefix (i1, i2) (either may be absent) and an aligned block
 // of four last indices i3 = 4b + z, z = 0..3; slot z is a feature when the
-// tuple (i1, i2, 4b+z) is sorted, else padding.  Quads run in the same order
-// as the features, so the valid slots of consecutive quads are consecutive
-// features.  Absent indices point at the constant-1 slot (d_K), padding quads
-// at the constant-0 slot (d_K+1); order 0 is the quad (-, -, b = d_K/4) whose
-// slots d_K..d_K+3 hold 1, 0, 0, 0.
+// tuple (i1, i2, 4b+z) is sorted, else padding.  Quads come in positions of
+// four whose pairs sweep the same blocks side by side (see build_quads), so the
+// block b is common to a position.  Absent indices point at the constant-1
+// slot (d_K), padding quads at the constant-0 slot (d_K+1); order 0 is the
+// quad (-, -, b = d_K/4) whose slots d_K..d_K+3 hold 1, 0, 0, 0.
 struct QuadRec {
     uint32_t w0;
     int32_t cidx;

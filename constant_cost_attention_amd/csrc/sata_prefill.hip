@@ -42,40 +42,51 @@
 
 namespace sata {
 
-constexpr int kNW = 4;                           // wavefronts per workgroup
-constexpr int kThreads = 64 * kNW;
+constexpr int kNW = 4;                           // wavefronts per workgroup (default)
 constexpr int64_t kWorkCap = (int64_t)4 << 30;   // partial-sum workspace cap (bytes)
 
-template <int D, int DV, int C, int MT, typename TIn>
+template <int D, int DV, int C, int MT, int NW, typename TIn>
 struct ScanCfg {
     static constexpr bool BF = sizeof(TIn) == 2;
-    static constexpr int NQW = 4 * MT;           // quads per wavefront (four streams of MT)
-    static constexpr int NQ = kNW * NQW;         // quads per workgroup (slice)
-    static constexpr int NC = DV + 1;            // value columns + normaliser
-    static constexpr int NT = (NC + 15) / 16;    // 16-column MFMA tiles
-    static constexpr int NCP = NT * 16;
-    static constexpr int TT = C / 16;            // 16-token tiles per chunk
-    static constexpr int TH = (BF ? 64 : 32) < C ? (BF ? 64 : 32) : C;   // tokens per readout pass
-    static constexpr int TTH = TH / 16;          // token tiles per pass
-    static constexpr int NH = C / TH;            // passes per chunk
-    static constexpr int KR = D + 4;             // K rows: d_K dims, then 1, 0, 0, 0
-    static constexpr int KS = C + 4;             // Kt row stride (floats)
-    static constexpr int QS = D + 4;             // Qs row stride (floats): dims, then 1, 0, 0, 0
-    static constexpr int VS = BF ? C + 8 : C + 4;   // Vt row stride (elements)
+    static constexpr int THREADS = 64 * NW;       // NW wavefronts (4 or 8)
+    static constexpr int NP = NW * MT;            // positions (4 quads, 16 features) per slice
+    static constexpr int NC = DV + 1;             // value columns + normaliser
+    static constexpr int NT = (NC + 15) / 16;     // 16-column MFMA tiles
+    static constexpr int TT = C / 16;             // 16-token tiles per chunk
+    // Readout work split: TG groups of two token tiles each, and KH = NW / TG halves of the
+    // slice's positions; wavefronts w and w + TG read out the same tiles from different halves.
+    static constexpr int TPW = 2;                 // readout token tiles per wavefront
+    static constexpr int TG = TT / TPW;
+    static constexpr int KH = NW / TG;
+    static constexpr int NPH = NP / KH;           // readout positions per K half
+    static constexpr int KR = D + 4;              // K rows: d_K dims, then 1, 0, 0, 0
+    static constexpr int KS = C + 4;              // Kt row stride (floats)
+    static constexpr int QS = D + 4;              // Qs row stride (floats): dims, then 1, 0, 0, 0
     static constexpr int ES = BF ? 2 : 4;
-    static constexpr int OFF_K = 0;
-    static constexpr int OFF_Q = OFF_K + KR * KS * 4;
-    static constexpr int OFF_V = OFF_Q + TH * QS * 4;
-    static constexpr int OFF_Y = (OFF_V + NC * VS * ES + 15) / 16 * 16;
-    static constexpr int YB = TTH * NT * 64;     // f32x4 per wavefront readout buffer
-    static constexpr int OFF_W = OFF_Y + kNW * YB * 16;
-    static constexpr int OFF_QC = OFF_W + NQ * 4;
-    static constexpr int LDS = OFF_QC + NQ * 16;
-    static_assert(MT % 2 == 0, "tiles per wave must be even");
-    static_assert(C % 32 == 0, "chunk must be a multiple of 32");
-    static_assert(D % 8 == 0, "d_K must be a multiple of 8");
-    static_assert(TTH <= kNW, "one token tile per wavefront in the reduce-scatter");
-    static_assert(OFF_V % 16 == 0 && OFF_QC % 16 == 0, "alignment");
+    static constexpr int VS = BF ? C + 8 : C + 4; // Vt row stride (elements)
+    // Readout operand copy of the slice's state.  bf16: [NP/2 K steps][NT][64 lanes] x 8 bf16;
+    // fp32: [4 NP K steps][NT][64 lanes] x 1 float.  Shares its LDS with Kt + Vt (update phase).
+    static constexpr int BCB = BF ? NP / 2 * NT * 64 * 16 : NP * 4 * NT * 64 * 4;
+    static constexpr int KVB = KR * KS * 4 + (NC * VS * ES + 15) / 16 * 16;
+    static constexpr int XB = (BCB > KVB ? BCB : KVB);
+    static constexpr int OFF_VT = KR * KS * 4;
+    static constexpr int OFF_Q = (XB + 15) / 16 * 16;    // Qs [C][QS] fp32, scaled by 1/sqrt(d)
+    static constexpr int OFF_W = OFF_Q + C * QS * 4;     // quad words [NP][4]
+    static constexpr int OFF_QC = OFF_W + NP * 4 * 4;    // quad weights [NP][4] float4
+    static constexpr int OFF_F = OFF_QC + NP * 4 * 16;   // position flags [NP]
+    static constexpr int OFF_E = OFF_F + NP * 4;         // readout exchange of the second K half
+    static constexpr int LDS = OFF_E + (KH - 1) * TG * TPW * NT * 64 * 16;
+    // Prefetch of one chunk's q, k or v: 16-byte units per thread.
+    static constexpr int EPU = 16 / ES;                  // elements per unit
+    static constexpr int UNITS = C * D / EPU;
+    static constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
+    static_assert(DV == D, "d_V = d_K");
+    static_assert(D % EPU == 0, "a unit holds whole dims of one token");
+    static_assert(C % 64 == 0 && TG * KH == NW && KH <= 2, "readout split: 64 or 128 tokens per chunk");
+    static_assert(!BF || NPH % 2 == 0, "bf16 K steps pair two positions");
+    static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
+    static_assert(OFF_E % 16 == 0, "alignment");
+    static_assert(OFF_Q % 16 == 0 && OFF_QC % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -211,41 +222,73 @@ __device__ __forceinline__ void stage_v(unsigned char *vt, const TIn *vh, int64_
     }
 }
 
-template <int D, int DV, int C, int MT, typename TIn>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// One 16-byte unit of the chunk's q, k or v per (thread, u): token and first dim.
+// Consecutive lanes take consecutive tokens, so the transposed (dim-major) LDS
+// writes of k and v fall in consecutive banks.
+template <int C, int EPU>
+__device__ __forceinline__ void unit_coords(int i, int &t, int &d0) {
+    t = i % C;
+    d0 = (i / C) * EPU;
+}
+
+// Unpack one 16-byte unit into fp32.
+template <typename TIn>
+__device__ __forceinline__ void unpack_unit(const uint4 u, float (&x)[16 / sizeof(TIn)]) {
+    if constexpr (sizeof(TIn) == 2) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(w[j] << 16);
+            x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    } else {
+        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+        x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+    }
+}
+
+template <int D, int DV, int C, int MT, int NW, typename TIn>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
-                         const float4 *__restrict__ qcoef, float *__restrict__ state, int64_t m_pad,
+                         const float4 *__restrict__ qcoef, const uint32_t *__restrict__ qflags,
+                         float *__restrict__ state, int64_t m_pad,
                          const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
                          int64_t n, int64_t tok0, int nchunk, float *__restrict__ partial, float qscale) {
-    using Cfg = ScanCfg<D, DV, C, MT, TIn>;
-    constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TH = Cfg::TH, TTH = Cfg::TTH;
-    constexpr int KS = Cfg::KS, QS = Cfg::QS, VS = Cfg::VS, NQ = Cfg::NQ, NQW = Cfg::NQW, YB = Cfg::YB;
+    using Cfg = ScanCfg<D, DV, C, MT, NW, TIn>;
+    constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TPW = Cfg::TPW, NP = Cfg::NP, NPH = Cfg::NPH;
+    constexpr int kThreads = Cfg::THREADS;
+    constexpr int KS = Cfg::KS, QS = Cfg::QS, VS = Cfg::VS, EPU = Cfg::EPU, UNITS = Cfg::UNITS,
+                  UPT = Cfg::UPT;
     extern __shared__ __align__(16) unsigned char lds[];
-    float *Kt = reinterpret_cast<float *>(lds + Cfg::OFF_K);      // [KR][KS]  dim-major, whole chunk
-    float *Qs = reinterpret_cast<float *>(lds + Cfg::OFF_Q);      // [TH][QS]  one readout pass, dims scaled
-    f32x4 *Yb = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_Y);      // [kNW][TTH][NT][64] accumulator layout
-    uint32_t *W0 = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_W);   // [NQ]
-    float4 *QC = reinterpret_cast<float4 *>(lds + Cfg::OFF_QC);      // [NQ]
+    float *Kt = reinterpret_cast<float *>(lds);                      // [KR][KS] dim-major (update)
+    unsigned char *Vt = lds + Cfg::OFF_VT;                           // [NC][VS] operand dtype (update)
+    unsigned char *Bc = lds;                                         // state copy (readout)
+    float *Qs = reinterpret_cast<float *>(lds + Cfg::OFF_Q);         // [C][QS]
+    uint32_t *W0 = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_W);   // [NP][4]
+    float4 *QC = reinterpret_cast<float4 *>(lds + Cfg::OFF_QC);      // [NP][4]
+    uint32_t *QF = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_F);   // [NP]
+    f32x4 *YE = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_E);         // [TG][TPW][NT][64]
 
     const int slice = blockIdx.x, nslices = gridDim.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
-    const int64_t qs0 = (int64_t)slice * NQ;          // first quad of the slice
-    const int wq0 = wave * NQW;                       // first quad of this wave within the slice
-    // Four streams of MT consecutive quads per wave: tile j holds quad wq0 + s*MT + j in rows 4s..4s+3.
-    // This lane's accumulator rows (4g + r) are stream g; its update rows (li) are stream li/4, slot li%4.
+    const int64_t ps0 = (int64_t)slice * NP;          // first position of the slice
+    const int p0 = wave * MT;                         // this wave's first position within the slice
+    // Tile j of this wave is position p0 + j; its rows 4s + z are stream s, slot z.  The lane's
+    // accumulator rows (4g + r) are stream g; its update row (li) is stream li/4, slot li%4.
 
-    for (int i = tid; i < NQ; i += kThreads) {
-        W0[i] = qw0[qs0 + i];
-        QC[i] = qcoef[qs0 + i];
+    for (int i = tid; i < NP * 4; i += kThreads) {
+        W0[i] = qw0[ps0 * 4 + i];
+        QC[i] = qcoef[ps0 * 4 + i];
     }
+    for (int i = tid; i < NP; i += kThreads) QF[i] = qflags[ps0 + i];
 
     float *Sh = state + bh * NC * m_pad;
     f32x4 S[MT][NT];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-        const int64_t qd = qs0 + wq0 + g * MT + j;
+        const int64_t qd = (ps0 + p0 + j) * 4 + g;
         const uint32_t w = qw0[qd];
         const int32_t c0 = qcidx[qd];
         const uint32_t mask = qd_mask(w);
@@ -261,202 +304,291 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     }
     __syncthreads();
 
-    uint32_t myW[MT];                                  // update rows: stream li/4
+    // update-side view of this wave's positions: the lane's stream (li / 4) and slot (li % 4)
+    const int us = li >> 2, uz = li & 3;
+    uint32_t uw[MT];
+    uint32_t newgrp = 0;                               // bit j: position p0 + j starts a pair group
 #pragma unroll
-    for (int j = 0; j < MT; ++j) myW[j] = W0[wq0 + (li >> 2) * MT + j];
-    uint32_t shared_pair = 0;                          // readout K step kk: quads 2kk, 2kk+1 of stream g
-#pragma unroll
-    for (int kk = 0; kk < MT / 2; ++kk) {
-        const int qa = wq0 + g * MT + 2 * kk;
-        if (__all(qd_pair(W0[qa]) == qd_pair(W0[qa + 1]))) shared_pair |= 1u << kk;
+    for (int j = 0; j < MT; ++j) {
+        uw[j] = W0[(p0 + j) * 4 + us];
+        if (QF[p0 + j] & 2u) newgrp |= 1u << j;
     }
+    newgrp = (uint32_t)__builtin_amdgcn_readfirstlane((int)newgrp);
+    // slice-wide position masks (bit pos): group starts and mixed-weight positions
+    static_assert(NP <= 64, "position masks are 64-bit");
+    const uint64_t gmask = __ballot(lane < NP && (QF[lane < NP ? lane : 0] & 2u));
+    const uint64_t nmask = __ballot(lane < NP && (QF[lane < NP ? lane : 0] & 1u));
 
     const TIn *qh = q + bh * n * D;
     const TIn *kh = k + bh * n * D;
     const TIn *vh = v + bh * n * DV;
-
-    auto stage_q = [&](int64_t tq0, int nq_valid) {
-        for (int i = tid; i < TH * (D / 8); i += kThreads) {
-            const int t = i % TH, d8 = (i / TH) * 8;
-            float qv[8];
-            if (t < nq_valid) {
-                const int64_t src = (tq0 + t) * D + d8;
-                if constexpr (Cfg::BF) {
-                    const uint4 qu = *reinterpret_cast<const uint4 *>(qh + src);
-                    const uint32_t qw[4] = {qu.x, qu.y, qu.z, qu.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        qv[2 * j] = __uint_as_float(qw[j] << 16);
-                        qv[2 * j + 1] = __uint_as_float(qw[j] & 0xffff0000u);
-                    }
-                } else {
-                    const float4 q0 = *reinterpret_cast<const float4 *>(qh + src);
-                    const float4 q1 = *reinterpret_cast<const float4 *>(qh + src + 4);
-                    qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w;
-                    qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) qv[j] = 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) qv[j] *= qscale;
-            *reinterpret_cast<float4 *>(Qs + t * QS + d8) = float4{qv[0], qv[1], qv[2], qv[3]};
-            *reinterpret_cast<float4 *>(Qs + t * QS + d8 + 4) = float4{qv[4], qv[5], qv[6], qv[7]};
-        }
-        for (int t = tid; t < TH; t += kThreads)
-            *reinterpret_cast<float4 *>(Qs + t * QS + D) = float4{1.f, 0.f, 0.f, 0.f};
+    auto chunk_t0 = [&](int cc) { return tok0 + (int64_t)cc * C; };
+    auto chunk_nv = [&](int cc) {
+        const int64_t r = n - chunk_t0(cc);
+        return r < C ? (int)r : C;
     };
 
-    for (int cc = 0; cc < nchunk; ++cc) {
-        const int64_t t0 = tok0 + (int64_t)cc * C;
-        const int nvalid = n - t0 < C ? (int)(n - t0) : C;
-        __syncthreads();          // previous chunk: update done with Kt/Vt, reduce-scatter done with Yb
-        // ---- stage K (dim-major fp32), [V | 1] (operand dtype) for the chunk, Q for pass 0
-        for (int i = tid; i < C * (D / 8); i += kThreads) {
-            const int t = i % C, d8 = (i / C) * 8;     // consecutive lanes: consecutive tokens
-            float kv[8];
-            if (t < nvalid) {
-                const int64_t src = (t0 + t) * D + d8;
-                if constexpr (Cfg::BF) {
-                    const uint4 ku = *reinterpret_cast<const uint4 *>(kh + src);
-                    const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+    // ---- chunk staging: global -> registers (issued a phase ahead), registers -> LDS
+    auto gload = [&](uint4 (&r)[UPT], const TIn *src, int cc) {
+        const int64_t t0 = chunk_t0(cc);
+        const int nv = chunk_nv(cc);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        kv[2 * j] = __uint_as_float(kw[j] << 16);
-                        kv[2 * j + 1] = __uint_as_float(kw[j] & 0xffff0000u);
-                    }
-                } else {
-                    const float4 k0 = *reinterpret_cast<const float4 *>(kh + src);
-                    const float4 k1 = *reinterpret_cast<const float4 *>(kh + src + 4);
-                    kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
-                    kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
+        for (int u = 0; u < UPT; ++u) {
+            const int i = tid + u * kThreads;
+            int t, d0;
+            unit_coords<C, EPU>(i, t, d0);
+            r[u] = uint4{0u, 0u, 0u, 0u};
+            if (i < UNITS && t < nv) r[u] = *reinterpret_cast<const uint4 *>(src + (t0 + t) * D + d0);
+        }
+    };
+    auto write_q = [&](const uint4 (&r)[UPT]) {     // Qs <- q / sqrt(d), row-major; invalid tokens are 0
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int i = tid + u * kThreads;
+            if (i >= UNITS) break;
+            int t, d0;
+            unit_coords<C, EPU>(i, t, d0);
+            float x[EPU];
+            unpack_unit<TIn>(r[u], x);
+#pragma unroll
+            for (int e = 0; e < EPU; e += 4)
+                *reinterpret_cast<float4 *>(Qs + t * QS + d0 + e) =
+                    float4{x[e] * qscale, x[e + 1] * qscale, x[e + 2] * qscale, x[e + 3] * qscale};
+        }
+        for (int t = tid; t < C; t += kThreads) *reinterpret_cast<float4 *>(Qs + t * QS + D) = float4{1.f, 0.f, 0.f, 0.f};
+    };
+    auto write_kv = [&](const uint4 (&rk)[UPT], const uint4 (&rv)[UPT], int nv) {   // Kt, Vt dim-major
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int i = tid + u * kThreads;
+            if (i >= UNITS) break;
+            int t, d0;
+            unit_coords<C, EPU>(i, t, d0);
+            float x[EPU];
+            unpack_unit<TIn>(rk[u], x);
+#pragma unroll
+            for (int e = 0; e < EPU; ++e) Kt[(d0 + e) * KS + t] = x[e];
+            if constexpr (Cfg::BF) {
+                const uint32_t w[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
+                uint16_t *V16 = reinterpret_cast<uint16_t *>(Vt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    V16[(d0 + 2 * e) * VS + t] = (uint16_t)(w[e] & 0xffffu);
+                    V16[(d0 + 2 * e + 1) * VS + t] = (uint16_t)(w[e] >> 16);
                 }
             } else {
+                unpack_unit<TIn>(rv[u], x);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) kv[j] = 0.f;
+                for (int e = 0; e < EPU; ++e) reinterpret_cast<float *>(Vt)[(d0 + e) * VS + t] = x[e];
             }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) Kt[(d8 + j) * KS + t] = kv[j];
         }
         for (int t = tid; t < C; t += kThreads) {
             Kt[D * KS + t] = 1.f;
             Kt[(D + 1) * KS + t] = 0.f; Kt[(D + 2) * KS + t] = 0.f; Kt[(D + 3) * KS + t] = 0.f;
+            if constexpr (Cfg::BF) reinterpret_cast<bf16_t *>(Vt)[DV * VS + t] = from_f32<bf16_t>(t < nv ? 1.f : 0.f);
+            else reinterpret_cast<float *>(Vt)[DV * VS + t] = t < nv ? 1.f : 0.f;
         }
-        stage_v<DV, C, NC, VS, TIn>(lds + Cfg::OFF_V, vh, t0, nvalid, tid, kThreads);
-        stage_q(t0, nvalid);
-        __syncthreads();
-
-        // ---- inter-chunk readout, Y = psi(Q_c)[:, slice] . S^(c-1)[slice, :], in passes of TH
-        //      tokens; each wave's partial goes to its own LDS buffer, then wave w adds the four
-        //      buffers' token tile w and writes it out (one barrier, no serial chain)
+    };
+    // state accumulators -> readout operand copy in LDS (this wave's K steps)
+    auto write_bcopy = [&]() {
+        if constexpr (Cfg::BF) {
+            // position p fills half p % 2 of K step p / 2 (8 bytes per lane): whole K steps when
+            // this wave's first position is even, else a leading and a trailing half step
+            if constexpr (MT % 2 == 0) {
+                if (p0 % 2 == 0) {
 #pragma unroll
-        for (int hf = 0; hf < Cfg::NH; ++hf) {
-            if (hf > 0) {
-                const int64_t tq0 = t0 + hf * TH;
-                stage_q(tq0, n - tq0 < TH ? (int)(n - tq0) : TH);
-                __syncthreads();
+                    for (int kk = 0; kk < MT / 2; ++kk)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            float b[8];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) { b[r] = S[2 * kk][nt][r]; b[4 + r] = S[2 * kk + 1][nt][r]; }
+                            const int ks = p0 / 2 + kk;
+                            *reinterpret_cast<bf16x8 *>(Bc + ((ks * NT + nt) * 64 + lane) * 16) = pack_bf16x8(b);
+                        }
+                    return;
+                }
             }
-            f32x4 Y[TTH][NT];
 #pragma unroll
-            for (int tt = 0; tt < TTH; ++tt)
+            for (int j = 0; j < MT; ++j)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int p = p0 + j;
+                    const uint2 h = {pack_bf16x2(S[j][nt][0], S[j][nt][1]), pack_bf16x2(S[j][nt][2], S[j][nt][3])};
+                    *reinterpret_cast<uint2 *>(Bc + (((p / 2) * NT + nt) * 64 + lane) * 16 + (p % 2) * 8) = h;
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        reinterpret_cast<float *>(Bc)[(((p0 + j) * 4 + r) * NT + nt) * 64 + lane] = S[j][nt][r];
+        }
+    };
+
+    uint4 rk[UPT], rv[UPT], rq[UPT];
+    if (nchunk > 0) {
+        gload(rk, kh, 0);
+        gload(rv, vh, 0);
+        gload(rq, qh, 0);
+        write_q(rq);
+        if (nchunk > 1) gload(rq, qh, 1);
+    }
+    write_bcopy();
+    __syncthreads();
+
+    constexpr int TG = Cfg::TG;
+    const int tt0 = (wave % TG) * TPW;                // this wave's readout token tiles
+    const int half = wave / TG;                       // and K half: positions [half * NPH, (half + 1) * NPH)
+    const int pbeg = half * NPH;
+    for (int cc = 0; cc < nchunk; ++cc) {
+        // ---- inter-chunk readout Y = psi(Q_c)[:, slice] . S^(c-1)[slice, :] for this wave's tiles,
+        //      over its half of the slice's positions (state operand from LDS)
+        f32x4 Y[TPW][NT];
+        {
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-            if constexpr (Cfg::BF) {
-                // psi = coef_z * (q_i1 q_i2) * q_(4b+z); q carries 1/sqrt(d), coef_z = 1/alpha!
+            const float *qrow[TPW];
 #pragma unroll
-                for (int kk = 0; kk < MT / 2; ++kk) {
+            for (int tt = 0; tt < TPW; ++tt) qrow[tt] = Qs + (16 * (tt0 + tt) + li) * QS;
+            float pcur[TPW];                          // pair weight * q_i1 * q_i2 of stream g
+            float pz[TPW][4];                         // per-slot factor: pcur, times the slot weight ratio
+            int xo = 0;                               // 4 b: the position's block of q
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                pcur[tt] = 0.f;
+#pragma unroll
+                for (int z = 0; z < 4; ++z) pz[tt][z] = 0.f;
+            }
+            // Within a pair group the block advances by one per position, so only group starts
+            // (uniform bit masks) read the quad tables; the rest of the loop has fixed addresses.
+            // Mixed-weight positions are group starts; the position after one restores pz.
+            auto position = [&](int pos) {
+                if (((gmask >> pos) & 1u) || pos == pbeg) {
+                    __asm__ volatile("" ::: "memory");
+                    const uint32_t w = W0[pos * 4 + g];
+                    const int i1 = qd_i1(w), i2 = qd_i2(w);
+                    const bool half = i1 == i2 && i1 < D;
+                    const float cp = half ? 0.5f : 1.f;
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) pcur[tt] = cp * qrow[tt][i1] * qrow[tt][i2];
+                    xo = 4 * qd_b(w);
+                    if ((nmask >> pos) & 1u) {
+                        const float4 cq = QC[pos * 4 + g];
+                        const float rinv = half ? 2.f : 1.f;
+                        const float r4[4] = {cq.x * rinv, cq.y * rinv, cq.z * rinv, cq.w * rinv};
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                            for (int z = 0; z < 4; ++z) pz[tt][z] = pcur[tt] * r4[z];
+                    } else {
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                            for (int z = 0; z < 4; ++z) pz[tt][z] = pcur[tt];
+                    }
+                } else {
+                    xo += 4;
+                    if (pos > pbeg && ((nmask >> (pos - 1)) & 1u)) {
+                        __asm__ volatile("" ::: "memory");
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                            for (int z = 0; z < 4; ++z) pz[tt][z] = pcur[tt];
+                    }
+                }
+            };
+            if constexpr (Cfg::BF) {
+                const bf16x8 *Bv = reinterpret_cast<const bf16x8 *>(Bc);
+#pragma unroll 1
+                for (int kk = pbeg / 2; kk < (pbeg + NPH) / 2; ++kk) {
                     bf16x8 B[NT];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        float b[8];
+                    for (int nt = 0; nt < NT; ++nt) B[nt] = Bv[(kk * NT + nt) * 64 + lane];
+                    float a[TPW][8];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) { b[r] = S[2 * kk][nt][r]; b[4 + r] = S[2 * kk + 1][nt][r]; }
-                        B[nt] = pack_bf16x8(b);
-                    }
-                    const int qa = wq0 + g * MT + 2 * kk, qb = qa + 1;
-                    const uint32_t wa = W0[qa], wb = W0[qb];
-                    const float4 ca = QC[qa], cb = QC[qb];
-                    const bool sp = (shared_pair >> kk) & 1u;
-                    const int a1 = qd_i1(wa), a2 = qd_i2(wa), ab = 4 * qd_b(wa);
-                    const int b1 = qd_i1(wb), b2 = qd_i2(wb), bb = 4 * qd_b(wb);
-                    const float *row = Qs + li * QS;
-                    float pa1 = row[a1], pa2 = row[a2], pb1 = 0.f, pb2 = 0.f;
-                    if (!sp) { pb1 = row[b1]; pb2 = row[b2]; }
-                    float4 xa = *reinterpret_cast<const float4 *>(row + ab);
-                    float4 xb = *reinterpret_cast<const float4 *>(row + bb);
+                    for (int h = 0; h < 2; ++h) {
+                        const int pos = 2 * kk + h;
+                        position(pos);
 #pragma unroll
-                    for (int tt = 0; tt < TTH; ++tt) {
-                        float npa1 = 0.f, npa2 = 0.f, npb1 = 0.f, npb2 = 0.f;
-                        float4 nxa = {0.f, 0.f, 0.f, 0.f}, nxb = {0.f, 0.f, 0.f, 0.f};
-                        if (tt + 1 < TTH) {          // next tile's loads go out before this tile's math
-                            const float *nrow = Qs + (16 * (tt + 1) + li) * QS;
-                            npa1 = nrow[a1]; npa2 = nrow[a2];
-                            if (!sp) { npb1 = nrow[b1]; npb2 = nrow[b2]; }
-                            nxa = *reinterpret_cast<const float4 *>(nrow + ab);
-                            nxb = *reinterpret_cast<const float4 *>(nrow + bb);
+                        for (int tt = 0; tt < TPW; ++tt) {
+                            const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
+                            a[tt][4 * h + 0] = pz[tt][0] * x.x;
+                            a[tt][4 * h + 1] = pz[tt][1] * x.y;
+                            a[tt][4 * h + 2] = pz[tt][2] * x.z;
+                            a[tt][4 * h + 3] = pz[tt][3] * x.w;
                         }
-                        const float pa = pa1 * pa2;
-                        const float pb = sp ? pa : pb1 * pb2;
-                        float a[8] = {ca.x * xa.x, ca.y * xa.y, ca.z * xa.z, ca.w * xa.w,
-                                      cb.x * xb.x, cb.y * xb.y, cb.z * xb.z, cb.w * xb.w};
+                    }
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) { a[j] *= pa; a[4 + j] *= pb; }
-                        const bf16x8 A = pack_bf16x8(a);
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        const bf16x8 A = pack_bf16x8(a[tt]);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A, B[nt], Y[tt][nt]);
-                        pa1 = npa1; pa2 = npa2; pb1 = npb1; pb2 = npb2; xa = nxa; xb = nxb;
                     }
                 }
             } else {
-                // K step (j, r): lane group g holds slot r of quad wq0 + g*MT + j
+                const float *Bf = reinterpret_cast<const float *>(Bc);
+#pragma unroll 1
+                for (int pos = pbeg; pos < pbeg + NPH; ++pos) {
+                    position(pos);
+                    float a[TPW][4];
 #pragma unroll
-                for (int j = 0; j < MT; ++j) {
-                    const int qd = wq0 + g * MT + j;
-                    const uint32_t w = W0[qd];
-                    const float4 cq = QC[qd];
-                    const float cr[4] = {cq.x, cq.y, cq.z, cq.w};
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
+                        a[tt][0] = pz[tt][0] * x.x; a[tt][1] = pz[tt][1] * x.y;
+                        a[tt][2] = pz[tt][2] * x.z; a[tt][3] = pz[tt][3] * x.w;
+                    }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
+                        float B[NT];
 #pragma unroll
-                        for (int tt = 0; tt < TTH; ++tt) {
-                            const float *row = Qs + (16 * tt + li) * QS;
-                            const float a = cr[r] * row[qd_i1(w)] * row[qd_i2(w)] * row[4 * qd_b(w) + r];
+                        for (int nt = 0; nt < NT; ++nt) B[nt] = Bf[((pos * 4 + r) * NT + nt) * 64 + lane];
 #pragma unroll
-                            for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_f32(a, S[j][nt][r], Y[tt][nt]);
-                        }
+                        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_f32(a[tt][r], B[nt], Y[tt][nt]);
                     }
                 }
             }
-
-            f32x4 *mine = Yb + wave * YB;
+            if (half > 0) {                           // second K half: hand the partial to the first
 #pragma unroll
-            for (int tt = 0; tt < TTH; ++tt)
+                for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) mine[(tt * NT + nt) * 64 + lane] = Y[tt][nt];
-            __syncthreads();
-            if (wave < TTH) {
-                // partial layout per (bh, chunk, slice): [tt][c][16 tokens]; lane writes rows 4g..4g+3
-                float *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16);
-                const int tt = wave;
+                    for (int nt = 0; nt < NT; ++nt) YE[(((wave % TG) * TPW + tt) * NT + nt) * 64 + lane] = Y[tt][nt];
+            }
+        }
+        __syncthreads();                              // state copy and Qs no longer read; exchange written
+        if (half == 0) {
+            // partial layout per (bh, chunk, slice): [TT][NC][16 tokens]; lane writes rows 4g..4g+3
+            float *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
+                    f32x4 y = Y[tt][nt];
+                    if constexpr (Cfg::KH > 1) y += YE[(((wave % TG) * TPW + tt) * NT + nt) * 64 + lane];
                     const int c = 16 * nt + li;
-                    if (c < NC) {
-                        f32x4 y = Yb[(tt * NT + nt) * 64 + lane];
-#pragma unroll
-                        for (int w = 1; w < kNW; ++w) y += Yb[w * YB + (tt * NT + nt) * 64 + lane];
-                        *reinterpret_cast<f32x4 *>(pdst + ((int64_t)(hf * TTH + tt) * NC + c) * 16 + 4 * g) = y;
-                    }
+                    if (c < NC) *reinterpret_cast<f32x4 *>(pdst + ((int64_t)(tt0 + tt) * NC + c) * 16 + 4 * g) = y;
                 }
-            }
-            if (hf + 1 < Cfg::NH) __syncthreads();   // Yb and Qs are rewritten by the next pass
+        }
+
+        write_kv(rk, rv, chunk_nv(cc));
+        if (cc + 1 < nchunk) write_q(rq);
+        __syncthreads();
+        if (cc + 1 < nchunk) {                        // next chunk's k, v: in flight during the update
+            gload(rk, kh, cc + 1);
+            gload(rv, vh, cc + 1);
         }
 
         // ---- chunk state: S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1]
-        if constexpr (Cfg::BF) {
-            const bf16_t *Vt = reinterpret_cast<const bf16_t *>(lds + Cfg::OFF_V);
+        if constexpr (Cfg::BF && NW == 8) {
+            // Chunk's 32-token K steps outer, positions inner (register budget of two waves per
+            // SIMD); pair products are re-formed at each K step's first position and group starts.
+            const bf16_t *V16 = reinterpret_cast<const bf16_t *>(Vt);
 #pragma unroll 1
             for (int ks = 0; ks < C / 32; ++ks) {
                 const int tb = 32 * ks + 8 * g;
@@ -464,21 +596,22 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     uint4 u = {0u, 0u, 0u, 0u};
-                    if (16 * nt + li < NC) u = *reinterpret_cast<const uint4 *>(Vt + (16 * nt + li) * VS + tb);
+                    if (16 * nt + li < NC) u = *reinterpret_cast<const uint4 *>(V16 + (16 * nt + li) * VS + tb);
                     B[nt] = __builtin_bit_cast(bf16x8, u);
                 }
                 float p2[8];
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
-                    const uint32_t w = myW[j];
-                    if (j == 0 || qd_pair(w) != qd_pair(myW[j > 0 ? j - 1 : 0])) {   // per lane: new pair
+                    const uint32_t w = uw[j];
+                    if (j == 0 || ((newgrp >> j) & 1u)) {
+                        __asm__ volatile("" ::: "memory");
                         const float4 *k1 = reinterpret_cast<const float4 *>(Kt + qd_i1(w) * KS + tb);
                         const float4 *k2 = reinterpret_cast<const float4 *>(Kt + qd_i2(w) * KS + tb);
                         const float4 a0 = k1[0], a1 = k1[1], b0 = k2[0], b1 = k2[1];
                         p2[0] = a0.x * b0.x; p2[1] = a0.y * b0.y; p2[2] = a0.z * b0.z; p2[3] = a0.w * b0.w;
                         p2[4] = a1.x * b1.x; p2[5] = a1.y * b1.y; p2[6] = a1.z * b1.z; p2[7] = a1.w * b1.w;
                     }
-                    const float4 *k3 = reinterpret_cast<const float4 *>(Kt + (4 * qd_b(w) + (li & 3)) * KS + tb);
+                    const float4 *k3 = reinterpret_cast<const float4 *>(Kt + (4 * qd_b(w) + uz) * KS + tb);
                     const float4 c0 = k3[0], c1 = k3[1];
                     float a[8] = {p2[0] * c0.x, p2[1] * c0.y, p2[2] * c0.z, p2[3] * c0.w,
                                   p2[4] * c1.x, p2[5] * c1.y, p2[6] * c1.z, p2[7] * c1.w};
@@ -487,30 +620,83 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_bf16(A, B[nt], S[j][nt]);
                 }
             }
+        } else if constexpr (Cfg::BF) {
+            // Positions outer, the chunk's 32-token K steps inner: the [V | 1] operand tiles of the
+            // whole chunk stay in registers, and the pair products (per K step) are formed only where
+            // a pair group starts (the same positions for all four streams).
+            constexpr int NKS = C / 32;
+            const bf16_t *V16 = reinterpret_cast<const bf16_t *>(Vt);
+            bf16x8 B[NKS][NT];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    uint4 u = {0u, 0u, 0u, 0u};
+                    if (16 * nt + li < NC) u = *reinterpret_cast<const uint4 *>(V16 + (16 * nt + li) * VS + 32 * ks + 8 * g);
+                    B[ks][nt] = __builtin_bit_cast(bf16x8, u);
+                }
+            float p2[NKS][8];
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+                const uint32_t w = uw[j];
+                if (j == 0 || ((newgrp >> j) & 1u)) {
+                    __asm__ volatile("" ::: "memory");   // keep the reload behind its (uniform) branch
+                    const float *k1 = Kt + qd_i1(w) * KS + 8 * g;
+                    const float *k2 = Kt + qd_i2(w) * KS + 8 * g;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const float4 a0 = *reinterpret_cast<const float4 *>(k1 + 32 * ks);
+                        const float4 a1 = *reinterpret_cast<const float4 *>(k1 + 32 * ks + 4);
+                        const float4 b0 = *reinterpret_cast<const float4 *>(k2 + 32 * ks);
+                        const float4 b1 = *reinterpret_cast<const float4 *>(k2 + 32 * ks + 4);
+                        p2[ks][0] = a0.x * b0.x; p2[ks][1] = a0.y * b0.y; p2[ks][2] = a0.z * b0.z; p2[ks][3] = a0.w * b0.w;
+                        p2[ks][4] = a1.x * b1.x; p2[ks][5] = a1.y * b1.y; p2[ks][6] = a1.z * b1.z; p2[ks][7] = a1.w * b1.w;
+                    }
+                }
+                const float *k3 = Kt + (4 * qd_b(w) + uz) * KS + 8 * g;
+                float4 c[NKS][2];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    c[ks][0] = *reinterpret_cast<const float4 *>(k3 + 32 * ks);
+                    c[ks][1] = *reinterpret_cast<const float4 *>(k3 + 32 * ks + 4);
+                }
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    float a[8] = {p2[ks][0] * c[ks][0].x, p2[ks][1] * c[ks][0].y, p2[ks][2] * c[ks][0].z,
+                                  p2[ks][3] * c[ks][0].w, p2[ks][4] * c[ks][1].x, p2[ks][5] * c[ks][1].y,
+                                  p2[ks][6] * c[ks][1].z, p2[ks][7] * c[ks][1].w};
+                    const bf16x8 A = pack_bf16x8(a);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_bf16(A, B[ks][nt], S[j][nt]);
+                }
+            }
         } else {
-            const float *Vt = reinterpret_cast<const float *>(lds + Cfg::OFF_V);
+            const float *Vf = reinterpret_cast<const float *>(Vt);
 #pragma unroll 1
             for (int ks = 0; ks < C / 4; ++ks) {
                 const int tb = 4 * ks + g;
                 float B[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) B[nt] = 16 * nt + li < NC ? Vt[(16 * nt + li) * VS + tb] : 0.f;
+                for (int nt = 0; nt < NT; ++nt) B[nt] = 16 * nt + li < NC ? Vf[(16 * nt + li) * VS + tb] : 0.f;
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
-                    const uint32_t w = myW[j];
-                    const float a = Kt[qd_i1(w) * KS + tb] * Kt[qd_i2(w) * KS + tb] *
-                                    Kt[(4 * qd_b(w) + (li & 3)) * KS + tb];
+                    const uint32_t w = uw[j];
+                    const float a = Kt[qd_i1(w) * KS + tb] * Kt[qd_i2(w) * KS + tb] * Kt[(4 * qd_b(w) + uz) * KS + tb];
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_f32(a, B[nt], S[j][nt]);
                 }
             }
         }
+        __syncthreads();                              // Kt, Vt no longer read
+        write_bcopy();
+        if (cc + 2 < nchunk) gload(rq, qh, cc + 2);   // the chunk after next's q: in flight during the readout
+        __syncthreads();
     }
 
     // accumulators -> state slice
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-        const int64_t qd = qs0 + wq0 + g * MT + j;
+        const int64_t qd = (ps0 + p0 + j) * 4 + g;
         const uint32_t w = qw0[qd];
         const int32_t c0 = qcidx[qd];
         const uint32_t mask = qd_mask(w);
@@ -629,41 +815,49 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
 
 // ---------------------------------------------------------------- host side
 
-// Tiles per wavefront (16 features each, four quads): as many as the register
-// budget allows for the d_V + 1 columns, fewer when the head has few features.
-static int pick_mt(const sata_index *idx, int64_t bh) {
+// Wavefronts per workgroup and positions per wavefront (16 features each); a
+// slice holds NW * MT positions.  Four wavefronts with as many positions as the
+// register budget allows for the d_V + 1 columns, fewer when the grid would not
+// fill the chip.  The fp32 path keeps a 4-byte state copy in LDS, so it stops
+// at 4.  (The kernel also supports eight wavefronts of fewer positions each.)
+struct ScanShape {
+    int nw, mt;
+};
+static ScanShape pick_shape(const sata_index *idx, int64_t bh, int chunk, sata_dtype in_dt) {
+    const int64_t npos = idx->nq / 4;
     for (int mt : {8, 4}) {
-        const int64_t per = (int64_t)kNW * 4 * mt;
-        if (bh * ((idx->nq + per - 1) / per) >= 256) return mt;
+        if (mt == 8 && in_dt == SATA_F32) continue;
+        const int64_t per = (int64_t)kNW * mt;
+        if (bh * ((npos + per - 1) / per) >= 256) return {4, mt};
     }
-    return 2;
+    return {4, 2};
 }
 
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt) {
     PrefillPlan p;
-    (void)in_dt;
     p.chunk = chunk ? chunk : (idx->dk == 64 ? 128 : 64);
     if (p.chunk != 64 && p.chunk != 128) return p;
-    const int mt = pick_mt(idx, bh);
-    p.fw = 16 * mt;
-    p.fs = kNW * p.fw;
-    const int64_t nq_slice = (int64_t)kNW * 4 * mt;
-    p.slices = (int)((idx->nq + nq_slice - 1) / nq_slice);
+    const ScanShape sh = pick_shape(idx, bh, p.chunk, in_dt);
+    p.fw = 16 * sh.mt;
+    p.fs = sh.nw * p.fw;
+    const int64_t np_slice = (int64_t)sh.nw * sh.mt;
+    const int64_t npos = idx->nq / 4;
+    p.slices = (int)((npos + np_slice - 1) / np_slice);
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
     const int64_t per_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * 4;
     p.seg_chunks = std::max<int64_t>(1, std::min<int64_t>(nchunks, kWorkCap / per_chunk));
     p.work_bytes = p.seg_chunks * per_chunk;
-    p.ok = (int64_t)p.slices * nq_slice <= idx->nq_tab;
+    p.ok = (int64_t)p.slices * np_slice * 4 <= idx->nq_tab;
     return p;
 }
 
-template <int D, int C, int MT, typename TIn, typename TOut>
+template <int D, int C, int MT, int NW, typename TIn, typename TOut>
 static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                               const void *q, const void *k, const void *v, void *out, int64_t n,
                               hipStream_t stream) {
-    using Cfg = ScanCfg<D, D, C, MT, TIn>;
+    using Cfg = ScanCfg<D, D, C, MT, NW, TIn>;
     const int64_t bh = (int64_t)st->batch * st->heads;
-    auto scan = prefill_scan_kernel<D, D, C, MT, TIn>;
+    auto scan = prefill_scan_kernel<D, D, C, MT, NW, TIn>;
     auto red = prefill_reduce_kernel<D, D, C, TIn, TOut>;
     hipError_t e = hipFuncSetAttribute((const void *)scan, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
     if (e != hipSuccess) return e;
@@ -678,9 +872,9 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
         const int64_t tok0 = c0 * C;
         {
             ProfScope ps(kProfScan, stream);
-            hipLaunchKernelGGL(scan, dim3(plan.slices, (unsigned)bh), dim3(kThreads), Cfg::LDS, stream,
+            hipLaunchKernelGGL(scan, dim3(plan.slices, (unsigned)bh), dim3(Cfg::THREADS), Cfg::LDS, stream,
                                idx->d_qw0, idx->d_qcidx, reinterpret_cast<const float4 *>(idx->d_qcoef),
-                               st->d_state, idx->m_pad, static_cast<const TIn *>(q),
+                               idx->d_qflags, st->d_state, idx->m_pad, static_cast<const TIn *>(q),
                                static_cast<const TIn *>(k), static_cast<const TIn *>(v), n, tok0, nseg,
                                partial, ta.scale);
         }
@@ -698,16 +892,18 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     return hipSuccess;
 }
 
-template <int D, int C, int MT>
+template <int D, int C, int MT, int NW>
 static hipError_t run_dt(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                          const void *q, const void *k, const void *v, void *out, int64_t n,
                          sata_dtype in_dt, sata_dtype out_dt, hipStream_t s) {
-    if (in_dt == SATA_F32) {
-        if (out_dt == SATA_F32) return run_prefill<D, C, MT, float, float>(idx, st, plan, q, k, v, out, n, s);
-        return run_prefill<D, C, MT, float, bf16_t>(idx, st, plan, q, k, v, out, n, s);
+    if constexpr (MT > 4 || NW > 4) {
+        if (in_dt == SATA_F32) return hipErrorInvalidValue;   // pick_shape never plans this
+    } else if (in_dt == SATA_F32) {
+        if (out_dt == SATA_F32) return run_prefill<D, C, MT, NW, float, float>(idx, st, plan, q, k, v, out, n, s);
+        return run_prefill<D, C, MT, NW, float, bf16_t>(idx, st, plan, q, k, v, out, n, s);
     }
-    if (out_dt == SATA_F32) return run_prefill<D, C, MT, bf16_t, float>(idx, st, plan, q, k, v, out, n, s);
-    return run_prefill<D, C, MT, bf16_t, bf16_t>(idx, st, plan, q, k, v, out, n, s);
+    if (out_dt == SATA_F32) return run_prefill<D, C, MT, NW, bf16_t, float>(idx, st, plan, q, k, v, out, n, s);
+    return run_prefill<D, C, MT, NW, bf16_t, bf16_t>(idx, st, plan, q, k, v, out, n, s);
 }
 
 template <int D>
@@ -716,13 +912,13 @@ static hipError_t run_d(const sata_index *idx, const sata_state *st, const Prefi
                         sata_dtype in_dt, sata_dtype out_dt, hipStream_t s) {
     const int mt = plan.fw / 16;
     if (plan.chunk == 64) {
-        if (mt == 2) return run_dt<D, 64, 2>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-        if (mt == 4) return run_dt<D, 64, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-        return run_dt<D, 64, 8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        if (mt == 2) return run_dt<D, 64, 2, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        if (mt == 4) return run_dt<D, 64, 4, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        return run_dt<D, 64, 8, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
     }
-    if (mt == 2) return run_dt<D, 128, 2>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-    if (mt == 4) return run_dt<D, 128, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-    return run_dt<D, 128, 8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+    if (mt == 2) return run_dt<D, 128, 2, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+    if (mt == 4) return run_dt<D, 128, 4, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+    return run_dt<D, 128, 8, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
 }
 
 hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,

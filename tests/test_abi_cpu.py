@@ -108,33 +108,38 @@ def test_binding_rejects_cpu_tensors():
 
 
 @pytest.mark.parametrize("d,P", [(8, 1), (8, 2), (8, 3), (16, 4), (32, 4), (64, 4)])
-def test_quads_cover_the_features_in_order(d, P):
-    """Every valid quad slot is exactly the feature (i1, i2, 4b+z) with the same
-    readout weight as the feature table; valid slots are consecutive features;
-    padding slots carry weight 0."""
+def test_quads_cover_every_feature_once(d, P):
+    """Every valid quad slot is the feature (i1, i2, 4b+z) at state index
+    cidx + (z - first valid slot), with the feature table's readout weight;
+    together the valid slots cover every feature exactly once; padding slots
+    carry weight 0; the four quads of a position share the block b."""
     from constant_cost_attention_amd import sata
     tup, coef = sata.sata_describe_features(d, P)
     w0, cidx, qc = sata.sata_describe_quads(d, P)
+    assert len(w0) % 4 == 0
     slots = np.stack([(tup >> (8 * r)) & 0xFF for r in range(3)], axis=1).astype(np.int64)
     order = (tup >> 24).astype(np.int64)
-    f = 0
+    seen = np.zeros(len(tup), dtype=np.int64)
     for q in range(len(w0)):
         i1, i2, b, mask = int(w0[q] & 0xFF), int((w0[q] >> 8) & 0xFF), int((w0[q] >> 16) & 0xFF), int(w0[q] >> 24)
-        if mask:
-            assert cidx[q] == f
+        assert b == int((w0[q - q % 4] >> 16) & 0xFF)
+        if not mask:
+            assert cidx[q] == -1
+            assert np.all(qc[q] == 0)
+            continue
+        z0 = (mask & -mask).bit_length() - 1
         for z in range(4):
             if not (mask >> z) & 1:
                 assert qc[q, z] == 0
                 continue
-            # the feature this slot stands for, with absent indices dropped
+            f = int(cidx[q]) + z - z0
             idx = [i for i in (i1, i2) if i < d]
             if b * 4 < d:
                 idx.append(4 * b + z)
             want = sorted(idx)
             assert idx == want
-            got = [int(x) for x in slots[f, :order[f]]]
-            assert got == want, (q, z, got, want)
+            assert [int(x) for x in slots[f, :order[f]]] == want, (q, z, want)
             # quad weight = multinomial part; the feature weight also carries d^(-p/2)
             assert abs(qc[q, z] / math.sqrt(d) ** len(want) - coef[f]) <= 1e-6 * coef[f]
-            f += 1
-    assert f == len(tup)
+            seen[f] += 1
+    assert np.all(seen == 1)
