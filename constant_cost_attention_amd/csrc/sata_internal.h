@@ -85,6 +85,8 @@ struct PrefillPlan {
     int fs = 0;             // features per workgroup slice
     int slices = 0;         // workgroups per head
     int64_t seg_chunks = 0; // chunks per segment (bounded by the workspace cap)
+    int64_t sync_off = 0;   // byte offset of the scan's counter and progress flags in the workspace
+    int64_t sync_words = 0; // their count (a multiple of 4)
     int64_t work_bytes = 0; // workspace needed
     bool ok = false;
 };
@@ -105,6 +107,7 @@ struct ProfScope {
     hipEvent_t start = nullptr;
 };
 
+hipError_t launch_zero(float *p, int64_t count, hipStream_t stream);
 hipError_t launch_expand(const sata_index *idx, const void *x, void *out, int64_t rows, int side,
                          sata_dtype in_dt, hipStream_t stream);
 

@@ -37,6 +37,10 @@
 //            engineering a constant per-token cost" (2026-02-05).
 #include <algorithm>
 
+#ifndef UPDATE_KS_OUTER
+#define UPDATE_KS_OUTER 0
+#endif
+
 #include "sata_device.h"
 #include "sata_internal.h"
 
@@ -49,6 +53,9 @@ template <int D, int DV, int C, int MT, int NW, typename TIn>
 struct ScanCfg {
     static constexpr bool BF = sizeof(TIn) == 2;
     static constexpr int THREADS = 64 * NW;       // NW wavefronts (4 or 8)
+    // Persistent scheduling for the smaller heads; the d_K = 64 kernel, at the edge of its
+    // register budget, runs one workgroup per work item.
+    static constexpr bool PERSIST = D <= 32;
     static constexpr int NP = NW * MT;            // positions (4 quads, 16 features) per slice
     static constexpr int NC = DV + 1;             // value columns + normaliser
     static constexpr int NT = (NC + 15) / 16;     // 16-column MFMA tiles
@@ -253,7 +260,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                          const float4 *__restrict__ qcoef, const uint32_t *__restrict__ qflags,
                          float *__restrict__ state, int64_t m_pad,
                          const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-                         int64_t n, int64_t tok0, int nchunk, float *__restrict__ partial, float qscale) {
+                         int64_t n, int64_t tok0, int nchunk, float *__restrict__ partial, float qscale,
+                         int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync) {
     using Cfg = ScanCfg<D, DV, C, MT, NW, TIn>;
     constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TPW = Cfg::TPW, NP = Cfg::NP, NPH = Cfg::NPH;
     constexpr int kThreads = Cfg::THREADS;
@@ -269,12 +277,46 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     uint32_t *QF = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_F);   // [NP]
     f32x4 *YE = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_E);         // [TG][TPW][NT][64]
 
-    const int slice = blockIdx.x, nslices = gridDim.x;
-    const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
-    const int64_t ps0 = (int64_t)slice * NP;          // first position of the slice
     const int p0 = wave * MT;                         // this wave's first position within the slice
+    __shared__ int64_t s_item;
+
+    // Work items are (sub-segment u, head bh, slice), u-major.  With a grid of one workgroup per
+    // item (nsub = 1) the item is the block index.  Otherwise persistent workgroups take items
+    // from a counter; item (u, bh, slice) continues the state left by (u - 1, bh, slice), which
+    // was taken earlier by a running workgroup, and its flag (the number of finished
+    // sub-segments, released at agent scope) is awaited with a bounded spin.
+    const int64_t per_sub = nbh * nslices;
+    const int64_t nitems = per_sub * nsub;
+    for (int64_t pass = 0;; ++pass) {
+    int64_t item;
+    if constexpr (Cfg::PERSIST) {
+        if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u);
+        __syncthreads();
+        item = s_item;
+        __syncthreads();
+    } else {
+        item = pass == 0 ? (int64_t)blockIdx.x : nitems;
+    }
+    if (item >= nitems) break;
+    const int u = (int)(item / per_sub);
+    const int64_t rem = item % per_sub;
+    const int64_t bh = rem / nslices;
+    const int slice = (int)(rem % nslices);
+    const int cbeg = u * sub_chunks;
+    const int cend = cbeg + sub_chunks < nchunk ? cbeg + sub_chunks : nchunk;
+    if (Cfg::PERSIST && u > 0) {
+        if (tid == 0) {
+            for (int spin = 0; spin < (1 << 24); ++spin) {
+                if (__hip_atomic_load(&sync[1 + rem], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)u) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    const int64_t ps0 = (int64_t)slice * NP;          // first position of the slice
     // Tile j of this wave is position p0 + j; its rows 4s + z are stream s, slot z.  The lane's
     // accumulator rows (4g + r) are stream g; its update row (li) is stream li/4, slot li%4.
 
@@ -429,12 +471,12 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     };
 
     uint4 rk[UPT], rv[UPT], rq[UPT];
-    if (nchunk > 0) {
-        gload(rk, kh, 0);
-        gload(rv, vh, 0);
-        gload(rq, qh, 0);
+    if (cbeg < cend) {
+        gload(rk, kh, cbeg);
+        gload(rv, vh, cbeg);
+        gload(rq, qh, cbeg);
         write_q(rq);
-        if (nchunk > 1) gload(rq, qh, 1);
+        if (cbeg + 1 < cend) gload(rq, qh, cbeg + 1);
     }
     write_bcopy();
     __syncthreads();
@@ -443,7 +485,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     const int tt0 = (wave % TG) * TPW;                // this wave's readout token tiles
     const int half = wave / TG;                       // and K half: positions [half * NPH, (half + 1) * NPH)
     const int pbeg = half * NPH;
-    for (int cc = 0; cc < nchunk; ++cc) {
+    for (int cc = cbeg; cc < cend; ++cc) {
         // ---- inter-chunk readout Y = psi(Q_c)[:, slice] . S^(c-1)[slice, :] for this wave's tiles,
         //      over its half of the slice's positions (state operand from LDS)
         f32x4 Y[TPW][NT];
@@ -577,17 +619,17 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         }
 
         write_kv(rk, rv, chunk_nv(cc));
-        if (cc + 1 < nchunk) write_q(rq);
+        if (cc + 1 < cend) write_q(rq);
         __syncthreads();
-        if (cc + 1 < nchunk) {                        // next chunk's k, v: in flight during the update
+        if (cc + 1 < cend) {                          // next chunk's k, v: in flight during the update
             gload(rk, kh, cc + 1);
             gload(rv, vh, cc + 1);
         }
 
         // ---- chunk state: S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1]
-        if constexpr (Cfg::BF && NW == 8) {
-            // Chunk's 32-token K steps outer, positions inner (register budget of two waves per
-            // SIMD); pair products are re-formed at each K step's first position and group starts.
+        if constexpr (Cfg::BF && (NW == 8 || UPDATE_KS_OUTER)) {
+            // Chunk's 32-token K steps outer, positions inner (smaller register footprint); pair
+            // products are re-formed at each K step's first position and at group starts.
             const bf16_t *V16 = reinterpret_cast<const bf16_t *>(Vt);
 #pragma unroll 1
             for (int ks = 0; ks < C / 32; ++ks) {
@@ -689,7 +731,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         }
         __syncthreads();                              // Kt, Vt no longer read
         write_bcopy();
-        if (cc + 2 < nchunk) gload(rq, qh, cc + 2);   // the chunk after next's q: in flight during the readout
+        if (cc + 2 < cend) gload(rq, qh, cc + 2);     // the chunk after next's q: in flight during the readout
         __syncthreads();
     }
 
@@ -708,6 +750,13 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 const int c = 16 * nt + li;
                 if (((mask >> r) & 1u) && c < NC) Sh[(int64_t)c * m_pad + c0 + (r - z0)] = S[j][nt][r];
             }
+    }
+    if constexpr (Cfg::PERSIST) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this thread's state stores, then the flag
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(&sync[1 + rem], (uint32_t)(u + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
     }
 }
 
@@ -846,7 +895,10 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
     const int64_t per_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * 4;
     p.seg_chunks = std::max<int64_t>(1, std::min<int64_t>(nchunks, kWorkCap / per_chunk));
-    p.work_bytes = p.seg_chunks * per_chunk;
+    // after the partial sums: the scan's work counter and one progress flag per (head, slice)
+    p.sync_off = (p.seg_chunks * per_chunk + 255) / 256 * 256;
+    p.sync_words = (1 + bh * p.slices + 3) / 4 * 4;
+    p.work_bytes = p.sync_off + p.sync_words * 4;
     p.ok = (int64_t)p.slices * np_slice * 4 <= idx->nq_tab;
     return p;
 }
@@ -867,16 +919,37 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     ta.P = idx->P;
     const int64_t nchunks = (n + C - 1) / C;
     float *partial = static_cast<float *>(st->d_work);
+    uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(st->d_work) + plan.sync_off);
+    // Persistent grid: as many workgroups as fit on the device at once.
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, st->device);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan, Cfg::THREADS, Cfg::LDS);
+    if (e != hipSuccess) return e;
+    const int64_t resident = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+    const int64_t items0 = bh * plan.slices;
     for (int64_t c0 = 0; c0 < nchunks; c0 += plan.seg_chunks) {
         const int nseg = (int)std::min<int64_t>(plan.seg_chunks, nchunks - c0);
         const int64_t tok0 = c0 * C;
+        // Split the segment into sub-segments of at least 16 chunks until there are about a dozen
+        // items per resident workgroup, so every CU gets the same share of the work (a grid of
+        // at most one workgroup per CU gains nothing from splitting).
+        int nsub = !Cfg::PERSIST || items0 <= cus ? 1
+                 : (int)std::min<int64_t>((12 * resident + items0 - 1) / items0, std::max(1, nseg / 16));
+        const int sub_chunks = (nseg + nsub - 1) / nsub;
+        nsub = (nseg + sub_chunks - 1) / sub_chunks;
+        const int64_t grid = Cfg::PERSIST ? std::min<int64_t>(items0 * nsub, resident) : items0;
+        if (Cfg::PERSIST) {
+            e = launch_zero(reinterpret_cast<float *>(sync), plan.sync_words, stream);
+            if (e != hipSuccess) return e;
+        }
         {
             ProfScope ps(kProfScan, stream);
-            hipLaunchKernelGGL(scan, dim3(plan.slices, (unsigned)bh), dim3(Cfg::THREADS), Cfg::LDS, stream,
+            hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(Cfg::THREADS), Cfg::LDS, stream,
                                idx->d_qw0, idx->d_qcidx, reinterpret_cast<const float4 *>(idx->d_qcoef),
                                idx->d_qflags, st->d_state, idx->m_pad, static_cast<const TIn *>(q),
                                static_cast<const TIn *>(k), static_cast<const TIn *>(v), n, tok0, nseg,
-                               partial, ta.scale);
+                               partial, ta.scale, plan.slices, bh, nsub, sub_chunks, sync);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
