@@ -254,13 +254,31 @@ __device__ __forceinline__ void unpack_unit(const uint4 u, float (&x)[16 / sizeo
     }
 }
 
+// Readout partials are kept in the input dtype's width: fp32 for fp32 inputs,
+// bf16 for bf16 inputs (the operands of the readout are bf16 there already;
+// the partials are summed in fp32).
+template <typename TIn> struct PartialOf { using type = float; };
+template <> struct PartialOf<bf16_t> { using type = bf16_t; };
+
+__device__ __forceinline__ void store4(float *p, f32x4 y) { *reinterpret_cast<f32x4 *>(p) = y; }
+__device__ __forceinline__ void store4(bf16_t *p, f32x4 y) {
+    *reinterpret_cast<uint2 *>(p) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+}
+__device__ __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4(const bf16_t *p) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+
 template <int D, int DV, int C, int MT, int NW, typename TIn>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
                          const float4 *__restrict__ qcoef, const uint32_t *__restrict__ qflags,
                          float *__restrict__ state, int64_t m_pad,
                          const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-                         int64_t n, int64_t tok0, int nchunk, float *__restrict__ partial, float qscale,
+                         int64_t n, int64_t tok0, int nchunk, typename PartialOf<TIn>::type *__restrict__ partial,
+                         float qscale,
                          int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync) {
     using Cfg = ScanCfg<D, DV, C, MT, NW, TIn>;
     constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TPW = Cfg::TPW, NP = Cfg::NP, NPH = Cfg::NPH;
@@ -606,7 +624,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         __syncthreads();                              // state copy and Qs no longer read; exchange written
         if (half == 0) {
             // partial layout per (bh, chunk, slice): [TT][NC][16 tokens]; lane writes rows 4g..4g+3
-            float *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16);
+            auto *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16);
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
@@ -614,7 +632,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     f32x4 y = Y[tt][nt];
                     if constexpr (Cfg::KH > 1) y += YE[(((wave % TG) * TPW + tt) * NT + nt) * 64 + lane];
                     const int c = 16 * nt + li;
-                    if (c < NC) *reinterpret_cast<f32x4 *>(pdst + ((int64_t)(tt0 + tt) * NC + c) * 16 + 4 * g) = y;
+                    if (c < NC) store4(pdst + ((int64_t)(tt0 + tt) * NC + c) * 16 + 4 * g, y);
                 }
         }
 
@@ -767,7 +785,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
 // tiles w and C/16-1-w (tile qt needs qt+1 key tiles, so each wave does
 // C/16+1 tiles' worth).
 template <int D, int DV, int C, typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__restrict__ partial, int nslices,
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename PartialOf<TIn>::type *__restrict__ partial,
+                                                             int nslices,
                                                              int nchunk, int64_t n, int64_t tok0,
                                                              const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                              const TIn *__restrict__ v, TOut *__restrict__ out,
@@ -790,19 +809,19 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
     const TIn *vh = v + bh * n * DV;
 
     // partial sums first: their loads are the long pole, issue them before the MFMA work
-    const float4 *base = reinterpret_cast<const float4 *>(partial) + (bh * nchunk + cc) * (int64_t)nslices * NV;
+    const auto *base = partial + (bh * nchunk + cc) * (int64_t)nslices * NV * 4;   // NV groups of 4 per slice
     float4 acc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = float4{0.f, 0.f, 0.f, 0.f};
     int s = 0;
     for (; s + 1 < nslices; s += 2) {
-        const float4 *p0 = base + (int64_t)s * NV, *p1 = p0 + NV;
+        const auto *p0 = base + (int64_t)s * NV * 4, *p1 = p0 + NV * 4;
         float4 a[PER], b[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 256 * j;
-            a[j] = i < NV ? p0[i] : float4{0.f, 0.f, 0.f, 0.f};
-            b[j] = i < NV ? p1[i] : float4{0.f, 0.f, 0.f, 0.f};
+            a[j] = i < NV ? load4(p0 + 4 * i) : float4{0.f, 0.f, 0.f, 0.f};
+            b[j] = i < NV ? load4(p1 + 4 * i) : float4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -811,12 +830,12 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
         }
     }
     if (s < nslices) {
-        const float4 *p0 = base + (int64_t)s * NV;
+        const auto *p0 = base + (int64_t)s * NV * 4;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 256 * j;
             if (i < NV) {
-                const float4 a = p0[i];
+                const float4 a = load4(p0 + 4 * i);
                 acc[j].x += a.x; acc[j].y += a.y; acc[j].z += a.z; acc[j].w += a.w;
             }
         }
@@ -893,7 +912,8 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     const int64_t npos = idx->nq / 4;
     p.slices = (int)((npos + np_slice - 1) / np_slice);
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
-    const int64_t per_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * 4;
+    const int64_t pbytes = in_dt == SATA_BF16 ? 2 : 4;   // readout partials in the input's width
+    const int64_t per_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * pbytes;
     p.seg_chunks = std::max<int64_t>(1, std::min<int64_t>(nchunks, kWorkCap / per_chunk));
     // after the partial sums: the scan's work counter and one progress flag per (head, slice)
     p.sync_off = (p.seg_chunks * per_chunk + 255) / 256 * 256;
@@ -918,7 +938,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     ta.c0 = idx->taylor[0]; ta.c1 = idx->taylor[1]; ta.c2 = idx->taylor[2]; ta.c3 = idx->taylor[3];
     ta.P = idx->P;
     const int64_t nchunks = (n + C - 1) / C;
-    float *partial = static_cast<float *>(st->d_work);
+    auto *partial = static_cast<typename PartialOf<TIn>::type *>(st->d_work);
     uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(st->d_work) + plan.sync_off);
     // Persistent grid: as many workgroups as fit on the device at once.
     int cus = 0, per_cu = 0;
