@@ -53,9 +53,8 @@ template <int D, int DV, int C, int MT, int NW, typename TIn>
 struct ScanCfg {
     static constexpr bool BF = sizeof(TIn) == 2;
     static constexpr int THREADS = 64 * NW;       // NW wavefronts (4 or 8)
-    // Persistent scheduling for the smaller heads; the d_K = 64 kernel, at the edge of its
-    // register budget, runs one workgroup per work item.
-    static constexpr bool PERSIST = D <= 32;
+    // Persistent scheduling (see the kernel); one workgroup per item when false.
+    static constexpr bool PERSIST = true;
     static constexpr int NP = NW * MT;            // positions (4 quads, 16 features) per slice
     static constexpr int NC = DV + 1;             // value columns + normaliser
     static constexpr int NT = (NC + 15) / 16;     // 16-column MFMA tiles
@@ -82,7 +81,13 @@ struct ScanCfg {
     static constexpr int OFF_QC = OFF_W + NP * 4 * 4;    // quad weights [NP][4] float4
     static constexpr int OFF_F = OFF_QC + NP * 4 * 16;   // position flags [NP]
     static constexpr int OFF_E = OFF_F + NP * 4;         // readout exchange of the second K half
-    static constexpr int LDS = OFF_E + (KH - 1) * TG * TPW * NT * 64 * 16;
+    static constexpr int OFF_R = OFF_E + (KH - 1) * TG * TPW * NT * 64 * 16;
+    // bf16 inputs: the next chunk's k and v arrive by direct global -> LDS loads into a raw
+    // buffer of 1 KB blocks; block s holds 64 consecutive tokens x one 16-byte unit of dims.
+    static constexpr bool DMA = BF;
+    static constexpr int DB = D / (16 / ES);             // 16-byte units per token
+    static constexpr int NSB = C / 64 * DB;              // blocks per tensor
+    static constexpr int LDS = OFF_R + (DMA ? 2 * NSB * 1024 : 0);
     // Prefetch of one chunk's q, k or v: 16-byte units per thread.
     static constexpr int EPU = 16 / ES;                  // elements per unit
     static constexpr int UNITS = C * D / EPU;
@@ -92,7 +97,7 @@ struct ScanCfg {
     static_assert(C % 64 == 0 && TG * KH == NW && KH <= 2, "readout split: 64 or 128 tokens per chunk");
     static_assert(!BF || NPH % 2 == 0, "bf16 K steps pair two positions");
     static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
-    static_assert(OFF_E % 16 == 0, "alignment");
+    static_assert(OFF_E % 16 == 0 && OFF_R % 16 == 0, "alignment");
     static_assert(OFF_Q % 16 == 0 && OFF_QC % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -294,6 +299,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     float4 *QC = reinterpret_cast<float4 *>(lds + Cfg::OFF_QC);      // [NP][4]
     uint32_t *QF = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_F);   // [NP]
     f32x4 *YE = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_E);         // [TG][TPW][NT][64]
+    uint4 *Raw = reinterpret_cast<uint4 *>(lds + Cfg::OFF_R);        // [2][NSB][64] (bf16 inputs)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
@@ -449,6 +455,53 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
             else reinterpret_cast<float *>(Vt)[DV * VS + t] = t < nv ? 1.f : 0.f;
         }
     };
+    // bf16: issue the chunk's k and v as direct global -> LDS loads (no registers held); lanes
+    // of block s take 64 consecutive tokens, so the later transposing read is conflict-free.
+    auto dma_kv = [&](int cc) {
+        if constexpr (Cfg::DMA) {
+            constexpr int DB = Cfg::DB, NSB = Cfg::NSB;
+            const int64_t t0 = chunk_t0(cc);
+            const int nv = chunk_nv(cc);
+            for (int sb = wave; sb < NSB; sb += NW) {
+                const int t = (sb / DB) * 64 + lane;
+                const int d0 = (sb % DB) * EPU;
+                if (t < nv) {
+                    __builtin_amdgcn_global_load_lds((const void *)(kh + (t0 + t) * D + d0),
+                                                     (__attribute__((address_space(3))) void *)(Raw + sb * 64), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds((const void *)(vh + (t0 + t) * D + d0),
+                                                     (__attribute__((address_space(3))) void *)(Raw + (NSB + sb) * 64),
+                                                     16, 0, 0);
+                }
+            }
+        }
+    };
+    auto write_kv_raw = [&](int nv) {               // raw blocks -> Kt (fp32), Vt (bf16), dim-major
+        if constexpr (Cfg::DMA) {
+            constexpr int DB = Cfg::DB, NSB = Cfg::NSB;
+            uint16_t *V16 = reinterpret_cast<uint16_t *>(Vt);
+            for (int i = tid; i < NSB * 64; i += kThreads) {
+                const int sb = i / 64, t = (sb / DB) * 64 + (i % 64), d0 = (sb % DB) * EPU;
+                const bool ok = t < nv;
+                const uint4 uk = ok ? Raw[i] : uint4{0u, 0u, 0u, 0u};
+                const uint4 uv = ok ? Raw[NSB * 64 + i] : uint4{0u, 0u, 0u, 0u};
+                float x[EPU];
+                unpack_unit<TIn>(uk, x);
+#pragma unroll
+                for (int e = 0; e < EPU; ++e) Kt[(d0 + e) * KS + t] = x[e];
+                const uint32_t w[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    V16[(d0 + 2 * e) * VS + t] = (uint16_t)(w[e] & 0xffffu);
+                    V16[(d0 + 2 * e + 1) * VS + t] = (uint16_t)(w[e] >> 16);
+                }
+            }
+            for (int t = tid; t < C; t += kThreads) {
+                Kt[D * KS + t] = 1.f;
+                Kt[(D + 1) * KS + t] = 0.f; Kt[(D + 2) * KS + t] = 0.f; Kt[(D + 3) * KS + t] = 0.f;
+                reinterpret_cast<bf16_t *>(Vt)[DV * VS + t] = from_f32<bf16_t>(t < nv ? 1.f : 0.f);
+            }
+        }
+    };
     // state accumulators -> readout operand copy in LDS (this wave's K steps)
     auto write_bcopy = [&]() {
         if constexpr (Cfg::BF) {
@@ -488,10 +541,14 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         }
     };
 
-    uint4 rk[UPT], rv[UPT], rq[UPT];
+    uint4 rk[Cfg::DMA ? 1 : UPT], rv[Cfg::DMA ? 1 : UPT], rq[UPT];
     if (cbeg < cend) {
-        gload(rk, kh, cbeg);
-        gload(rv, vh, cbeg);
+        if constexpr (Cfg::DMA) {
+            dma_kv(cbeg);
+        } else {
+            gload(rk, kh, cbeg);
+            gload(rv, vh, cbeg);
+        }
         gload(rq, qh, cbeg);
         write_q(rq);
         if (cbeg + 1 < cend) gload(rq, qh, cbeg + 1);
@@ -621,7 +678,11 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     for (int nt = 0; nt < NT; ++nt) YE[(((wave % TG) * TPW + tt) * NT + nt) * 64 + lane] = Y[tt][nt];
             }
         }
+        if constexpr (Cfg::DMA) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this chunk's k, v in LDS
         __syncthreads();                              // state copy and Qs no longer read; exchange written
+        if constexpr (Cfg::DMA) write_kv_raw(chunk_nv(cc));
+        else write_kv(rk, rv, chunk_nv(cc));
+        if (cc + 1 < cend) write_q(rq);
         if (half == 0) {
             // partial layout per (bh, chunk, slice): [TT][NC][16 tokens]; lane writes rows 4g..4g+3
             auto *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16);
@@ -635,13 +696,14 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     if (c < NC) store4(pdst + ((int64_t)(tt0 + tt) * NC + c) * 16 + 4 * g, y);
                 }
         }
-
-        write_kv(rk, rv, chunk_nv(cc));
-        if (cc + 1 < cend) write_q(rq);
         __syncthreads();
         if (cc + 1 < cend) {                          // next chunk's k, v: in flight during the update
-            gload(rk, kh, cc + 1);
-            gload(rv, vh, cc + 1);
+            if constexpr (Cfg::DMA) {
+                dma_kv(cc + 1);
+            } else {
+                gload(rk, kh, cc + 1);
+                gload(rv, vh, cc + 1);
+            }
         }
 
         // ---- chunk state: S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1]
