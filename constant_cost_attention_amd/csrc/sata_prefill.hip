@@ -337,8 +337,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 __builtin_amdgcn_s_sleep(2);
             }
         }
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();   // thread 0's acquire invalidated the caches every wave reads through
     }
     const int64_t ps0 = (int64_t)slice * NP;          // first position of the slice
     // Tile j of this wave is position p0 + j; its rows 4s + z are stream s, slot z.  The lane's
@@ -832,7 +831,9 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
             }
     }
     if constexpr (Cfg::PERSIST) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this thread's state stores, then the flag
+        // every wave's state stores reach L2 before the barrier; thread 0's agent-scope release
+        // then writes L2 back before the flag
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         __syncthreads();
         if (tid == 0)
             __hip_atomic_store(&sync[1 + rem], (uint32_t)(u + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
