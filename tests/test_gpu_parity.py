@@ -191,6 +191,33 @@ def test_state_content_matches_definition(sata):
     assert np.all(S[:, m:] == 0)
 
 
+def test_many_heads_subsegment_handoff(sata, oracle):
+    """320 heads x 4096 tokens (d=16, fp32, chunk 128): more scan work items
+    than CUs, so each slice's 32 chunks run as two sub-segments whose state
+    is handed over through memory between workgroups.  Sampled rows of four
+    heads and two decode steps that continue from the handed-over state are
+    held to the fp32 bar."""
+    d, P, n, t, nh = 16, 4, 4096, 2, 320
+    x = si.draw_qkv((1, nh), n + t, d, d, 4242, "f32")
+    heads = [0, 101, 202, nh - 1]
+    rows = sample_rows(n, 128, 48, 77)
+    idx = sata.Index(d, d, P)
+    st = sata.State(idx, 1, nh)
+    q, k, v = dev_all(x)
+    say("sub-segment handoff: %d heads x %d tokens" % (nh, n))
+    o = prefill(idx, st, q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous(), chunk=128)
+    od = [decode(idx, st, q[:, :, i].contiguous(), k[:, :, i].contiguous(), v[:, :, i].contiguous())
+          for i in range(n, n + t)]
+    got = o.cpu().numpy()[:, heads][:, :, rows]
+    sub = lambda a: np.ascontiguousarray(a[:, heads])
+    ref = oracle.taylor_attention(sub(x.q), sub(x.k), sub(x.v), P, rows=np.concatenate([rows, np.arange(n, n + t)]))
+    err = rel_err(got, ref[:, :, :len(rows)])
+    gotd = torch.stack(od, dim=2).cpu().numpy()[:, heads]
+    errd = rel_err(gotd, ref[:, :, len(rows):])
+    say("  err %.3e, decode err %.3e" % (err, errd))
+    assert err <= TOL_F32 and errd <= TOL_F32
+
+
 def test_deterministic_and_checkpoint_restore(sata):
     d, P, n = 32, 4, 300
     x = si.draw_qkv((2, 2), n + 4, d, d, 8080, "f32")
