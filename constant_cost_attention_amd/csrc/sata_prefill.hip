@@ -301,7 +301,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     f32x4 *YE = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_E);         // [TG][TPW][NT][64]
     uint4 *Raw = reinterpret_cast<uint4 *>(lds + Cfg::OFF_R);        // [2][NSB][64] (bf16 inputs)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
     const int g = lane >> 4, li = lane & 15;
     const int p0 = wave * MT;                         // this wave's first position within the slice
     __shared__ int64_t s_item;
@@ -501,42 +502,41 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
             }
         }
     };
-    // state accumulators -> readout operand copy in LDS (this wave's K steps)
+    // state accumulators -> readout operand copy in LDS (this wave's positions).  The copy
+    // carries the slot weight relative to the pair weight: 1 except at a group's first position
+    // (diagonal and invalid slots), so the readout forms every position alike.
+    auto slot_ratio = [&](int p, float (&r4)[4]) {
+        const float4 cq = QC[p * 4 + g];
+        const uint32_t w = W0[p * 4 + g];
+        const float rinv = (qd_i1(w) == qd_i2(w) && qd_i1(w) < D) ? 2.f : 1.f;
+        r4[0] = cq.x * rinv; r4[1] = cq.y * rinv; r4[2] = cq.z * rinv; r4[3] = cq.w * rinv;
+    };
     auto write_bcopy = [&]() {
-        if constexpr (Cfg::BF) {
-            // position p fills half p % 2 of K step p / 2 (8 bytes per lane): whole K steps when
-            // this wave's first position is even, else a leading and a trailing half step
-            if constexpr (MT % 2 == 0) {
-                if (p0 % 2 == 0) {
 #pragma unroll
-                    for (int kk = 0; kk < MT / 2; ++kk)
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            float b[8];
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) { b[r] = S[2 * kk][nt][r]; b[4 + r] = S[2 * kk + 1][nt][r]; }
-                            const int ks = p0 / 2 + kk;
-                            *reinterpret_cast<bf16x8 *>(Bc + ((ks * NT + nt) * 64 + lane) * 16) = pack_bf16x8(b);
-                        }
-                    return;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < MT; ++j)
+        for (int j = 0; j < MT; ++j) {
+            const int p = p0 + j;
+            float r4[4] = {1.f, 1.f, 1.f, 1.f};
+            const bool mixed = (nmask >> p) & 1u;
+            if (mixed) slot_ratio(p, r4);
+            if constexpr (Cfg::BF) {
+                // K step p / 2; reader lane group 2 (p % 2) + g / 2, elements 4 (g % 2) .. + 3
+                const int kk = p >> 1, gr = 2 * (p & 1) + (g >> 1);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const int p = p0 + j;
-                    const uint2 h = {pack_bf16x2(S[j][nt][0], S[j][nt][1]), pack_bf16x2(S[j][nt][2], S[j][nt][3])};
-                    *reinterpret_cast<uint2 *>(Bc + (((p / 2) * NT + nt) * 64 + lane) * 16 + (p % 2) * 8) = h;
+                    uint2 h;
+                    if (mixed) h = {pack_bf16x2(S[j][nt][0] * r4[0], S[j][nt][1] * r4[1]),
+                                    pack_bf16x2(S[j][nt][2] * r4[2], S[j][nt][3] * r4[3])};
+                    else h = {pack_bf16x2(S[j][nt][0], S[j][nt][1]), pack_bf16x2(S[j][nt][2], S[j][nt][3])};
+                    *reinterpret_cast<uint2 *>(Bc + ((kk * NT + nt) * 64 + gr * 16 + li) * 16 + (g & 1) * 8) = h;
                 }
-        } else {
-#pragma unroll
-            for (int j = 0; j < MT; ++j)
+            } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-                        reinterpret_cast<float *>(Bc)[(((p0 + j) * 4 + r) * NT + nt) * 64 + lane] = S[j][nt][r];
+                        reinterpret_cast<float *>(Bc)[((p * 4 + r) * NT + nt) * 64 + lane] =
+                            mixed ? S[j][nt][r] * r4[r] : S[j][nt][r];
+            }
         }
     };
 
@@ -571,92 +571,101 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
             const float *qrow[TPW];
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt) qrow[tt] = Qs + (16 * (tt0 + tt) + li) * QS;
-            float pcur[TPW];                          // pair weight * q_i1 * q_i2 of stream g
-            float pz[TPW][4];                         // per-slot factor: pcur, times the slot weight ratio
-            int xo = 0;                               // 4 b: the position's block of q
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) {
-                pcur[tt] = 0.f;
-#pragma unroll
-                for (int z = 0; z < 4; ++z) pz[tt][z] = 0.f;
-            }
-            // Within a pair group the block advances by one per position, so only group starts
-            // (uniform bit masks) read the quad tables; the rest of the loop has fixed addresses.
-            // Mixed-weight positions are group starts; the position after one restores pz.
-            auto position = [&](int pos) {
-                if (((gmask >> pos) & 1u) || pos == pbeg) {
-                    __asm__ volatile("" ::: "memory");
-                    const uint32_t w = W0[pos * 4 + g];
-                    const int i1 = qd_i1(w), i2 = qd_i2(w);
-                    const bool half = i1 == i2 && i1 < D;
-                    const float cp = half ? 0.5f : 1.f;
-#pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt) pcur[tt] = cp * qrow[tt][i1] * qrow[tt][i2];
-                    xo = 4 * qd_b(w);
-                    if ((nmask >> pos) & 1u) {
-                        const float4 cq = QC[pos * 4 + g];
-                        const float rinv = half ? 2.f : 1.f;
-                        const float r4[4] = {cq.x * rinv, cq.y * rinv, cq.z * rinv, cq.w * rinv};
-#pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                            for (int z = 0; z < 4; ++z) pz[tt][z] = pcur[tt] * r4[z];
-                    } else {
-#pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                            for (int z = 0; z < 4; ++z) pz[tt][z] = pcur[tt];
-                    }
-                } else {
-                    xo += 4;
-                    if (pos > pbeg && ((nmask >> (pos - 1)) & 1u)) {
-                        __asm__ volatile("" ::: "memory");
-#pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                            for (int z = 0; z < 4; ++z) pz[tt][z] = pcur[tt];
-                    }
-                }
-            };
             if constexpr (Cfg::BF) {
+                // K step kk covers positions 2 kk and 2 kk + 1.  Lane group g takes position
+                // 2 kk + g / 2, streams 2 (g % 2) and 2 (g % 2) + 1, slots 0..3: one 16-byte q load
+                // per token tile and two pair products.  Within a pair group the block advances by
+                // one per position; the pair products and block are re-read from the quad table only
+                // where a group starts (a uniform test: the lanes' positions see a start in the
+                // three positions ending at 2 kk + 1).
+                static_assert((NPH / 2) % 2 == 0, "an even number of K steps per wavefront");
                 const bf16x8 *Bv = reinterpret_cast<const bf16x8 *>(Bc);
-#pragma unroll 1
-                for (int kk = pbeg / 2; kk < (pbeg + NPH) / 2; ++kk) {
-                    bf16x8 B[NT];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) B[nt] = Bv[(kk * NT + nt) * 64 + lane];
-                    float a[TPW][8];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int pos = 2 * kk + h;
-                        position(pos);
-#pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt) {
-                            const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
-                            a[tt][4 * h + 0] = pz[tt][0] * x.x;
-                            a[tt][4 * h + 1] = pz[tt][1] * x.y;
-                            a[tt][4 * h + 2] = pz[tt][2] * x.z;
-                            a[tt][4 * h + 3] = pz[tt][3] * x.w;
-                        }
-                    }
+                const int hh = g >> 1, sp = 2 * (g & 1);
+                const int kbeg = pbeg / 2, kend = (pbeg + NPH) / 2;
+                float pc[TPW][2];
+                int xo = 0;
+                auto regroup = [&](int kk) {
+                    const uint2 w2 = *reinterpret_cast<const uint2 *>(W0 + (2 * kk + hh) * 4 + sp);
+                    const int i1a = qd_i1(w2.x), i2a = qd_i2(w2.x), i1b = qd_i1(w2.y), i2b = qd_i2(w2.y);
+                    const float ca = (i1a == i2a && i1a < D) ? 0.5f : 1.f;
+                    const float cb = (i1b == i2b && i1b < D) ? 0.5f : 1.f;
 #pragma unroll
                     for (int tt = 0; tt < TPW; ++tt) {
-                        const bf16x8 A = pack_bf16x8(a[tt]);
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A, B[nt], Y[tt][nt]);
+                        pc[tt][0] = ca * qrow[tt][i1a] * qrow[tt][i2a];
+                        pc[tt][1] = cb * qrow[tt][i1b] * qrow[tt][i2b];
                     }
+                    xo = 4 * qd_b(w2.x);
+                };
+                auto advance = [&](int kk) {         // the lanes' positions move from 2 kk - 2 + hh
+                    if (((gmask >> (2 * kk - 1)) & 7u) != 0) {
+                        __asm__ volatile("" ::: "memory");
+                        regroup(kk);
+                    } else {
+                        xo += 8;
+                    }
+                };
+                auto load_b = [&](bf16x8 (&B)[NT], int kk) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) B[nt] = Bv[(kk * NT + nt) * 64 + lane];
+                };
+                auto form = [&](bf16x8 (&A)[TPW]) {
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
+                        const float a[8] = {pc[tt][0] * x.x, pc[tt][0] * x.y, pc[tt][0] * x.z, pc[tt][0] * x.w,
+                                            pc[tt][1] * x.x, pc[tt][1] * x.y, pc[tt][1] * x.z, pc[tt][1] * x.w};
+                        A[tt] = pack_bf16x8(a);
+                    }
+                };
+                auto mma = [&](const bf16x8 (&A)[TPW], const bf16x8 (&B)[NT]) {
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A[tt], B[nt], Y[tt][nt]);
+                };
+                // two operand sets in turn: step kk's products run while step kk + 1's are formed
+                bf16x8 A0[TPW], B0[NT], A1[TPW], B1[NT];
+                regroup(kbeg);
+                load_b(B0, kbeg);
+                form(A0);
+#pragma unroll 1
+                for (int kk = kbeg; kk + 2 < kend; kk += 2) {
+                    advance(kk + 1);
+                    load_b(B1, kk + 1);
+                    form(A1);
+                    mma(A0, B0);
+                    advance(kk + 2);
+                    load_b(B0, kk + 2);
+                    form(A0);
+                    mma(A1, B1);
                 }
+                advance(kend - 1);
+                load_b(B1, kend - 1);
+                form(A1);
+                mma(A0, B0);
+                mma(A1, B1);
             } else {
+                float pcur[TPW];                      // pair weight * q_i1 * q_i2 of stream g
+                int xo = 0;                           // 4 b: the position's block of q
                 const float *Bf = reinterpret_cast<const float *>(Bc);
 #pragma unroll 1
                 for (int pos = pbeg; pos < pbeg + NPH; ++pos) {
-                    position(pos);
+                    if (((gmask >> pos) & 1u) || pos == pbeg) {
+                        const uint32_t w = W0[pos * 4 + g];
+                        const int i1 = qd_i1(w), i2 = qd_i2(w);
+                        const float cp = (i1 == i2 && i1 < D) ? 0.5f : 1.f;
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) pcur[tt] = cp * qrow[tt][i1] * qrow[tt][i2];
+                        xo = 4 * qd_b(w);
+                    } else {
+                        xo += 4;
+                    }
                     float a[TPW][4];
 #pragma unroll
                     for (int tt = 0; tt < TPW; ++tt) {
                         const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
-                        a[tt][0] = pz[tt][0] * x.x; a[tt][1] = pz[tt][1] * x.y;
-                        a[tt][2] = pz[tt][2] * x.z; a[tt][3] = pz[tt][3] * x.w;
+                        a[tt][0] = pcur[tt] * x.x; a[tt][1] = pcur[tt] * x.y;
+                        a[tt][2] = pcur[tt] * x.z; a[tt][3] = pcur[tt] * x.w;
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -863,7 +872,8 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename Part
     __shared__ __align__(16) float ys[TT * NC * 16];
     const int cc = blockIdx.x;
     const int64_t bh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
     const int g = lane >> 4, li = lane & 15;
     const int64_t t0 = tok0 + (int64_t)cc * C;
     const int nvalid = n - t0 < C ? (int)(n - t0) : C;
