@@ -512,30 +512,49 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         r4[0] = cq.x * rinv; r4[1] = cq.y * rinv; r4[2] = cq.z * rinv; r4[3] = cq.w * rinv;
     };
     auto write_bcopy = [&]() {
-#pragma unroll
-        for (int j = 0; j < MT; ++j) {
-            const int p = p0 + j;
-            float r4[4] = {1.f, 1.f, 1.f, 1.f};
-            const bool mixed = (nmask >> p) & 1u;
-            if (mixed) slot_ratio(p, r4);
-            if constexpr (Cfg::BF) {
-                // K step p / 2; reader lane group 2 (p % 2) + g / 2, elements 4 (g % 2) .. + 3
+        // plain copies of every position, then the wave's mixed-weight positions (uniform
+        // branches) written again, rescaled; LDS keeps a wave's order, so the second write wins
+        const uint32_t mixed = (uint32_t)((nmask >> p0) & ((1ull << MT) - 1));
+        if constexpr (Cfg::BF) {
+            // position p: K step p / 2, reader lane group 2 (p % 2) + g / 2, elements 4 (g % 2) .. + 3
+            uint2 *B2 = reinterpret_cast<uint2 *>(Bc);
+            auto entry = [&](int p, int nt) {   // index into B2
                 const int kk = p >> 1, gr = 2 * (p & 1) + (g >> 1);
+                return ((kk * NT + nt) * 64 + gr * 16 + li) * 2 + (g & 1);
+            };
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    uint2 h;
-                    if (mixed) h = {pack_bf16x2(S[j][nt][0] * r4[0], S[j][nt][1] * r4[1]),
-                                    pack_bf16x2(S[j][nt][2] * r4[2], S[j][nt][3] * r4[3])};
-                    else h = {pack_bf16x2(S[j][nt][0], S[j][nt][1]), pack_bf16x2(S[j][nt][2], S[j][nt][3])};
-                    *reinterpret_cast<uint2 *>(Bc + ((kk * NT + nt) * 64 + gr * 16 + li) * 16 + (g & 1) * 8) = h;
+            for (int j = 0; j < MT; ++j)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    B2[entry(p0 + j, nt)] = uint2{pack_bf16x2(S[j][nt][0], S[j][nt][1]),
+                                               pack_bf16x2(S[j][nt][2], S[j][nt][3])};
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+                if ((mixed >> j) & 1u) {
+                    float r4[4];
+                    slot_ratio(p0 + j, r4);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        B2[entry(p0 + j, nt)] = uint2{pack_bf16x2(S[j][nt][0] * r4[0], S[j][nt][1] * r4[1]),
+                                                      pack_bf16x2(S[j][nt][2] * r4[2], S[j][nt][3] * r4[3])};
                 }
-            } else {
+            }
+        } else {
+            float *Bf = reinterpret_cast<float *>(Bc);
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        reinterpret_cast<float *>(Bc)[((p * 4 + r) * NT + nt) * 64 + lane] =
-                            mixed ? S[j][nt][r] * r4[r] : S[j][nt][r];
+                    for (int nt = 0; nt < NT; ++nt) Bf[(((p0 + j) * 4 + r) * NT + nt) * 64 + lane] = S[j][nt][r];
+            for (uint32_t mm = mixed; mm; mm &= mm - 1) {
+                const int p = p0 + __builtin_ctz(mm);
+                float r4[4];
+                slot_ratio(p, r4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) Bf[((p * 4 + r) * NT + nt) * 64 + lane] *= r4[r];
             }
         }
     };
