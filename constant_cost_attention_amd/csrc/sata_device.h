@@ -57,6 +57,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Lane 4 * (lane / 4) + X's value of x, for every lane (DPP quad broadcast; folds into the
+// consuming VALU operation's source).
+template <int X>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), X * 0x55, 0xf, 0xf, true));
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8]) {
     bf16x8 r;
 #pragma unroll

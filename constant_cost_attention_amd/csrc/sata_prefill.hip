@@ -74,14 +74,18 @@ struct ScanCfg {
     // fp32: [4 NP K steps][NT][64 lanes] x 1 float.  Shares its LDS with Kt + Vt (update phase).
     static constexpr int BCB = BF ? NP / 2 * NT * 64 * 16 : NP * 4 * NT * 64 * 4;
     static constexpr int KVB = KR * KS * 4 + (NC * VS * ES + 15) / 16 * 16;
-    static constexpr int XB = (BCB > KVB ? BCB : KVB);
+    // Second K half's readout, handed to the first: bf16 (the partials' width) behind Kt + Vt in
+    // the shared region; fp32 in a region of its own.
+    static constexpr int YEB = (KH - 1) * TG * TPW * NT * 64 * (BF ? 8 : 16);
+    static constexpr int XB0 = BF ? KVB + YEB : KVB;
+    static constexpr int XB = (BCB > XB0 ? BCB : XB0);
     static constexpr int OFF_VT = KR * KS * 4;
     static constexpr int OFF_Q = (XB + 15) / 16 * 16;    // Qs [C][QS] fp32, scaled by 1/sqrt(d)
     static constexpr int OFF_W = OFF_Q + C * QS * 4;     // quad words [NP][4]
     static constexpr int OFF_QC = OFF_W + NP * 4 * 4;    // quad weights [NP][4] float4
     static constexpr int OFF_F = OFF_QC + NP * 4 * 16;   // position flags [NP]
-    static constexpr int OFF_E = OFF_F + NP * 4;         // readout exchange of the second K half
-    static constexpr int OFF_R = OFF_E + (KH - 1) * TG * TPW * NT * 64 * 16;
+    static constexpr int OFF_E = BF ? KVB : (OFF_F + NP * 4 + 15) / 16 * 16;   // second K half's readout
+    static constexpr int OFF_R = BF ? (OFF_F + NP * 4 + 15) / 16 * 16 : OFF_E + YEB;
     // bf16 inputs: the next chunk's k and v arrive by direct global -> LDS loads into a raw
     // buffer of 1 KB blocks; block s holds 64 consecutive tokens x one 16-byte unit of dims.
     static constexpr bool DMA = BF;
@@ -298,7 +302,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     uint32_t *W0 = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_W);   // [NP][4]
     float4 *QC = reinterpret_cast<float4 *>(lds + Cfg::OFF_QC);      // [NP][4]
     uint32_t *QF = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_F);   // [NP]
-    f32x4 *YE = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_E);         // [TG][TPW][NT][64]
+    unsigned char *YE = lds + Cfg::OFF_E;                            // [TG][TPW][NT][64] x 4 values
     uint4 *Raw = reinterpret_cast<uint4 *>(lds + Cfg::OFF_R);        // [2][NSB][64] (bf16 inputs)
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -324,6 +328,9 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     } else {
         item = pass == 0 ? (int64_t)blockIdx.x : nitems;
     }
+    // uniform: every item-derived index and address stays scalar
+    item = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(item >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)item));
     if (item >= nitems) break;
     const int u = (int)(item / per_sub);
     const int64_t rem = item % per_sub;
@@ -341,8 +348,13 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         __syncthreads();   // thread 0's acquire invalidated the caches every wave reads through
     }
     const int64_t ps0 = (int64_t)slice * NP;          // first position of the slice
-    // Tile j of this wave is position p0 + j; its rows 4s + z are stream s, slot z.  The lane's
-    // accumulator rows (4g + r) are stream g; its update row (li) is stream li/4, slot li%4.
+    // Tile j of this wave is position p0 + j (16 features: 4 streams x 4 slots).  Feature rows of
+    // a tile: bf16 operands put stream li % 4, slot li / 4 on row li, so that the four lanes of a
+    // DPP quad share a slot (one key load feeds all four); fp32 operands put stream li / 4, slot
+    // li % 4 there.  The lane's accumulator rows 4g + r are then (stream r, slot g) for bf16 and
+    // (stream g, slot r) for fp32.
+    auto acc_stream = [&](int r) { return Cfg::BF ? r : g; };
+    auto acc_slot = [&](int r) { return Cfg::BF ? g : r; };
 
     for (int i = tid; i < NP * 4; i += kThreads) {
         W0[i] = qw0[ps0 * 4 + i];
@@ -353,25 +365,25 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     float *Sh = state + bh * NC * m_pad;
     f32x4 S[MT][NT];
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-        const int64_t qd = (ps0 + p0 + j) * 4 + g;
-        const uint32_t w = qw0[qd];
-        const int32_t c0 = qcidx[qd];
-        const uint32_t mask = qd_mask(w);
-        const int z0 = mask ? __builtin_ctz(mask) : 0;
+    for (int j = 0; j < MT; ++j)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int r = 0; r < 4; ++r) {
+            const int64_t qd = (ps0 + p0 + j) * 4 + acc_stream(r);
+            const uint32_t w = qw0[qd];
+            const int32_t c0 = qcidx[qd];
+            const uint32_t mask = qd_mask(w);
+            const int z0 = mask ? __builtin_ctz(mask) : 0, z = acc_slot(r);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int nt = 0; nt < NT; ++nt) {
                 const int c = 16 * nt + li;
-                const bool ok = ((mask >> r) & 1u) && c < NC;
-                S[j][nt][r] = ok ? Sh[(int64_t)c * m_pad + c0 + (r - z0)] : 0.f;
+                const bool ok = ((mask >> z) & 1u) && c < NC;
+                S[j][nt][r] = ok ? Sh[(int64_t)c * m_pad + c0 + (z - z0)] : 0.f;
             }
-    }
+        }
     __syncthreads();
 
-    // update-side view of this wave's positions: the lane's stream (li / 4) and slot (li % 4)
-    const int us = li >> 2, uz = li & 3;
+    // update-side view of this wave's positions: the lane's row li is (stream us, slot uz)
+    const int us = Cfg::BF ? (li & 3) : (li >> 2), uz = Cfg::BF ? (li >> 2) : (li & 3);
     uint32_t uw[MT];
     uint32_t newgrp = 0;                               // bit j: position p0 + j starts a pair group
 #pragma unroll
@@ -505,38 +517,45 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     // state accumulators -> readout operand copy in LDS (this wave's positions).  The copy
     // carries the slot weight relative to the pair weight: 1 except at a group's first position
     // (diagonal and invalid slots), so the readout forms every position alike.
-    auto slot_ratio = [&](int p, float (&r4)[4]) {
-        const float4 cq = QC[p * 4 + g];
-        const uint32_t w = W0[p * 4 + g];
-        const float rinv = (qd_i1(w) == qd_i2(w) && qd_i1(w) < D) ? 2.f : 1.f;
-        r4[0] = cq.x * rinv; r4[1] = cq.y * rinv; r4[2] = cq.z * rinv; r4[3] = cq.w * rinv;
+    auto slot_ratio = [&](int p, float (&r4)[4]) {   // for the lane's accumulator rows r
+        const float *qcf = reinterpret_cast<const float *>(QC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int st = acc_stream(r);
+            const uint32_t w = W0[p * 4 + st];
+            const float rinv = (qd_i1(w) == qd_i2(w) && qd_i1(w) < D) ? 2.f : 1.f;
+            r4[r] = qcf[(p * 4 + st) * 4 + acc_slot(r)] * rinv;
+        }
     };
     auto write_bcopy = [&]() {
         // plain copies of every position, then the wave's mixed-weight positions (uniform
         // branches) written again, rescaled; LDS keeps a wave's order, so the second write wins
         const uint32_t mixed = (uint32_t)((nmask >> p0) & ((1ull << MT) - 1));
         if constexpr (Cfg::BF) {
-            // position p: K step p / 2, reader lane group 2 (p % 2) + g / 2, elements 4 (g % 2) .. + 3
-            uint2 *B2 = reinterpret_cast<uint2 *>(Bc);
-            auto entry = [&](int p, int nt) {   // index into B2
-                const int kk = p >> 1, gr = 2 * (p & 1) + (g >> 1);
-                return ((kk * NT + nt) * 64 + gr * 16 + li) * 2 + (g & 1);
+            // position p, streams 2 h2 and 2 h2 + 1 of slot g: K step p / 2, reader lane group
+            // 2 (p % 2) + h2, elements 2 g and 2 g + 1
+            uint32_t *B4 = reinterpret_cast<uint32_t *>(Bc);
+            auto entry = [&](int p, int nt, int h2) {   // index into B4
+                const int kk = p >> 1, gr = 2 * (p & 1) + h2;
+                return ((kk * NT + nt) * 64 + gr * 16 + li) * 4 + g;
             };
 #pragma unroll
             for (int j = 0; j < MT; ++j)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    B2[entry(p0 + j, nt)] = uint2{pack_bf16x2(S[j][nt][0], S[j][nt][1]),
-                                               pack_bf16x2(S[j][nt][2], S[j][nt][3])};
+                for (int nt = 0; nt < NT; ++nt) {
+                    B4[entry(p0 + j, nt, 0)] = pack_bf16x2(S[j][nt][0], S[j][nt][1]);
+                    B4[entry(p0 + j, nt, 1)] = pack_bf16x2(S[j][nt][2], S[j][nt][3]);
+                }
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
                 if ((mixed >> j) & 1u) {
                     float r4[4];
                     slot_ratio(p0 + j, r4);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        B2[entry(p0 + j, nt)] = uint2{pack_bf16x2(S[j][nt][0] * r4[0], S[j][nt][1] * r4[1]),
-                                                      pack_bf16x2(S[j][nt][2] * r4[2], S[j][nt][3] * r4[3])};
+                    for (int nt = 0; nt < NT; ++nt) {
+                        B4[entry(p0 + j, nt, 0)] = pack_bf16x2(S[j][nt][0] * r4[0], S[j][nt][1] * r4[1]);
+                        B4[entry(p0 + j, nt, 1)] = pack_bf16x2(S[j][nt][2] * r4[2], S[j][nt][3] * r4[3]);
+                    }
                 }
             }
         } else {
@@ -592,8 +611,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
             for (int tt = 0; tt < TPW; ++tt) qrow[tt] = Qs + (16 * (tt0 + tt) + li) * QS;
             if constexpr (Cfg::BF) {
                 // K step kk covers positions 2 kk and 2 kk + 1.  Lane group g takes position
-                // 2 kk + g / 2, streams 2 (g % 2) and 2 (g % 2) + 1, slots 0..3: one 16-byte q load
-                // per token tile and two pair products.  Within a pair group the block advances by
+                // 2 kk + g / 2, streams 2 (g % 2) + sl (sl = 0, 1) and slots z = 0..3 as elements
+                // 2 z + sl: one 16-byte q load per token tile and two pair products.  Within a pair group the block advances by
                 // one per position; the pair products and block are re-read from the quad table only
                 // where a group starts (a uniform test: the lanes' positions see a start in the
                 // three positions ending at 2 kk + 1).
@@ -631,8 +650,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
 #pragma unroll
                     for (int tt = 0; tt < TPW; ++tt) {
                         const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
-                        const float a[8] = {pc[tt][0] * x.x, pc[tt][0] * x.y, pc[tt][0] * x.z, pc[tt][0] * x.w,
-                                            pc[tt][1] * x.x, pc[tt][1] * x.y, pc[tt][1] * x.z, pc[tt][1] * x.w};
+                        const float a[8] = {pc[tt][0] * x.x, pc[tt][1] * x.x, pc[tt][0] * x.y, pc[tt][1] * x.y,
+                                            pc[tt][0] * x.z, pc[tt][1] * x.z, pc[tt][0] * x.w, pc[tt][1] * x.w};
                         A[tt] = pack_bf16x8(a);
                     }
                 };
@@ -642,6 +661,18 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A[tt], B[nt], Y[tt][nt]);
                 };
+                if constexpr (NW == 8) {
+                    // two wavefronts per SIMD hide each other's latency: one operand set
+                    regroup(kbeg);
+#pragma unroll 1
+                    for (int kk = kbeg; kk < kend; ++kk) {
+                        if (kk > kbeg) advance(kk);
+                        bf16x8 A[TPW], B[NT];
+                        load_b(B, kk);
+                        form(A);
+                        mma(A, B);
+                    }
+                } else {
                 // two operand sets in turn: step kk's products run while step kk + 1's are formed
                 bf16x8 A0[TPW], B0[NT], A1[TPW], B1[NT];
                 regroup(kbeg);
@@ -663,6 +694,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 form(A1);
                 mma(A0, B0);
                 mma(A1, B1);
+                }
             } else {
                 float pcur[TPW];                      // pair weight * q_i1 * q_i2 of stream g
                 int xo = 0;                           // 4 b: the position's block of q
@@ -698,32 +730,50 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     }
                 }
             }
-            if (half > 0) {                           // second K half: hand the partial to the first
-#pragma unroll
-                for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) YE[(((wave % TG) * TPW + tt) * NT + nt) * 64 + lane] = Y[tt][nt];
-            }
         }
         if constexpr (Cfg::DMA) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this chunk's k, v in LDS
-        __syncthreads();                              // state copy and Qs no longer read; exchange written
+        __syncthreads();                              // state copy and Qs no longer read
+        // second K half: hand the readout to the first (bf16 inputs: in bf16, behind Kt + Vt)
+        auto ye_index = [&](int tt, int nt) { return (((wave % TG) * TPW + tt) * NT + nt) * 64 + lane; };
+        if (Cfg::KH > 1 && half > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    if constexpr (Cfg::BF)
+                        reinterpret_cast<uint2 *>(YE)[ye_index(tt, nt)] =
+                            uint2{pack_bf16x2(Y[tt][nt][0], Y[tt][nt][1]), pack_bf16x2(Y[tt][nt][2], Y[tt][nt][3])};
+                    else
+                        reinterpret_cast<f32x4 *>(YE)[ye_index(tt, nt)] = Y[tt][nt];
+                }
+        }
         if constexpr (Cfg::DMA) write_kv_raw(chunk_nv(cc));
         else write_kv(rk, rv, chunk_nv(cc));
         if (cc + 1 < cend) write_q(rq);
+        __syncthreads();                              // exchange written
         if (half == 0) {
             // partial layout per (bh, chunk, slice): [TT][NC][16 tokens]; lane writes rows 4g..4g+3
-            auto *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16);
+            // one lane address per chunk; the tiles are constant offsets from it
+            auto *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16) +
+                         (int64_t)tt0 * NC * 16 + (li * 16 + 4 * g);
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     f32x4 y = Y[tt][nt];
-                    if constexpr (Cfg::KH > 1) y += YE[(((wave % TG) * TPW + tt) * NT + nt) * 64 + lane];
+                    if constexpr (Cfg::KH > 1) {
+                        if constexpr (Cfg::BF) {
+                            const uint2 h = reinterpret_cast<const uint2 *>(YE)[ye_index(tt, nt)];
+                            y[0] += __uint_as_float(h.x << 16); y[1] += __uint_as_float(h.x & 0xffff0000u);
+                            y[2] += __uint_as_float(h.y << 16); y[3] += __uint_as_float(h.y & 0xffff0000u);
+                        } else {
+                            y += reinterpret_cast<const f32x4 *>(YE)[ye_index(tt, nt)];
+                        }
+                    }
                     const int c = 16 * nt + li;
-                    if (c < NC) store4(pdst + ((int64_t)(tt0 + tt) * NC + c) * 16 + 4 * g, y);
+                    if (c < NC) store4(pdst + (tt * NC + 16 * nt) * 16, y);
                 }
         }
-        __syncthreads();
         if (cc + 1 < cend) {                          // next chunk's k, v: in flight during the update
             if constexpr (Cfg::DMA) {
                 dma_kv(cc + 1);
@@ -735,44 +785,64 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
 
         // ---- chunk state: S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1]
         if constexpr (Cfg::BF && (NW == 8 || UPDATE_KS_OUTER)) {
-            // Chunk's 32-token K steps outer, positions inner (smaller register footprint); pair
-            // products are re-formed at each K step's first position and at group starts.
+            // The chunk's 32-token K steps outer, positions inner (smaller register footprint): one
+            // [V | 1] operand set at a time, the next K step's loaded during this one; the pair
+            // products are re-formed at each K step's first position and at group starts.  Key
+            // values of the last index come by DPP quad broadcast, as below.
+            constexpr int NKS = C / 32;
             const bf16_t *V16 = reinterpret_cast<const bf16_t *>(Vt);
-#pragma unroll 1
-            for (int ks = 0; ks < C / 32; ++ks) {
-                const int tb = 32 * ks + 8 * g;
-                bf16x8 B[NT];
+            auto load_v = [&](bf16x8 (&B)[NT], int ks) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     uint4 u = {0u, 0u, 0u, 0u};
-                    if (16 * nt + li < NC) u = *reinterpret_cast<const uint4 *>(V16 + (16 * nt + li) * VS + tb);
+                    if (16 * nt + li < NC) u = *reinterpret_cast<const uint4 *>(V16 + (16 * nt + li) * VS + 32 * ks + 8 * g);
                     B[nt] = __builtin_bit_cast(bf16x8, u);
                 }
+            };
+            auto load_k3 = [&](int j, int ks) {
+                return *reinterpret_cast<const float2 *>(Kt + (4 * qd_b(uw[j]) + uz) * KS + 32 * ks + 8 * g + 2 * us);
+            };
+            auto step = [&](const bf16x8 (&B)[NT], int ks) {
+                const int tb = 32 * ks + 8 * g;
                 float p2[8];
+                float2 kc = load_k3(0, ks);
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
                     const uint32_t w = uw[j];
                     if (j == 0 || ((newgrp >> j) & 1u)) {
-                        __asm__ volatile("" ::: "memory");
+                        __asm__ volatile("" ::: "memory");   // keep the reload behind its (uniform) branch
                         const float4 *k1 = reinterpret_cast<const float4 *>(Kt + qd_i1(w) * KS + tb);
                         const float4 *k2 = reinterpret_cast<const float4 *>(Kt + qd_i2(w) * KS + tb);
                         const float4 a0 = k1[0], a1 = k1[1], b0 = k2[0], b1 = k2[1];
                         p2[0] = a0.x * b0.x; p2[1] = a0.y * b0.y; p2[2] = a0.z * b0.z; p2[3] = a0.w * b0.w;
                         p2[4] = a1.x * b1.x; p2[5] = a1.y * b1.y; p2[6] = a1.z * b1.z; p2[7] = a1.w * b1.w;
                     }
-                    const float4 *k3 = reinterpret_cast<const float4 *>(Kt + (4 * qd_b(w) + uz) * KS + tb);
-                    const float4 c0 = k3[0], c1 = k3[1];
-                    float a[8] = {p2[0] * c0.x, p2[1] * c0.y, p2[2] * c0.z, p2[3] * c0.w,
-                                  p2[4] * c1.x, p2[5] * c1.y, p2[6] * c1.z, p2[7] * c1.w};
+                    float2 kn = kc;
+                    if (j + 1 < MT) kn = load_k3(j + 1, ks);
+                    const float x = kc.x, y = kc.y;
+                    float a[8] = {p2[0] * quad_bcast<0>(x), p2[1] * quad_bcast<0>(y),
+                                  p2[2] * quad_bcast<1>(x), p2[3] * quad_bcast<1>(y),
+                                  p2[4] * quad_bcast<2>(x), p2[5] * quad_bcast<2>(y),
+                                  p2[6] * quad_bcast<3>(x), p2[7] * quad_bcast<3>(y)};
                     const bf16x8 A = pack_bf16x8(a);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_bf16(A, B[nt], S[j][nt]);
+                    kc = kn;
                 }
+            };
+#pragma unroll 1
+            for (int ks = 0; ks < NKS; ++ks) {
+                bf16x8 B[NT];
+                load_v(B, ks);
+                step(B, ks);
             }
         } else if constexpr (Cfg::BF) {
             // Positions outer, the chunk's 32-token K steps inner: the [V | 1] operand tiles of the
             // whole chunk stay in registers, and the pair products (per K step) are formed only where
-            // a pair group starts (the same positions for all four streams).
+            // a pair group starts (the same positions for all four streams).  The last-index key
+            // values of a K step: each lane of a DPP quad (one slot, four streams) loads two of the
+            // eight tokens, and the products take all eight by quad broadcast.  The next position's
+            // key values are loaded while this position's products run.
             constexpr int NKS = C / 32;
             const bf16_t *V16 = reinterpret_cast<const bf16_t *>(Vt);
             bf16x8 B[NKS][NT];
@@ -784,7 +854,14 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     if (16 * nt + li < NC) u = *reinterpret_cast<const uint4 *>(V16 + (16 * nt + li) * VS + 32 * ks + 8 * g);
                     B[ks][nt] = __builtin_bit_cast(bf16x8, u);
                 }
+            auto load_k3 = [&](float2 (&kd)[NKS], int j) {
+                const float *k3 = Kt + (4 * qd_b(uw[j]) + uz) * KS + 8 * g + 2 * us;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) kd[ks] = *reinterpret_cast<const float2 *>(k3 + 32 * ks);
+            };
             float p2[NKS][8];
+            float2 kc[NKS];
+            load_k3(kc, 0);
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
                 const uint32_t w = uw[j];
@@ -802,21 +879,22 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                         p2[ks][4] = a1.x * b1.x; p2[ks][5] = a1.y * b1.y; p2[ks][6] = a1.z * b1.z; p2[ks][7] = a1.w * b1.w;
                     }
                 }
-                const float *k3 = Kt + (4 * qd_b(w) + uz) * KS + 8 * g;
-                float4 c[NKS][2];
+                float2 kn[NKS];
+                if (j + 1 < MT) load_k3(kn, j + 1);
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
-                    c[ks][0] = *reinterpret_cast<const float4 *>(k3 + 32 * ks);
-                    c[ks][1] = *reinterpret_cast<const float4 *>(k3 + 32 * ks + 4);
-                }
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    float a[8] = {p2[ks][0] * c[ks][0].x, p2[ks][1] * c[ks][0].y, p2[ks][2] * c[ks][0].z,
-                                  p2[ks][3] * c[ks][0].w, p2[ks][4] * c[ks][1].x, p2[ks][5] * c[ks][1].y,
-                                  p2[ks][6] * c[ks][1].z, p2[ks][7] * c[ks][1].w};
+                    const float x = kc[ks].x, y = kc[ks].y;
+                    float a[8] = {p2[ks][0] * quad_bcast<0>(x), p2[ks][1] * quad_bcast<0>(y),
+                                  p2[ks][2] * quad_bcast<1>(x), p2[ks][3] * quad_bcast<1>(y),
+                                  p2[ks][4] * quad_bcast<2>(x), p2[ks][5] * quad_bcast<2>(y),
+                                  p2[ks][6] * quad_bcast<3>(x), p2[ks][7] * quad_bcast<3>(y)};
                     const bf16x8 A = pack_bf16x8(a);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_bf16(A, B[ks][nt], S[j][nt]);
+                }
+                if (j + 1 < MT) {
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) kc[ks] = kn[ks];
                 }
             }
         } else {
@@ -844,20 +922,20 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
 
     // accumulators -> state slice
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-        const int64_t qd = (ps0 + p0 + j) * 4 + g;
-        const uint32_t w = qw0[qd];
-        const int32_t c0 = qcidx[qd];
-        const uint32_t mask = qd_mask(w);
-        const int z0 = mask ? __builtin_ctz(mask) : 0;
+    for (int j = 0; j < MT; ++j)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int r = 0; r < 4; ++r) {
+            const int64_t qd = (ps0 + p0 + j) * 4 + acc_stream(r);
+            const uint32_t w = qw0[qd];
+            const int32_t c0 = qcidx[qd];
+            const uint32_t mask = qd_mask(w);
+            const int z0 = mask ? __builtin_ctz(mask) : 0, z = acc_slot(r);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int nt = 0; nt < NT; ++nt) {
                 const int c = 16 * nt + li;
-                if (((mask >> r) & 1u) && c < NC) Sh[(int64_t)c * m_pad + c0 + (r - z0)] = S[j][nt][r];
+                if (((mask >> z) & 1u) && c < NC) Sh[(int64_t)c * m_pad + c0 + (z - z0)] = S[j][nt][r];
             }
-    }
+        }
     if constexpr (Cfg::PERSIST) {
         // every wave's state stores reach L2 before the barrier; thread 0's agent-scope release
         // then writes L2 back before the flag
@@ -985,12 +1063,15 @@ struct ScanShape {
 };
 static ScanShape pick_shape(const sata_index *idx, int64_t bh, int chunk, sata_dtype in_dt) {
     const int64_t npos = idx->nq / 4;
+    // bf16 inputs, 128-token chunks: eight wavefronts (two per SIMD, each hiding the other's
+    // latency) with four or two positions each
+    if (in_dt == SATA_BF16 && chunk == 128) return {8, bh * ((npos + 31) / 32) >= 256 ? 4 : 2};
     for (int mt : {8, 4}) {
         if (mt == 8 && in_dt == SATA_F32) continue;
         const int64_t per = (int64_t)kNW * mt;
-        if (bh * ((npos + per - 1) / per) >= 256) return {4, mt};
+        if (bh * ((npos + per - 1) / per) >= 256) return {kNW, mt};
     }
-    return {4, 2};
+    return {kNW, 2};
 }
 
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt) {
@@ -1095,7 +1176,12 @@ template <int D>
 static hipError_t run_d(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                         const void *q, const void *k, const void *v, void *out, int64_t n,
                         sata_dtype in_dt, sata_dtype out_dt, hipStream_t s) {
-    const int mt = plan.fw / 16;
+    const int mt = plan.fw / 16, nw = plan.fs / plan.fw;
+    if (nw == 8) {
+        if (plan.chunk != 128 || in_dt != SATA_BF16) return hipErrorInvalidValue;   // never planned
+        if (mt == 2) return run_dt<D, 128, 2, 8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        return run_dt<D, 128, 4, 8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+    }
     if (plan.chunk == 64) {
         if (mt == 2) return run_dt<D, 64, 2, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
         if (mt == 4) return run_dt<D, 64, 4, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);

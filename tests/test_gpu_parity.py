@@ -117,6 +117,24 @@ def test_all_shapes_ragged_every_row(sata, oracle, d, P, dtype):
     assert err <= _tol(dtype)
 
 
+@pytest.mark.parametrize("d", [8, 16, 32, 64])
+@pytest.mark.parametrize("heads", [1, 64])
+def test_bf16_chunk128_every_row(sata, oracle, d, heads):
+    """bf16 inputs in 128-token chunks (eight wavefronts per workgroup): few heads give two
+    positions per wavefront, many heads four; n = 2 chunks + a ragged tail, every row."""
+    P, chunk = 4, 128
+    n = 2 * chunk + 45
+    say("prefill bf16 chunk 128 d=%d heads=%d n=%d" % (d, heads, n))
+    x = si.draw_qkv((1, heads), n, d, d, 5151 + d + heads, "bf16")
+    idx = sata.Index(d, d, P)
+    st = sata.State(idx, 1, heads)
+    q, k, v = dev_all(x)
+    o = prefill(idx, st, q, k, v, chunk=chunk).cpu().numpy()
+    err = rel_err(o, oracle.taylor_attention(x.q, x.k, x.v, P))
+    say("  err %.3e" % err)
+    assert err <= TOL_BF16
+
+
 def test_short_sequences_and_empty(sata, oracle):
     d, P = 16, 4
     idx = sata.Index(d, d, P)
