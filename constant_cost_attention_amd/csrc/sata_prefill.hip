@@ -662,11 +662,21 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                         for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A[tt], B[nt], Y[tt][nt]);
                 };
                 if constexpr (NW == 8) {
-                    // two wavefronts per SIMD hide each other's latency: one operand set
+                    // two wavefronts per SIMD hide each other's latency: one operand set; the first
+                    // step starts the accumulators from zero
                     regroup(kbeg);
+                    {
+                        bf16x8 A[TPW], B[NT];
+                        load_b(B, kbeg);
+                        form(A);
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A[tt], B[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
 #pragma unroll 1
-                    for (int kk = kbeg; kk < kend; ++kk) {
-                        if (kk > kbeg) advance(kk);
+                    for (int kk = kbeg + 1; kk < kend; ++kk) {
+                        advance(kk);
                         bf16x8 A[TPW], B[NT];
                         load_b(B, kk);
                         form(A);
@@ -830,7 +840,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     kc = kn;
                 }
             };
-#pragma unroll 1
+#pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 bf16x8 B[NT];
                 load_v(B, ks);
