@@ -988,42 +988,63 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename Part
     const TIn *kh = k + bh * n * D;
     const TIn *vh = v + bh * n * DV;
 
-    // partial sums first: their loads are the long pole, issue them before the MFMA work
-    const auto *base = partial + (bh * nchunk + cc) * (int64_t)nslices * NV * 4;   // NV groups of 4 per slice
-    float4 acc[PER];
+    // partial sums first: their loads are the long pole, issue them before the MFMA work.
+    // 16-byte loads (8 bf16 or 4 fp32 values), four slices in flight per thread.
+    using PT = typename PartialOf<TIn>::type;
+    constexpr int VEC = 16 / (int)sizeof(PT);       // values per load
+    constexpr int NVV = NV * 4 / VEC;               // loads per slice
+    constexpr int PERV = (NVV + 255) / 256;
+    constexpr int SU = 4;                           // slices per round
+    const PT *base = partial + (bh * nchunk + cc) * (int64_t)nslices * NV * 4;
+    float acc[PERV][VEC];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = float4{0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 1 < nslices; s += 2) {
-        const auto *p0 = base + (int64_t)s * NV * 4, *p1 = p0 + NV * 4;
-        float4 a[PER], b[PER];
+    for (int j = 0; j < PERV; ++j)
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int i = tid + 256 * j;
-            a[j] = i < NV ? load4(p0 + 4 * i) : float4{0.f, 0.f, 0.f, 0.f};
-            b[j] = i < NV ? load4(p1 + 4 * i) : float4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int e = 0; e < VEC; ++e) acc[j][e] = 0.f;
+    auto add_vec = [&](float (&a)[VEC], const uint4 &u) {
+        if constexpr (VEC == 8) {
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            acc[j].x += a[j].x; acc[j].y += a[j].y; acc[j].z += a[j].z; acc[j].w += a[j].w;
-            acc[j].x += b[j].x; acc[j].y += b[j].y; acc[j].z += b[j].z; acc[j].w += b[j].w;
-        }
-    }
-    if (s < nslices) {
-        const auto *p0 = base + (int64_t)s * NV * 4;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int i = tid + 256 * j;
-            if (i < NV) {
-                const float4 a = load4(p0 + 4 * i);
-                acc[j].x += a.x; acc[j].y += a.y; acc[j].z += a.z; acc[j].w += a.w;
+            for (int e = 0; e < 4; ++e) {
+                a[2 * e] += __uint_as_float(w[e] << 16);
+                a[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
             }
+        } else {
+            a[0] += __uint_as_float(u.x); a[1] += __uint_as_float(u.y);
+            a[2] += __uint_as_float(u.z); a[3] += __uint_as_float(u.w);
+        }
+    };
+    int s = 0;
+    for (; s + SU <= nslices; s += SU) {
+        uint4 u[SU][PERV];
+#pragma unroll
+        for (int r = 0; r < SU; ++r)
+#pragma unroll
+            for (int j = 0; j < PERV; ++j) {
+                const int i = tid + 256 * j;
+                u[r][j] = i < NVV ? *reinterpret_cast<const uint4 *>(base + ((int64_t)(s + r) * NVV + i) * VEC)
+                                  : uint4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+        for (int r = 0; r < SU; ++r)
+#pragma unroll
+            for (int j = 0; j < PERV; ++j) add_vec(acc[j], u[r][j]);
+    }
+    for (; s < nslices; ++s) {
+#pragma unroll
+        for (int j = 0; j < PERV; ++j) {
+            const int i = tid + 256 * j;
+            if (i < NVV) add_vec(acc[j], *reinterpret_cast<const uint4 *>(base + ((int64_t)s * NVV + i) * VEC));
         }
     }
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
+    for (int j = 0; j < PERV; ++j) {
         const int i = tid + 256 * j;
-        if (i < NV) reinterpret_cast<float4 *>(ys)[i] = acc[j];
+        if (i < NVV) {
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+                reinterpret_cast<float4 *>(ys)[i * (VEC / 4) + e / 4] = float4{acc[j][e], acc[j][e + 1], acc[j][e + 2], acc[j][e + 3]};
+        }
     }
 
     stage_v<DV, C, NCP, VS, TIn>(vt, vh, t0, nvalid, tid, 256);
