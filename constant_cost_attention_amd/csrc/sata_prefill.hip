@@ -91,7 +91,11 @@ struct ScanCfg {
     static constexpr bool DMA = BF;
     static constexpr int DB = D / (16 / ES);             // 16-byte units per token
     static constexpr int NSB = C / 64 * DB;              // blocks per tensor
-    static constexpr int LDS = OFF_R + (DMA ? 2 * NSB * 1024 : 0);
+    // The raw buffer is a __shared__ array of its own (RAWB bytes): the compiler can then tell
+    // its asynchronous fills from every other LDS access and does not make those wait for them.
+    // LDS is the dynamic part (launch argument).
+    static constexpr int RAWB = DMA ? 2 * NSB * 1024 : 16;
+    static constexpr int LDS = OFF_R;
     // Prefetch of one chunk's q, k or v: 16-byte units per thread.
     static constexpr int EPU = 16 / ES;                  // elements per unit
     static constexpr int UNITS = C * D / EPU;
@@ -103,7 +107,7 @@ struct ScanCfg {
     static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
     static_assert(OFF_E % 16 == 0 && OFF_R % 16 == 0, "alignment");
     static_assert(OFF_Q % 16 == 0 && OFF_QC % 16 == 0, "alignment");
-    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(LDS + RAWB <= 160 * 1024, "LDS budget");
 };
 
 __device__ __forceinline__ int qd_i1(uint32_t w) { return (int)(w & 0xffu); }
@@ -280,6 +284,17 @@ __device__ __forceinline__ float4 load4(const bf16_t *p) {
                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
 
+// One 16-byte global -> LDS load per lane: lane i's bytes land at LDS offset lds + 16 i (lds is
+// uniform).  Issued from asm so that the compiler does not hold every later LDS read until the
+// load has landed (it cannot tell these writes from the update's reads); the consumer waits on
+// vmcnt itself before a barrier.  The asm sets M0, which nothing else in these kernels uses.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 template <int D, int DV, int C, int MT, int NW, typename TIn>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
@@ -303,7 +318,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     float4 *QC = reinterpret_cast<float4 *>(lds + Cfg::OFF_QC);      // [NP][4]
     uint32_t *QF = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_F);   // [NP]
     unsigned char *YE = lds + Cfg::OFF_E;                            // [TG][TPW][NT][64] x 4 values
-    uint4 *Raw = reinterpret_cast<uint4 *>(lds + Cfg::OFF_R);        // [2][NSB][64] (bf16 inputs)
+    __shared__ __align__(16) uint4 raw_lds[Cfg::RAWB / 16];
+    uint4 *Raw = raw_lds;                                            // [2][NSB][64] (bf16 inputs)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
@@ -478,11 +494,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 const int t = (sb / DB) * 64 + lane;
                 const int d0 = (sb % DB) * EPU;
                 if (t < nv) {
-                    __builtin_amdgcn_global_load_lds((const void *)(kh + (t0 + t) * D + d0),
-                                                     (__attribute__((address_space(3))) void *)(Raw + sb * 64), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds((const void *)(vh + (t0 + t) * D + d0),
-                                                     (__attribute__((address_space(3))) void *)(Raw + (NSB + sb) * 64),
-                                                     16, 0, 0);
+                    dma16(kh + (t0 + t) * D + d0, lds_offset(Raw + sb * 64));
+                    dma16(vh + (t0 + t) * D + d0, lds_offset(Raw + (NSB + sb) * 64));
                 }
             }
         }
