@@ -83,6 +83,7 @@ struct PrefillPlan {
     int chunk = 0;          // tokens per chunk
     int fw = 0;             // features per wave
     int fs = 0;             // features per workgroup slice
+    bool ws = false;        // warp-specialised scan (fw = features per update wavefront)
     int slices = 0;         // workgroups per head
     int64_t seg_chunks = 0; // chunks per segment (bounded by the workspace cap)
     int64_t sync_off = 0;   // byte offset of the scan's counter and progress flags in the workspace

@@ -36,6 +36,7 @@
 //   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
 //            engineering a constant per-token cost" (2026-02-05).
 #include <algorithm>
+#include <type_traits>
 
 #ifndef UPDATE_KS_OUTER
 #define UPDATE_KS_OUTER 0
@@ -970,6 +971,447 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Warp-specialised scan (bf16 inputs).  Eight wavefronts, two per SIMD: four "update"
+// wavefronts keep the slice's state in their registers (MT positions each) and form the chunk
+// state contraction; four "readout" wavefronts read the chunk out against the state copy in LDS
+// (TPW token tiles each, every position of the slice) and stage the next chunk through their
+// registers.  Readout and update of a chunk touch disjoint data (the state copy holds
+// S^(c-1), the registers turn into S^(c)), so the two run at the same time on every SIMD; the
+// second phase of a chunk writes the new state copy (update wavefronts) and the readout
+// partials plus the next chunk's q, k and v (readout wavefronts).  Two barriers per chunk.
+template <int D, int DV, int C, int MT>
+struct WsCfg {
+    static constexpr int NR = 4, NU = 4, NW = NR + NU, THREADS = 64 * NW;
+    static constexpr int NP = NU * MT;            // positions per slice
+    static constexpr int NS = NP / 2;             // readout K steps
+    static constexpr int NC = DV + 1, NT = (NC + 15) / 16;
+    static constexpr int TT = C / 16, TPW = TT / NR;
+    static constexpr int KR = D + 4, KS = C + 4, QS = D + 4, VS = C + 8;
+    // State copy: the NT - 1 full column tiles [NS][NT-1][64 lanes] x 16 B, then the last tile.
+    // When the last tile holds only the normaliser column, just its lanes 16 g are kept:
+    // [NS][4] x 16 B; otherwise [NS][64] x 16 B.
+    static constexpr int LC = NC - 16 * (NT - 1);          // real columns of the last tile
+    static constexpr int LASTW = LC == 1 ? 4 : 64;
+    static constexpr int FULLB = NS * (NT - 1) * 64 * 16;
+    static constexpr int BCB = FULLB + NS * LASTW * 16;
+    static constexpr int OFF_K = (BCB + 15) / 16 * 16;     // Kt fp32 [KR][KS], dim-major
+    static constexpr int OFF_V = OFF_K + KR * KS * 4;      // Vt bf16 [NC][VS], dim-major
+    static constexpr int OFF_Q = OFF_V + (NC * VS * 2 + 15) / 16 * 16;   // Qs fp32 [C][QS]
+    static constexpr int OFF_W = OFF_Q + C * QS * 4;       // quad words [NP][4]
+    static constexpr int OFF_QC = OFF_W + NP * 16;         // quad weights [NP][4] float4
+    static constexpr int OFF_F = OFF_QC + NP * 64;         // position flags [NP]
+    static constexpr int LDS = OFF_F + NP * 4;
+    static constexpr int EPU = 8;                          // bf16 values per 16-byte unit
+    static constexpr int UNITS = C * D / EPU;              // units per tensor and chunk
+    static constexpr int UPT = (UNITS + 64 * NR - 1) / (64 * NR);
+    static_assert(DV == D, "d_V = d_K");
+    static_assert(C % 64 == 0 && TT % NR == 0, "64 or 128 tokens per chunk");
+    static_assert(NS % 2 == 0, "an even number of readout K steps");
+    static_assert(NP <= 64 && (NP & (NP - 1)) == 0, "position masks are 64-bit");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int D, int DV, int C, int MT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
+                            const float4 *__restrict__ qcoef, const uint32_t *__restrict__ qflags,
+                            float *__restrict__ state, int64_t m_pad,
+                            const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
+                            int64_t n, int64_t tok0, int nchunk, bf16_t *__restrict__ partial, float qscale,
+                            int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync) {
+    using Cfg = WsCfg<D, DV, C, MT>;
+    constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TPW = Cfg::TPW, NP = Cfg::NP, NS = Cfg::NS;
+    constexpr int KS = Cfg::KS, QS = Cfg::QS, VS = Cfg::VS, EPU = Cfg::EPU, UNITS = Cfg::UNITS, UPT = Cfg::UPT;
+    constexpr int LASTW = Cfg::LASTW;
+    extern __shared__ __align__(16) unsigned char lds[];
+    unsigned char *Bc = lds;
+    float *Kt = reinterpret_cast<float *>(lds + Cfg::OFF_K);
+    uint16_t *Vt = reinterpret_cast<uint16_t *>(lds + Cfg::OFF_V);
+    float *Qs = reinterpret_cast<float *>(lds + Cfg::OFF_Q);
+    uint32_t *W0 = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_W);
+    float4 *QC = reinterpret_cast<float4 *>(lds + Cfg::OFF_QC);
+    uint32_t *QF = reinterpret_cast<uint32_t *>(lds + Cfg::OFF_F);
+    __shared__ int64_t s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool reader = wave < Cfg::NR;
+    const int g = lane >> 4, li = lane & 15;
+    const int64_t per_sub = nbh * nslices;
+    const int64_t nitems = per_sub * nsub;
+
+    for (;;) {
+        if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u);
+        __syncthreads();
+        int64_t item = s_item;
+        __syncthreads();
+        item = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(item >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)item));
+        if (item >= nitems) break;
+        const int u = (int)(item / per_sub);
+        const int64_t rem = item % per_sub;
+        const int64_t bh = rem / nslices;
+        const int slice = (int)(rem % nslices);
+        const int cbeg = u * sub_chunks;
+        const int cend = cbeg + sub_chunks < nchunk ? cbeg + sub_chunks : nchunk;
+        if (u > 0) {   // the state of (u - 1, bh, slice) must have landed
+            if (tid == 0) {
+                for (int spin = 0; spin < (1 << 24); ++spin) {
+                    if (__hip_atomic_load(&sync[1 + rem], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)u) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+        }
+        const int64_t ps0 = (int64_t)slice * NP;
+        for (int i = tid; i < NP * 4; i += Cfg::THREADS) {
+            W0[i] = qw0[ps0 * 4 + i];
+            QC[i] = qcoef[ps0 * 4 + i];
+        }
+        for (int i = tid; i < NP; i += Cfg::THREADS) QF[i] = qflags[ps0 + i];
+        __syncthreads();
+        const uint64_t gmask = __ballot(lane < NP && (QF[lane < NP ? lane : 0] & 2u));
+        const uint64_t nmask = __ballot(lane < NP && (QF[lane < NP ? lane : 0] & 1u));
+        const bf16_t *qh = q + bh * n * D;
+        const bf16_t *kh = k + bh * n * D;
+        const bf16_t *vh = v + bh * n * DV;
+        auto chunk_t0 = [&](int cc) { return tok0 + (int64_t)cc * C; };
+        auto chunk_nv = [&](int cc) {
+            const int64_t r = n - chunk_t0(cc);
+            return r < C ? (int)r : C;
+        };
+
+        if (reader) {
+            // ------------------------------------------------ readout wavefronts
+            const int rtid = tid;                       // 0 .. 255
+            uint4 rq[UPT], rk[UPT], rv[UPT];
+            // thread rtid's units: token rtid % C, dims (rtid / C) EPU + uu DU (a thread's units
+            // share the token, as 64 NR is a multiple of C)
+            static_assert((64 * Cfg::NR) % C == 0, "units of a thread share their token");
+            constexpr int DU = (64 * Cfg::NR / C) * EPU;
+            auto gload = [&](uint4 (&r)[UPT], const bf16_t *src, int cc) {
+                const int64_t t0 = chunk_t0(cc);
+                const int nv = chunk_nv(cc);
+                const int t = rtid % C, db = (rtid / C) * EPU;
+                const bf16_t *gs = src + (t0 + t) * D + db;
+#pragma unroll
+                for (int uu = 0; uu < UPT; ++uu) {
+                    r[uu] = uint4{0u, 0u, 0u, 0u};
+                    if (db + uu * DU < D && t < nv) r[uu] = *reinterpret_cast<const uint4 *>(gs + uu * DU);
+                }
+            };
+            auto stage = [&](int cc) {                  // registers -> Qs, Kt, Vt for chunk cc
+                const int nv = chunk_nv(cc);
+                int t = rtid % C, db = (rtid / C) * EPU;
+                __asm__ volatile("" : "+v"(t), "+v"(db));   // one lane base per call, constant offsets
+                float *qd = Qs + t * QS + db;
+                float *kd = Kt + db * KS + t;
+                uint16_t *vd = Vt + db * VS + t;
+#pragma unroll
+                for (int uu = 0; uu < UPT; ++uu) {
+                    if (db + uu * DU >= D) break;
+                    float x[EPU];
+                    unpack_unit<bf16_t>(rq[uu], x);
+#pragma unroll
+                    for (int e = 0; e < EPU; e += 4)
+                        *reinterpret_cast<float4 *>(qd + uu * DU + e) =
+                            float4{x[e] * qscale, x[e + 1] * qscale, x[e + 2] * qscale, x[e + 3] * qscale};
+                    unpack_unit<bf16_t>(rk[uu], x);
+#pragma unroll
+                    for (int e = 0; e < EPU; ++e) kd[(uu * DU + e) * KS] = x[e];
+                    const uint32_t w[4] = {rv[uu].x, rv[uu].y, rv[uu].z, rv[uu].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        vd[(uu * DU + 2 * e) * VS] = (uint16_t)(w[e] & 0xffffu);
+                        vd[(uu * DU + 2 * e + 1) * VS] = (uint16_t)(w[e] >> 16);
+                    }
+                }
+                for (int tt = rtid; tt < C; tt += 64 * Cfg::NR) {
+                    *reinterpret_cast<float4 *>(Qs + tt * QS + D) = float4{1.f, 0.f, 0.f, 0.f};
+                    Kt[D * KS + tt] = 1.f;
+                    Kt[(D + 1) * KS + tt] = 0.f; Kt[(D + 2) * KS + tt] = 0.f; Kt[(D + 3) * KS + tt] = 0.f;
+                    Vt[DV * VS + tt] = tt < nv ? (uint16_t)0x3f80u : (uint16_t)0u;   // bf16 1 (valid token), 0
+                }
+            };
+            auto fetch = [&](int cc) {
+                gload(rq, qh, cc);
+                gload(rk, kh, cc);
+                gload(rv, vh, cc);
+            };
+            if (cbeg < cend) {
+                fetch(cbeg);
+                stage(cbeg);
+                if (cbeg + 1 < cend) fetch(cbeg + 1);
+            }
+            __syncthreads();   // A: first chunk staged, first state copy written
+
+            // readout geometry: tiles tt0 .. tt0 + TPW - 1; lane group g takes position 2 kk + g / 2,
+            // streams 2 (g % 2) + sl, slots z as elements 2 z + sl
+            const int tt0 = wave * TPW;
+            const int hh = g >> 1, sp = 2 * (g & 1);
+            const float *qrow[TPW];
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) qrow[tt] = Qs + (16 * (tt0 + tt) + li) * QS;
+            const bf16x8 *Bv = reinterpret_cast<const bf16x8 *>(Bc);
+            const bf16x8 *Bl = reinterpret_cast<const bf16x8 *>(Bc + Cfg::FULLB);
+            for (int cc = cbeg; cc < cend; ++cc) {
+                f32x4 Y[TPW][NT];
+                float pc[TPW][2];
+                int xo = 0;
+                auto regroup = [&](int kk) {
+                    const uint2 w2 = *reinterpret_cast<const uint2 *>(W0 + (2 * kk + hh) * 4 + sp);
+                    const int i1a = qd_i1(w2.x), i2a = qd_i2(w2.x), i1b = qd_i1(w2.y), i2b = qd_i2(w2.y);
+                    const float ca = (i1a == i2a && i1a < D) ? 0.5f : 1.f;
+                    const float cb = (i1b == i2b && i1b < D) ? 0.5f : 1.f;
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        pc[tt][0] = ca * qrow[tt][i1a] * qrow[tt][i2a];
+                        pc[tt][1] = cb * qrow[tt][i1b] * qrow[tt][i2b];
+                    }
+                    xo = 4 * qd_b(w2.x);
+                };
+                auto advance = [&](int kk) {
+                    if (((gmask >> (2 * kk - 1)) & 7u) != 0) {
+                        __asm__ volatile("" ::: "memory");
+                        regroup(kk);
+                    } else {
+                        xo += 8;
+                    }
+                };
+                auto load_b = [&](bf16x8 (&B)[NT], int kk) {
+#pragma unroll
+                    for (int nt = 0; nt + 1 < NT; ++nt) B[nt] = Bv[(kk * (NT - 1) + nt) * 64 + lane];
+                    if constexpr (LASTW == 4) {
+                        uint4 z = {0u, 0u, 0u, 0u};
+                        B[NT - 1] = __builtin_bit_cast(bf16x8, z);
+                        if (li == 0) B[NT - 1] = Bl[kk * 4 + g];
+                    } else {
+                        B[NT - 1] = Bl[kk * 64 + lane];
+                    }
+                };
+                auto form = [&](bf16x8 (&A)[TPW]) {
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
+                        const float a[8] = {pc[tt][0] * x.x, pc[tt][1] * x.x, pc[tt][0] * x.y, pc[tt][1] * x.y,
+                                            pc[tt][0] * x.z, pc[tt][1] * x.z, pc[tt][0] * x.w, pc[tt][1] * x.w};
+                        A[tt] = pack_bf16x8(a);
+                    }
+                };
+                auto mma = [&](const bf16x8 (&A)[TPW], const bf16x8 (&B)[NT]) {
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A[tt], B[nt], Y[tt][nt]);
+                };
+                // two operand sets in turn: step kk's products run while step kk + 1's are formed
+                bf16x8 A0[TPW], B0[NT], A1[TPW], B1[NT];
+                regroup(0);
+                load_b(B0, 0);
+                form(A0);
+                advance(1);
+                load_b(B1, 1);
+                form(A1);
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A0[tt], B0[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll 1
+                for (int kk = 1; kk + 2 < NS; kk += 2) {
+                    advance(kk + 1);
+                    load_b(B0, kk + 1);
+                    form(A0);
+                    mma(A1, B1);
+                    advance(kk + 2);
+                    load_b(B1, kk + 2);
+                    form(A1);
+                    mma(A0, B0);
+                }
+                mma(A1, B1);
+                __syncthreads();   // B: readout and update of chunk cc done
+
+                // partials of chunk cc: [TT][NC][16 tokens] per (bh, chunk, slice)
+                bf16_t *pdst = partial + ((bh * nchunk + cc) * nslices + slice) * (int64_t)(TT * NC * 16) +
+                               (int64_t)tt0 * NC * 16 + (li * 16 + 4 * g);
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        if (16 * nt + li < NC) store4(pdst + (tt * NC + 16 * nt) * 16, Y[tt][nt]);
+                if (cc + 1 < cend) {
+                    stage(cc + 1);
+                    if (cc + 2 < cend) fetch(cc + 2);
+                }
+                __syncthreads();   // A: next chunk staged, new state copy written
+            }
+        } else {
+            // ------------------------------------------------ update wavefronts
+            const int uw_ = wave - Cfg::NR;
+            const int p0 = uw_ * MT;
+            // tile rows: stream li % 4, slot li / 4 (a DPP quad shares its slot); accumulator rows
+            // 4 g + r: stream r, slot g
+            const int us = li & 3, uz = li >> 2;
+            float *Sh = state + bh * NC * m_pad;
+            f32x4 S[MT][NT];
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t qd = (ps0 + p0 + j) * 4 + r;
+                    const uint32_t w = qw0[qd];
+                    const int32_t c0 = qcidx[qd];
+                    const uint32_t mask = qd_mask(w);
+                    const int z0 = mask ? __builtin_ctz(mask) : 0;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int c = 16 * nt + li;
+                        const bool ok = ((mask >> g) & 1u) && c < NC;
+                        S[j][nt][r] = ok ? Sh[(int64_t)c * m_pad + c0 + (g - z0)] : 0.f;
+                    }
+                }
+            uint32_t uw[MT];
+            uint32_t newgrp = 0;
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+                uw[j] = W0[(p0 + j) * 4 + us];
+                if (QF[p0 + j] & 2u) newgrp |= 1u << j;
+            }
+            newgrp = (uint32_t)__builtin_amdgcn_readfirstlane((int)newgrp);
+            const uint32_t mixed = (uint32_t)((nmask >> p0) & ((1ull << MT) - 1));
+
+            auto slot_ratio = [&](int p, float (&r4)[4]) {
+                const float *qcf = reinterpret_cast<const float *>(QC);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t w = W0[p * 4 + r];
+                    const float rinv = (qd_i1(w) == qd_i2(w) && qd_i1(w) < D) ? 2.f : 1.f;
+                    r4[r] = qcf[(p * 4 + r) * 4 + g] * rinv;
+                }
+            };
+            // state accumulators -> state copy (slot weight over pair weight at mixed positions).
+            // Position p0 + j, streams 2 h2 and 2 h2 + 1 of slot g: K step p0 / 2 + j / 2, reader
+            // lane group 2 (j % 2) + h2 (p0 is even), word g of the 16-byte entry.  One lane base
+            // per call (kept opaque so that the compiler does not hold an address per entry through
+            // the chunk loop); every entry is a constant offset from it.
+            static_assert(MT % 2 == 0, "positions of an update wavefront pair up in K steps");
+            auto write_bcopy = [&]() {
+                int lb = (p0 / 2) * (NT - 1) * 256 + li * 4 + g;
+                int lbl = LASTW == 4 ? (p0 / 2) * 16 + g : (p0 / 2) * 256 + li * 4 + g;
+                __asm__ volatile("" : "+v"(lb), "+v"(lbl));
+                uint32_t *B4 = reinterpret_cast<uint32_t *>(Bc) + lb;
+                uint32_t *BL4 = reinterpret_cast<uint32_t *>(Bc + Cfg::FULLB) + lbl;
+                auto put = [&](int j, int nt, int h2, uint32_t val) {
+                    const int kj = j >> 1, gr = 2 * (j & 1) + h2;
+                    if (nt + 1 < NT) {
+                        B4[(kj * (NT - 1) + nt) * 256 + gr * 64] = val;
+                    } else if constexpr (LASTW == 4) {
+                        if (li == 0) BL4[kj * 16 + gr * 4] = val;
+                    } else {
+                        BL4[kj * 256 + gr * 64] = val;
+                    }
+                };
+#pragma unroll
+                for (int j = 0; j < MT; ++j)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        put(j, nt, 0, pack_bf16x2(S[j][nt][0], S[j][nt][1]));
+                        put(j, nt, 1, pack_bf16x2(S[j][nt][2], S[j][nt][3]));
+                    }
+#pragma unroll
+                for (int j = 0; j < MT; ++j) {
+                    if ((mixed >> j) & 1u) {
+                        float r4[4];
+                        slot_ratio(p0 + j, r4);
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            put(j, nt, 0, pack_bf16x2(S[j][nt][0] * r4[0], S[j][nt][1] * r4[1]));
+                            put(j, nt, 1, pack_bf16x2(S[j][nt][2] * r4[2], S[j][nt][3] * r4[3]));
+                        }
+                    }
+                }
+            };
+            write_bcopy();
+            __syncthreads();   // A
+
+            constexpr int NKS = C / 32;
+            const bf16_t *V16 = reinterpret_cast<const bf16_t *>(Vt);
+            auto load_v = [&](bf16x8 (&B)[NT], int ks) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    uint4 z = {0u, 0u, 0u, 0u};
+                    if (16 * nt + li < NC) z = *reinterpret_cast<const uint4 *>(V16 + (16 * nt + li) * VS + 32 * ks + 8 * g);
+                    B[nt] = __builtin_bit_cast(bf16x8, z);
+                }
+            };
+            auto load_k3 = [&](int j, int ks) {
+                return *reinterpret_cast<const float2 *>(Kt + (4 * qd_b(uw[j]) + uz) * KS + 32 * ks + 8 * g + 2 * us);
+            };
+            for (int cc = cbeg; cc < cend; ++cc) {
+                // S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1], the chunk's K steps outer
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    bf16x8 B[NT];
+                    load_v(B, ks);
+                    const int tb = 32 * ks + 8 * g;
+                    float p2[8];
+                    float2 kc = load_k3(0, ks);
+#pragma unroll
+                    for (int j = 0; j < MT; ++j) {
+                        const uint32_t w = uw[j];
+                        if (j == 0 || ((newgrp >> j) & 1u)) {
+                            __asm__ volatile("" ::: "memory");   // keep the reload behind its (uniform) branch
+                            const float4 *k1 = reinterpret_cast<const float4 *>(Kt + qd_i1(w) * KS + tb);
+                            const float4 *k2 = reinterpret_cast<const float4 *>(Kt + qd_i2(w) * KS + tb);
+                            const float4 a0 = k1[0], a1 = k1[1], b0 = k2[0], b1 = k2[1];
+                            p2[0] = a0.x * b0.x; p2[1] = a0.y * b0.y; p2[2] = a0.z * b0.z; p2[3] = a0.w * b0.w;
+                            p2[4] = a1.x * b1.x; p2[5] = a1.y * b1.y; p2[6] = a1.z * b1.z; p2[7] = a1.w * b1.w;
+                        }
+                        float2 kn = kc;
+                        if (j + 1 < MT) kn = load_k3(j + 1, ks);
+                        const float x = kc.x, y = kc.y;
+                        float a[8] = {p2[0] * quad_bcast<0>(x), p2[1] * quad_bcast<0>(y),
+                                      p2[2] * quad_bcast<1>(x), p2[3] * quad_bcast<1>(y),
+                                      p2[4] * quad_bcast<2>(x), p2[5] * quad_bcast<2>(y),
+                                      p2[6] * quad_bcast<3>(x), p2[7] * quad_bcast<3>(y)};
+                        const bf16x8 A = pack_bf16x8(a);
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_bf16(A, B[nt], S[j][nt]);
+                        kc = kn;
+                    }
+                }
+                __syncthreads();   // B
+                write_bcopy();
+                __syncthreads();   // A
+            }
+            // accumulators -> state slice (the memory clobber makes the compiler recompute the
+            // addresses instead of holding the load's ones through the chunk loop)
+            __asm__ volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t qd = (ps0 + p0 + j) * 4 + r;
+                    const uint32_t w = qw0[qd];
+                    const int32_t c0 = qcidx[qd];
+                    const uint32_t mask = qd_mask(w);
+                    const int z0 = mask ? __builtin_ctz(mask) : 0;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int c = 16 * nt + li;
+                        if (((mask >> g) & 1u) && c < NC) Sh[(int64_t)c * m_pad + c0 + (g - z0)] = S[j][nt][r];
+                    }
+                }
+        }
+        // every wave's state stores reach L2 before the barrier; thread 0's agent-scope release
+        // then writes L2 back before the flag
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(&sync[1 + rem], (uint32_t)(u + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Kernel 2: y = (direct intra-chunk term) + sum over slices of the partials
 // (fixed order), o = y[:d_V] / y[d_V].  Partial layout per (bh, chunk, slice):
 // [C/16][d_V+1][16 tokens] fp32.  Every thread first adds the slices' partials
@@ -1104,18 +1546,25 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename Part
 // at 4.  (The kernel also supports eight wavefronts of fewer positions each.)
 struct ScanShape {
     int nw, mt;
+    bool ws;   // warp-specialised kernel: 4 update wavefronts of mt positions, 4 readout wavefronts
 };
 static ScanShape pick_shape(const sata_index *idx, int64_t bh, int chunk, sata_dtype in_dt) {
     const int64_t npos = idx->nq / 4;
-    // bf16 inputs, 128-token chunks: eight wavefronts (two per SIMD, each hiding the other's
-    // latency) with four or two positions each
-    if (in_dt == SATA_BF16 && chunk == 128) return {8, bh * ((npos + 31) / 32) >= 256 ? 4 : 2};
+    // bf16 inputs.  d_K = 64 in 128-token chunks: eight wavefronts that each read out and update
+    // (four or two positions each); the warp-specialised kernel holds too few positions per
+    // wavefront there.  Otherwise the warp-specialised kernel, 32 positions per slice when that
+    // still gives every CU a slice, else 16.
+    if (in_dt == SATA_BF16) {
+        const bool many = bh * ((npos + 31) / 32) >= 256;
+        if (idx->dk == 64 && chunk == 128) return {8, many ? 4 : 2, false};
+        return {8, many ? 8 : 4, true};
+    }
     for (int mt : {8, 4}) {
         if (mt == 8 && in_dt == SATA_F32) continue;
         const int64_t per = (int64_t)kNW * mt;
-        if (bh * ((npos + per - 1) / per) >= 256) return {kNW, mt};
+        if (bh * ((npos + per - 1) / per) >= 256) return {kNW, mt, false};
     }
-    return {kNW, 2};
+    return {kNW, 2, false};
 }
 
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt) {
@@ -1123,9 +1572,10 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     p.chunk = chunk ? chunk : (idx->dk == 64 ? 128 : 64);
     if (p.chunk != 64 && p.chunk != 128) return p;
     const ScanShape sh = pick_shape(idx, bh, p.chunk, in_dt);
+    p.ws = sh.ws;
     p.fw = 16 * sh.mt;
-    p.fs = sh.nw * p.fw;
-    const int64_t np_slice = (int64_t)sh.nw * sh.mt;
+    const int64_t np_slice = (int64_t)(sh.ws ? 4 : sh.nw) * sh.mt;
+    p.fs = (int)(16 * np_slice);
     const int64_t npos = idx->nq / 4;
     p.slices = (int)((npos + np_slice - 1) / np_slice);
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
@@ -1140,13 +1590,29 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     return p;
 }
 
-template <int D, int C, int MT, int NW, typename TIn, typename TOut>
+// The scan kernel and its launch shape: the general kernel, or the warp-specialised one.
+template <int D, int C, int MT, int NW, typename TIn, bool WS>
+struct ScanSel {
+    using Cfg = ScanCfg<D, D, C, MT, NW, TIn>;
+    static constexpr int THREADS = Cfg::THREADS, LDS = Cfg::LDS;
+    static constexpr bool PERSIST = Cfg::PERSIST;
+    static constexpr auto kernel = prefill_scan_kernel<D, D, C, MT, NW, TIn>;
+};
+template <int D, int C, int MT, int NW>
+struct ScanSel<D, C, MT, NW, bf16_t, true> {
+    using Cfg = WsCfg<D, D, C, MT>;
+    static constexpr int THREADS = Cfg::THREADS, LDS = Cfg::LDS;
+    static constexpr bool PERSIST = true;
+    static constexpr auto kernel = prefill_scan_ws_kernel<D, D, C, MT>;
+};
+
+template <int D, int C, int MT, int NW, typename TIn, typename TOut, bool WS = false>
 static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                               const void *q, const void *k, const void *v, void *out, int64_t n,
                               hipStream_t stream) {
-    using Cfg = ScanCfg<D, D, C, MT, NW, TIn>;
+    using Cfg = ScanSel<D, C, MT, NW, TIn, WS>;
     const int64_t bh = (int64_t)st->batch * st->heads;
-    auto scan = prefill_scan_kernel<D, D, C, MT, NW, TIn>;
+    auto scan = Cfg::kernel;
     auto red = prefill_reduce_kernel<D, D, C, TIn, TOut>;
     hipError_t e = hipFuncSetAttribute((const void *)scan, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
     if (e != hipSuccess) return e;
@@ -1221,6 +1687,20 @@ static hipError_t run_d(const sata_index *idx, const sata_state *st, const Prefi
                         const void *q, const void *k, const void *v, void *out, int64_t n,
                         sata_dtype in_dt, sata_dtype out_dt, hipStream_t s) {
     const int mt = plan.fw / 16, nw = plan.fs / plan.fw;
+    if (plan.ws) {
+        if (in_dt != SATA_BF16) return hipErrorInvalidValue;   // never planned
+        auto go = [&](auto cw, auto mw) -> hipError_t {
+            constexpr int CC = decltype(cw)::value, MM = decltype(mw)::value;
+            if (out_dt == SATA_F32) return run_prefill<D, CC, MM, 8, bf16_t, float, true>(idx, st, plan, q, k, v, out, n, s);
+            return run_prefill<D, CC, MM, 8, bf16_t, bf16_t, true>(idx, st, plan, q, k, v, out, n, s);
+        };
+        using I64 = std::integral_constant<int, 64>;
+        using I128 = std::integral_constant<int, 128>;
+        using M4 = std::integral_constant<int, 4>;
+        using M8 = std::integral_constant<int, 8>;
+        if (plan.chunk == 64) return mt == 8 ? go(I64{}, M8{}) : go(I64{}, M4{});
+        return mt == 8 ? go(I128{}, M8{}) : go(I128{}, M4{});
+    }
     if (nw == 8) {
         if (plan.chunk != 128 || in_dt != SATA_BF16) return hipErrorInvalidValue;   // never planned
         if (mt == 2) return run_dt<D, 128, 2, 8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);

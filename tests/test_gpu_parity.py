@@ -119,12 +119,14 @@ def test_all_shapes_ragged_every_row(sata, oracle, d, P, dtype):
 
 @pytest.mark.parametrize("d", [8, 16, 32, 64])
 @pytest.mark.parametrize("heads", [1, 64])
-def test_bf16_chunk128_every_row(sata, oracle, d, heads):
-    """bf16 inputs in 128-token chunks (eight wavefronts per workgroup): few heads give two
-    positions per wavefront, many heads four; n = 2 chunks + a ragged tail, every row."""
-    P, chunk = 4, 128
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_bf16_eight_wave_shapes_every_row(sata, oracle, d, heads, chunk):
+    """bf16 inputs run on eight wavefronts per workgroup (d_K = 64 in 128-token chunks: every
+    wavefront reads out and updates; otherwise readout and update wavefronts apart).  Few heads
+    give the smaller slices, many heads the larger; n = 2 chunks + a ragged tail, every row."""
+    P = 4
     n = 2 * chunk + 45
-    say("prefill bf16 chunk 128 d=%d heads=%d n=%d" % (d, heads, n))
+    say("prefill bf16 chunk %d d=%d heads=%d n=%d" % (chunk, d, heads, n))
     x = si.draw_qkv((1, heads), n, d, d, 5151 + d + heads, "bf16")
     idx = sata.Index(d, d, P)
     st = sata.State(idx, 1, heads)
