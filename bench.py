@@ -271,8 +271,8 @@ COPY_BYTES = 1 << 30
 # kernel-name pattern -> (kernel, workload, source file)
 TRAFFIC_KERNELS = [
     (r"prefill_scan_kernel<64, 64, 128, \d+, \d+, unsigned short>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
-    (r"prefill_scan_kernel<32, 32, 64, \d+, \d+, unsigned short>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
-    (r"prefill_scan_kernel<16, 16, 128, \d+, \d+, unsigned short>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
+    (r"prefill_scan_ws_kernel<32, 32, 64, \d+>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
+    (r"prefill_scan_ws_kernel<16, 16, 128, \d+>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
     (r"decode_kernel<64, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
 
