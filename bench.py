@@ -93,11 +93,12 @@ def prefill_flops(wl) -> float:
     return 4.0 * features(wl.d_k, wl.P) * (wl.d_v + 1) * wl.batch * wl.heads * wl.n
 
 
-def decode_bytes(wl) -> float:
-    """Algorithmic HBM bytes of one decode step: every head's fp32 state read
-    and written once, plus the token's q, k, v in and out's write."""
+def decode_bytes(wl, state_elem: int = 4) -> float:
+    """Algorithmic HBM bytes of one decode step: every head's state (fp32, or
+    bf16 with state_elem = 2) read and written once, plus the token's fp32
+    q, k, v in and out's write."""
     m = features(wl.d_k, wl.P)
-    return float(wl.batch * wl.heads * (8 * m * (wl.d_v + 1) + 4 * (2 * wl.d_k + 2 * wl.d_v)))
+    return float(wl.batch * wl.heads * (2 * state_elem * m * (wl.d_v + 1) + 4 * (2 * wl.d_k + 2 * wl.d_v)))
 
 
 # ------------------------------------------------------------------ prefill
@@ -203,11 +204,19 @@ def time_decode(sata, idx, st, wl, steps: int, warmup: int, seed: int):
 
 
 def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
+    import torch
     idx = sata.Index(wl.d_k, wl.d_v, wl.P)
     log("decode: fp32 prefill of %d tokens x %d heads" % (wl.n, wl.batch * wl.heads))
     st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
     ms, kern_ms, fin_ms = time_decode(sata, idx, st, wl, steps, warmup, wl.seed + 30)
+    st16 = sata.State(idx, wl.batch, wl.heads, dtype=torch.bfloat16)
+    sata.sata_state_convert(st, st16)
     st.free()
+    log("decode: the same state converted to bf16 storage")
+    ms16, kern16, fin16 = time_decode(sata, idx, st16, wl, steps, warmup, wl.seed + 30)
+    st16.free()
+    nbytes16 = decode_bytes(wl, 2)
+    ach16 = nbytes16 / (kern16 * 1e-3) / 1e9
     nbytes = decode_bytes(wl)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     res = {
@@ -220,6 +229,15 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
         },
         "finish_ms_per_step": fin_ms,
         "gbs_whole_step": nbytes / (ms * 1e-3) / 1e9,
+        "bf16_state": {
+            "value": wl.batch / (ms16 * 1e-3), "unit": "tokens/s", "ms_per_step": ms16,
+            "roofline": {
+                "bound": "hbm", "achieved": ach16, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach16 / PEAK_HBM_GBS, "kernel": "decode_stream", "avg_launch_ms": kern16,
+                "bytes_per_launch": nbytes16, "traffic": traffic_for("decode_stream_bf16", wl.name),
+            },
+            "finish_ms_per_step": fin16,
+        },
     }
     if flatness:
         flat = {}
@@ -273,7 +291,8 @@ TRAFFIC_KERNELS = [
     (r"prefill_scan_kernel<64, 64, 128, \d+, \d+, unsigned short>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
     (r"prefill_scan_ws_kernel<32, 32, 64, \d+>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
     (r"prefill_scan_ws_kernel<16, 16, 128, \d+>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
-    (r"decode_kernel<64, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_kernel<64, float, unsigned short>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
 
 
@@ -310,7 +329,12 @@ def traffic_run():
     st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
     time_decode(sata, idx, st, wl, 2, 0, wl.seed + 30)
     log("traffic run: decode done")
+    st16 = sata.State(idx, wl.batch, wl.heads, dtype=torch.bfloat16)
+    sata.sata_state_convert(st, st16)
     st.free()
+    time_decode(sata, idx, st16, wl, 2, 0, wl.seed + 30)
+    log("traffic run: bf16-state decode done")
+    st16.free()
     idx.free()
 
 
@@ -420,6 +444,9 @@ def main():
         dec = decode_section(sata, dwl, args.decode_steps, 8, not args.no_flatness)
         log("decode: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak)"
             % (dec["ms_per_step"], dec["value"], dec["roofline"]["achieved"], 100 * dec["roofline"]["frac"]))
+        b16 = dec["bf16_state"]
+        log("decode, bf16 state: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak)"
+            % (b16["ms_per_step"], b16["value"], b16["roofline"]["achieved"], 100 * b16["roofline"]["frac"]))
         result["decode"] = dec
         torch.cuda.empty_cache()
 

@@ -399,11 +399,13 @@ sata_status sata_index_info(const sata_index *idx, int *d_k, int *d_v, int *P, i
     return SATA_OK;
 }
 
-sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *stream, sata_state **out) {
+sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, sata_dtype state_dt, void *stream,
+                                   sata_state **out) {
     g_last_error.clear();
     if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
     if (!out) return fail(SATA_ERR_INVALID, "out is NULL");
     if (batch < 1 || heads < 1) return fail(SATA_ERR_INVALID, "batch and heads must be >= 1 (%d, %d)", batch, heads);
+    if (!valid_dtype(state_dt)) return fail(SATA_ERR_INVALID, "unknown state dtype");
     const int64_t bh = (int64_t)batch * heads;
     if (bh > 65535) return fail(SATA_ERR_UNSUPPORTED, "batch*heads <= 65535 supported (got %lld)", (long long)bh);
     DeviceGuard g(idx->device);
@@ -414,14 +416,17 @@ sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *
     st->batch = batch;
     st->heads = heads;
     st->device = idx->device;
-    st->state_bytes = bh * (idx->dv + 1) * idx->m_pad * (int64_t)sizeof(float);
+    st->dtype = state_dt;
+    // m_pad is a multiple of 64, so the byte size is a multiple of 4 for either dtype
+    st->state_bytes = bh * (idx->dv + 1) * idx->m_pad * dtype_bytes(state_dt);
     hipError_t e = hipMalloc(&st->d_state, (size_t)st->state_bytes);
     if (e != hipSuccess) {
         (void)hipGetLastError();
+        const long long nbytes = (long long)st->state_bytes;
         delete st;
-        return fail(SATA_ERR_OOM, "state allocation of %lld bytes failed", (long long)bh * (idx->dv + 1) * idx->m_pad * 4);
+        return fail(SATA_ERR_OOM, "state allocation of %lld bytes failed", nbytes);
     }
-    e = sata::launch_zero(st->d_state, st->state_bytes / 4, (hipStream_t)stream);
+    e = sata::launch_zero(static_cast<float *>(st->d_state), st->state_bytes / 4, (hipStream_t)stream);
     if (e != hipSuccess) {
         (void)hipFree(st->d_state);
         delete st;
@@ -431,11 +436,29 @@ sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *
     return SATA_OK;
 }
 
+sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *stream, sata_state **out) {
+    return sata_state_alloc_dtype(idx, batch, heads, SATA_F32, stream, out);
+}
+
+sata_status sata_state_convert(const sata_state *src, sata_state *dst, void *stream) {
+    g_last_error.clear();
+    if (!src || !dst) return fail(SATA_ERR_INVALID, "src and dst must be non-NULL");
+    if (src == dst) return fail(SATA_ERR_INVALID, "src and dst must be different states");
+    if (src->idx != dst->idx) return fail(SATA_ERR_INVALID, "src and dst were allocated for different indexes");
+    if (src->batch != dst->batch || src->heads != dst->heads)
+        return fail(SATA_ERR_INVALID, "src and dst differ in batch or heads");
+    DeviceGuard g(dst->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    hipError_t e = sata::launch_state_convert(src, dst, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "state conversion");
+    return SATA_OK;
+}
+
 sata_status sata_state_reset(sata_state *st, void *stream) {
     g_last_error.clear();
     if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
     DeviceGuard g(st->device);
-    hipError_t e = sata::launch_zero(st->d_state, st->state_bytes / 4, (hipStream_t)stream);
+    hipError_t e = sata::launch_zero(static_cast<float *>(st->d_state), st->state_bytes / 4, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "state clear");
     return SATA_OK;
 }
@@ -465,6 +488,8 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     if (chunk != 0 && chunk != 64 && chunk != 128)
         return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
     if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
+    if (st->dtype != SATA_F32)
+        return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 state with sata_state_convert)");
     if (n == 0) return SATA_OK;
     if (!q || !k || !v || !out) return fail(SATA_ERR_INVALID, "q, k, v and out must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))

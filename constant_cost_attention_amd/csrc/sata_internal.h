@@ -43,7 +43,8 @@ struct sata_state {
     const sata_index *idx = nullptr;
     int batch = 0, heads = 0;
     int device = 0;
-    float *d_state = nullptr;    // [B*H][d_V+1][m_pad]
+    sata_dtype dtype = SATA_F32; // element type of the state
+    void *d_state = nullptr;     // [B*H][d_V+1][m_pad] of dtype
     int64_t state_bytes = 0;
     void *d_work = nullptr;      // prefill / decode partial sums (grown on demand)
     int64_t work_bytes = 0;
@@ -76,6 +77,7 @@ hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void
                          const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt,
                          hipStream_t stream);
 int64_t decode_workspace_bytes(const sata_index *idx, int64_t bh);
+hipError_t launch_state_convert(const sata_state *src, sata_state *dst, hipStream_t stream);
 
 // Prefill plan: how the sequence is split into chunks, feature slices and
 // segments, and how large the partial-sum workspace must be.

@@ -1650,7 +1650,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
             ProfScope ps(kProfScan, stream);
             hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(Cfg::THREADS), Cfg::LDS, stream,
                                idx->d_qw0, idx->d_qcidx, reinterpret_cast<const float4 *>(idx->d_qcoef),
-                               idx->d_qflags, st->d_state, idx->m_pad, static_cast<const TIn *>(q),
+                               idx->d_qflags, static_cast<float *>(st->d_state), idx->m_pad, static_cast<const TIn *>(q),
                                static_cast<const TIn *>(k), static_cast<const TIn *>(v), n, tok0, nseg,
                                partial, ta.scale, plan.slices, bh, nsub, sub_chunks, sync);
         }

@@ -24,7 +24,8 @@ SATA_F32, SATA_BF16 = 0, 1
 
 _EXPORTS = (
     "sata_build_index", "sata_index_free", "sata_index_features", "sata_index_info",
-    "sata_state_alloc", "sata_state_reset", "sata_state_free", "sata_state_data",
+    "sata_state_alloc", "sata_state_alloc_dtype", "sata_state_convert", "sata_state_reset", "sata_state_free",
+    "sata_state_data",
     "sata_prefill", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
@@ -67,6 +68,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_index_info.argtypes = [vp, ctypes.POINTER(cint), ctypes.POINTER(cint), ctypes.POINTER(cint),
                                     ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.sata_state_alloc.argtypes = [vp, cint, cint, vp, pvp]
+    lib.sata_state_alloc_dtype.argtypes = [vp, cint, cint, cint, vp, pvp]
+    lib.sata_state_convert.argtypes = [vp, vp, vp]
     lib.sata_state_reset.argtypes = [vp, vp]
     lib.sata_state_free.argtypes = [vp]
     lib.sata_state_free.restype = None
@@ -88,7 +91,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_profile_query.argtypes = [cint, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     lib.sata_profile_kernel_name.argtypes = [cint]
     lib.sata_profile_kernel_name.restype = ctypes.c_char_p
-    for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_reset",
+    for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_alloc_dtype",
+                 "sata_state_convert", "sata_state_reset",
                  "sata_state_data", "sata_prefill", "sata_decode_step", "sata_expand_features"):
         getattr(lib, name).restype = cint
     _lib = lib
@@ -98,6 +102,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
 def _check(status: int, func: str):
     if status != SATA_OK:
         raise SataError(status, func, load().sata_last_error().decode())
+
+
+_DTYPES = {torch.float32: SATA_F32, torch.bfloat16: SATA_BF16}
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -144,12 +151,17 @@ class Index:
 
 
 class State:
-    """Handle of sata_state (fixed-size state of batch x heads heads)."""
+    """Handle of sata_state (fixed-size state of batch x heads heads); dtype is
+    torch.float32 (default) or torch.bfloat16 (decode only)."""
 
-    def __init__(self, index: Index, batch: int, heads: int, stream=None):
+    def __init__(self, index: Index, batch: int, heads: int, stream=None, dtype=torch.float32):
         self.index = index
         self.batch, self.heads = batch, heads
-        self.ptr = sata_state_alloc(index, batch, heads, stream)
+        self.dtype = dtype
+        if dtype == torch.float32:
+            self.ptr = sata_state_alloc(index, batch, heads, stream)
+        else:
+            self.ptr = sata_state_alloc_dtype(index, batch, heads, _DTYPES.get(dtype, -1), stream)
 
     def free(self):
         if self.ptr:
@@ -194,6 +206,18 @@ def sata_state_alloc(index: Index, batch: int, heads: int, stream=None) -> ctype
     return out
 
 
+def sata_state_alloc_dtype(index: Index, batch: int, heads: int, state_dt: int, stream=None) -> ctypes.c_void_p:
+    out = ctypes.c_void_p()
+    _check(load().sata_state_alloc_dtype(index.ptr, int(batch), int(heads), int(state_dt), _stream(stream),
+                                         ctypes.byref(out)), "sata_state_alloc_dtype")
+    return out
+
+
+def sata_state_convert(src: State, dst: State, stream=None):
+    """Copy src into dst, converting the element type (fp32 -> bf16 rounds to nearest even)."""
+    _check(load().sata_state_convert(src.ptr, dst.ptr, _stream(stream)), "sata_state_convert")
+
+
 def sata_state_reset(state: State, stream=None):
     _check(load().sata_state_reset(state.ptr, _stream(stream)), "sata_state_reset")
 
@@ -218,12 +242,15 @@ class _CudaArray:
 
 
 def state_tensor(state: State) -> torch.Tensor:
-    """The state buffer viewed as a float32 tensor [B, H, d_V+1, m_pad] (no copy)."""
+    """The state buffer viewed as a tensor [B, H, d_V+1, m_pad] of the state's dtype (no copy)."""
     ptr, nbytes = sata_state_data(state)
     idx = state.index
     shape = (state.batch, state.heads, idx.d_v + 1, idx.m_pad)
-    assert nbytes == 4 * shape[0] * shape[1] * shape[2] * shape[3]
-    return torch.as_tensor(_CudaArray(ptr, shape, "<f4"), device="cuda")
+    if state.dtype == torch.float32:
+        assert nbytes == 4 * shape[0] * shape[1] * shape[2] * shape[3]
+        return torch.as_tensor(_CudaArray(ptr, shape, "<f4"), device="cuda")
+    assert nbytes == 2 * shape[0] * shape[1] * shape[2] * shape[3]
+    return torch.as_tensor(_CudaArray(ptr, shape, "<i2"), device="cuda").view(torch.bfloat16)
 
 
 def sata_prefill(index: Index, state: State, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -104,6 +104,26 @@ sata_status sata_index_info(const sata_index *idx, int *d_k, int *d_v, int *P,
 sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *stream,
                              sata_state **out);
 
+/* As sata_state_alloc, with the state's element type chosen: SATA_F32 (what
+ * sata_state_alloc gives) or SATA_BF16, same layout, half the bytes.  A bf16
+ * state serves sata_decode_step only: each step widens the stored values to
+ * fp32, adds the new token's term, reads out from the fp32 sums and stores them
+ * rounded to the nearest bf16 (ties to even), so the step streams half the
+ * bytes of the fp32 state [hotdry, "Hardware optimisation paths and current
+ * limits": half-precision storage halves the bandwidth of the state] at the
+ * price of one bf16 rounding per element per step.  sata_prefill on it returns
+ * SATA_ERR_UNSUPPORTED: prefill into an fp32 state and convert.  An unknown
+ * state_dt returns SATA_ERR_INVALID. */
+sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, sata_dtype state_dt,
+                                   void *stream, sata_state **out);
+
+/* Copy src's content into dst, converting the element type (fp32 -> bf16
+ * rounds to nearest even; bf16 -> fp32 is exact; equal types copy).  Both must
+ * belong to the same index and have the same batch and heads; src != dst
+ * (else SATA_ERR_INVALID, nothing enqueued).  Enqueued on `stream`; dst's
+ * workspace is untouched. */
+sata_status sata_state_convert(const sata_state *src, sata_state *dst, void *stream);
+
 /* Zero the state (start a new sequence); enqueued on `stream`. */
 sata_status sata_state_reset(sata_state *st, void *stream);
 
@@ -111,7 +131,8 @@ sata_status sata_state_reset(sata_state *st, void *stream);
 void sata_state_free(sata_state *st);
 
 /* Device pointer and byte size of the state buffer (for checkpointing or
- * inspection; the layout is given at sata_state_alloc). */
+ * inspection; the layout is given at sata_state_alloc, elements of the type
+ * given at allocation). */
 sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes);
 
 /* Causal prefill of n tokens for every head of the state, continuing from the

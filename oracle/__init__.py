@@ -24,6 +24,8 @@ Functions (what pins each one is listed in the tests and in the design notes):
 * ``phi``                O4, symmetric feature map from the O3 groups.
 * ``recurrent_attention`` O5, the constant-size state form (tiny inputs).
 * ``recurrent_attention_f32`` O7, O5 carried out in float (diagnostic).
+* ``round_bf16``         O8a, round to nearest bfloat16, ties to even.
+* ``bf16_state_decode``  O8, decode steps on a state stored in bf16.
 * ``basis_size``, ``state_size``, ``flops_per_token`` O6, the closed forms the
   page prints, in exact integers.
 """
@@ -75,6 +77,10 @@ def _load():
     lib.orc_basis_bruteforce.restype = i64
     lib.orc_phi.argtypes = [f64p, cint, cint, f64p, i64]
     lib.orc_phi.restype = i64
+    lib.orc_round_bf16_array.argtypes = [f64p, f64p, i64]
+    lib.orc_round_bf16_array.restype = None
+    lib.orc_bf16_state_decode.argtypes = [f32p, f32p, f32p, f64p, i64, i64, i64, cint, cint, cint, cint]
+    lib.orc_bf16_state_decode.restype = cint
     for name in ("orc_recurrent_attention", "orc_recurrent_attention_f32"):
         fn = getattr(lib, name)
         fn.argtypes = [f32p, f32p, f32p, f64p, i64, i64, cint, cint, cint]
@@ -207,6 +213,38 @@ def recurrent_attention_f32(q, k, v, P: int) -> np.ndarray:
     """O7: O5 with the state and arithmetic in float32 (diagnostic of the error
     that fp32 state accumulation carries by itself)."""
     return _recurrent("orc_recurrent_attention_f32", q, k, v, P)
+
+
+def round_bf16(x) -> np.ndarray:
+    """O8a: round to the nearest bfloat16 value, ties to even (8 significant
+    bits, binary32 exponent range), returned as float64."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(a)
+    _load().orc_round_bf16_array(a.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), a.size)
+    return out
+
+
+def bf16_state_decode(q, k, v, P: int, n0: int, rounding: bool = True) -> np.ndarray:
+    """O8: decode steps on a bf16-stored state [hotdry, "Hardware optimisation
+    paths and current limits": 16-bit storage of the state].  Tokens 0..n0-1
+    are summed exactly into the one-sided state and rounded once; each later
+    token is added exactly, read out from the unrounded sums and the sums are
+    rounded to bf16 (ties to even) when stored.  Returns rows n0..n-1:
+    [..., n - n0, d_V].  rounding=False gives the exact one-sided recurrent
+    form.  fp64; moderate inputs."""
+    lead, bh, n, dk, dv = _heads(np.asarray(q), np.asarray(k), np.asarray(v))
+    if not 0 <= n0 <= n:
+        raise ValueError("need 0 <= n0 <= n")
+    q32, qp = _f32(q)
+    k32, kp = _f32(k)
+    v32, vp = _f32(v)
+    out = np.empty((bh, n - n0, dv), dtype=np.float64)
+    rc = _load().orc_bf16_state_decode(qp, kp, vp, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                       bh, int(n0), n, dk, dv, int(P), 1 if rounding else 0)
+    if rc:
+        raise ValueError("orc_bf16_state_decode rejected its arguments")
+    return out.reshape(tuple(lead) + (n - n0, dv))
 
 
 # ---------------------------------------------------------------- closed forms (O6)

@@ -330,3 +330,155 @@ int NAME(const float *q, const float *k, const float *v, double *out,           
 
 DEFINE_RECURRENT(orc_recurrent_attention, double)
 DEFINE_RECURRENT(orc_recurrent_attention_f32, float)
+
+/* ------------------------------------------------------------------ */
+/* O8: decode on a state stored in bf16                                */
+/* ------------------------------------------------------------------ */
+
+/* Rounds x to the nearest bfloat16 value, ties to even: 8 significant bits
+ * (7 stored plus the implicit one) and the exponent range of binary32, with
+ * gradual underflow below 2^-126.  Inputs here are finite and far below
+ * bf16's largest value; a result beyond it becomes +-inf.  nearbyint() in the
+ * default rounding mode rounds half-way cases to even. */
+double orc_round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    (void)frexp(x, &e);              /* x = f * 2^e, 0.5 <= |f| < 1 */
+    if (e < -125) e = -125;          /* subnormal range: fixed quantum 2^-133 */
+    const double r = ldexp(nearbyint(ldexp(x, 8 - e)), e - 8);
+    return fabs(r) > 0x1.fep127 ? copysign(INFINITY, r) : r;
+}
+
+void orc_round_bf16_array(const double *x, double *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_round_bf16(x[i]);
+}
+
+/* Decode steps on a state whose stored elements are bfloat16.
+ *
+ * The state is the one of the recurrent form [hotdry, "Engineering
+ * realisation of the constant compute cost"] kept in the layout the library
+ * documents: for every sorted index tuple t of order p < P (the minimal basis
+ * [hotdry, "Core insight of symmetric tensor decomposition"]) the key side
+ * carries the plain monomial prod_r k[t_r], so element (t, c) holds
+ * sum_s prod_r k_s[t_r] * [v_s, 1][c]; the query side carries
+ * prod_r q[t_r] * (p!/alpha_t!) / (p! d^(p/2)), where p!/alpha_t! is the
+ * number of ordered tuples sorting to t.
+ *
+ * Storing the elements in a 16-bit format is the page's suggestion for
+ * halving the state's bandwidth [hotdry, "Hardware optimisation paths and
+ * current limits"]; the reading taken here: the tokens 0..n0-1 are summed
+ * exactly and rounded once (a prefill in full precision, then converted);
+ * every later token s is added to the stored values exactly, read out from
+ * those unrounded sums, and the sums are rounded to bf16 when stored back.
+ * Rows n0..n-1 are written to out: [bh][n - n0][dv].
+ *
+ * round_mode 0 skips every rounding: the exact one-sided recurrent form.
+ * Tiny to moderate inputs; returns nonzero on bad arguments. */
+/* The summed prefix of one head, features [f_lo, f_hi) per thread. */
+typedef struct {
+    const float *k, *v;
+    const int32_t *tup;
+    const int *ord;
+    double *S;
+    int64_t n0, f_lo, f_hi;
+    int dk, dv, W, round_mode;
+} prefix_job;
+
+static void *prefix_worker(void *arg) {
+    const prefix_job *J = (const prefix_job *)arg;
+    const int dv = J->dv;
+    double *a = (double *)malloc(sizeof(double) * (size_t)(J->n0 > 0 ? J->n0 : 1));
+    if (!a) return (void *)1;
+    for (int64_t f = J->f_lo; f < J->f_hi; ++f) {
+        for (int64_t s = 0; s < J->n0; ++s) {
+            double mono = 1.0;
+            for (int r = 0; r < J->ord[f]; ++r) mono *= (double)J->k[s * J->dk + J->tup[f * J->W + r]];
+            a[s] = mono;
+        }
+        for (int c = 0; c <= dv; ++c) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < J->n0; ++s) acc += a[s] * (c < dv ? (double)J->v[s * dv + c] : 1.0);
+            J->S[f * (dv + 1) + c] = J->round_mode ? orc_round_bf16(acc) : acc;
+        }
+    }
+    free(a);
+    return NULL;
+}
+
+int orc_bf16_state_decode(const float *q, const float *k, const float *v, double *out,
+                          int64_t bh, int64_t n0, int64_t n, int dk, int dv, int P, int round_mode) {
+    if (bh < 0 || n0 < 0 || n < n0 || dk <= 0 || dv <= 0 || P < 1 || P > 8) return 1;
+    int64_t ng[8], off[8], m = 0;
+    for (int p = 0; p < P; ++p) {
+        ng[p] = orc_basis_bruteforce(dk, p, NULL, NULL, 0);
+        if (ng[p] < 0) return 1;
+        off[p] = m;
+        m += ng[p];
+    }
+    int32_t *tup = (int32_t *)malloc(sizeof(int32_t) * (size_t)(m * (P > 1 ? P - 1 : 1)));
+    double *qw = (double *)malloc(sizeof(double) * (size_t)m);     /* query-side weight per feature */
+    int *ord = (int *)malloc(sizeof(int) * (size_t)m);
+    double *S = (double *)malloc(sizeof(double) * (size_t)(m * (dv + 1)));
+    double *y = (double *)malloc(sizeof(double) * (size_t)(dv + 1));
+    if (!tup || !qw || !ord || !S || !y) {
+        free(tup); free(qw); free(ord); free(S); free(y);
+        return 1;
+    }
+    const int W = P > 1 ? P - 1 : 1;   /* tuple slots per feature */
+    {
+        double fact = 1.0;
+        for (int p = 0; p < P; ++p) {
+            if (p) fact *= p;
+            int32_t *tp = (int32_t *)malloc(sizeof(int32_t) * (size_t)(ng[p] * (p ? p : 1)));
+            int64_t *cp = (int64_t *)malloc(sizeof(int64_t) * (size_t)ng[p]);
+            orc_basis_bruteforce(dk, p, tp, cp, ng[p]);
+            for (int64_t t = 0; t < ng[p]; ++t) {
+                const int64_t f = off[p] + t;
+                ord[f] = p;
+                for (int r = 0; r < p; ++r) tup[f * W + r] = tp[t * p + r];
+                qw[f] = (double)cp[t] / (fact * pow(sqrt((double)dk), (double)p));
+            }
+            free(tp);
+            free(cp);
+        }
+    }
+    for (int64_t h = 0; h < bh; ++h) {
+        const float *qh = q + h * n * dk, *kh = k + h * n * dk, *vh = v + h * n * dv;
+        /* tokens 0..n0-1: exact sums, then one rounding (features split over threads) */
+        {
+            int nt = orc_num_cpus();
+            if (nt > 64) nt = 64;
+            if ((int64_t)nt > m) nt = (int)m;
+            prefix_job jobs[64];
+            pthread_t th[64];
+            int started[64] = {0};
+            for (int t = 0; t < nt; ++t) {
+                jobs[t] = (prefix_job){kh, vh, tup, ord, S, n0, m * t / nt, m * (t + 1) / nt, dk, dv, W, round_mode};
+                started[t] = t > 0 && pthread_create(&th[t], NULL, prefix_worker, &jobs[t]) == 0;
+                if (t > 0 && !started[t]) prefix_worker(&jobs[t]);
+            }
+            prefix_worker(&jobs[0]);
+            for (int t = 1; t < nt; ++t)
+                if (started[t]) pthread_join(th[t], NULL);
+        }
+        /* decode steps */
+        for (int64_t s = n0; s < n; ++s) {
+            for (int c = 0; c <= dv; ++c) y[c] = 0.0;
+            for (int64_t f = 0; f < m; ++f) {
+                double mk = 1.0, mq = qw[f];
+                for (int r = 0; r < ord[f]; ++r) {
+                    mk *= (double)kh[s * dk + tup[f * W + r]];
+                    mq *= (double)qh[s * dk + tup[f * W + r]];
+                }
+                for (int c = 0; c <= dv; ++c) {
+                    const double x = S[f * (dv + 1) + c] + mk * (c < dv ? (double)vh[s * dv + c] : 1.0);
+                    y[c] += mq * x;
+                    S[f * (dv + 1) + c] = round_mode ? orc_round_bf16(x) : x;
+                }
+            }
+            for (int c = 0; c < dv; ++c) out[(h * (n - n0) + (s - n0)) * dv + c] = y[c] / y[dv];
+        }
+    }
+    free(tup); free(qw); free(ord); free(S); free(y);
+    return 0;
+}

@@ -1,0 +1,161 @@
+"""GPU parity of the bf16-stored decode state (opt-in, decode only) against the
+oracle's emulation of it (O8: exact sums, read out before the store, stored
+rounded to nearest bf16, ties to even).
+
+Bar, on the usual metric (max over rows of the normwise relative error):
+TOL_BF16_STATE + DRIFT_SHARE * drift, where drift is the emulation's own
+distance from the exact result.  Where the kernel's fp32 sum and the oracle's
+fp64 sum fall on either side of a bf16 half-way point the two store
+neighbouring values, and from then on the two runs carry different rounding
+errors.  Both that difference and the drift are sums of one-ulp errors of
+the state read out through the same query weights, so they grow with the
+same conditioning of the readout; a CPU emulation in fp32 arithmetic lands
+1e-4 from the fp64 one on well-conditioned cases.  A kernel that stored fp32,
+truncated, or read out after rounding would sit about one drift away from the
+emulation, far outside the bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from sata_testutil import TOL_BF16, decode, dev_all, prefill, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16_STATE = 1e-3
+DRIFT_SHARE = 1e-2
+
+
+@pytest.fixture(scope="module")
+def sata():
+    from constant_cost_attention_amd import sata as s
+    s.load()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return s
+
+
+def _bf16_state_from_prefill(sata, idx, B, H, q, k, v):
+    """fp32 prefill of the given tokens, then conversion into a new bf16 state."""
+    st32 = sata.State(idx, B, H)
+    if q.shape[2]:
+        prefill(idx, st32, q, k, v)
+    st16 = sata.State(idx, B, H, dtype=torch.bfloat16)
+    sata.sata_state_convert(st32, st16)
+    return st32, st16
+
+
+def test_convert_rounds_to_nearest_even_and_widens_exactly(sata):
+    d, P, n = 16, 4, 300
+    x = si.draw_qkv((2, 3), n, d, d, 4242, "f32")
+    idx = sata.Index(d, d, P)
+    q, k, v = dev_all(x)
+    say("state convert d=%d n=%d" % (d, n))
+    st32, st16 = _bf16_state_from_prefill(sata, idx, 2, 3, q, k, v)
+    s32 = sata.state_tensor(st32).clone()
+    s16 = sata.state_tensor(st16).clone()
+    assert s16.dtype == torch.bfloat16 and s16.shape == s32.shape
+    ref = s32.to(torch.bfloat16)                                   # torch: round to nearest even
+    assert torch.equal(s16.view(torch.int16), ref.view(torch.int16))
+    assert torch.all(s16[..., idx.m:].float() == 0)
+    back = sata.State(idx, 2, 3)
+    sata.sata_state_convert(st16, back)
+    assert torch.equal(sata.state_tensor(back), s16.float())
+    copy = sata.State(idx, 2, 3)
+    sata.sata_state_convert(st32, copy)
+    assert torch.equal(sata.state_tensor(copy), s32)
+
+
+@pytest.mark.parametrize("d,P,n0,T,heads", [
+    (8, 3, 64, 600, 2),      # the normaliser passes 256 and 512: additions start to round away
+    (16, 4, 256, 300, 2),
+    (32, 4, 200, 24, 2),
+    (64, 4, 128, 12, 2),
+    (16, 4, 0, 40, 3),       # from an empty state, every step a decode step
+])
+def test_bf16_state_decode_matches_emulation(sata, oracle, d, P, n0, T, heads):
+    x = si.draw_qkv((1, heads), n0 + T, d, d, 900 + d + n0, "f32")
+    idx = sata.Index(d, d, P)
+    q, k, v = dev_all(x)
+    say("bf16-state decode d=%d P=%d n0=%d T=%d heads=%d" % (d, P, n0, T, heads))
+    _, st = _bf16_state_from_prefill(sata, idx, 1, heads, q[:, :, :n0].contiguous(), k[:, :, :n0].contiguous(),
+                                     v[:, :, :n0].contiguous())
+    outs = [decode(idx, st, q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous())
+            for t in range(n0, n0 + T)]
+    o = torch.stack(outs, dim=2).cpu().numpy()
+    ref = oracle.bf16_state_decode(x.q, x.k, x.v, P, n0)
+    exact = oracle.taylor_attention(x.q, x.k, x.v, P, rows=np.arange(n0, n0 + T, dtype=np.int64))
+    err, drift = rel_err(o, ref), rel_err(ref, exact)
+    say("  err vs emulation %.3e, emulation drift from exact %.3e" % (err, drift))
+    assert err <= TOL_BF16_STATE + DRIFT_SHARE * drift
+
+
+def test_bf16_state_decode_bf16_io(sata, oracle):
+    """bf16 q/k/v and bf16 output on a bf16 state: the oracle consumes the
+    bf16-rounded inputs; the bar is the bf16-input one."""
+    d, P, n0, T = 64, 4, 96, 8
+    x = si.draw_qkv((1, 2), n0 + T, d, d, 77, "bf16")
+    idx = sata.Index(d, d, P)
+    q, k, v = dev_all(x)
+    say("bf16-state decode, bf16 io")
+    _, st = _bf16_state_from_prefill(sata, idx, 1, 2, q[:, :, :n0].contiguous(), k[:, :, :n0].contiguous(),
+                                     v[:, :, :n0].contiguous())
+    outs = [decode(idx, st, q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                   out_dtype=torch.bfloat16) for t in range(n0, n0 + T)]
+    o = torch.stack(outs, dim=2).float().cpu().numpy()
+    ref = oracle.bf16_state_decode(x.q, x.k, x.v, P, n0)
+    err = rel_err(o, ref)
+    say("  err %.3e" % err)
+    assert err <= TOL_BF16
+
+
+def test_bf16_state_workload_d64_after_8192(sata, oracle):
+    """32 x 8 heads, fp32 prefill of 8192 tokens converted to bf16, then decode
+    steps; two sampled heads against the emulation (each takes seconds)."""
+    wl = si.WORKLOADS["decode_d64_p4_f32"]
+    steps = 4
+    say("bf16-state decode workload %s (%d steps)" % (wl.name, steps))
+    pre = wl.draw()
+    dec = wl.draw_decode(steps)
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    q, k, v = dev_all(pre)
+    st32, st = _bf16_state_from_prefill(sata, idx, wl.batch, wl.heads, q, k, v)
+    st32.free()
+    del q, k, v
+    dq, dk_, dv_ = dev_all(dec)
+    outs = [decode(idx, st, dq[:, :, t].contiguous(), dk_[:, :, t].contiguous(), dv_[:, :, t].contiguous())
+            for t in range(steps)]
+    o = torch.stack(outs, dim=2).cpu().numpy()
+    for b, h in ((0, 0), (wl.batch - 1, wl.heads - 1)):
+        qa = np.concatenate([pre.q[b, h], dec.q[b, h]], axis=0)[None]
+        ka = np.concatenate([pre.k[b, h], dec.k[b, h]], axis=0)[None]
+        va = np.concatenate([pre.v[b, h], dec.v[b, h]], axis=0)[None]
+        ref = oracle.bf16_state_decode(qa, ka, va, wl.P, wl.n)[0]
+        exact = oracle.taylor_attention(qa, ka, va, wl.P, rows=np.arange(wl.n, wl.n + steps, dtype=np.int64))[0]
+        err, drift = rel_err(o[b, h], ref), rel_err(ref, exact)
+        say("  head (%d, %d): err vs emulation %.3e, emulation drift %.3e" % (b, h, err, drift))
+        assert err <= TOL_BF16_STATE + DRIFT_SHARE * drift
+
+
+def test_bf16_state_error_paths(sata):
+    idx = sata.Index(16, 16, 4)
+    st16 = sata.State(idx, 1, 2, dtype=torch.bfloat16)
+    q = torch.zeros((1, 2, 8, 16), device="cuda")
+    with pytest.raises(sata.SataError) as e:
+        sata.sata_prefill(idx, st16, q, q, q, torch.zeros_like(q))
+    assert e.value.status == sata.SATA_ERR_UNSUPPORTED
+    with pytest.raises(sata.SataError) as e:
+        sata.sata_state_convert(st16, st16)
+    assert e.value.status == sata.SATA_ERR_INVALID
+    other = sata.State(idx, 2, 1)
+    with pytest.raises(sata.SataError) as e:
+        sata.sata_state_convert(st16, other)
+    assert e.value.status == sata.SATA_ERR_INVALID
+    idx2 = sata.Index(16, 16, 3)
+    third = sata.State(idx2, 1, 2)
+    with pytest.raises(sata.SataError) as e:
+        sata.sata_state_convert(st16, third)
+    assert e.value.status == sata.SATA_ERR_INVALID
+    with pytest.raises(sata.SataError) as e:
+        sata.sata_state_alloc_dtype(idx, 1, 1, 7)
+    assert e.value.status == sata.SATA_ERR_INVALID

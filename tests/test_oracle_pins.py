@@ -286,3 +286,78 @@ def test_page_basis_sizes_for_P3_P5_are_rejected(oracle):
     g = json.load(open(GOLDEN))["rejected_basis_sizes"]["page_value"]
     assert oracle.cumulative_basis(64, 3) == 2145 != g["P=3"]
     assert oracle.cumulative_basis(64, 5) == 814385 != g["P=5"]
+
+
+# ------------------------------------------------------------ bf16-stored state (O8)
+
+def test_round_bf16_matches_library_rounding(oracle):
+    """O8a against torch's float32 -> bfloat16 conversion (round to nearest,
+    ties to even) on random bit patterns over the whole binary32 range,
+    explicit half-way cases and subnormals: bit-exact."""
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2**32, size=200000, dtype=np.uint64).astype(np.uint32)
+    ties = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)          # exactly half-way
+    sub = rng.integers(0, 2**23, size=20000, dtype=np.uint64).astype(np.uint32)   # fp32 subnormals
+    x = np.concatenate([bits, ties, sub]).view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3.3e38)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_integers(oracle):
+    """Integers above 256 are spaced 2 apart in bf16; half-way cases go to the
+    even significand."""
+    got = oracle.round_bf16([255, 256, 257, 258, 259, 261, 263, 513, 515])
+    assert list(got) == [255, 256, 256, 258, 260, 260, 264, 512, 516]
+
+
+@pytest.mark.parametrize("d,P,n0", [(1, 1, 0), (2, 3, 5), (3, 4, 0), (4, 4, 17), (4, 2, 39)])
+def test_bf16_state_unrounded_equals_quadratic(oracle, d, P, n0):
+    """O8 with rounding off is the one-sided recurrent form, whatever the
+    split between summed prefix and steps: equal to the quadratic
+    definition (O1) on rows n0.. .  Catches a wrong query weight
+    (p!/alpha!, 1/p!, d^(p/2)), a step read out before its update, or a
+    prefix that misses a token."""
+    q, k, v = _rand_qkv(300 + 10 * d + P, (2,), 40, d, 3)
+    a = oracle.bf16_state_decode(q, k, v, P, n0, rounding=False)
+    b = oracle.taylor_attention(q, k, v, P)[:, n0:]
+    assert a.shape == b.shape
+    assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
+
+
+def test_bf16_state_exact_when_sums_are_representable(oracle):
+    """With q, k in {0, +-1/2, +-1}, v in {+-1/2, +-1}, P = 3 and 12 tokens,
+    every state element is a multiple of 1/8 below 12 in magnitude, which bf16
+    holds exactly: the bf16-stored state must give the exact result (O1)."""
+    rng = np.random.default_rng(9)
+    q = rng.choice([0.0, 0.5, -0.5, 1.0, -1.0], size=(2, 12, 4)).astype(np.float32)
+    k = rng.choice([0.0, 0.5, -0.5, 1.0, -1.0], size=(2, 12, 4)).astype(np.float32)
+    v = rng.choice([0.5, -0.5, 1.0, -1.0], size=(2, 12, 3)).astype(np.float32)
+    for n0 in (0, 5):
+        a = oracle.bf16_state_decode(q, k, v, 3, n0)
+        b = oracle.taylor_attention(q, k, v, 3)[:, n0:]
+        assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
+
+
+@pytest.mark.parametrize("n0", [0, 300])
+def test_bf16_state_count_stalls(oracle, n0):
+    """P = 1 keeps the constant order: the normaliser element counts tokens.
+    Stored in bf16 it stops growing where adding 1 is a half-way case that
+    rounds back to the even neighbour (256 from zero; 300 stays 300 after an
+    exact prefix of 300), while each step reads out from the unrounded sum
+    stored + 1.  With v_0 = w and v_s = 0 after it, row s is
+    w / (min(s, stall) + 1)."""
+    n = 620
+    w = np.array([256.0, -3.0, 0.375], dtype=np.float32)
+    v = np.zeros((1, n, 3), dtype=np.float32)
+    v[0, 0] = w
+    q = np.zeros((1, n, 2), dtype=np.float32)
+    k = np.zeros((1, n, 2), dtype=np.float32)
+    o = oracle.bf16_state_decode(q, k, v, 1, n0)[0]
+    stall = 256 if n0 == 0 else 300
+    s = np.arange(n0, n)
+    ref = w[None, :].astype(np.float64) / (np.minimum(s, stall) + 1)[:, None]
+    assert np.array_equal(o, ref)
+    exact = oracle.bf16_state_decode(q, k, v, 1, n0, rounding=False)[0]
+    assert np.array_equal(exact, w[None, :].astype(np.float64) / (s + 1)[:, None])
