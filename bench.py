@@ -93,6 +93,16 @@ def prefill_flops(wl) -> float:
     return 4.0 * features(wl.d_k, wl.P) * (wl.d_v + 1) * wl.batch * wl.heads * wl.n
 
 
+DECODE_WINDOW = 16
+
+
+def decode_read_bytes(wl, state_elem: int = 4) -> float:
+    """Algorithmic HBM bytes of a deferred step's readout: every head's state
+    read once, plus the query."""
+    m = features(wl.d_k, wl.P)
+    return float(wl.batch * wl.heads * (state_elem * m * (wl.d_v + 1) + 4 * wl.d_k))
+
+
 def decode_bytes(wl, state_elem: int = 4) -> float:
     """Algorithmic HBM bytes of one decode step: every head's state (fp32, or
     bf16 with state_elem = 2) read and written once, plus the token's fp32
@@ -198,9 +208,12 @@ def time_decode(sata, idx, st, wl, steps: int, warmup: int, seed: int):
     torch.cuda.synchronize()
     sata.sata_profile_enable(False)
     ms = e0.elapsed_time(e1) / steps
-    dms, dn = sata.sata_profile_query("decode_stream")
-    fms, fn = sata.sata_profile_query("decode_finish")
-    return ms, dms / dn, fms / fn
+    kern = {}
+    for name in ("decode_stream", "decode_finish", "decode_read", "decode_fold"):
+        kms, kn = sata.sata_profile_query(name)
+        if kn:
+            kern[name] = (kms / kn, kn)
+    return ms, kern
 
 
 def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
@@ -208,15 +221,26 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
     idx = sata.Index(wl.d_k, wl.d_v, wl.P)
     log("decode: fp32 prefill of %d tokens x %d heads" % (wl.n, wl.batch * wl.heads))
     st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
-    ms, kern_ms, fin_ms = time_decode(sata, idx, st, wl, steps, warmup, wl.seed + 30)
+    ms, kern = time_decode(sata, idx, st, wl, steps, warmup, wl.seed + 30)
+    kern_ms, fin_ms = kern["decode_stream"][0], kern["decode_finish"][0]
     st16 = sata.State(idx, wl.batch, wl.heads, dtype=torch.bfloat16)
     sata.sata_state_convert(st, st16)
     st.free()
     log("decode: the same state converted to bf16 storage")
-    ms16, kern16, fin16 = time_decode(sata, idx, st16, wl, steps, warmup, wl.seed + 30)
+    ms16, k16 = time_decode(sata, idx, st16, wl, steps, warmup, wl.seed + 30)
+    kern16, fin16 = k16["decode_stream"][0], k16["decode_finish"][0]
     st16.free()
     nbytes16 = decode_bytes(wl, 2)
     ach16 = nbytes16 / (kern16 * 1e-3) / 1e9
+    log("decode: window of %d steps per state update (fp32 state)" % DECODE_WINDOW)
+    st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
+    sata.sata_state_set_decode_window(st, DECODE_WINDOW)
+    msw, kw = time_decode(sata, idx, st, wl, steps, warmup, wl.seed + 30)
+    st.free()
+    nread = decode_read_bytes(wl)
+    read_ms, fold_ms = kw["decode_read"][0], kw["decode_fold"][0]
+    ach_read = nread / (read_ms * 1e-3) / 1e9
+    ach_fold = decode_bytes(wl) / (fold_ms * 1e-3) / 1e9
     nbytes = decode_bytes(wl)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     res = {
@@ -238,15 +262,27 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
             },
             "finish_ms_per_step": fin16,
         },
+        "window": {
+            "window": DECODE_WINDOW, "state": "fp32",
+            "value": wl.batch / (msw * 1e-3), "unit": "tokens/s", "ms_per_step": msw,
+            "roofline": {
+                "bound": "hbm", "achieved": ach_read, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach_read / PEAK_HBM_GBS, "kernel": "decode_read", "avg_launch_ms": read_ms,
+                "bytes_per_launch": nread, "traffic": traffic_for("decode_read", wl.name),
+            },
+            "fold": {"avg_launch_ms": fold_ms, "launches": kw["decode_fold"][1], "achieved_gbs": ach_fold,
+                     "bytes_per_launch": decode_bytes(wl)},
+            "finish_ms_per_step": kw["decode_finish"][0],
+        },
     }
     if flatness:
         flat = {}
         for prefix in (8192, 32768, 65536):
             log("decode flatness: bf16 prefill of %d tokens" % prefix)
             st = build_state(sata, idx, wl, prefix, "bf16", wl.seed + 100 + prefix)
-            fms, fk, _ = time_decode(sata, idx, st, wl, 256, 8, wl.seed + 200 + prefix)
+            fms, fk = time_decode(sata, idx, st, wl, 256, 8, wl.seed + 200 + prefix)
             st.free()
-            flat[str(prefix)] = {"ms_per_step": fms, "kernel_ms": fk}
+            flat[str(prefix)] = {"ms_per_step": fms, "kernel_ms": fk["decode_stream"][0]}
         base = flat["8192"]["ms_per_step"]
         res["flatness"] = {"per_prefix": flat,
                            "max_rel_dev": max(abs(f["ms_per_step"] / base - 1) for f in flat.values())}
@@ -291,8 +327,10 @@ TRAFFIC_KERNELS = [
     (r"prefill_scan_kernel<64, 64, 128, \d+, \d+, unsigned short>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
     (r"prefill_scan_ws_kernel<32, 32, 64, \d+>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
     (r"prefill_scan_ws_kernel<16, 16, 128, \d+>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
-    (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
-    (r"decode_kernel<64, float, unsigned short>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_kernel<64, float, float, 1>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_kernel<64, float, unsigned short, 1>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_kernel<64, float, float, 16>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
 
 
@@ -335,6 +373,11 @@ def traffic_run():
     time_decode(sata, idx, st16, wl, 2, 0, wl.seed + 30)
     log("traffic run: bf16-state decode done")
     st16.free()
+    st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
+    sata.sata_state_set_decode_window(st, 2)
+    time_decode(sata, idx, st, wl, 2, 0, wl.seed + 30)      # one read step, one fold
+    log("traffic run: windowed decode done")
+    st.free()
     idx.free()
 
 
@@ -447,6 +490,12 @@ def main():
         b16 = dec["bf16_state"]
         log("decode, bf16 state: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak)"
             % (b16["ms_per_step"], b16["value"], b16["roofline"]["achieved"], 100 * b16["roofline"]["frac"]))
+        dw = dec["window"]
+        log("decode, window %d: %.3f ms/step, %.3e tok/s, read %.3f ms at %.0f GB/s (%.1f%% of peak), "
+            "fold %.3f ms at %.0f GB/s"
+            % (dw["window"], dw["ms_per_step"], dw["value"], dw["roofline"]["avg_launch_ms"],
+               dw["roofline"]["achieved"], 100 * dw["roofline"]["frac"], dw["fold"]["avg_launch_ms"],
+               dw["fold"]["achieved_gbs"]))
         result["decode"] = dec
         torch.cuda.empty_cache()
 

@@ -25,34 +25,55 @@
 //
 //   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
 //            engineering a constant per-token cost" (2026-02-05).
+#include <type_traits>
+
 #include "sata_device.h"
 #include "sata_internal.h"
 
 namespace sata {
 
 constexpr int kDecThreads = 256;
-template <typename TS> constexpr int dec_fpt() { return 16 / (int)sizeof(TS); }   // features per lane
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte word of a state row
-
-// A state word as fp32 values, and back.
-__device__ __forceinline__ void widen(const u32x4 u, float (&x)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(u[j]);
+// Features per lane: one 16-byte word of every state row (4 fp32 or 8 bf16),
+// except for a bf16 fold of W > 1 tokens, whose lanes take 8-byte words (4
+// bf16) so that 4 features x W key monomials fit the register file.
+template <typename TS, int W> constexpr int dec_fpt() {
+    return (W > 1 && sizeof(TS) == 2) ? 4 : 16 / (int)sizeof(TS);
 }
-__device__ __forceinline__ void widen(const u32x4 u, float (&x)[8]) {
+
+// A lane's word of one state row, and its conversion to FPT fp32 values and
+// back (bf16 rounds to nearest even).
+template <typename TS, int FPT> struct Word;
+template <> struct Word<float, 4> {
+    typedef u32x4 T;
+    static __device__ __forceinline__ void widen(const T u, float (&x)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        x[2 * j] = __uint_as_float(u[j] << 16);
-        x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(u[j]);
     }
-}
-__device__ __forceinline__ u32x4 narrow(const float (&x)[4]) {
-    return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-}
-__device__ __forceinline__ u32x4 narrow(const float (&x)[8]) {
-    return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-}
+    static __device__ __forceinline__ T narrow(const float (&x)[4]) {
+        return T{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    }
+};
+template <int N> struct WordBf16 {
+    typedef uint32_t T __attribute__((ext_vector_type(N / 2)));
+    static __device__ __forceinline__ void widen(const T u, float (&x)[N]) {
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            x[2 * j] = __uint_as_float(u[j] << 16);
+            x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ T narrow(const float (&x)[N]) {
+        T r;
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) r[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        return r;
+    }
+};
+template <> struct Word<bf16_t, 8> : WordBf16<8> {};
+template <> struct Word<bf16_t, 4> : WordBf16<4> {};
 
 // Wave-level reduce-scatter of DV (power of two) per-lane values followed by a
 // plain reduction across the remaining lane groups: afterwards lane l holds the
@@ -82,88 +103,31 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// The lane's column loads are issued in two batches of ~(d_V+1)/2 rows, the
-// second batch before any store of the first, so each lane keeps up to d_V+1
-// 16-byte loads in flight; one wavefront per SIMD then saturates the HBM
-// read-modify-write stream (the state is far larger than every cache).
-template <int DV, typename TIn, typename TS>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
-                   int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
-                   const TIn *__restrict__ v, float *__restrict__ partial) {
-    constexpr int NC = DV + 1;
-    constexpr int R = (NC + 1) / 2;          // rows per load batch
-    constexpr int FPT = dec_fpt<TS>();
-    __shared__ float sq[72], sk[72], sv[NC];
-    __shared__ float red[kDecThreads / 64][NC];
-    const int bh = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
-    const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
-    TS *Sb = state + (int64_t)bh * NC * m_pad + f0;
-    auto row = [&](int r) { return reinterpret_cast<u32x4 *>(Sb + (int64_t)r * m_pad); };
-
-    // first batch of state rows goes out before anything else
-    u32x4 s0[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (valid) s0[r] = __builtin_nontemporal_load(row(r));
-    uint4 t4[FPT / 4];
-    float4 c4[FPT / 4];
+// Per-lane feature weights of the lane's FPT features: the query side
+// (coefficient times monomial) or the key side (plain monomial).
+template <int FPT>
+__device__ __forceinline__ void lane_tables(bool valid, const uint32_t *tup, const float *coef, int64_t f0,
+                                            uint32_t (&tt)[FPT], float (&cc)[FPT]) {
 #pragma unroll
     for (int h = 0; h < FPT / 4; ++h) {
-        t4[h] = uint4{0u, 0u, 0u, 0u};
-        c4[h] = float4{0.f, 0.f, 0.f, 0.f};
+        uint4 t4 = uint4{0u, 0u, 0u, 0u};
+        float4 c4 = float4{0.f, 0.f, 0.f, 0.f};
         if (valid) {
-            t4[h] = *reinterpret_cast<const uint4 *>(tup + f0 + 4 * h);
-            c4[h] = *reinterpret_cast<const float4 *>(coef + f0 + 4 * h);
+            t4 = *reinterpret_cast<const uint4 *>(tup + f0 + 4 * h);
+            c4 = *reinterpret_cast<const float4 *>(coef + f0 + 4 * h);
         }
+        tt[4 * h] = t4.x; tt[4 * h + 1] = t4.y; tt[4 * h + 2] = t4.z; tt[4 * h + 3] = t4.w;
+        cc[4 * h] = c4.x; cc[4 * h + 1] = c4.y; cc[4 * h + 2] = c4.z; cc[4 * h + 3] = c4.w;
     }
-    if (tid < dk) {
-        sq[tid] = to_f32(q[(int64_t)bh * dk + tid]);
-        sk[tid] = to_f32(k[(int64_t)bh * dk + tid]);
-    }
-    if (tid == 0) {
-        sq[dk] = 1.f; sk[dk] = 1.f; sq[dk + 1] = 0.f; sk[dk + 1] = 0.f;
-        sv[DV] = 1.f;
-    }
-    if (tid < DV) sv[tid] = to_f32(v[(int64_t)bh * DV + tid]);
-    __syncthreads();
+}
 
-    float phk[FPT], psq[FPT];
-#pragma unroll
-    for (int h = 0; h < FPT / 4; ++h) {
-        const uint32_t tt[4] = {t4[h].x, t4[h].y, t4[h].z, t4[h].w};
-        const float cc[4] = {c4[h].x, c4[h].y, c4[h].z, c4[h].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            phk[4 * h + j] = monomial(tt[j], sk, 1);
-            psq[4 * h + j] = cc[j] * monomial(tt[j], sq, 1);
-        }
-    }
-
-    // second batch in flight while the first is updated, stored and read out
-    u32x4 s1[NC - R];
-#pragma unroll
-    for (int r = 0; r < NC - R; ++r)
-        if (valid) s1[r] = __builtin_nontemporal_load(row(R + r));
-    float acc[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        float x[FPT];
-        widen(c < R ? s0[c] : s1[c - R], x);
-        const float vc = sv[c];
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < FPT; ++j) {
-            x[j] += phk[j] * vc;
-            a += psq[j] * x[j];
-        }
-        if (valid) __builtin_nontemporal_store(narrow(x), row(c));
-        acc[c] = valid ? a : 0.f;
-    }
-
-    // workgroup reduction of the d_V + 1 readout sums
+// Workgroup reduction of the d_V + 1 per-lane readout sums into one partial
+// row per workgroup.
+template <int DV>
+__device__ __forceinline__ void store_partial(float (&acc)[DV + 1], float (&red)[kDecThreads / 64][DV + 1],
+                                              float *partial, int bh) {
+    constexpr int NC = DV + 1;
+    const int tid = threadIdx.x;
     float vals[DV];
 #pragma unroll
     for (int c = 0; c < DV; ++c) vals[c] = acc[c];
@@ -181,20 +145,256 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
     }
 }
 
-// Adds a head's partial sums in block order and divides by the normaliser.
-template <int DV, typename TOut>
+// State update by up to W tokens, then (if q is given) readout of the updated
+// state.  The tokens are the npend pending ones of the head (fp32 rows of the
+// pending buffers), followed by the step's own k, v if k is given.  W = 1 is
+// the plain decode step; larger W folds a window of deferred tokens in one
+// pass.
+//
+// The lane's row loads are issued in NB batches, each batch before any store
+// of the previous one, so each lane keeps up to two batches of 16-byte loads
+// in flight (all d_V+1 rows for the plain step); one wavefront per SIMD then
+// saturates the HBM read-modify-write stream (the state is far larger than
+// every cache).  A bf16 fold holds 8 features x W key monomials per lane, so
+// it streams in four batches to stay within the register file.
+template <int DV, typename TIn, typename TS, int W>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
+                   int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
+                   const TIn *__restrict__ v, const float *__restrict__ pend_k, const float *__restrict__ pend_v,
+                   int npend, float *__restrict__ partial) {
+    constexpr int NC = DV + 1;
+    constexpr int FPT = dec_fpt<TS, W>();
+    constexpr int NB = 2;                              // load batches
+    constexpr int RB = (NC + NB - 1) / NB;             // rows per batch
+    typedef Word<TS, FPT> Wd;
+    __shared__ float sq[72], sk[W][72];
+    __shared__ __align__(16) float sv[NC][W];      // token-minor: one row's W values are contiguous
+    __shared__ float red[kDecThreads / 64][NC];
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
+    const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
+    const bool readout = q != nullptr;
+    TS *Sb = state + (int64_t)bh * NC * m_pad + f0;
+    auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
+
+    // first batch of state rows goes out before anything else
+    typename Wd::T s[NC];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+        if (valid) s[r] = __builtin_nontemporal_load(row(r));
+    uint32_t tt[FPT];
+    float cc[FPT];
+    lane_tables<FPT>(valid, tup, coef, f0, tt, cc);
+
+    // tokens into LDS: slot t < npend from the pending buffers, slot npend the
+    // step's own token, the rest zero (they add nothing)
+    const int ntok = npend + (k != nullptr ? 1 : 0);
+    for (int i = tid; i < W * 72; i += kDecThreads) {
+        const int t = i / 72, c = i % 72;
+        float x = 0.f;
+        if (t < ntok) {
+            if (c < dk)
+                x = t < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + t) * dk + c] : to_f32(k[(int64_t)bh * dk + c]);
+            else if (c == dk) x = 1.f;
+        }
+        sk[t][c] = x;
+    }
+    for (int i = tid; i < W * NC; i += kDecThreads) {
+        const int t = i / NC, c = i % NC;
+        float x = 0.f;
+        if (t < ntok) {
+            if (c == DV) x = 1.f;
+            else x = t < npend ? pend_v[((int64_t)bh * kMaxDecodeWindow + t) * DV + c] : to_f32(v[(int64_t)bh * DV + c]);
+        }
+        sv[c][t] = x;
+    }
+    if (readout && tid < 72) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    __syncthreads();
+
+    float phk[W][FPT], psq[FPT];
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) {
+#pragma unroll
+        for (int t = 0; t < W; ++t) phk[t][j] = monomial(tt[j], sk[t], 1);
+        psq[j] = readout ? cc[j] * monomial(tt[j], sq, 1) : 0.f;
+    }
+
+    float acc[NC];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        // next batch in flight while this one is updated, stored and read out
+#pragma unroll
+        for (int r = (b + 1) * RB; r < (b + 2) * RB && r < NC; ++r)
+            if (valid) s[r] = __builtin_nontemporal_load(row(r));
+#pragma unroll
+        for (int c = b * RB; c < (b + 1) * RB && c < NC; ++c) {
+            float x[FPT];
+            Wd::widen(s[c], x);
+            float vc[W];
+#pragma unroll
+            for (int t = 0; t < W; ++t) vc[t] = sv[c][t];
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < FPT; ++j) {
+#pragma unroll
+                for (int t = 0; t < W; ++t) x[j] += phk[t][j] * vc[t];
+                a += psq[j] * x[j];
+            }
+            if (valid) __builtin_nontemporal_store(Wd::narrow(x), row(c));
+            acc[c] = valid ? a : 0.f;
+        }
+    }
+    if (readout) store_partial<DV>(acc, red, partial, bh);
+}
+
+// Readout of the state as it stands, without an update: the non-folding steps
+// of a deferred decode.  A pure read stream, so a workgroup walks TPW
+// consecutive feature tiles (256 * FPT features each) of its head and keeps
+// the next half-tile's rows in flight while it reads out the current half;
+// the readout sums accumulate across the tiles and are reduced once.
+constexpr int kReadTiles = 4;
+template <int DV, typename TIn, typename TS>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef,
+                        const TS *__restrict__ state, int64_t m_pad, int dk, const TIn *__restrict__ q,
+                        float *__restrict__ partial) {
+    constexpr int NC = DV + 1;
+    constexpr int RA = (NC + 1) / 2;   // rows of the first half-tile
+    constexpr int FPT = dec_fpt<TS, 1>();
+    constexpr int TILE = kDecThreads * FPT;
+    typedef Word<TS, FPT> Wd;
+    typedef typename Wd::T WT;
+    __shared__ float sq[72];
+    __shared__ float red[kDecThreads / 64][NC];
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t tiles = (m_pad + TILE - 1) / TILE;
+    const int64_t first = (int64_t)blockIdx.x * kReadTiles;
+    const int tn = (int)min<int64_t>(kReadTiles, tiles - first);
+    const TS *Sb = state + (int64_t)bh * NC * m_pad;
+    // A lane past the last feature re-reads the last word (in bounds, weight 0),
+    // so every load is unconditional.
+    auto fidx = [&](int i) { return (first + i) * TILE + (int64_t)tid * FPT; };
+    auto fclamp = [&](int i) { return min<int64_t>(fidx(i), m_pad - FPT); };
+    auto row = [&](int64_t f, int r) { return reinterpret_cast<const WT *>(Sb + (int64_t)r * m_pad + f); };
+    auto tables = [&](int i, uint32_t (&tt)[FPT], float (&cc)[FPT]) {
+        lane_tables<FPT>(true, tup, coef, fclamp(i), tt, cc);
+    };
+
+    uint32_t tt[FPT];
+    float cc[FPT];
+    tables(0, tt, cc);
+    bool valid = fidx(0) < m_pad;
+    WT sa[RA], sb[NC - RA];
+    {
+        const int64_t f = fclamp(0);
+#pragma unroll
+        for (int r = 0; r < RA; ++r) sa[r] = __builtin_nontemporal_load(row(f, r));
+#pragma unroll
+        for (int r = RA; r < NC; ++r) sb[r - RA] = __builtin_nontemporal_load(row(f, r));
+    }
+    if (tid < 72) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    __syncthreads();
+
+    float acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+    // One tile's readout, half by half.  With `next`, the following tile's
+    // tables and first half are issued once the first half is consumed, its
+    // second half once the second half is; the phases stay in program order.
+    auto tile = [&](auto next, int64_t fn, int inext) {
+        float psq[FPT];
+#pragma unroll
+        for (int j = 0; j < FPT; ++j) psq[j] = valid ? cc[j] * monomial(tt[j], sq, 1) : 0.f;
+#pragma unroll
+        for (int c = 0; c < RA; ++c) {
+            float x[FPT];
+            Wd::widen(sa[c], x);
+#pragma unroll
+            for (int j = 0; j < FPT; ++j) acc[c] += psq[j] * x[j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(next)::value) {
+            tables(inext, tt, cc);
+            valid = fidx(inext) < m_pad;
+#pragma unroll
+            for (int r = 0; r < RA; ++r) sa[r] = __builtin_nontemporal_load(row(fn, r));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = RA; c < NC; ++c) {
+            float x[FPT];
+            Wd::widen(sb[c - RA], x);
+#pragma unroll
+            for (int j = 0; j < FPT; ++j) acc[c] += psq[j] * x[j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(next)::value) {
+#pragma unroll
+            for (int r = RA; r < NC; ++r) sb[r - RA] = __builtin_nontemporal_load(row(fn, r));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int i = 0; i + 1 < tn; ++i) tile(std::true_type{}, fclamp(i + 1), i + 1);
+    tile(std::false_type{}, 0, 0);
+    store_partial<DV>(acc, red, partial, bh);
+}
+
+// Adds a head's partial sums in block order, then (deferred steps) the direct
+// Taylor-weighted terms of the npend pending tokens and of the step's own
+// token, w(q.k_t / sqrt(d_K)) [v_t, 1] with w(x) = sum_{p<P} x^p / p!, the
+// same sum the state's orders give for one token [hotdry, "Core insight of
+// symmetric tensor decomposition"]; divides by the normaliser; and (deferred
+// steps) appends the step's token to the pending buffers at slot npend.
+template <int DV, typename TIn, typename TOut>
 __global__ __launch_bounds__(128) void decode_finish_kernel(const float *__restrict__ partial, int nblk,
-                                                            TOut *__restrict__ out) {
+                                                            TOut *__restrict__ out, int direct, int dk, int P,
+                                                            const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                            const TIn *__restrict__ v, float *__restrict__ pend_k,
+                                                            float *__restrict__ pend_v, int npend) {
     constexpr int NC = DV + 1;
     __shared__ float y[NC];
+    __shared__ float wt[kMaxDecodeWindow];
+    static_assert(kMaxDecodeWindow <= 128, "one thread per token");
     const int bh = blockIdx.x, tid = threadIdx.x;
+    const int ntok = direct ? npend + 1 : 0;
+    if (tid < ntok) {
+        // token tid: pending slot tid, or the step's own token
+        const float rs = rsqrtf((float)dk);
+        float dot = 0.f;
+        for (int i = 0; i < dk; ++i) {
+            const float kv =
+                tid < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + tid) * dk + i] : to_f32(k[(int64_t)bh * dk + i]);
+            dot += to_f32(q[(int64_t)bh * dk + i]) * kv;
+        }
+        const float x = dot * rs;
+        float w = 0.f, term = 1.f;
+        for (int p = 0; p < P; ++p) {
+            w += term;
+            term = term * x / (float)(p + 1);
+        }
+        wt[tid] = w;
+    }
+    __syncthreads();
     if (tid < NC) {
         float s = 0.f;
         for (int b = 0; b < nblk; ++b) s += partial[((int64_t)bh * nblk + b) * NC + tid];
+        for (int t = 0; t < ntok; ++t) {
+            const float vt = tid == DV ? 1.f
+                             : (t < npend ? pend_v[((int64_t)bh * kMaxDecodeWindow + t) * DV + tid]
+                                          : to_f32(v[(int64_t)bh * DV + tid]));
+            s += wt[t] * vt;
+        }
         y[tid] = s;
     }
     __syncthreads();
     if (tid < DV) out[(int64_t)bh * DV + tid] = from_f32<TOut>(y[tid] / y[DV]);
+    if (direct) {
+        if (tid < dk) pend_k[((int64_t)bh * kMaxDecodeWindow + npend) * dk + tid] = to_f32(k[(int64_t)bh * dk + tid]);
+        if (tid < DV) pend_v[((int64_t)bh * kMaxDecodeWindow + npend) * DV + tid] = to_f32(v[(int64_t)bh * DV + tid]);
+    }
 }
 
 static int64_t decode_blocks(const sata_index *idx, int fpt) {
@@ -207,24 +407,49 @@ int64_t decode_workspace_bytes(const sata_index *idx, int64_t bh) {
 }
 
 template <int DV, typename TIn, typename TOut, typename TS>
-static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, const void *q,
-                                  const void *k, const void *v, void *out, hipStream_t stream) {
+static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, const void *q, const void *k,
+                                  const void *v, void *out, DecodeMode mode, hipStream_t stream) {
     const int64_t bh = (int64_t)st->batch * st->heads;
-    const int nblk = (int)decode_blocks(idx, dec_fpt<TS>());
+    const bool fold = mode == kDecodeFold || mode == kDecodeFlush;
+    const int fpt = fold ? dec_fpt<TS, kMaxDecodeWindow>() : dec_fpt<TS, 1>();
+    const int64_t tiles = decode_blocks(idx, fpt);
+    const dim3 grid((unsigned)(mode == kDecodeRead ? (tiles + kReadTiles - 1) / kReadTiles : tiles), (unsigned)bh);
+    const int nblk = (int)grid.x;
     float *partial = static_cast<float *>(st->d_work);
-    {
-        ProfScope ps(kProfDecode, stream);
-        hipLaunchKernelGGL((decode_kernel<DV, TIn, TS>), dim3(nblk, (unsigned)bh), dim3(kDecThreads), 0, stream,
-                           idx->d_tup, idx->d_coef, static_cast<TS *>(st->d_state), idx->m_pad, idx->dk,
-                           static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), partial);
+    TS *S = static_cast<TS *>(st->d_state);
+    const TIn *qi = static_cast<const TIn *>(q), *ki = static_cast<const TIn *>(k), *vi = static_cast<const TIn *>(v);
+    switch (mode) {
+        case kDecodePlain: {
+            ProfScope ps(kProfDecode, stream);
+            hipLaunchKernelGGL((decode_kernel<DV, TIn, TS, 1>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
+                               idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, nullptr, nullptr, 0, partial);
+            break;
+        }
+        case kDecodeRead: {
+            ProfScope ps(kProfDecodeRead, stream);
+            hipLaunchKernelGGL((decode_read_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
+                               idx->d_coef, S, idx->m_pad, idx->dk, qi, partial);
+            break;
+        }
+        case kDecodeFold:
+        case kDecodeFlush: {
+            ProfScope ps(kProfDecodeFold, stream);
+            const bool step = mode == kDecodeFold;
+            hipLaunchKernelGGL((decode_kernel<DV, TIn, TS, kMaxDecodeWindow>), grid, dim3(kDecThreads), 0, stream,
+                               idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, step ? qi : nullptr,
+                               step ? ki : nullptr, step ? vi : nullptr, st->d_pend_k, st->d_pend_v, st->npend,
+                               partial);
+            break;
+        }
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || mode == kDecodeFlush) return e;
     {
         ProfScope ps(kProfDecodeFinish, stream);
-        hipLaunchKernelGGL((decode_finish_kernel<DV, TOut>), dim3((unsigned)bh), dim3(128), 0, stream,
-                           partial, nblk, static_cast<TOut *>(out));
+        const int direct = mode == kDecodeRead ? 1 : 0;
+        hipLaunchKernelGGL((decode_finish_kernel<DV, TIn, TOut>), dim3((unsigned)bh), dim3(128), 0, stream, partial,
+                           nblk, static_cast<TOut *>(out), direct, idx->dk, idx->P, qi, ki, vi, st->d_pend_k,
+                           st->d_pend_v, st->npend);
     }
     return hipGetLastError();
 }
@@ -232,19 +457,22 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
 template <int DV, typename TS>
 static hipError_t launch_decode_ts(const sata_index *idx, const sata_state *st, const void *q,
                                    const void *k, const void *v, void *out, sata_dtype in_dt,
-                                   sata_dtype out_dt, hipStream_t s) {
-    if (in_dt == SATA_F32 && out_dt == SATA_F32) return launch_decode_t<DV, float, float, TS>(idx, st, q, k, v, out, s);
-    if (in_dt == SATA_F32 && out_dt == SATA_BF16) return launch_decode_t<DV, float, bf16_t, TS>(idx, st, q, k, v, out, s);
-    if (in_dt == SATA_BF16 && out_dt == SATA_F32) return launch_decode_t<DV, bf16_t, float, TS>(idx, st, q, k, v, out, s);
-    return launch_decode_t<DV, bf16_t, bf16_t, TS>(idx, st, q, k, v, out, s);
+                                   sata_dtype out_dt, DecodeMode mode, hipStream_t s) {
+    if (in_dt == SATA_F32 && out_dt == SATA_F32)
+        return launch_decode_t<DV, float, float, TS>(idx, st, q, k, v, out, mode, s);
+    if (in_dt == SATA_F32 && out_dt == SATA_BF16)
+        return launch_decode_t<DV, float, bf16_t, TS>(idx, st, q, k, v, out, mode, s);
+    if (in_dt == SATA_BF16 && out_dt == SATA_F32)
+        return launch_decode_t<DV, bf16_t, float, TS>(idx, st, q, k, v, out, mode, s);
+    return launch_decode_t<DV, bf16_t, bf16_t, TS>(idx, st, q, k, v, out, mode, s);
 }
 
 template <int DV>
 static hipError_t launch_decode_dv(const sata_index *idx, const sata_state *st, const void *q,
                                    const void *k, const void *v, void *out, sata_dtype in_dt,
-                                   sata_dtype out_dt, hipStream_t s) {
-    if (st->dtype == SATA_BF16) return launch_decode_ts<DV, bf16_t>(idx, st, q, k, v, out, in_dt, out_dt, s);
-    return launch_decode_ts<DV, float>(idx, st, q, k, v, out, in_dt, out_dt, s);
+                                   sata_dtype out_dt, DecodeMode mode, hipStream_t s) {
+    if (st->dtype == SATA_BF16) return launch_decode_ts<DV, bf16_t>(idx, st, q, k, v, out, in_dt, out_dt, mode, s);
+    return launch_decode_ts<DV, float>(idx, st, q, k, v, out, in_dt, out_dt, mode, s);
 }
 
 // Element-wise state conversion between fp32 and bf16 (round to nearest even).
@@ -269,13 +497,13 @@ hipError_t launch_state_convert(const sata_state *src, sata_state *dst, hipStrea
 }
 
 hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void *q, const void *k,
-                         const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt,
+                         const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt, DecodeMode mode,
                          hipStream_t stream) {
     switch (idx->dv) {
-        case 8: return launch_decode_dv<8>(idx, st, q, k, v, out, in_dt, out_dt, stream);
-        case 16: return launch_decode_dv<16>(idx, st, q, k, v, out, in_dt, out_dt, stream);
-        case 32: return launch_decode_dv<32>(idx, st, q, k, v, out, in_dt, out_dt, stream);
-        case 64: return launch_decode_dv<64>(idx, st, q, k, v, out, in_dt, out_dt, stream);
+        case 8: return launch_decode_dv<8>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
+        case 16: return launch_decode_dv<16>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
+        case 32: return launch_decode_dv<32>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
+        case 64: return launch_decode_dv<64>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -110,6 +110,16 @@ sata_status ensure_work(sata_state *st, int64_t bytes) {
     return SATA_OK;
 }
 
+// Folds a state's deferred decode tokens into its buffer (no-op without any).
+sata_status flush_pending(sata_state *st, hipStream_t stream) {
+    if (st->npend == 0) return SATA_OK;
+    hipError_t e = sata::launch_decode(st->idx, st, nullptr, nullptr, nullptr, nullptr, SATA_F32, SATA_F32,
+                                       sata::kDecodeFlush, stream);
+    if (e != hipSuccess) return fail_hip(e, "fold of deferred decode tokens");
+    st->npend = 0;
+    return SATA_OK;
+}
+
 sata_status check_index_state(const sata_index *idx, const sata_state *st) {
     if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
     if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
@@ -440,7 +450,7 @@ sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *
     return sata_state_alloc_dtype(idx, batch, heads, SATA_F32, stream, out);
 }
 
-sata_status sata_state_convert(const sata_state *src, sata_state *dst, void *stream) {
+sata_status sata_state_convert(sata_state *src, sata_state *dst, void *stream) {
     g_last_error.clear();
     if (!src || !dst) return fail(SATA_ERR_INVALID, "src and dst must be non-NULL");
     if (src == dst) return fail(SATA_ERR_INVALID, "src and dst must be different states");
@@ -449,8 +459,11 @@ sata_status sata_state_convert(const sata_state *src, sata_state *dst, void *str
         return fail(SATA_ERR_INVALID, "src and dst differ in batch or heads");
     DeviceGuard g(dst->device);
     if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    sata_status s = flush_pending(src, (hipStream_t)stream);
+    if (s != SATA_OK) return s;
     hipError_t e = sata::launch_state_convert(src, dst, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "state conversion");
+    dst->npend = 0;
     return SATA_OK;
 }
 
@@ -460,6 +473,7 @@ sata_status sata_state_reset(sata_state *st, void *stream) {
     DeviceGuard g(st->device);
     hipError_t e = sata::launch_zero(static_cast<float *>(st->d_state), st->state_bytes / 4, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "state clear");
+    st->npend = 0;
     return SATA_OK;
 }
 
@@ -468,6 +482,8 @@ void sata_state_free(sata_state *st) {
     DeviceGuard g(st->device);
     if (st->d_state) (void)hipFree(st->d_state);
     if (st->d_work) (void)hipFree(st->d_work);
+    if (st->d_pend_k) (void)hipFree(st->d_pend_k);
+    if (st->d_pend_v) (void)hipFree(st->d_pend_v);
     delete st;
 }
 
@@ -505,6 +521,8 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
     s = ensure_work(st, plan.work_bytes);
     if (s != SATA_OK) return s;
+    s = flush_pending(st, (hipStream_t)stream);
+    if (s != SATA_OK) return s;
     hipError_t e = sata::launch_prefill(idx, st, plan, q, k, v, out, n, in_dt, out_dt, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "prefill launch");
     return SATA_OK;
@@ -528,9 +546,48 @@ sata_status sata_decode_step(const sata_index *idx, sata_state *st, const void *
     if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
     s = ensure_work(st, sata::decode_workspace_bytes(idx, bh));
     if (s != SATA_OK) return s;
-    hipError_t e = sata::launch_decode(idx, st, q, k, v, out, in_dt, out_dt, (hipStream_t)stream);
+    const sata::DecodeMode mode = st->window <= 1              ? sata::kDecodePlain
+                                  : st->npend + 1 < st->window ? sata::kDecodeRead
+                                                               : sata::kDecodeFold;
+    hipError_t e = sata::launch_decode(idx, st, q, k, v, out, in_dt, out_dt, mode, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "decode launch");
+    if (mode == sata::kDecodeRead) ++st->npend;
+    if (mode == sata::kDecodeFold) st->npend = 0;
     return SATA_OK;
+}
+
+sata_status sata_state_set_decode_window(sata_state *st, int window, void *stream) {
+    g_last_error.clear();
+    if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
+    if (window < 1 || window > kMaxDecodeWindow)
+        return fail(SATA_ERR_INVALID, "window must be in [1, %d] (got %d)", kMaxDecodeWindow, window);
+    DeviceGuard g(st->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    if (window > 1 && !st->d_pend_k) {
+        const int64_t slots = (int64_t)st->batch * st->heads * kMaxDecodeWindow;
+        float *pk = nullptr, *pv = nullptr;
+        hipError_t e = hipMalloc(&pk, (size_t)(slots * st->idx->dk * sizeof(float)));
+        if (e == hipSuccess) e = hipMalloc(&pv, (size_t)(slots * st->idx->dv * sizeof(float)));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            if (pk) (void)hipFree(pk);
+            return fail(SATA_ERR_OOM, "pending-token buffers of %lld slots", (long long)slots);
+        }
+        st->d_pend_k = pk;
+        st->d_pend_v = pv;
+    }
+    sata_status s = flush_pending(st, (hipStream_t)stream);
+    if (s != SATA_OK) return s;
+    st->window = window;
+    return SATA_OK;
+}
+
+sata_status sata_state_flush(sata_state *st, void *stream) {
+    g_last_error.clear();
+    if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
+    DeviceGuard g(st->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    return flush_pending(st, (hipStream_t)stream);
 }
 
 sata_status sata_expand_features(const sata_index *idx, const void *x, void *out, int64_t rows, int side,
@@ -593,7 +650,7 @@ void prof_clear_locked() {
 }
 
 const char *const kProfNames[sata::kProfCount] = {"prefill_scan", "prefill_combine", "decode_stream",
-                                                   "decode_finish"};
+                                                   "decode_finish", "decode_read", "decode_fold"};
 
 }  // namespace
 

@@ -20,6 +20,9 @@
 
 #include "../../include/sata.h"
 
+// Largest decode window: deferred tokens held per head before a fold.
+constexpr int kMaxDecodeWindow = 16;
+
 struct sata_index {
     int dk = 0, dv = 0, P = 0;
     int64_t m = 0;       // C(d_K+P-1, P-1)
@@ -48,6 +51,10 @@ struct sata_state {
     int64_t state_bytes = 0;
     void *d_work = nullptr;      // prefill / decode partial sums (grown on demand)
     int64_t work_bytes = 0;
+    int window = 1;              // decode steps per state update (1: every step)
+    int npend = 0;               // deferred tokens not yet in d_state (host-side count, < window)
+    float *d_pend_k = nullptr;   // [B*H][kMaxDecodeWindow][d_K] deferred keys (fp32)
+    float *d_pend_v = nullptr;   // [B*H][kMaxDecodeWindow][d_V] deferred values (fp32)
 };
 
 namespace sata {
@@ -73,8 +80,13 @@ constexpr int kMaxOrder = 3;             // P <= 4
 // ---- launchers (defined in the .hip files) --------------------------------
 
 // Decode: one token per head.  Returns hipSuccess or the launch error.
+// Decode launches: a plain step (update by the step's token, read out), a
+// deferred step's readout of the state as it stands (direct terms for the
+// pending tokens and the step's own), a fold (update by the pending tokens and
+// the step's own, read out), or a flush (update by the pending tokens only).
+enum DecodeMode { kDecodePlain, kDecodeRead, kDecodeFold, kDecodeFlush };
 hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void *q, const void *k,
-                         const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt,
+                         const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt, DecodeMode mode,
                          hipStream_t stream);
 int64_t decode_workspace_bytes(const sata_index *idx, int64_t bh);
 hipError_t launch_state_convert(const sata_state *src, sata_state *dst, hipStream_t stream);
@@ -101,7 +113,10 @@ hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const Pre
 // Kernel timing instrumentation (see sata_profile_enable).  A ProfScope
 // records an event before and after the launches in its lifetime when
 // profiling is on, and does nothing otherwise.
-enum ProfKernel { kProfScan = 0, kProfCombine = 1, kProfDecode = 2, kProfDecodeFinish = 3, kProfCount = 4 };
+enum ProfKernel {
+    kProfScan = 0, kProfCombine = 1, kProfDecode = 2, kProfDecodeFinish = 3, kProfDecodeRead = 4, kProfDecodeFold = 5,
+    kProfCount = 6
+};
 struct ProfScope {
     ProfScope(int kernel, hipStream_t stream);
     ~ProfScope();

@@ -24,7 +24,8 @@ SATA_F32, SATA_BF16 = 0, 1
 
 _EXPORTS = (
     "sata_build_index", "sata_index_free", "sata_index_features", "sata_index_info",
-    "sata_state_alloc", "sata_state_alloc_dtype", "sata_state_convert", "sata_state_reset", "sata_state_free",
+    "sata_state_alloc", "sata_state_alloc_dtype", "sata_state_convert", "sata_state_set_decode_window",
+    "sata_state_flush", "sata_state_reset", "sata_state_free",
     "sata_state_data",
     "sata_prefill", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
     "sata_status_string", "sata_last_error",
@@ -70,6 +71,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_state_alloc.argtypes = [vp, cint, cint, vp, pvp]
     lib.sata_state_alloc_dtype.argtypes = [vp, cint, cint, cint, vp, pvp]
     lib.sata_state_convert.argtypes = [vp, vp, vp]
+    lib.sata_state_set_decode_window.argtypes = [vp, cint, vp]
+    lib.sata_state_flush.argtypes = [vp, vp]
     lib.sata_state_reset.argtypes = [vp, vp]
     lib.sata_state_free.argtypes = [vp]
     lib.sata_state_free.restype = None
@@ -92,7 +95,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_profile_kernel_name.argtypes = [cint]
     lib.sata_profile_kernel_name.restype = ctypes.c_char_p
     for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_alloc_dtype",
-                 "sata_state_convert", "sata_state_reset",
+                 "sata_state_convert", "sata_state_set_decode_window", "sata_state_flush", "sata_state_reset",
                  "sata_state_data", "sata_prefill", "sata_decode_step", "sata_expand_features"):
         getattr(lib, name).restype = cint
     _lib = lib
@@ -218,6 +221,17 @@ def sata_state_convert(src: State, dst: State, stream=None):
     _check(load().sata_state_convert(src.ptr, dst.ptr, _stream(stream)), "sata_state_convert")
 
 
+def sata_state_set_decode_window(state: State, window: int, stream=None):
+    """Decode steps per state update (1..16); deferred tokens are read out from their direct weights."""
+    _check(load().sata_state_set_decode_window(state.ptr, int(window), _stream(stream)),
+           "sata_state_set_decode_window")
+
+
+def sata_state_flush(state: State, stream=None):
+    """Fold deferred decode tokens into the state buffer."""
+    _check(load().sata_state_flush(state.ptr, _stream(stream)), "sata_state_flush")
+
+
 def sata_state_reset(state: State, stream=None):
     _check(load().sata_state_reset(state.ptr, _stream(stream)), "sata_state_reset")
 
@@ -312,7 +326,8 @@ def sata_describe_features(d_k: int, P: int):
     return tup, coef
 
 
-PROFILE_KERNELS = {"prefill_scan": 0, "prefill_combine": 1, "decode_stream": 2, "decode_finish": 3}
+PROFILE_KERNELS = {"prefill_scan": 0, "prefill_combine": 1, "decode_stream": 2, "decode_finish": 3,
+                   "decode_read": 4, "decode_fold": 5}
 
 
 def sata_profile_enable(on: bool):

@@ -120,9 +120,33 @@ sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, 
 /* Copy src's content into dst, converting the element type (fp32 -> bf16
  * rounds to nearest even; bf16 -> fp32 is exact; equal types copy).  Both must
  * belong to the same index and have the same batch and heads; src != dst
- * (else SATA_ERR_INVALID, nothing enqueued).  Enqueued on `stream`; dst's
- * workspace is untouched. */
-sata_status sata_state_convert(const sata_state *src, sata_state *dst, void *stream);
+ * (else SATA_ERR_INVALID, nothing enqueued).  src's deferred decode tokens
+ * (sata_state_set_decode_window) are folded into src first; dst's are
+ * discarded.  Enqueued on `stream`; dst's workspace and window are
+ * untouched. */
+sata_status sata_state_convert(sata_state *src, sata_state *dst, void *stream);
+
+/* Decode window: the number W of decode steps per update of the state buffer
+ * (1 <= W <= 16, else SATA_ERR_INVALID; default 1).  With W > 1,
+ * sata_decode_step defers the update: W - 1 steps in a row only read the
+ * state out, adding each deferred token's (and the step's own) term from its
+ * direct Taylor weight w(q.k_t / sqrt(d_K)) [v_t, 1] -- the single-token sum
+ * that the state's orders hold for it [hotdry, "Core insight of symmetric
+ * tensor decomposition"] -- and keep k and v of the step in a small per-head
+ * buffer; every W-th step adds all of them to the state in one
+ * read-modify-write pass and reads out from the result.  The outputs are the
+ * same as with W = 1 up to rounding, and each step still costs a bounded
+ * amount of work whatever the context length [hotdry, "Engineering
+ * realisation of the constant compute cost"], while W - 1 of every W steps
+ * stream the state once instead of twice.  Deferred tokens are folded in
+ * before the window changes, before a prefill, before a conversion, and by
+ * sata_state_flush; sata_state_reset discards them.  The first call with
+ * W > 1 allocates the token buffers (hipMalloc, 16 slots per head). */
+sata_status sata_state_set_decode_window(sata_state *st, int window, void *stream);
+
+/* Fold the deferred decode tokens into the state buffer (no-op if none), so
+ * that the buffer holds every token seen.  Enqueued on `stream`. */
+sata_status sata_state_flush(sata_state *st, void *stream);
 
 /* Zero the state (start a new sequence); enqueued on `stream`. */
 sata_status sata_state_reset(sata_state *st, void *stream);
@@ -132,7 +156,8 @@ void sata_state_free(sata_state *st);
 
 /* Device pointer and byte size of the state buffer (for checkpointing or
  * inspection; the layout is given at sata_state_alloc, elements of the type
- * given at allocation). */
+ * given at allocation).  Deferred decode tokens are not in it until
+ * sata_state_flush. */
 sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes);
 
 /* Causal prefill of n tokens for every head of the state, continuing from the
@@ -156,7 +181,8 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
  * order's state, then read out and normalise into out: [batch][heads][d_V]
  * [hotdry, "Engineering realisation of the constant compute cost": the cost
  * per token is fixed by d_K, d_V and P].  Each head's state is streamed once
- * (read and written), coalesced along the feature axis. */
+ * (read and written), coalesced along the feature axis.  With a decode window
+ * above 1 the update is deferred (sata_state_set_decode_window). */
 sata_status sata_decode_step(const sata_index *idx, sata_state *st, const void *q, const void *k,
                              const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt,
                              void *stream);
@@ -199,8 +225,8 @@ int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *
  * (0) stops recording and keeps them.  sata_profile_query waits for the
  * recorded events of one kernel and returns the summed duration (ms) and the
  * launch count.  Kernel ids: 0 prefill scan, 1 prefill combine, 2 decode
- * stream, 3 decode finish (names from sata_profile_kernel_name, NULL for an
- * unknown id).  Host-thread safe; not meant to be left on in production. */
+ * stream, 3 decode finish, 4 decode read (deferred steps), 5 decode fold
+ * (names from sata_profile_kernel_name, NULL for an unknown id).  Host-thread safe; not meant to be left on in production. */
 sata_status sata_profile_enable(int on);
 sata_status sata_profile_query(int kernel, double *total_ms, int64_t *launches);
 const char *sata_profile_kernel_name(int kernel);

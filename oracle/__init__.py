@@ -79,7 +79,7 @@ def _load():
     lib.orc_phi.restype = i64
     lib.orc_round_bf16_array.argtypes = [f64p, f64p, i64]
     lib.orc_round_bf16_array.restype = None
-    lib.orc_bf16_state_decode.argtypes = [f32p, f32p, f32p, f64p, i64, i64, i64, cint, cint, cint, cint]
+    lib.orc_bf16_state_decode.argtypes = [f32p, f32p, f32p, f64p, i64, i64, i64, cint, cint, cint, cint, cint]
     lib.orc_bf16_state_decode.restype = cint
     for name in ("orc_recurrent_attention", "orc_recurrent_attention_f32"):
         fn = getattr(lib, name)
@@ -225,13 +225,15 @@ def round_bf16(x) -> np.ndarray:
     return out
 
 
-def bf16_state_decode(q, k, v, P: int, n0: int, rounding: bool = True) -> np.ndarray:
+def bf16_state_decode(q, k, v, P: int, n0: int, rounding: bool = True, window: int = 1) -> np.ndarray:
     """O8: decode steps on a bf16-stored state [hotdry, "Hardware optimisation
     paths and current limits": 16-bit storage of the state].  Tokens 0..n0-1
     are summed exactly into the one-sided state and rounded once; each later
     token is added exactly, read out from the unrounded sums and the sums are
     rounded to bf16 (ties to even) when stored.  Returns rows n0..n-1:
-    [..., n - n0, d_V].  rounding=False gives the exact one-sided recurrent
+    [..., n - n0, d_V].  window > 1 stores only every window-th step: the
+    steps between read out the stored values plus the exact terms of the
+    tokens not yet stored.  rounding=False gives the exact one-sided recurrent
     form.  fp64; moderate inputs."""
     lead, bh, n, dk, dv = _heads(np.asarray(q), np.asarray(k), np.asarray(v))
     if not 0 <= n0 <= n:
@@ -241,7 +243,7 @@ def bf16_state_decode(q, k, v, P: int, n0: int, rounding: bool = True) -> np.nda
     v32, vp = _f32(v)
     out = np.empty((bh, n - n0, dv), dtype=np.float64)
     rc = _load().orc_bf16_state_decode(qp, kp, vp, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                                       bh, int(n0), n, dk, dv, int(P), 1 if rounding else 0)
+                                       bh, int(n0), n, dk, dv, int(P), 1 if rounding else 0, int(window))
     if rc:
         raise ValueError("orc_bf16_state_decode rejected its arguments")
     return out.reshape(tuple(lead) + (n - n0, dv))

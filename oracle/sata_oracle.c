@@ -372,6 +372,12 @@ void orc_round_bf16_array(const double *x, double *out, int64_t n) {
  * those unrounded sums, and the sums are rounded to bf16 when stored back.
  * Rows n0..n-1 are written to out: [bh][n - n0][dv].
  *
+ * window W >= 1 defers the stores: W - 1 steps in a row read out the stored
+ * values plus, exactly, the terms of the tokens not yet stored and of the
+ * step's own token; every W-th step adds all of them to the stored values,
+ * reads out from those sums and stores them rounded.  W = 1 stores every
+ * step.
+ *
  * round_mode 0 skips every rounding: the exact one-sided recurrent form.
  * Tiny to moderate inputs; returns nonzero on bad arguments. */
 /* The summed prefix of one head, features [f_lo, f_hi) per thread. */
@@ -406,8 +412,8 @@ static void *prefix_worker(void *arg) {
 }
 
 int orc_bf16_state_decode(const float *q, const float *k, const float *v, double *out,
-                          int64_t bh, int64_t n0, int64_t n, int dk, int dv, int P, int round_mode) {
-    if (bh < 0 || n0 < 0 || n < n0 || dk <= 0 || dv <= 0 || P < 1 || P > 8) return 1;
+                          int64_t bh, int64_t n0, int64_t n, int dk, int dv, int P, int round_mode, int window) {
+    if (bh < 0 || n0 < 0 || n < n0 || dk <= 0 || dv <= 0 || P < 1 || P > 8 || window < 1) return 1;
     int64_t ng[8], off[8], m = 0;
     for (int p = 0; p < P; ++p) {
         ng[p] = orc_basis_bruteforce(dk, p, NULL, NULL, 0);
@@ -461,21 +467,26 @@ int orc_bf16_state_decode(const float *q, const float *k, const float *v, double
             for (int t = 1; t < nt; ++t)
                 if (started[t]) pthread_join(th[t], NULL);
         }
-        /* decode steps */
+        /* decode steps; tokens first..s are not yet in the stored values */
+        int64_t first = n0;
         for (int64_t s = n0; s < n; ++s) {
+            const int store = (s - first + 1) >= window;
             for (int c = 0; c <= dv; ++c) y[c] = 0.0;
             for (int64_t f = 0; f < m; ++f) {
-                double mk = 1.0, mq = qw[f];
-                for (int r = 0; r < ord[f]; ++r) {
-                    mk *= (double)kh[s * dk + tup[f * W + r]];
-                    mq *= (double)qh[s * dk + tup[f * W + r]];
-                }
+                double mq = qw[f];
+                for (int r = 0; r < ord[f]; ++r) mq *= (double)qh[s * dk + tup[f * W + r]];
                 for (int c = 0; c <= dv; ++c) {
-                    const double x = S[f * (dv + 1) + c] + mk * (c < dv ? (double)vh[s * dv + c] : 1.0);
+                    double x = S[f * (dv + 1) + c];
+                    for (int64_t t = first; t <= s; ++t) {
+                        double mk = 1.0;
+                        for (int r = 0; r < ord[f]; ++r) mk *= (double)kh[t * dk + tup[f * W + r]];
+                        x += mk * (c < dv ? (double)vh[t * dv + c] : 1.0);
+                    }
                     y[c] += mq * x;
-                    S[f * (dv + 1) + c] = round_mode ? orc_round_bf16(x) : x;
+                    if (store) S[f * (dv + 1) + c] = round_mode ? orc_round_bf16(x) : x;
                 }
             }
+            if (store) first = s + 1;
             for (int c = 0; c < dv; ++c) out[(h * (n - n0) + (s - n0)) * dv + c] = y[c] / y[dv];
         }
     }

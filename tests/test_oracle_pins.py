@@ -312,15 +312,16 @@ def test_round_bf16_integers(oracle):
     assert list(got) == [255, 256, 256, 258, 260, 260, 264, 512, 516]
 
 
-@pytest.mark.parametrize("d,P,n0", [(1, 1, 0), (2, 3, 5), (3, 4, 0), (4, 4, 17), (4, 2, 39)])
-def test_bf16_state_unrounded_equals_quadratic(oracle, d, P, n0):
+@pytest.mark.parametrize("d,P,n0,window", [(1, 1, 0, 1), (2, 3, 5, 1), (3, 4, 0, 1), (4, 4, 17, 1), (4, 2, 39, 1),
+                                          (3, 4, 0, 4), (4, 3, 7, 16), (2, 4, 11, 5)])
+def test_bf16_state_unrounded_equals_quadratic(oracle, d, P, n0, window):
     """O8 with rounding off is the one-sided recurrent form, whatever the
     split between summed prefix and steps: equal to the quadratic
     definition (O1) on rows n0.. .  Catches a wrong query weight
     (p!/alpha!, 1/p!, d^(p/2)), a step read out before its update, or a
     prefix that misses a token."""
     q, k, v = _rand_qkv(300 + 10 * d + P, (2,), 40, d, 3)
-    a = oracle.bf16_state_decode(q, k, v, P, n0, rounding=False)
+    a = oracle.bf16_state_decode(q, k, v, P, n0, rounding=False, window=window)
     b = oracle.taylor_attention(q, k, v, P)[:, n0:]
     assert a.shape == b.shape
     assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
@@ -361,3 +362,20 @@ def test_bf16_state_count_stalls(oracle, n0):
     assert np.array_equal(o, ref)
     exact = oracle.bf16_state_decode(q, k, v, 1, n0, rounding=False)[0]
     assert np.array_equal(exact, w[None, :].astype(np.float64) / (s + 1)[:, None])
+
+
+@pytest.mark.parametrize("window", [4, 16])
+def test_bf16_state_count_stalls_with_window(oracle, window):
+    """With stores every W steps the P = 1 normaliser grows by W per store and
+    stops at 256 W (adding W is then a half-way case); between stores each
+    step adds its pending tokens and its own exactly, so row s reads out
+    min(floor(s / W) W, 256 W) + (s mod W) + 1."""
+    n = 256 * window + 3 * window + 2
+    w = np.array([512.0, -1.5], dtype=np.float32)
+    v = np.zeros((1, n, 2), dtype=np.float32)
+    v[0, 0] = w
+    q = np.zeros((1, n, 1), dtype=np.float32)
+    o = oracle.bf16_state_decode(q, q, v, 1, 0, window=window)[0]
+    s = np.arange(n)
+    den = np.minimum((s // window) * window, 256 * window) + s % window + 1
+    assert np.array_equal(o, w[None, :].astype(np.float64) / den[:, None])
