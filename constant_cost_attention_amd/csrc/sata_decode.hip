@@ -108,6 +108,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int FPT>
 __device__ __forceinline__ void lane_tables(bool valid, const uint32_t *tup, const float *coef, int64_t f0,
                                             uint32_t (&tt)[FPT], float (&cc)[FPT]) {
+    static_assert(FPT % 4 == 0, "tables are read 16 bytes (4 features) at a time");
 #pragma unroll
     for (int h = 0; h < FPT / 4; ++h) {
         uint4 t4 = uint4{0u, 0u, 0u, 0u};
@@ -175,7 +176,7 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
     const int tid = threadIdx.x;
     const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
     const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
-    const bool readout = q != nullptr;
+    const bool readout = W == 1 || q != nullptr;   // a plain step always reads out
     TS *Sb = state + (int64_t)bh * NC * m_pad + f0;
     auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
 
@@ -189,7 +190,15 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
     lane_tables<FPT>(valid, tup, coef, f0, tt, cc);
 
     // tokens into LDS: slot t < npend from the pending buffers, slot npend the
-    // step's own token, the rest zero (they add nothing)
+    // step's own token, the rest zero (they add nothing).  Only entries up to
+    // d_K + 1 are read (index d_K is the constant 1, d_K + 1 the padding 0).
+    if constexpr (W == 1) {
+        if (tid <= dk + 1) {
+            sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+            sk[0][tid] = tid < dk ? to_f32(k[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+        }
+        if (tid < NC) sv[tid][0] = tid < DV ? to_f32(v[(int64_t)bh * DV + tid]) : 1.f;
+    } else {
     const int ntok = npend + (k != nullptr ? 1 : 0);
     for (int i = tid; i < W * 72; i += kDecThreads) {
         const int t = i / 72, c = i % 72;
@@ -211,6 +220,7 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
         sv[c][t] = x;
     }
     if (readout && tid < 72) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    }
     __syncthreads();
 
     float phk[W][FPT], psq[FPT];
@@ -254,7 +264,7 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
 // consecutive feature tiles (256 * FPT features each) of its head and keeps
 // the next half-tile's rows in flight while it reads out the current half;
 // the readout sums accumulate across the tiles and are reduced once.
-constexpr int kReadTiles = 4;
+constexpr int kReadTiles = 8;
 template <int DV, typename TIn, typename TS>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef,
