@@ -216,6 +216,33 @@ def time_decode(sata, idx, st, wl, steps: int, warmup: int, seed: int):
     return ms, kern
 
 
+def stream_ceiling(nbytes: float, reps: int = 10):
+    """Measured HBM ceilings of plain library streams over a buffer the size of
+    the decode workload's state (far larger than every cache): an in-place
+    fp32 scale (read and write once) and row sums over 4096-wide rows (read
+    once; the fastest of the torch read-only reductions tried, a flat sum
+    reaches only about 3.9 TB/s), timed with events on torch's stream.  GB/s
+    of algorithmic bytes."""
+    import torch
+    x = torch.ones(int(nbytes) // 4 // 4096 * 4096, dtype=torch.float32, device="cuda")
+    out = {}
+    for name, fn, moved in (("rmw_gbs", lambda: x.mul_(1.0), 2 * x.numel() * 4),
+                            ("read_gbs", lambda: x.view(-1, 4096).sum(1), x.numel() * 4)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del x
+    torch.cuda.empty_cache()
+    out["method"] = "torch in-place mul_, and row sums of 4096, over a %.2f GB fp32 tensor" % (nbytes / 1e9)
+    return out
+
+
 def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
     import torch
     idx = sata.Index(wl.d_k, wl.d_v, wl.P)
@@ -253,6 +280,7 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
         },
         "finish_ms_per_step": fin_ms,
         "gbs_whole_step": nbytes / (ms * 1e-3) / 1e9,
+        "ceiling": None,
         "bf16_state": {
             "value": wl.batch / (ms16 * 1e-3), "unit": "tokens/s", "ms_per_step": ms16,
             "roofline": {
@@ -275,6 +303,10 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
             "finish_ms_per_step": kw["decode_finish"][0],
         },
     }
+    ceil = stream_ceiling(decode_read_bytes(wl))
+    ceil["decode_stream_frac"] = achieved / ceil["rmw_gbs"]
+    ceil["decode_read_frac"] = ach_read / ceil["read_gbs"]
+    res["ceiling"] = ceil
     if flatness:
         flat = {}
         for prefix in (8192, 32768, 65536):
@@ -490,6 +522,10 @@ def main():
         b16 = dec["bf16_state"]
         log("decode, bf16 state: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak)"
             % (b16["ms_per_step"], b16["value"], b16["roofline"]["achieved"], 100 * b16["roofline"]["frac"]))
+        c = dec["ceiling"]
+        log("decode ceilings: library RMW stream %.0f GB/s (decode kernel at %.1f%% of it), read stream %.0f GB/s "
+            "(read kernel at %.1f%%)" % (c["rmw_gbs"], 100 * c["decode_stream_frac"], c["read_gbs"],
+                                         100 * c["decode_read_frac"]))
         dw = dec["window"]
         log("decode, window %d: %.3f ms/step, %.3e tok/s, read %.3f ms at %.0f GB/s (%.1f%% of peak), "
             "fold %.3f ms at %.0f GB/s"

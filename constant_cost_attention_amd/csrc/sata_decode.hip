@@ -352,45 +352,65 @@ void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restric
     store_partial<DV>(acc, red, partial, bh);
 }
 
-// Adds a head's partial sums in block order, then (deferred steps) the direct
+// Adds a head's partial sums in a fixed order (four interleaved groups of
+// workgroups, then the groups in turn), then (deferred steps) the direct
 // Taylor-weighted terms of the npend pending tokens and of the step's own
 // token, w(q.k_t / sqrt(d_K)) [v_t, 1] with w(x) = sum_{p<P} x^p / p!, the
 // same sum the state's orders give for one token [hotdry, "Core insight of
 // symmetric tensor decomposition"]; divides by the normaliser; and (deferred
 // steps) appends the step's token to the pending buffers at slot npend.
+constexpr int kFinishThreads = 320;
 template <int DV, typename TIn, typename TOut>
-__global__ __launch_bounds__(128) void decode_finish_kernel(const float *__restrict__ partial, int nblk,
-                                                            TOut *__restrict__ out, int direct, int dk, int P,
-                                                            const TIn *__restrict__ q, const TIn *__restrict__ k,
-                                                            const TIn *__restrict__ v, float *__restrict__ pend_k,
-                                                            float *__restrict__ pend_v, int npend) {
+__global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(
+    const float *__restrict__ partial, int nblk, TOut *__restrict__ out, int direct, int dk, int P,
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, float *__restrict__ pend_k,
+    float *__restrict__ pend_v, int npend) {
     constexpr int NC = DV + 1;
+    constexpr int G = 4;                        // partial-sum groups per column
+    static_assert(G * NC <= kFinishThreads, "one thread per (group, column)");
+    static_assert(kMaxDecodeWindow * 16 <= kFinishThreads, "16 threads per token");
+    __shared__ float part[G][NC];
     __shared__ float y[NC];
     __shared__ float wt[kMaxDecodeWindow];
-    static_assert(kMaxDecodeWindow <= 128, "one thread per token");
     const int bh = blockIdx.x, tid = threadIdx.x;
     const int ntok = direct ? npend + 1 : 0;
-    if (tid < ntok) {
-        // token tid: pending slot tid, or the step's own token
-        const float rs = rsqrtf((float)dk);
-        float dot = 0.f;
-        for (int i = 0; i < dk; ++i) {
-            const float kv =
-                tid < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + tid) * dk + i] : to_f32(k[(int64_t)bh * dk + i]);
-            dot += to_f32(q[(int64_t)bh * dk + i]) * kv;
+    // column c, group g: the partial rows b = g, g + G, ... (several loads in flight)
+    if (tid < G * NC) {
+        const int c = tid % NC, g = tid / NC;
+        const float *pr = partial + (int64_t)bh * nblk * NC + c;
+        float s = 0.f;
+#pragma unroll 4
+        for (int b = g; b < nblk; b += G) s += pr[(int64_t)b * NC];
+        part[g][c] = s;
+    }
+    // token t (a deferred slot, or the step's own): 16 threads share q.k_t
+    {
+        const int t = tid >> 4, i = tid & 15;
+        float d = 0.f;
+        if (t < ntok) {
+            for (int r = i; r < dk; r += 16) {
+                const float kv = t < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + t) * dk + r]
+                                           : to_f32(k[(int64_t)bh * dk + r]);
+                d += to_f32(q[(int64_t)bh * dk + r]) * kv;
+            }
         }
-        const float x = dot * rs;
-        float w = 0.f, term = 1.f;
-        for (int p = 0; p < P; ++p) {
-            w += term;
-            term = term * x / (float)(p + 1);
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off, 16);
+        if (t < ntok && i == 0) {
+            const float x = d * rsqrtf((float)dk);
+            float w = 0.f, term = 1.f;
+            for (int p = 0; p < P; ++p) {
+                w += term;
+                term = term * x / (float)(p + 1);
+            }
+            wt[t] = w;
         }
-        wt[tid] = w;
     }
     __syncthreads();
     if (tid < NC) {
         float s = 0.f;
-        for (int b = 0; b < nblk; ++b) s += partial[((int64_t)bh * nblk + b) * NC + tid];
+#pragma unroll
+        for (int g = 0; g < G; ++g) s += part[g][tid];
         for (int t = 0; t < ntok; ++t) {
             const float vt = tid == DV ? 1.f
                              : (t < npend ? pend_v[((int64_t)bh * kMaxDecodeWindow + t) * DV + tid]
@@ -457,7 +477,7 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
     {
         ProfScope ps(kProfDecodeFinish, stream);
         const int direct = mode == kDecodeRead ? 1 : 0;
-        hipLaunchKernelGGL((decode_finish_kernel<DV, TIn, TOut>), dim3((unsigned)bh), dim3(128), 0, stream, partial,
+        hipLaunchKernelGGL((decode_finish_kernel<DV, TIn, TOut>), dim3((unsigned)bh), dim3(kFinishThreads), 0, stream, partial,
                            nblk, static_cast<TOut *>(out), direct, idx->dk, idx->P, qi, ki, vi, st->d_pend_k,
                            st->d_pend_v, st->npend);
     }
