@@ -93,7 +93,7 @@ def prefill_flops(wl) -> float:
     return 4.0 * features(wl.d_k, wl.P) * (wl.d_v + 1) * wl.batch * wl.heads * wl.n
 
 
-DECODE_WINDOW = 16
+DECODE_WINDOW = 64
 
 
 def decode_read_bytes(wl, state_elem: int = 4) -> float:
@@ -359,10 +359,10 @@ TRAFFIC_KERNELS = [
     (r"prefill_scan_kernel<64, 64, 128, \d+, \d+, unsigned short>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
     (r"prefill_scan_ws_kernel<32, 32, 64, \d+>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
     (r"prefill_scan_ws_kernel<16, 16, 128, \d+>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
-    (r"decode_kernel<64, float, float, 1>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
-    (r"decode_kernel<64, float, unsigned short, 1>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_kernel<64, float, unsigned short>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
-    (r"decode_kernel<64, float, float, 16>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_fold_kernel<64, float, float>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
 
 
@@ -407,7 +407,7 @@ def traffic_run():
     st16.free()
     st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
     sata.sata_state_set_decode_window(st, 2)
-    time_decode(sata, idx, st, wl, 2, 0, wl.seed + 30)      # one read step, one fold
+    time_decode(sata, idx, st, wl, 2, 0, wl.seed + 30)      # one read step, one fold (of two tokens)
     log("traffic run: windowed decode done")
     st.free()
     idx.free()

@@ -36,12 +36,9 @@ constexpr int kDecThreads = 256;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Features per lane: one 16-byte word of every state row (4 fp32 or 8 bf16),
-// except for a bf16 fold of W > 1 tokens, whose lanes take 8-byte words (4
-// bf16) so that 4 features x W key monomials fit the register file.
-template <typename TS, int W> constexpr int dec_fpt() {
-    return (W > 1 && sizeof(TS) == 2) ? 4 : 16 / (int)sizeof(TS);
-}
+// Features per lane of the plain step and the read kernel: one 16-byte word of
+// every state row (4 fp32 or 8 bf16).
+template <typename TS> constexpr int dec_fpt() { return 16 / (int)sizeof(TS); }
 
 // A lane's word of one state row, and its conversion to FPT fp32 values and
 // back (bf16 rounds to nearest even).
@@ -146,117 +143,212 @@ __device__ __forceinline__ void store_partial(float (&acc)[DV + 1], float (&red)
     }
 }
 
-// State update by up to W tokens, then (if q is given) readout of the updated
-// state.  The tokens are the npend pending ones of the head (fp32 rows of the
-// pending buffers), followed by the step's own k, v if k is given.  W = 1 is
-// the plain decode step; larger W folds a window of deferred tokens in one
-// pass.
+// The plain decode step: update the state by the step's token, read out the
+// updated state.
 //
-// The lane's row loads are issued in NB batches, each batch before any store
-// of the previous one, so each lane keeps up to two batches of 16-byte loads
-// in flight (all d_V+1 rows for the plain step); one wavefront per SIMD then
-// saturates the HBM read-modify-write stream (the state is far larger than
-// every cache).  A bf16 fold holds 8 features x W key monomials per lane, so
-// it streams in four batches to stay within the register file.
-template <int DV, typename TIn, typename TS, int W>
+// The lane's row loads are issued in two batches, the second before any
+// store of the first, so each lane keeps up to d_V+1 16-byte loads in flight;
+// one wavefront per SIMD then saturates the HBM read-modify-write stream (the
+// state is far larger than every cache).
+template <int DV, typename TIn, typename TS>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
                    int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
-                   const TIn *__restrict__ v, const float *__restrict__ pend_k, const float *__restrict__ pend_v,
-                   int npend, float *__restrict__ partial) {
+                   const TIn *__restrict__ v, float *__restrict__ partial) {
     constexpr int NC = DV + 1;
-    constexpr int FPT = dec_fpt<TS, W>();
-    constexpr int NB = 2;                              // load batches
-    constexpr int RB = (NC + NB - 1) / NB;             // rows per batch
+    constexpr int FPT = dec_fpt<TS>();
+    constexpr int R = (NC + 1) / 2;                    // rows of the first load batch
     typedef Word<TS, FPT> Wd;
-    __shared__ float sq[72], sk[W][72];
-    __shared__ __align__(16) float sv[NC][W];      // token-minor: one row's W values are contiguous
+    __shared__ float sq[72], sk[72], sv[NC];
     __shared__ float red[kDecThreads / 64][NC];
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
     const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
-    const bool readout = W == 1 || q != nullptr;   // a plain step always reads out
     TS *Sb = state + (int64_t)bh * NC * m_pad + f0;
     auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
 
     // first batch of state rows goes out before anything else
     typename Wd::T s[NC];
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+    for (int r = 0; r < R; ++r)
         if (valid) s[r] = __builtin_nontemporal_load(row(r));
     uint32_t tt[FPT];
     float cc[FPT];
     lane_tables<FPT>(valid, tup, coef, f0, tt, cc);
+    // the token into LDS; only entries up to d_K + 1 are read (index d_K is the
+    // constant 1, d_K + 1 the padding 0)
+    if (tid <= dk + 1) {
+        sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+        sk[tid] = tid < dk ? to_f32(k[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    }
+    if (tid < NC) sv[tid] = tid < DV ? to_f32(v[(int64_t)bh * DV + tid]) : 1.f;
+    __syncthreads();
 
-    // tokens into LDS: slot t < npend from the pending buffers, slot npend the
-    // step's own token, the rest zero (they add nothing).  Only entries up to
-    // d_K + 1 are read (index d_K is the constant 1, d_K + 1 the padding 0).
-    if constexpr (W == 1) {
-        if (tid <= dk + 1) {
-            sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
-            sk[0][tid] = tid < dk ? to_f32(k[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    float phk[FPT], psq[FPT];
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) {
+        phk[j] = monomial(tt[j], sk, 1);
+        psq[j] = cc[j] * monomial(tt[j], sq, 1);
+    }
+
+    // second batch in flight while the first is updated, stored and read out
+#pragma unroll
+    for (int r = R; r < NC; ++r)
+        if (valid) s[r] = __builtin_nontemporal_load(row(r));
+    float acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        float x[FPT];
+        Wd::widen(s[c], x);
+        const float vc = sv[c];
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < FPT; ++j) {
+            x[j] += phk[j] * vc;
+            a += psq[j] * x[j];
         }
-        if (tid < NC) sv[tid][0] = tid < DV ? to_f32(v[(int64_t)bh * DV + tid]) : 1.f;
-    } else {
+        if (valid) __builtin_nontemporal_store(Wd::narrow(x), row(c));
+        acc[c] = valid ? a : 0.f;
+    }
+    store_partial<DV>(acc, red, partial, bh);
+}
+
+// Fold of a decode window on the matrix cores: the state update by the
+// window's tokens is the rank-T product S[c][f] += sum_t [v_t, 1][c] phi(k_t)[f],
+// a dense contraction over the tokens.  On v_mfma_f32_16x16x4f32 (A: features x
+// 4 tokens, B: 4 tokens x 16 columns) a lane's accumulator holds 4
+// consecutive features of one state row, i.e. one state word: the word is
+// loaded into the accumulator, ceil(T/4) MFMAs add the tokens, and it is
+// read out (if q is given) and stored back.  fp32 throughout (bf16 words are
+// widened and rounded to nearest even when stored), so the result matches
+// T plain steps up to rounding.  A wavefront owns 64 features (4 groups of
+// 16) of every row, in 5 column tiles of 16 (rows past d_V are masked); the
+// tokens are the npend deferred ones followed by the step's own if k is
+// given, staged in LDS with padding slots whose [v, 1] row is zero.  Four
+// wavefronts per SIMD (123 registers, 40 KB of LDS per workgroup) keep enough
+// state words in flight: a load covers 64 bytes of 16 rows, so HBM is served
+// best by many wavefronts at once.
+constexpr int kFoldThreads = 256;
+template <int DV, typename TIn, typename TS>
+__global__ __launch_bounds__(kFoldThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
+                        int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
+                        const TIn *__restrict__ v, const float *__restrict__ pend_k, const float *__restrict__ pend_v,
+                        int npend, float *__restrict__ partial) {
+    constexpr int NC = DV + 1;
+    constexpr int CT = (NC + 15) / 16;               // column tiles
+    constexpr int T = kMaxDecodeWindow;
+    typedef Word<TS, 4> Wd;
+    __shared__ float sq[72], sk[T][72];
+    __shared__ float sv[T][CT * 16];                 // [token][column], zero past d_V and for padding slots
+    __shared__ float red[kFoldThreads / 64][CT * 16];
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const bool readout = q != nullptr;
     const int ntok = npend + (k != nullptr ? 1 : 0);
-    for (int i = tid; i < W * 72; i += kDecThreads) {
+    const int kt = (ntok + 3) / 4;                   // token groups of 4
+    const int64_t fw = ((int64_t)blockIdx.x * (kFoldThreads / 64) + wave) * 64;   // the wavefront's first feature
+    const bool active = fw < m_pad;                  // m_pad is a multiple of 64
+    TS *Sb = state + (int64_t)bh * NC * m_pad;
+
+    // the wavefront's state words: feature group g, column tile ct -> row ct*16 + l16,
+    // features fw + 16 g + 4 lg .. + 3
+    f32x4 acc[4][CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int c = ct * 16 + l16;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            acc[g][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (active && c < NC) {
+                float x[4];
+                Wd::widen(*reinterpret_cast<const typename Wd::T *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg), x);
+                acc[g][ct] = f32x4{x[0], x[1], x[2], x[3]};
+            }
+        }
+    }
+    for (int i = tid; i < T * 72; i += kFoldThreads) {
         const int t = i / 72, c = i % 72;
         float x = 0.f;
-        if (t < ntok) {
-            if (c < dk)
-                x = t < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + t) * dk + c] : to_f32(k[(int64_t)bh * dk + c]);
-            else if (c == dk) x = 1.f;
-        }
+        if (t < ntok && c < dk)
+            x = t < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + t) * dk + c] : to_f32(k[(int64_t)bh * dk + c]);
+        else if (c == dk)
+            x = 1.f;
         sk[t][c] = x;
     }
-    for (int i = tid; i < W * NC; i += kDecThreads) {
-        const int t = i / NC, c = i % NC;
+    for (int i = tid; i < T * CT * 16; i += kFoldThreads) {
+        const int t = i / (CT * 16), c = i % (CT * 16);
         float x = 0.f;
         if (t < ntok) {
             if (c == DV) x = 1.f;
-            else x = t < npend ? pend_v[((int64_t)bh * kMaxDecodeWindow + t) * DV + c] : to_f32(v[(int64_t)bh * DV + c]);
+            else if (c < DV) x = t < npend ? pend_v[((int64_t)bh * kMaxDecodeWindow + t) * DV + c]
+                                           : to_f32(v[(int64_t)bh * DV + c]);
         }
-        sv[c][t] = x;
+        sv[t][c] = x;
     }
     if (readout && tid < 72) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
-    }
     __syncthreads();
 
-    float phk[W][FPT], psq[FPT];
+    if (active) {
+        // A operand: lane holds feature fw + 16 g + l16 of token 4 kk + lg
+        uint32_t ta[4];
 #pragma unroll
-    for (int j = 0; j < FPT; ++j) {
+        for (int g = 0; g < 4; ++g) ta[g] = tup[fw + 16 * g + l16];
+        for (int kk = 0; kk < kt; ++kk) {
+            float a[4];
 #pragma unroll
-        for (int t = 0; t < W; ++t) phk[t][j] = monomial(tt[j], sk[t], 1);
-        psq[j] = readout ? cc[j] * monomial(tt[j], sq, 1) : 0.f;
-    }
-
-    float acc[NC];
+            for (int g = 0; g < 4; ++g) a[g] = monomial(ta[g], sk[4 * kk + lg], 1);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        // next batch in flight while this one is updated, stored and read out
+            for (int ct = 0; ct < CT; ++ct) {
+                const float b = sv[4 * kk + lg][ct * 16 + l16];
 #pragma unroll
-        for (int r = (b + 1) * RB; r < (b + 2) * RB && r < NC; ++r)
-            if (valid) s[r] = __builtin_nontemporal_load(row(r));
-#pragma unroll
-        for (int c = b * RB; c < (b + 1) * RB && c < NC; ++c) {
-            float x[FPT];
-            Wd::widen(s[c], x);
-            float vc[W];
-#pragma unroll
-            for (int t = 0; t < W; ++t) vc[t] = sv[c][t];
-            float a = 0.f;
-#pragma unroll
-            for (int j = 0; j < FPT; ++j) {
-#pragma unroll
-                for (int t = 0; t < W; ++t) x[j] += phk[t][j] * vc[t];
-                a += psq[j] * x[j];
+                for (int g = 0; g < 4; ++g) acc[g][ct] = mfma_f32(a[g], b, acc[g][ct]);
             }
-            if (valid) __builtin_nontemporal_store(Wd::narrow(x), row(c));
-            acc[c] = valid ? a : 0.f;
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int c = ct * 16 + l16;
+            if (c < NC) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float x[4] = {acc[g][ct][0], acc[g][ct][1], acc[g][ct][2], acc[g][ct][3]};
+                    *reinterpret_cast<typename Wd::T *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg) = Wd::narrow(x);
+                }
+            }
         }
     }
-    if (readout) store_partial<DV>(acc, red, partial, bh);
+    if (!readout) return;
+    // readout of the updated words: lane's column ct*16 + l16, summed over its
+    // 16 features, then over the 4 lane groups, the wavefronts and (in the
+    // finish kernel) the workgroups
+    float psq[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t f = fw + 16 * g + 4 * lg + r;
+            psq[g][r] = active ? coef[f] * monomial(tup[f], sq, 1) : 0.f;
+        }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        float y = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y += psq[g][r] * acc[g][ct][r];
+        y += __shfl_xor(y, 16, 64);
+        y += __shfl_xor(y, 32, 64);
+        if (lg == 0) red[wave][ct * 16 + l16] = y;
+    }
+    __syncthreads();
+    if (tid < NC) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFoldThreads / 64; ++w) sum += red[w][tid];
+        partial[((int64_t)bh * gridDim.x + blockIdx.x) * NC + tid] = sum;
+    }
 }
 
 // Readout of the state as it stands, without an update: the non-folding steps
@@ -272,7 +364,7 @@ void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restric
                         float *__restrict__ partial) {
     constexpr int NC = DV + 1;
     constexpr int RA = (NC + 1) / 2;   // rows of the first half-tile
-    constexpr int FPT = dec_fpt<TS, 1>();
+    constexpr int FPT = dec_fpt<TS>();
     constexpr int TILE = kDecThreads * FPT;
     typedef Word<TS, FPT> Wd;
     typedef typename Wd::T WT;
@@ -368,7 +460,7 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(
     constexpr int NC = DV + 1;
     constexpr int G = 4;                        // partial-sum groups per column
     static_assert(G * NC <= kFinishThreads, "one thread per (group, column)");
-    static_assert(kMaxDecodeWindow * 16 <= kFinishThreads, "16 threads per token");
+    static_assert(kFinishThreads % 16 == 0, "16 threads per token");
     __shared__ float part[G][NC];
     __shared__ float y[NC];
     __shared__ float wt[kMaxDecodeWindow];
@@ -384,8 +476,8 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(
         part[g][c] = s;
     }
     // token t (a deferred slot, or the step's own): 16 threads share q.k_t
-    {
-        const int t = tid >> 4, i = tid & 15;
+    for (int t0 = 0; t0 < ntok; t0 += kFinishThreads / 16) {
+        const int t = t0 + (tid >> 4), i = tid & 15;
         float d = 0.f;
         if (t < ntok) {
             for (int r = i; r < dk; r += 16) {
@@ -431,9 +523,15 @@ static int64_t decode_blocks(const sata_index *idx, int fpt) {
     const int64_t per = (int64_t)kDecThreads * fpt;
     return (idx->m_pad + per - 1) / per;
 }
+static int64_t fold_blocks(const sata_index *idx) {
+    const int64_t per = kFoldThreads / 64 * 64;   // 64 features per wavefront
+    return (idx->m_pad + per - 1) / per;
+}
 
 int64_t decode_workspace_bytes(const sata_index *idx, int64_t bh) {
-    return bh * decode_blocks(idx, 4) * (idx->dv + 1) * (int64_t)sizeof(float);   // the larger (fp32) grid
+    // one partial row per workgroup; the fold has the most workgroups
+    const int64_t blocks = std::max(fold_blocks(idx), decode_blocks(idx, 4));
+    return bh * blocks * (idx->dv + 1) * (int64_t)sizeof(float);
 }
 
 template <int DV, typename TIn, typename TOut, typename TS>
@@ -441,9 +539,11 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
                                   const void *v, void *out, DecodeMode mode, hipStream_t stream) {
     const int64_t bh = (int64_t)st->batch * st->heads;
     const bool fold = mode == kDecodeFold || mode == kDecodeFlush;
-    const int fpt = fold ? dec_fpt<TS, kMaxDecodeWindow>() : dec_fpt<TS, 1>();
-    const int64_t tiles = decode_blocks(idx, fpt);
-    const dim3 grid((unsigned)(mode == kDecodeRead ? (tiles + kReadTiles - 1) / kReadTiles : tiles), (unsigned)bh);
+    // workgroups per head: the plain step one tile of 256 lanes x FPT features,
+    // the read kernel kReadTiles such tiles, the fold 64 features per wavefront
+    const int64_t tiles = decode_blocks(idx, dec_fpt<TS>());
+    const dim3 grid((unsigned)(fold ? fold_blocks(idx) : mode == kDecodeRead ? (tiles + kReadTiles - 1) / kReadTiles : tiles),
+                    (unsigned)bh);
     const int nblk = (int)grid.x;
     float *partial = static_cast<float *>(st->d_work);
     TS *S = static_cast<TS *>(st->d_state);
@@ -451,8 +551,8 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
     switch (mode) {
         case kDecodePlain: {
             ProfScope ps(kProfDecode, stream);
-            hipLaunchKernelGGL((decode_kernel<DV, TIn, TS, 1>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
-                               idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, nullptr, nullptr, 0, partial);
+            hipLaunchKernelGGL((decode_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
+                               idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
             break;
         }
         case kDecodeRead: {
@@ -465,10 +565,9 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
         case kDecodeFlush: {
             ProfScope ps(kProfDecodeFold, stream);
             const bool step = mode == kDecodeFold;
-            hipLaunchKernelGGL((decode_kernel<DV, TIn, TS, kMaxDecodeWindow>), grid, dim3(kDecThreads), 0, stream,
-                               idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, step ? qi : nullptr,
-                               step ? ki : nullptr, step ? vi : nullptr, st->d_pend_k, st->d_pend_v, st->npend,
-                               partial);
+            hipLaunchKernelGGL((decode_fold_kernel<DV, TIn, TS>), grid, dim3(kFoldThreads), 0, stream, idx->d_tup,
+                               idx->d_coef, S, idx->m_pad, idx->dk, step ? qi : nullptr, step ? ki : nullptr,
+                               step ? vi : nullptr, st->d_pend_k, st->d_pend_v, st->npend, partial);
             break;
         }
     }

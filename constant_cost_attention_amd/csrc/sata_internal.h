@@ -21,7 +21,7 @@
 #include "../../include/sata.h"
 
 // Largest decode window: deferred tokens held per head before a fold.
-constexpr int kMaxDecodeWindow = 16;
+constexpr int kMaxDecodeWindow = 64;
 
 struct sata_index {
     int dk = 0, dv = 0, P = 0;

@@ -222,7 +222,7 @@ def sata_state_convert(src: State, dst: State, stream=None):
 
 
 def sata_state_set_decode_window(state: State, window: int, stream=None):
-    """Decode steps per state update (1..16); deferred tokens are read out from their direct weights."""
+    """Decode steps per state update (1..64); deferred tokens are read out from their direct weights."""
     _check(load().sata_state_set_decode_window(state.ptr, int(window), _stream(stream)),
            "sata_state_set_decode_window")
 

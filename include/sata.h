@@ -127,21 +127,22 @@ sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, 
 sata_status sata_state_convert(sata_state *src, sata_state *dst, void *stream);
 
 /* Decode window: the number W of decode steps per update of the state buffer
- * (1 <= W <= 16, else SATA_ERR_INVALID; default 1).  With W > 1,
+ * (1 <= W <= 64, else SATA_ERR_INVALID; default 1).  With W > 1,
  * sata_decode_step defers the update: W - 1 steps in a row only read the
  * state out, adding each deferred token's (and the step's own) term from its
  * direct Taylor weight w(q.k_t / sqrt(d_K)) [v_t, 1] -- the single-token sum
  * that the state's orders hold for it [hotdry, "Core insight of symmetric
  * tensor decomposition"] -- and keep k and v of the step in a small per-head
  * buffer; every W-th step adds all of them to the state in one
- * read-modify-write pass and reads out from the result.  The outputs are the
+ * read-modify-write pass (a rank-W product on the matrix cores, fp32) and
+ * reads out from the result.  The outputs are the
  * same as with W = 1 up to rounding, and each step still costs a bounded
  * amount of work whatever the context length [hotdry, "Engineering
  * realisation of the constant compute cost"], while W - 1 of every W steps
  * stream the state once instead of twice.  Deferred tokens are folded in
  * before the window changes, before a prefill, before a conversion, and by
  * sata_state_flush; sata_state_reset discards them.  The first call with
- * W > 1 allocates the token buffers (hipMalloc, 16 slots per head). */
+ * W > 1 allocates the token buffers (hipMalloc, 64 slots per head). */
 sata_status sata_state_set_decode_window(sata_state *st, int window, void *stream);
 
 /* Fold the deferred decode tokens into the state buffer (no-op if none), so

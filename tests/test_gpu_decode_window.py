@@ -34,9 +34,9 @@ def _steps(idx, st, q, k, v, lo, hi, out_dtype=torch.float32):
     return torch.stack(outs, dim=2).float().cpu().numpy()
 
 
-@pytest.mark.parametrize("window", [2, 5, 16])
-def test_window_from_empty_every_row_and_flushed_state(sata, oracle, window):
-    d, P, n = 16, 4, 40
+@pytest.mark.parametrize("window,n", [(2, 40), (5, 40), (16, 40), (64, 150)])
+def test_window_from_empty_every_row_and_flushed_state(sata, oracle, window, n):
+    d, P = 16, 4
     x = si.draw_qkv((2, 2), n, d, d, 3100 + window, "f32")
     idx = sata.Index(d, d, P)
     q, k, v = dev_all(x)
@@ -116,7 +116,7 @@ def test_window_bf16_io(sata, oracle):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("d,n0,T,window", [(16, 256, 300, 16), (64, 128, 40, 16), (8, 64, 600, 4)])
+@pytest.mark.parametrize("d,n0,T,window", [(16, 256, 300, 16), (64, 128, 40, 16), (8, 64, 600, 4), (32, 100, 140, 64)])
 def test_window_on_bf16_state_matches_emulation(sata, oracle, d, n0, T, window):
     P, heads = 4, 2
     x = si.draw_qkv((1, heads), n0 + T, d, d, 3500 + d, "f32")
@@ -136,12 +136,12 @@ def test_window_on_bf16_state_matches_emulation(sata, oracle, d, n0, T, window):
     assert err <= TOL_BF16_STATE + DRIFT_SHARE * drift
 
 
-def test_window_workload_d64_after_8192(sata, oracle):
-    """32 x 8 heads after an fp32 prefill of 8192 tokens, W = 16, 20 steps
-    (one fold at the 16th): every head of every step against O1."""
+@pytest.mark.parametrize("window,steps", [(16, 20), (64, 70)])
+def test_window_workload_d64_after_8192(sata, oracle, window, steps):
+    """32 x 8 heads after an fp32 prefill of 8192 tokens, folds at every
+    window-th step: every head of every step against O1."""
     wl = si.WORKLOADS["decode_d64_p4_f32"]
-    steps = 20
-    say("decode window 16 workload %s (%d steps)" % (wl.name, steps))
+    say("decode window %d workload %s (%d steps)" % (window, wl.name, steps))
     pre = wl.draw()
     dec = wl.draw_decode(steps)
     idx = sata.Index(wl.d_k, wl.d_v, wl.P)
@@ -149,7 +149,7 @@ def test_window_workload_d64_after_8192(sata, oracle):
     q, k, v = dev_all(pre)
     prefill(idx, st, q, k, v)
     del q, k, v
-    sata.sata_state_set_decode_window(st, 16)
+    sata.sata_state_set_decode_window(st, window)
     dq, dk_, dv_ = dev_all(dec)
     o = _steps(idx, st, dq, dk_, dv_, 0, steps)
     qa = np.concatenate([pre.q, dec.q], axis=2)
@@ -164,7 +164,7 @@ def test_window_workload_d64_after_8192(sata, oracle):
 def test_window_error_paths(sata):
     idx = sata.Index(16, 16, 4)
     st = sata.State(idx, 1, 1)
-    for bad in (0, 17, -3):
+    for bad in (0, 65, -3):
         with pytest.raises(sata.SataError) as e:
             sata.sata_state_set_decode_window(st, bad)
         assert e.value.status == sata.SATA_ERR_INVALID
