@@ -56,6 +56,7 @@ def parse_args():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-flatness", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--traffic-run", action="store_true",
@@ -214,6 +215,42 @@ def time_decode(sata, idx, st, wl, steps: int, warmup: int, seed: int):
         if kn:
             kern[name] = (kms / kn, kn)
     return ms, kern
+
+
+def backward_flops(wl) -> float:
+    """Algorithmic FLOPs of the backward's prefill passes: two passes of P orders
+    (the forward recompute and dv) and 2 (d_V + 1) pseudo-head passes of P - 1
+    orders (dk, dq), each 4 m (d_V + 1) per head-token."""
+    m_p = features(wl.d_k, wl.P)
+    m_l = features(wl.d_k, wl.P - 1) if wl.P > 1 else 0
+    per = 2 * 4 * m_p * (wl.d_v + 1) + 2 * (wl.d_v + 1) * 4 * m_l * (wl.d_v + 1)
+    return float(per) * wl.batch * wl.heads * wl.n
+
+
+def time_backward(sata, wl, steps: int):
+    """Whole sata_prefill_backward calls (they synchronise) on seeded device inputs."""
+    import torch
+    import synth_inputs as si
+    q, k, v = si.draw_qkv_device((wl.batch, wl.heads), wl.n, wl.d_k, wl.d_v, wl.seed, wl.dtype)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 77)
+    dout = torch.randn(v.shape, generator=g, device="cuda", dtype=torch.float32).to(v.dtype)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    sata.sata_prefill_backward(idx, q, k, v, dout, *grads, chunk=wl.chunk)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sata.sata_prefill_backward(idx, q, k, v, dout, *grads, chunk=wl.chunk)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    idx.free()
+    del q, k, v, dout, grads
+    torch.cuda.empty_cache()
+    fl = backward_flops(wl)
+    return {"workload": wl.name, "ms_per_call": ms, "value": wl.batch * wl.n / (ms * 1e-3),
+            "unit": "tokens/s", "algorithmic_tflops": fl / (ms * 1e-3) / 1e12, "flops_per_call": fl,
+            "timing": "host clock around whole calls (each call synchronises its stream)"}
 
 
 def stream_ceiling(nbytes: float, reps: int = 10):
@@ -547,6 +584,15 @@ def main():
             del eq, ek, ev
             torch.cuda.empty_cache()
         result["extra"] = extra
+
+    if not args.no_backward:
+        bwd = []
+        for name in ("prefill_d64_p4_bf16", "prefill_d16_p4_f32"):
+            bw = time_backward(sata, si.WORKLOADS[name], 2)
+            log("backward %s: %.2f ms per call, %.3e tok/s, %.1f TFLOP/s algorithmic"
+                % (name, bw["ms_per_call"], bw["value"], bw["algorithmic_tflops"]))
+            bwd.append(bw)
+        result["backward"] = bwd
 
     if not args.no_cpu:
         log("cpu baseline: oracle on the host (budget %.0f s)" % args.cpu_budget)

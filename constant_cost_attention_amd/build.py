@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsata.so")
 ARCH = os.environ.get("SATA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["sata_host.cpp", "sata_decode.hip", "sata_prefill.hip", "sata_expand.hip"]
+SOURCES = ["sata_host.cpp", "sata_decode.hip", "sata_prefill.hip", "sata_expand.hip", "sata_backward.hip"]
 
 # Packed-fp32 VALU instructions are switched off for every device pass.
 HIPCC_FLAGS = [

@@ -528,6 +528,52 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     return SATA_OK;
 }
 
+sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, const void *q, const void *k,
+                                  const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n, int chunk,
+                                  sata_dtype in_dt, sata_dtype grad_dt, void *stream) {
+    g_last_error.clear();
+    if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
+    if (batch < 1 || heads < 1) return fail(SATA_ERR_INVALID, "batch and heads must be >= 1 (%d, %d)", batch, heads);
+    if (n < 0) return fail(SATA_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
+    if (!valid_dtype(in_dt) || !valid_dtype(grad_dt)) return fail(SATA_ERR_INVALID, "unknown dtype");
+    if (chunk != 0 && chunk != 64 && chunk != 128)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
+    if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "the backward pass needs d_k == d_v");
+    const int64_t bh = (int64_t)batch * heads;
+    if (bh > 65535) return fail(SATA_ERR_UNSUPPORTED, "batch*heads <= 65535 supported (got %lld)", (long long)bh);
+    if (n == 0) return SATA_OK;
+    const void *ins[4] = {q, k, v, dout};
+    void *outs[3] = {dq, dk, dv};
+    for (const void *p : ins)
+        if (!p || !aligned16(p)) return fail(SATA_ERR_INVALID, "q, k, v and dout must be non-NULL and 16-byte aligned");
+    for (void *p : outs)
+        if (!p || !aligned16(p)) return fail(SATA_ERR_INVALID, "dq, dk and dv must be non-NULL and 16-byte aligned");
+    const int64_t nin = bh * n * idx->dk * dtype_bytes(in_dt), nout = bh * n * idx->dk * dtype_bytes(grad_dt);
+    for (int a = 0; a < 3; ++a) {
+        for (const void *i : ins)
+            if (overlaps(outs[a], nout, i, nin)) return fail(SATA_ERR_INVALID, "gradients overlap the inputs");
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], nout, outs[b], nout)) return fail(SATA_ERR_INVALID, "gradients overlap each other");
+    }
+    DeviceGuard g(idx->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the index's device");
+    sata_index *lower = nullptr;
+    if (idx->P >= 2) {
+        sata_status s = sata_build_index(idx->dk, idx->dv, idx->P - 1, &lower);
+        if (s != SATA_OK) return s;
+    }
+    const int64_t kBudget = (int64_t)8 << 30;   // bytes of per-column temporaries per pass
+    hipError_t e = sata::launch_backward(idx, lower, bh, q, k, v, dout, dq, dk, dv, n, chunk, in_dt, grad_dt, kBudget,
+                                         (hipStream_t)stream);
+    if (lower) sata_index_free(lower);
+    if (e == hipErrorMemoryAllocation || e == hipErrorOutOfMemory) {
+        (void)hipGetLastError();
+        return fail(SATA_ERR_OOM, "backward temporaries could not be allocated");
+    }
+    if (e != hipSuccess) return fail_hip(e, "backward");
+    return SATA_OK;
+}
+
 sata_status sata_decode_step(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
                              void *out, sata_dtype in_dt, sata_dtype out_dt, void *stream) {
     g_last_error.clear();

@@ -104,8 +104,19 @@ struct PrefillPlan {
     int64_t sync_words = 0; // their count (a multiple of 4)
     int64_t work_bytes = 0; // workspace needed
     bool ok = false;
+    // output options for internal callers (the backward pass): write the
+    // unnormalised numerator y[:d_V] instead of y[:d_V] / y[d_V], and/or the
+    // normaliser y[d_V] of every token to den_out [B*H][n] (fp32)
+    bool raw = false;
+    float *den_out = nullptr;
 };
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt);
+// Backward pass of a causal prefill from a zero state (sata_backward.hip);
+// lower is the index with P - 1 orders (NULL when P == 1).  Synchronises the
+// stream before returning (it frees its temporaries).
+hipError_t launch_backward(const sata_index *idx, const sata_index *lower, int64_t bh, const void *q, const void *k,
+                           const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n, int chunk,
+                           sata_dtype in_dt, sata_dtype out_dt, int64_t mem_budget, hipStream_t s);
 hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                           const void *q, const void *k, const void *v, void *out, int64_t n,
                           sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream);

@@ -128,6 +128,7 @@ __device__ __forceinline__ float taylor_w(float x, float c0, float c1, float c2,
 struct TaylorArgs {
     float scale, c0, c1, c2, c3;
     int P;
+    int raw;          // write the numerator y[:d_V] unnormalised
 };
 
 // Direct intra-chunk term for query tile qt of chunk (t0, nvalid): Z (rows =
@@ -1413,7 +1414,8 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
 }
 
 // Kernel 2: y = (direct intra-chunk term) + sum over slices of the partials
-// (fixed order), o = y[:d_V] / y[d_V].  Partial layout per (bh, chunk, slice):
+// (fixed order), o = y[:d_V] / y[d_V] (or y[:d_V] itself when ta.raw; the
+// normaliser y[d_V] also goes to den_out when that is given).  Partial layout per (bh, chunk, slice):
 // [C/16][d_V+1][16 tokens] fp32.  Every thread first adds the slices' partials
 // with 16-byte loads; then wave w < C/32 adds the intra-chunk term of query
 // tiles w and C/16-1-w (tile qt needs qt+1 key tiles, so each wave does
@@ -1424,7 +1426,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename Part
                                                              int nchunk, int64_t n, int64_t tok0,
                                                              const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                              const TIn *__restrict__ v, TOut *__restrict__ out,
-                                                             TaylorArgs ta) {
+                                                             TaylorArgs ta, float *__restrict__ den_out) {
     constexpr int NC = DV + 1, TT = C / 16, NT = (NC + 15) / 16, NCP = 16 * NT;
     constexpr int VS = sizeof(TIn) == 2 ? C + 8 : C + 4;
     constexpr int NV = TT * NC * 4;                 // float4 per partial
@@ -1532,7 +1534,8 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename Part
             const int tt = t >> 4, t16 = t & 15;
             const float y = ys[(tt * NC + c) * 16 + t16];
             const float den = ys[(tt * NC + DV) * 16 + t16];
-            out[(bh * n + t0 + t) * DV + c] = from_f32<TOut>(y / den);
+            out[(bh * n + t0 + t) * DV + c] = from_f32<TOut>(ta.raw ? y : y / den);
+            if (den_out && c == 0) den_out[bh * n + t0 + t] = den;
         }
     }
 }
@@ -1620,6 +1623,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     ta.scale = 1.0f / sqrtf((float)D);
     ta.c0 = idx->taylor[0]; ta.c1 = idx->taylor[1]; ta.c2 = idx->taylor[2]; ta.c3 = idx->taylor[3];
     ta.P = idx->P;
+    ta.raw = plan.raw ? 1 : 0;
     const int64_t nchunks = (n + C - 1) / C;
     auto *partial = static_cast<typename PartialOf<TIn>::type *>(st->d_work);
     uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(st->d_work) + plan.sync_off);
@@ -1660,7 +1664,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
             ProfScope ps(kProfCombine, stream);
             hipLaunchKernelGGL(red, dim3(nseg, (unsigned)bh), dim3(256), 0, stream, partial, plan.slices, nseg,
                                n, tok0, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                               static_cast<const TIn *>(v), static_cast<TOut *>(out), ta);
+                               static_cast<const TIn *>(v), static_cast<TOut *>(out), ta, plan.den_out);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;

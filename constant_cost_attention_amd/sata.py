@@ -27,7 +27,7 @@ _EXPORTS = (
     "sata_state_alloc", "sata_state_alloc_dtype", "sata_state_convert", "sata_state_set_decode_window",
     "sata_state_flush", "sata_state_reset", "sata_state_free",
     "sata_state_data",
-    "sata_prefill", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
+    "sata_prefill", "sata_prefill_backward", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
 )
@@ -79,6 +79,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_state_data.argtypes = [vp, pvp, ctypes.POINTER(i64)]
     lib.sata_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, cint, cint, cint, vp]
     lib.sata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, cint, cint, vp]
+    lib.sata_prefill_backward.argtypes = [vp, cint, cint, vp, vp, vp, vp, vp, vp, vp, i64, cint, cint, cint, vp]
     lib.sata_expand_features.argtypes = [vp, vp, vp, i64, cint, cint, vp]
     lib.sata_describe_features.argtypes = [cint, cint, ctypes.POINTER(ctypes.c_uint32),
                                            ctypes.POINTER(ctypes.c_float), i64]
@@ -96,7 +97,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_profile_kernel_name.restype = ctypes.c_char_p
     for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_alloc_dtype",
                  "sata_state_convert", "sata_state_set_decode_window", "sata_state_flush", "sata_state_reset",
-                 "sata_state_data", "sata_prefill", "sata_decode_step", "sata_expand_features"):
+                 "sata_state_data", "sata_prefill", "sata_prefill_backward", "sata_decode_step", "sata_expand_features"):
         getattr(lib, name).restype = cint
     _lib = lib
     return lib
@@ -284,6 +285,28 @@ def sata_prefill(index: Index, state: State, q: torch.Tensor, k: torch.Tensor, v
                                _dev_ptr(out, "out"), int(n), int(chunk), _dtype(q), _dtype(out),
                                _stream(stream)), "sata_prefill")
     return out
+
+
+def sata_prefill_backward(index: Index, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                          dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, chunk: int = 0, stream=None):
+    """Gradients of a causal prefill from a zero state: q, k, v, dout, dq, dk, dv all [B, H, n, d]."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, n, d_K]")
+    B, H, n, dk_ = q.shape
+    if dk_ != index.d_k or index.d_k != index.d_v:
+        raise ValueError("q's last dim must be d_K (== d_V)")
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape:
+            raise ValueError("%s must have q's shape %s" % (name, tuple(q.shape)))
+    if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("q, k, v, dout must share a dtype")
+    if dk.dtype != dq.dtype or dv.dtype != dq.dtype:
+        raise ValueError("dq, dk, dv must share a dtype")
+    _check(load().sata_prefill_backward(index.ptr, int(B), int(H), _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                        _dev_ptr(dout, "dout"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"),
+                                        _dev_ptr(dv, "dv"), int(n), int(chunk), _dtype(q), _dtype(dq),
+                                        _stream(stream)), "sata_prefill_backward")
+    return dq, dk, dv
 
 
 def sata_decode_step(index: Index, state: State, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

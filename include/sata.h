@@ -177,6 +177,24 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
                          const void *v, void *out, int64_t n, int chunk, sata_dtype in_dt,
                          sata_dtype out_dt, void *stream);
 
+/* Gradients of a causal prefill of n tokens that starts from a zero state
+ * (a fresh sequence): given dout = dL/dout for out = the prefill's output on
+ * q, k, v, write dq, dk, dv = dL/dq, dL/dk, dL/dv.  Shapes and dtypes as for
+ * sata_prefill: q, k, v, dout [batch][heads][n][d_K] of in_dt; dq, dk, dv of
+ * grad_dt; d_K == d_V.  With g_i = [dout_i, -dout_i.out_i] / z_i (z_i the
+ * normaliser) and w' the series with P - 1 orders, every gradient is a
+ * causal or (on reversed time) anti-causal Taylor attention read out without
+ * normalisation, so the pass runs on the prefill's fixed-state kernels with
+ * a constant cost per token [hotdry, "Engineering realisation of the constant
+ * compute cost"]: a forward pass for out and z, a pass of P orders for dv, and
+ * passes of P - 1 orders over d_V + 1 pseudo-heads per head for dk and dq
+ * (none when P == 1: dq = dk = 0).  Allocates its temporaries (hipMalloc, up
+ * to a few GB) and synchronises `stream` before returning.  Gradients must
+ * not overlap the inputs or each other; n = 0 is a no-op. */
+sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, const void *q, const void *k,
+                                  const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n,
+                                  int chunk, sata_dtype in_dt, sata_dtype grad_dt, void *stream);
+
 /* One decode step for every head: with q, k: [batch][heads][d_K] and
  * v: [batch][heads][d_V] of the new token, add phi(k) (x) [v, 1] to every
  * order's state, then read out and normalise into out: [batch][heads][d_V]

@@ -26,6 +26,8 @@ Functions (what pins each one is listed in the tests and in the design notes):
 * ``recurrent_attention_f32`` O7, O5 carried out in float (diagnostic).
 * ``round_bf16``         O8a, round to nearest bfloat16, ties to even.
 * ``bf16_state_decode``  O8, decode steps on a state stored in bf16.
+* ``taylor_attention_grad`` O9, gradients of O1 (fp64 autograd of the
+  quadratic form, plain PyTorch CPU ops).
 * ``basis_size``, ``state_size``, ``flops_per_token`` O6, the closed forms the
   page prints, in exact integers.
 """
@@ -247,6 +249,39 @@ def bf16_state_decode(q, k, v, P: int, n0: int, rounding: bool = True, window: i
     if rc:
         raise ValueError("orc_bf16_state_decode rejected its arguments")
     return out.reshape(tuple(lead) + (n - n0, dv))
+
+
+def taylor_attention_grad(q, k, v, dout, P: int):
+    """O9: dL/dq, dL/dk, dL/dv for L = sum(dout * O1(q, k, v)), by fp64 reverse-mode
+    differentiation (torch autograd on CPU) of the quadratic definition
+    x = q k^T / sqrt(d_K), w = sum_{p<P} x^p/p! on j <= i, o = (w v) / sum_j w
+    [hotdry, "Core insight of symmetric tensor decomposition"].  One head at a
+    time (n x n weights); inputs [..., n, d] as float32 values."""
+    import torch
+    q = np.asarray(q, dtype=np.float32)
+    k = np.asarray(k, dtype=np.float32)
+    v = np.asarray(v, dtype=np.float32)
+    dout = np.asarray(dout, dtype=np.float32)
+    lead, bh, n, dk, dv = _heads(q, k, v)
+    outs = [np.empty((bh, n, dk)), np.empty((bh, n, dk)), np.empty((bh, n, dv))]
+    qf, kf, vf, df = (a.reshape(bh, n, -1) for a in (q, k, v, dout))
+    mask = torch.tril(torch.ones(n, n, dtype=torch.float64))
+    for h in range(bh):
+        Q = torch.tensor(qf[h], dtype=torch.float64, requires_grad=True)
+        K = torch.tensor(kf[h], dtype=torch.float64, requires_grad=True)
+        V = torch.tensor(vf[h], dtype=torch.float64, requires_grad=True)
+        x = (Q @ K.T) / math.sqrt(dk)
+        w = torch.zeros_like(x)
+        term = torch.ones_like(x)
+        for p in range(P):
+            w = w + term
+            term = term * x / (p + 1)
+        W = w * mask
+        o = (W @ V) / W.sum(dim=1, keepdim=True)
+        o.backward(torch.tensor(df[h], dtype=torch.float64))
+        for slot, t in enumerate((Q, K, V)):   # P = 1: o does not depend on q, k (no gradient)
+            outs[slot][h] = t.grad.numpy() if t.grad is not None else 0.0
+    return tuple(a.reshape(tuple(lead) + (n, -1)) for a in outs)
 
 
 # ---------------------------------------------------------------- closed forms (O6)

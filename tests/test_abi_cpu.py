@@ -63,6 +63,12 @@ def test_argument_checks_before_any_device_call(lib):
     assert lib.sata_state_alloc(None, 1, 1, None, ctypes.byref(out)) == sata.SATA_ERR_INVALID
     assert lib.sata_state_reset(None, None) == sata.SATA_ERR_INVALID
     assert lib.sata_expand_features(None, None, None, 1, 0, 0, None) == sata.SATA_ERR_INVALID
+    assert lib.sata_prefill_backward(None, 1, 1, None, None, None, None, None, None, None, 8, 0, 0, 0,
+                                     None) == sata.SATA_ERR_INVALID
+    assert lib.sata_state_alloc_dtype(None, 1, 1, 1, None, ctypes.byref(out)) == sata.SATA_ERR_INVALID
+    assert lib.sata_state_convert(None, None, None) == sata.SATA_ERR_INVALID
+    assert lib.sata_state_set_decode_window(None, 4, None) == sata.SATA_ERR_INVALID
+    assert lib.sata_state_flush(None, None) == sata.SATA_ERR_INVALID
     lib.sata_index_free(None)
     lib.sata_state_free(None)
 

@@ -379,3 +379,75 @@ def test_bf16_state_count_stalls_with_window(oracle, window):
     s = np.arange(n)
     den = np.minimum((s // window) * window, 256 * window) + s % window + 1
     assert np.array_equal(o, w[None, :].astype(np.float64) / den[:, None])
+
+
+# ------------------------------------------------------------ gradients (O9)
+
+def _dyadic(rng, shape, scale=64):
+    """Values k/scale with |k| <= scale: exact in fp32, and so are their sums with 2^-10."""
+    return (rng.integers(-scale, scale + 1, size=shape) / scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+def test_grad_matches_finite_differences(oracle, P):
+    """O9 against central differences of O1 (the C oracle) on dyadic inputs, so
+    that every perturbed value is exact in fp32: L = sum(dout * o)."""
+    rng = np.random.default_rng(40 + P)
+    n, d = 7, 3
+    q, k, v, dout = (_dyadic(rng, (1, n, d)) for _ in range(4))
+    gq, gk, gv = oracle.taylor_attention_grad(q, k, v, dout, P)
+    h = 2.0 ** -10
+    loss = lambda qq, kk, vv: float(np.sum(dout.astype(np.float64) * oracle.taylor_attention(qq, kk, vv, P)))
+    for which, grad in ((0, gq), (1, gk), (2, gv)):
+        for (i, c) in [(0, 0), (3, 1), (6, 2), (4, 0)]:
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][0, i, c] += h
+            up = loss(*args)
+            args[which][0, i, c] -= 2 * h
+            dn = loss(*args)
+            fd = (up - dn) / (2 * h)
+            assert abs(fd - grad[0, i, c]) <= 1e-5 * max(1.0, abs(fd)), (which, i, c, fd, grad[0, i, c])
+
+
+def test_grad_P1_closed_form(oracle):
+    """P = 1: o_i is the running mean of v, so dv_j = sum_{i>=j} dout_i / (i + 1)
+    and q, k get no gradient."""
+    rng = np.random.default_rng(3)
+    n, d = 20, 4
+    q, k, v, dout = (rng.standard_normal((2, n, d)).astype(np.float32) for _ in range(4))
+    gq, gk, gv = oracle.taylor_attention_grad(q, k, v, dout, 1)
+    w = dout.astype(np.float64) / np.arange(1, n + 1)[None, :, None]
+    ref = np.cumsum(w[:, ::-1], axis=1)[:, ::-1]
+    assert np.max(np.abs(gv - ref)) < 1e-12
+    assert np.max(np.abs(gq)) == 0 and np.max(np.abs(gk)) == 0
+
+
+@pytest.mark.parametrize("P", [2, 3, 4])
+def test_grad_state_form_identities(oracle, P):
+    """The identities the GPU backward is built on, written out from the
+    definitions: with g_i = [dout_i, -dout_i.o_i] / z_i and w' the series
+    with P - 1 orders, dv_j = sum_{i>=j} w_ij g_i[:d], dk_j = sum_{i>=j}
+    w'_ij ([v_j,1].g_i) q_i / sqrt d, dq_i = sum_{j<=i} w'_ij ([v_j,1].g_i)
+    k_j / sqrt d.  Checked against O9."""
+    rng = np.random.default_rng(50 + P)
+    n, d = 30, 5
+    q, k, v, dout = (rng.standard_normal((1, n, d)).astype(np.float32) for _ in range(4))
+    q, k = (a / np.linalg.norm(a, axis=-1, keepdims=True) * d ** 0.25 for a in (q, k))
+    q, k = q.astype(np.float32), k.astype(np.float32)
+    Q, K, V, G = (a[0].astype(np.float64) for a in (q, k, v, dout))
+    x = Q @ K.T / np.sqrt(d)
+    w = sum(x ** p / math.factorial(p) for p in range(P))
+    wd = sum(x ** p / math.factorial(p) for p in range(P - 1))
+    m = np.tril(np.ones((n, n)))
+    W, Wd = w * m, wd * m
+    z = W.sum(1)
+    o = W @ V / z[:, None]
+    g = np.concatenate([G, -(G * o).sum(1, keepdims=True)], axis=1) / z[:, None]
+    v1 = np.concatenate([V, np.ones((n, 1))], axis=1)
+    gv_ref = W.T @ g[:, :d]
+    s = g @ v1.T                      # s[i, j] = g_i . [v_j, 1]
+    gk_ref = (Wd * s).T @ Q / np.sqrt(d)
+    gq_ref = (Wd * s) @ K / np.sqrt(d)
+    gq, gk, gv = oracle.taylor_attention_grad(q, k, v, dout, P)
+    for a, b in ((gq[0], gq_ref), (gk[0], gk_ref), (gv[0], gv_ref)):
+        assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
