@@ -185,8 +185,9 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
 // applies d^(-p/2) by scaling q by 1/sqrt(d_K).  The pair product is shared by
 // the four slots of a quad and by all blocks of its group [hotdry, "Hardware
 // optimisation paths and current limits": the hierarchical index structure].
-// Order 0 is a position of its own (block d/4: the constant-1 slot).  Unused
-// streams are padding quads (pair product 0).  flags[pos]: bit 0 = some quad
+// Order 0 (the constant feature) has no quad: its state entries are running
+// sums of [v, 1], which the prefill keeps outside the scan.  Unused streams
+// are padding quads (pair product 0).  flags[pos]: bit 0 = some quad
 // of the position has slots with different weights (or invalid slots), bit 1 =
 // the position starts a new group of pairs.
 static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags) {
@@ -200,7 +201,7 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
         }
     }
     const int none = d, pad = d + 1;
-    auto make = [&](int i1, int i2, int b, bool order0, uint32_t &nonuni) {
+    auto make = [&](int i1, int i2, int b, uint32_t &nonuni) {
         sata::QuadRec q{};
         q.w0 = (uint32_t)pad | ((uint32_t)pad << 8) | ((uint32_t)b << 16);
         q.cidx = -1;
@@ -212,14 +213,9 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
         int first = -1;
         for (int z = 0; z < 4; ++z) {
             std::vector<int> t = prefix;
-            bool ok;
-            if (order0) {
-                ok = z == 0;
-            } else {
-                const int i3 = 4 * b + z;
-                ok = t.empty() || i3 >= t.back();
-                t.push_back(i3);
-            }
+            const int i3 = 4 * b + z;
+            const bool ok = t.empty() || i3 >= t.back();
+            t.push_back(i3);
             q.coef[z] = 0.f;
             if (!ok) continue;
             mask |= 1u << z;
@@ -247,17 +243,11 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
                 for (size_t s = 0; s < 4; ++s) {
                     const bool have = g + s < pairs.size();
                     out.push_back(make(have ? pairs[g + s].first : pad, have ? pairs[g + s].second : pad, b,
-                                       false, nonuni));
+                                       nonuni));
                 }
                 flags.push_back(nonuni | (b == a ? 2u : 0u));
             }
         }
-    }
-    {
-        uint32_t nonuni = 0;
-        out.push_back(make(none, none, d / 4, true, nonuni));
-        for (int s = 1; s < 4; ++s) out.push_back(make(pad, pad, d / 4, false, nonuni));
-        flags.push_back(nonuni | 2u);
     }
 }
 
@@ -329,7 +319,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     std::vector<uint32_t> qflags;
     build_quads(d_k, P, quads, qflags);
     idx->nq = (int64_t)quads.size();
-    idx->nq_tab = round_up(idx->nq, sata::kQuadPad);
+    idx->nq_tab = round_up(std::max<int64_t>(idx->nq, 1), sata::kQuadPad);   // never empty (P = 1 has no quads)
     {
         sata::QuadRec padq{};
         padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8);   // pair product 0

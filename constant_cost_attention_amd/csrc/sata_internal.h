@@ -102,6 +102,7 @@ struct PrefillPlan {
     int64_t seg_chunks = 0; // chunks per segment (bounded by the workspace cap)
     int64_t sync_off = 0;   // byte offset of the scan's counter and progress flags in the workspace
     int64_t sync_words = 0; // their count (a multiple of 4)
+    int64_t o0_off = 0;     // byte offset of the order-0 chunk sums and prefixes (2 x [B*H][chunks][d_V+1] fp32)
     int64_t work_bytes = 0; // workspace needed
     bool ok = false;
     // output options for internal callers (the backward pass): write the

@@ -1413,9 +1413,64 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
     }
 }
 
+// Order 0, the constant feature, is kept out of the scan: its state entries
+// S[c][0] are the running sums of [v, 1][c] over all tokens seen [hotdry,
+// "Engineering realisation of the constant compute cost": the "+1" column and
+// the constant Taylor term], so a chunk's inter-chunk readout from order 0 is
+// the sum of [v, 1] over every earlier token (weight 1/0! d^0 = 1).  First the
+// per-chunk sums (block (chunk, head); groups of d_V + 1 threads split the
+// tokens, then add in a fixed order), then per head the exclusive prefix over
+// the chunks starting from S[:, 0], which also leaves S[:, 0] covering the call.
+template <int DV, typename TIn>
+__global__ __launch_bounds__(256) void order0_sums_kernel(const TIn *__restrict__ v, int64_t n, int C,
+                                                          float *__restrict__ sums) {
+    constexpr int NC = DV + 1, G = 256 / NC;
+    __shared__ float part[G][NC];
+    const int64_t cc = blockIdx.x, bh = blockIdx.y, nchunks = gridDim.x;
+    const int64_t t0 = cc * C;
+    const int nv = (int)min<int64_t>(C, n - t0);
+    const int tid = threadIdx.x, g = tid / NC, c = tid % NC;
+    if (g < G) {
+        float s = 0.f;
+        if (c < DV) {
+            for (int t = g; t < nv; t += G) s += to_f32(v[(bh * n + t0 + t) * DV + c]);
+        } else if (g == 0) {
+            s = (float)nv;
+        }
+        part[g][c] = s;
+    }
+    __syncthreads();
+    if (tid < NC) {
+        float s = 0.f;
+        for (int gg = 0; gg < G; ++gg) s += part[gg][tid];
+        sums[(bh * nchunks + cc) * NC + tid] = s;
+    }
+}
+
+template <int DV>
+__global__ __launch_bounds__(128) void order0_prefix_kernel(const float *__restrict__ sums, float *__restrict__ prefix,
+                                                            int64_t nchunks, float *__restrict__ state, int64_t m_pad) {
+    constexpr int NC = DV + 1;
+    const int64_t bh = blockIdx.x;
+    const int c = threadIdx.x;
+    if (c >= NC) return;
+    float *s0 = state + (bh * NC + c) * m_pad;     // feature 0 of row c
+    float run = *s0;
+    const float *in = sums + bh * nchunks * NC + c;
+    float *out = prefix + bh * nchunks * NC + c;
+#pragma unroll 16
+    for (int64_t cc = 0; cc < nchunks; ++cc) {
+        const float x = in[cc * NC];
+        out[cc * NC] = run;
+        run += x;
+    }
+    *s0 = run;
+}
+
 // Kernel 2: y = (direct intra-chunk term) + sum over slices of the partials
-// (fixed order), o = y[:d_V] / y[d_V] (or y[:d_V] itself when ta.raw; the
-// normaliser y[d_V] also goes to den_out when that is given).  Partial layout per (bh, chunk, slice):
+// (fixed order) + the chunk's order-0 prefix, o = y[:d_V] / y[d_V] (or y[:d_V]
+// itself when ta.raw; the normaliser y[d_V] also goes to den_out when that is
+// given).  Partial layout per (bh, chunk, slice):
 // [C/16][d_V+1][16 tokens] fp32.  Every thread first adds the slices' partials
 // with 16-byte loads; then wave w < C/32 adds the intra-chunk term of query
 // tiles w and C/16-1-w (tile qt needs qt+1 key tiles, so each wave does
@@ -1426,7 +1481,8 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename Part
                                                              int nchunk, int64_t n, int64_t tok0,
                                                              const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                              const TIn *__restrict__ v, TOut *__restrict__ out,
-                                                             TaylorArgs ta, float *__restrict__ den_out) {
+                                                             TaylorArgs ta, float *__restrict__ den_out,
+                                                             const float *__restrict__ o0pre) {
     constexpr int NC = DV + 1, TT = C / 16, NT = (NC + 15) / 16, NCP = 16 * NT;
     constexpr int VS = sizeof(TIn) == 2 ? C + 8 : C + 4;
     constexpr int NV = TT * NC * 4;                 // float4 per partial
@@ -1528,12 +1584,13 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const typename Part
         }
     }
     __syncthreads();
+    const float *pre = o0pre + (bh * ((n + C - 1) / C) + t0 / C) * NC;   // this chunk's order-0 prefix
     for (int i = tid; i < C * DV; i += 256) {
         const int t = i / DV, c = i - t * DV;
         if (t < nvalid) {
             const int tt = t >> 4, t16 = t & 15;
-            const float y = ys[(tt * NC + c) * 16 + t16];
-            const float den = ys[(tt * NC + DV) * 16 + t16];
+            const float y = ys[(tt * NC + c) * 16 + t16] + pre[c];
+            const float den = ys[(tt * NC + DV) * 16 + t16] + pre[DV];
             out[(bh * n + t0 + t) * DV + c] = from_f32<TOut>(ta.raw ? y : y / den);
             if (den_out && c == 0) den_out[bh * n + t0 + t] = den;
         }
@@ -1584,11 +1641,13 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
     const int64_t pbytes = in_dt == SATA_BF16 ? 2 : 4;   // readout partials in the input's width
     const int64_t per_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * pbytes;
-    p.seg_chunks = std::max<int64_t>(1, std::min<int64_t>(nchunks, kWorkCap / per_chunk));
-    // after the partial sums: the scan's work counter and one progress flag per (head, slice)
+    p.seg_chunks = per_chunk ? std::max<int64_t>(1, std::min<int64_t>(nchunks, kWorkCap / per_chunk)) : nchunks;
+    // after the partial sums: the scan's work counter and one progress flag per (head, slice),
+    // then the order-0 chunk sums and their prefixes for the whole call
     p.sync_off = (p.seg_chunks * per_chunk + 255) / 256 * 256;
     p.sync_words = (1 + bh * p.slices + 3) / 4 * 4;
-    p.work_bytes = p.sync_off + p.sync_words * 4;
+    p.o0_off = (p.sync_off + p.sync_words * 4 + 255) / 256 * 256;
+    p.work_bytes = p.o0_off + 2 * bh * std::max<int64_t>(nchunks, 1) * (idx->dv + 1) * (int64_t)sizeof(float);
     p.ok = (int64_t)p.slices * np_slice * 4 <= idx->nq_tab;
     return p;
 }
@@ -1635,6 +1694,15 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     if (e != hipSuccess) return e;
     const int64_t resident = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     const int64_t items0 = bh * plan.slices;
+    // order 0: chunk sums of [v, 1], their prefixes from the state's entries, and those entries' update
+    float *o0sums = reinterpret_cast<float *>(static_cast<char *>(st->d_work) + plan.o0_off);
+    float *o0pre = o0sums + bh * nchunks * (D + 1);
+    hipLaunchKernelGGL((order0_sums_kernel<D, TIn>), dim3((unsigned)nchunks, (unsigned)bh), dim3(256), 0, stream,
+                       static_cast<const TIn *>(v), n, C, o0sums);
+    hipLaunchKernelGGL((order0_prefix_kernel<D>), dim3((unsigned)bh), dim3(128), 0, stream, o0sums, o0pre, nchunks,
+                       static_cast<float *>(st->d_state), idx->m_pad);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     for (int64_t c0 = 0; c0 < nchunks; c0 += plan.seg_chunks) {
         const int nseg = (int)std::min<int64_t>(plan.seg_chunks, nchunks - c0);
         const int64_t tok0 = c0 * C;
@@ -1646,11 +1714,11 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
         const int sub_chunks = (nseg + nsub - 1) / nsub;
         nsub = (nseg + sub_chunks - 1) / sub_chunks;
         const int64_t grid = Cfg::PERSIST ? std::min<int64_t>(items0 * nsub, resident) : items0;
-        if (Cfg::PERSIST) {
+        if (Cfg::PERSIST && items0 > 0) {
             e = launch_zero(reinterpret_cast<float *>(sync), plan.sync_words, stream);
             if (e != hipSuccess) return e;
         }
-        {
+        if (items0 > 0) {   // P = 1: order 0 alone, no scan
             ProfScope ps(kProfScan, stream);
             hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(Cfg::THREADS), Cfg::LDS, stream,
                                idx->d_qw0, idx->d_qcidx, reinterpret_cast<const float4 *>(idx->d_qcoef),
@@ -1664,7 +1732,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
             ProfScope ps(kProfCombine, stream);
             hipLaunchKernelGGL(red, dim3(nseg, (unsigned)bh), dim3(256), 0, stream, partial, plan.slices, nseg,
                                n, tok0, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                               static_cast<const TIn *>(v), static_cast<TOut *>(out), ta, plan.den_out);
+                               static_cast<const TIn *>(v), static_cast<TOut *>(out), ta, plan.den_out, o0pre);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -117,8 +117,10 @@ def test_binding_rejects_cpu_tensors():
 def test_quads_cover_every_feature_once(d, P):
     """Every valid quad slot is the feature (i1, i2, 4b+z) at state index
     cidx + (z - first valid slot), with the feature table's readout weight;
-    together the valid slots cover every feature exactly once; padding slots
-    carry weight 0; the four quads of a position share the block b."""
+    together the valid slots cover every feature exactly once except feature
+    0, the constant order 0, which the prefill keeps out of the quads (P = 1
+    has no quads at all); padding slots carry weight 0; the four quads of a
+    position share the block b."""
     from constant_cost_attention_amd import sata
     tup, coef = sata.sata_describe_features(d, P)
     w0, cidx, qc = sata.sata_describe_quads(d, P)
@@ -140,12 +142,12 @@ def test_quads_cover_every_feature_once(d, P):
                 continue
             f = int(cidx[q]) + z - z0
             idx = [i for i in (i1, i2) if i < d]
-            if b * 4 < d:
-                idx.append(4 * b + z)
+            idx.append(4 * b + z)
             want = sorted(idx)
             assert idx == want
             assert [int(x) for x in slots[f, :order[f]]] == want, (q, z, want)
             # quad weight = multinomial part; the feature weight also carries d^(-p/2)
             assert abs(qc[q, z] / math.sqrt(d) ** len(want) - coef[f]) <= 1e-6 * coef[f]
             seen[f] += 1
-    assert np.all(seen == 1)
+    assert seen[0] == 0 and order[0] == 0
+    assert np.all(seen[1:] == 1)
