@@ -356,7 +356,81 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
         res["flatness"] = {"per_prefix": flat,
                            "max_rel_dev": max(abs(f["ms_per_step"] / base - 1) for f in flat.values())}
     idx.free()
+    res["single_sequence"] = [decode_graph(sata, wl, d) for d in (wl.d_k, 16)]
     return res
+
+
+def decode_graph(sata, wl, d: int, prefix: int = 8192, graph_steps: int = 64, reps: int = 16):
+    """Small-batch decode: one sequence of the workload's heads (head size d)
+    after a prefix, where the grid is small (the row-split kernels run) and,
+    at small d, the host's launches set the pace.  The same steps are timed
+    issued one call at a time and replayed from a HIP graph that holds
+    graph_steps consecutive steps (captured once; before each replay the
+    next graph_steps tokens are copied into the buffers the graph reads, and
+    that copy is inside the timed region)."""
+    import dataclasses
+    import torch
+    import synth_inputs as si
+    one = dataclasses.replace(wl, batch=1, d_k=d, d_v=d)
+    wl = one
+    idx = sata.Index(d, d, wl.P)
+    total = graph_steps * (reps + 2)
+    q, k, v = si.draw_qkv_device((1, wl.heads), total, wl.d_k, wl.d_v, wl.seed + 500, "f32")
+    q, k, v = (t.permute(2, 0, 1, 3).contiguous() for t in (q, k, v))     # [steps, 1, H, d]
+    out = torch.empty((total, 1, wl.heads, wl.d_v), dtype=torch.float32, device="cuda")
+
+    def eager(lo, hi):
+        for t in range(lo, hi):
+            sata.sata_decode_step(idx, st, q[t], k[t], v[t], out[t])
+
+    st = build_state(sata, idx, one, prefix, "f32", wl.seed + 400)
+    eager(0, graph_steps)                              # warm-up (first step allocates the workspace)
+    torch.cuda.synchronize()
+    lo, hi = graph_steps, graph_steps * (reps + 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    eager(lo, hi)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / (hi - lo)
+    sata.sata_profile_enable(True)
+    eager(0, graph_steps)
+    torch.cuda.synchronize()
+    sata.sata_profile_enable(False)
+    kms, kn = sata.sata_profile_query("decode_stream")
+    stream_ms = kms / max(kn, 1)
+    st.free()
+
+    st = build_state(sata, idx, one, prefix, "f32", wl.seed + 400)
+    eager(0, graph_steps)
+    sq, sk, sv = (torch.empty((graph_steps,) + t.shape[1:], device="cuda") for t in (q, k, v))
+    so = torch.empty((graph_steps,) + out.shape[1:], device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for g in range(graph_steps):
+            sata.sata_decode_step(idx, st, sq[g], sk[g], sv[g], so[g])
+    torch.cuda.synchronize()
+    e0.record()
+    for r in range(reps):
+        a = graph_steps * (r + 1)
+        sq.copy_(q[a:a + graph_steps]); sk.copy_(k[a:a + graph_steps]); sv.copy_(v[a:a + graph_steps])
+        graph.replay()
+        out[a:a + graph_steps].copy_(so)
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / (graph_steps * reps)
+    st.free()
+    idx.free()
+    del graph, q, k, v, out, sq, sk, sv, so
+    torch.cuda.empty_cache()
+    nbytes = decode_bytes(wl)
+    return {"workload": "1 x %d heads, d=%d, P=%d, after %d tokens" % (wl.heads, d, wl.P, prefix),
+            "graph_steps": graph_steps, "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+            "speedup": eager_ms / graph_ms, "stream_kernel_ms": stream_ms,
+            "stream_kernel_gbs": nbytes / (stream_ms * 1e-3) / 1e9, "bytes_per_step": nbytes,
+            "timing": "events on torch's stream; graph time includes the token copies in and out; "
+                      "the stream kernel's time from the library's per-launch events"}
 
 
 # ------------------------------------------------------------------ oracle on the host
@@ -569,6 +643,11 @@ def main():
             % (dw["window"], dw["ms_per_step"], dw["value"], dw["roofline"]["avg_launch_ms"],
                dw["roofline"]["achieved"], 100 * dw["roofline"]["frac"], dw["fold"]["avg_launch_ms"],
                dw["fold"]["achieved_gbs"]))
+        for gr in dec["single_sequence"]:
+            log("decode, %s: %.1f us/step issued call by call, %.1f us/step replayed from a graph of %d steps; "
+                "stream kernel %.1f us at %.0f GB/s"
+                % (gr["workload"], 1e3 * gr["eager_ms_per_step"], 1e3 * gr["graph_ms_per_step"], gr["graph_steps"],
+                   1e3 * gr["stream_kernel_ms"], gr["stream_kernel_gbs"]))
         result["decode"] = dec
         torch.cuda.empty_cache()
 

@@ -214,6 +214,93 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
     store_partial<DV>(acc, red, partial, bh);
 }
 
+// Small-batch variant of the plain step (UPDATE) and of the read kernel: the
+// d_V + 1 rows of a feature tile are split over workgroups, rows_per_group()
+// each (at most 16).  With few heads the whole-tile kernels leave a grid of a
+// few hundred long workgroups, at one per compute unit, in which each
+// workgroup's two load batches wait on each other and the last round runs
+// on part of the chip.  Here every workgroup issues all its rows at once
+// (one round trip), holds a fraction of the registers (several workgroups
+// per compute unit) and the grid is d_V + 1 / rows_per_group() times
+// finer.  A lane past the last feature re-reads the last word (in bounds,
+// weight 0) and stores nothing.  The key-side monomials and tables are
+// recomputed per group (cheap, and the tables stay in L2).  Each workgroup
+// writes the partial sums of its own rows of its tile's partial row.
+template <int DV> constexpr int rows_per_group() {
+    constexpr int NC = DV + 1;
+    constexpr int groups = (NC + 15) / 16;
+    return (NC + groups - 1) / groups;
+}
+template <int DV, typename TIn, typename TS, bool UPDATE>
+__global__ __launch_bounds__(kDecThreads)
+void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
+                        int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
+                        const TIn *__restrict__ v, float *__restrict__ partial) {
+    constexpr int NC = DV + 1;
+    constexpr int NR = rows_per_group<DV>();
+    constexpr int FPT = dec_fpt<TS>();
+    typedef Word<TS, FPT> Wd;
+    __shared__ float sq[72], sk[72], sv[NR];
+    __shared__ float red[kDecThreads / 64][16];
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int r0 = blockIdx.z * NR;
+    const int nr = min(NR, NC - r0);                 // rows of this group (uniform)
+    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
+    const bool valid = f0 < m_pad;                   // m_pad is a multiple of 64
+    TS *Sb = state + ((int64_t)bh * NC + r0) * m_pad + min<int64_t>(f0, m_pad - FPT);
+    auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
+
+    typename Wd::T s[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+        if (r < nr) s[r] = __builtin_nontemporal_load(row(r));
+    uint32_t tt[FPT];
+    float cc[FPT];
+    lane_tables<FPT>(true, tup, coef, min<int64_t>(f0, m_pad - FPT), tt, cc);
+    if (tid <= dk + 1) {
+        sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+        if (UPDATE) sk[tid] = tid < dk ? to_f32(k[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    }
+    if (UPDATE && tid < nr) sv[tid] = r0 + tid < DV ? to_f32(v[(int64_t)bh * DV + r0 + tid]) : 1.f;
+    __syncthreads();
+
+    float phk[FPT], psq[FPT];
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) {
+        if (UPDATE) phk[j] = monomial(tt[j], sk, 1);
+        psq[j] = valid ? cc[j] * monomial(tt[j], sq, 1) : 0.f;
+    }
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        if (r < nr) {
+            float x[FPT];
+            Wd::widen(s[r], x);
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < FPT; ++j) {
+                if (UPDATE) x[j] += phk[j] * sv[r];
+                a += psq[j] * x[j];
+            }
+            if (UPDATE && valid) __builtin_nontemporal_store(Wd::narrow(x), row(r));
+            acc[r] = a;
+        }
+    }
+    const float col = wave_reduce_scatter<16>(acc);
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane < 16) red[wave][lane] = col;
+    __syncthreads();
+    if (tid < nr) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecThreads / 64; ++w) sum += red[w][tid];
+        partial[((int64_t)bh * gridDim.x + blockIdx.x) * NC + r0 + tid] = sum;
+    }
+}
+
 // Fold of a decode window on the matrix cores: the state update by the
 // window's tokens is the rank-T product S[c][f] += sum_t [v_t, 1][c] phi(k_t)[f],
 // a dense contraction over the tokens.  On v_mfma_f32_16x16x4f32 (A: features x
@@ -352,16 +439,17 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
 }
 
 // Readout of the state as it stands, without an update: the non-folding steps
-// of a deferred decode.  A pure read stream, so a workgroup walks TPW
+// of a deferred decode.  A pure read stream, so a workgroup walks tpw
 // consecutive feature tiles (256 * FPT features each) of its head and keeps
 // the next half-tile's rows in flight while it reads out the current half;
-// the readout sums accumulate across the tiles and are reduced once.
+// the readout sums accumulate across the tiles and are reduced once.  tpw is
+// at most kReadTiles, fewer when the batch is small (read_tiles_per_block).
 constexpr int kReadTiles = 8;
 template <int DV, typename TIn, typename TS>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef,
                         const TS *__restrict__ state, int64_t m_pad, int dk, const TIn *__restrict__ q,
-                        float *__restrict__ partial) {
+                        float *__restrict__ partial, int tpw) {
     constexpr int NC = DV + 1;
     constexpr int RA = (NC + 1) / 2;   // rows of the first half-tile
     constexpr int FPT = dec_fpt<TS>();
@@ -373,8 +461,8 @@ void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restric
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int64_t tiles = (m_pad + TILE - 1) / TILE;
-    const int64_t first = (int64_t)blockIdx.x * kReadTiles;
-    const int tn = (int)min<int64_t>(kReadTiles, tiles - first);
+    const int64_t first = (int64_t)blockIdx.x * tpw;
+    const int tn = (int)min<int64_t>(tpw, tiles - first);
     const TS *Sb = state + (int64_t)bh * NC * m_pad;
     // A lane past the last feature re-reads the last word (in bounds, weight 0),
     // so every load is unconditional.
@@ -523,6 +611,18 @@ static int64_t decode_blocks(const sata_index *idx, int fpt) {
     const int64_t per = (int64_t)kDecThreads * fpt;
     return (idx->m_pad + per - 1) / per;
 }
+// Tiles per workgroup of the read kernel: kReadTiles while the grid still has
+// about four workgroups per compute unit (256 of them), fewer for small
+// batches, down to one tile per workgroup.
+static int read_tiles_per_block(int64_t bh, int64_t tiles) {
+    return (int)std::max<int64_t>(1, std::min<int64_t>(kReadTiles, bh * tiles / 1024));
+}
+// Whether the plain step and the read kernel split each tile's rows over
+// workgroups: when the whole-tile grid would hold fewer than 24 workgroups per
+// compute unit (256 of them).  Measured at d = 64, fp32 state: the split grid
+// is ahead up to 128 heads (by 30% at 8 heads, 1 to 3% at 128), the
+// whole-tile kernels from 256 heads (by 2 to 4%).
+static bool split_rows(int64_t bh, int64_t tiles) { return bh * tiles < 24 * 256; }
 static int64_t fold_blocks(const sata_index *idx) {
     const int64_t per = kFoldThreads / 64 * 64;   // 64 features per wavefront
     return (idx->m_pad + per - 1) / per;
@@ -540,10 +640,13 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
     const int64_t bh = (int64_t)st->batch * st->heads;
     const bool fold = mode == kDecodeFold || mode == kDecodeFlush;
     // workgroups per head: the plain step one tile of 256 lanes x FPT features,
-    // the read kernel kReadTiles such tiles, the fold 64 features per wavefront
+    // the read kernel tpw such tiles, the fold 64 features per wavefront
     const int64_t tiles = decode_blocks(idx, dec_fpt<TS>());
-    const dim3 grid((unsigned)(fold ? fold_blocks(idx) : mode == kDecodeRead ? (tiles + kReadTiles - 1) / kReadTiles : tiles),
-                    (unsigned)bh);
+    const int tpw = read_tiles_per_block(bh, tiles);
+    constexpr int NR = rows_per_group<DV>();
+    const int groups = split_rows(bh, tiles) ? (DV + 1 + NR - 1) / NR : 1;
+    const dim3 grid((unsigned)(fold ? fold_blocks(idx) : mode == kDecodeRead && groups == 1 ? (tiles + tpw - 1) / tpw : tiles),
+                    (unsigned)bh, (unsigned)(fold ? 1 : groups));
     const int nblk = (int)grid.x;
     float *partial = static_cast<float *>(st->d_work);
     TS *S = static_cast<TS *>(st->d_state);
@@ -551,14 +654,22 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
     switch (mode) {
         case kDecodePlain: {
             ProfScope ps(kProfDecode, stream);
-            hipLaunchKernelGGL((decode_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
-                               idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
+            if (groups > 1)
+                hipLaunchKernelGGL((decode_rows_kernel<DV, TIn, TS, true>), grid, dim3(kDecThreads), 0, stream,
+                                   idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
+            else
+                hipLaunchKernelGGL((decode_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
+                                   idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
             break;
         }
         case kDecodeRead: {
             ProfScope ps(kProfDecodeRead, stream);
-            hipLaunchKernelGGL((decode_read_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
-                               idx->d_coef, S, idx->m_pad, idx->dk, qi, partial);
+            if (groups > 1)
+                hipLaunchKernelGGL((decode_rows_kernel<DV, TIn, TS, false>), grid, dim3(kDecThreads), 0, stream,
+                                   idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, nullptr, nullptr, partial);
+            else
+                hipLaunchKernelGGL((decode_read_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
+                                   idx->d_coef, S, idx->m_pad, idx->dk, qi, partial, tpw);
             break;
         }
         case kDecodeFold:
