@@ -433,6 +433,33 @@ def decode_graph(sata, wl, d: int, prefix: int = 8192, graph_steps: int = 64, re
                       "the stream kernel's time from the library's per-launch events"}
 
 
+def order5_section(sata, steps: int):
+    """Five orders at d = 64 (814,385 features, 212 MB of fp32 state per head):
+    the prefill of prefill_d64_p5_bf16, then plain decode steps on an fp32
+    state filled by a prefill of the same length."""
+    import torch
+    import synth_inputs as si
+    wl = si.WORKLOADS["prefill_d64_p5_bf16"]
+    q, k, v = si.draw_qkv_device((wl.batch, wl.heads), wl.n, wl.d_k, wl.d_v, wl.seed, wl.dtype)
+    pre = time_prefill(sata, wl, q, k, v, max(3, steps // 2), 1)
+    del q, k, v
+    torch.cuda.empty_cache()
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    st = build_state(sata, idx, wl, wl.n, "bf16", wl.seed + 1)
+    ms, kern = time_decode(sata, idx, st, wl, 64, 4, wl.seed + 2)
+    st.free()
+    idx.free()
+    torch.cuda.empty_cache()
+    nbytes = decode_bytes(wl)
+    kms = kern["decode_stream"][0]
+    ach = nbytes / (kms * 1e-3) / 1e9
+    return {"prefill": pre,
+            "decode": {"workload": "%d x %d heads, d=%d, P=%d, after %d tokens" % (wl.batch, wl.heads, wl.d_k, wl.P, wl.n),
+                       "value": wl.batch / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+                       "stream_kernel_ms": kms, "bytes_per_step": nbytes, "achieved_gbs": ach,
+                       "frac": ach / PEAK_HBM_GBS}}
+
+
 # ------------------------------------------------------------------ oracle on the host
 
 def cpu_baseline(wl, x, budget_s: float):
@@ -467,13 +494,13 @@ def cpu_baseline(wl, x, budget_s: float):
 COPY_BYTES = 1 << 30
 # kernel-name pattern -> (kernel, workload, source file)
 TRAFFIC_KERNELS = [
-    (r"prefill_scan_kernel<64, 64, 128, \d+, \d+, unsigned short>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
-    (r"prefill_scan_ws_kernel<32, 32, 64, \d+>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
-    (r"prefill_scan_ws_kernel<16, 16, 128, \d+>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
+    (r"prefill_scan_kernel<64, 64, 128, \d+, \d+, unsigned short, false>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
+    (r"prefill_scan_ws_kernel<32, 32, 64, \d+, false>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
+    (r"prefill_scan_ws_kernel<16, 16, 128, \d+, false>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
     (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_kernel<64, float, unsigned short>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
-    (r"decode_fold_kernel<64, float, float>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_fold_kernel<64, float, float, 3>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
 
 
@@ -663,6 +690,12 @@ def main():
             del eq, ek, ev
             torch.cuda.empty_cache()
         result["extra"] = extra
+        o5 = order5_section(sata, args.steps)
+        log("order 5, %s: %.3f ms/step, %.3e tok/s, %.1f%% of peak; decode %s: %.3f ms/step, stream %.0f GB/s "
+            "(%.1f%% of peak)" % (o5["prefill"]["workload"], o5["prefill"]["ms_per_step"], o5["prefill"]["value"],
+                                  100 * o5["prefill"]["roofline"]["frac"], o5["decode"]["workload"],
+                                  o5["decode"]["ms_per_step"], o5["decode"]["achieved_gbs"], 100 * o5["decode"]["frac"]))
+        result["order5"] = o5
 
     if not args.no_backward:
         bwd = []

@@ -316,8 +316,9 @@ void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restric
 // wavefronts per SIMD (123 registers, 40 KB of LDS per workgroup) keep enough
 // state words in flight: a load covers 64 bytes of 16 rows, so HBM is served
 // best by many wavefronts at once.
+// NF: index slots the monomials multiply (3 up to P = 4, 4 for P = 5).
 constexpr int kFoldThreads = 256;
-template <int DV, typename TIn, typename TS>
+template <int DV, typename TIn, typename TS, int NF>
 __global__ __launch_bounds__(kFoldThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
                         int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
@@ -386,7 +387,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
         for (int kk = 0; kk < kt; ++kk) {
             float a[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) a[g] = monomial(ta[g], sk[4 * kk + lg], 1);
+            for (int g = 0; g < 4; ++g) a[g] = monomial_n<NF>(ta[g], sk[4 * kk + lg], 1);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 const float b = sv[4 * kk + lg][ct * 16 + l16];
@@ -416,7 +417,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t f = fw + 16 * g + 4 * lg + r;
-            psq[g][r] = active ? coef[f] * monomial(tup[f], sq, 1) : 0.f;
+            psq[g][r] = active ? coef[f] * monomial_n<NF>(tup[f], sq, 1) : 0.f;
         }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -676,9 +677,10 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
         case kDecodeFlush: {
             ProfScope ps(kProfDecodeFold, stream);
             const bool step = mode == kDecodeFold;
-            hipLaunchKernelGGL((decode_fold_kernel<DV, TIn, TS>), grid, dim3(kFoldThreads), 0, stream, idx->d_tup,
-                               idx->d_coef, S, idx->m_pad, idx->dk, step ? qi : nullptr, step ? ki : nullptr,
-                               step ? vi : nullptr, st->d_pend_k, st->d_pend_v, st->npend, partial);
+            auto fold = idx->P >= 5 ? decode_fold_kernel<DV, TIn, TS, 4> : decode_fold_kernel<DV, TIn, TS, 3>;
+            hipLaunchKernelGGL(fold, grid, dim3(kFoldThreads), 0, stream, idx->d_tup, idx->d_coef, S, idx->m_pad,
+                               idx->dk, step ? qi : nullptr, step ? ki : nullptr, step ? vi : nullptr, st->d_pend_k,
+                               st->d_pend_v, st->npend, partial);
             break;
         }
     }

@@ -24,17 +24,27 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
     return __builtin_bit_cast(bf16_t, b);
 }
 
-// Packed feature tuple (see sata_internal.h): three index slots and the order.
+// Packed feature tuple (see sata_internal.h): four index slots, unused ones
+// pointing at the constant-1 slot.
 __device__ __forceinline__ int tup_i1(uint32_t t) { return (int)(t & 0xffu); }
 __device__ __forceinline__ int tup_i2(uint32_t t) { return (int)((t >> 8) & 0xffu); }
 __device__ __forceinline__ int tup_i3(uint32_t t) { return (int)((t >> 16) & 0xffu); }
+__device__ __forceinline__ int tup_i4(uint32_t t) { return (int)(t >> 24); }
 
 // Monomial prod_r x[i_r] of one feature, reading x from an array laid out with
 // `stride` between consecutive dims; slot d_K holds 1 and slot d_K+1 holds 0
 // [hotdry, "Engineering realisation of the constant compute cost": keys (and
 // queries) are mapped to the minimal-basis features through M_p].
 __device__ __forceinline__ float monomial(uint32_t t, const float *x, int stride) {
-    return x[tup_i1(t) * stride] * x[tup_i2(t) * stride] * x[tup_i3(t) * stride];
+    return x[tup_i1(t) * stride] * x[tup_i2(t) * stride] * x[tup_i3(t) * stride] * x[tup_i4(t) * stride];
+}
+// The same with the first NF slots only, for index tables of features of
+// degree below NF + 1 (P <= NF: the remaining slots hold the constant 1).
+template <int NF> __device__ __forceinline__ float monomial_n(uint32_t t, const float *x, int stride) {
+    static_assert(NF == 3 || NF == 4, "three or four slots");
+    const float m = x[tup_i1(t) * stride] * x[tup_i2(t) * stride] * x[tup_i3(t) * stride];
+    if constexpr (NF == 4) return m * x[tup_i4(t) * stride];
+    return m;
 }
 
 // ---- MFMA -------------------------------------------------------------------

@@ -159,7 +159,7 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
         enumerate_order(d_k, p, tuples);
         const double dp = std::pow(sqd, (double)p);
         for (const auto &t : tuples) {
-            uint32_t w = (uint32_t)p << 24;
+            uint32_t w = 0;
             for (int r = 0; r < sata::kMaxOrder; ++r) {
                 const uint32_t slot = r < p ? (uint32_t)t[r] : (uint32_t)d_k;   // d_k -> constant 1
                 w |= slot << (8 * r);
@@ -171,25 +171,27 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
 }
 
 // Quads for the prefill, in the order the scan kernel walks them.  A quad is a
-// pair prefix (i1, i2) (either may be absent) and an aligned block of four last
-// indices i3 = 4b + z; slot z is a feature when (i1, i2, 4b+z) is sorted.  Quads
-// come in "positions" of four, one per stream, whose pairs have the same block
-// range: every pair with i2 in [4a, 4a+4) (order 3: i1 <= i2; order 2: i1
-// absent; for a = 0 also the order-1 pair with both absent) sweeps the blocks
-// b = a .. d/4-1, and four such pairs sweep them side by side.  So within a
-// position the block b is common, and only the first block of a group (the
-// one holding i3 = i2) has slots below i2 (invalid) or a diagonal slot whose
-// multiplicity differs from the rest.  Each valid slot carries the multinomial
-// part 1/alpha! of its feature's readout weight 1/(alpha! d^(p/2))
-// [hotdry, "Core insight of symmetric tensor decomposition"]; the prefill
-// applies d^(-p/2) by scaling q by 1/sqrt(d_K).  The pair product is shared by
-// the four slots of a quad and by all blocks of its group [hotdry, "Hardware
-// optimisation paths and current limits": the hierarchical index structure].
-// Order 0 (the constant feature) has no quad: its state entries are running
-// sums of [v, 1], which the prefill keeps outside the scan.  Unused streams
-// are padding quads (pair product 0).  flags[pos]: bit 0 = some quad
-// of the position has slots with different weights (or invalid slots), bit 1 =
-// the position starts a new group of pairs.
+// prefix (i0, i1, i2) of up to three sorted indices (absent ones first) and an
+// aligned block of four last indices 4b + z; slot z is a feature when
+// (prefix, 4b+z) is sorted.  Quads come in "positions" of four, one per
+// stream, whose prefixes have the same block range: every prefix whose last
+// index i2 lies in [4a, 4a+4) (order 4: i0 <= i1 <= i2; order 3: i1 <= i2;
+// order 2: i2 alone; for a = 0 also the order-1 prefix with all absent)
+// sweeps the blocks b = a .. d/4-1, and four such prefixes sweep them side by
+// side.  So within a position the block b is common, and only the first
+// block of a group (the one holding 4b+z = i2) has slots below i2 (invalid)
+// or a diagonal slot whose multiplicity differs from the rest.  Each valid
+// slot carries the multinomial part 1/alpha! of its feature's readout weight
+// 1/(alpha! d^(p/2)) [hotdry, "Core insight of symmetric tensor
+// decomposition"]; the prefill applies d^(-p/2) by scaling q by 1/sqrt(d_K).
+// The prefix product is shared by the four slots of a quad and by all blocks
+// of its group [hotdry, "Hardware optimisation paths and current limits": the
+// hierarchical index structure].  Order 0 (the constant feature) has no quad:
+// its state entries are running sums of [v, 1], which the prefill keeps
+// outside the scan.  Unused streams are padding quads (prefix product 0).
+// flags[pos]: bit 0 = some quad of the position has slots with different
+// weights (or invalid slots), bit 1 = the position starts a new group of
+// prefixes.
 static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags) {
     std::map<std::vector<int>, int32_t> index;   // sorted tuple -> feature index
     {
@@ -201,21 +203,22 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
         }
     }
     const int none = d, pad = d + 1;
-    auto make = [&](int i1, int i2, int b, uint32_t &nonuni) {
+    struct Prefix { int i0, i1, i2; };
+    auto make = [&](const Prefix &x, int b, uint32_t &nonuni) {
         sata::QuadRec q{};
-        q.w0 = (uint32_t)pad | ((uint32_t)pad << 8) | ((uint32_t)b << 16);
+        q.w0 = (uint32_t)pad | ((uint32_t)pad << 8) | ((uint32_t)none << 16) | ((uint32_t)b << 24);
         q.cidx = -1;
-        if (i1 == pad) return q;
+        if (x.i2 == pad) return q;
         std::vector<int> prefix;
-        if (i1 != none) prefix.push_back(i1);
-        if (i2 != none) prefix.push_back(i2);
+        for (int i : {x.i0, x.i1, x.i2})
+            if (i != none) prefix.push_back(i);
         uint32_t mask = 0;
         int first = -1;
         for (int z = 0; z < 4; ++z) {
             std::vector<int> t = prefix;
-            const int i3 = 4 * b + z;
-            const bool ok = t.empty() || i3 >= t.back();
-            t.push_back(i3);
+            const int last = 4 * b + z;
+            const bool ok = t.empty() || last >= t.back();
+            t.push_back(last);
             q.coef[z] = 0.f;
             if (!ok) continue;
             mask |= 1u << z;
@@ -225,25 +228,27 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
             }
             q.coef[z] = (float)(1.0 / alpha_factorial(t));
         }
-        q.w0 = (uint32_t)i1 | ((uint32_t)i2 << 8) | ((uint32_t)b << 16) | (mask << 24);
+        q.w0 = (uint32_t)x.i1 | ((uint32_t)x.i2 << 8) | ((uint32_t)x.i0 << 16) | ((uint32_t)b << 24) | (mask << 28);
         if (mask != 0xfu || q.coef[0] != q.coef[1] || q.coef[0] != q.coef[2] || q.coef[0] != q.coef[3]) nonuni = 1;
         return q;
     };
     for (int a = 0; a < d / 4; ++a) {
-        std::vector<std::pair<int, int>> pairs;
-        if (P >= 2 && a == 0) pairs.push_back({none, none});
+        std::vector<Prefix> prefixes;
+        if (P >= 2 && a == 0) prefixes.push_back({none, none, none});
         for (int i2 = 4 * a; i2 < 4 * a + 4; ++i2) {
+            if (P >= 5)
+                for (int i1 = 0; i1 <= i2; ++i1)
+                    for (int i0 = 0; i0 <= i1; ++i0) prefixes.push_back({i0, i1, i2});
             if (P >= 4)
-                for (int i1 = 0; i1 <= i2; ++i1) pairs.push_back({i1, i2});
-            if (P >= 3) pairs.push_back({none, i2});
+                for (int i1 = 0; i1 <= i2; ++i1) prefixes.push_back({none, i1, i2});
+            if (P >= 3) prefixes.push_back({none, none, i2});
         }
-        for (size_t g = 0; g < pairs.size(); g += 4) {
+        for (size_t g = 0; g < prefixes.size(); g += 4) {
             for (int b = a; b < d / 4; ++b) {
                 uint32_t nonuni = 0;
                 for (size_t s = 0; s < 4; ++s) {
-                    const bool have = g + s < pairs.size();
-                    out.push_back(make(have ? pairs[g + s].first : pad, have ? pairs[g + s].second : pad, b,
-                                       nonuni));
+                    const bool have = g + s < prefixes.size();
+                    out.push_back(make(have ? prefixes[g + s] : Prefix{none, pad, pad}, b, nonuni));
                 }
                 flags.push_back(nonuni | (b == a ? 2u : 0u));
             }
@@ -312,7 +317,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
         if (p) fact *= p;
         idx->taylor[p] = (float)(1.0 / fact);
     }
-    const uint32_t pad = (0xffu << 24) | ((uint32_t)(d_k + 1) * 0x010101u);   // slots -> constant 0
+    const uint32_t pad = (uint32_t)(d_k + 1) * 0x01010101u;   // slots -> constant 0
     tup.resize((size_t)idx->m_tab, pad);
     coef.resize((size_t)idx->m_tab, 0.f);
     std::vector<sata::QuadRec> quads;
@@ -322,7 +327,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     idx->nq_tab = round_up(std::max<int64_t>(idx->nq, 1), sata::kQuadPad);   // never empty (P = 1 has no quads)
     {
         sata::QuadRec padq{};
-        padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8);   // pair product 0
+        padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8) | ((uint32_t)d_k << 16);   // prefix product 0
         padq.cidx = -1;
         quads.resize((size_t)idx->nq_tab, padq);
         qflags.resize((size_t)(idx->nq_tab / 4), 2u);

@@ -29,14 +29,14 @@ struct sata_index {
     int64_t m_pad = 0;   // state row stride (multiple of 64)
     int64_t m_tab = 0;   // table length (multiple of kTablePad, covers every kernel's tail)
     int device = 0;
-    uint32_t *d_tup = nullptr;   // [m_tab] packed tuples
+    uint32_t *d_tup = nullptr;   // [m_tab] packed tuples: i1 | i2 << 8 | i3 << 16 | i4 << 24
     float *d_coef = nullptr;     // [m_tab] query-side readout weight 1/(alpha! d_K^(p/2)); 0 for padding
     float taylor[8] = {0};       // 1/p!, p < P (intra-chunk direct weights)
     // Prefill-side "pair-quad" view of the same features (see build_quads):
     // quads come in positions of four (one per stream), position-major.
     int64_t nq = 0;              // quads (4 per position)
     int64_t nq_tab = 0;          // quad table length (padded)
-    uint32_t *d_qw0 = nullptr;   // [nq_tab] i1 | i2 << 8 | b << 16 | mask << 24
+    uint32_t *d_qw0 = nullptr;   // [nq_tab] i1 | i2 << 8 | i0 << 16 | b << 24 | mask << 28
     int32_t *d_qcidx = nullptr;  // [nq_tab] state index of the first valid slot (-1: none)
     float *d_qcoef = nullptr;    // [nq_tab][4] query-side weights per slot (0: invalid)
     uint32_t *d_qflags = nullptr;   // [nq_tab / 4] per position: bit 0 mixed weights, bit 1 new pair group
@@ -62,20 +62,21 @@ namespace sata {
 constexpr int kTablePad = 2048;          // tables cover every slice up to this granularity
 constexpr int kQuadPad = 1024;           // quad tables cover every prefill slice up to this granularity
 
-// Prefill feature view.  The features of orders 0..P-1 are grouped into
-// "quads": a pair prefix (i1, i2) (either may be absent) and an aligned block
-// of four last indices i3 = 4b + z, z = 0..3; slot z is a feature when the
-// tuple (i1, i2, 4b+z) is sorted, else padding.  Quads come in positions of
-// four whose pairs sweep the same blocks side by side (see build_quads), so the
-// block b is common to a position.  Absent indices point at the constant-1
-// slot (d_K), padding quads at the constant-0 slot (d_K+1); order 0 is the
-// quad (-, -, b = d_K/4) whose slots d_K..d_K+3 hold 1, 0, 0, 0.
+// Prefill feature view.  The features of orders 1..P-1 are grouped into
+// "quads": a prefix (i0, i1, i2), sorted, any of which may be absent (absent
+// ones come first), and an aligned block of four last indices 4b + z,
+// z = 0..3; slot z is a feature when the tuple (prefix, 4b+z) is sorted, else
+// padding.  Quads come in positions of four whose prefixes sweep the same
+// blocks side by side (see build_quads), so the block b is common to a
+// position.  Absent indices point at the constant-1 slot (d_K), padding quads
+// at the constant-0 slot (d_K+1).  Order 0 has no quad.  b < 16 and the slot
+// mask share the top byte of the quad word, so d_K <= 64.
 struct QuadRec {
     uint32_t w0;
     int32_t cidx;
     float coef[4];
 };
-constexpr int kMaxOrder = 3;             // P <= 4
+constexpr int kMaxOrder = 4;             // P <= 5: four index slots per feature tuple
 
 // ---- launchers (defined in the .hip files) --------------------------------
 

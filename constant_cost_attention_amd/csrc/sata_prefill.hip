@@ -113,20 +113,40 @@ struct ScanCfg {
 
 __device__ __forceinline__ int qd_i1(uint32_t w) { return (int)(w & 0xffu); }
 __device__ __forceinline__ int qd_i2(uint32_t w) { return (int)((w >> 8) & 0xffu); }
-__device__ __forceinline__ int qd_b(uint32_t w) { return (int)((w >> 16) & 0xffu); }
-__device__ __forceinline__ uint32_t qd_mask(uint32_t w) { return w >> 24; }
-__device__ __forceinline__ uint32_t qd_pair(uint32_t w) { return w & 0xffffu; }
+__device__ __forceinline__ int qd_i0(uint32_t w) { return (int)((w >> 16) & 0xffu); }
+__device__ __forceinline__ int qd_b(uint32_t w) { return (int)((w >> 24) & 0xfu); }
+__device__ __forceinline__ uint32_t qd_mask(uint32_t w) { return w >> 28; }
+// alpha! of the quad's prefix (i0, i1, i2) (sorted; absent indices are >= D),
+// and its reciprocal, the prefix's share of the multinomial readout weight.
+// Without order-4 features (TRIPLE false) i0 is always absent.
+template <int D, bool TRIPLE> __device__ __forceinline__ float qd_pfact(uint32_t w) {
+    const int i1 = qd_i1(w), i2 = qd_i2(w);
+    const bool e12 = i1 == i2 && i1 < D;
+    if constexpr (!TRIPLE) return e12 ? 2.f : 1.f;
+    const int i0 = qd_i0(w);
+    const bool e01 = i0 == i1 && i0 < D;
+    return e01 ? (e12 ? 6.f : 2.f) : (e12 ? 2.f : 1.f);
+}
+template <int D, bool TRIPLE> __device__ __forceinline__ float qd_pweight(uint32_t w) {
+    const int i1 = qd_i1(w), i2 = qd_i2(w);
+    const bool e12 = i1 == i2 && i1 < D;
+    if constexpr (!TRIPLE) return e12 ? 0.5f : 1.f;
+    const int i0 = qd_i0(w);
+    const bool e01 = i0 == i1 && i0 < D;
+    return e01 ? (e12 ? 1.f / 6.f : 0.5f) : (e12 ? 0.5f : 1.f);
+}
 
-// w(x) = sum_{p<P} x^p/p! (Horner, P <= 4)
-__device__ __forceinline__ float taylor_w(float x, float c0, float c1, float c2, float c3, int P) {
-    float w = P >= 4 ? c3 : 0.f;
+// w(x) = sum_{p<P} x^p/p! (Horner, P <= 5)
+__device__ __forceinline__ float taylor_w(float x, float c0, float c1, float c2, float c3, float c4, int P) {
+    float w = P >= 5 ? c4 : 0.f;
+    if (P >= 4) w = w * x + c3;
     if (P >= 3) w = w * x + c2;
     if (P >= 2) w = w * x + c1;
     return w * x + c0;
 }
 
 struct TaylorArgs {
-    float scale, c0, c1, c2, c3;
+    float scale, c0, c1, c2, c3, c4;
     int P;
     int raw;          // write the numerator y[:d_V] unnormalised
 };
@@ -167,8 +187,8 @@ __device__ __forceinline__ void intra_tile(f32x4 (&Z)[NT], int qt, int g, int li
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int keyA = 32 * ks + 4 * g + r, keyB = keyA + 16;
-                w8[r] = keyA <= query ? taylor_w(sA[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.P) : 0.f;
-                w8[4 + r] = keyB <= query ? taylor_w(sB[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.P) : 0.f;
+                w8[r] = keyA <= query ? taylor_w(sA[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.c4, ta.P) : 0.f;
+                w8[4 + r] = keyB <= query ? taylor_w(sB[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.c4, ta.P) : 0.f;
             }
             const bf16x8 A = pack_bf16x8(w8);
             // [V | 1] operand in the same key order: keys 32ks + 4g + 0..3 and +16
@@ -198,7 +218,7 @@ __device__ __forceinline__ void intra_tile(f32x4 (&Z)[NT], int qt, int g, int li
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int kr = 16 * kt + 4 * g + r;
-                const float w = kr <= query ? taylor_w(s[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.P) : 0.f;
+                const float w = kr <= query ? taylor_w(s[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.c4, ta.P) : 0.f;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) Z[nt] = mfma_f32(w, Vt[(16 * nt + li) * VS + kr], Z[nt]);
             }
@@ -297,7 +317,7 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-template <int D, int DV, int C, int MT, int NW, typename TIn>
+template <int D, int DV, int C, int MT, int NW, typename TIn, bool TRIPLE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
                          const float4 *__restrict__ qcoef, const uint32_t *__restrict__ qflags,
@@ -538,7 +558,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         for (int r = 0; r < 4; ++r) {
             const int st = acc_stream(r);
             const uint32_t w = W0[p * 4 + st];
-            const float rinv = (qd_i1(w) == qd_i2(w) && qd_i1(w) < D) ? 2.f : 1.f;
+            const float rinv = qd_pfact<D, TRIPLE>(w);
             r4[r] = qcf[(p * 4 + st) * 4 + acc_slot(r)] * rinv;
         }
     };
@@ -640,12 +660,20 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                 auto regroup = [&](int kk) {
                     const uint2 w2 = *reinterpret_cast<const uint2 *>(W0 + (2 * kk + hh) * 4 + sp);
                     const int i1a = qd_i1(w2.x), i2a = qd_i2(w2.x), i1b = qd_i1(w2.y), i2b = qd_i2(w2.y);
-                    const float ca = (i1a == i2a && i1a < D) ? 0.5f : 1.f;
-                    const float cb = (i1b == i2b && i1b < D) ? 0.5f : 1.f;
+                    const float ca = qd_pweight<D, TRIPLE>(w2.x);
+                    const float cb = qd_pweight<D, TRIPLE>(w2.y);
 #pragma unroll
                     for (int tt = 0; tt < TPW; ++tt) {
                         pc[tt][0] = ca * qrow[tt][i1a] * qrow[tt][i2a];
                         pc[tt][1] = cb * qrow[tt][i1b] * qrow[tt][i2b];
+                    }
+                    if constexpr (TRIPLE) {
+                        const int i0a = qd_i0(w2.x), i0b = qd_i0(w2.y);
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) {
+                            pc[tt][0] *= qrow[tt][i0a];
+                            pc[tt][1] *= qrow[tt][i0b];
+                        }
                     }
                     xo = 4 * qd_b(w2.x);
                 };
@@ -729,9 +757,14 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                     if (((gmask >> pos) & 1u) || pos == pbeg) {
                         const uint32_t w = W0[pos * 4 + g];
                         const int i1 = qd_i1(w), i2 = qd_i2(w);
-                        const float cp = (i1 == i2 && i1 < D) ? 0.5f : 1.f;
+                        const float cp = qd_pweight<D, TRIPLE>(w);
 #pragma unroll
                         for (int tt = 0; tt < TPW; ++tt) pcur[tt] = cp * qrow[tt][i1] * qrow[tt][i2];
+                        if constexpr (TRIPLE) {
+                            const int i0 = qd_i0(w);
+#pragma unroll
+                            for (int tt = 0; tt < TPW; ++tt) pcur[tt] *= qrow[tt][i0];
+                        }
                         xo = 4 * qd_b(w);
                     } else {
                         xo += 4;
@@ -841,6 +874,12 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                         const float4 a0 = k1[0], a1 = k1[1], b0 = k2[0], b1 = k2[1];
                         p2[0] = a0.x * b0.x; p2[1] = a0.y * b0.y; p2[2] = a0.z * b0.z; p2[3] = a0.w * b0.w;
                         p2[4] = a1.x * b1.x; p2[5] = a1.y * b1.y; p2[6] = a1.z * b1.z; p2[7] = a1.w * b1.w;
+                        if constexpr (TRIPLE) {
+                            const float4 *k0 = reinterpret_cast<const float4 *>(Kt + qd_i0(w) * KS + tb);
+                            const float4 c0 = k0[0], c1 = k0[1];
+                            p2[0] *= c0.x; p2[1] *= c0.y; p2[2] *= c0.z; p2[3] *= c0.w;
+                            p2[4] *= c1.x; p2[5] *= c1.y; p2[6] *= c1.z; p2[7] *= c1.w;
+                        }
                     }
                     float2 kn = kc;
                     if (j + 1 < MT) kn = load_k3(j + 1, ks);
@@ -903,6 +942,16 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                         p2[ks][0] = a0.x * b0.x; p2[ks][1] = a0.y * b0.y; p2[ks][2] = a0.z * b0.z; p2[ks][3] = a0.w * b0.w;
                         p2[ks][4] = a1.x * b1.x; p2[ks][5] = a1.y * b1.y; p2[ks][6] = a1.z * b1.z; p2[ks][7] = a1.w * b1.w;
                     }
+                    if constexpr (TRIPLE) {
+                        const float *k0 = Kt + qd_i0(w) * KS + 8 * g;
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            const float4 c0 = *reinterpret_cast<const float4 *>(k0 + 32 * ks);
+                            const float4 c1 = *reinterpret_cast<const float4 *>(k0 + 32 * ks + 4);
+                            p2[ks][0] *= c0.x; p2[ks][1] *= c0.y; p2[ks][2] *= c0.z; p2[ks][3] *= c0.w;
+                            p2[ks][4] *= c1.x; p2[ks][5] *= c1.y; p2[ks][6] *= c1.z; p2[ks][7] *= c1.w;
+                        }
+                    }
                 }
                 float2 kn[NKS];
                 if (j + 1 < MT) load_k3(kn, j + 1);
@@ -933,7 +982,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
                     const uint32_t w = uw[j];
-                    const float a = Kt[qd_i1(w) * KS + tb] * Kt[qd_i2(w) * KS + tb] * Kt[(4 * qd_b(w) + uz) * KS + tb];
+                    float a = Kt[qd_i1(w) * KS + tb] * Kt[qd_i2(w) * KS + tb] * Kt[(4 * qd_b(w) + uz) * KS + tb];
+                    if constexpr (TRIPLE) a *= Kt[qd_i0(w) * KS + tb];
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_f32(a, B[nt], S[j][nt]);
                 }
@@ -1013,7 +1063,7 @@ struct WsCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int DV, int C, int MT>
+template <int D, int DV, int C, int MT, bool TRIPLE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
                             const float4 *__restrict__ qcoef, const uint32_t *__restrict__ qflags,
@@ -1163,12 +1213,20 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
                 auto regroup = [&](int kk) {
                     const uint2 w2 = *reinterpret_cast<const uint2 *>(W0 + (2 * kk + hh) * 4 + sp);
                     const int i1a = qd_i1(w2.x), i2a = qd_i2(w2.x), i1b = qd_i1(w2.y), i2b = qd_i2(w2.y);
-                    const float ca = (i1a == i2a && i1a < D) ? 0.5f : 1.f;
-                    const float cb = (i1b == i2b && i1b < D) ? 0.5f : 1.f;
+                    const float ca = qd_pweight<D, TRIPLE>(w2.x);
+                    const float cb = qd_pweight<D, TRIPLE>(w2.y);
 #pragma unroll
                     for (int tt = 0; tt < TPW; ++tt) {
                         pc[tt][0] = ca * qrow[tt][i1a] * qrow[tt][i2a];
                         pc[tt][1] = cb * qrow[tt][i1b] * qrow[tt][i2b];
+                    }
+                    if constexpr (TRIPLE) {
+                        const int i0a = qd_i0(w2.x), i0b = qd_i0(w2.y);
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) {
+                            pc[tt][0] *= qrow[tt][i0a];
+                            pc[tt][1] *= qrow[tt][i0b];
+                        }
                     }
                     xo = 4 * qd_b(w2.x);
                 };
@@ -1286,7 +1344,7 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t w = W0[p * 4 + r];
-                    const float rinv = (qd_i1(w) == qd_i2(w) && qd_i1(w) < D) ? 2.f : 1.f;
+                    const float rinv = qd_pfact<D, TRIPLE>(w);
                     r4[r] = qcf[(p * 4 + r) * 4 + g] * rinv;
                 }
             };
@@ -1367,6 +1425,12 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
                             const float4 a0 = k1[0], a1 = k1[1], b0 = k2[0], b1 = k2[1];
                             p2[0] = a0.x * b0.x; p2[1] = a0.y * b0.y; p2[2] = a0.z * b0.z; p2[3] = a0.w * b0.w;
                             p2[4] = a1.x * b1.x; p2[5] = a1.y * b1.y; p2[6] = a1.z * b1.z; p2[7] = a1.w * b1.w;
+                            if constexpr (TRIPLE) {
+                                const float4 *k0 = reinterpret_cast<const float4 *>(Kt + qd_i0(w) * KS + tb);
+                                const float4 c0 = k0[0], c1 = k0[1];
+                                p2[0] *= c0.x; p2[1] *= c0.y; p2[2] *= c0.z; p2[3] *= c0.w;
+                                p2[4] *= c1.x; p2[5] *= c1.y; p2[6] *= c1.z; p2[7] *= c1.w;
+                            }
                         }
                         float2 kn = kc;
                         if (j + 1 < MT) kn = load_k3(j + 1, ks);
@@ -1653,26 +1717,27 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
 }
 
 // The scan kernel and its launch shape: the general kernel, or the warp-specialised one.
-template <int D, int C, int MT, int NW, typename TIn, bool WS>
+// TRIPLE: features of order 4 (P = 5), whose quads carry a three-index prefix.
+template <int D, int C, int MT, int NW, typename TIn, bool WS, bool TRIPLE>
 struct ScanSel {
     using Cfg = ScanCfg<D, D, C, MT, NW, TIn>;
     static constexpr int THREADS = Cfg::THREADS, LDS = Cfg::LDS;
     static constexpr bool PERSIST = Cfg::PERSIST;
-    static constexpr auto kernel = prefill_scan_kernel<D, D, C, MT, NW, TIn>;
+    static constexpr auto kernel = prefill_scan_kernel<D, D, C, MT, NW, TIn, TRIPLE>;
 };
-template <int D, int C, int MT, int NW>
-struct ScanSel<D, C, MT, NW, bf16_t, true> {
+template <int D, int C, int MT, int NW, bool TRIPLE>
+struct ScanSel<D, C, MT, NW, bf16_t, true, TRIPLE> {
     using Cfg = WsCfg<D, D, C, MT>;
     static constexpr int THREADS = Cfg::THREADS, LDS = Cfg::LDS;
     static constexpr bool PERSIST = true;
-    static constexpr auto kernel = prefill_scan_ws_kernel<D, D, C, MT>;
+    static constexpr auto kernel = prefill_scan_ws_kernel<D, D, C, MT, TRIPLE>;
 };
 
-template <int D, int C, int MT, int NW, typename TIn, typename TOut, bool WS = false>
+template <int D, int C, int MT, int NW, typename TIn, typename TOut, bool WS, bool TRIPLE>
 static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                               const void *q, const void *k, const void *v, void *out, int64_t n,
                               hipStream_t stream) {
-    using Cfg = ScanSel<D, C, MT, NW, TIn, WS>;
+    using Cfg = ScanSel<D, C, MT, NW, TIn, WS, TRIPLE>;
     const int64_t bh = (int64_t)st->batch * st->heads;
     auto scan = Cfg::kernel;
     auto red = prefill_reduce_kernel<D, D, C, TIn, TOut>;
@@ -1681,6 +1746,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     TaylorArgs ta;
     ta.scale = 1.0f / sqrtf((float)D);
     ta.c0 = idx->taylor[0]; ta.c1 = idx->taylor[1]; ta.c2 = idx->taylor[2]; ta.c3 = idx->taylor[3];
+    ta.c4 = idx->taylor[4];
     ta.P = idx->P;
     ta.raw = plan.raw ? 1 : 0;
     const int64_t nchunks = (n + C - 1) / C;
@@ -1740,21 +1806,21 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     return hipSuccess;
 }
 
-template <int D, int C, int MT, int NW>
+template <int D, int C, int MT, int NW, bool TRIPLE>
 static hipError_t run_dt(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                          const void *q, const void *k, const void *v, void *out, int64_t n,
                          sata_dtype in_dt, sata_dtype out_dt, hipStream_t s) {
     if constexpr (MT > 4 || NW > 4) {
         if (in_dt == SATA_F32) return hipErrorInvalidValue;   // pick_shape never plans this
     } else if (in_dt == SATA_F32) {
-        if (out_dt == SATA_F32) return run_prefill<D, C, MT, NW, float, float>(idx, st, plan, q, k, v, out, n, s);
-        return run_prefill<D, C, MT, NW, float, bf16_t>(idx, st, plan, q, k, v, out, n, s);
+        if (out_dt == SATA_F32) return run_prefill<D, C, MT, NW, float, float, false, TRIPLE>(idx, st, plan, q, k, v, out, n, s);
+        return run_prefill<D, C, MT, NW, float, bf16_t, false, TRIPLE>(idx, st, plan, q, k, v, out, n, s);
     }
-    if (out_dt == SATA_F32) return run_prefill<D, C, MT, NW, bf16_t, float>(idx, st, plan, q, k, v, out, n, s);
-    return run_prefill<D, C, MT, NW, bf16_t, bf16_t>(idx, st, plan, q, k, v, out, n, s);
+    if (out_dt == SATA_F32) return run_prefill<D, C, MT, NW, bf16_t, float, false, TRIPLE>(idx, st, plan, q, k, v, out, n, s);
+    return run_prefill<D, C, MT, NW, bf16_t, bf16_t, false, TRIPLE>(idx, st, plan, q, k, v, out, n, s);
 }
 
-template <int D>
+template <int D, bool TRIPLE>
 static hipError_t run_d(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                         const void *q, const void *k, const void *v, void *out, int64_t n,
                         sata_dtype in_dt, sata_dtype out_dt, hipStream_t s) {
@@ -1763,8 +1829,8 @@ static hipError_t run_d(const sata_index *idx, const sata_state *st, const Prefi
         if (in_dt != SATA_BF16) return hipErrorInvalidValue;   // never planned
         auto go = [&](auto cw, auto mw) -> hipError_t {
             constexpr int CC = decltype(cw)::value, MM = decltype(mw)::value;
-            if (out_dt == SATA_F32) return run_prefill<D, CC, MM, 8, bf16_t, float, true>(idx, st, plan, q, k, v, out, n, s);
-            return run_prefill<D, CC, MM, 8, bf16_t, bf16_t, true>(idx, st, plan, q, k, v, out, n, s);
+            if (out_dt == SATA_F32) return run_prefill<D, CC, MM, 8, bf16_t, float, true, TRIPLE>(idx, st, plan, q, k, v, out, n, s);
+            return run_prefill<D, CC, MM, 8, bf16_t, bf16_t, true, TRIPLE>(idx, st, plan, q, k, v, out, n, s);
         };
         using I64 = std::integral_constant<int, 64>;
         using I128 = std::integral_constant<int, 128>;
@@ -1775,27 +1841,31 @@ static hipError_t run_d(const sata_index *idx, const sata_state *st, const Prefi
     }
     if (nw == 8) {
         if (plan.chunk != 128 || in_dt != SATA_BF16) return hipErrorInvalidValue;   // never planned
-        if (mt == 2) return run_dt<D, 128, 2, 8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-        return run_dt<D, 128, 4, 8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        if (mt == 2) return run_dt<D, 128, 2, 8, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        return run_dt<D, 128, 4, 8, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
     }
     if (plan.chunk == 64) {
-        if (mt == 2) return run_dt<D, 64, 2, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-        if (mt == 4) return run_dt<D, 64, 4, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-        return run_dt<D, 64, 8, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        if (mt == 2) return run_dt<D, 64, 2, 4, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        if (mt == 4) return run_dt<D, 64, 4, 4, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+        return run_dt<D, 64, 8, 4, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
     }
-    if (mt == 2) return run_dt<D, 128, 2, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-    if (mt == 4) return run_dt<D, 128, 4, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
-    return run_dt<D, 128, 8, 4>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+    if (mt == 2) return run_dt<D, 128, 2, 4, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+    if (mt == 4) return run_dt<D, 128, 4, 4, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
+    return run_dt<D, 128, 8, 4, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
 }
 
 hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                           const void *q, const void *k, const void *v, void *out, int64_t n,
                           sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream) {
     switch (idx->dk) {
-        case 8: return run_d<8>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
-        case 16: return run_d<16>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
-        case 32: return run_d<32>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
-        case 64: return run_d<64>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
+        case 8: return idx->P >= 5 ? run_d<8, true>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream)
+                                   : run_d<8, false>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
+        case 16: return idx->P >= 5 ? run_d<16, true>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream)
+                                    : run_d<16, false>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
+        case 32: return idx->P >= 5 ? run_d<32, true>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream)
+                                    : run_d<32, false>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
+        case 64: return idx->P >= 5 ? run_d<64, true>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream)
+                                    : run_d<64, false>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -38,7 +38,9 @@
  *     library owns index and state memory (hipMalloc) and frees it in the
  *     *_free calls.
  *   - Supported shapes: d_K, d_V in {8, 16, 32, 64} with d_K == d_V for
- *     prefill; 1 <= P <= 4.  Other values return SATA_ERR_UNSUPPORTED.
+ *     prefill; 1 <= P <= 5.  Other values return SATA_ERR_UNSUPPORTED.  The
+ *     state grows as C(d_K+P-1, P-1) (d_V+1) fp32 values per head: at
+ *     d_K = 64, 12.5 MB for P = 4 and 212 MB for P = 5.
  */
 #ifndef SATA_H
 #define SATA_H

@@ -120,6 +120,8 @@ WORKLOADS = {
     "prefill_d64_p4_bf16": Workload("prefill_d64_p4_bf16", 1, 8, 65536, 64, 64, 4, "bf16", 128, SEED_BASE + 4),
     "prefill_d16x64h_p4_bf16": Workload("prefill_d16x64h_p4_bf16", 1, 64, 131072, 16, 16, 4, "bf16", 128,
                                         SEED_BASE + 5),
+    # five orders (814,385 features, 212 MB of fp32 state per head at d = 64)
+    "prefill_d64_p5_bf16": Workload("prefill_d64_p5_bf16", 1, 8, 8192, 64, 64, 5, "bf16", 128, SEED_BASE + 6),
 }
 
 

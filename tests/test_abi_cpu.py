@@ -55,7 +55,7 @@ def test_argument_checks_before_any_device_call(lib):
     assert lib.sata_build_index(0, 64, 4, ctypes.byref(out)) == sata.SATA_ERR_INVALID
     assert lib.sata_build_index(64, 64, 0, ctypes.byref(out)) == sata.SATA_ERR_INVALID
     assert lib.sata_build_index(12, 12, 4, ctypes.byref(out)) == sata.SATA_ERR_UNSUPPORTED
-    assert lib.sata_build_index(64, 64, 5, ctypes.byref(out)) == sata.SATA_ERR_UNSUPPORTED
+    assert lib.sata_build_index(64, 64, 6, ctypes.byref(out)) == sata.SATA_ERR_UNSUPPORTED
     assert b"P <=" in lib.sata_last_error()
     assert lib.sata_index_features(None) == -1
     assert lib.sata_prefill(None, None, None, None, None, None, 16, 0, 0, 0, None) == sata.SATA_ERR_INVALID
@@ -73,7 +73,7 @@ def test_argument_checks_before_any_device_call(lib):
     lib.sata_state_free(None)
 
 
-@pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2)])
+@pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2), (8, 5), (16, 5)])
 def test_feature_tables_match_bruteforce_basis(oracle, d, P):
     """Host index builder vs oracle: same sorted tuples in the same order (orders
     0..P-1, lexicographic within an order), and readout weight
@@ -89,8 +89,8 @@ def test_feature_tables_match_bruteforce_basis(oracle, d, P):
             btup, bcnt = oracle.basis_bruteforce(d, p)
         g = len(bcnt)
         t = tup[f:f + g]
-        assert np.all((t >> 24) == p)
-        slots = np.stack([(t >> (8 * r)) & 0xFF for r in range(3)], axis=1).astype(np.int64)
+        slots = np.stack([(t >> (8 * r)) & 0xFF for r in range(4)], axis=1).astype(np.int64)
+        assert np.all(np.sum(slots < d, axis=1) == p)
         assert np.array_equal(slots[:, :p], btup.astype(np.int64))
         assert np.all(slots[:, p:] == d)
         expect = bcnt.astype(np.float64) / (math.factorial(p) * math.sqrt(d) ** p)
@@ -102,8 +102,9 @@ def test_feature_tables_match_bruteforce_basis(oracle, d, P):
 def test_describe_rejects_what_build_rejects(lib):
     from constant_cost_attention_amd import sata
     assert lib.sata_describe_features(12, 4, None, None, 0) == -1
-    assert lib.sata_describe_features(64, 5, None, None, 0) == -1
+    assert lib.sata_describe_features(64, 6, None, None, 0) == -1
     assert lib.sata_describe_features(64, 4, None, None, 0) == 47905
+    assert lib.sata_describe_features(64, 5, None, None, 0) == 814385
 
 
 def test_binding_rejects_cpu_tensors():
@@ -113,9 +114,9 @@ def test_binding_rejects_cpu_tensors():
         sata._dev_ptr(torch.zeros(4), "q")
 
 
-@pytest.mark.parametrize("d,P", [(8, 1), (8, 2), (8, 3), (16, 4), (32, 4), (64, 4)])
+@pytest.mark.parametrize("d,P", [(8, 1), (8, 2), (8, 3), (16, 4), (32, 4), (64, 4), (8, 5), (16, 5), (32, 5)])
 def test_quads_cover_every_feature_once(d, P):
-    """Every valid quad slot is the feature (i1, i2, 4b+z) at state index
+    """Every valid quad slot is the feature (i0, i1, i2, 4b+z) at state index
     cidx + (z - first valid slot), with the feature table's readout weight;
     together the valid slots cover every feature exactly once except feature
     0, the constant order 0, which the prefill keeps out of the quads (P = 1
@@ -125,12 +126,13 @@ def test_quads_cover_every_feature_once(d, P):
     tup, coef = sata.sata_describe_features(d, P)
     w0, cidx, qc = sata.sata_describe_quads(d, P)
     assert len(w0) % 4 == 0
-    slots = np.stack([(tup >> (8 * r)) & 0xFF for r in range(3)], axis=1).astype(np.int64)
-    order = (tup >> 24).astype(np.int64)
+    slots = np.stack([(tup >> (8 * r)) & 0xFF for r in range(4)], axis=1).astype(np.int64)
+    order = np.sum(slots < d, axis=1).astype(np.int64)
     seen = np.zeros(len(tup), dtype=np.int64)
     for q in range(len(w0)):
-        i1, i2, b, mask = int(w0[q] & 0xFF), int((w0[q] >> 8) & 0xFF), int((w0[q] >> 16) & 0xFF), int(w0[q] >> 24)
-        assert b == int((w0[q - q % 4] >> 16) & 0xFF)
+        i1, i2, i0 = int(w0[q] & 0xFF), int((w0[q] >> 8) & 0xFF), int((w0[q] >> 16) & 0xFF)
+        b, mask = int((w0[q] >> 24) & 0xF), int(w0[q] >> 28)
+        assert b == int((w0[q - q % 4] >> 24) & 0xF)
         if not mask:
             assert cidx[q] == -1
             assert np.all(qc[q] == 0)
@@ -141,7 +143,7 @@ def test_quads_cover_every_feature_once(d, P):
                 assert qc[q, z] == 0
                 continue
             f = int(cidx[q]) + z - z0
-            idx = [i for i in (i1, i2) if i < d]
+            idx = [i for i in (i0, i1, i2) if i < d]
             idx.append(4 * b + z)
             want = sorted(idx)
             assert idx == want
