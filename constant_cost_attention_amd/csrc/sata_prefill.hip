@@ -1208,86 +1208,159 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
             const bf16x8 *Bl = reinterpret_cast<const bf16x8 *>(Bc + Cfg::FULLB);
             for (int cc = cbeg; cc < cend; ++cc) {
                 f32x4 Y[TPW][NT];
-                float pc[TPW][2];
-                int xo = 0;
-                auto regroup = [&](int kk) {
-                    const uint2 w2 = *reinterpret_cast<const uint2 *>(W0 + (2 * kk + hh) * 4 + sp);
-                    const int i1a = qd_i1(w2.x), i2a = qd_i2(w2.x), i1b = qd_i1(w2.y), i2b = qd_i2(w2.y);
-                    const float ca = qd_pweight<D, TRIPLE>(w2.x);
-                    const float cb = qd_pweight<D, TRIPLE>(w2.y);
-#pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt) {
-                        pc[tt][0] = ca * qrow[tt][i1a] * qrow[tt][i2a];
-                        pc[tt][1] = cb * qrow[tt][i1b] * qrow[tt][i2b];
-                    }
-                    if constexpr (TRIPLE) {
-                        const int i0a = qd_i0(w2.x), i0b = qd_i0(w2.y);
-#pragma unroll
+                if constexpr (TPW == 1) {
+                    // A K step's prefix factors (prefix weight times the prefix product of the lane's
+                    // two streams at position 2 kk + hh) and q block offset, gathered two steps
+                    // before its products: the quad-word read and the q reads that depend on it then
+                    // overlap the products of the steps in between instead of stalling at each group
+                    // start.  (The loop is unrolled, so each step's entries live for three steps.)
+                    float pf[NS][TPW][2];
+                    int xs[NS];
+                    auto gather = [&](int kk) {
+                        const uint2 w2 = *reinterpret_cast<const uint2 *>(W0 + (2 * kk + hh) * 4 + sp);
+                        const int i1a = qd_i1(w2.x), i2a = qd_i2(w2.x), i1b = qd_i1(w2.y), i2b = qd_i2(w2.y);
+                        const float ca = qd_pweight<D, TRIPLE>(w2.x);
+                        const float cb = qd_pweight<D, TRIPLE>(w2.y);
+    #pragma unroll
                         for (int tt = 0; tt < TPW; ++tt) {
-                            pc[tt][0] *= qrow[tt][i0a];
-                            pc[tt][1] *= qrow[tt][i0b];
+                            pf[kk][tt][0] = ca * qrow[tt][i1a] * qrow[tt][i2a];
+                            pf[kk][tt][1] = cb * qrow[tt][i1b] * qrow[tt][i2b];
                         }
+                        if constexpr (TRIPLE) {
+                            const int i0a = qd_i0(w2.x), i0b = qd_i0(w2.y);
+    #pragma unroll
+                            for (int tt = 0; tt < TPW; ++tt) {
+                                pf[kk][tt][0] *= qrow[tt][i0a];
+                                pf[kk][tt][1] *= qrow[tt][i0b];
+                            }
+                        }
+                        xs[kk] = 4 * qd_b(w2.x);
+                    };
+                    auto load_b = [&](bf16x8 (&B)[NT], int kk) {
+    #pragma unroll
+                        for (int nt = 0; nt + 1 < NT; ++nt) B[nt] = Bv[(kk * (NT - 1) + nt) * 64 + lane];
+                        if constexpr (LASTW == 4) {
+                            uint4 z = {0u, 0u, 0u, 0u};
+                            B[NT - 1] = __builtin_bit_cast(bf16x8, z);
+                            if (li == 0) B[NT - 1] = Bl[kk * 4 + g];
+                        } else {
+                            B[NT - 1] = Bl[kk * 64 + lane];
+                        }
+                    };
+                    auto form = [&](bf16x8 (&A)[TPW], int kk) {
+    #pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) {
+                            const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xs[kk]);
+                            const float p0 = pf[kk][tt][0], p1 = pf[kk][tt][1];
+                            const float a[8] = {p0 * x.x, p1 * x.x, p0 * x.y, p1 * x.y,
+                                                p0 * x.z, p1 * x.z, p0 * x.w, p1 * x.w};
+                            A[tt] = pack_bf16x8(a);
+                        }
+                    };
+                    // two operand sets in turn: step kk's products run while step kk + 1's are formed
+                    bf16x8 A[2][TPW], B[2][NT];
+                    gather(0);
+                    gather(1);
+                    load_b(B[0], 0);
+                    form(A[0], 0);
+    #pragma unroll
+                    for (int kk = 0; kk < NS; ++kk) {
+                        if (kk + 2 < NS) gather(kk + 2);
+                        if (kk + 1 < NS) {
+                            load_b(B[(kk + 1) & 1], kk + 1);
+                            form(A[(kk + 1) & 1], kk + 1);
+                        }
+    #pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+    #pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+                                Y[tt][nt] = mfma_bf16(A[kk & 1][tt], B[kk & 1][nt],
+                                                      kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : Y[tt][nt]);
                     }
-                    xo = 4 * qd_b(w2.x);
-                };
-                auto advance = [&](int kk) {
-                    if (((gmask >> (2 * kk - 1)) & 7u) != 0) {
-                        __asm__ volatile("" ::: "memory");
-                        regroup(kk);
-                    } else {
-                        xo += 8;
-                    }
-                };
-                auto load_b = [&](bf16x8 (&B)[NT], int kk) {
-#pragma unroll
-                    for (int nt = 0; nt + 1 < NT; ++nt) B[nt] = Bv[(kk * (NT - 1) + nt) * 64 + lane];
-                    if constexpr (LASTW == 4) {
-                        uint4 z = {0u, 0u, 0u, 0u};
-                        B[NT - 1] = __builtin_bit_cast(bf16x8, z);
-                        if (li == 0) B[NT - 1] = Bl[kk * 4 + g];
-                    } else {
-                        B[NT - 1] = Bl[kk * 64 + lane];
-                    }
-                };
-                auto form = [&](bf16x8 (&A)[TPW]) {
-#pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt) {
-                        const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
-                        const float a[8] = {pc[tt][0] * x.x, pc[tt][1] * x.x, pc[tt][0] * x.y, pc[tt][1] * x.y,
-                                            pc[tt][0] * x.z, pc[tt][1] * x.z, pc[tt][0] * x.w, pc[tt][1] * x.w};
-                        A[tt] = pack_bf16x8(a);
-                    }
-                };
-                auto mma = [&](const bf16x8 (&A)[TPW], const bf16x8 (&B)[NT]) {
-#pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A[tt], B[nt], Y[tt][nt]);
-                };
-                // two operand sets in turn: step kk's products run while step kk + 1's are formed
-                bf16x8 A0[TPW], B0[NT], A1[TPW], B1[NT];
-                regroup(0);
-                load_b(B0, 0);
-                form(A0);
-                advance(1);
-                load_b(B1, 1);
-                form(A1);
-#pragma unroll
-                for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A0[tt], B0[nt], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll 1
-                for (int kk = 1; kk + 2 < NS; kk += 2) {
-                    advance(kk + 1);
-                    load_b(B0, kk + 1);
+                } else {
+                    // Two token tiles per wavefront: the pair products are re-formed only where a
+                    // pair group starts (measured faster here than gathering every step ahead).
+                    float pc[TPW][2];
+                    int xo = 0;
+                    auto regroup = [&](int kk) {
+                        const uint2 w2 = *reinterpret_cast<const uint2 *>(W0 + (2 * kk + hh) * 4 + sp);
+                        const int i1a = qd_i1(w2.x), i2a = qd_i2(w2.x), i1b = qd_i1(w2.y), i2b = qd_i2(w2.y);
+                        const float ca = qd_pweight<D, TRIPLE>(w2.x);
+                        const float cb = qd_pweight<D, TRIPLE>(w2.y);
+    #pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) {
+                            pc[tt][0] = ca * qrow[tt][i1a] * qrow[tt][i2a];
+                            pc[tt][1] = cb * qrow[tt][i1b] * qrow[tt][i2b];
+                        }
+                        if constexpr (TRIPLE) {
+                            const int i0a = qd_i0(w2.x), i0b = qd_i0(w2.y);
+    #pragma unroll
+                            for (int tt = 0; tt < TPW; ++tt) {
+                                pc[tt][0] *= qrow[tt][i0a];
+                                pc[tt][1] *= qrow[tt][i0b];
+                            }
+                        }
+                        xo = 4 * qd_b(w2.x);
+                    };
+                    auto advance = [&](int kk) {
+                        if (((gmask >> (2 * kk - 1)) & 7u) != 0) {
+                            __asm__ volatile("" ::: "memory");
+                            regroup(kk);
+                        } else {
+                            xo += 8;
+                        }
+                    };
+                    auto load_b = [&](bf16x8 (&B)[NT], int kk) {
+    #pragma unroll
+                        for (int nt = 0; nt + 1 < NT; ++nt) B[nt] = Bv[(kk * (NT - 1) + nt) * 64 + lane];
+                        if constexpr (LASTW == 4) {
+                            uint4 z = {0u, 0u, 0u, 0u};
+                            B[NT - 1] = __builtin_bit_cast(bf16x8, z);
+                            if (li == 0) B[NT - 1] = Bl[kk * 4 + g];
+                        } else {
+                            B[NT - 1] = Bl[kk * 64 + lane];
+                        }
+                    };
+                    auto form = [&](bf16x8 (&A)[TPW]) {
+    #pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) {
+                            const float4 x = *reinterpret_cast<const float4 *>(qrow[tt] + xo);
+                            const float a[8] = {pc[tt][0] * x.x, pc[tt][1] * x.x, pc[tt][0] * x.y, pc[tt][1] * x.y,
+                                                pc[tt][0] * x.z, pc[tt][1] * x.z, pc[tt][0] * x.w, pc[tt][1] * x.w};
+                            A[tt] = pack_bf16x8(a);
+                        }
+                    };
+                    auto mma = [&](const bf16x8 (&A)[TPW], const bf16x8 (&B)[NT]) {
+    #pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+    #pragma unroll
+                            for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A[tt], B[nt], Y[tt][nt]);
+                    };
+                    // two operand sets in turn: step kk's products run while step kk + 1's are formed
+                    bf16x8 A0[TPW], B0[NT], A1[TPW], B1[NT];
+                    regroup(0);
+                    load_b(B0, 0);
                     form(A0);
-                    mma(A1, B1);
-                    advance(kk + 2);
-                    load_b(B1, kk + 2);
+                    advance(1);
+                    load_b(B1, 1);
                     form(A1);
-                    mma(A0, B0);
+    #pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt)
+    #pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) Y[tt][nt] = mfma_bf16(A0[tt], B0[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+    #pragma unroll 1
+                    for (int kk = 1; kk + 2 < NS; kk += 2) {
+                        advance(kk + 1);
+                        load_b(B0, kk + 1);
+                        form(A0);
+                        mma(A1, B1);
+                        advance(kk + 2);
+                        load_b(B1, kk + 2);
+                        form(A1);
+                        mma(A0, B0);
+                    }
+                    mma(A1, B1);
                 }
-                mma(A1, B1);
                 __syncthreads();   // B: readout and update of chunk cc done
 
                 // partials of chunk cc: [TT][NC][16 tokens] per (bh, chunk, slice)
