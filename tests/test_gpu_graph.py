@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import synth_inputs as si
-from sata_testutil import TOL_F32, decode, dev_all, prefill, rel_err, say
+from sata_testutil import TOL_BF16, TOL_F32, decode, dev_all, prefill, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -58,3 +58,33 @@ def test_decode_steps_replayed_from_a_graph(sata, oracle, window):
     err = rel_err(o, ref)
     say("  err %.3e" % err)
     assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("d,heads,n", [(32, 3, 200), (64, 2, 300)])
+def test_prefill_replayed_from_a_graph(sata, oracle, d, heads, n):
+    """A state reset and a bf16 prefill captured once (after an eager call of
+    the same size, which sizes the workspace) and replayed on new inputs
+    copied into the captured buffers: every replay against the oracle."""
+    P, reps = 4, 3
+    idx = sata.Index(d, d, P)
+    st = sata.State(idx, 1, heads)
+    draws = [si.draw_qkv((1, heads), n, d, d, 7100 + 10 * d + r, "bf16") for r in range(reps + 1)]
+    say("prefill in a HIP graph, d=%d heads=%d n=%d, %d replays" % (d, heads, n, reps))
+    sq, sk, sv = dev_all(draws[0])
+    so = torch.empty(sv.shape, dtype=torch.float32, device="cuda")
+    sata.sata_prefill(idx, st, sq, sk, sv, so)                 # eager: sizes the workspace
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sata.sata_state_reset(st)
+        sata.sata_prefill(idx, st, sq, sk, sv, so)
+    for r in range(1, reps + 1):
+        q, k, v = dev_all(draws[r])
+        sq.copy_(q); sk.copy_(k); sv.copy_(v)
+        graph.replay()
+        torch.cuda.synchronize()
+        err = rel_err(so.cpu().numpy(), oracle.taylor_attention(draws[r].q, draws[r].k, draws[r].v, P))
+        say("  replay %d: err %.3e" % (r, err))
+        assert err <= TOL_BF16
+    st.free()
+    idx.free()
