@@ -460,6 +460,28 @@ def order5_section(sata, steps: int):
                        "frac": ach / PEAK_HBM_GBS}}
 
 
+def d128_section(sata):
+    """Head size 128 on the decode side (366,145 features at P = 4, 189 MB of
+    fp32 state per head): one sequence of 8 heads, plain steps from an empty
+    state (a step's cost does not depend on what the state holds)."""
+    import dataclasses
+    import torch
+    import synth_inputs as si
+    wl = dataclasses.replace(si.WORKLOADS["decode_d64_p4_f32"], batch=1, d_k=128, d_v=128)
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    st = sata.State(idx, wl.batch, wl.heads)
+    ms, kern = time_decode(sata, idx, st, wl, 64, 8, wl.seed + 3)
+    st.free()
+    idx.free()
+    torch.cuda.empty_cache()
+    nbytes = decode_bytes(wl)
+    kms = kern["decode_stream"][0]
+    ach = nbytes / (kms * 1e-3) / 1e9
+    return {"workload": "%d x %d heads, d=%d, P=%d" % (wl.batch, wl.heads, wl.d_k, wl.P),
+            "value": wl.batch / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "stream_kernel_ms": kms,
+            "bytes_per_step": nbytes, "achieved_gbs": ach, "frac": ach / PEAK_HBM_GBS}
+
+
 # ------------------------------------------------------------------ oracle on the host
 
 def cpu_baseline(wl, x, budget_s: float):
@@ -696,6 +718,10 @@ def main():
                                   100 * o5["prefill"]["roofline"]["frac"], o5["decode"]["workload"],
                                   o5["decode"]["ms_per_step"], o5["decode"]["achieved_gbs"], 100 * o5["decode"]["frac"]))
         result["order5"] = o5
+        dd = d128_section(sata)
+        log("decode, %s: %.3f ms/step, stream %.0f GB/s (%.1f%% of peak)"
+            % (dd["workload"], dd["ms_per_step"], dd["achieved_gbs"], 100 * dd["frac"]))
+        result["d128_decode"] = dd
 
     if not args.no_backward:
         bwd = []

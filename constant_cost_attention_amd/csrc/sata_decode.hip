@@ -33,6 +33,10 @@
 namespace sata {
 
 constexpr int kDecThreads = 256;
+// LDS staging length of a token's q or k: the d_K values, the constant-1 and
+// constant-0 slots, padding (d_K <= 64 goes with d_V <= 64, d_K = 128 with
+// d_V = 128).
+template <int DV> constexpr int tok_stage() { return DV > 64 ? 136 : 72; }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -159,7 +163,7 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
     constexpr int FPT = dec_fpt<TS>();
     constexpr int R = (NC + 1) / 2;                    // rows of the first load batch
     typedef Word<TS, FPT> Wd;
-    __shared__ float sq[72], sk[72], sv[NC];
+    __shared__ float sq[tok_stage<DV>()], sk[tok_stage<DV>()], sv[NC];
     __shared__ float red[kDecThreads / 64][NC];
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
@@ -240,7 +244,7 @@ void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restric
     constexpr int NR = rows_per_group<DV>();
     constexpr int FPT = dec_fpt<TS>();
     typedef Word<TS, FPT> Wd;
-    __shared__ float sq[72], sk[72], sv[NR];
+    __shared__ float sq[tok_stage<DV>()], sk[tok_stage<DV>()], sv[NR];
     __shared__ float red[kDecThreads / 64][16];
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
@@ -319,7 +323,7 @@ void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restric
 // NF: index slots the monomials multiply (3 up to P = 4, 4 for P = 5).
 constexpr int kFoldThreads = 256;
 template <int DV, typename TIn, typename TS, int NF>
-__global__ __launch_bounds__(kFoldThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ __launch_bounds__(kFoldThreads) __attribute__((amdgpu_waves_per_eu(DV > 64 ? 2 : 4, DV > 64 ? 2 : 4)))
 void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
                         int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
                         const TIn *__restrict__ v, const float *__restrict__ pend_k, const float *__restrict__ pend_v,
@@ -328,7 +332,8 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
     constexpr int CT = (NC + 15) / 16;               // column tiles
     constexpr int T = kMaxDecodeWindow;
     typedef Word<TS, 4> Wd;
-    __shared__ float sq[72], sk[T][72];
+    constexpr int KST = tok_stage<DV>();
+    __shared__ float sq[KST], sk[T][KST];
     __shared__ float sv[T][CT * 16];                 // [token][column], zero past d_V and for padding slots
     __shared__ float red[kFoldThreads / 64][CT * 16];
     const int bh = blockIdx.y;
@@ -357,8 +362,8 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
             }
         }
     }
-    for (int i = tid; i < T * 72; i += kFoldThreads) {
-        const int t = i / 72, c = i % 72;
+    for (int i = tid; i < T * KST; i += kFoldThreads) {
+        const int t = i / KST, c = i % KST;
         float x = 0.f;
         if (t < ntok && c < dk)
             x = t < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + t) * dk + c] : to_f32(k[(int64_t)bh * dk + c]);
@@ -376,7 +381,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
         }
         sv[t][c] = x;
     }
-    if (readout && tid < 72) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    if (readout && tid < KST) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
     __syncthreads();
 
     if (active) {
@@ -457,7 +462,7 @@ void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restric
     constexpr int TILE = kDecThreads * FPT;
     typedef Word<TS, FPT> Wd;
     typedef typename Wd::T WT;
-    __shared__ float sq[72];
+    __shared__ float sq[tok_stage<DV>()];
     __shared__ float red[kDecThreads / 64][NC];
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
@@ -486,7 +491,7 @@ void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restric
 #pragma unroll
         for (int r = RA; r < NC; ++r) sb[r - RA] = __builtin_nontemporal_load(row(f, r));
     }
-    if (tid < 72) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    if (tid < tok_stage<DV>()) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
     __syncthreads();
 
     float acc[NC];
@@ -547,7 +552,7 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, float *__restrict__ pend_k,
     float *__restrict__ pend_v, int npend) {
     constexpr int NC = DV + 1;
-    constexpr int G = 4;                        // partial-sum groups per column
+    constexpr int G = 4 * NC <= kFinishThreads ? 4 : 2;   // partial-sum groups per column
     static_assert(G * NC <= kFinishThreads, "one thread per (group, column)");
     static_assert(kFinishThreads % 16 == 0, "16 threads per token");
     __shared__ float part[G][NC];
@@ -645,7 +650,8 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
     const int64_t tiles = decode_blocks(idx, dec_fpt<TS>());
     const int tpw = read_tiles_per_block(bh, tiles);
     constexpr int NR = rows_per_group<DV>();
-    const int groups = split_rows(bh, tiles) ? (DV + 1 + NR - 1) / NR : 1;
+    // d_V = 128 always splits: a whole tile's 129 rows do not fit one lane's registers
+    const int groups = DV > 64 || split_rows(bh, tiles) ? (DV + 1 + NR - 1) / NR : 1;
     const dim3 grid((unsigned)(fold ? fold_blocks(idx) : mode == kDecodeRead && groups == 1 ? (tiles + tpw - 1) / tpw : tiles),
                     (unsigned)bh, (unsigned)(fold ? 1 : groups));
     const int nblk = (int)grid.x;
@@ -658,7 +664,7 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
             if (groups > 1)
                 hipLaunchKernelGGL((decode_rows_kernel<DV, TIn, TS, true>), grid, dim3(kDecThreads), 0, stream,
                                    idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
-            else
+            else if constexpr (DV <= 64)
                 hipLaunchKernelGGL((decode_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
                                    idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
             break;
@@ -668,7 +674,7 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
             if (groups > 1)
                 hipLaunchKernelGGL((decode_rows_kernel<DV, TIn, TS, false>), grid, dim3(kDecThreads), 0, stream,
                                    idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, nullptr, nullptr, partial);
-            else
+            else if constexpr (DV <= 64)
                 hipLaunchKernelGGL((decode_read_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
                                    idx->d_coef, S, idx->m_pad, idx->dk, qi, partial, tpw);
             break;
@@ -746,6 +752,7 @@ hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void
         case 16: return launch_decode_dv<16>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
         case 32: return launch_decode_dv<32>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
         case 64: return launch_decode_dv<64>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
+        case 128: return launch_decode_dv<128>(idx, st, q, k, v, out, in_dt, out_dt, mode, stream);
         default: return hipErrorInvalidValue;
     }
 }

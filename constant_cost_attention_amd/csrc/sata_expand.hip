@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint32_t *__restrict_
                                                      const float *__restrict__ coef, int dk,
                                                      int64_t m_pad, const TIn *__restrict__ x,
                                                      float *__restrict__ out, int side) {
-    __shared__ float sx[72];
+    __shared__ float sx[136];   // d_K <= 128 values, then the constant-1 and constant-0 slots
     const int64_t row = blockIdx.y;
     const int tid = threadIdx.x;
     if (tid < dk) sx[tid] = to_f32(x[row * dk + tid]);

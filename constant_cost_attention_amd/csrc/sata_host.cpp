@@ -34,7 +34,9 @@ sata_status fail_hip(hipError_t e, const char *what) {
     return fail(SATA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool supported_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64; }
+bool supported_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
+// The prefill's quad words hold the block index in four bits (d_K / 4 <= 16).
+constexpr int kMaxPrefillDim = 64;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -260,7 +262,9 @@ static sata_status check_dims(int d_k, int d_v, int P) {
     if (d_k <= 0 || d_v <= 0) return fail(SATA_ERR_INVALID, "head dims must be positive (d_k=%d, d_v=%d)", d_k, d_v);
     if (P < 1) return fail(SATA_ERR_INVALID, "P must be >= 1 (got %d)", P);
     if (!supported_dim(d_k) || !supported_dim(d_v))
-        return fail(SATA_ERR_UNSUPPORTED, "head dims must be 8, 16, 32 or 64 (d_k=%d, d_v=%d)", d_k, d_v);
+        return fail(SATA_ERR_UNSUPPORTED, "head dims must be 8, 16, 32, 64 or 128 (d_k=%d, d_v=%d)", d_k, d_v);
+    if ((d_k == 128) != (d_v == 128))
+        return fail(SATA_ERR_UNSUPPORTED, "d_k = 128 goes with d_v = 128 only (d_k=%d, d_v=%d)", d_k, d_v);
     if (P > sata::kMaxOrder + 1) return fail(SATA_ERR_UNSUPPORTED, "P <= %d supported (got %d)", sata::kMaxOrder + 1, P);
     return SATA_OK;
 }
@@ -284,7 +288,7 @@ int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *
     if (check_dims(d_k, d_k, P) != SATA_OK) return -1;
     std::vector<sata::QuadRec> quads;
     std::vector<uint32_t> flags;
-    build_quads(d_k, P, quads, flags);
+    if (d_k <= kMaxPrefillDim) build_quads(d_k, P, quads, flags);   // no prefill (and no quads) above
     const int64_t nq = (int64_t)quads.size();
     for (int64_t i = 0; i < nq && i < cap; ++i) {
         if (w0) w0[i] = quads[(size_t)i].w0;
@@ -322,7 +326,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     coef.resize((size_t)idx->m_tab, 0.f);
     std::vector<sata::QuadRec> quads;
     std::vector<uint32_t> qflags;
-    build_quads(d_k, P, quads, qflags);
+    if (d_k <= kMaxPrefillDim) build_quads(d_k, P, quads, qflags);   // prefill only
     idx->nq = (int64_t)quads.size();
     idx->nq_tab = round_up(std::max<int64_t>(idx->nq, 1), sata::kQuadPad);   // never empty (P = 1 has no quads)
     {
@@ -499,6 +503,9 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     if (chunk != 0 && chunk != 64 && chunk != 128)
         return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
     if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
+    if (idx->dk > kMaxPrefillDim)
+        return fail(SATA_ERR_UNSUPPORTED, "prefill supports d_k <= %d (got %d); decode supports 128", kMaxPrefillDim,
+                    idx->dk);
     if (st->dtype != SATA_F32)
         return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 state with sata_state_convert)");
     if (n == 0) return SATA_OK;
@@ -534,6 +541,8 @@ sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, c
     if (chunk != 0 && chunk != 64 && chunk != 128)
         return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
     if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "the backward pass needs d_k == d_v");
+    if (idx->dk > kMaxPrefillDim)
+        return fail(SATA_ERR_UNSUPPORTED, "the backward pass supports d_k <= %d (got %d)", kMaxPrefillDim, idx->dk);
     const int64_t bh = (int64_t)batch * heads;
     if (bh > 65535) return fail(SATA_ERR_UNSUPPORTED, "batch*heads <= 65535 supported (got %lld)", (long long)bh);
     if (n == 0) return SATA_OK;

@@ -37,10 +37,13 @@
  *     row-major, 16-byte aligned; `out` must not overlap q, k or v.  The
  *     library owns index and state memory (hipMalloc) and frees it in the
  *     *_free calls.
- *   - Supported shapes: d_K, d_V in {8, 16, 32, 64} with d_K == d_V for
- *     prefill; 1 <= P <= 5.  Other values return SATA_ERR_UNSUPPORTED.  The
- *     state grows as C(d_K+P-1, P-1) (d_V+1) fp32 values per head: at
- *     d_K = 64, 12.5 MB for P = 4 and 212 MB for P = 5.
+ *   - Supported shapes: d_K, d_V in {8, 16, 32, 64}, or d_K = d_V = 128;
+ *     1 <= P <= 5.  Prefill and its backward need d_K == d_V <= 64 (their
+ *     feature blocking holds the block index in four bits); d_K = 128 runs
+ *     the decode step, decode windows, bf16 states and the expansion.  Other
+ *     values return SATA_ERR_UNSUPPORTED.  The state grows as
+ *     C(d_K+P-1, P-1) (d_V+1) fp32 values per head: at d_K = 64, 12.5 MB for
+ *     P = 4 and 212 MB for P = 5; at d_K = 128 and P = 4, 189 MB.
  */
 #ifndef SATA_H
 #define SATA_H

@@ -57,6 +57,9 @@ def test_argument_checks_before_any_device_call(lib):
     assert lib.sata_build_index(12, 12, 4, ctypes.byref(out)) == sata.SATA_ERR_UNSUPPORTED
     assert lib.sata_build_index(64, 64, 6, ctypes.byref(out)) == sata.SATA_ERR_UNSUPPORTED
     assert b"P <=" in lib.sata_last_error()
+    assert lib.sata_build_index(64, 128, 4, ctypes.byref(out)) == sata.SATA_ERR_UNSUPPORTED
+    assert lib.sata_build_index(128, 64, 4, ctypes.byref(out)) == sata.SATA_ERR_UNSUPPORTED
+    assert b"128" in lib.sata_last_error()
     assert lib.sata_index_features(None) == -1
     assert lib.sata_prefill(None, None, None, None, None, None, 16, 0, 0, 0, None) == sata.SATA_ERR_INVALID
     assert lib.sata_decode_step(None, None, None, None, None, None, 0, 0, None) == sata.SATA_ERR_INVALID
@@ -73,7 +76,7 @@ def test_argument_checks_before_any_device_call(lib):
     lib.sata_state_free(None)
 
 
-@pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2), (8, 5), (16, 5)])
+@pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2), (8, 5), (16, 5), (128, 3)])
 def test_feature_tables_match_bruteforce_basis(oracle, d, P):
     """Host index builder vs oracle: same sorted tuples in the same order (orders
     0..P-1, lexicographic within an order), and readout weight
@@ -105,6 +108,8 @@ def test_describe_rejects_what_build_rejects(lib):
     assert lib.sata_describe_features(64, 6, None, None, 0) == -1
     assert lib.sata_describe_features(64, 4, None, None, 0) == 47905
     assert lib.sata_describe_features(64, 5, None, None, 0) == 814385
+    assert lib.sata_describe_features(128, 4, None, None, 0) == 366145
+    assert lib.sata_describe_quads(128, 4, None, None, None, 0) == 0          # no prefill above d_K = 64
 
 
 def test_binding_rejects_cpu_tensors():

@@ -1,0 +1,120 @@
+"""Head size 128 (d_K = d_V = 128) on the decode side: the table-driven
+kernels (expansion, the row-split decode step and read kernel, the matrix-core
+fold, the finish kernel) against the oracle, from an empty state; prefill and
+backward refuse d_K = 128 (the prefill's quad words hold the block index in
+four bits)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from sata_testutil import TOL_F32, decode, dev_all, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+@pytest.fixture(scope="module")
+def sata():
+    from constant_cost_attention_amd import sata as s
+    s.load()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return s
+
+
+def _steps(idx, st, x, lo, hi):
+    q, k, v = dev_all(x)
+    outs = [decode(idx, st, q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous())
+            for t in range(lo, hi)]
+    return torch.stack(outs, dim=2).cpu().numpy()
+
+
+def test_expand_d128_matches_bruteforce_basis(sata, oracle):
+    P = 3
+    say("expand d=128 P=3")
+    idx = sata.Index(D, D, P)
+    x = si.draw_qkv((1,), 5, D, D, 8800, "f32").q[0]
+    xt = torch.from_numpy(x).cuda()
+    outs = []
+    for side in (0, 1):
+        o = torch.zeros((5, idx.m_pad), dtype=torch.float32, device="cuda")
+        sata.sata_expand_features(idx, xt, o, side)
+        outs.append(o.cpu().numpy().astype(np.float64))
+    xd = x.astype(np.float64)
+    f = 0
+    for p in range(P):
+        tup, cnt = oracle.basis_bruteforce(D, p)
+        mono = np.prod(xd[:, tup], axis=-1) if p else np.ones((5, 1))
+        w = cnt / (math.factorial(p) * math.sqrt(D) ** p)
+        g = len(cnt)
+        np.testing.assert_allclose(outs[0][:, f:f + g], mono, rtol=4e-7, atol=1e-30)
+        np.testing.assert_allclose(outs[1][:, f:f + g], mono * w, rtol=8e-7, atol=1e-30)
+        f += g
+    assert f == idx.m
+    idx.free()
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+def test_decode_d128_from_empty_every_row(sata, oracle, P):
+    n, heads = 20, 2
+    x = si.draw_qkv((1, heads), n, D, D, 8900 + P, "f32")
+    idx = sata.Index(D, D, P)
+    say("decode d=128 P=%d, %d steps from empty" % (P, n))
+    st = sata.State(idx, 1, heads)
+    o = _steps(idx, st, x, 0, n)
+    err = rel_err(o, oracle.taylor_attention(x.q, x.k, x.v, P))
+    say("  err %.3e" % err)
+    assert err <= TOL_F32
+    st.free()
+    idx.free()
+
+
+@pytest.mark.parametrize("window,n", [(4, 23), (64, 70)])
+def test_decode_d128_window(sata, oracle, window, n):
+    P, heads = 4, 2
+    x = si.draw_qkv((1, heads), n, D, D, 9000 + window, "f32")
+    idx = sata.Index(D, D, P)
+    say("decode d=128 window %d, %d steps" % (window, n))
+    st = sata.State(idx, 1, heads)
+    sata.sata_state_set_decode_window(st, window)
+    o = _steps(idx, st, x, 0, n)
+    err = rel_err(o, oracle.taylor_attention(x.q, x.k, x.v, P))
+    say("  err %.3e" % err)
+    assert err <= TOL_F32
+    st.free()
+    idx.free()
+
+
+def test_decode_d128_bf16_state_matches_emulation(sata, oracle):
+    P, n, heads = 3, 30, 2
+    x = si.draw_qkv((1, heads), n, D, D, 9100, "f32")
+    idx = sata.Index(D, D, P)
+    say("decode d=128 on a bf16 state, %d steps" % n)
+    st = sata.State(idx, 1, heads, dtype=torch.bfloat16)
+    o = _steps(idx, st, x, 0, n)
+    ref = oracle.bf16_state_decode(x.q, x.k, x.v, P, 0)
+    exact = oracle.taylor_attention(x.q, x.k, x.v, P)
+    err, drift = rel_err(o, ref), rel_err(ref, exact)
+    say("  err vs emulation %.3e, drift %.3e" % (err, drift))
+    assert err <= 1e-3 + 1e-2 * drift
+    st.free()
+    idx.free()
+
+
+def test_d128_prefill_and_backward_refused(sata):
+    idx = sata.Index(D, D, 3)
+    st = sata.State(idx, 1, 1)
+    q = torch.zeros((1, 1, 8, D), device="cuda")
+    with pytest.raises(sata.SataError) as e:
+        sata.sata_prefill(idx, st, q, q, q, torch.zeros_like(q))
+    assert e.value.status == sata.SATA_ERR_UNSUPPORTED
+    g = [torch.zeros_like(q) for _ in range(3)]
+    with pytest.raises(sata.SataError) as e:
+        sata.sata_prefill_backward(idx, q, q, q, q, g[0], g[1], g[2])
+    assert e.value.status == sata.SATA_ERR_UNSUPPORTED
+    assert float(sata.state_tensor(st).abs().max()) == 0.0          # refused calls leave the state alone
+    st.free()
+    idx.free()
