@@ -471,15 +471,40 @@ def d128_section(sata):
     idx = sata.Index(wl.d_k, wl.d_v, wl.P)
     st = sata.State(idx, wl.batch, wl.heads)
     ms, kern = time_decode(sata, idx, st, wl, 64, 8, wl.seed + 3)
-    st.free()
-    idx.free()
-    torch.cuda.empty_cache()
     nbytes = decode_bytes(wl)
     kms = kern["decode_stream"][0]
     ach = nbytes / (kms * 1e-3) / 1e9
-    return {"workload": "%d x %d heads, d=%d, P=%d" % (wl.batch, wl.heads, wl.d_k, wl.P),
-            "value": wl.batch / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "stream_kernel_ms": kms,
-            "bytes_per_step": nbytes, "achieved_gbs": ach, "frac": ach / PEAK_HBM_GBS}
+    res = {"workload": "%d x %d heads, d=%d, P=%d" % (wl.batch, wl.heads, wl.d_k, wl.P),
+           "value": wl.batch / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "stream_kernel_ms": kms,
+           "bytes_per_step": nbytes, "achieved_gbs": ach, "frac": ach / PEAK_HBM_GBS}
+    # block prefill: blocks of 64 tokens, each reading the state once and folding into it
+    # (a read and a write): three passes over the state per block
+    n = 4096
+    q, k, v = si.draw_qkv_device((wl.batch, wl.heads), n, wl.d_k, wl.d_v, wl.seed + 4, "bf16")
+    out = torch.empty(v.shape, dtype=torch.bfloat16, device="cuda")
+    sata.sata_state_reset(st)
+    sata.sata_prefill(idx, st, q, k, v, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        sata.sata_state_reset(st)
+        sata.sata_prefill(idx, st, q, k, v, out)
+    e1.record()
+    torch.cuda.synchronize()
+    pms = e0.elapsed_time(e1) / reps
+    state_bytes = 4.0 * features(wl.d_k, wl.P) * (wl.d_v + 1) * wl.batch * wl.heads
+    pbytes = 3 * state_bytes * ((n + 63) // 64)
+    res["prefill"] = {"workload": "%d x %d heads x %d tokens, d=%d, P=%d, bf16 in" % (wl.batch, wl.heads, n, wl.d_k, wl.P),
+                      "ms_per_call": pms, "value": wl.batch * n / (pms * 1e-3), "unit": "tokens/s",
+                      "state_bytes_per_call": pbytes, "achieved_gbs": pbytes / (pms * 1e-3) / 1e9,
+                      "frac": pbytes / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del q, k, v, out
+    st.free()
+    idx.free()
+    torch.cuda.empty_cache()
+    return res
 
 
 # ------------------------------------------------------------------ oracle on the host
@@ -719,8 +744,10 @@ def main():
                                   o5["decode"]["ms_per_step"], o5["decode"]["achieved_gbs"], 100 * o5["decode"]["frac"]))
         result["order5"] = o5
         dd = d128_section(sata)
-        log("decode, %s: %.3f ms/step, stream %.0f GB/s (%.1f%% of peak)"
-            % (dd["workload"], dd["ms_per_step"], dd["achieved_gbs"], 100 * dd["frac"]))
+        log("decode, %s: %.3f ms/step, stream %.0f GB/s (%.1f%% of peak); block prefill %s: %.2f ms, %.3e tok/s, "
+            "%.0f GB/s of state passes" % (dd["workload"], dd["ms_per_step"], dd["achieved_gbs"], 100 * dd["frac"],
+                                           dd["prefill"]["workload"], dd["prefill"]["ms_per_call"],
+                                           dd["prefill"]["value"], dd["prefill"]["achieved_gbs"]))
         result["d128_decode"] = dd
 
     if not args.no_backward:

@@ -757,4 +757,223 @@ hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void
     }
 }
 
+// ---- Prefill in blocks through the state in HBM (head sizes the scan kernels do not take) ----
+// A sequence runs in blocks of up to kMaxDecodeWindow tokens.  The block's queries are read
+// out against the state as it stands before the block (one pass over the state for all of
+// them), each query adds the direct Taylor-weighted terms w(q.k_j / sqrt(d_K)) [v_j, 1] of the
+// block's tokens up to itself -- what those tokens contribute through the state's orders
+// [hotdry, "Core insight of symmetric tensor decomposition"] -- and the fold then adds the
+// block's tokens to the state.  Per block the state crosses HBM three times (a read, then the
+// fold's read and write), so this path is bound by HBM; it serves d_K = 128.
+
+// fp32 copies of a block's rows: q into qs, k and v into the pending-token buffers, each laid
+// out [bh][kMaxDecodeWindow][d] as the fold reads them.  Grid (T, B*H).
+template <typename TIn>
+__global__ __launch_bounds__(128) void block_stage_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                          const TIn *__restrict__ v, int64_t n, int64_t t0, int dk,
+                                                          int dv, float *__restrict__ qs, float *__restrict__ pk,
+                                                          float *__restrict__ pv) {
+    const int64_t bh = blockIdx.y;
+    const int t = blockIdx.x;
+    const int64_t src = bh * n + t0 + t, dst = bh * kMaxDecodeWindow + t;
+    for (int c = threadIdx.x; c < dk; c += 128) {
+        qs[dst * dk + c] = to_f32(q[src * dk + c]);
+        pk[dst * dk + c] = to_f32(k[src * dk + c]);
+    }
+    for (int c = threadIdx.x; c < dv; c += 128) pv[dst * dv + c] = to_f32(v[src * dv + c]);
+}
+
+// Readout of T queries against the fp32 state, without an update, on the matrix cores: the
+// readout of the block is the contraction Y[t][c] = sum_f phi_f(q_t) S[c][f] over the features.
+// The layout is the fold's: a wavefront holds 64 features (4 groups of 16) of every row, lane
+// l the state value S[16 ct + l % 16][fw + 16 g + 4 (l / 16) + r], which is the B element of
+// v_mfma_f32_16x16x4f32 for K index l / 16 and column l % 16 when the step's four K indices are
+// the features fw + 16 g + 4 k + r.  The A element of lane l is the query-side monomial of
+// that feature for query l % 16 of the tile, formed once per (query tile, g, r) and used by
+// every column tile.  fp32 throughout, so results match the decode readout up to rounding.
+// A query tile's per-wavefront sums meet in LDS; one partial row per (workgroup, query):
+// partial [bh][workgroups][64][d_V+1].  Grid (fold workgroups, B*H).
+template <int DV>
+__global__ __launch_bounds__(kFoldThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void block_readout_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef,
+                          const float *__restrict__ state, int64_t m_pad, int dk, const float *__restrict__ qs,
+                          int T, float *__restrict__ partial) {
+    constexpr int NC = DV + 1;
+    constexpr int CT = (NC + 15) / 16;
+    constexpr int KST = tok_stage<DV>();
+    constexpr int NWV = kFoldThreads / 64;
+    __shared__ float sq[kMaxDecodeWindow][KST];
+    __shared__ float red[NWV][16][CT * 16];
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int64_t fw = ((int64_t)blockIdx.x * NWV + wave) * 64;   // the wavefront's first feature
+    const bool active = fw < m_pad;                                 // m_pad is a multiple of 64
+    const float *Sb = state + (int64_t)bh * NC * m_pad;
+    f32x4 sv[4][CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int c = ct * 16 + l16;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            sv[g][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (active && c < NC) {
+                const float4 w = *reinterpret_cast<const float4 *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg);
+                sv[g][ct] = f32x4{w.x, w.y, w.z, w.w};
+            }
+        }
+    }
+    for (int i = tid; i < kMaxDecodeWindow * KST; i += kFoldThreads) {
+        const int t = i / KST, c = i % KST;
+        float x = 0.f;
+        if (t < T) x = c < dk ? qs[((int64_t)bh * kMaxDecodeWindow + t) * dk + c] : (c == dk ? 1.f : 0.f);
+        sq[t][c] = x;
+    }
+    __syncthreads();
+    for (int qt = 0; qt < (T + 15) / 16; ++qt) {
+        const float *qrow = sq[16 * qt + l16];
+        f32x4 Y[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            // the lane's four features of group g (tables re-read per query tile: they stay in L2)
+            uint32_t tt[4];
+            float cc[4];
+            lane_tables<4>(active, tup, coef, active ? fw + 16 * g + 4 * lg : 0, tt, cc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = cc[r] * monomial(tt[r], qrow, 1);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Y[ct] = mfma_f32(a, sv[g][ct][r], Y[ct]);
+            }
+        }
+        // Y[ct][rr]: query 16 qt + 4 lg + rr, column 16 ct + l16, summed over the wave's features
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) red[wave][4 * lg + rr][16 * ct + l16] = Y[ct][rr];
+        __syncthreads();
+        for (int i = tid; i < 16 * NC; i += kFoldThreads) {
+            const int qi = i / NC, c = i % NC, t = 16 * qt + qi;
+            if (t < T) {
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < NWV; ++w) sum += red[w][qi][c];
+                partial[(((int64_t)bh * gridDim.x + blockIdx.x) * kMaxDecodeWindow + t) * NC + c] = sum;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Query t of the block: its partial rows (one per readout workgroup, some 1400 per head at
+// d_K = 128) added in a fixed order by G interleaved groups of threads per column, plus the
+// direct terms of the block's tokens j <= t, normalised.  Grid (T, B*H).
+constexpr int kBlockFinishThreads = 1024;
+template <int DV, typename TOut>
+__global__ __launch_bounds__(kBlockFinishThreads) void block_finish_kernel(
+    const float *__restrict__ partial, int nblk, const float *__restrict__ qs, const float *__restrict__ pk,
+    const float *__restrict__ pv, int dk, int P, int64_t n, int64_t t0, TOut *__restrict__ out) {
+    constexpr int NC = DV + 1;
+    constexpr int G = kBlockFinishThreads / NC;
+    __shared__ float part[G][NC];
+    __shared__ float y[NC];
+    __shared__ float wt[kMaxDecodeWindow];
+    const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const int ntok = t + 1;
+    if (tid < G * NC) {
+        const int c = tid % NC, g = tid / NC;
+        float s = 0.f;
+#pragma unroll 4
+        for (int b = g; b < nblk; b += G) s += partial[(((int64_t)bh * nblk + b) * kMaxDecodeWindow + t) * NC + c];
+        part[g][c] = s;
+    }
+    const float *qt = qs + ((int64_t)bh * kMaxDecodeWindow + t) * dk;
+    for (int j0 = 0; j0 < ntok; j0 += kBlockFinishThreads / 16) {
+        const int j = j0 + (tid >> 4), i = tid & 15;
+        float d = 0.f;
+        if (j < ntok)
+            for (int r = i; r < dk; r += 16) d += qt[r] * pk[((int64_t)bh * kMaxDecodeWindow + j) * dk + r];
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off, 16);
+        if (j < ntok && i == 0) {
+            const float xs = d * rsqrtf((float)dk);
+            float w = 0.f, term = 1.f;
+            for (int p = 0; p < P; ++p) {
+                w += term;
+                term = term * xs / (float)(p + 1);
+            }
+            wt[j] = w;
+        }
+    }
+    __syncthreads();
+    if (tid < NC) {
+        float s = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) s += part[g][tid];
+        for (int j = 0; j < ntok; ++j)
+            s += wt[j] * (tid == DV ? 1.f : pv[((int64_t)bh * kMaxDecodeWindow + j) * DV + tid]);
+        y[tid] = s;
+    }
+    __syncthreads();
+    if (tid < DV) out[((int64_t)bh * n + t0 + t) * DV + tid] = from_f32<TOut>(y[tid] / y[DV]);
+}
+
+int64_t block_prefill_workspace_bytes(const sata_index *idx, int64_t bh) {
+    const int64_t tiles = fold_blocks(idx);
+    return bh * tiles * kMaxDecodeWindow * (idx->dv + 1) * (int64_t)sizeof(float) +
+           bh * kMaxDecodeWindow * idx->dk * (int64_t)sizeof(float);
+}
+
+template <int DV, typename TIn, typename TOut>
+static hipError_t block_prefill_t(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
+                                  void *out, int64_t n, hipStream_t stream) {
+    const int64_t bh = (int64_t)st->batch * st->heads;
+    const int64_t tiles = fold_blocks(idx);
+    float *partial = static_cast<float *>(st->d_work);
+    float *qs = partial + bh * tiles * kMaxDecodeWindow * (DV + 1);
+    const TIn *qi = static_cast<const TIn *>(q), *ki = static_cast<const TIn *>(k), *vi = static_cast<const TIn *>(v);
+    for (int64_t t0 = 0; t0 < n; t0 += kMaxDecodeWindow) {
+        const int T = (int)std::min<int64_t>(kMaxDecodeWindow, n - t0);
+        hipLaunchKernelGGL((block_stage_kernel<TIn>), dim3((unsigned)T, (unsigned)bh), dim3(128), 0, stream, qi, ki,
+                           vi, n, t0, idx->dk, DV, qs, st->d_pend_k, st->d_pend_v);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        {
+            ProfScope ps(kProfScan, stream);
+            hipLaunchKernelGGL((block_readout_kernel<DV>), dim3((unsigned)tiles, (unsigned)bh), dim3(kFoldThreads), 0,
+                               stream, idx->d_tup, idx->d_coef,
+                               static_cast<const float *>(st->d_state), idx->m_pad, idx->dk, qs, T, partial);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        {
+            ProfScope ps(kProfCombine, stream);
+            hipLaunchKernelGGL((block_finish_kernel<DV, TOut>), dim3((unsigned)T, (unsigned)bh), dim3(kBlockFinishThreads),
+                               0, stream, partial, (int)tiles, qs, st->d_pend_k, st->d_pend_v, idx->dk, idx->P, n, t0,
+                               static_cast<TOut *>(out));
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        st->npend = T;                                   // the fold adds the block's staged tokens
+        e = launch_decode(idx, st, nullptr, nullptr, nullptr, nullptr, SATA_F32, SATA_F32, kDecodeFlush, stream);
+        st->npend = 0;
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_block_prefill(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
+                                void *out, int64_t n, sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream) {
+    if (idx->dv != 128 || st->dtype != SATA_F32) return hipErrorInvalidValue;
+    if (in_dt == SATA_F32 && out_dt == SATA_F32)
+        return block_prefill_t<128, float, float>(idx, st, q, k, v, out, n, stream);
+    if (in_dt == SATA_F32 && out_dt == SATA_BF16)
+        return block_prefill_t<128, float, bf16_t>(idx, st, q, k, v, out, n, stream);
+    if (in_dt == SATA_BF16 && out_dt == SATA_F32)
+        return block_prefill_t<128, bf16_t, float>(idx, st, q, k, v, out, n, stream);
+    return block_prefill_t<128, bf16_t, bf16_t>(idx, st, q, k, v, out, n, stream);
+}
+
 }  // namespace sata

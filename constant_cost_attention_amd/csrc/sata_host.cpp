@@ -122,6 +122,23 @@ sata_status flush_pending(sata_state *st, hipStream_t stream) {
     return SATA_OK;
 }
 
+// Allocates a state's pending-token buffers (kMaxDecodeWindow slots per head) on first use.
+sata_status ensure_pending(sata_state *st) {
+    if (st->d_pend_k) return SATA_OK;
+    const int64_t slots = (int64_t)st->batch * st->heads * kMaxDecodeWindow;
+    float *pk = nullptr, *pv = nullptr;
+    hipError_t e = hipMalloc(&pk, (size_t)(slots * st->idx->dk * sizeof(float)));
+    if (e == hipSuccess) e = hipMalloc(&pv, (size_t)(slots * st->idx->dv * sizeof(float)));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        if (pk) (void)hipFree(pk);
+        return fail(SATA_ERR_OOM, "pending-token buffers of %lld slots", (long long)slots);
+    }
+    st->d_pend_k = pk;
+    st->d_pend_v = pv;
+    return SATA_OK;
+}
+
 sata_status check_index_state(const sata_index *idx, const sata_state *st) {
     if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
     if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
@@ -503,9 +520,6 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     if (chunk != 0 && chunk != 64 && chunk != 128)
         return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
     if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
-    if (idx->dk > kMaxPrefillDim)
-        return fail(SATA_ERR_UNSUPPORTED, "prefill supports d_k <= %d (got %d); decode supports 128", kMaxPrefillDim,
-                    idx->dk);
     if (st->dtype != SATA_F32)
         return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 state with sata_state_convert)");
     if (n == 0) return SATA_OK;
@@ -517,6 +531,21 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     const int64_t nq = bh * n * idx->dk * in_b, nv = bh * n * idx->dv * in_b, no = bh * n * idx->dv * out_b;
     if (overlaps(out, no, q, nq) || overlaps(out, no, k, nq) || overlaps(out, no, v, nv))
         return fail(SATA_ERR_INVALID, "out overlaps q, k or v");
+    if (idx->dk > kMaxPrefillDim) {
+        // d_K = 128: blocks of up to kMaxDecodeWindow tokens through the state in HBM (the
+        // chunk length does not apply)
+        DeviceGuard g(st->device);
+        if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+        s = ensure_pending(st);
+        if (s != SATA_OK) return s;
+        s = ensure_work(st, std::max(sata::block_prefill_workspace_bytes(idx, bh), sata::decode_workspace_bytes(idx, bh)));
+        if (s != SATA_OK) return s;
+        s = flush_pending(st, (hipStream_t)stream);
+        if (s != SATA_OK) return s;
+        hipError_t e = sata::launch_block_prefill(idx, st, q, k, v, out, n, in_dt, out_dt, (hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "block prefill launch");
+        return SATA_OK;
+    }
     const sata::PrefillPlan plan = sata::plan_prefill(idx, bh, n, chunk, in_dt);
     if (!plan.ok) return fail(SATA_ERR_UNSUPPORTED, "no prefill plan for this configuration");
     DeviceGuard g(st->device);
@@ -613,18 +642,9 @@ sata_status sata_state_set_decode_window(sata_state *st, int window, void *strea
         return fail(SATA_ERR_INVALID, "window must be in [1, %d] (got %d)", kMaxDecodeWindow, window);
     DeviceGuard g(st->device);
     if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
-    if (window > 1 && !st->d_pend_k) {
-        const int64_t slots = (int64_t)st->batch * st->heads * kMaxDecodeWindow;
-        float *pk = nullptr, *pv = nullptr;
-        hipError_t e = hipMalloc(&pk, (size_t)(slots * st->idx->dk * sizeof(float)));
-        if (e == hipSuccess) e = hipMalloc(&pv, (size_t)(slots * st->idx->dv * sizeof(float)));
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            if (pk) (void)hipFree(pk);
-            return fail(SATA_ERR_OOM, "pending-token buffers of %lld slots", (long long)slots);
-        }
-        st->d_pend_k = pk;
-        st->d_pend_v = pv;
+    if (window > 1) {
+        sata_status sp = ensure_pending(st);
+        if (sp != SATA_OK) return sp;
     }
     sata_status s = flush_pending(st, (hipStream_t)stream);
     if (s != SATA_OK) return s;

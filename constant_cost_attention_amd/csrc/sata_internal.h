@@ -90,6 +90,12 @@ hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void
                          const void *v, void *out, sata_dtype in_dt, sata_dtype out_dt, DecodeMode mode,
                          hipStream_t stream);
 int64_t decode_workspace_bytes(const sata_index *idx, int64_t bh);
+// Prefill in blocks of up to kMaxDecodeWindow tokens through the state in HBM (d_K = d_V = 128,
+// fp32 state): needs the pending-token buffers and block_prefill_workspace_bytes of workspace;
+// the state must have no deferred tokens.
+int64_t block_prefill_workspace_bytes(const sata_index *idx, int64_t bh);
+hipError_t launch_block_prefill(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
+                                void *out, int64_t n, sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream);
 hipError_t launch_state_convert(const sata_state *src, sata_state *dst, hipStream_t stream);
 
 // Prefill plan: how the sequence is split into chunks, feature slices and

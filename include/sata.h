@@ -38,10 +38,11 @@
  *     library owns index and state memory (hipMalloc) and frees it in the
  *     *_free calls.
  *   - Supported shapes: d_K, d_V in {8, 16, 32, 64}, or d_K = d_V = 128;
- *     1 <= P <= 5.  Prefill and its backward need d_K == d_V <= 64 (their
- *     feature blocking holds the block index in four bits); d_K = 128 runs
- *     the decode step, decode windows, bf16 states and the expansion.  Other
- *     values return SATA_ERR_UNSUPPORTED.  The state grows as
+ *     1 <= P <= 5.  Prefill needs d_K == d_V; at d_K = 128 it runs in blocks
+ *     of 64 tokens through the state in HBM (slower than the chunked scan of
+ *     d_K <= 64, whose feature blocking holds the block index in four bits),
+ *     and the backward refuses it.  Other values return
+ *     SATA_ERR_UNSUPPORTED.  The state grows as
  *     C(d_K+P-1, P-1) (d_V+1) fp32 values per head: at d_K = 64, 12.5 MB for
  *     P = 4 and 212 MB for P = 5; at d_K = 128 and P = 4, 189 MB.
  */

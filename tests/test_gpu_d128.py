@@ -1,8 +1,8 @@
-"""Head size 128 (d_K = d_V = 128) on the decode side: the table-driven
-kernels (expansion, the row-split decode step and read kernel, the matrix-core
-fold, the finish kernel) against the oracle, from an empty state; prefill and
-backward refuse d_K = 128 (the prefill's quad words hold the block index in
-four bits)."""
+"""Head size 128 (d_K = d_V = 128): the table-driven kernels (expansion, the
+row-split decode step and read kernel, the matrix-core fold, the finish
+kernel) and the block prefill (blocks of up to 64 tokens read out against the
+state in HBM, direct terms inside the block, then folded in) against the
+oracle; the backward refuses d_K = 128."""
 import math
 
 import numpy as np
@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth_inputs as si
-from sata_testutil import TOL_F32, decode, dev_all, rel_err, say
+from sata_testutil import TOL_BF16, TOL_F32, decode, dev_all, prefill, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -104,17 +104,51 @@ def test_decode_d128_bf16_state_matches_emulation(sata, oracle):
     idx.free()
 
 
-def test_d128_prefill_and_backward_refused(sata):
+@pytest.mark.parametrize("P,dtype", [(4, "f32"), (2, "f32"), (4, "bf16")])
+def test_prefill_d128_every_row(sata, oracle, P, dtype):
+    n, heads = 150, 2                                    # blocks of 64, 64 and 22 tokens
+    x = si.draw_qkv((1, heads), n, D, D, 9200 + P, dtype)
+    idx = sata.Index(D, D, P)
+    say("prefill d=128 P=%d %s n=%d" % (P, dtype, n))
+    st = sata.State(idx, 1, heads)
+    q, k, v = dev_all(x)
+    o = prefill(idx, st, q, k, v).cpu().numpy()
+    err = rel_err(o, oracle.taylor_attention(x.q, x.k, x.v, P))
+    say("  err %.3e" % err)
+    assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    st.free()
+    idx.free()
+
+
+def test_prefill_d128_continued_by_decode_and_prefill(sata, oracle):
+    """prefill 70, decode 5 at window 4 (one token left pending), prefill 30
+    (folds it first), decode 3: every row against O1."""
+    P, heads, n1, t1, n2, t2 = 3, 2, 70, 5, 30, 3
+    n = n1 + t1 + n2 + t2
+    x = si.draw_qkv((1, heads), n, D, D, 9300, "f32")
+    idx = sata.Index(D, D, P)
+    q, k, v = dev_all(x)
+    sl = lambda a, lo, hi: a[:, :, lo:hi].contiguous()
+    say("prefill/decode interleaved d=128, n=%d" % n)
+    st = sata.State(idx, 1, heads)
+    outs = [prefill(idx, st, sl(q, 0, n1), sl(k, 0, n1), sl(v, 0, n1)).cpu().numpy()]
+    sata.sata_state_set_decode_window(st, 4)
+    outs.append(_steps(idx, st, x, n1, n1 + t1))
+    p0 = n1 + t1
+    outs.append(prefill(idx, st, sl(q, p0, p0 + n2), sl(k, p0, p0 + n2), sl(v, p0, p0 + n2)).cpu().numpy())
+    outs.append(_steps(idx, st, x, p0 + n2, n))
+    err = rel_err(np.concatenate(outs, axis=2), oracle.taylor_attention(x.q, x.k, x.v, P))
+    say("  err %.3e" % err)
+    assert err <= TOL_F32
+    st.free()
+    idx.free()
+
+
+def test_d128_backward_refused(sata):
     idx = sata.Index(D, D, 3)
-    st = sata.State(idx, 1, 1)
     q = torch.zeros((1, 1, 8, D), device="cuda")
-    with pytest.raises(sata.SataError) as e:
-        sata.sata_prefill(idx, st, q, q, q, torch.zeros_like(q))
-    assert e.value.status == sata.SATA_ERR_UNSUPPORTED
     g = [torch.zeros_like(q) for _ in range(3)]
     with pytest.raises(sata.SataError) as e:
         sata.sata_prefill_backward(idx, q, q, q, q, g[0], g[1], g[2])
     assert e.value.status == sata.SATA_ERR_UNSUPPORTED
-    assert float(sata.state_tensor(st).abs().max()) == 0.0          # refused calls leave the state alone
-    st.free()
     idx.free()
