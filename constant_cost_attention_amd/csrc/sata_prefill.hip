@@ -48,7 +48,7 @@
 namespace sata {
 
 constexpr int kNW = 4;                           // wavefronts per workgroup (default)
-constexpr int64_t kWorkCap = (int64_t)4 << 30;   // partial-sum workspace cap (bytes)
+constexpr int64_t kWorkCap = (int64_t)16 << 30;  // partial-sum workspace cap (bytes; 288 GB of HBM)
 
 template <int D, int DV, int C, int MT, int NW, typename TIn>
 struct ScanCfg {

@@ -150,3 +150,25 @@ def test_workload_prefill_d64_p5_bf16_sampled_rows(sata, oracle):
     assert err <= TOL_BF16
     st.free()
     idx.free()
+
+
+def test_prefill_in_two_segments_sampled_rows(sata, oracle):
+    """1 x 16 heads x 8192 tokens at d = 64, P = 5, bf16: the readout partials
+    (about 30 GB) exceed the 16 GB workspace cap, so the call runs as two
+    segments, the second continuing the state the first left; sampled rows of
+    every head against O1."""
+    d, heads, n = 64, 16, 8192
+    say("prefill P=5 d=64 1x%d heads n=%d (two segments)" % (heads, n))
+    x = si.draw_qkv((1, heads), n, d, d, 5900, "bf16")
+    idx = sata.Index(d, d, P)
+    st = sata.State(idx, 1, heads)
+    q, k, v = dev_all(x)
+    o = prefill(idx, st, q, k, v, chunk=128).cpu().numpy()
+    rows = sample_rows(n, 128, 48, 13)
+    err = rel_err(o[:, :, rows], oracle.taylor_attention(x.q, x.k, x.v, P, rows=rows))
+    say("  err %.3e over %d rows x %d heads" % (err, len(rows), heads))
+    assert err <= TOL_BF16
+    del q, k, v
+    st.free()
+    idx.free()
+    torch.cuda.empty_cache()
