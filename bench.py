@@ -545,7 +545,7 @@ TRAFFIC_KERNELS = [
     (r"prefill_scan_ws_kernel<32, 32, 64, \d+, false>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
     (r"prefill_scan_ws_kernel<16, 16, 128, \d+, false>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
     (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
-    (r"decode_kernel<64, float, unsigned short>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_rows_kernel<64, float, unsigned short, true>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_fold_kernel<64, float, float, 3>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
 ]

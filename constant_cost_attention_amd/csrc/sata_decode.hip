@@ -624,11 +624,12 @@ static int read_tiles_per_block(int64_t bh, int64_t tiles) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(kReadTiles, bh * tiles / 1024));
 }
 // Whether the plain step and the read kernel split each tile's rows over
-// workgroups: when the whole-tile grid would hold fewer than 24 workgroups per
-// compute unit (256 of them).  Measured at d = 64, fp32 state: the split grid
-// is ahead up to 128 heads (by 30% at 8 heads, 1 to 3% at 128), the
-// whole-tile kernels from 256 heads (by 2 to 4%).
-static bool split_rows(int64_t bh, int64_t tiles) { return bh * tiles < 24 * 256; }
+// workgroups: when the whole-tile grid would hold fewer than 32 workgroups per
+// compute unit (256 of them).  Measured at d = 64: the split grid is ahead up
+// to 6144 tile workgroups (by 30% at 8 heads of fp32 state, 1 to 3% at 128
+// heads, 2.6% for 256 heads of bf16 state), the whole-tile kernels at 12032
+// (256 heads of fp32 state, by 2 to 4%).
+static bool split_rows(int64_t bh, int64_t tiles) { return bh * tiles < 32 * 256; }
 static int64_t fold_blocks(const sata_index *idx) {
     const int64_t per = kFoldThreads / 64 * 64;   // 64 features per wavefront
     return (idx->m_pad + per - 1) / per;

@@ -46,9 +46,9 @@ def _run(sata, idx, heads, x, n0, T, window, dtype):
 
 
 # (d, P, heads of the whole-tile run, state dtype): heads x feature tiles of
-# 1024 (fp32) or 2048 (bf16) features reach 6144 workgroups
-@pytest.mark.parametrize("d,P,big,dtype", [(64, 4, 136, "f32"), (32, 4, 880, "f32"), (16, 4, 6144, "f32"),
-                                           (8, 4, 6144, "f32"), (64, 4, 256, "bf16"), (64, 3, 2048, "f32")])
+# 1024 (fp32) or 2048 (bf16) features reach 8192 workgroups
+@pytest.mark.parametrize("d,P,big,dtype", [(64, 4, 176, "f32"), (32, 4, 1176, "f32"), (16, 4, 8192, "f32"),
+                                           (8, 4, 8192, "f32"), (64, 4, 344, "bf16"), (64, 3, 2736, "f32")])
 @pytest.mark.parametrize("window", [1, 4])
 def test_split_and_whole_tile_grids_agree(sata, oracle, d, P, big, dtype, window):
     small, n0, T = 6, 20, 6
