@@ -477,8 +477,8 @@ def d128_section(sata):
     res = {"workload": "%d x %d heads, d=%d, P=%d" % (wl.batch, wl.heads, wl.d_k, wl.P),
            "value": wl.batch / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "stream_kernel_ms": kms,
            "bytes_per_step": nbytes, "achieved_gbs": ach, "frac": ach / PEAK_HBM_GBS}
-    # block prefill: blocks of 64 tokens, each reading the state once and folding into it
-    # (a read and a write): three passes over the state per block
+    # block prefill: blocks of 64 tokens, each read out and folded into the state in one
+    # pass (a read and a write of the state per block)
     n = 4096
     q, k, v = si.draw_qkv_device((wl.batch, wl.heads), n, wl.d_k, wl.d_v, wl.seed + 4, "bf16")
     out = torch.empty(v.shape, dtype=torch.bfloat16, device="cuda")
@@ -495,7 +495,7 @@ def d128_section(sata):
     torch.cuda.synchronize()
     pms = e0.elapsed_time(e1) / reps
     state_bytes = 4.0 * features(wl.d_k, wl.P) * (wl.d_v + 1) * wl.batch * wl.heads
-    pbytes = 3 * state_bytes * ((n + 63) // 64)
+    pbytes = 2 * state_bytes * ((n + 63) // 64)
     res["prefill"] = {"workload": "%d x %d heads x %d tokens, d=%d, P=%d, bf16 in" % (wl.batch, wl.heads, n, wl.d_k, wl.P),
                       "ms_per_call": pms, "value": wl.batch * n / (pms * 1e-3), "unit": "tokens/s",
                       "state_bytes_per_call": pbytes, "achieved_gbs": pbytes / (pms * 1e-3) / 1e9,

@@ -322,12 +322,19 @@ void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restric
 // best by many wavefronts at once.
 // NF: index slots the monomials multiply (3 up to P = 4, 4 for P = 5).
 constexpr int kFoldThreads = 256;
-template <int DV, typename TIn, typename TS, int NF>
+// BLOCK (the block prefill): before the update, the block's nq queries (fp32 rows of qs,
+// [bh][kMaxDecodeWindow][d_K]) are read out against the state as loaded, on
+// v_mfma_f32_16x16x4f32: a lane's state value S[16 ct + l16][fw + 16 g + 4 lg + r] is the B
+// element for K index lg and column l16 of step (g, r), and the query-side monomial of that
+// feature for query l16 of the tile the A element, used by every column tile.  One partial
+// row per (workgroup, query): bpartial [bh][workgroups][kMaxDecodeWindow][d_V+1].
+template <int DV, typename TIn, typename TS, int NF, bool BLOCK = false>
 __global__ __launch_bounds__(kFoldThreads) __attribute__((amdgpu_waves_per_eu(DV > 64 ? 2 : 4, DV > 64 ? 2 : 4)))
 void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
                         int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
                         const TIn *__restrict__ v, const float *__restrict__ pend_k, const float *__restrict__ pend_v,
-                        int npend, float *__restrict__ partial) {
+                        int npend, float *__restrict__ partial, const float *__restrict__ qs, int nq,
+                        float *__restrict__ bpartial) {
     constexpr int NC = DV + 1;
     constexpr int CT = (NC + 15) / 16;               // column tiles
     constexpr int T = kMaxDecodeWindow;
@@ -360,6 +367,53 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
                 Wd::widen(*reinterpret_cast<const typename Wd::T *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg), x);
                 acc[g][ct] = f32x4{x[0], x[1], x[2], x[3]};
             }
+        }
+    }
+    if constexpr (BLOCK) {
+        // the block's queries in the key area, their readout sums in the value area
+        // ([waves][16 queries][columns] fills the [tokens][columns] area exactly)
+        static_assert(kFoldThreads / 64 * 16 == T, "readout sums fit the value area");
+        float(*redb)[16][CT * 16] = reinterpret_cast<float(*)[16][CT * 16]>(&sv[0][0]);
+        for (int i = tid; i < T * KST; i += kFoldThreads) {
+            const int t = i / KST, c = i % KST;
+            float x = 0.f;
+            if (t < nq) x = c < dk ? qs[((int64_t)bh * kMaxDecodeWindow + t) * dk + c] : (c == dk ? 1.f : 0.f);
+            sk[t][c] = x;
+        }
+        __syncthreads();
+        for (int qt = 0; qt < (nq + 15) / 16; ++qt) {
+            const float *qrow = sk[16 * qt + l16];
+            f32x4 Y[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) Y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint32_t tt[4];
+                float cc[4];
+                lane_tables<4>(active, tup, coef, active ? fw + 16 * g + 4 * lg : 0, tt, cc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = cc[r] * monomial_n<NF>(tt[r], qrow, 1);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Y[ct] = mfma_f32(a, acc[g][ct][r], Y[ct]);
+                }
+            }
+            // Y[ct][rr]: query 16 qt + 4 lg + rr, column 16 ct + l16
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) redb[wave][4 * lg + rr][16 * ct + l16] = Y[ct][rr];
+            __syncthreads();
+            for (int i = tid; i < 16 * NC; i += kFoldThreads) {
+                const int qi = i / NC, c = i % NC, t = 16 * qt + qi;
+                if (t < nq) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kFoldThreads / 64; ++w) sum += redb[w][qi][c];
+                    bpartial[(((int64_t)bh * gridDim.x + blockIdx.x) * kMaxDecodeWindow + t) * NC + c] = sum;
+                }
+            }
+            __syncthreads();
         }
     }
     for (int i = tid; i < T * KST; i += kFoldThreads) {
@@ -687,7 +741,7 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
             auto fold = idx->P >= 5 ? decode_fold_kernel<DV, TIn, TS, 4> : decode_fold_kernel<DV, TIn, TS, 3>;
             hipLaunchKernelGGL(fold, grid, dim3(kFoldThreads), 0, stream, idx->d_tup, idx->d_coef, S, idx->m_pad,
                                idx->dk, step ? qi : nullptr, step ? ki : nullptr, step ? vi : nullptr, st->d_pend_k,
-                               st->d_pend_v, st->npend, partial);
+                               st->d_pend_v, st->npend, partial, nullptr, 0, nullptr);
             break;
         }
     }
@@ -784,90 +838,6 @@ __global__ __launch_bounds__(128) void block_stage_kernel(const TIn *__restrict_
     for (int c = threadIdx.x; c < dv; c += 128) pv[dst * dv + c] = to_f32(v[src * dv + c]);
 }
 
-// Readout of T queries against the fp32 state, without an update, on the matrix cores: the
-// readout of the block is the contraction Y[t][c] = sum_f phi_f(q_t) S[c][f] over the features.
-// The layout is the fold's: a wavefront holds 64 features (4 groups of 16) of every row, lane
-// l the state value S[16 ct + l % 16][fw + 16 g + 4 (l / 16) + r], which is the B element of
-// v_mfma_f32_16x16x4f32 for K index l / 16 and column l % 16 when the step's four K indices are
-// the features fw + 16 g + 4 k + r.  The A element of lane l is the query-side monomial of
-// that feature for query l % 16 of the tile, formed once per (query tile, g, r) and used by
-// every column tile.  fp32 throughout, so results match the decode readout up to rounding.
-// A query tile's per-wavefront sums meet in LDS; one partial row per (workgroup, query):
-// partial [bh][workgroups][64][d_V+1].  Grid (fold workgroups, B*H).
-template <int DV>
-__global__ __launch_bounds__(kFoldThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void block_readout_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef,
-                          const float *__restrict__ state, int64_t m_pad, int dk, const float *__restrict__ qs,
-                          int T, float *__restrict__ partial) {
-    constexpr int NC = DV + 1;
-    constexpr int CT = (NC + 15) / 16;
-    constexpr int KST = tok_stage<DV>();
-    constexpr int NWV = kFoldThreads / 64;
-    __shared__ float sq[kMaxDecodeWindow][KST];
-    __shared__ float red[NWV][16][CT * 16];
-    const int bh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, lg = lane >> 4;
-    const int64_t fw = ((int64_t)blockIdx.x * NWV + wave) * 64;   // the wavefront's first feature
-    const bool active = fw < m_pad;                                 // m_pad is a multiple of 64
-    const float *Sb = state + (int64_t)bh * NC * m_pad;
-    f32x4 sv[4][CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        const int c = ct * 16 + l16;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            sv[g][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (active && c < NC) {
-                const float4 w = *reinterpret_cast<const float4 *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg);
-                sv[g][ct] = f32x4{w.x, w.y, w.z, w.w};
-            }
-        }
-    }
-    for (int i = tid; i < kMaxDecodeWindow * KST; i += kFoldThreads) {
-        const int t = i / KST, c = i % KST;
-        float x = 0.f;
-        if (t < T) x = c < dk ? qs[((int64_t)bh * kMaxDecodeWindow + t) * dk + c] : (c == dk ? 1.f : 0.f);
-        sq[t][c] = x;
-    }
-    __syncthreads();
-    for (int qt = 0; qt < (T + 15) / 16; ++qt) {
-        const float *qrow = sq[16 * qt + l16];
-        f32x4 Y[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) Y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            // the lane's four features of group g (tables re-read per query tile: they stay in L2)
-            uint32_t tt[4];
-            float cc[4];
-            lane_tables<4>(active, tup, coef, active ? fw + 16 * g + 4 * lg : 0, tt, cc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float a = cc[r] * monomial(tt[r], qrow, 1);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) Y[ct] = mfma_f32(a, sv[g][ct][r], Y[ct]);
-            }
-        }
-        // Y[ct][rr]: query 16 qt + 4 lg + rr, column 16 ct + l16, summed over the wave's features
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) red[wave][4 * lg + rr][16 * ct + l16] = Y[ct][rr];
-        __syncthreads();
-        for (int i = tid; i < 16 * NC; i += kFoldThreads) {
-            const int qi = i / NC, c = i % NC, t = 16 * qt + qi;
-            if (t < T) {
-                float sum = 0.f;
-#pragma unroll
-                for (int w = 0; w < NWV; ++w) sum += red[w][qi][c];
-                partial[(((int64_t)bh * gridDim.x + blockIdx.x) * kMaxDecodeWindow + t) * NC + c] = sum;
-            }
-        }
-        __syncthreads();
-    }
-}
-
 // Query t of the block: its partial rows (one per readout workgroup, some 1400 per head at
 // d_K = 128) added in a fixed order by G interleaved groups of threads per column, plus the
 // direct terms of the block's tokens j <= t, normalised.  Grid (T, B*H).
@@ -942,10 +912,13 @@ static hipError_t block_prefill_t(const sata_index *idx, sata_state *st, const v
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         {
-            ProfScope ps(kProfScan, stream);
-            hipLaunchKernelGGL((block_readout_kernel<DV>), dim3((unsigned)tiles, (unsigned)bh), dim3(kFoldThreads), 0,
-                               stream, idx->d_tup, idx->d_coef,
-                               static_cast<const float *>(st->d_state), idx->m_pad, idx->dk, qs, T, partial);
+            // the block's readout against the state before it, and the block's tokens added
+            ProfScope ps(kProfDecodeFold, stream);
+            auto fold = idx->P >= 5 ? decode_fold_kernel<DV, float, float, 4, true>
+                                    : decode_fold_kernel<DV, float, float, 3, true>;
+            hipLaunchKernelGGL(fold, dim3((unsigned)tiles, (unsigned)bh), dim3(kFoldThreads), 0, stream, idx->d_tup,
+                               idx->d_coef, static_cast<float *>(st->d_state), idx->m_pad, idx->dk, nullptr, nullptr,
+                               nullptr, st->d_pend_k, st->d_pend_v, T, nullptr, qs, T, partial);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -956,10 +929,6 @@ static hipError_t block_prefill_t(const sata_index *idx, sata_state *st, const v
                                static_cast<TOut *>(out));
         }
         e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        st->npend = T;                                   // the fold adds the block's staged tokens
-        e = launch_decode(idx, st, nullptr, nullptr, nullptr, nullptr, SATA_F32, SATA_F32, kDecodeFlush, stream);
-        st->npend = 0;
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
