@@ -547,7 +547,7 @@ TRAFFIC_KERNELS = [
     (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_rows_kernel<64, float, unsigned short, true>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
-    (r"decode_fold_kernel<64, float, float, 3>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_fold_kernel<64, float, float, 3, false>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
 
 
