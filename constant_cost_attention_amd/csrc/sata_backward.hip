@@ -165,9 +165,11 @@ struct Arena {
 struct TempState {
     sata_state st;
     int64_t max_heads = 0;
-    hipError_t make(Arena &ar, const sata_index *idx, int64_t heads, int64_t n, int chunk, sata_dtype in_dt) {
+    hipError_t make(Arena &ar, const sata_index *idx, int64_t heads, int64_t n, int chunk, sata_dtype in_dt,
+                    uint32_t *err) {
         const PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt);
         if (!plan.ok) return hipErrorInvalidValue;
+        st.d_err = err;
         st.idx = idx;
         st.batch = 1;
         st.device = idx->device;
@@ -207,9 +209,13 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     float *r = ar.get<float>(elems);
     TIn *rq = ar.get<TIn>(elems), *rk = ar.get<TIn>(elems), *rg = ar.get<TIn>(elems);
     if (ar.err != hipSuccess) return ar.err;
-    TempState top;
-    hipError_t e = top.make(ar, idx, bh, n, chunk, in_dt);
+    // error word of every pass's scan (a timed-out wait for a predecessor item), read back at the end
+    uint32_t *err = ar.get<uint32_t>(1);
+    if (ar.err != hipSuccess) return ar.err;
+    hipError_t e = launch_zero(reinterpret_cast<float *>(err), 1, s);
     if (e != hipSuccess) return e;
+    TempState top;
+    if ((e = top.make(ar, idx, bh, n, chunk, in_dt, err)) != hipSuccess) return e;
     // 1. forward: o and z
     if ((e = run_pass(top, bh, q, k, v, o, z, n, chunk, in_dt, false, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(bw_prep_g<TIn>, dim3(bw_grid(bh * n)), dim3(kBwThreads), 0, s,
@@ -236,7 +242,7 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
         float *gr = ar.get<float>(elems * cg);
         if (ar.err != hipSuccess) return ar.err;
         TempState low;
-        if ((e = low.make(ar, lower, bh * cg, n, chunk, in_dt)) != hipSuccess) return e;
+        if ((e = low.make(ar, lower, bh * cg, n, chunk, in_dt, err)) != hipSuccess) return e;
         const float sc = 1.0f / sqrtf((float)D);
         for (int pass = 0; pass < 2; ++pass) {
             const int kdk = pass == 0 ? 1 : 0;
@@ -257,7 +263,10 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     hipLaunchKernelGGL(bw_cast<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, acc_q, static_cast<TOut *>(dqv), elems);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // the temporaries are freed on return: let the stream drain first
-    return hipStreamSynchronize(s);
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    uint32_t bits = 0;
+    if ((e = hipMemcpy(&bits, err, sizeof(bits), hipMemcpyDeviceToHost)) != hipSuccess) return e;
+    return bits ? hipErrorLaunchTimeOut : hipSuccess;   // a scan's wait ran out: the gradients are invalid
 }
 
 }  // namespace

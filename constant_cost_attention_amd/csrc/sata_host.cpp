@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <map>
 #include <new>
 #include <string>
@@ -146,10 +147,33 @@ sata_status check_index_state(const sata_index *idx, const sata_state *st) {
     return SATA_OK;
 }
 
+// Reports (and clears) what the device has written to the state's error word so far.  The
+// word lives in pinned, device-mapped host memory, so reading it needs no synchronisation;
+// work still in flight may set it later.
+sata_status take_state_error(sata_state *st) {
+    if (!st->h_err) return SATA_OK;
+    const uint32_t bits = __atomic_exchange_n(st->h_err, 0u, __ATOMIC_ACQ_REL);
+    if (bits & sata::kErrScanWait)
+        return fail(SATA_ERR_HIP,
+                    "an earlier prefill on this state is invalid: a scan work item gave up waiting for the "
+                    "state of its predecessor (output and state of that call are wrong; reset the state)");
+    if (bits) return fail(SATA_ERR_HIP, "an earlier call on this state reported device error bits 0x%x", bits);
+    return SATA_OK;
+}
+
+std::atomic<int> g_debug_item_base{0};
+std::atomic<int> g_debug_spin_limit{sata::kScanSpinLimit};
+
 }  // namespace
 
 namespace sata {
 hipError_t launch_zero(float *p, int64_t count, hipStream_t stream);
+ScanDebug scan_debug() {
+    ScanDebug d;
+    d.item_base = g_debug_item_base.load(std::memory_order_relaxed);
+    d.spin_limit = g_debug_spin_limit.load(std::memory_order_relaxed);
+    return d;
+}
 }
 
 extern "C" {
@@ -452,8 +476,22 @@ sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, 
         delete st;
         return fail(SATA_ERR_OOM, "state allocation of %lld bytes failed", nbytes);
     }
+    e = hipHostMalloc(reinterpret_cast<void **>(&st->h_err), sizeof(uint32_t),
+                      hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) {
+        *st->h_err = 0u;
+        e = hipHostGetDevicePointer(reinterpret_cast<void **>(&st->d_err), st->h_err, 0);
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        if (st->h_err) (void)hipHostFree(st->h_err);
+        (void)hipFree(st->d_state);
+        delete st;
+        return fail(SATA_ERR_OOM, "pinned error word allocation failed");
+    }
     e = sata::launch_zero(static_cast<float *>(st->d_state), st->state_bytes / 4, (hipStream_t)stream);
     if (e != hipSuccess) {
+        (void)hipHostFree(st->h_err);
         (void)hipFree(st->d_state);
         delete st;
         return fail_hip(e, "state clear");
@@ -500,6 +538,7 @@ void sata_state_free(sata_state *st) {
     if (st->d_work) (void)hipFree(st->d_work);
     if (st->d_pend_k) (void)hipFree(st->d_pend_k);
     if (st->d_pend_v) (void)hipFree(st->d_pend_v);
+    if (st->h_err) (void)hipHostFree(st->h_err);
     delete st;
 }
 
@@ -522,6 +561,8 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
     if (st->dtype != SATA_F32)
         return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 state with sata_state_convert)");
+    s = take_state_error(st);
+    if (s != SATA_OK) return s;
     if (n == 0) return SATA_OK;
     if (!q || !k || !v || !out) return fail(SATA_ERR_INVALID, "q, k, v and out must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -546,12 +587,19 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
         if (e != hipSuccess) return fail_hip(e, "block prefill launch");
         return SATA_OK;
     }
-    const sata::PrefillPlan plan = sata::plan_prefill(idx, bh, n, chunk, in_dt);
-    if (!plan.ok) return fail(SATA_ERR_UNSUPPORTED, "no prefill plan for this configuration");
     DeviceGuard g(st->device);
     if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
-    s = ensure_work(st, plan.work_bytes);
-    if (s != SATA_OK) return s;
+    // Plan under the default workspace cap; if that workspace cannot be allocated, plan again
+    // under half the previous workspace (fewer chunks per segment), down to one chunk.
+    sata::PrefillPlan plan;
+    for (int64_t cap = sata::kWorkCap;;) {
+        plan = sata::plan_prefill(idx, bh, n, chunk, in_dt, cap);
+        if (!plan.ok) return fail(SATA_ERR_UNSUPPORTED, "no prefill plan for this configuration");
+        s = ensure_work(st, plan.work_bytes);
+        if (s == SATA_OK) break;
+        if (s != SATA_ERR_OOM || plan.seg_chunks <= 1) return s;
+        cap = plan.work_bytes / 2;
+    }
     s = flush_pending(st, (hipStream_t)stream);
     if (s != SATA_OK) return s;
     hipError_t e = sata::launch_prefill(idx, st, plan, q, k, v, out, n, in_dt, out_dt, (hipStream_t)stream);
@@ -603,6 +651,9 @@ sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, c
         (void)hipGetLastError();
         return fail(SATA_ERR_OOM, "backward temporaries could not be allocated");
     }
+    if (e == hipErrorLaunchTimeOut)
+        return fail(SATA_ERR_HIP, "backward: a prefill scan work item gave up waiting for the state of its "
+                                  "predecessor (the gradients are invalid)");
     if (e != hipSuccess) return fail_hip(e, "backward");
     return SATA_OK;
 }
@@ -616,6 +667,8 @@ sata_status sata_decode_step(const sata_index *idx, sata_state *st, const void *
     if (!q || !k || !v || !out) return fail(SATA_ERR_INVALID, "q, k, v and out must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(SATA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    s = take_state_error(st);
+    if (s != SATA_OK) return s;
     const int64_t bh = (int64_t)st->batch * st->heads;
     const int64_t in_b = dtype_bytes(in_dt), out_b = dtype_bytes(out_dt);
     const int64_t nq = bh * idx->dk * in_b, nv = bh * idx->dv * in_b, no = bh * idx->dv * out_b;
@@ -657,7 +710,56 @@ sata_status sata_state_flush(sata_state *st, void *stream) {
     if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
     DeviceGuard g(st->device);
     if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    sata_status s = take_state_error(st);
+    if (s != SATA_OK) return s;
     return flush_pending(st, (hipStream_t)stream);
+}
+
+sata_status sata_state_check(sata_state *st, void *stream) {
+    g_last_error.clear();
+    if (!st) return fail(SATA_ERR_INVALID, "state is NULL");
+    DeviceGuard g(st->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "stream synchronisation");
+    return take_state_error(st);
+}
+
+sata_status sata_debug_scan_faults(int item_base, int spin_limit) {
+    g_last_error.clear();
+    if (item_base < 0) return fail(SATA_ERR_INVALID, "item_base must be >= 0 (got %d)", item_base);
+    if (spin_limit < 0) return fail(SATA_ERR_INVALID, "spin_limit must be >= 0 (got %d)", spin_limit);
+    g_debug_item_base.store(item_base, std::memory_order_relaxed);
+    g_debug_spin_limit.store(spin_limit ? spin_limit : sata::kScanSpinLimit, std::memory_order_relaxed);
+    return SATA_OK;
+}
+
+int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t n, int chunk, int in_dt,
+                                   int64_t work_cap, int64_t *seg_chunks, int64_t *slices) {
+    g_last_error.clear();
+    if (check_dims(d_k, d_k, P) != SATA_OK) return -1;
+    if (d_k > kMaxPrefillDim || batch_heads < 1 || n < 1 || !valid_dtype(in_dt) || work_cap < 1 ||
+        (chunk != 0 && chunk != 64 && chunk != 128)) {
+        fail(SATA_ERR_INVALID, "no chunked prefill plan for these arguments");
+        return -1;
+    }
+    // the plan reads only the index's shape and quad count: a host-only stand-in suffices
+    sata_index idx;
+    idx.dk = idx.dv = d_k;
+    idx.P = P;
+    std::vector<sata::QuadRec> quads;
+    std::vector<uint32_t> flags;
+    build_quads(d_k, P, quads, flags);
+    idx.nq = (int64_t)quads.size();
+    idx.nq_tab = round_up(std::max<int64_t>(idx.nq, 1), sata::kQuadPad);
+    const sata::PrefillPlan plan = sata::plan_prefill(&idx, batch_heads, n, chunk, (sata_dtype)in_dt, work_cap);
+    if (!plan.ok) {
+        fail(SATA_ERR_UNSUPPORTED, "no prefill plan for this configuration");
+        return -1;
+    }
+    if (seg_chunks) *seg_chunks = plan.seg_chunks;
+    if (slices) *slices = plan.slices;
+    return plan.work_bytes;
 }
 
 sata_status sata_expand_features(const sata_index *idx, const void *x, void *out, int64_t rows, int side,

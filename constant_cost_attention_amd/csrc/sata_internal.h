@@ -55,6 +55,12 @@ struct sata_state {
     int npend = 0;               // deferred tokens not yet in d_state (host-side count, < window)
     float *d_pend_k = nullptr;   // [B*H][kMaxDecodeWindow][d_K] deferred keys (fp32)
     float *d_pend_v = nullptr;   // [B*H][kMaxDecodeWindow][d_V] deferred values (fp32)
+    // Error word of the asynchronous work on this state, in pinned host memory that the
+    // device writes (d_err is its device address): bit 0 = a prefill scan item gave up
+    // waiting for its predecessor's state (the output and state of that call are invalid).
+    // Checked, and cleared, by the next call on the state and by sata_state_check.
+    uint32_t *h_err = nullptr;
+    uint32_t *d_err = nullptr;
 };
 
 namespace sata {
@@ -118,7 +124,12 @@ struct PrefillPlan {
     bool raw = false;
     float *den_out = nullptr;
 };
-PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt);
+// Largest prefill workspace planned by default (bytes; the device has 288 GB of HBM).  Longer
+// calls run in segments of whole chunks; when the allocation fails, sata_prefill plans again
+// under half the cap, down to one chunk per segment.
+constexpr int64_t kWorkCap = (int64_t)16 << 30;
+PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt,
+                         int64_t work_cap = kWorkCap);
 // Backward pass of a causal prefill from a zero state (sata_backward.hip);
 // lower is the index with P - 1 orders (NULL when P == 1).  Synchronises the
 // stream before returning (it frees its temporaries).
@@ -145,6 +156,19 @@ struct ProfScope {
 };
 
 hipError_t launch_zero(float *p, int64_t count, hipStream_t stream);
+
+// Error bits a kernel may set in a state's error word.
+constexpr uint32_t kErrScanWait = 1u;
+// Bounded wait of the persistent scans for a predecessor's state: polls before giving up.
+constexpr int kScanSpinLimit = 1 << 24;
+// Fault injection for tests of the scans' error path (sata_debug_scan_faults): the persistent
+// scans start taking work items at item_base instead of 0 (so the items before it never run
+// and their successors' waits time out), and give up after spin_limit polls.
+struct ScanDebug {
+    int item_base = 0;
+    int spin_limit = kScanSpinLimit;
+};
+ScanDebug scan_debug();
 hipError_t launch_expand(const sata_index *idx, const void *x, void *out, int64_t rows, int side,
                          sata_dtype in_dt, hipStream_t stream);
 

@@ -48,7 +48,6 @@
 namespace sata {
 
 constexpr int kNW = 4;                           // wavefronts per workgroup (default)
-constexpr int64_t kWorkCap = (int64_t)16 << 30;  // partial-sum workspace cap (bytes; 288 GB of HBM)
 
 template <int D, int DV, int C, int MT, int NW, typename TIn>
 struct ScanCfg {
@@ -317,6 +316,20 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// A persistent scan's wait for the state its predecessor item leaves: poll the item's progress
+// flag (agent-scope acquire) until it reaches `need`, at most spin_limit times.  A wait that
+// runs out sets kErrScanWait in the state's error word (pinned host memory, system scope; NULL
+// for internal states whose caller checks otherwise) and returns, so the kernel still ends;
+// the call's output and state are then invalid and the host reports it.
+__device__ __forceinline__ void wait_predecessor(uint32_t *flag, uint32_t need, int spin_limit, uint32_t *err) {
+    for (int spin = 0; spin < spin_limit; ++spin) {
+        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= need) return;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= need) return;
+    if (err) __hip_atomic_fetch_or(err, kErrScanWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 template <int D, int DV, int C, int MT, int NW, typename TIn, bool TRIPLE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
@@ -325,7 +338,8 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
                          const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
                          int64_t n, int64_t tok0, int nchunk, typename PartialOf<TIn>::type *__restrict__ partial,
                          float qscale,
-                         int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync) {
+                         int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync,
+                         int item_base, int spin_limit, uint32_t *err) {
     using Cfg = ScanCfg<D, DV, C, MT, NW, TIn>;
     constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TPW = Cfg::TPW, NP = Cfg::NP, NPH = Cfg::NPH;
     constexpr int kThreads = Cfg::THREADS;
@@ -359,7 +373,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     for (int64_t pass = 0;; ++pass) {
     int64_t item;
     if constexpr (Cfg::PERSIST) {
-        if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u);
+        if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
         __syncthreads();
         item = s_item;
         __syncthreads();
@@ -377,12 +391,7 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     const int cbeg = u * sub_chunks;
     const int cend = cbeg + sub_chunks < nchunk ? cbeg + sub_chunks : nchunk;
     if (Cfg::PERSIST && u > 0) {
-        if (tid == 0) {
-            for (int spin = 0; spin < (1 << 24); ++spin) {
-                if (__hip_atomic_load(&sync[1 + rem], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)u) break;
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
+        if (tid == 0) wait_predecessor(sync + 1 + rem, (uint32_t)u, spin_limit, err);
         __syncthreads();   // thread 0's acquire invalidated the caches every wave reads through
     }
     const int64_t ps0 = (int64_t)slice * NP;          // first position of the slice
@@ -1070,7 +1079,8 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
                             float *__restrict__ state, int64_t m_pad,
                             const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
                             int64_t n, int64_t tok0, int nchunk, bf16_t *__restrict__ partial, float qscale,
-                            int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync) {
+                            int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync,
+                            int item_base, int spin_limit, uint32_t *err) {
     using Cfg = WsCfg<D, DV, C, MT>;
     constexpr int NC = Cfg::NC, NT = Cfg::NT, TT = Cfg::TT, TPW = Cfg::TPW, NP = Cfg::NP, NS = Cfg::NS;
     constexpr int KS = Cfg::KS, QS = Cfg::QS, VS = Cfg::VS, EPU = Cfg::EPU, UNITS = Cfg::UNITS, UPT = Cfg::UPT;
@@ -1093,7 +1103,7 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
     const int64_t nitems = per_sub * nsub;
 
     for (;;) {
-        if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u);
+        if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
         __syncthreads();
         int64_t item = s_item;
         __syncthreads();
@@ -1107,12 +1117,7 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
         const int cbeg = u * sub_chunks;
         const int cend = cbeg + sub_chunks < nchunk ? cbeg + sub_chunks : nchunk;
         if (u > 0) {   // the state of (u - 1, bh, slice) must have landed
-            if (tid == 0) {
-                for (int spin = 0; spin < (1 << 24); ++spin) {
-                    if (__hip_atomic_load(&sync[1 + rem], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)u) break;
-                    __builtin_amdgcn_s_sleep(2);
-                }
-            }
+            if (tid == 0) wait_predecessor(sync + 1 + rem, (uint32_t)u, spin_limit, err);
             __syncthreads();
         }
         const int64_t ps0 = (int64_t)slice * NP;
@@ -1764,7 +1769,7 @@ static ScanShape pick_shape(const sata_index *idx, int64_t bh, int chunk, sata_d
     return {kNW, 2, false};
 }
 
-PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt) {
+PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt, int64_t work_cap) {
     PrefillPlan p;
     p.chunk = chunk ? chunk : (idx->dk == 64 ? 128 : 64);
     if (p.chunk != 64 && p.chunk != 128) return p;
@@ -1778,11 +1783,13 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
     const int64_t pbytes = in_dt == SATA_BF16 ? 2 : 4;   // readout partials in the input's width
     const int64_t per_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * pbytes;
-    p.seg_chunks = per_chunk ? std::max<int64_t>(1, std::min<int64_t>(nchunks, kWorkCap / per_chunk)) : nchunks;
     // after the partial sums: the scan's work counter and one progress flag per (head, slice),
-    // then the order-0 chunk sums and their prefixes for the whole call
-    p.sync_off = (p.seg_chunks * per_chunk + 255) / 256 * 256;
+    // then the order-0 chunk sums and their prefixes for the whole call (not segmented)
     p.sync_words = (1 + bh * p.slices + 3) / 4 * 4;
+    const int64_t fixed = 512 + p.sync_words * 4 + 2 * bh * std::max<int64_t>(nchunks, 1) * (idx->dv + 1) * (int64_t)sizeof(float);
+    const int64_t room = std::max<int64_t>(work_cap - fixed, 0);
+    p.seg_chunks = per_chunk ? std::max<int64_t>(1, std::min<int64_t>(nchunks, room / per_chunk)) : nchunks;
+    p.sync_off = (p.seg_chunks * per_chunk + 255) / 256 * 256;
     p.o0_off = (p.sync_off + p.sync_words * 4 + 255) / 256 * 256;
     p.work_bytes = p.o0_off + 2 * bh * std::max<int64_t>(nchunks, 1) * (idx->dv + 1) * (int64_t)sizeof(float);
     p.ok = (int64_t)p.slices * np_slice * 4 <= idx->nq_tab;
@@ -1833,6 +1840,7 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     if (e != hipSuccess) return e;
     const int64_t resident = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     const int64_t items0 = bh * plan.slices;
+    const ScanDebug dbg = scan_debug();
     // order 0: chunk sums of [v, 1], their prefixes from the state's entries, and those entries' update
     float *o0sums = reinterpret_cast<float *>(static_cast<char *>(st->d_work) + plan.o0_off);
     float *o0pre = o0sums + bh * nchunks * (D + 1);
@@ -1863,7 +1871,8 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
                                idx->d_qw0, idx->d_qcidx, reinterpret_cast<const float4 *>(idx->d_qcoef),
                                idx->d_qflags, static_cast<float *>(st->d_state), idx->m_pad, static_cast<const TIn *>(q),
                                static_cast<const TIn *>(k), static_cast<const TIn *>(v), n, tok0, nseg,
-                               partial, ta.scale, plan.slices, bh, nsub, sub_chunks, sync);
+                               partial, ta.scale, plan.slices, bh, nsub, sub_chunks, sync, dbg.item_base,
+                               dbg.spin_limit, st->d_err);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;

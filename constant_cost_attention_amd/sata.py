@@ -25,11 +25,12 @@ SATA_F32, SATA_BF16 = 0, 1
 _EXPORTS = (
     "sata_build_index", "sata_index_free", "sata_index_features", "sata_index_info",
     "sata_state_alloc", "sata_state_alloc_dtype", "sata_state_convert", "sata_state_set_decode_window",
-    "sata_state_flush", "sata_state_reset", "sata_state_free",
+    "sata_state_flush", "sata_state_check", "sata_state_reset", "sata_state_free",
     "sata_state_data",
     "sata_prefill", "sata_prefill_backward", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
+    "sata_describe_prefill_plan", "sata_debug_scan_faults",
 )
 
 _lib = None
@@ -73,6 +74,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_state_convert.argtypes = [vp, vp, vp]
     lib.sata_state_set_decode_window.argtypes = [vp, cint, vp]
     lib.sata_state_flush.argtypes = [vp, vp]
+    lib.sata_state_check.argtypes = [vp, vp]
+    lib.sata_debug_scan_faults.argtypes = [cint, cint]
+    lib.sata_describe_prefill_plan.argtypes = [cint, cint, i64, i64, cint, cint, i64, ctypes.POINTER(i64),
+                                               ctypes.POINTER(i64)]
+    lib.sata_describe_prefill_plan.restype = i64
     lib.sata_state_reset.argtypes = [vp, vp]
     lib.sata_state_free.argtypes = [vp]
     lib.sata_state_free.restype = None
@@ -96,7 +102,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_profile_kernel_name.argtypes = [cint]
     lib.sata_profile_kernel_name.restype = ctypes.c_char_p
     for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_alloc_dtype",
-                 "sata_state_convert", "sata_state_set_decode_window", "sata_state_flush", "sata_state_reset",
+                 "sata_state_convert", "sata_state_set_decode_window", "sata_state_flush", "sata_state_check",
+                 "sata_debug_scan_faults", "sata_state_reset",
                  "sata_state_data", "sata_prefill", "sata_prefill_backward", "sata_decode_step", "sata_expand_features"):
         getattr(lib, name).restype = cint
     _lib = lib
@@ -233,6 +240,29 @@ def sata_state_flush(state: State, stream=None):
     _check(load().sata_state_flush(state.ptr, _stream(stream)), "sata_state_flush")
 
 
+def sata_state_check(state: State, stream=None):
+    """Synchronise the stream; raise SataError(SATA_ERR_HIP) if asynchronous work on the state
+    recorded a failure (a prefill scan item that gave up waiting for its predecessor)."""
+    _check(load().sata_state_check(state.ptr, _stream(stream)), "sata_state_check")
+
+
+def sata_debug_scan_faults(item_base: int = 0, spin_limit: int = 0):
+    """Fault injection for tests of the scan's error path; (0, 0) restores the defaults."""
+    _check(load().sata_debug_scan_faults(int(item_base), int(spin_limit)), "sata_debug_scan_faults")
+
+
+def sata_describe_prefill_plan(d_k: int, P: int, batch_heads: int, n: int, chunk: int = 0, in_dt: int = SATA_BF16,
+                               work_cap: int = 16 << 30) -> dict:
+    """Host-only: workspace bytes, chunks per segment and slices per head of the chunked prefill."""
+    lib = load()
+    seg, sl = ctypes.c_int64(), ctypes.c_int64()
+    wb = lib.sata_describe_prefill_plan(int(d_k), int(P), int(batch_heads), int(n), int(chunk), int(in_dt),
+                                        int(work_cap), ctypes.byref(seg), ctypes.byref(sl))
+    if wb < 0:
+        raise SataError(SATA_ERR_INVALID, "sata_describe_prefill_plan", lib.sata_last_error().decode())
+    return {"work_bytes": wb, "seg_chunks": seg.value, "slices": sl.value}
+
+
 def sata_state_reset(state: State, stream=None):
     _check(load().sata_state_reset(state.ptr, _stream(stream)), "sata_state_reset")
 
@@ -341,7 +371,8 @@ def sata_describe_features(d_k: int, P: int):
     lib = load()
     m = lib.sata_describe_features(int(d_k), int(P), None, None, 0)
     if m < 0:
-        raise SataError(SATA_ERR_INVALID, "sata_describe_features", "sata_describe_quads", lib.sata_last_error().decode())
+        raise SataError(SATA_ERR_UNSUPPORTED if d_k > 0 and P >= 1 else SATA_ERR_INVALID, "sata_describe_features",
+                        lib.sata_last_error().decode())
     tup = np.zeros(m, dtype=np.uint32)
     coef = np.zeros(m, dtype=np.float32)
     lib.sata_describe_features(int(d_k), int(P), tup.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
@@ -376,7 +407,8 @@ def sata_describe_quads(d_k: int, P: int):
     lib = load()
     nq = lib.sata_describe_quads(int(d_k), int(P), None, None, None, 0)
     if nq < 0:
-        raise SataError(SATA_ERR_INVALID, "sata_describe_quads", lib.sata_last_error().decode())
+        raise SataError(SATA_ERR_UNSUPPORTED if d_k > 0 and P >= 1 else SATA_ERR_INVALID, "sata_describe_quads",
+                        lib.sata_last_error().decode())
     w0 = np.zeros(nq, dtype=np.uint32)
     cidx = np.zeros(nq, dtype=np.int32)
     coef = np.zeros((nq, 4), dtype=np.float32)

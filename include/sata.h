@@ -155,6 +155,15 @@ sata_status sata_state_set_decode_window(sata_state *st, int window, void *strea
  * that the buffer holds every token seen.  Enqueued on `stream`. */
 sata_status sata_state_flush(sata_state *st, void *stream);
 
+/* Synchronise `stream`, then report what asynchronous work on the state has
+ * recorded in its error word since the last report: SATA_ERR_HIP (with the
+ * detail in sata_last_error) if a prefill's scan gave up waiting for a work
+ * item's predecessor, which leaves that prefill's output and the state
+ * invalid; SATA_OK otherwise.  The word is cleared once reported.  Every
+ * sata_prefill, sata_decode_step and sata_state_flush on the state reports
+ * the word the same way (without synchronising) before enqueueing work. */
+sata_status sata_state_check(sata_state *st, void *stream);
+
 /* Zero the state (start a new sequence); enqueued on `stream`. */
 sata_status sata_state_reset(sata_state *st, void *stream);
 
@@ -178,7 +187,15 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
  * orders' states are scanned and read out [hotdry, "Engineering realisation
  * of the constant compute cost"]; results do not depend on the chunk length
  * beyond rounding.  n = 0 is a no-op.  May grow the state's workspace
- * (hipMalloc) on the first call at a given size. */
+ * (hipMalloc) on the first call at a given size: the partial readouts of up
+ * to 16 GB are planned at once (longer calls run in segments of whole chunks);
+ * if that allocation fails, the call plans again under half the workspace,
+ * down to one chunk per segment, before it returns SATA_ERR_OOM.  A device-side
+ * failure of the scan's work scheduling (a work item that gives up waiting for
+ * its predecessor's state) cannot be seen when the call returns: it is
+ * recorded in the state and reported as SATA_ERR_HIP by the next call on the
+ * state or by sata_state_check, and that earlier call's output and state are
+ * invalid. */
 sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, const void *k,
                          const void *v, void *out, int64_t n, int chunk, sata_dtype in_dt,
                          sata_dtype out_dt, void *stream);
@@ -243,6 +260,27 @@ int64_t sata_describe_features(int d_k, int P, uint32_t *tuples, float *coef, in
  * valid slots of consecutive quads are consecutive features.  Returns the
  * number of quads, or -1 for arguments sata_build_index would reject. */
 int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *coef4, int64_t cap);
+
+/* Host-only: the chunked prefill's plan for batch_heads heads of n tokens of
+ * (d_k = d_v, P) with in_dt inputs under a workspace cap of work_cap bytes
+ * (sata_prefill starts at 16 GB): returns the workspace bytes and writes the
+ * chunks per segment and the feature slices per head (either pointer may be
+ * NULL); -1 for arguments the chunked prefill does not take (d_k > 64 runs in
+ * blocks and has no such plan).  For tests and capacity planning. */
+int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t n, int chunk, int in_dt,
+                                   int64_t work_cap, int64_t *seg_chunks, int64_t *slices);
+
+/* Fault injection for tests of the prefill scan's error path (process-wide,
+ * affects every later prefill until reset with (0, 0)): the persistent scan
+ * starts taking work items at item_base instead of 0, so the first item_base
+ * items never run, and gives up a wait for a predecessor after spin_limit
+ * polls (0 = the default, 2^24).  An item whose predecessor never ran then
+ * times out, records the failure in the state's error word and carries on,
+ * so every kernel still ends; the call's output is invalid.  Without
+ * sub-segments (a grid of at most one work item per compute unit) no item
+ * waits and skipped items go unreported.  Negative arguments return
+ * SATA_ERR_INVALID.  Not for production use. */
+sata_status sata_debug_scan_faults(int item_base, int spin_limit);
 
 /* Kernel timing instrumentation.  While enabled, every launch of the
  * library's kernels is bracketed by a HIP event pair recorded on the stream

@@ -158,3 +158,49 @@ def test_quads_cover_every_feature_once(d, P):
             seen[f] += 1
     assert seen[0] == 0 and order[0] == 0
     assert np.all(seen[1:] == 1)
+
+
+def test_describe_errors_raise_sata_error():
+    """The binding's describe calls turn a rejected (d_k, P) into SataError with the
+    library's status and message (an unsupported head size is SATA_ERR_UNSUPPORTED)."""
+    from constant_cost_attention_amd import sata
+    with pytest.raises(sata.SataError) as ei:
+        sata.sata_describe_features(12, 4)
+    assert ei.value.status == sata.SATA_ERR_UNSUPPORTED
+    assert "head dims" in str(ei.value)
+    with pytest.raises(sata.SataError) as ei:
+        sata.sata_describe_quads(64, 6)
+    assert ei.value.status == sata.SATA_ERR_UNSUPPORTED
+    with pytest.raises(sata.SataError) as ei:
+        sata.sata_describe_features(0, 4)
+    assert ei.value.status == sata.SATA_ERR_INVALID
+
+
+def test_prefill_plan_shrinks_segments_under_a_smaller_cap():
+    """Workspace re-planning: under a smaller cap the plan keeps the same slices, takes fewer
+    chunks per segment, and its workspace fits the cap (down to one chunk per segment, which
+    may exceed it); the default cap runs the headline workload (1 x 8 x 65536, d = 64, bf16)
+    as one segment."""
+    from constant_cost_attention_amd import sata
+    full = sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16)
+    assert full["seg_chunks"] == 512
+    caps = [full["work_bytes"] // 2, full["work_bytes"] // 7, 1 << 26, 1]
+    prev = full
+    for cap in caps:
+        p = sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16, work_cap=cap)
+        assert p["slices"] == full["slices"]
+        assert 1 <= p["seg_chunks"] <= prev["seg_chunks"]
+        assert p["work_bytes"] <= cap or p["seg_chunks"] == 1
+        prev = p
+    assert prev["seg_chunks"] == 1
+    # halving the failed workspace (what sata_prefill does on SATA_ERR_OOM) always makes progress
+    cap, segs = 16 << 30, []
+    while True:
+        p = sata.sata_describe_prefill_plan(16, 4, 64, 131072, 128, sata.SATA_BF16, work_cap=cap)
+        segs.append(p["seg_chunks"])
+        if p["seg_chunks"] == 1:
+            break
+        cap = p["work_bytes"] // 2
+    assert all(a > b for a, b in zip(segs, segs[1:]))
+    with pytest.raises(sata.SataError):
+        sata.sata_describe_prefill_plan(128, 4, 8, 4096)

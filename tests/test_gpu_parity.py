@@ -364,3 +364,56 @@ def test_workload_decode_d64_after_8192(sata, oracle):
     err = rel_err(o, ref)
     say("  err %.3e" % err)
     assert err <= TOL_F32
+
+
+def test_workload_decode_d64_all_1024_steps(sata, oracle):
+    """The decode workload as configured: 32 x 8 heads, an fp32 prefill of 8192
+    tokens, then all 1024 recurrent decode steps with fresh inputs.  Every step
+    of eight heads spread over the batch (entries 0, 9, 22 and 31) is held to
+    the fp32 bar against the oracle's rows 8192 .. 9215, so drift of the
+    state over the full run of read-modify-write steps would show."""
+    wl = WL["decode_d64_p4_f32"]
+    steps = 1024
+    say("decode workload %s, all %d steps" % (wl.name, steps))
+    pre = wl.draw()
+    dec = wl.draw_decode(steps)
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    st = sata.State(idx, wl.batch, wl.heads)
+    q, k, v = dev_all(pre)
+    prefill(idx, st, q, k, v)
+    del q, k, v
+    dq, dk_, dv_ = dev_all(dec)
+    o = torch.empty((wl.batch, wl.heads, steps, wl.d_v), device="cuda")
+    for t in range(steps):
+        o[:, :, t] = decode(idx, st, dq[:, :, t].contiguous(), dk_[:, :, t].contiguous(), dv_[:, :, t].contiguous())
+    torch.cuda.synchronize()
+    picks = [(0, 0), (0, 7), (9, 3), (9, 4), (22, 1), (22, 6), (31, 0), (31, 7)]
+    got = np.stack([o[b, h].cpu().numpy() for b, h in picks])[None]
+    cat = lambda a, b: np.stack([np.concatenate([a[bb, hh], b[bb, hh]]) for bb, hh in picks])[None]
+    rows = np.arange(wl.n, wl.n + steps, dtype=np.int64)
+    ref = oracle.taylor_attention(cat(pre.q, dec.q), cat(pre.k, dec.k), cat(pre.v, dec.v), wl.P, rows=rows)
+    per_step = np.max(np.max(np.abs(got - ref), axis=-1) / np.max(np.abs(ref), axis=-1), axis=(0, 1))
+    say("  err %.3e (first 16 steps %.3e, last 16 steps %.3e)" % (per_step.max(), per_step[:16].max(),
+                                                                  per_step[-16:].max()))
+    assert per_step.max() <= TOL_F32
+
+
+def test_decode_d64_after_32768_token_prefix(sata, oracle):
+    """Decode after a longer fp32 prefix (the 32768-token latency case): one
+    sequence of 2 heads, sampled prefill rows and 16 decode steps against the
+    oracle at the fp32 bar."""
+    d, P, n, t = 64, 4, 32768, 16
+    x = si.draw_qkv((1, 2), n + t, d, d, 32768 + 5, "f32")
+    idx = sata.Index(d, d, P)
+    st = sata.State(idx, 1, 2)
+    q, k, v = dev_all(x)
+    say("decode after a %d-token prefix" % n)
+    o = prefill(idx, st, q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous())
+    od = [decode(idx, st, q[:, :, i].contiguous(), k[:, :, i].contiguous(), v[:, :, i].contiguous())
+          for i in range(n, n + t)]
+    rows = sample_rows(n, 128, 24, 3)
+    ref = oracle.taylor_attention(x.q, x.k, x.v, P, rows=np.concatenate([rows, np.arange(n, n + t)]))
+    err = rel_err(o.cpu().numpy()[:, :, rows], ref[:, :, :len(rows)])
+    errd = rel_err(torch.stack(od, dim=2).cpu().numpy(), ref[:, :, len(rows):])
+    say("  prefill err %.3e, decode err %.3e" % (err, errd))
+    assert err <= TOL_F32 and errd <= TOL_F32

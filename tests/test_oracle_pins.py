@@ -109,11 +109,63 @@ def test_recurrent_state_equals_quadratic(oracle, d, P):
     assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
 
 
-def test_fp32_emulation_runs_close(oracle):
-    q, k, v = _rand_qkv(7, (1,), 64, 4, 4)
-    a = oracle.recurrent_attention_f32(q, k, v, 4)
-    b = oracle.taylor_attention(q, k, v, 4)
-    assert np.max(np.abs(a - b)) < 1e-5 * np.max(np.abs(b)) * 10
+def _fp32_floor_bound(q, k, v, P, o):
+    """First-order bound on |O7 - O5| per output element.  With u = 2^-24 and
+    gamma_N = N u / (1 - N u): every state element is a sum over the n tokens of
+    products carrying at most P + 2 roundings each, and the readout sums the m
+    features of an order, so each numerator or normaliser sum is exact up to
+    gamma_N times the same sum taken over absolute values, N = n + m + 2P + 8.
+    The absolute-value sum of the symmetric features is sum_p (|q|.|k|/sqrt d)^p/p!
+    (the multinomial counts add up to the plain power), so
+      |dy_c| <= gamma_N * sum_j wabs_j |v_jc|,  |dz| <= gamma_N * sum_j wabs_j,
+    and o_c = y_c / z changes by at most (|dy_c| + |o_c| |dz|)/z + 2u|o_c|."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    n, d = q.shape[-2:]
+    m = math.comb(d + P - 1, P - 1)
+    u = 2.0 ** -24
+    N = n + m + 2 * P + 8
+    gam = N * u / (1 - N * u)
+    x = np.einsum("...id,...jd->...ij", q, k) / math.sqrt(d)
+    xa = np.einsum("...id,...jd->...ij", np.abs(q), np.abs(k)) / math.sqrt(d)
+    w = sum(x ** p / math.factorial(p) for p in range(P))
+    wa = sum(xa ** p / math.factorial(p) for p in range(P))
+    causal = np.tril(np.ones((n, n)))
+    w, wa = w * causal, wa * causal
+    z = w.sum(-1)[..., None]
+    dy = gam * (wa @ np.abs(v))
+    dz = gam * wa.sum(-1)[..., None]
+    return (dy + np.abs(o) * dz) / np.abs(z) + 2 * u * np.abs(o)
+
+
+@pytest.mark.parametrize("d,P,n", [(4, 3, 300), (6, 4, 200), (8, 2, 400)])
+def test_fp32_emulation_is_fp32(oracle, d, P, n):
+    """O7 carries the recurrent form's sums in float: it stays within the
+    first-order fp32 error bound of the exact form O5 everywhere (a dropped or
+    wrong term would leave it), and it is measurably not fp64 (a version that
+    kept double would sit within 1e-13 of O5)."""
+    q, k, v = _rand_qkv(7 + d, (2,), n, d, d)
+    a = oracle.recurrent_attention_f32(q, k, v, P)
+    b = oracle.recurrent_attention(q, k, v, P)
+    bound = _fp32_floor_bound(q, k, v, P, b)
+    assert np.all(np.abs(a - b) <= bound)
+    rel = np.max(np.abs(a - b)) / np.max(np.abs(b))
+    assert rel > 1e-9, rel
+
+
+def test_fp32_emulation_is_exact_on_dyadic_inputs(oracle):
+    """On inputs whose every product and partial sum fits a float exactly
+    (small dyadic rationals, few tokens), O7 equals O5 up to the final division
+    rounding: the emulation rounds only where fp32 itself must."""
+    rng = np.random.default_rng(17)
+    d, P, n = 3, 3, 12
+    q = (rng.integers(-4, 5, size=(1, n, d)) / 4.0).astype(np.float32)
+    k = (rng.integers(-4, 5, size=(1, n, d)) / 4.0).astype(np.float32)
+    v = (rng.integers(-8, 9, size=(1, n, d)) / 8.0).astype(np.float32)
+    a = oracle.recurrent_attention_f32(q, k, v, P)
+    b = oracle.recurrent_attention(q, k, v, P)
+    # sqrt(count) and 1/(p! d^(p/2)) weights are irrational here, so equality is to fp32 rounding of
+    # a handful of operations, far below the sums' floor on random inputs
+    assert np.max(np.abs(a - b)) <= 64 * 2.0 ** -24 * np.max(np.abs(b))
 
 
 # ------------------------------------------------------------ special cases (O1)
