@@ -38,19 +38,23 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint32_t *__restrict_
 }
 
 // Zero fill (used instead of hipMemsetAsync so that a caller may capture the
-// clear in a HIP graph).  count is a multiple of 4 for every buffer here.
-__global__ __launch_bounds__(256) void zero_kernel(float4 *__restrict__ p, int64_t count4) {
+// clear in a HIP graph): count4 16-byte units from p (16-byte aligned), then the
+// last count % 4 floats one at a time.
+__global__ __launch_bounds__(256) void zero_kernel(float4 *__restrict__ p, int64_t count4, float *__restrict__ tail,
+                                                   int ntail) {
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count4; i += stride)
         p[i] = float4{0.f, 0.f, 0.f, 0.f};
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0.f;
 }
 
 hipError_t launch_zero(float *p, int64_t count, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
     const int64_t count4 = count / 4;
-    if (count4 == 0) return hipSuccess;
-    const int64_t blocks = std::min<int64_t>((count4 + 255) / 256, 8192);
+    const int ntail = (int)(count - 4 * count4);
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((count4 + 255) / 256, 8192));
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<float4 *>(p), count4);
+                       reinterpret_cast<float4 *>(p), count4, p + 4 * count4, ntail);
     return hipGetLastError();
 }
 

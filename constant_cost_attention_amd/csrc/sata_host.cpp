@@ -216,12 +216,13 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
 // Quads for the prefill, in the order the scan kernel walks them.  A quad is a
 // prefix (i0, i1, i2) of up to three sorted indices (absent ones first) and an
 // aligned block of four last indices 4b + z; slot z is a feature when
-// (prefix, 4b+z) is sorted.  Quads come in "positions" of four, one per
-// stream, whose prefixes have the same block range: every prefix whose last
+// (prefix, 4b+z) is sorted.  Quads come in "positions" of `streams` quads (4
+// for the general scan, 16 for the fp16-operand scan), one per stream, whose
+// prefixes have the same block range: every prefix whose last
 // index i2 lies in [4a, 4a+4) (order 4: i0 <= i1 <= i2; order 3: i1 <= i2;
 // order 2: i2 alone; for a = 0 also the order-1 prefix with all absent)
-// sweeps the blocks b = a .. d/4-1, and four such prefixes sweep them side by
-// side.  So within a position the block b is common, and only the first
+// sweeps the blocks b = a .. d/4-1, and `streams` such prefixes sweep them side
+// by side.  So within a position the block b is common, and only the first
 // block of a group (the one holding 4b+z = i2) has slots below i2 (invalid)
 // or a diagonal slot whose multiplicity differs from the rest.  Each valid
 // slot carries the multinomial part 1/alpha! of its feature's readout weight
@@ -235,7 +236,8 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
 // flags[pos]: bit 0 = some quad of the position has slots with different
 // weights (or invalid slots), bit 1 = the position starts a new group of
 // prefixes.
-static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags) {
+static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags,
+                        size_t streams = 4) {
     std::map<std::vector<int>, int32_t> index;   // sorted tuple -> feature index
     {
         int32_t f = 0;
@@ -286,10 +288,10 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
                 for (int i1 = 0; i1 <= i2; ++i1) prefixes.push_back({none, i1, i2});
             if (P >= 3) prefixes.push_back({none, none, i2});
         }
-        for (size_t g = 0; g < prefixes.size(); g += 4) {
+        for (size_t g = 0; g < prefixes.size(); g += streams) {
             for (int b = a; b < d / 4; ++b) {
                 uint32_t nonuni = 0;
-                for (size_t s = 0; s < 4; ++s) {
+                for (size_t s = 0; s < streams; ++s) {
                     const bool have = g + s < prefixes.size();
                     out.push_back(make(have ? prefixes[g + s] : Prefix{none, pad, pad}, b, nonuni));
                 }
@@ -377,6 +379,20 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
         quads.resize((size_t)idx->nq_tab, padq);
         qflags.resize((size_t)(idx->nq_tab / 4), 2u);
     }
+    // 16-stream positions for the fp16-operand scan (P <= 4, 16 <= d_K <= 64), padded with
+    // positions of padding quads (prefix product 0, flagged as group starts) so that every
+    // slice of up to kPos16Pad positions lies inside the table
+    std::vector<sata::QuadRec> quads16;
+    std::vector<uint32_t> flags16;
+    if (P <= 4 && d_k >= 16 && d_k <= kMaxPrefillDim) {
+        build_quads(d_k, P, quads16, flags16, 16);
+        idx->np16 = (int64_t)flags16.size();
+        sata::QuadRec padq{};
+        padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8) | ((uint32_t)d_k << 16);
+        padq.cidx = -1;
+        quads16.resize((size_t)(idx->np16 + sata::kPos16Pad) * 16, padq);
+        flags16.resize((size_t)(idx->np16 + sata::kPos16Pad), 2u);
+    }
     std::vector<uint32_t> qw0(quads.size());
     std::vector<int32_t> qcidx(quads.size());
     std::vector<float> qcoef(quads.size() * 4);
@@ -391,6 +407,8 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
         return fail(SATA_ERR_HIP, "no HIP device available");
     }
     auto release = [&]() {
+        for (void *p : {(void *)idx->d_p16_w0, (void *)idx->d_p16_cidx, (void *)idx->d_p16_coef, (void *)idx->d_p16_flags})
+            if (p) (void)hipFree(p);
         if (idx->d_tup) (void)hipFree(idx->d_tup);
         if (idx->d_coef) (void)hipFree(idx->d_coef);
         if (idx->d_qw0) (void)hipFree(idx->d_qw0);
@@ -405,6 +423,20 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     if (e == hipSuccess) e = hipMalloc(&idx->d_qcidx, qcidx.size() * sizeof(int32_t));
     if (e == hipSuccess) e = hipMalloc(&idx->d_qcoef, qcoef.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc(&idx->d_qflags, qflags.size() * sizeof(uint32_t));
+    std::vector<uint32_t> p16w0(quads16.size());
+    std::vector<int32_t> p16cidx(quads16.size());
+    std::vector<float> p16coef(quads16.size() * 4);
+    for (size_t i = 0; i < quads16.size(); ++i) {
+        p16w0[i] = quads16[i].w0;
+        p16cidx[i] = quads16[i].cidx;
+        for (int z = 0; z < 4; ++z) p16coef[i * 4 + z] = quads16[i].coef[z];
+    }
+    if (!quads16.empty()) {
+        if (e == hipSuccess) e = hipMalloc(&idx->d_p16_w0, p16w0.size() * sizeof(uint32_t));
+        if (e == hipSuccess) e = hipMalloc(&idx->d_p16_cidx, p16cidx.size() * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMalloc(&idx->d_p16_coef, p16coef.size() * sizeof(float));
+        if (e == hipSuccess) e = hipMalloc(&idx->d_p16_flags, flags16.size() * sizeof(uint32_t));
+    }
     if (e != hipSuccess) {
         (void)hipGetLastError();
         release();
@@ -417,6 +449,16 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     if (e == hipSuccess) e = hipMemcpy(idx->d_qcoef, qcoef.data(), qcoef.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(idx->d_qflags, qflags.data(), qflags.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+    if (!quads16.empty()) {
+        if (e == hipSuccess)
+            e = hipMemcpy(idx->d_p16_w0, p16w0.data(), p16w0.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+        if (e == hipSuccess)
+            e = hipMemcpy(idx->d_p16_cidx, p16cidx.data(), p16cidx.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+        if (e == hipSuccess)
+            e = hipMemcpy(idx->d_p16_coef, p16coef.data(), p16coef.size() * sizeof(float), hipMemcpyHostToDevice);
+        if (e == hipSuccess)
+            e = hipMemcpy(idx->d_p16_flags, flags16.data(), flags16.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+    }
     if (e != hipSuccess) {
         release();
         return fail_hip(e, "index upload");
@@ -434,6 +476,8 @@ void sata_index_free(sata_index *idx) {
     if (idx->d_qcidx) (void)hipFree(idx->d_qcidx);
     if (idx->d_qcoef) (void)hipFree(idx->d_qcoef);
     if (idx->d_qflags) (void)hipFree(idx->d_qflags);
+    for (void *p : {(void *)idx->d_p16_w0, (void *)idx->d_p16_cidx, (void *)idx->d_p16_coef, (void *)idx->d_p16_flags})
+        if (p) (void)hipFree(p);
     delete idx;
 }
 
@@ -752,6 +796,12 @@ int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t 
     build_quads(d_k, P, quads, flags);
     idx.nq = (int64_t)quads.size();
     idx.nq_tab = round_up(std::max<int64_t>(idx.nq, 1), sata::kQuadPad);
+    if (P <= 4 && d_k >= 16) {
+        std::vector<sata::QuadRec> q16;
+        std::vector<uint32_t> f16;
+        build_quads(d_k, P, q16, f16, 16);
+        idx.np16 = (int64_t)f16.size();
+    }
     const sata::PrefillPlan plan = sata::plan_prefill(&idx, batch_heads, n, chunk, (sata_dtype)in_dt, work_cap);
     if (!plan.ok) {
         fail(SATA_ERR_UNSUPPORTED, "no prefill plan for this configuration");

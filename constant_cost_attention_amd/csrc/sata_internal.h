@@ -40,6 +40,15 @@ struct sata_index {
     int32_t *d_qcidx = nullptr;  // [nq_tab] state index of the first valid slot (-1: none)
     float *d_qcoef = nullptr;    // [nq_tab][4] query-side weights per slot (0: invalid)
     uint32_t *d_qflags = nullptr;   // [nq_tab / 4] per position: bit 0 mixed weights, bit 1 new pair group
+    // The same features in positions of 16 quads (16 streams sharing a block), for the
+    // fp16-operand scan: np16 positions, each [16] quad words, state indices and [16][4]
+    // weights, plus a flag word; kPos16Pad padding positions follow.  Built for P <= 4 and
+    // 16 <= d_K <= 64 (np16 = 0 otherwise).
+    int64_t np16 = 0;
+    uint32_t *d_p16_w0 = nullptr;
+    int32_t *d_p16_cidx = nullptr;
+    float *d_p16_coef = nullptr;
+    uint32_t *d_p16_flags = nullptr;
 };
 
 struct sata_state {
@@ -67,6 +76,7 @@ namespace sata {
 
 constexpr int kTablePad = 2048;          // tables cover every slice up to this granularity
 constexpr int kQuadPad = 1024;           // quad tables cover every prefill slice up to this granularity
+constexpr int kPos16Pad = 64;            // padding positions after the 16-stream table (> any slice)
 
 // Prefill feature view.  The features of orders 1..P-1 are grouped into
 // "quads": a prefix (i0, i1, i2), sorted, any of which may be absent (absent
@@ -117,6 +127,8 @@ struct PrefillPlan {
     int64_t sync_words = 0; // their count (a multiple of 4)
     int64_t o0_off = 0;     // byte offset of the order-0 chunk sums and prefixes (2 x [B*H][chunks][d_V+1] fp32)
     int64_t work_bytes = 0; // workspace needed
+    bool s16 = false;       // fp16-operand scan (16-stream positions; sata_scan16.hip)
+    int64_t img_off = 0;    // (s16) byte offset of the chunks' operand images in the workspace
     bool ok = false;
     // output options for internal callers (the backward pass): write the
     // unnormalised numerator y[:d_V] instead of y[:d_V] / y[d_V], and/or the
@@ -136,6 +148,15 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
 hipError_t launch_backward(const sata_index *idx, const sata_index *lower, int64_t bh, const void *q, const void *k,
                            const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n, int chunk,
                            sata_dtype in_dt, sata_dtype out_dt, int64_t mem_budget, hipStream_t s);
+// fp16-operand scan (sata_scan16.hip): positions per slice and the operand image of one chunk
+int scan16_positions_per_slice(int dk);
+int64_t scan16_image_bytes(int dk, int chunk);
+struct TaylorArgs;
+// One segment of an fp16-operand prefill: operand images, scan, reduce (the order-0 prefixes
+// o0pre of the whole call come first).
+hipError_t launch_scan16_segment(const sata_index *idx, const sata_state *st, const PrefillPlan &plan, const void *q,
+                                 const void *k, const void *v, void *out, int64_t n, int64_t tok0, int nseg,
+                                 const float *o0pre, const TaylorArgs &ta, sata_dtype out_dt, hipStream_t stream);
 hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                           const void *q, const void *k, const void *v, void *out, int64_t n,
                           sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream);

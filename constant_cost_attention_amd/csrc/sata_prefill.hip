@@ -44,6 +44,7 @@
 
 #include "sata_device.h"
 #include "sata_internal.h"
+#include "sata_scan_common.h"
 
 namespace sata {
 
@@ -108,46 +109,6 @@ struct ScanCfg {
     static_assert(OFF_E % 16 == 0 && OFF_R % 16 == 0, "alignment");
     static_assert(OFF_Q % 16 == 0 && OFF_QC % 16 == 0, "alignment");
     static_assert(LDS + RAWB <= 160 * 1024, "LDS budget");
-};
-
-__device__ __forceinline__ int qd_i1(uint32_t w) { return (int)(w & 0xffu); }
-__device__ __forceinline__ int qd_i2(uint32_t w) { return (int)((w >> 8) & 0xffu); }
-__device__ __forceinline__ int qd_i0(uint32_t w) { return (int)((w >> 16) & 0xffu); }
-__device__ __forceinline__ int qd_b(uint32_t w) { return (int)((w >> 24) & 0xfu); }
-__device__ __forceinline__ uint32_t qd_mask(uint32_t w) { return w >> 28; }
-// alpha! of the quad's prefix (i0, i1, i2) (sorted; absent indices are >= D),
-// and its reciprocal, the prefix's share of the multinomial readout weight.
-// Without order-4 features (TRIPLE false) i0 is always absent.
-template <int D, bool TRIPLE> __device__ __forceinline__ float qd_pfact(uint32_t w) {
-    const int i1 = qd_i1(w), i2 = qd_i2(w);
-    const bool e12 = i1 == i2 && i1 < D;
-    if constexpr (!TRIPLE) return e12 ? 2.f : 1.f;
-    const int i0 = qd_i0(w);
-    const bool e01 = i0 == i1 && i0 < D;
-    return e01 ? (e12 ? 6.f : 2.f) : (e12 ? 2.f : 1.f);
-}
-template <int D, bool TRIPLE> __device__ __forceinline__ float qd_pweight(uint32_t w) {
-    const int i1 = qd_i1(w), i2 = qd_i2(w);
-    const bool e12 = i1 == i2 && i1 < D;
-    if constexpr (!TRIPLE) return e12 ? 0.5f : 1.f;
-    const int i0 = qd_i0(w);
-    const bool e01 = i0 == i1 && i0 < D;
-    return e01 ? (e12 ? 1.f / 6.f : 0.5f) : (e12 ? 0.5f : 1.f);
-}
-
-// w(x) = sum_{p<P} x^p/p! (Horner, P <= 5)
-__device__ __forceinline__ float taylor_w(float x, float c0, float c1, float c2, float c3, float c4, int P) {
-    float w = P >= 5 ? c4 : 0.f;
-    if (P >= 4) w = w * x + c3;
-    if (P >= 3) w = w * x + c2;
-    if (P >= 2) w = w * x + c1;
-    return w * x + c0;
-}
-
-struct TaylorArgs {
-    float scale, c0, c1, c2, c3, c4;
-    int P;
-    int raw;          // write the numerator y[:d_V] unnormalised
 };
 
 // Direct intra-chunk term for query tile qt of chunk (t0, nvalid): Z (rows =
@@ -316,20 +277,6 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// A persistent scan's wait for the state its predecessor item leaves: poll the item's progress
-// flag (agent-scope acquire) until it reaches `need`, at most spin_limit times.  A wait that
-// runs out sets kErrScanWait in the state's error word (pinned host memory, system scope; NULL
-// for internal states whose caller checks otherwise) and returns, so the kernel still ends;
-// the call's output and state are then invalid and the host reports it.
-__device__ __forceinline__ void wait_predecessor(uint32_t *flag, uint32_t need, int spin_limit, uint32_t *err) {
-    for (int spin = 0; spin < spin_limit; ++spin) {
-        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= need) return;
-        __builtin_amdgcn_s_sleep(2);
-    }
-    if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= need) return;
-    if (err) __hip_atomic_fetch_or(err, kErrScanWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
 template <int D, int DV, int C, int MT, int NW, typename TIn, bool TRIPLE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__restrict__ qcidx,
@@ -370,13 +317,17 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
     // sub-segments, released at agent scope) is awaited with a bounded spin.
     const int64_t per_sub = nbh * nslices;
     const int64_t nitems = per_sub * nsub;
-    for (int64_t pass = 0;; ++pass) {
-    int64_t item;
+    // Thread 0 takes the next item in the same block that releases the finished one (see the
+    // warp-specialised scan below for why there is only one such block per pass).
     if constexpr (Cfg::PERSIST) {
         if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
         __syncthreads();
+    }
+    for (int64_t pass = 0;; ++pass) {
+    int64_t item;
+    if constexpr (Cfg::PERSIST) {
         item = s_item;
-        __syncthreads();
+        __syncthreads();   // every thread has read the item before thread 0 replaces it
     } else {
         item = pass == 0 ? (int64_t)blockIdx.x : nitems;
     }
@@ -1025,8 +976,11 @@ void prefill_scan_kernel(const uint32_t *__restrict__ qw0, const int32_t *__rest
         // then writes L2 back before the flag
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         __syncthreads();
-        if (tid == 0)
+        if (tid == 0) {
             __hip_atomic_store(&sync[1 + rem], (uint32_t)(u + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
+        }
+        __syncthreads();
     }
     }
 }
@@ -1102,11 +1056,15 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
     const int64_t per_sub = nbh * nslices;
     const int64_t nitems = per_sub * nsub;
 
+    // One thread-0 block per pass, at its end, both releases the finished item and takes the
+    // next.  With a second thread-0 block at the top of the loop the compiler may thread one
+    // branch into the other; the loop it then builds runs its barriers without thread 0, and
+    // the other threads re-read an item that never changes.
+    if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
+    __syncthreads();
     for (;;) {
-        if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
-        __syncthreads();
         int64_t item = s_item;
-        __syncthreads();
+        __syncthreads();   // every thread has read the item before thread 0 replaces it
         item = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(item >> 32)) << 32) |
                          (uint32_t)__builtin_amdgcn_readfirstlane((int)item));
         if (item >= nitems) break;
@@ -1550,8 +1508,11 @@ void prefill_scan_ws_kernel(const uint32_t *__restrict__ qw0, const int32_t *__r
         // then writes L2 back before the flag
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         __syncthreads();
-        if (tid == 0)
+        if (tid == 0) {
             __hip_atomic_store(&sync[1 + rem], (uint32_t)(u + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
+        }
+        __syncthreads();
     }
 }
 
@@ -1773,6 +1734,28 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     PrefillPlan p;
     p.chunk = chunk ? chunk : (idx->dk == 64 ? 128 : 64);
     if (p.chunk != 64 && p.chunk != 128) return p;
+    const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
+    if (in_dt == SATA_BF16 && idx->np16 > 0 && idx->dk == idx->dv && (idx->dk == 16 || idx->dk == 32 || idx->dk == 64)) {
+        // fp16-operand scan: fp16 partials and one operand image per chunk of a segment
+        p.s16 = true;
+        const int np = scan16_positions_per_slice(idx->dk);
+        p.fs = 64 * np;
+        p.fw = p.fs / 4;
+        p.slices = (int)((idx->np16 + np - 1) / np);
+        const int64_t part_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * 2;
+        const int64_t img_chunk = bh * scan16_image_bytes(idx->dk, p.chunk);
+        p.sync_words = (1 + bh * p.slices + 3) / 4 * 4;
+        const int64_t o0_bytes = 2 * bh * std::max<int64_t>(nchunks, 1) * (idx->dv + 1) * (int64_t)sizeof(float);
+        const int64_t fixed = 1024 + p.sync_words * 4 + o0_bytes;
+        const int64_t room = std::max<int64_t>(work_cap - fixed, 0);
+        p.seg_chunks = std::max<int64_t>(1, std::min<int64_t>(nchunks, room / (part_chunk + img_chunk)));
+        p.sync_off = (p.seg_chunks * part_chunk + 255) / 256 * 256;
+        p.o0_off = (p.sync_off + p.sync_words * 4 + 255) / 256 * 256;
+        p.img_off = (p.o0_off + o0_bytes + 255) / 256 * 256;
+        p.work_bytes = p.img_off + p.seg_chunks * img_chunk;
+        p.ok = (int64_t)p.slices * np <= idx->np16 + kPos16Pad;
+        return p;
+    }
     const ScanShape sh = pick_shape(idx, bh, p.chunk, in_dt);
     p.ws = sh.ws;
     p.fw = 16 * sh.mt;
@@ -1780,7 +1763,6 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     p.fs = (int)(16 * np_slice);
     const int64_t npos = idx->nq / 4;
     p.slices = (int)((npos + np_slice - 1) / np_slice);
-    const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
     const int64_t pbytes = in_dt == SATA_BF16 ? 2 : 4;   // readout partials in the input's width
     const int64_t per_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * pbytes;
     // after the partial sums: the scan's work counter and one progress flag per (head, slice),
@@ -1936,9 +1918,49 @@ static hipError_t run_d(const sata_index *idx, const sata_state *st, const Prefi
     return run_dt<D, 128, 8, 4, TRIPLE>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, s);
 }
 
+// fp16-operand scan: the order-0 chunk sums and prefixes of the whole call, then per segment the
+// operand images, the scan and the reduce (sata_scan16.hip).
+template <int D>
+static hipError_t run_prefill16(const sata_index *idx, const sata_state *st, const PrefillPlan &plan, const void *q,
+                                const void *k, const void *v, void *out, int64_t n, sata_dtype out_dt,
+                                hipStream_t stream) {
+    const int C = plan.chunk;
+    const int64_t bh = (int64_t)st->batch * st->heads;
+    const int64_t nchunks = (n + C - 1) / C;
+    TaylorArgs ta;
+    ta.scale = 1.0f / sqrtf((float)D);
+    ta.c0 = idx->taylor[0]; ta.c1 = idx->taylor[1]; ta.c2 = idx->taylor[2]; ta.c3 = idx->taylor[3];
+    ta.c4 = idx->taylor[4];
+    ta.P = idx->P;
+    ta.raw = plan.raw ? 1 : 0;
+    float *o0sums = reinterpret_cast<float *>(static_cast<char *>(st->d_work) + plan.o0_off);
+    float *o0pre = o0sums + bh * nchunks * (D + 1);
+    hipLaunchKernelGGL((order0_sums_kernel<D, bf16_t>), dim3((unsigned)nchunks, (unsigned)bh), dim3(256), 0, stream,
+                       static_cast<const bf16_t *>(v), n, C, o0sums);
+    hipLaunchKernelGGL((order0_prefix_kernel<D>), dim3((unsigned)bh), dim3(128), 0, stream, o0sums, o0pre, nchunks,
+                       static_cast<float *>(st->d_state), idx->m_pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += plan.seg_chunks) {
+        const int nseg = (int)std::min<int64_t>(plan.seg_chunks, nchunks - c0);
+        e = launch_scan16_segment(idx, st, plan, q, k, v, out, n, c0 * C, nseg, o0pre, ta, out_dt, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                           const void *q, const void *k, const void *v, void *out, int64_t n,
                           sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream) {
+    if (plan.s16) {
+        if (in_dt != SATA_BF16) return hipErrorInvalidValue;   // never planned
+        switch (idx->dk) {
+            case 16: return run_prefill16<16>(idx, st, plan, q, k, v, out, n, out_dt, stream);
+            case 32: return run_prefill16<32>(idx, st, plan, q, k, v, out, n, out_dt, stream);
+            case 64: return run_prefill16<64>(idx, st, plan, q, k, v, out, n, out_dt, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (idx->dk) {
         case 8: return idx->P >= 5 ? run_d<8, true>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream)
                                    : run_d<8, false>(idx, st, plan, q, k, v, out, n, in_dt, out_dt, stream);
