@@ -36,6 +36,7 @@
 //   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
 //            engineering a constant per-token cost" (2026-02-05).
 #include <algorithm>
+#include <type_traits>
 
 #include "sata_device.h"
 #include "sata_internal.h"
@@ -242,7 +243,8 @@ __device__ __forceinline__ S16Item item_from_lds(const S16Item *s) {
 
 // The two roles of a work item, each compiled on its own (not inlined into the kernel), so that
 // the register allocator sizes each role's live values separately instead of holding the union
-// of both across the kernel.  Lane indices come in as opaque values for the same reason.
+// of both across the kernel.  Each role derives its wavefront index (uniform, a scalar register,
+// so loop bounds and branches on it stay scalar) and its lane itself.
 
 // Readout wavefront rw: token half th = rw & 1 (token tiles TPW th ..), feature half
 // fh = rw >> 1 (K steps KPR fh ..).  Per chunk: Y = psi(Q_c)[tiles, half] . S^(c-1)[half, :]
@@ -250,8 +252,10 @@ __device__ __forceinline__ S16Item item_from_lds(const S16Item *s) {
 // finalised tiles stored as fp16 partials.  Also stages each next chunk's image through its
 // registers.
 template <int D, int C, int MT>
-__device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit, int rw, int lane) {
+__device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     const S16Item it = item_from_lds(sit);
+    const int rw = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = __lane_id();
     using Cfg = S16Cfg<D, C, MT>;
     using I = typename Cfg::I;
     constexpr int NR = Cfg::NR, NC = Cfg::NC, NT = Cfg::NT, NTF = Cfg::NTF, KPR = Cfg::KPR;
@@ -336,32 +340,36 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit, int
             }
         }
     };
+    // one K step: the first of a chunk starts the accumulators from zero (the MFMA's constant
+    // operand), every other adds to them
+    auto kstep = [&](int kk, auto first) {
+        const int p = kk >> 1, h = kk & 1;
+        if (first || (h == 0 && ((it.gstart >> p) & 1u))) {
+            __asm__ volatile("" ::: "memory");
+            regroup(p);
+        }
+        f16x8 B[NT];
+#pragma unroll
+        for (int nt = 0; nt < NTF; ++nt) B[nt] = __builtin_bit_cast(f16x8, CP[(kk * NTF + nt) * 64 + lane]);
+        B[NTF] = __builtin_bit_cast(f16x8, clast[kk * clast_step]);
+        const int xo = 4 * qd_b(W0[p * 16]) + 2 * h;
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const f16x2 x = *reinterpret_cast<const f16x2 *>(qrow[tt] + xo);
+            const f16x2 xl = {x[0], x[0]}, xh = {x[1], x[1]};
+            const f16x2 a0 = pc[tt][0] * xl, a1 = pc[tt][1] * xl, a2 = pc[tt][0] * xh, a3 = pc[tt][1] * xh;
+            const f16x8 A = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                Y[tt][nt] = mfma_f16(A, B[nt], first ? f32x4{0.f, 0.f, 0.f, 0.f} : Y[tt][nt]);
+        }
+    };
     for (int cc = it.cbeg; cc < it.cend; ++cc) {
         if (cc > it.cbeg) receive_store(cc - 1);
         // ---- phase A: readout of chunk cc against S^(c-1)
+        kstep(kbeg, std::true_type{});
 #pragma unroll 1
-        for (int kk = kbeg; kk < kend; ++kk) {
-            const int p = kk >> 1, h = kk & 1;
-            if (kk == kbeg || (h == 0 && ((it.gstart >> p) & 1u))) {
-                __asm__ volatile("" ::: "memory");
-                regroup(p);
-            }
-            f16x8 B[NT];
-#pragma unroll
-            for (int nt = 0; nt < NTF; ++nt) B[nt] = __builtin_bit_cast(f16x8, CP[(kk * NTF + nt) * 64 + lane]);
-            B[NTF] = __builtin_bit_cast(f16x8, clast[kk * clast_step]);
-            const int xo = 4 * qd_b(W0[p * 16]) + 2 * h;
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) {
-                const f16x2 x = *reinterpret_cast<const f16x2 *>(qrow[tt] + xo);
-                const f16x2 xl = {x[0], x[0]}, xh = {x[1], x[1]};
-                const f16x2 a0 = pc[tt][0] * xl, a1 = pc[tt][1] * xl, a2 = pc[tt][0] * xh, a3 = pc[tt][1] * xh;
-                const f16x8 A = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    Y[tt][nt] = mfma_f16(A, B[nt], kk == kbeg ? f32x4{0.f, 0.f, 0.f, 0.f} : Y[tt][nt]);
-            }
-        }
+        for (int kk = kbeg + 1; kk < kend; ++kk) kstep(kk, std::false_type{});
         __syncthreads();   // X: copy, image and exchange area free
         // ---- phase B: hand the partner its tiles (fp32), stage the next chunk
 #pragma unroll
@@ -383,8 +391,10 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit, int
 // (S^ = S / 4^p).  Per chunk: S += phi(K_c)^T [V_c | 1] on fp16 MFMA, then the fp16 copy of the
 // new state for the readout wavefronts.
 template <int D, int C, int MT>
-__device__ __attribute__((noinline)) void scan16_update(const S16Item *sit, int uw, int lane) {
+__device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
     const S16Item it = item_from_lds(sit);
+    const int uw = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) - S16Cfg<D, C, MT>::NR;
+    const int lane = __lane_id();
     using Cfg = S16Cfg<D, C, MT>;
     using I = typename Cfg::I;
     constexpr int NC = Cfg::NC, NT = Cfg::NT, NTF = Cfg::NTF, UKS = Cfg::UKS, KS = I::KS;
@@ -615,10 +625,8 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
         it.chunk0 = chunk0;
         if (tid == 0) s_it = it;
         __syncthreads();
-        int lane = tid & 63;
-        __asm__ volatile("" : "+v"(lane));
-        if (wave < Cfg::NR) scan16_readout<D, C, MT>(&s_it, wave, lane);
-        else scan16_update<D, C, MT>(&s_it, wave - Cfg::NR, lane);
+        if (wave < Cfg::NR) scan16_readout<D, C, MT>(&s_it);
+        else scan16_update<D, C, MT>(&s_it);
         // every wave's stores reach L2 before the barrier; thread 0's agent-scope release then
         // writes L2 back before the flag
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
