@@ -77,6 +77,7 @@ namespace sata {
 constexpr int kTablePad = 2048;          // tables cover every slice up to this granularity
 constexpr int kQuadPad = 1024;           // quad tables cover every prefill slice up to this granularity
 constexpr int kPos16Pad = 64;            // padding positions after the 16-stream table (> any slice)
+constexpr int kScanQueues = 8;           // work queues of the fp16-operand scan (one per XCD)
 
 // Prefill feature view.  The features of orders 1..P-1 are grouped into
 // "quads": a prefix (i0, i1, i2), sorted, any of which may be absent (absent

@@ -1744,7 +1744,7 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
         p.slices = (int)((idx->np16 + np - 1) / np);
         const int64_t part_chunk = bh * p.slices * (int64_t)p.chunk * (idx->dv + 1) * 2;
         const int64_t img_chunk = bh * scan16_image_bytes(idx->dk, p.chunk);
-        p.sync_words = (1 + bh * p.slices + 3) / 4 * 4;
+        p.sync_words = (kScanQueues + bh * p.slices + 3) / 4 * 4;   // queue counters, then the flags
         const int64_t o0_bytes = 2 * bh * std::max<int64_t>(nchunks, 1) * (idx->dv + 1) * (int64_t)sizeof(float);
         const int64_t fixed = 1024 + p.sync_words * 4 + o0_bytes;
         const int64_t room = std::max<int64_t>(work_cap - fixed, 0);

@@ -200,13 +200,35 @@ __device__ __forceinline__ float partial_scale(float tokens_before, int C) {
 // Arguments of one scan work item: the run of chunks [cbeg, cend) of head bh, for the slice of
 // positions starting at ps0.  gstart / mixedm: bit p set where position ps0 + p starts a
 // prefix group / has slots of different weights.
+// The record's pointers carry the global address space: read back from LDS they would otherwise
+// be generic, and generic (FLAT) accesses also count against the LDS wait counter, so every LDS
+// wait would wait for the image prefetch and the partial stores in flight as well.
+#define S16_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS pointers of the role functions.  Outside a kernel, the dynamic LDS block is found through a
+// per-kernel table in global memory; under register pressure the compiler reloads that base
+// inside loops, and each reload waits for every global access in flight.  So each role reads
+// the base once into a scalar register (opaque to the compiler, so it cannot be re-derived from
+// the table) and forms typed LDS pointers (address space 3) from it.
+#define S16_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ uint32_t s16_lds_base() {
+    extern __shared__ __align__(16) unsigned char lds[];
+    uint32_t b = (uint32_t)(uintptr_t)(S16_LDS unsigned char *)lds;
+    __asm__ volatile("" : "+s"(b));   // opaque: kept in a scalar register, never re-derived
+    return b;
+}
+template <typename T> __device__ __forceinline__ S16_LDS T *s16_lds(uint32_t base, int off) {
+    return (S16_LDS T *)(uintptr_t)(base + (uint32_t)off);
+}
 struct S16Item {
-    const int32_t *pcidx;
-    float *state;
+    const S16_GLOBAL int32_t *pcidx;
+    S16_GLOBAL float *state;
     int64_t m_pad;
-    const unsigned char *img;     // this head's chunk images of the segment
-    f16 *partial;
-    const float *o0pre;           // this head's order-0 prefixes of the call's chunks
+    const S16_GLOBAL unsigned char *img;   // this head's chunk images of the segment
+    S16_GLOBAL f16 *partial;
+    const S16_GLOBAL float *o0pre;         // this head's order-0 prefixes of the call's chunks
     int64_t chunk0;               // first chunk of the segment within the call
     int64_t pbase;                // partial offset of (head, chunk 0, slice): ((bh nchunk) nslices + slice) ...
     int64_t pstride;              // partial stride per chunk
@@ -260,12 +282,12 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     using I = typename Cfg::I;
     constexpr int NR = Cfg::NR, NC = Cfg::NC, NT = Cfg::NT, NTF = Cfg::NTF, KPR = Cfg::KPR;
     constexpr int TT = Cfg::TT, TPW = Cfg::TPW, TKEEP = Cfg::TKEEP, UPT = Cfg::UPT, QS = I::QS;
-    extern __shared__ __align__(16) unsigned char lds[];
-    const uint4 *CP = reinterpret_cast<const uint4 *>(lds + Cfg::OFF_CP);
-    const uint4 *CL = reinterpret_cast<const uint4 *>(lds + Cfg::OFF_CL);
-    const f16 *Qs = reinterpret_cast<const f16 *>(lds + Cfg::OFF_IMG + I::Q_OFF);
-    f32x4 *EX = reinterpret_cast<f32x4 *>(lds + Cfg::OFF_EX);
-    const uint32_t *W0 = reinterpret_cast<const uint32_t *>(lds + Cfg::OFF_W0);
+    const uint32_t lb = s16_lds_base();
+    const S16_LDS u32x4 *CP = s16_lds<const u32x4>(lb, Cfg::OFF_CP);
+    const S16_LDS u32x4 *CL = s16_lds<const u32x4>(lb, Cfg::OFF_CL);
+    const S16_LDS f16 *Qs = s16_lds<const f16>(lb, Cfg::OFF_IMG + I::Q_OFF);
+    S16_LDS f32x4 *EX = s16_lds<f32x4>(lb, Cfg::OFF_EX);
+    const S16_LDS uint32_t *W0 = s16_lds<const uint32_t>(lb, Cfg::OFF_W0);
     const int g = lane >> 4, li = lane & 15;
     const int th = rw & 1, fh = rw >> 1, partner = rw ^ 2;
     const int kbeg = fh * KPR, kend = kbeg + KPR;
@@ -273,37 +295,49 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     const int rtid = rw * 64 + lane;          // 0 .. 64 NR - 1
     uint4 pre[UPT];
     auto fetch = [&](int cc) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(it.img + (int64_t)cc * I::BYTES);
+        const S16_GLOBAL u32x4 *src = reinterpret_cast<const S16_GLOBAL u32x4 *>(it.img + (int64_t)cc * I::BYTES);
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
             const int un = rtid + i * 64 * NR;
-            pre[i] = un < Cfg::UNITS ? src[un] : uint4{0u, 0u, 0u, 0u};
+            // every lane loads (the last ones repeat the final unit, which stage() skips): a fixed
+            // number of loads in flight lets later waits count past them instead of draining all
+            pre[i] = __builtin_bit_cast(uint4, src[un < Cfg::UNITS ? un : Cfg::UNITS - 1]);
         }
     };
     auto stage = [&]() {
-        uint4 *dst = reinterpret_cast<uint4 *>(lds + Cfg::OFF_IMG);
+        S16_LDS u32x4 *dst = s16_lds<u32x4>(lb, Cfg::OFF_IMG);
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
             const int un = rtid + i * 64 * NR;
-            if (un < Cfg::UNITS) dst[un] = pre[i];
+            if (un < Cfg::UNITS) dst[un] = __builtin_bit_cast(u32x4, pre[i]);
         }
     };
+    // loads are issued every chunk (chunk indices clamped to the item's last), so each iteration
+    // has the same loads in flight and the waits for them count exactly
+    const int clast_chunk = it.cend - 1;
     fetch(it.cbeg);
     stage();
-    if (it.cbeg + 1 < it.cend) fetch(it.cbeg + 1);
+    fetch(it.cbeg + 1 < it.cend ? it.cbeg + 1 : clast_chunk);
     __syncthreads();   // Y: image of the first chunk and the first copy written
 
     f32x4 Y[TPW][NT];
-    const f16 *qrow[TPW];
+    const S16_LDS f16 *qrow[TPW];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) qrow[tt] = Qs + (16 * (tbase + tt) + li) * QS;
-    const uint4 *clast = li == 0 ? CL + g : CL + Cfg::NKS * 4;   // normaliser lanes, else the zero entry
+    const S16_LDS u32x4 *clast = li == 0 ? CL + g : CL + Cfg::NKS * 4;   // normaliser lanes, else the zero entry
     const int clast_step = li == 0 ? 4 : 0;
     // partials: [chunk][TT][NC][16 tokens] fp16 per (head, slice)
     // (tile indices stay compile-time constants: a runtime index into Y would put it in scratch)
-    auto receive_store = [&](int cc) {
-        const float sc = partial_scale(it.o0pre[(it.chunk0 + cc) * NC + D], C);
-        f16 *pd = it.partial + it.pbase + cc * it.pstride + (int64_t)tbase * NC * 16 + (li * 16 + 4 * g);
+    // Token count before each chunk (the normaliser entry of its order-0 prefix), loaded one
+    // chunk ahead through the vector memory path (a lane-opaque offset keeps it off the scalar
+    // cache, whose wait would also stall every LDS wait in between).
+    int opq = 0;
+    __asm__ volatile("" : "+v"(opq));
+    auto count_before = [&](int cc) { return it.o0pre[(it.chunk0 + cc) * NC + D + opq]; };
+    float cnt_next = count_before(it.cbeg);
+    auto receive_store = [&](int cc, float cnt) {
+        const float sc = partial_scale(cnt, C);
+        S16_GLOBAL f16 *pd = it.partial + it.pbase + cc * it.pstride + (int64_t)tbase * NC * 16 + (li * 16 + 4 * g);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             if (tt / TKEEP != fh) continue;   // uniform
@@ -313,8 +347,8 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
                 if (nt < NTF || li == 0) {
                     const f16x2 a = {(f16)(y[0] * sc), (f16)(y[1] * sc)};
                     const f16x2 b = {(f16)(y[2] * sc), (f16)(y[3] * sc)};
-                    *reinterpret_cast<uint2 *>(pd + (tt * NC + 16 * nt) * 16) =
-                        uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+                    *reinterpret_cast<S16_GLOBAL u32x2 *>(pd + (tt * NC + 16 * nt) * 16) =
+                        u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
                 }
             }
         }
@@ -322,7 +356,7 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     // prefix factors of the lane's four streams (4g .. 4g+3) for its token in each tile
     f16x2 pc[TPW][2];
     auto regroup = [&](int p) {
-        const uint32_t *wp = W0 + p * 16 + 4 * g;
+        const S16_LDS uint32_t *wp = W0 + p * 16 + 4 * g;
         uint32_t w[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] = wp[r];
@@ -355,7 +389,7 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
         const int xo = 4 * qd_b(W0[p * 16]) + 2 * h;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            const f16x2 x = *reinterpret_cast<const f16x2 *>(qrow[tt] + xo);
+            const f16x2 x = *reinterpret_cast<const S16_LDS f16x2 *>(qrow[tt] + xo);
             const f16x2 xl = {x[0], x[0]}, xh = {x[1], x[1]};
             const f16x2 a0 = pc[tt][0] * xl, a1 = pc[tt][1] * xl, a2 = pc[tt][0] * xh, a3 = pc[tt][1] * xh;
             const f16x8 A = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
@@ -364,8 +398,11 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
                 Y[tt][nt] = mfma_f16(A, B[nt], first ? f32x4{0.f, 0.f, 0.f, 0.f} : Y[tt][nt]);
         }
     };
+    float cnt_prev = 0.f;
     for (int cc = it.cbeg; cc < it.cend; ++cc) {
-        if (cc > it.cbeg) receive_store(cc - 1);
+        if (cc > it.cbeg) receive_store(cc - 1, cnt_prev);
+        cnt_prev = cnt_next;
+        cnt_next = count_before(cc + 1 < it.cend ? cc + 1 : clast_chunk);
         // ---- phase A: readout of chunk cc against S^(c-1)
         kstep(kbeg, std::true_type{});
 #pragma unroll 1
@@ -378,13 +415,11 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) EX[((rw * TKEEP + tt % TKEEP) * NT + nt) * 64 + lane] = Y[tt][nt];
         }
-        if (cc + 1 < it.cend) {
-            stage();
-            if (cc + 2 < it.cend) fetch(cc + 2);
-        }
+        if (cc + 1 < it.cend) stage();
+        fetch(cc + 2 < it.cend ? cc + 2 : clast_chunk);
         __syncthreads();   // Y: next image, copy and exchange written
     }
-    receive_store(it.cend - 1);
+    receive_store(it.cend - 1, cnt_prev);
 }
 
 // Update wavefront uw: positions p0 = MT uw .. of the slice, their state in accumulators
@@ -398,16 +433,16 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
     using Cfg = S16Cfg<D, C, MT>;
     using I = typename Cfg::I;
     constexpr int NC = Cfg::NC, NT = Cfg::NT, NTF = Cfg::NTF, UKS = Cfg::UKS, KS = I::KS;
-    extern __shared__ __align__(16) unsigned char lds[];
-    uint4 *CP = reinterpret_cast<uint4 *>(lds + Cfg::OFF_CP);
-    uint4 *CL = reinterpret_cast<uint4 *>(lds + Cfg::OFF_CL);
-    const f16 *Kt = reinterpret_cast<const f16 *>(lds + Cfg::OFF_IMG + I::KT_OFF);
-    const f16 *Vt = reinterpret_cast<const f16 *>(lds + Cfg::OFF_IMG + I::V_OFF);
-    const uint32_t *W0 = reinterpret_cast<const uint32_t *>(lds + Cfg::OFF_W0);
-    const float4 *QC = reinterpret_cast<const float4 *>(lds + Cfg::OFF_QC);
+    const uint32_t lb = s16_lds_base();
+    S16_LDS u32x4 *CP = s16_lds<u32x4>(lb, Cfg::OFF_CP);
+    S16_LDS u32x4 *CL = s16_lds<u32x4>(lb, Cfg::OFF_CL);
+    const S16_LDS f16 *Kt = s16_lds<const f16>(lb, Cfg::OFF_IMG + I::KT_OFF);
+    const S16_LDS f16 *Vt = s16_lds<const f16>(lb, Cfg::OFF_IMG + I::V_OFF);
+    const S16_LDS uint32_t *W0 = s16_lds<const uint32_t>(lb, Cfg::OFF_W0);
+    const S16_LDS f32x4 *QC = s16_lds<const f32x4>(lb, Cfg::OFF_QC);
     const int g = lane >> 4, li = lane & 15;
     const int p0 = uw * MT;
-    float *Sh = it.state + it.bh * NC * it.m_pad;
+    S16_GLOBAL float *Sh = it.state + it.bh * NC * it.m_pad;
     f32x4 S[MT][4][NT];
     uint32_t wr[MT];                          // quad word of the lane's prefix (row li) per position
     int blk[MT];
@@ -446,7 +481,7 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
                 // head's first element instead, and the value is dropped: every address stays
                 // inside this head's state
                 const bool cok = 16 * nt + li < NC;
-                const float *rp = Sh + (cok ? nt * tstride + off : 0);
+                const S16_GLOBAL float *rp = Sh + (cok ? nt * tstride + off : 0);
 #pragma unroll
                 for (int z = 0; z < 4; ++z) {
                     const bool ok = ((vm >> z) & 1u) && cok;
@@ -468,9 +503,9 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t w = W0[(p0 + j) * 16 + 4 * g + r];
-                    const float4 cf = QC[(p0 + j) * 16 + 4 * g + r];
+                    const f32x4 cf = QC[(p0 + j) * 16 + 4 * g + r];
                     const float pf = qd_pfact<D, false>(w);
-                    rt[r][0] = cf.x * pf; rt[r][1] = cf.y * pf; rt[r][2] = cf.z * pf; rt[r][3] = cf.w * pf;
+                    rt[r][0] = cf[0] * pf; rt[r][1] = cf[1] * pf; rt[r][2] = cf[2] * pf; rt[r][3] = cf[3] * pf;
                 }
             }
 #pragma unroll
@@ -487,7 +522,7 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
                     }
                     const f16x2 e0 = {(f16)s0[0], (f16)s0[1]}, e1 = {(f16)s0[2], (f16)s0[3]};
                     const f16x2 e2 = {(f16)s1[0], (f16)s1[1]}, e3 = {(f16)s1[2], (f16)s1[3]};
-                    const uint4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
+                    const u32x4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
                                        __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)};
                     const int kk = 2 * (p0 + j) + h;
                     if (nt < NTF) CP[(kk * NTF + nt) * 64 + lane] = val;
@@ -506,20 +541,20 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
             const int tb = 32 * ks + 8 * g;
             f16x8 B[NT];
 #pragma unroll
-            for (int nt = 0; nt < NTF; ++nt) B[nt] = *reinterpret_cast<const f16x8 *>(Vt + (16 * nt + li) * KS + tb);
-            B[NTF] = *reinterpret_cast<const f16x8 *>(Vt + vlast * KS + tb);
+            for (int nt = 0; nt < NTF; ++nt) B[nt] = *reinterpret_cast<const S16_LDS f16x8 *>(Vt + (16 * nt + li) * KS + tb);
+            B[NTF] = *reinterpret_cast<const S16_LDS f16x8 *>(Vt + vlast * KS + tb);
             f16x8 p2;
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
                 if (j == 0 || ((newgrp >> j) & 1u)) {
                     __asm__ volatile("" ::: "memory");
-                    const f16x8 a = *reinterpret_cast<const f16x8 *>(Kt + qd_i1(wr[j]) * KS + tb);
-                    const f16x8 b = *reinterpret_cast<const f16x8 *>(Kt + qd_i2(wr[j]) * KS + tb);
+                    const f16x8 a = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + qd_i1(wr[j]) * KS + tb);
+                    const f16x8 b = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + qd_i2(wr[j]) * KS + tb);
                     p2 = a * b;
                 }
 #pragma unroll
                 for (int z = 0; z < 4; ++z) {
-                    const f16x8 k3 = *reinterpret_cast<const f16x8 *>(Kt + (4 * blk[j] + z) * KS + tb);
+                    const f16x8 k3 = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + (4 * blk[j] + z) * KS + tb);
                     const f16x8 A = p2 * k3;
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) S[j][z][nt] = mfma_f16(A, B[nt], S[j][z][nt]);
@@ -542,7 +577,7 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
             sc = 1.0f / sc;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                float *rp = Sh + nt * tstride + off;
+                S16_GLOBAL float *rp = Sh + nt * tstride + off;
                 if (16 * nt + li < NC) {
 #pragma unroll
                     for (int z = 0; z < 4; ++z)
@@ -554,9 +589,10 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
 }
 
 // Persistent scan: a grid of one workgroup per resident slot takes (sub-segment u, head, slice)
-// items from a counter, u-major; an item continues the state its predecessor (u - 1, head,
-// slice) left, after an agent-scope acquire of that slice's progress flag (bounded wait), and
-// releases its own flag once every wavefront's state stores are out.  Wavefronts 0..3 read out,
+// items from one of kScanQueues counters, u-major; an item continues the state its predecessor
+// (u - 1, head, slice) left, after an agent-scope acquire of that slice's progress flag (bounded
+// wait), and releases its own flag once every wavefront's state stores are out.  The predecessor
+// sits in the same queue, earlier, so a running workgroup has taken it.  Wavefronts 0..3 read out,
 // 4..7 update (one of each per SIMD).
 template <int D, int C, int MT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -579,12 +615,23 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t per_sub = nbh * nslices;
-    const int64_t nitems = per_sub * nsub;
+    // Queue q of ngroups serves the (head, slice) pairs [lo, hi) (contiguous, head-major), for
+    // every sub-segment, u-major; the workgroups with blockIdx.x % ngroups == q take from it.
+    // Workgroups are dispatched to the chip's XCDs in turn, so with ngroups = kScanQueues a
+    // queue's workgroups share one XCD and its L2, and the slices of a head walk the same
+    // chunk images at the same time.
+    const int ngroups = (int)gridDim.x < kScanQueues ? (int)gridDim.x : kScanQueues;
+    const int grp = (int)blockIdx.x % ngroups;
+    const int64_t lo = per_sub * grp / ngroups, hi = per_sub * (grp + 1) / ngroups;
+    const int64_t cnt = hi - lo;
+    const int64_t nitems = cnt * nsub;
+    uint32_t *counter = sync + grp;
+    uint32_t *flags = sync + kScanQueues;   // one per (head, slice): sub-segments finished
     // One thread-0 block per pass, at its end, both releases the finished item and takes
     // the next; a second thread-0 block at the top of the loop would let the compiler
     // thread one branch into the other and leave a loop whose barriers the other
     // threads pass without thread 0, re-reading an item that never changes.
-    if (tid == 0) s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
+    if (tid == 0) s_item = (int64_t)atomicAdd(counter, 1u) + item_base;
     __syncthreads();
     for (;;) {
         int64_t item = s_item;
@@ -592,15 +639,15 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
         item = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(item >> 32)) << 32) |
                          (uint32_t)__builtin_amdgcn_readfirstlane((int)item));
         if (item >= nitems) break;
-        const int u = (int)(item / per_sub);
-        const int64_t rem = item % per_sub;
+        const int u = (int)(item / cnt);
+        const int64_t rem = lo + item % cnt;
         S16Item it;
         it.bh = rem / nslices;
         const int slice = (int)(rem % nslices);
         it.cbeg = u * sub_chunks;
         it.cend = it.cbeg + sub_chunks < nchunk ? it.cbeg + sub_chunks : nchunk;
         if (u > 0) {
-            if (tid == 0) wait_predecessor(sync + 1 + rem, (uint32_t)u, spin_limit, err);
+            if (tid == 0) wait_predecessor(flags + rem, (uint32_t)u, spin_limit, err);
             __syncthreads();   // thread 0's acquire invalidated the caches every wave reads through
         }
         it.ps0 = (int64_t)slice * NP;
@@ -614,14 +661,14 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
         const int l0 = tid & 63;
         it.gstart = (uint32_t)__ballot(l0 < NP && (FL[l0 < NP ? l0 : 0] & 2u));
         it.mixedm = (uint32_t)__ballot(l0 < NP && (FL[l0 < NP ? l0 : 0] & 1u));
-        it.pcidx = pcidx;
-        it.state = state;
+        it.pcidx = (const S16_GLOBAL int32_t *)pcidx;
+        it.state = (S16_GLOBAL float *)state;
         it.m_pad = m_pad;
-        it.img = img + it.bh * nchunk * (int64_t)I::BYTES;
-        it.partial = partial;
+        it.img = (const S16_GLOBAL unsigned char *)(img + it.bh * nchunk * (int64_t)I::BYTES);
+        it.partial = (S16_GLOBAL f16 *)partial;
         it.pstride = (int64_t)nslices * (Cfg::TT * Cfg::NC * 16);
         it.pbase = (it.bh * nchunk * nslices + slice) * (int64_t)(Cfg::TT * Cfg::NC * 16);
-        it.o0pre = o0pre + it.bh * call_chunks * Cfg::NC;
+        it.o0pre = (const S16_GLOBAL float *)(o0pre + it.bh * call_chunks * Cfg::NC);
         it.chunk0 = chunk0;
         if (tid == 0) s_it = it;
         __syncthreads();
@@ -632,8 +679,8 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         __syncthreads();
         if (tid == 0) {
-            __hip_atomic_store(&sync[1 + rem], (uint32_t)(u + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            s_item = (int64_t)atomicAdd(&sync[0], 1u) + item_base;
+            __hip_atomic_store(&flags[rem], (uint32_t)(u + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            s_item = (int64_t)atomicAdd(counter, 1u) + item_base;
         }
         __syncthreads();
     }
