@@ -11,6 +11,7 @@
 #include <cstring>
 #include <atomic>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -20,6 +21,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+// Set while sata_prefill_noalloc runs on this thread: its launches record no timing events
+// (which would create hipEvents).
+thread_local bool t_prof_off = false;
 
 sata_status fail(sata_status s, const char *fmt, ...) {
     char buf[512];
@@ -175,6 +179,77 @@ ScanDebug scan_debug() {
     return d;
 }
 }
+
+namespace {
+
+// Argument and state checks shared by sata_prefill and sata_prefill_noalloc (the second also
+// reports, and clears, an error the device recorded on the state since the last call).  Sets
+// *nothing for n == 0.
+sata_status check_prefill_args(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
+                               void *out, int64_t n, int chunk, sata_dtype in_dt, sata_dtype out_dt, bool *nothing) {
+    sata_status s = check_index_state(idx, st);
+    if (s != SATA_OK) return s;
+    if (n < 0) return fail(SATA_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return fail(SATA_ERR_INVALID, "unknown dtype");
+    if (chunk != 0 && chunk != 64 && chunk != 128)
+        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
+    if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
+    if (st->dtype != SATA_F32)
+        return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 state with sata_state_convert)");
+    s = take_state_error(st);
+    if (s != SATA_OK) return s;
+    *nothing = n == 0;
+    if (*nothing) return SATA_OK;
+    if (!q || !k || !v || !out) return fail(SATA_ERR_INVALID, "q, k, v and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(SATA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    const int64_t bh = (int64_t)st->batch * st->heads;
+    const int64_t in_b = dtype_bytes(in_dt), out_b = dtype_bytes(out_dt);
+    const int64_t nq = bh * n * idx->dk * in_b, nv = bh * n * idx->dv * in_b, no = bh * n * idx->dv * out_b;
+    if (overlaps(out, no, q, nq) || overlaps(out, no, k, nq) || overlaps(out, no, v, nv))
+        return fail(SATA_ERR_INVALID, "out overlaps q, k or v");
+    return SATA_OK;
+}
+
+// ---- allocation-free prefill workspace
+// sata_prefill_noalloc keeps its workspace (split-K partials, work-queue counters and progress
+// flags, order-0 sums, chunk images) in this file-scope device array: every device the library
+// runs on holds its own copy until the process ends.  In host code the name is a host-side
+// stand-in, not a device address; the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that pointer is used.
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[SATA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's (dev's) address of the scratch array.
+sata_status scratch_address(int dev, void **ptr) {
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(SATA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the allocation-free prefill tracks", dev,
+                    kScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail_hip(e, "address of the allocation-free prefill's scratch array");
+        if (!p) return fail(SATA_ERR_HIP, "the allocation-free prefill's scratch array has no device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SATA_OK;
+}
+
+struct ProfOff {
+    ProfOff() { t_prof_off = true; }
+    ~ProfOff() { t_prof_off = false; }
+};
+
+}  // namespace
 
 extern "C" {
 
@@ -596,26 +671,10 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
 sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
                          void *out, int64_t n, int chunk, sata_dtype in_dt, sata_dtype out_dt, void *stream) {
     g_last_error.clear();
-    sata_status s = check_index_state(idx, st);
-    if (s != SATA_OK) return s;
-    if (n < 0) return fail(SATA_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
-    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return fail(SATA_ERR_INVALID, "unknown dtype");
-    if (chunk != 0 && chunk != 64 && chunk != 128)
-        return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
-    if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
-    if (st->dtype != SATA_F32)
-        return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 state with sata_state_convert)");
-    s = take_state_error(st);
-    if (s != SATA_OK) return s;
-    if (n == 0) return SATA_OK;
-    if (!q || !k || !v || !out) return fail(SATA_ERR_INVALID, "q, k, v and out must be non-NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(SATA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    bool nothing = false;
+    sata_status s = check_prefill_args(idx, st, q, k, v, out, n, chunk, in_dt, out_dt, &nothing);
+    if (s != SATA_OK || nothing) return s;
     const int64_t bh = (int64_t)st->batch * st->heads;
-    const int64_t in_b = dtype_bytes(in_dt), out_b = dtype_bytes(out_dt);
-    const int64_t nq = bh * n * idx->dk * in_b, nv = bh * n * idx->dv * in_b, no = bh * n * idx->dv * out_b;
-    if (overlaps(out, no, q, nq) || overlaps(out, no, k, nq) || overlaps(out, no, v, nv))
-        return fail(SATA_ERR_INVALID, "out overlaps q, k or v");
     if (idx->dk > kMaxPrefillDim) {
         // d_K = 128: blocks of up to kMaxDecodeWindow tokens through the state in HBM (the
         // chunk length does not apply)
@@ -648,6 +707,43 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     if (s != SATA_OK) return s;
     hipError_t e = sata::launch_prefill(idx, st, plan, q, k, v, out, n, in_dt, out_dt, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "prefill launch");
+    return SATA_OK;
+}
+
+sata_status sata_prefill_noalloc(const sata_index *idx, sata_state *st, const void *q, const void *k, const void *v,
+                                 void *out, int64_t n, int chunk, sata_dtype in_dt, sata_dtype out_dt, void *stream) {
+    g_last_error.clear();
+    bool nothing = false;
+    sata_status s = check_prefill_args(idx, st, q, k, v, out, n, chunk, in_dt, out_dt, &nothing);
+    if (s != SATA_OK || nothing) return s;
+    if (idx->dk > kMaxPrefillDim)
+        return fail(SATA_ERR_UNSUPPORTED, "the allocation-free prefill covers d_k <= %d (got %d)", kMaxPrefillDim,
+                    idx->dk);
+    const int64_t bh = (int64_t)st->batch * st->heads;
+    ProfOff quiet;   // no timing events for any launch of this call
+    DeviceGuard g(st->device);
+    if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
+    void *scr = nullptr;
+    s = scratch_address(st->device, &scr);
+    if (s != SATA_OK) return s;
+    // segments sized to the scratch array; a call whose single-chunk segments still need more
+    // (many heads) is refused
+    const sata::PrefillPlan plan = sata::plan_prefill(idx, bh, n, chunk, in_dt, SATA_NOALLOC_SCRATCH_BYTES);
+    if (!plan.ok) return fail(SATA_ERR_UNSUPPORTED, "no prefill plan for this configuration");
+    if (plan.work_bytes > SATA_NOALLOC_SCRATCH_BYTES)
+        return fail(SATA_ERR_UNSUPPORTED,
+                    "this prefill needs a workspace of %lld bytes; the allocation-free scratch holds %lld "
+                    "(use sata_prefill, or fewer heads per call)",
+                    (long long)plan.work_bytes, (long long)SATA_NOALLOC_SCRATCH_BYTES);
+    // deferred decode tokens fold into the state first; their buffers (and the decode
+    // workspace) exist whenever there are any, so this allocates nothing either
+    s = flush_pending(st, (hipStream_t)stream);
+    if (s != SATA_OK) return s;
+    sata_state view = *st;   // the same state, with the scratch array as its workspace
+    view.d_work = scr;
+    view.work_bytes = SATA_NOALLOC_SCRATCH_BYTES;
+    hipError_t e = sata::launch_prefill(idx, &view, plan, q, k, v, out, n, in_dt, out_dt, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "allocation-free prefill launch");
     return SATA_OK;
 }
 
@@ -879,6 +975,7 @@ const char *const kProfNames[sata::kProfCount] = {"prefill_scan", "prefill_combi
 namespace sata {
 
 ProfScope::ProfScope(int k, hipStream_t s) : kernel(k), stream(s) {
+    if (t_prof_off) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
     start = prof_event();

@@ -20,6 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsata.so")
 
 SATA_OK, SATA_ERR_INVALID, SATA_ERR_UNSUPPORTED, SATA_ERR_OOM, SATA_ERR_HIP = range(5)
+SATA_NOALLOC_SCRATCH_BYTES = 128 << 20   # include/sata.h
 SATA_F32, SATA_BF16 = 0, 1
 
 _EXPORTS = (
@@ -27,7 +28,7 @@ _EXPORTS = (
     "sata_state_alloc", "sata_state_alloc_dtype", "sata_state_convert", "sata_state_set_decode_window",
     "sata_state_flush", "sata_state_check", "sata_state_reset", "sata_state_free",
     "sata_state_data",
-    "sata_prefill", "sata_prefill_backward", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
+    "sata_prefill", "sata_prefill_noalloc", "sata_prefill_backward", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
     "sata_describe_prefill_plan", "sata_debug_scan_faults",
@@ -84,6 +85,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_state_free.restype = None
     lib.sata_state_data.argtypes = [vp, pvp, ctypes.POINTER(i64)]
     lib.sata_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, cint, cint, cint, vp]
+    lib.sata_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, cint, cint, cint, vp]
     lib.sata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, cint, cint, vp]
     lib.sata_prefill_backward.argtypes = [vp, cint, cint, vp, vp, vp, vp, vp, vp, vp, i64, cint, cint, cint, vp]
     lib.sata_expand_features.argtypes = [vp, vp, vp, i64, cint, cint, vp]
@@ -104,7 +106,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_alloc_dtype",
                  "sata_state_convert", "sata_state_set_decode_window", "sata_state_flush", "sata_state_check",
                  "sata_debug_scan_faults", "sata_state_reset",
-                 "sata_state_data", "sata_prefill", "sata_prefill_backward", "sata_decode_step", "sata_expand_features"):
+                 "sata_state_data", "sata_prefill", "sata_prefill_noalloc", "sata_prefill_backward", "sata_decode_step",
+                 "sata_expand_features"):
         getattr(lib, name).restype = cint
     _lib = lib
     return lib
@@ -298,9 +301,7 @@ def state_tensor(state: State) -> torch.Tensor:
     return torch.as_tensor(_CudaArray(ptr, shape, "<i2"), device="cuda").view(torch.bfloat16)
 
 
-def sata_prefill(index: Index, state: State, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                 out: torch.Tensor, chunk: int = 0, stream=None):
-    """q, k: [B, H, n, d_K]; v, out: [B, H, n, d_V] on the GPU."""
+def _prefill_args(index: Index, state: State, q, k, v, out):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, n, d_K]")
     B, H, n, dk = q.shape
@@ -311,9 +312,26 @@ def sata_prefill(index: Index, state: State, q: torch.Tensor, k: torch.Tensor, v
         raise ValueError("k, v, out shapes disagree with q")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share a dtype")
+    return n
+
+
+def sata_prefill(index: Index, state: State, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 out: torch.Tensor, chunk: int = 0, stream=None):
+    """q, k: [B, H, n, d_K]; v, out: [B, H, n, d_V] on the GPU."""
+    n = _prefill_args(index, state, q, k, v, out)
     _check(load().sata_prefill(index.ptr, state.ptr, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
                                _dev_ptr(out, "out"), int(n), int(chunk), _dtype(q), _dtype(out),
                                _stream(stream)), "sata_prefill")
+    return out
+
+
+def sata_prefill_noalloc(index: Index, state: State, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         out: torch.Tensor, chunk: int = 0, stream=None):
+    """sata_prefill without device allocation (workspace: the library's per-device scratch array)."""
+    n = _prefill_args(index, state, q, k, v, out)
+    _check(load().sata_prefill_noalloc(index.ptr, state.ptr, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                       _dev_ptr(out, "out"), int(n), int(chunk), _dtype(q), _dtype(out),
+                                       _stream(stream)), "sata_prefill_noalloc")
     return out
 
 

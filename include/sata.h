@@ -200,6 +200,29 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
                          const void *v, void *out, int64_t n, int chunk, sata_dtype in_dt,
                          sata_dtype out_dt, void *stream);
 
+/* Byte size of sata_prefill_noalloc's scratch array (128 MiB), which every
+ * device the library runs on holds until the process ends. */
+#define SATA_NOALLOC_SCRATCH_BYTES ((int64_t)128 << 20)
+
+/* sata_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid allocation.
+ * Same arguments, results and error reporting as sata_prefill (outputs equal
+ * sata_prefill's up to rounding; with the same segment plan, bit for bit), but
+ * the call performs no hipMalloc, hipFree or other allocation: its workspace
+ * is a file-scope device array of SATA_NOALLOC_SCRATCH_BYTES, looked up once
+ * per device on the first call there, and the prefill runs in segments of
+ * whole chunks sized to fit it (timing events of sata_profile_enable are not
+ * recorded for it).  The caller still provides q, k, v, out and the state
+ * (allocated beforehand).  Every call on a device shares that device's
+ * array: calls that overlap in time on one device (other streams or host
+ * threads) race and give wrong results; order them.  Returns
+ * SATA_ERR_UNSUPPORTED for d_K > 64 and when even single-chunk segments need
+ * more workspace than the array holds (about 1.6 MB per head at d_K = 64,
+ * P = 4), with the size needed in sata_last_error. */
+sata_status sata_prefill_noalloc(const sata_index *idx, sata_state *st, const void *q, const void *k,
+                                 const void *v, void *out, int64_t n, int chunk, sata_dtype in_dt,
+                                 sata_dtype out_dt, void *stream);
+
 /* Gradients of a causal prefill of n tokens that starts from a zero state
  * (a fresh sequence): given dout = dL/dout for out = the prefill's output on
  * q, k, v, write dq, dk, dv = dL/dq, dL/dk, dL/dv.  Shapes and dtypes as for
