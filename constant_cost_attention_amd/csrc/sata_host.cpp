@@ -481,6 +481,13 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
         (void)hipGetLastError();
         return fail(SATA_ERR_HIP, "no HIP device available");
     }
+    {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, idx->device) == hipSuccess && cus > 0)
+            idx->cus = cus;
+        else
+            (void)hipGetLastError();
+    }
     auto release = [&]() {
         for (void *p : {(void *)idx->d_p16_w0, (void *)idx->d_p16_cidx, (void *)idx->d_p16_coef, (void *)idx->d_p16_flags})
             if (p) (void)hipFree(p);

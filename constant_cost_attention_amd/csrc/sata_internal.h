@@ -29,6 +29,7 @@ struct sata_index {
     int64_t m_pad = 0;   // state row stride (multiple of 64)
     int64_t m_tab = 0;   // table length (multiple of kTablePad, covers every kernel's tail)
     int device = 0;
+    int cus = 256;       // compute units of the device (work-item counts are planned against it)
     uint32_t *d_tup = nullptr;   // [m_tab] packed tuples: i1 | i2 << 8 | i3 << 16 | i4 << 24
     float *d_coef = nullptr;     // [m_tab] query-side readout weight 1/(alpha! d_K^(p/2)); 0 for padding
     float taylor[8] = {0};       // 1/p!, p < P (intra-chunk direct weights)
@@ -130,6 +131,7 @@ struct PrefillPlan {
     int64_t work_bytes = 0; // workspace needed
     bool s16 = false;       // fp16-operand scan (16-stream positions; sata_scan16.hip)
     int64_t img_off = 0;    // (s16) byte offset of the chunks' operand images in the workspace
+    int mt = 0;             // (s16) positions per update wavefront
     bool ok = false;
     // output options for internal callers (the backward pass): write the
     // unnormalised numerator y[:d_V] instead of y[:d_V] / y[d_V], and/or the
@@ -150,7 +152,7 @@ hipError_t launch_backward(const sata_index *idx, const sata_index *lower, int64
                            const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n, int chunk,
                            sata_dtype in_dt, sata_dtype out_dt, int64_t mem_budget, hipStream_t s);
 // fp16-operand scan (sata_scan16.hip): positions per slice and the operand image of one chunk
-int scan16_positions_per_slice(int dk);
+int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus);
 int64_t scan16_image_bytes(int dk, int chunk);
 struct TaylorArgs;
 // One segment of an fp16-operand prefill: operand images, scan, reduce (the order-0 prefixes

@@ -1738,7 +1738,8 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     if (in_dt == SATA_BF16 && idx->np16 > 0 && idx->dk == idx->dv && (idx->dk == 16 || idx->dk == 32 || idx->dk == 64)) {
         // fp16-operand scan: fp16 partials and one operand image per chunk of a segment
         p.s16 = true;
-        const int np = scan16_positions_per_slice(idx->dk);
+        p.mt = scan16_choose_mt(idx->dk, idx->np16, bh, idx->cus);
+        const int np = 4 * p.mt;
         p.fs = 64 * np;
         p.fw = p.fs / 4;
         p.slices = (int)((idx->np16 + np - 1) / np);

@@ -848,10 +848,16 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
 // ---------------------------------------------------------------- host side
 
 // Positions per update wavefront: as many as its accumulators (MT x 4 slots x column tiles x 4
-// registers) allow next to the operands within 256 registers.
-constexpr int scan16_mt(int dk) { return dk == 64 ? 2 : dk == 32 ? 3 : 5; }
+// registers) allow next to the operands within 256 registers, or one when that many leaves
+// fewer (head, slice) work items than compute units (few heads of a small head size: a head's
+// chunks run one after another, so only more slices spread it over the chip).
+constexpr int scan16_mt_max(int dk) { return dk == 64 ? 2 : dk == 32 ? 3 : 5; }
 
-int scan16_positions_per_slice(int dk) { return 4 * scan16_mt(dk); }
+int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus) {
+    const int big = scan16_mt_max(dk);
+    const int64_t slices = (np16 + 4 * big - 1) / (4 * big);
+    return bh * slices >= cus ? big : 1;
+}
 
 int64_t scan16_image_bytes(int dk, int chunk) {
     auto b = [&](auto d, auto c) { return (int64_t)Img16<decltype(d)::value, decltype(c)::value>::BYTES; };
@@ -865,11 +871,10 @@ int64_t scan16_image_bytes(int dk, int chunk) {
     return chunk == 64 ? b(I64{}, C64{}) : b(I64{}, C128{});
 }
 
-template <int D, int C, typename TOut>
+template <int D, int C, int MT, typename TOut>
 static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const PrefillPlan &plan, const void *q,
                              const void *k, const void *v, void *out, int64_t n, int64_t tok0, int nseg,
                              const float *o0pre, const TaylorArgs &ta, hipStream_t stream) {
-    constexpr int MT = scan16_mt(D);
     using Cfg = S16Cfg<D, C, MT>;
     const int64_t bh = (int64_t)st->batch * st->heads;
     auto scan = scan16_kernel<D, C, MT>;
@@ -919,9 +924,16 @@ hipError_t launch_scan16_segment(const sata_index *idx, const sata_state *st, co
                                  const void *k, const void *v, void *out, int64_t n, int64_t tok0, int nseg,
                                  const float *o0pre, const TaylorArgs &ta, sata_dtype out_dt, hipStream_t stream) {
     auto go = [&](auto dw, auto cw) -> hipError_t {
-        constexpr int DD = decltype(dw)::value, CC = decltype(cw)::value;
-        if (out_dt == SATA_F32) return run_scan16<DD, CC, float>(idx, st, plan, q, k, v, out, n, tok0, nseg, o0pre, ta, stream);
-        return run_scan16<DD, CC, bf16_t>(idx, st, plan, q, k, v, out, n, tok0, nseg, o0pre, ta, stream);
+        constexpr int DD = decltype(dw)::value, CC = decltype(cw)::value, MX = scan16_mt_max(DD);
+        if (plan.mt == MX) {
+            if (out_dt == SATA_F32)
+                return run_scan16<DD, CC, MX, float>(idx, st, plan, q, k, v, out, n, tok0, nseg, o0pre, ta, stream);
+            return run_scan16<DD, CC, MX, bf16_t>(idx, st, plan, q, k, v, out, n, tok0, nseg, o0pre, ta, stream);
+        }
+        if (plan.mt != 1) return hipErrorInvalidValue;   // never planned
+        if (out_dt == SATA_F32)
+            return run_scan16<DD, CC, 1, float>(idx, st, plan, q, k, v, out, n, tok0, nseg, o0pre, ta, stream);
+        return run_scan16<DD, CC, 1, bf16_t>(idx, st, plan, q, k, v, out, n, tok0, nseg, o0pre, ta, stream);
     };
     using C64 = std::integral_constant<int, 64>;
     using C128 = std::integral_constant<int, 128>;

@@ -137,6 +137,30 @@ def test_bf16_eight_wave_shapes_every_row(sata, oracle, d, heads, chunk):
     assert err <= TOL_BF16
 
 
+# bf16 inputs with d_K = d_V in {16, 32, 64}, P <= 4 run the fp16-operand scan, whose update
+# wavefronts hold the largest number of positions their registers allow (5, 3, 2 at d = 16, 32,
+# 64) unless that leaves fewer (head, slice) work items than compute units; then one.  The
+# planned slice count shows which ran: (d, heads, slices).
+@pytest.mark.parametrize("d,heads,slices", [(16, 320, 1), (16, 4, 5), (32, 32, 10), (32, 4, 30),
+                                            (64, 4, 102), (64, 1, 204)])
+def test_fp16_scan_both_slice_widths(sata, oracle, d, heads, slices):
+    P, chunk = 4, 128
+    n = 2 * chunk + 45
+    plan = sata.sata_describe_prefill_plan(d, P, heads, n, chunk, sata.SATA_BF16)
+    say("prefill bf16 d=%d heads=%d n=%d: %d slices per head" % (d, heads, n, plan["slices"]))
+    assert plan["slices"] == slices
+    x = si.draw_qkv((1, heads), n, d, d, 5353 + d + heads, "bf16")
+    idx = sata.Index(d, d, P)
+    st = sata.State(idx, 1, heads)
+    q, k, v = dev_all(x)
+    o = prefill(idx, st, q, k, v, chunk=chunk).cpu().numpy()
+    hs = sorted({0, min(1, heads - 1), heads // 2, heads - 1})
+    sub = lambda a: np.ascontiguousarray(a[:, hs])
+    err = rel_err(o[:, hs], oracle.taylor_attention(sub(x.q), sub(x.k), sub(x.v), P))
+    say("  heads %s: err %.3e" % (hs, err))
+    assert err <= TOL_BF16
+
+
 def test_short_sequences_and_empty(sata, oracle):
     d, P = 16, 4
     idx = sata.Index(d, d, P)
