@@ -541,9 +541,10 @@ def cpu_baseline(wl, x, budget_s: float):
 COPY_BYTES = 1 << 30
 # kernel-name pattern -> (kernel, workload, source file)
 TRAFFIC_KERNELS = [
-    (r"prefill_scan_kernel<64, 64, 128, \d+, \d+, unsigned short, false>", "prefill_scan", "prefill_d64_p4_bf16", "sata_prefill.hip"),
-    (r"prefill_scan_ws_kernel<32, 32, 64, \d+, false>", "prefill_scan", "prefill_d32_p4_bf16", "sata_prefill.hip"),
-    (r"prefill_scan_ws_kernel<16, 16, 128, \d+, false>", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_prefill.hip"),
+    # the fp16-operand scan (its names stay mangled in rocprofv3 output): D, C, positions per wave
+    (r"scan16_kernelILi64ELi128ELi2E", "prefill_scan", "prefill_d64_p4_bf16", "sata_scan16.hip"),
+    (r"scan16_kernelILi32ELi64ELi3E", "prefill_scan", "prefill_d32_p4_bf16", "sata_scan16.hip"),
+    (r"scan16_kernelILi16ELi128ELi1E", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_scan16.hip"),
     (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_rows_kernel<64, float, unsigned short, true>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
