@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libsata.so")
 ARCH = os.environ.get("SATA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["sata_host.cpp", "sata_decode.hip", "sata_prefill.hip", "sata_scan16.hip", "sata_expand.hip",
-           "sata_backward.hip"]
+           "sata_backward.hip", "sata_measure.hip"]
 
 # Packed-fp32 VALU instructions are switched off for every device pass.
 HIPCC_FLAGS = [

@@ -187,6 +187,9 @@ hipError_t run_pass(TempState &ts, int64_t heads, const void *q, const void *k, 
                     int64_t n, int chunk, sata_dtype in_dt, bool raw, hipStream_t s) {
     const sata_index *idx = ts.st.idx;
     PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt);
+    // fewer heads than the state was made for can fit more chunks under the default cap than
+    // its workspace holds: plan again under the workspace it has (shorter segments)
+    if (plan.ok && plan.work_bytes > ts.st.work_bytes) plan = plan_prefill(idx, heads, n, chunk, in_dt, ts.st.work_bytes);
     if (!plan.ok || heads > ts.max_heads || plan.work_bytes > ts.st.work_bytes) return hipErrorInvalidValue;
     plan.raw = raw;
     plan.den_out = den;
@@ -197,6 +200,9 @@ hipError_t run_pass(TempState &ts, int64_t heads, const void *q, const void *k, 
     return launch_prefill(idx, &ts.st, plan, q, k, v, out, n, in_dt, SATA_F32, s);
 }
 
+// The step of the running backward call (per host thread), for the error message of a failure.
+thread_local const char *t_bw_step = "";
+
 template <typename TIn, typename TOut>
 hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh, const void *qv, const void *kv,
                       const void *vv, const void *doutv, void *dqv, void *dkv, void *dvv, int64_t n, int chunk,
@@ -204,6 +210,7 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     const int D = idx->dk;
     const TIn *q = static_cast<const TIn *>(qv), *k = static_cast<const TIn *>(kv), *v = static_cast<const TIn *>(vv);
     const int64_t elems = bh * n * D;
+    t_bw_step = "temporaries";
     Arena ar;
     float *o = ar.get<float>(elems), *z = ar.get<float>(bh * n), *g = ar.get<float>(bh * n * (D + 1));
     float *r = ar.get<float>(elems);
@@ -215,9 +222,12 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     hipError_t e = launch_zero(reinterpret_cast<float *>(err), 1, s);
     if (e != hipSuccess) return e;
     TempState top;
+    t_bw_step = "state of the P-order passes";
     if ((e = top.make(ar, idx, bh, n, chunk, in_dt, err)) != hipSuccess) return e;
     // 1. forward: o and z
+    t_bw_step = "forward pass";
     if ((e = run_pass(top, bh, q, k, v, o, z, n, chunk, in_dt, false, s)) != hipSuccess) return e;
+    t_bw_step = "inputs of the dv pass";
     hipLaunchKernelGGL(bw_prep_g<TIn>, dim3(bw_grid(bh * n)), dim3(kBwThreads), 0, s,
                        static_cast<const TIn *>(doutv), o, z, g, bh * n, D);
     // 2. dv: reversed time, queries k, keys q, values g[:d_V], P orders
@@ -225,7 +235,9 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     hipLaunchKernelGGL(bw_reverse<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, q, rk, bh, n, D);
     hipLaunchKernelGGL(bw_rev_g<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, g, rg, bh, n, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    t_bw_step = "dv pass";
     if ((e = run_pass(top, bh, rq, rk, rg, r, nullptr, n, chunk, in_dt, true, s)) != hipSuccess) return e;
+    t_bw_step = "dk and dq accumulators";
     hipLaunchKernelGGL(bw_finish_dv<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, r, static_cast<TOut *>(dvv),
                        bh, n, D);
     // 3. dk and dq: P - 1 orders, one pseudo-head per column c in groups of cg
@@ -242,23 +254,28 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
         float *gr = ar.get<float>(elems * cg);
         if (ar.err != hipSuccess) return ar.err;
         TempState low;
+        t_bw_step = "state of the (P-1)-order passes";
         if ((e = low.make(ar, lower, bh * cg, n, chunk, in_dt, err)) != hipSuccess) return e;
         const float sc = 1.0f / sqrtf((float)D);
         for (int pass = 0; pass < 2; ++pass) {
             const int kdk = pass == 0 ? 1 : 0;
             for (int c0 = 0; c0 <= D; c0 += cg) {
                 const int n_c = std::min(cg, D + 1 - c0);
+                t_bw_step = kdk ? "inputs of a dk pass" : "inputs of a dq pass";
                 hipLaunchKernelGGL(bw_group_inputs<TIn>, dim3(bw_grid(elems * n_c)), dim3(kBwThreads), 0, s, q, k, v,
                                    g, gq, gk, gv, bh, n, D, c0, n_c, kdk);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
+                t_bw_step = kdk ? "dk pass" : "dq pass";
                 if ((e = run_pass(low, bh * n_c, gq, gk, gv, gr, nullptr, n, chunk, in_dt, true, s)) != hipSuccess)
                     return e;
+                t_bw_step = "contraction";
                 hipLaunchKernelGGL(bw_contract<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, gr, v, g,
                                    kdk ? acc_k : acc_q, bh, n, D, c0, n_c, kdk, sc);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
         }
     }
+    t_bw_step = "gradient output";
     hipLaunchKernelGGL(bw_cast<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, acc_k, static_cast<TOut *>(dkv), elems);
     hipLaunchKernelGGL(bw_cast<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, acc_q, static_cast<TOut *>(dqv), elems);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -270,6 +287,8 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
 }
 
 }  // namespace
+
+const char *backward_last_step() { return t_bw_step; }
 
 hipError_t launch_backward(const sata_index *idx, const sata_index *lower, int64_t bh, const void *q, const void *k,
                            const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n, int chunk,

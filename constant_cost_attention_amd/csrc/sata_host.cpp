@@ -754,6 +754,14 @@ sata_status sata_prefill_noalloc(const sata_index *idx, sata_state *st, const vo
     return SATA_OK;
 }
 
+sata_status sata_measure_mfma_loop(int bf16, double *tflops) {
+    g_last_error.clear();
+    if (!tflops) return fail(SATA_ERR_INVALID, "tflops is NULL");
+    const hipError_t e = sata::measure_mfma_loop(bf16 != 0, tflops);
+    if (e != hipSuccess) return fail_hip(e, "MFMA loop measurement");
+    return SATA_OK;
+}
+
 sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, const void *q, const void *k,
                                   const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n, int chunk,
                                   sata_dtype in_dt, sata_dtype grad_dt, void *stream) {
@@ -801,7 +809,10 @@ sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, c
     if (e == hipErrorLaunchTimeOut)
         return fail(SATA_ERR_HIP, "backward: a prefill scan work item gave up waiting for the state of its "
                                   "predecessor (the gradients are invalid)");
-    if (e != hipSuccess) return fail_hip(e, "backward");
+    if (e != hipSuccess) {
+        const std::string what = std::string("backward (") + sata::backward_last_step() + ")";
+        return fail_hip(e, what.c_str());
+    }
     return SATA_OK;
 }
 

@@ -151,6 +151,8 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
 hipError_t launch_backward(const sata_index *idx, const sata_index *lower, int64_t bh, const void *q, const void *k,
                            const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n, int chunk,
                            sata_dtype in_dt, sata_dtype out_dt, int64_t mem_budget, hipStream_t s);
+// The step the calling thread's last backward call was in (for error messages).
+const char *backward_last_step();
 // fp16-operand scan (sata_scan16.hip): positions per slice and the operand image of one chunk
 int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus);
 int64_t scan16_image_bytes(int dk, int chunk);
@@ -180,6 +182,8 @@ struct ProfScope {
 };
 
 hipError_t launch_zero(float *p, int64_t count, hipStream_t stream);
+// Dense TFLOP/s of a plain 16x16x32 MFMA loop on the current device (sata_measure.hip).
+hipError_t measure_mfma_loop(bool bf16, double *tflops);
 
 // Error bits a kernel may set in a state's error word.
 constexpr uint32_t kErrScanWait = 1u;

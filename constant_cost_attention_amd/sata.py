@@ -31,7 +31,7 @@ _EXPORTS = (
     "sata_prefill", "sata_prefill_noalloc", "sata_prefill_backward", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
-    "sata_describe_prefill_plan", "sata_debug_scan_faults",
+    "sata_describe_prefill_plan", "sata_debug_scan_faults", "sata_measure_mfma_loop",
 )
 
 _lib = None
@@ -99,6 +99,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_status_string.restype = ctypes.c_char_p
     lib.sata_last_error.argtypes = []
     lib.sata_last_error.restype = ctypes.c_char_p
+    lib.sata_measure_mfma_loop.argtypes = [cint, ctypes.POINTER(ctypes.c_double)]
+    lib.sata_measure_mfma_loop.restype = cint
     lib.sata_profile_enable.argtypes = [cint]
     lib.sata_profile_query.argtypes = [cint, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     lib.sata_profile_kernel_name.argtypes = [cint]
@@ -264,6 +266,13 @@ def sata_describe_prefill_plan(d_k: int, P: int, batch_heads: int, n: int, chunk
     if wb < 0:
         raise SataError(SATA_ERR_INVALID, "sata_describe_prefill_plan", lib.sata_last_error().decode())
     return {"work_bytes": wb, "seg_chunks": seg.value, "slices": sl.value}
+
+
+def sata_measure_mfma_loop(bf16: bool = True) -> float:
+    """Dense TFLOP/s of a plain 16x16x32 MFMA loop on the current device (a measured ceiling)."""
+    t = ctypes.c_double()
+    _check(load().sata_measure_mfma_loop(1 if bf16 else 0, ctypes.byref(t)), "sata_measure_mfma_loop")
+    return t.value
 
 
 def sata_state_reset(state: State, stream=None):

@@ -241,6 +241,16 @@ sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, c
                                   const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n,
                                   int chunk, sata_dtype in_dt, sata_dtype grad_dt, void *stream);
 
+/* Measurement helper for benchmarks (not part of the attention path): runs a
+ * loop of v_mfma_f32_16x16x32 instructions (bf16 operands when bf16 != 0,
+ * else fp16; fp32 accumulation; 16 independent accumulator chains per
+ * wavefront and nothing else in the loop) on every compute unit of the
+ * current device, two wavefronts per SIMD, and writes the dense TFLOP/s it
+ * reaches to *tflops: the ceiling a kernel made of such instructions can
+ * reach on this device, beside the published peak.  Synchronous; allocates
+ * and frees a small output buffer and two events. */
+sata_status sata_measure_mfma_loop(int bf16, double *tflops);
+
 /* One decode step for every head: with q, k: [batch][heads][d_K] and
  * v: [batch][heads][d_V] of the new token, add phi(k) (x) [v, 1] to every
  * order's state, then read out and normalise into out: [batch][heads][d_V]
