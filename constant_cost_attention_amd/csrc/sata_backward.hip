@@ -167,7 +167,7 @@ struct TempState {
     int64_t max_heads = 0;
     hipError_t make(Arena &ar, const sata_index *idx, int64_t heads, int64_t n, int chunk, sata_dtype in_dt,
                     uint32_t *err) {
-        const PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt);
+        const PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt, kWorkCap, false);
         if (!plan.ok) return hipErrorInvalidValue;
         st.d_err = err;
         st.idx = idx;
@@ -186,10 +186,13 @@ struct TempState {
 hipError_t run_pass(TempState &ts, int64_t heads, const void *q, const void *k, const void *v, float *out, float *den,
                     int64_t n, int chunk, sata_dtype in_dt, bool raw, hipStream_t s) {
     const sata_index *idx = ts.st.idx;
-    PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt);
+    // The passes' inputs are weighted by the gradient (g = dout / z, small for long sequences),
+    // below fp16's normal range: they plan without the fp16-operand scan.
+    PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt, kWorkCap, false);
     // fewer heads than the state was made for can fit more chunks under the default cap than
     // its workspace holds: plan again under the workspace it has (shorter segments)
-    if (plan.ok && plan.work_bytes > ts.st.work_bytes) plan = plan_prefill(idx, heads, n, chunk, in_dt, ts.st.work_bytes);
+    if (plan.ok && plan.work_bytes > ts.st.work_bytes)
+        plan = plan_prefill(idx, heads, n, chunk, in_dt, ts.st.work_bytes, false);
     if (!plan.ok || heads > ts.max_heads || plan.work_bytes > ts.st.work_bytes) return hipErrorInvalidValue;
     plan.raw = raw;
     plan.den_out = den;

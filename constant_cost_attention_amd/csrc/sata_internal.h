@@ -143,8 +143,11 @@ struct PrefillPlan {
 // calls run in segments of whole chunks; when the allocation fails, sata_prefill plans again
 // under half the cap, down to one chunk per segment.
 constexpr int64_t kWorkCap = (int64_t)16 << 30;
+// fp16_operands: bf16 inputs may take the fp16-operand scan (exact for inputs inside fp16's
+// normal range once scaled; callers whose inputs can be far smaller, such as the backward's
+// gradient-weighted passes, plan without it).
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt,
-                         int64_t work_cap = kWorkCap);
+                         int64_t work_cap = kWorkCap, bool fp16_operands = true);
 // Backward pass of a causal prefill from a zero state (sata_backward.hip);
 // lower is the index with P - 1 orders (NULL when P == 1).  Synchronises the
 // stream before returning (it frees its temporaries).

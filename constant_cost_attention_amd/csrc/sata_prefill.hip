@@ -1730,12 +1730,14 @@ static ScanShape pick_shape(const sata_index *idx, int64_t bh, int chunk, sata_d
     return {kNW, 2, false};
 }
 
-PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt, int64_t work_cap) {
+PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt, int64_t work_cap,
+                         bool fp16_operands) {
     PrefillPlan p;
     p.chunk = chunk ? chunk : (idx->dk == 64 ? 128 : 64);
     if (p.chunk != 64 && p.chunk != 128) return p;
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
-    if (in_dt == SATA_BF16 && idx->np16 > 0 && idx->dk == idx->dv && (idx->dk == 16 || idx->dk == 32 || idx->dk == 64)) {
+    if (fp16_operands && in_dt == SATA_BF16 && idx->np16 > 0 && idx->dk == idx->dv &&
+        (idx->dk == 16 || idx->dk == 32 || idx->dk == 64)) {
         // fp16-operand scan: fp16 partials and one operand image per chunk of a segment
         p.s16 = true;
         p.mt = scan16_choose_mt(idx->dk, idx->np16, bh, idx->cus);

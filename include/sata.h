@@ -186,7 +186,13 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
  * within a chunk the Taylor weights are formed directly, across chunks the
  * orders' states are scanned and read out [hotdry, "Engineering realisation
  * of the constant compute cost"]; results do not depend on the chunk length
- * beyond rounding.  n = 0 is a no-op.  May grow the state's workspace
+ * beyond rounding.  For bf16 inputs with d_K = d_V in {16, 32, 64} and
+ * P <= 4 the scan's matrix operands are fp16: k / 4, 4 q / sqrt(d_K) and v
+ * convert to fp16 exactly when their magnitudes lie in fp16's normal range
+ * (6.1e-5 to 65504, or zero); smaller ones keep less precision and larger
+ * ones overflow.  Rows of q and k of norm up to d_K^(1/4) and v of unit
+ * scale lie well inside; give inputs far outside that scale as fp32.
+ * n = 0 is a no-op.  May grow the state's workspace
  * (hipMalloc) on the first call at a given size: the partial readouts of up
  * to 16 GB are planned at once (longer calls run in segments of whole chunks);
  * if that allocation fails, the call plans again under half the workspace,

@@ -98,6 +98,54 @@ def test_backward_workload_d16_f32(sata, oracle):
     _check(oracle, x, do_np, wl.P, got, TOL_GRAD_F32, wl.name)
 
 
+def test_backward_d64_bf16_workload_heads(sata, oracle):
+    """The d_K = 64, P = 4 bf16 workload's head count (1 x 8) on 8192 tokens (the oracle's
+    n x n weights bound n), two heads against O9."""
+    d, P, n = 64, 4, 8192
+    x = si.draw_qkv((1, 8), n, d, d, 4646, "bf16")
+    dout = torch.from_numpy(np.random.default_rng(4647).standard_normal((1, 8, n, d)).astype(np.float32)).cuda()
+    idx = sata.Index(d, d, P)
+    say("backward bf16 d=64 P=4, 1 x 8 heads x %d tokens" % n)
+    got, do_np = _run(sata, idx, x, dout, chunk=128)
+    hs = [0, 7]
+    sub = lambda a: np.ascontiguousarray(a[:, hs])
+    xs = si.QKV(sub(x.q), sub(x.k), sub(x.v), "f32")
+    _check(oracle, xs, sub(do_np), P, [sub(g) for g in got], TOL_BF16, "heads 0, 7")
+    idx.free()
+
+
+def test_backward_d64_bf16_workload_full_size(sata):
+    """The full d_K = 64 workload (1 x 8 heads x 65536 tokens, bf16), whose passes plan
+    workspaces near the 16 GB cap, where O9 cannot run: properties that hold at any size.
+    Every pass is linear in dout, and the passes run on bf16 / fp32 operands whose exponent
+    range holds the gradient-weighted values, where scaling by two commutes with every
+    rounding: doubling dout doubles every gradient bit for bit.  The attention weights of each
+    query sum to one, so sum_j dv_j = sum_i dout_i (normwise within the bf16-input bar)."""
+    wl = si.WORKLOADS["prefill_d64_p4_bf16"]
+    say("backward full size %s" % wl.name)
+    q, k, v = si.draw_qkv_device((wl.batch, wl.heads), wl.n, wl.d_k, wl.d_v, wl.seed, "bf16")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4648)
+    do = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    grads = []
+    for scale in (1.0, 2.0):
+        g = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+        sata.sata_prefill_backward(idx, q, k, v, (do.float() * scale).to(torch.bfloat16), *g, chunk=wl.chunk)
+        torch.cuda.synchronize()
+        grads.append(g)
+    for name, a, b in zip(("dq", "dk", "dv"), grads[0], grads[1]):
+        assert torch.isfinite(a).all(), name
+        say("  %s: doubling dout doubles it exactly: %s" % (name, bool(torch.equal(b, 2 * a))))
+        assert torch.equal(b, 2 * a), name
+    dv_sum = grads[0][2].double().sum(dim=2)                  # [B, H, d_V]
+    do_sum = do.double().sum(dim=2)
+    err = float(((dv_sum - do_sum).abs().amax(-1) / do_sum.abs().amax(-1)).max())
+    say("  sum dv vs sum dout: %.3e" % err)
+    assert err <= TOL_BF16
+    idx.free()
+
+
 def test_backward_error_paths(sata):
     idx = sata.Index(16, 16, 4)
     q = torch.zeros((1, 1, 8, 16), device="cuda")
