@@ -117,7 +117,13 @@ sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *
  * rounded to the nearest bf16 (ties to even), so the step streams half the
  * bytes of the fp32 state [hotdry, "Hardware optimisation paths and current
  * limits": half-precision storage halves the bandwidth of the state] at the
- * price of one bf16 rounding per element per step.  sata_prefill on it returns
+ * price of one bf16 rounding per element per step.  Those roundings
+ * accumulate: with P = 4 and d_K >= 16 the outputs of up to 16 decode steps
+ * after a conversion stay within 2e-2 (the bar of the bf16 paths) of the
+ * exact Taylor attention, and the error keeps growing with the number of
+ * steps (about 3e-2 after 64); fewer orders or smaller heads drift faster.
+ * Use it for short decodes after a long prefill; the fp32 state is exact to
+ * fp32 rounding at any length.  sata_prefill on it returns
  * SATA_ERR_UNSUPPORTED: prefill into an fp32 state and convert.  An unknown
  * state_dt returns SATA_ERR_INVALID. */
 sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, sata_dtype state_dt,

@@ -137,6 +137,43 @@ def test_bf16_state_workload_d64_after_8192(sata, oracle):
         assert err <= TOL_BF16_STATE + DRIFT_SHARE * drift
 
 
+# The supported use of a bf16 state (include/sata.h): with P = 4 and d_K >= 16, up to
+# BF16_STATE_STEPS decode steps after a conversion stay within the bf16-path bar of the
+# exact Taylor output (O1), not only of the rounding emulation.
+BF16_STATE_STEPS = 16
+
+
+@pytest.mark.parametrize("wl_name,pairs", [("decode_d64_p4_f32", ((0, 0), (31, 7))),
+                                           ("prefill_d16_p4_f32", ((0, 0), (0, 7)))])
+def test_bf16_state_supported_steps_against_exact(sata, oracle, wl_name, pairs):
+    wl = si.WORKLOADS[wl_name]
+    steps = BF16_STATE_STEPS
+    say("bf16-state decode %s: %d steps after the %d-token prefix against O1" % (wl.name, steps, wl.n))
+    pre = wl.draw()
+    dec = si.draw_qkv((wl.batch, wl.heads), steps, wl.d_k, wl.d_v, wl.seed + 31, "f32")
+    idx = sata.Index(wl.d_k, wl.d_v, wl.P)
+    q, k, v = dev_all(pre)
+    st32, st = _bf16_state_from_prefill(sata, idx, wl.batch, wl.heads, q, k, v)
+    st32.free()
+    del q, k, v
+    dq, dk_, dv_ = dev_all(dec)
+    outs = [decode(idx, st, dq[:, :, t].contiguous(), dk_[:, :, t].contiguous(), dv_[:, :, t].contiguous())
+            for t in range(steps)]
+    o = torch.stack(outs, dim=2).cpu().numpy()
+    worst = 0.0
+    for b, h in pairs:
+        qa = np.concatenate([pre.q[b, h], dec.q[b, h]], axis=0)[None]
+        ka = np.concatenate([pre.k[b, h], dec.k[b, h]], axis=0)[None]
+        va = np.concatenate([pre.v[b, h], dec.v[b, h]], axis=0)[None]
+        exact = oracle.taylor_attention(qa, ka, va, wl.P, rows=np.arange(wl.n, wl.n + steps, dtype=np.int64))[0]
+        err = rel_err(o[b, h], exact)
+        say("  head (%d, %d): %d steps, err vs exact %.3e" % (b, h, steps, err))
+        worst = max(worst, err)
+    assert worst <= TOL_BF16
+    st.free()
+    idx.free()
+
+
 def test_bf16_state_error_paths(sata):
     idx = sata.Index(16, 16, 4)
     st16 = sata.State(idx, 1, 2, dtype=torch.bfloat16)
