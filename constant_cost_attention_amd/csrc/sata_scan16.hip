@@ -159,23 +159,20 @@ struct S16Cfg {
     static constexpr int NC = D + 1, NT = (NC + 15) / 16, NTF = NT - 1;   // NTF full tiles + the normaliser tile
     static constexpr int NP = NU * MT;                  // positions (16 quads, 64 features) per slice
     static constexpr int NKS = 2 * NP;                  // readout K steps per slice: two slots of a position
-    static constexpr int KPR = NKS / 2;                 // per readout wavefront (half the slice)
-    static constexpr int TT = C / 16, TPW = TT / 2;     // token tiles per chunk, per readout wavefront
-    static constexpr int TKEEP = TPW / 2;               // tiles a readout wavefront finalises
+    static constexpr int TT = C / 16, TPW = TT / NR;    // token tiles per chunk, per readout wavefront
     static constexpr int UKS = C / 32;                  // update K steps per chunk
     using I = Img16<D, C>;
     static constexpr int OFF_CP = 0;                                     // copy [NKS][NTF][64] x 16 B
     static constexpr int OFF_CL = OFF_CP + NKS * NTF * 64 * 16;          // normaliser tile [NKS][4] x 16 B, zero entry
     static constexpr int OFF_IMG = OFF_CL + (NKS * 4 + 1) * 16;
-    static constexpr int OFF_EX = OFF_IMG + I::BYTES;                    // exchange [NR][TKEEP][NT][64] x 16 B
-    static constexpr int OFF_W0 = OFF_EX + NR * TKEEP * NT * 64 * 16;    // quad words [NP][16]
+    static constexpr int OFF_W0 = OFF_IMG + I::BYTES;                    // quad words [NP][16]
     static constexpr int OFF_QC = OFF_W0 + NP * 16 * 4;                  // quad weights [NP][16] x 4
     static constexpr int OFF_FL = OFF_QC + NP * 16 * 16;                 // position flags [NP]
     static constexpr int LDS = OFF_FL + NP * 4;
     static constexpr int UNITS = I::BYTES / 16;
     static constexpr int UPT = (UNITS + 64 * NR - 1) / (64 * NR);       // image units per readout thread
     static_assert(NC == 16 * NTF + 1, "the last column tile holds the normaliser alone");
-    static_assert(C % 64 == 0 && TPW % 2 == 0, "64 or 128 tokens per chunk");
+    static_assert(C % 64 == 0 && TT % NR == 0 && NKS % 2 == 0 && NKS >= 4, "64 or 128 tokens per chunk");
     static_assert(NP <= 32, "position flags fit a 32-bit mask");
     static_assert(LDS + 128 <= 160 * 1024, "LDS budget (the kernel adds its item record, 112 bytes)");
 };
@@ -206,6 +203,9 @@ __device__ __forceinline__ float partial_scale(float tokens_before, int C) {
 #define S16_GLOBAL __attribute__((address_space(1)))
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Word 3 of a raw buffer descriptor on this architecture: 32-bit data format, no swizzle, no
+// index stride (loads of whole dwords; the range check uses the descriptor's byte count).
+constexpr int kRawBufferWord3 = 0x00020000;
 
 // LDS pointers of the role functions.  Outside a kernel, the dynamic LDS block is found through a
 // per-kernel table in global memory; under register pressure the compiler reloads that base
@@ -268,11 +268,10 @@ __device__ __forceinline__ S16Item item_from_lds(const S16Item *s) {
 // of both across the kernel.  Each role derives its wavefront index (uniform, a scalar register,
 // so loop bounds and branches on it stay scalar) and its lane itself.
 
-// Readout wavefront rw: token half th = rw & 1 (token tiles TPW th ..), feature half
-// fh = rw >> 1 (K steps KPR fh ..).  Per chunk: Y = psi(Q_c)[tiles, half] . S^(c-1)[half, :]
-// from the fp16 state copy, handed half to the partner (rw ^ 2) in fp32 through LDS, and the
-// finalised tiles stored as fp16 partials.  Also stages each next chunk's image through its
-// registers.
+// Readout wavefront rw: token tiles TPW rw .. of the chunk, against every feature of the slice.
+// Per chunk: Y = psi(Q_c)[tiles] . S^(c-1)[slice, :] from the fp16 state copy, with the K step's
+// B operand loaded one step ahead (two register buffers), then the tiles stored as fp16
+// partials.  Also stages each next chunk's image through its registers.
 template <int D, int C, int MT>
 __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     const S16Item it = item_from_lds(sit);
@@ -280,28 +279,34 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     const int lane = __lane_id();
     using Cfg = S16Cfg<D, C, MT>;
     using I = typename Cfg::I;
-    constexpr int NR = Cfg::NR, NC = Cfg::NC, NT = Cfg::NT, NTF = Cfg::NTF, KPR = Cfg::KPR;
-    constexpr int TT = Cfg::TT, TPW = Cfg::TPW, TKEEP = Cfg::TKEEP, UPT = Cfg::UPT, QS = I::QS;
+    constexpr int NR = Cfg::NR, NC = Cfg::NC, NT = Cfg::NT, NTF = Cfg::NTF, NKS = Cfg::NKS;
+    constexpr int TPW = Cfg::TPW, UPT = Cfg::UPT, QS = I::QS;
     const uint32_t lb = s16_lds_base();
     const S16_LDS u32x4 *CP = s16_lds<const u32x4>(lb, Cfg::OFF_CP);
     const S16_LDS u32x4 *CL = s16_lds<const u32x4>(lb, Cfg::OFF_CL);
     const S16_LDS f16 *Qs = s16_lds<const f16>(lb, Cfg::OFF_IMG + I::Q_OFF);
-    S16_LDS f32x4 *EX = s16_lds<f32x4>(lb, Cfg::OFF_EX);
     const S16_LDS uint32_t *W0 = s16_lds<const uint32_t>(lb, Cfg::OFF_W0);
     const int g = lane >> 4, li = lane & 15;
-    const int th = rw & 1, fh = rw >> 1, partner = rw ^ 2;
-    const int kbeg = fh * KPR, kend = kbeg + KPR;
-    const int tbase = th * TPW;               // first token tile of this wave
+    const int tbase = rw * TPW;               // first token tile of this wave
     const int rtid = rw * 64 + lane;          // 0 .. 64 NR - 1
     uint4 pre[UPT];
     auto fetch = [&](int cc) {
-        const S16_GLOBAL u32x4 *src = reinterpret_cast<const S16_GLOBAL u32x4 *>(it.img + (int64_t)cc * I::BYTES);
+        // buffer loads: the chunk's image in a descriptor (uniform), one 32-bit offset per lane
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(it.img + (int64_t)cc * I::BYTES), 0, I::BYTES, kRawBufferWord3);
+        const int v0 = rtid * 16;
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
-            const int un = rtid + i * 64 * NR;
-            // every lane loads (the last ones repeat the final unit, which stage() skips): a fixed
-            // number of loads in flight lets later waits count past them instead of draining all
-            pre[i] = __builtin_bit_cast(uint4, src[un < Cfg::UNITS ? un : Cfg::UNITS - 1]);
+            // every lane loads (in the last pass the lanes past the image repeat its final unit,
+            // which stage() skips): a fixed number of loads in flight lets later waits count
+            // past them instead of draining all
+            if ((i + 1) * 64 * NR <= Cfg::UNITS) {
+                pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, v0, i * 64 * NR * 16, 0));
+            } else {
+                const int un = rtid + i * 64 * NR;
+                const int off = (un < Cfg::UNITS ? un : Cfg::UNITS - 1) * 16;
+                pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            }
         }
     };
     auto stage = [&]() {
@@ -326,8 +331,6 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     for (int tt = 0; tt < TPW; ++tt) qrow[tt] = Qs + (16 * (tbase + tt) + li) * QS;
     const S16_LDS u32x4 *clast = li == 0 ? CL + g : CL + Cfg::NKS * 4;   // normaliser lanes, else the zero entry
     const int clast_step = li == 0 ? 4 : 0;
-    // partials: [chunk][TT][NC][16 tokens] fp16 per (head, slice)
-    // (tile indices stay compile-time constants: a runtime index into Y would put it in scratch)
     // Token count before each chunk (the normaliser entry of its order-0 prefix), loaded one
     // chunk ahead through the vector memory path (a lane-opaque offset keeps it off the scalar
     // cache, whose wait would also stall every LDS wait in between).
@@ -335,23 +338,22 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
     __asm__ volatile("" : "+v"(opq));
     auto count_before = [&](int cc) { return it.o0pre[(it.chunk0 + cc) * NC + D + opq]; };
     float cnt_next = count_before(it.cbeg);
-    auto receive_store = [&](int cc, float cnt) {
+    // partials: [chunk][TT][NC][16 tokens] fp16 per (head, slice)
+    // (tile indices stay compile-time constants: a runtime index into Y would put it in scratch)
+    auto store_partials = [&](int cc, float cnt) {
         const float sc = partial_scale(cnt, C);
         S16_GLOBAL f16 *pd = it.partial + it.pbase + cc * it.pstride + (int64_t)tbase * NC * 16 + (li * 16 + 4 * g);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            if (tt / TKEEP != fh) continue;   // uniform
+        for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const f32x4 y = Y[tt][nt] + EX[((partner * TKEEP + tt % TKEEP) * NT + nt) * 64 + lane];
                 if (nt < NTF || li == 0) {
-                    const f16x2 a = {(f16)(y[0] * sc), (f16)(y[1] * sc)};
-                    const f16x2 b = {(f16)(y[2] * sc), (f16)(y[3] * sc)};
+                    const f16x2 a = {(f16)(Y[tt][nt][0] * sc), (f16)(Y[tt][nt][1] * sc)};
+                    const f16x2 b = {(f16)(Y[tt][nt][2] * sc), (f16)(Y[tt][nt][3] * sc)};
                     *reinterpret_cast<S16_GLOBAL u32x2 *>(pd + (tt * NC + 16 * nt) * 16) =
                         u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
                 }
             }
-        }
     };
     // prefix factors of the lane's four streams (4g .. 4g+3) for its token in each tile
     f16x2 pc[TPW][2];
@@ -374,52 +376,67 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
             }
         }
     };
-    // one K step: the first of a chunk starts the accumulators from zero (the MFMA's constant
-    // operand), every other adds to them
-    auto kstep = [&](int kk, auto first) {
+    // B operand of K step kk: the NTF tiles of the state copy and the normaliser entry
+    auto loadB = [&](int kk, f16x8 (&B)[NT]) {
+#pragma unroll
+        for (int nt = 0; nt < NTF; ++nt) B[nt] = __builtin_bit_cast(f16x8, CP[(kk * NTF + nt) * 64 + lane]);
+        B[NTF] = __builtin_bit_cast(f16x8, clast[kk * clast_step]);
+    };
+    // A operand of K step kk for each token tile (LDS reads of the query image, and the prefix
+    // factors regrouped where a position starts)
+    auto formA = [&](int kk, f16x8 (&A)[TPW], auto first) {
         const int p = kk >> 1, h = kk & 1;
         if (first || (h == 0 && ((it.gstart >> p) & 1u))) {
             __asm__ volatile("" ::: "memory");
             regroup(p);
         }
-        f16x8 B[NT];
-#pragma unroll
-        for (int nt = 0; nt < NTF; ++nt) B[nt] = __builtin_bit_cast(f16x8, CP[(kk * NTF + nt) * 64 + lane]);
-        B[NTF] = __builtin_bit_cast(f16x8, clast[kk * clast_step]);
         const int xo = 4 * qd_b(W0[p * 16]) + 2 * h;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const f16x2 x = *reinterpret_cast<const S16_LDS f16x2 *>(qrow[tt] + xo);
             const f16x2 xl = {x[0], x[0]}, xh = {x[1], x[1]};
             const f16x2 a0 = pc[tt][0] * xl, a1 = pc[tt][1] * xl, a2 = pc[tt][0] * xh, a3 = pc[tt][1] * xh;
-            const f16x8 A = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                Y[tt][nt] = mfma_f16(A, B[nt], first ? f32x4{0.f, 0.f, 0.f, 0.f} : Y[tt][nt]);
+            A[tt] = f16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
         }
     };
-    float cnt_prev = 0.f;
+    // the MFMAs of one K step: the first of a chunk starts the accumulators from zero (the
+    // MFMA's constant operand), every other adds to them
+    auto mma = [&](const f16x8 (&A)[TPW], const f16x8 (&B)[NT], auto first) {
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                Y[tt][nt] = mfma_f16(A[tt], B[nt], first ? f32x4{0.f, 0.f, 0.f, 0.f} : Y[tt][nt]);
+    };
     for (int cc = it.cbeg; cc < it.cend; ++cc) {
-        if (cc > it.cbeg) receive_store(cc - 1, cnt_prev);
-        cnt_prev = cnt_next;
+        const float cnt_cur = cnt_next;
         cnt_next = count_before(cc + 1 < it.cend ? cc + 1 : clast_chunk);
-        // ---- phase A: readout of chunk cc against S^(c-1)
-        kstep(kbeg, std::true_type{});
-#pragma unroll 1
-        for (int kk = kbeg + 1; kk < kend; ++kk) kstep(kk, std::false_type{});
-        __syncthreads();   // X: copy, image and exchange area free
-        // ---- phase B: hand the partner its tiles (fp32), stage the next chunk
+        // ---- phase A: readout of chunk cc against S^(c-1).  Even K steps take their B operand
+        // from Ba, odd ones from Bb; the next step's is read after the current step's A operand
+        // (LDS reads complete in order, so waiting for A does not wait for the prefetch).
+        f16x8 Ba[NT], Bb[NT], A[TPW];
+        loadB(0, Ba);
+        formA(0, A, std::true_type{});
+        loadB(1, Bb);
+        mma(A, Ba, std::true_type{});
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            if (tt / TKEEP == fh) continue;   // uniform: the partner's tiles
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) EX[((rw * TKEEP + tt % TKEEP) * NT + nt) * 64 + lane] = Y[tt][nt];
+        for (int kk = 1; kk + 2 < NKS; kk += 2) {
+            formA(kk, A, std::false_type{});
+            loadB(kk + 1, Ba);
+            mma(A, Bb, std::false_type{});
+            formA(kk + 1, A, std::false_type{});
+            loadB(kk + 2, Bb);
+            mma(A, Ba, std::false_type{});
         }
+        formA(NKS - 1, A, std::false_type{});
+        mma(A, Bb, std::false_type{});
+        store_partials(cc, cnt_cur);
+        __syncthreads();   // X: copy and image free
+        // ---- phase B: stage the next chunk
         if (cc + 1 < it.cend) stage();
         fetch(cc + 2 < it.cend ? cc + 2 : clast_chunk);
-        __syncthreads();   // Y: next image, copy and exchange written
+        __syncthreads();   // Y: next image and copy written
     }
-    receive_store(it.cend - 1, cnt_prev);
 }
 
 // Update wavefront uw: positions p0 = MT uw .. of the slice, their state in accumulators
@@ -494,40 +511,45 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
     // accumulators -> fp16 copy: K step 2 (p0 + j) + h holds slots 2h, 2h + 1 of position p0 + j;
     // the lane's 16 bytes are rows 4g .. 4g+3 of both slots, column li.  Slots of a group's first
     // position carry their weight relative to the prefix weight (0 for invalid slots).
+    auto copy_position = [&](int j, auto scaled) {
+        float rt[4][4];                       // [r][z]
+        if constexpr (scaled) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t w = W0[(p0 + j) * 16 + 4 * g + r];
+                const f32x4 cf = QC[(p0 + j) * 16 + 4 * g + r];
+                const float pf = qd_pfact<D, false>(w);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) rt[r][z] = cf[z] * pf;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 s0 = S[j][2 * h][nt], s1 = S[j][2 * h + 1][nt];
+                if constexpr (scaled) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s0[r] *= rt[r][2 * h];
+                        s1[r] *= rt[r][2 * h + 1];
+                    }
+                }
+                const f16x2 e0 = {(f16)s0[0], (f16)s0[1]}, e1 = {(f16)s0[2], (f16)s0[3]};
+                const f16x2 e2 = {(f16)s1[0], (f16)s1[1]}, e3 = {(f16)s1[2], (f16)s1[3]};
+                const u32x4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
+                                   __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)};
+                const int kk = 2 * (p0 + j) + h;
+                if (nt < NTF) CP[(kk * NTF + nt) * 64 + lane] = val;
+                else if (li == 0) CL[kk * 4 + g] = val;
+            }
+    };
+    // (the branch is per position and uniform: one straight run of conversions and stores each way)
     auto write_copy = [&]() {
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
-            float rt[4][4];                   // [r][z]
-            const bool mixed = (it.mixedm >> (p0 + j)) & 1u;
-            if (mixed) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t w = W0[(p0 + j) * 16 + 4 * g + r];
-                    const f32x4 cf = QC[(p0 + j) * 16 + 4 * g + r];
-                    const float pf = qd_pfact<D, false>(w);
-                    rt[r][0] = cf[0] * pf; rt[r][1] = cf[1] * pf; rt[r][2] = cf[2] * pf; rt[r][3] = cf[3] * pf;
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    f32x4 s0 = S[j][2 * h][nt], s1 = S[j][2 * h + 1][nt];
-                    if (mixed) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            s0[r] *= rt[r][2 * h];
-                            s1[r] *= rt[r][2 * h + 1];
-                        }
-                    }
-                    const f16x2 e0 = {(f16)s0[0], (f16)s0[1]}, e1 = {(f16)s0[2], (f16)s0[3]};
-                    const f16x2 e2 = {(f16)s1[0], (f16)s1[1]}, e3 = {(f16)s1[2], (f16)s1[3]};
-                    const u32x4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
-                                       __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)};
-                    const int kk = 2 * (p0 + j) + h;
-                    if (nt < NTF) CP[(kk * NTF + nt) * 64 + lane] = val;
-                    else if (li == 0) CL[kk * 4 + g] = val;
-                }
+            if ((it.mixedm >> (p0 + j)) & 1u) copy_position(j, std::true_type{});
+            else copy_position(j, std::false_type{});
         }
     };
     write_copy();
