@@ -470,9 +470,10 @@ def order5_section(sata, steps: int):
 
 
 def d128_section(sata):
-    """Head size 128 on the decode side (366,145 features at P = 4, 189 MB of
-    fp32 state per head): one sequence of 8 heads, plain steps from an empty
-    state (a step's cost does not depend on what the state holds)."""
+    """Head size 128 (366,145 features at P = 4, 189 MB of fp32 state per head):
+    decode for one sequence of 8 heads, plain steps from an empty state (a step's
+    cost does not depend on what the state holds); the chunked prefill of
+    1 x 8 x 4096 bf16 tokens, and the block path that fp32 inputs take."""
     import dataclasses
     import torch
     import synth_inputs as si
@@ -486,29 +487,34 @@ def d128_section(sata):
     res = {"workload": "%d x %d heads, d=%d, P=%d" % (wl.batch, wl.heads, wl.d_k, wl.P),
            "value": wl.batch / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "stream_kernel_ms": kms,
            "bytes_per_step": nbytes, "achieved_gbs": ach, "frac": ach / PEAK_HBM_GBS}
-    # block prefill: blocks of 64 tokens, each read out and folded into the state in one
-    # pass (a read and a write of the state per block)
-    n = 4096
-    q, k, v = si.draw_qkv_device((wl.batch, wl.heads), n, wl.d_k, wl.d_v, wl.seed + 4, "bf16")
-    out = torch.empty(v.shape, dtype=torch.bfloat16, device="cuda")
+    # prefill, bf16 inputs at P = 4: the chunked fp16-operand scan (64-token chunks)
+    pwl = si.WORKLOADS["prefill_d128_p4_bf16"]
+    q, k, v = si.draw_qkv_device((pwl.batch, pwl.heads), pwl.n, pwl.d_k, pwl.d_v, pwl.seed, "bf16")
+    res["prefill"] = time_prefill(sata, pwl, q, k, v, 3, 1)
+    res["prefill"]["workload"] = "%d x %d heads x %d tokens, d=%d, P=%d, bf16 in" % (
+        pwl.batch, pwl.heads, pwl.n, pwl.d_k, pwl.P)
+    # fp32 inputs take the block path (blocks of 64 tokens, each read out and folded into the
+    # state in one pass: a read and a write of the state per block); one timed call
+    q, k, v = (t.float() for t in (q, k, v))
+    out = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    n = pwl.n
     sata.sata_state_reset(st)
     sata.sata_prefill(idx, st, q, k, v, out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
+    sata.sata_state_reset(st)
     e0.record()
-    for _ in range(reps):
-        sata.sata_state_reset(st)
-        sata.sata_prefill(idx, st, q, k, v, out)
+    sata.sata_prefill(idx, st, q, k, v, out)
     e1.record()
     torch.cuda.synchronize()
-    pms = e0.elapsed_time(e1) / reps
+    pms = e0.elapsed_time(e1)
     state_bytes = 4.0 * features(wl.d_k, wl.P) * (wl.d_v + 1) * wl.batch * wl.heads
     pbytes = 2 * state_bytes * ((n + 63) // 64)
-    res["prefill"] = {"workload": "%d x %d heads x %d tokens, d=%d, P=%d, bf16 in" % (wl.batch, wl.heads, n, wl.d_k, wl.P),
-                      "ms_per_call": pms, "value": wl.batch * n / (pms * 1e-3), "unit": "tokens/s",
-                      "state_bytes_per_call": pbytes, "achieved_gbs": pbytes / (pms * 1e-3) / 1e9,
-                      "frac": pbytes / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    res["block_prefill_f32"] = {"workload": "%d x %d heads x %d tokens, d=%d, P=%d, fp32 in" % (
+                                    wl.batch, wl.heads, n, wl.d_k, wl.P),
+                                "ms_per_call": pms, "value": wl.batch * n / (pms * 1e-3), "unit": "tokens/s",
+                                "state_bytes_per_call": pbytes, "achieved_gbs": pbytes / (pms * 1e-3) / 1e9,
+                                "frac": pbytes / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del q, k, v, out
     st.free()
     idx.free()
@@ -875,11 +881,13 @@ def main():
                                   o5["decode"]["ms_per_step"], o5["decode"]["achieved_gbs"], 100 * o5["decode"]["frac"]))
         result["order5"] = o5
         dd = d128_section(sata)
-        log("decode, %s: %.3f ms/step, stream %.0f GB/s (%.1f%% of peak); block prefill %s: %.2f ms, %.3e tok/s, "
-            "%.0f GB/s of state passes" % (dd["workload"], dd["ms_per_step"], dd["achieved_gbs"], 100 * dd["frac"],
-                                           dd["prefill"]["workload"], dd["prefill"]["ms_per_call"],
-                                           dd["prefill"]["value"], dd["prefill"]["achieved_gbs"]))
-        result["d128_decode"] = dd
+        log("decode, %s: %.3f ms/step, stream %.0f GB/s (%.1f%% of peak)" % (
+            dd["workload"], dd["ms_per_step"], dd["achieved_gbs"], 100 * dd["frac"]))
+        log("chunked prefill %s: %.2f ms, %.3e tok/s, scan %.1f%% of peak; block prefill %s: %.2f ms, %.3e tok/s"
+            % (dd["prefill"]["workload"], dd["prefill"]["ms_per_step"], dd["prefill"]["value"],
+               100 * dd["prefill"]["roofline"]["frac"], dd["block_prefill_f32"]["workload"],
+               dd["block_prefill_f32"]["ms_per_call"], dd["block_prefill_f32"]["value"]))
+        result["d128"] = dd
 
     if not args.no_backward:
         bwd = []

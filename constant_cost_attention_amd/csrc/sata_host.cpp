@@ -42,6 +42,8 @@ sata_status fail_hip(hipError_t e, const char *what) {
 bool supported_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
 // The prefill's quad words hold the block index in four bits (d_K / 4 <= 16).
 constexpr int kMaxPrefillDim = 64;
+// The 16-stream view (at most four orders) holds it in a byte: the fp16-operand scan's range.
+constexpr int kMaxScan16Dim = 128;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -310,9 +312,11 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
 // outside the scan.  Unused streams are padding quads (prefix product 0).
 // flags[pos]: bit 0 = some quad of the position has slots with different
 // weights (or invalid slots), bit 1 = the position starts a new group of
-// prefixes.
+// prefixes.  Word w0: i1 | i2 << 8 | i0 << 16 | b << 24 | slot mask << 28; with
+// block_byte (views without three-index prefixes, P <= 4) b takes the i0 byte
+// instead: i1 | i2 << 8 | b << 16 | slot mask << 28, for d up to 1020.
 static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags,
-                        size_t streams = 4) {
+                        size_t streams = 4, bool block_byte = false) {
     std::map<std::vector<int>, int32_t> index;   // sorted tuple -> feature index
     {
         int32_t f = 0;
@@ -326,7 +330,8 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
     struct Prefix { int i0, i1, i2; };
     auto make = [&](const Prefix &x, int b, uint32_t &nonuni) {
         sata::QuadRec q{};
-        q.w0 = (uint32_t)pad | ((uint32_t)pad << 8) | ((uint32_t)none << 16) | ((uint32_t)b << 24);
+        q.w0 = block_byte ? (uint32_t)pad | ((uint32_t)pad << 8) | ((uint32_t)b << 16)
+                          : (uint32_t)pad | ((uint32_t)pad << 8) | ((uint32_t)none << 16) | ((uint32_t)b << 24);
         q.cidx = -1;
         if (x.i2 == pad) return q;
         std::vector<int> prefix;
@@ -348,7 +353,8 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
             }
             q.coef[z] = (float)(1.0 / alpha_factorial(t));
         }
-        q.w0 = (uint32_t)x.i1 | ((uint32_t)x.i2 << 8) | ((uint32_t)x.i0 << 16) | ((uint32_t)b << 24) | (mask << 28);
+        q.w0 = block_byte ? (uint32_t)x.i1 | ((uint32_t)x.i2 << 8) | ((uint32_t)b << 16) | (mask << 28)
+                          : (uint32_t)x.i1 | ((uint32_t)x.i2 << 8) | ((uint32_t)x.i0 << 16) | ((uint32_t)b << 24) | (mask << 28);
         if (mask != 0xfu || q.coef[0] != q.coef[1] || q.coef[0] != q.coef[2] || q.coef[0] != q.coef[3]) nonuni = 1;
         return q;
     };
@@ -454,16 +460,16 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
         quads.resize((size_t)idx->nq_tab, padq);
         qflags.resize((size_t)(idx->nq_tab / 4), 2u);
     }
-    // 16-stream positions for the fp16-operand scan (P <= 4, 16 <= d_K <= 64), padded with
-    // positions of padding quads (prefix product 0, flagged as group starts) so that every
-    // slice of up to kPos16Pad positions lies inside the table
+    // 16-stream positions for the fp16-operand scan (P <= 4, 16 <= d_K <= 128; block index
+    // in a byte), padded with positions of padding quads (prefix product 0, block 0, flagged as
+    // group starts) so that every slice of up to kPos16Pad positions lies inside the table
     std::vector<sata::QuadRec> quads16;
     std::vector<uint32_t> flags16;
-    if (P <= 4 && d_k >= 16 && d_k <= kMaxPrefillDim) {
-        build_quads(d_k, P, quads16, flags16, 16);
+    if (P <= 4 && d_k >= 16 && d_k <= kMaxScan16Dim) {
+        build_quads(d_k, P, quads16, flags16, 16, true);
         idx->np16 = (int64_t)flags16.size();
         sata::QuadRec padq{};
-        padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8) | ((uint32_t)d_k << 16);
+        padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8);
         padq.cidx = -1;
         quads16.resize((size_t)(idx->np16 + sata::kPos16Pad) * 16, padq);
         flags16.resize((size_t)(idx->np16 + sata::kPos16Pad), 2u);
@@ -682,9 +688,9 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
     sata_status s = check_prefill_args(idx, st, q, k, v, out, n, chunk, in_dt, out_dt, &nothing);
     if (s != SATA_OK || nothing) return s;
     const int64_t bh = (int64_t)st->batch * st->heads;
-    if (idx->dk > kMaxPrefillDim) {
-        // d_K = 128: blocks of up to kMaxDecodeWindow tokens through the state in HBM (the
-        // chunk length does not apply)
+    if (idx->dk > kMaxPrefillDim && !sata::scan16_covers(idx, in_dt)) {
+        // d_K = 128 outside the fp16-operand scan (fp32 inputs, five orders): blocks of up to
+        // kMaxDecodeWindow tokens through the state in HBM (the chunk length does not apply)
         DeviceGuard g(st->device);
         if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the state's device");
         s = ensure_pending(st);
@@ -723,9 +729,10 @@ sata_status sata_prefill_noalloc(const sata_index *idx, sata_state *st, const vo
     bool nothing = false;
     sata_status s = check_prefill_args(idx, st, q, k, v, out, n, chunk, in_dt, out_dt, &nothing);
     if (s != SATA_OK || nothing) return s;
-    if (idx->dk > kMaxPrefillDim)
-        return fail(SATA_ERR_UNSUPPORTED, "the allocation-free prefill covers d_k <= %d (got %d)", kMaxPrefillDim,
-                    idx->dk);
+    if (idx->dk > kMaxPrefillDim && !sata::scan16_covers(idx, in_dt))
+        return fail(SATA_ERR_UNSUPPORTED,
+                    "the allocation-free prefill covers d_k <= %d, and d_k = 128 for bf16 inputs with P <= 4 "
+                    "(got d_k=%d, P=%d)", kMaxPrefillDim, idx->dk, idx->P);
     const int64_t bh = (int64_t)st->batch * st->heads;
     ProfOff quiet;   // no timing events for any launch of this call
     DeviceGuard g(st->device);
@@ -896,7 +903,9 @@ int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t 
                                    int64_t work_cap, int64_t *seg_chunks, int64_t *slices) {
     g_last_error.clear();
     if (check_dims(d_k, d_k, P) != SATA_OK) return -1;
-    if (d_k > kMaxPrefillDim || batch_heads < 1 || n < 1 || !valid_dtype(in_dt) || work_cap < 1 ||
+    // chunked plans: d_K <= 64, and d_K = 128 on the fp16-operand scan (bf16 inputs, P <= 4)
+    const bool wide = d_k > kMaxPrefillDim && d_k <= kMaxScan16Dim && P <= 4 && in_dt == SATA_BF16;
+    if ((d_k > kMaxPrefillDim && !wide) || batch_heads < 1 || n < 1 || !valid_dtype(in_dt) || work_cap < 1 ||
         (chunk != 0 && chunk != 64 && chunk != 128)) {
         fail(SATA_ERR_INVALID, "no chunked prefill plan for these arguments");
         return -1;
@@ -907,13 +916,13 @@ int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t 
     idx.P = P;
     std::vector<sata::QuadRec> quads;
     std::vector<uint32_t> flags;
-    build_quads(d_k, P, quads, flags);
+    if (!wide) build_quads(d_k, P, quads, flags);
     idx.nq = (int64_t)quads.size();
     idx.nq_tab = round_up(std::max<int64_t>(idx.nq, 1), sata::kQuadPad);
     if (P <= 4 && d_k >= 16) {
         std::vector<sata::QuadRec> q16;
         std::vector<uint32_t> f16;
-        build_quads(d_k, P, q16, f16, 16);
+        build_quads(d_k, P, q16, f16, 16, true);
         idx.np16 = (int64_t)f16.size();
     }
     const sata::PrefillPlan plan = sata::plan_prefill(&idx, batch_heads, n, chunk, (sata_dtype)in_dt, work_cap);

@@ -156,7 +156,9 @@ hipError_t launch_backward(const sata_index *idx, const sata_index *lower, int64
                            sata_dtype in_dt, sata_dtype out_dt, int64_t mem_budget, hipStream_t s);
 // The step the calling thread's last backward call was in (for error messages).
 const char *backward_last_step();
-// fp16-operand scan (sata_scan16.hip): positions per slice and the operand image of one chunk
+// fp16-operand scan (sata_scan16.hip): whether it covers a prefill (bf16 inputs, P <= 4,
+// d_K = d_V in {16, 32, 64, 128}), positions per slice and the operand image of one chunk
+bool scan16_covers(const sata_index *idx, sata_dtype in_dt);
 int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus);
 int64_t scan16_image_bytes(int dk, int chunk);
 struct TaylorArgs;

@@ -1551,7 +1551,7 @@ __global__ __launch_bounds__(256) void order0_sums_kernel(const TIn *__restrict_
 }
 
 template <int DV>
-__global__ __launch_bounds__(128) void order0_prefix_kernel(const float *__restrict__ sums, float *__restrict__ prefix,
+__global__ __launch_bounds__(256) void order0_prefix_kernel(const float *__restrict__ sums, float *__restrict__ prefix,
                                                             int64_t nchunks, float *__restrict__ state, int64_t m_pad) {
     constexpr int NC = DV + 1;
     const int64_t bh = blockIdx.x;
@@ -1730,14 +1730,23 @@ static ScanShape pick_shape(const sata_index *idx, int64_t bh, int chunk, sata_d
     return {kNW, 2, false};
 }
 
+bool scan16_covers(const sata_index *idx, sata_dtype in_dt) {
+    return in_dt == SATA_BF16 && idx->np16 > 0 && idx->dk == idx->dv &&
+           (idx->dk == 16 || idx->dk == 32 || idx->dk == 64 || idx->dk == 128);
+}
+
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt, int64_t work_cap,
                          bool fp16_operands) {
     PrefillPlan p;
     p.chunk = chunk ? chunk : (idx->dk == 64 ? 128 : 64);
     if (p.chunk != 64 && p.chunk != 128) return p;
+    const bool s16 = fp16_operands && scan16_covers(idx, in_dt);
+    if (idx->dk == 128) {
+        if (!s16) return p;   // no chunked plan: the block prefill covers it
+        p.chunk = 64;         // the operand image of a 128-token chunk does not fit beside the state copy
+    }
     const int64_t nchunks = (n + p.chunk - 1) / p.chunk;
-    if (fp16_operands && in_dt == SATA_BF16 && idx->np16 > 0 && idx->dk == idx->dv &&
-        (idx->dk == 16 || idx->dk == 32 || idx->dk == 64)) {
+    if (s16) {
         // fp16-operand scan: fp16 partials and one operand image per chunk of a segment
         p.s16 = true;
         p.mt = scan16_choose_mt(idx->dk, idx->np16, bh, idx->cus);
@@ -1831,8 +1840,8 @@ static hipError_t run_prefill(const sata_index *idx, const sata_state *st, const
     float *o0pre = o0sums + bh * nchunks * (D + 1);
     hipLaunchKernelGGL((order0_sums_kernel<D, TIn>), dim3((unsigned)nchunks, (unsigned)bh), dim3(256), 0, stream,
                        static_cast<const TIn *>(v), n, C, o0sums);
-    hipLaunchKernelGGL((order0_prefix_kernel<D>), dim3((unsigned)bh), dim3(128), 0, stream, o0sums, o0pre, nchunks,
-                       static_cast<float *>(st->d_state), idx->m_pad);
+    hipLaunchKernelGGL((order0_prefix_kernel<D>), dim3((unsigned)bh), dim3((D + 1 + 63) / 64 * 64), 0, stream, o0sums,
+                       o0pre, nchunks, static_cast<float *>(st->d_state), idx->m_pad);   // a thread per column
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int64_t c0 = 0; c0 < nchunks; c0 += plan.seg_chunks) {
@@ -1940,8 +1949,8 @@ static hipError_t run_prefill16(const sata_index *idx, const sata_state *st, con
     float *o0pre = o0sums + bh * nchunks * (D + 1);
     hipLaunchKernelGGL((order0_sums_kernel<D, bf16_t>), dim3((unsigned)nchunks, (unsigned)bh), dim3(256), 0, stream,
                        static_cast<const bf16_t *>(v), n, C, o0sums);
-    hipLaunchKernelGGL((order0_prefix_kernel<D>), dim3((unsigned)bh), dim3(128), 0, stream, o0sums, o0pre, nchunks,
-                       static_cast<float *>(st->d_state), idx->m_pad);
+    hipLaunchKernelGGL((order0_prefix_kernel<D>), dim3((unsigned)bh), dim3((D + 1 + 63) / 64 * 64), 0, stream, o0sums,
+                       o0pre, nchunks, static_cast<float *>(st->d_state), idx->m_pad);   // a thread per column
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int64_t c0 = 0; c0 < nchunks; c0 += plan.seg_chunks) {
@@ -1961,6 +1970,7 @@ hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const Pre
             case 16: return run_prefill16<16>(idx, st, plan, q, k, v, out, n, out_dt, stream);
             case 32: return run_prefill16<32>(idx, st, plan, q, k, v, out, n, out_dt, stream);
             case 64: return run_prefill16<64>(idx, st, plan, q, k, v, out, n, out_dt, stream);
+            case 128: return run_prefill16<128>(idx, st, plan, q, k, v, out, n, out_dt, stream);
             default: return hipErrorInvalidValue;
         }
     }

@@ -52,6 +52,10 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Block index of a quad word of the 16-stream view: its third byte (the view has no three-index
+// prefixes), so head sizes up to 128 fit.
+__device__ __forceinline__ int qd16_b(uint32_t w) { return (int)((w >> 16) & 0xffu); }
+
 constexpr float kKeyScale = 0.25f;   // k^ = k / 4
 constexpr float kQueryScale = 4.0f;  // q^ = 4 q / sqrt(d_K)
 
@@ -390,7 +394,7 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
             __asm__ volatile("" ::: "memory");
             regroup(p);
         }
-        const int xo = 4 * qd_b(W0[p * 16]) + 2 * h;
+        const int xo = 4 * qd16_b(W0[p * 16]) + 2 * h;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const f16x2 x = *reinterpret_cast<const S16_LDS f16x2 *>(qrow[tt] + xo);
@@ -467,7 +471,7 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
         wr[j] = W0[(p0 + j) * 16 + li];
-        blk[j] = __builtin_amdgcn_readfirstlane(qd_b(W0[(p0 + j) * 16]));
+        blk[j] = __builtin_amdgcn_readfirstlane(qd16_b(W0[(p0 + j) * 16]));
         if ((it.gstart >> (p0 + j)) & 1u) newgrp |= 1u << j;
     }
     // State element (row c, feature f) of the lane's prefix 4g + r at position p0 + j, slot z:
@@ -873,7 +877,7 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
 // registers) allow next to the operands within 256 registers, or one when that many leaves
 // fewer (head, slice) work items than compute units (few heads of a small head size: a head's
 // chunks run one after another, so only more slices spread it over the chip).
-constexpr int scan16_mt_max(int dk) { return dk == 64 ? 2 : dk == 32 ? 3 : 5; }
+constexpr int scan16_mt_max(int dk) { return dk == 128 ? 1 : dk == 64 ? 2 : dk == 32 ? 3 : 5; }
 
 int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus) {
     const int big = scan16_mt_max(dk);
@@ -890,6 +894,7 @@ int64_t scan16_image_bytes(int dk, int chunk) {
     using C128 = std::integral_constant<int, 128>;
     if (dk == 16) return chunk == 64 ? b(I16{}, C64{}) : b(I16{}, C128{});
     if (dk == 32) return chunk == 64 ? b(I32{}, C64{}) : b(I32{}, C128{});
+    if (dk == 128) return b(std::integral_constant<int, 128>{}, C64{});   // 64-token chunks only
     return chunk == 64 ? b(I64{}, C64{}) : b(I64{}, C128{});
 }
 
@@ -963,6 +968,7 @@ hipError_t launch_scan16_segment(const sata_index *idx, const sata_state *st, co
         case 16: return plan.chunk == 64 ? go(std::integral_constant<int, 16>{}, C64{}) : go(std::integral_constant<int, 16>{}, C128{});
         case 32: return plan.chunk == 64 ? go(std::integral_constant<int, 32>{}, C64{}) : go(std::integral_constant<int, 32>{}, C128{});
         case 64: return plan.chunk == 64 ? go(std::integral_constant<int, 64>{}, C64{}) : go(std::integral_constant<int, 64>{}, C128{});
+        case 128: return plan.chunk == 64 ? go(std::integral_constant<int, 128>{}, C64{}) : hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

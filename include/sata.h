@@ -38,10 +38,10 @@
  *     library owns index and state memory (hipMalloc) and frees it in the
  *     *_free calls.
  *   - Supported shapes: d_K, d_V in {8, 16, 32, 64}, or d_K = d_V = 128;
- *     1 <= P <= 5.  Prefill needs d_K == d_V; at d_K = 128 it runs in blocks
- *     of 64 tokens through the state in HBM (slower than the chunked scan of
- *     d_K <= 64, whose feature blocking holds the block index in four bits),
- *     and the backward refuses it.  Other values return
+ *     1 <= P <= 5.  Prefill needs d_K == d_V; at d_K = 128 it runs the
+ *     chunked scan for bf16 inputs with P <= 4, and otherwise (fp32 inputs,
+ *     P = 5) blocks of 64 tokens through the state in HBM, which is much
+ *     slower; the backward refuses d_K = 128.  Other values return
  *     SATA_ERR_UNSUPPORTED.  The state grows as
  *     C(d_K+P-1, P-1) (d_V+1) fp32 values per head: at d_K = 64, 12.5 MB for
  *     P = 4 and 212 MB for P = 5; at d_K = 128 and P = 4, 189 MB.
@@ -188,11 +188,12 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
  * q, k: [batch][heads][n][d_K]; v, out: [batch][heads][n][d_V]; in_dt is the
  * dtype of q, k, v; out_dt that of out.  Token i attends to every earlier
  * token and to itself.  The sequence is processed in chunks of `chunk` tokens
- * (0 = default, 128 for d_K = 64 and 64 otherwise; supported: 64, 128):
+ * (0 = default, 128 for d_K = 64 and 64 otherwise; supported: 64, 128; at
+ * d_K = 128 the chunk is always 64 tokens):
  * within a chunk the Taylor weights are formed directly, across chunks the
  * orders' states are scanned and read out [hotdry, "Engineering realisation
  * of the constant compute cost"]; results do not depend on the chunk length
- * beyond rounding.  For bf16 inputs with d_K = d_V in {16, 32, 64} and
+ * beyond rounding.  For bf16 inputs with d_K = d_V in {16, 32, 64, 128} and
  * P <= 4 the scan's matrix operands are fp16: k / 4, 4 q / sqrt(d_K) and v
  * convert to fp16 exactly when their magnitudes lie in fp16's normal range
  * (6.1e-5 to 65504, or zero); smaller ones keep less precision and larger
@@ -228,9 +229,11 @@ sata_status sata_prefill(const sata_index *idx, sata_state *st, const void *q, c
  * (allocated beforehand).  Every call on a device shares that device's
  * array: calls that overlap in time on one device (other streams or host
  * threads) race and give wrong results; order them.  Returns
- * SATA_ERR_UNSUPPORTED for d_K > 64 and when even single-chunk segments need
+ * SATA_ERR_UNSUPPORTED where sata_prefill would take the block path (d_K =
+ * 128 with fp32 inputs or P = 5) and when even single-chunk segments need
  * more workspace than the array holds (about 1.6 MB per head at d_K = 64,
- * P = 4), with the size needed in sata_last_error. */
+ * P = 4, and 24 MB per head at d_K = 128), with the size needed in
+ * sata_last_error. */
 sata_status sata_prefill_noalloc(const sata_index *idx, sata_state *st, const void *q, const void *k,
                                  const void *v, void *out, int64_t n, int chunk, sata_dtype in_dt,
                                  sata_dtype out_dt, void *stream);

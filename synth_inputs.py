@@ -122,6 +122,8 @@ WORKLOADS = {
                                         SEED_BASE + 5),
     # five orders (814,385 features, 212 MB of fp32 state per head at d = 64)
     "prefill_d64_p5_bf16": Workload("prefill_d64_p5_bf16", 1, 8, 8192, 64, 64, 5, "bf16", 128, SEED_BASE + 6),
+    # head size 128 (366,145 features, 189 MB of fp32 state per head), 64-token chunks
+    "prefill_d128_p4_bf16": Workload("prefill_d128_p4_bf16", 1, 8, 4096, 128, 128, 4, "bf16", 64, SEED_BASE + 7),
 }
 
 

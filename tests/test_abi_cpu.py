@@ -202,5 +202,21 @@ def test_prefill_plan_shrinks_segments_under_a_smaller_cap():
             break
         cap = p["work_bytes"] // 2
     assert all(a > b for a, b in zip(segs, segs[1:]))
-    with pytest.raises(sata.SataError):
-        sata.sata_describe_prefill_plan(128, 4, 8, 4096)
+    # head size 128: chunked only on the fp16-operand scan (bf16 inputs, P <= 4)
+    for bad in ((128, 4, sata.SATA_F32), (128, 5, sata.SATA_BF16)):
+        with pytest.raises(sata.SataError):
+            sata.sata_describe_prefill_plan(bad[0], bad[1], 8, 4096, 0, bad[2])
+
+
+def test_prefill_plan_head_size_128():
+    """d_K = 128 (bf16, P <= 4): one position per update wavefront, so a slice holds 4 x 64
+    features; 64-token chunks whatever the request; the 1 x 8 x 4096 workload in one segment."""
+    from constant_cost_attention_amd import sata
+    P = 4
+    feats = sum(math.comb(128 + p - 1, p) for p in range(1, P))   # orders 1 .. P-1 (order 0 is outside)
+    p64 = sata.sata_describe_prefill_plan(128, P, 8, 4096, 0, sata.SATA_BF16)
+    assert p64 == sata.sata_describe_prefill_plan(128, P, 8, 4096, 128, sata.SATA_BF16)
+    assert p64["slices"] >= feats / 256
+    assert p64["seg_chunks"] == 4096 // 64
+    # partials (fp16) of every slice of every chunk fit the default workspace
+    assert 8 * p64["slices"] * 4096 * 129 * 2 <= p64["work_bytes"] <= 16 << 30

@@ -1,8 +1,10 @@
 """Head size 128 (d_K = d_V = 128): the table-driven kernels (expansion, the
 row-split decode step and read kernel, the matrix-core fold, the finish
-kernel) and the block prefill (blocks of up to 64 tokens read out against the
-state in HBM, direct terms inside the block, then folded in) against the
-oracle; the backward refuses d_K = 128."""
+kernel), the chunked fp16-operand prefill scan (bf16 inputs, P <= 4: 64-token
+chunks, one position per update wavefront) and the block prefill for the rest
+(fp32 inputs: blocks of up to 64 tokens read out against the state in HBM,
+direct terms inside the block, then folded in) against the oracle; the
+backward refuses d_K = 128."""
 import math
 
 import numpy as np
@@ -10,7 +12,7 @@ import pytest
 import torch
 
 import synth_inputs as si
-from sata_testutil import TOL_BF16, TOL_F32, decode, dev_all, prefill, rel_err, say
+from sata_testutil import TOL_BF16, TOL_F32, decode, dev_all, prefill, rel_err, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -116,6 +118,50 @@ def test_prefill_d128_every_row(sata, oracle, P, dtype):
     err = rel_err(o, oracle.taylor_attention(x.q, x.k, x.v, P))
     say("  err %.3e" % err)
     assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    st.free()
+    idx.free()
+
+
+@pytest.mark.parametrize("P", [2, 3, 4])
+def test_prefill_d128_chunked_every_row(sata, oracle, P):
+    """Chunked scan: four 64-token chunks and a ragged 37, every row against O1; then two
+    decode steps continue from the state the scan left."""
+    n, t, heads = 4 * 64 + 37, 2, 2
+    x = si.draw_qkv((1, heads), n + t, D, D, 9400 + P, "bf16")
+    plan = sata.sata_describe_prefill_plan(D, P, heads, n, 0, sata.SATA_BF16)
+    say("prefill d=128 chunked P=%d bf16 n=%d: %d slices per head" % (P, n, plan["slices"]))
+    idx = sata.Index(D, D, P)
+    st = sata.State(idx, 1, heads)
+    q, k, v = dev_all(x)
+    sl = lambda a, lo, hi: a[:, :, lo:hi].contiguous()
+    o = prefill(idx, st, sl(q, 0, n), sl(k, 0, n), sl(v, 0, n)).cpu().numpy()
+    ref = oracle.taylor_attention(x.q, x.k, x.v, P)
+    err = rel_err(o, ref[:, :, :n])
+    say("  prefill err %.3e; decode %d steps" % (err, t))
+    assert err <= TOL_BF16
+    od = _steps(idx, st, x, n, n + t)
+    errd = rel_err(od, ref[:, :, n:])
+    say("  decode err %.3e" % errd)
+    assert errd <= TOL_BF16
+    st.free()
+    idx.free()
+
+
+def test_prefill_d128_chunked_workload_sampled_rows(sata, oracle):
+    """The 1 x 8 x 4096 bf16 workload at P = 4 (1,430 slices per head, one segment): the
+    first and last chunk and 64 seeded rows of every head against O1."""
+    wl = si.WORKLOADS["prefill_d128_p4_bf16"]
+    x = wl.draw()
+    say("prefill %s" % wl.name)
+    idx = sata.Index(D, D, wl.P)
+    st = sata.State(idx, wl.batch, wl.heads)
+    q, k, v = dev_all(x)
+    o = prefill(idx, st, q, k, v, chunk=wl.chunk).cpu().numpy()
+    rows = sample_rows(wl.n, wl.chunk, 64, wl.seed + 1)
+    ref = oracle.taylor_attention(x.q, x.k, x.v, wl.P, rows=rows)
+    err = rel_err(o[:, :, rows], ref)
+    say("  %d rows x %d heads: err %.3e" % (len(rows), wl.heads, err))
+    assert err <= TOL_BF16
     st.free()
     idx.free()
 
