@@ -26,6 +26,8 @@ Functions (what pins each one is listed in the tests and in the design notes):
 * ``recurrent_attention_f32`` O7, O5 carried out in float (diagnostic).
 * ``round_bf16``         O8a, round to nearest bfloat16, ties to even.
 * ``bf16_state_decode``  O8, decode steps on a state stored in bf16.
+* ``round_f16``          O8b, round to nearest IEEE binary16, ties to even.
+* ``f16_state_decode``   O8 for an fp16 state whose lowest orders are fp32.
 * ``taylor_attention_grad`` O9, gradients of O1 (fp64 autograd of the
   quadratic form, plain PyTorch CPU ops).
 * ``basis_size``, ``state_size``, ``flops_per_token`` O6, the closed forms the
@@ -83,6 +85,10 @@ def _load():
     lib.orc_round_bf16_array.restype = None
     lib.orc_bf16_state_decode.argtypes = [f32p, f32p, f32p, f64p, i64, i64, i64, cint, cint, cint, cint, cint]
     lib.orc_bf16_state_decode.restype = cint
+    lib.orc_round_f16_array.argtypes = [f64p, f64p, i64]
+    lib.orc_round_f16_array.restype = None
+    lib.orc_f16_state_decode.argtypes = [f32p, f32p, f32p, f64p, i64, i64, i64, cint, cint, cint, cint, cint]
+    lib.orc_f16_state_decode.restype = cint
     for name in ("orc_recurrent_attention", "orc_recurrent_attention_f32"):
         fn = getattr(lib, name)
         fn.argtypes = [f32p, f32p, f32p, f64p, i64, i64, cint, cint, cint]
@@ -248,6 +254,37 @@ def bf16_state_decode(q, k, v, P: int, n0: int, rounding: bool = True, window: i
                                        bh, int(n0), n, dk, dv, int(P), 1 if rounding else 0, int(window))
     if rc:
         raise ValueError("orc_bf16_state_decode rejected its arguments")
+    return out.reshape(tuple(lead) + (n - n0, dv))
+
+
+def round_f16(x) -> np.ndarray:
+    """O8b: round to the nearest IEEE binary16 value, ties to even (11
+    significant bits, gradual underflow below 2^-14, +-inf past 65504),
+    returned as float64."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(a)
+    _load().orc_round_f16_array(a.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), a.size)
+    return out
+
+
+def f16_state_decode(q, k, v, P: int, n0: int, low_orders: int = 3, window: int = 1) -> np.ndarray:
+    """O8 for an fp16-stored state [hotdry, "Hardware optimisation paths and
+    current limits": Float16 storage at P = 4]: as bf16_state_decode, but the
+    features of orders below low_orders are stored in fp32 (round to nearest
+    binary32) and the others in fp16 (round to nearest binary16, ties to
+    even).  Returns rows n0..n-1: [..., n - n0, d_V].  fp64; moderate inputs."""
+    lead, bh, n, dk, dv = _heads(np.asarray(q), np.asarray(k), np.asarray(v))
+    if not 0 <= n0 <= n:
+        raise ValueError("need 0 <= n0 <= n")
+    q32, qp = _f32(q)
+    k32, kp = _f32(k)
+    v32, vp = _f32(v)
+    out = np.empty((bh, n - n0, dv), dtype=np.float64)
+    rc = _load().orc_f16_state_decode(qp, kp, vp, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                      bh, int(n0), n, dk, dv, int(P), int(low_orders), int(window))
+    if rc:
+        raise ValueError("orc_f16_state_decode rejected its arguments")
     return out.reshape(tuple(lead) + (n - n0, dv))
 
 

@@ -353,7 +353,34 @@ void orc_round_bf16_array(const double *x, double *out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_round_bf16(x[i]);
 }
 
-/* Decode steps on a state whose stored elements are bfloat16.
+/* Rounds x to the nearest IEEE binary16 value, ties to even: 11 significant
+ * bits (10 stored plus the implicit one), normal numbers from 2^-14 up to
+ * 65504, gradual underflow below 2^-14 (fixed quantum 2^-24), and anything
+ * that rounds past 65504 becomes +-inf. */
+double orc_round_f16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    (void)frexp(x, &e);              /* x = f * 2^e, 0.5 <= |f| < 1 */
+    if (e < -13) e = -13;            /* subnormal range: fixed quantum 2^-24 */
+    const double r = ldexp(nearbyint(ldexp(x, 11 - e)), e - 11);
+    return fabs(r) > 65504.0 ? copysign(INFINITY, r) : r;
+}
+
+void orc_round_f16_array(const double *x, double *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_round_f16(x[i]);
+}
+
+/* The value a 16-bit state stores for feature f: round_mode 0 keeps it exact,
+ * 1 rounds to bf16, 2 rounds to binary32 for the first m_low features (the
+ * lowest orders) and to binary16 for the rest. */
+static double store_round(int round_mode, int64_t f, int64_t m_low, double x) {
+    if (round_mode == 0) return x;
+    if (round_mode == 1) return orc_round_bf16(x);
+    return f < m_low ? (double)(float)x : orc_round_f16(x);
+}
+
+/* Decode steps on a state whose stored elements are 16-bit (bfloat16, or
+ * binary16 with the lowest orders in binary32: see store_round).
  *
  * The state is the one of the recurrent form [hotdry, "Engineering
  * realisation of the constant compute cost"] kept in the layout the library
@@ -386,7 +413,7 @@ typedef struct {
     const int32_t *tup;
     const int *ord;
     double *S;
-    int64_t n0, f_lo, f_hi;
+    int64_t n0, f_lo, f_hi, m_low;
     int dk, dv, W, round_mode;
 } prefix_job;
 
@@ -404,22 +431,24 @@ static void *prefix_worker(void *arg) {
         for (int c = 0; c <= dv; ++c) {
             double acc = 0.0;
             for (int64_t s = 0; s < J->n0; ++s) acc += a[s] * (c < dv ? (double)J->v[s * dv + c] : 1.0);
-            J->S[f * (dv + 1) + c] = J->round_mode ? orc_round_bf16(acc) : acc;
+            J->S[f * (dv + 1) + c] = store_round(J->round_mode, f, J->m_low, acc);
         }
     }
     free(a);
     return NULL;
 }
 
-int orc_bf16_state_decode(const float *q, const float *k, const float *v, double *out,
-                          int64_t bh, int64_t n0, int64_t n, int dk, int dv, int P, int round_mode, int window) {
-    if (bh < 0 || n0 < 0 || n < n0 || dk <= 0 || dv <= 0 || P < 1 || P > 8 || window < 1) return 1;
-    int64_t ng[8], off[8], m = 0;
+static int state16_decode(const float *q, const float *k, const float *v, double *out, int64_t bh, int64_t n0,
+                          int64_t n, int dk, int dv, int P, int round_mode, int low_orders, int window) {
+    if (bh < 0 || n0 < 0 || n < n0 || dk <= 0 || dv <= 0 || P < 1 || P > 8 || window < 1 || low_orders < 0)
+        return 1;
+    int64_t ng[8], off[8], m = 0, m_low = 0;
     for (int p = 0; p < P; ++p) {
         ng[p] = orc_basis_bruteforce(dk, p, NULL, NULL, 0);
         if (ng[p] < 0) return 1;
         off[p] = m;
         m += ng[p];
+        if (p < low_orders) m_low = m;   /* features are numbered order by order */
     }
     int32_t *tup = (int32_t *)malloc(sizeof(int32_t) * (size_t)(m * (P > 1 ? P - 1 : 1)));
     double *qw = (double *)malloc(sizeof(double) * (size_t)m);     /* query-side weight per feature */
@@ -459,7 +488,8 @@ int orc_bf16_state_decode(const float *q, const float *k, const float *v, double
             pthread_t th[64];
             int started[64] = {0};
             for (int t = 0; t < nt; ++t) {
-                jobs[t] = (prefix_job){kh, vh, tup, ord, S, n0, m * t / nt, m * (t + 1) / nt, dk, dv, W, round_mode};
+                jobs[t] = (prefix_job){kh, vh, tup, ord, S, n0, m * t / nt, m * (t + 1) / nt, m_low, dk, dv, W,
+                                       round_mode};
                 started[t] = t > 0 && pthread_create(&th[t], NULL, prefix_worker, &jobs[t]) == 0;
                 if (t > 0 && !started[t]) prefix_worker(&jobs[t]);
             }
@@ -483,7 +513,7 @@ int orc_bf16_state_decode(const float *q, const float *k, const float *v, double
                         x += mk * (c < dv ? (double)vh[t * dv + c] : 1.0);
                     }
                     y[c] += mq * x;
-                    if (store) S[f * (dv + 1) + c] = round_mode ? orc_round_bf16(x) : x;
+                    if (store) S[f * (dv + 1) + c] = store_round(round_mode, f, m_low, x);
                 }
             }
             if (store) first = s + 1;
@@ -492,4 +522,17 @@ int orc_bf16_state_decode(const float *q, const float *k, const float *v, double
     }
     free(tup); free(qw); free(ord); free(S); free(y);
     return 0;
+}
+
+int orc_bf16_state_decode(const float *q, const float *k, const float *v, double *out,
+                          int64_t bh, int64_t n0, int64_t n, int dk, int dv, int P, int round_mode, int window) {
+    return state16_decode(q, k, v, out, bh, n0, n, dk, dv, P, round_mode ? 1 : 0, 0, window);
+}
+
+/* O8 with the fp16 state: features of the orders below low_orders stored in
+ * binary32, the rest in binary16 (the same reading of the 16-bit storage
+ * otherwise: exact prefix rounded once, exact adds, rounding on every store). */
+int orc_f16_state_decode(const float *q, const float *k, const float *v, double *out, int64_t bh, int64_t n0,
+                         int64_t n, int dk, int dv, int P, int low_orders, int window) {
+    return state16_decode(q, k, v, out, bh, n0, n, dk, dv, P, 2, low_orders, window);
 }

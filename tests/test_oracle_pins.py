@@ -503,3 +503,114 @@ def test_grad_state_form_identities(oracle, P):
     gq, gk, gv = oracle.taylor_attention_grad(q, k, v, dout, P)
     for a, b in ((gq[0], gq_ref), (gk[0], gk_ref), (gv[0], gv_ref)):
         assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
+
+# ------------------------------------------------- fp16 state with fp32 low orders (O8)
+
+def test_round_f16_matches_library_rounding(oracle):
+    """O8b against numpy's float64 -> float16 conversion (IEEE round to nearest,
+    ties to even) on random values over binary16's whole range, exact half-way
+    cases of normal and subnormal spacing, and the overflow edge: bit-exact."""
+    rng = np.random.default_rng(15)
+    e = rng.integers(-30, 17, size=200000)
+    x = rng.uniform(1.0, 2.0, size=e.size) * np.exp2(e) * rng.choice([-1.0, 1.0], size=e.size)
+    m = rng.integers(0, 1024, size=20000)
+    ee = rng.integers(-14, 16, size=m.size)
+    ties = (1024 + m + 0.5) * np.exp2(ee - 10.0)                 # half-way between normal neighbours
+    sub_ties = (rng.integers(0, 1024, size=5000) + 0.5) * 2.0 ** -24   # half-way in the subnormal range
+    edge = np.array([65504.0, 65519.99, 65520.0, 65536.0, -65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26])
+    x = np.concatenate([x, ties, -ties, sub_ties, edge])
+    with np.errstate(over="ignore"):                            # the overflow edge becomes inf
+        ref = x.astype(np.float16).astype(np.float64)
+    got = oracle.round_f16(x)
+    assert np.array_equal(got, ref)
+
+
+def test_round_f16_integers(oracle):
+    """Integers above 2048 are spaced 2 apart in binary16; half-way cases go to
+    the even significand."""
+    got = oracle.round_f16([2047, 2048, 2049, 2050, 2051, 2053, 4097, 4099, 4101])
+    assert list(got) == [2047, 2048, 2048, 2050, 2052, 2052, 4096, 4100, 4100]
+
+
+@pytest.mark.parametrize("low_orders", [0, 1])
+def test_f16_state_count_stalls_only_in_fp16(oracle, low_orders):
+    """P = 1: the normaliser element counts tokens.  In fp16 (low_orders 0) it
+    stops at 2048, where adding 1 is a half-way case that rounds back to the
+    even neighbour; with order 0 in fp32 (low_orders 1) it counts on exactly.
+    With v_0 = w and v_s = 0 after it, row s is w / (count + 1)."""
+    n = 2200
+    w = np.array([2048.0, -3.0, 0.375], dtype=np.float32)
+    v = np.zeros((1, n, 3), dtype=np.float32)
+    v[0, 0] = w
+    q = np.zeros((1, n, 2), dtype=np.float32)
+    o = oracle.f16_state_decode(q, q, v, 1, 0, low_orders=low_orders)[0]
+    s = np.arange(n)
+    count = np.minimum(s, 2048) if low_orders == 0 else s
+    assert np.array_equal(o, w[None, :].astype(np.float64) / (count + 1)[:, None])
+
+
+@pytest.mark.parametrize("d,P,n0", [(2, 3, 5), (4, 4, 17), (3, 2, 0)])
+def test_f16_state_all_fp32_is_fp32_close(oracle, d, P, n0):
+    """With every order stored in fp32 (low_orders = P) the only error is one
+    binary32 rounding per element per store: within 1e-5 of O1."""
+    q, k, v = _rand_qkv(700 + 10 * d + P, (2,), 60, d, 3)
+    a = oracle.f16_state_decode(q, k, v, P, n0, low_orders=P)
+    b = oracle.taylor_attention(q, k, v, P)[:, n0:]
+    assert np.max(np.abs(a - b)) <= 1e-5 * np.max(np.abs(b))
+
+
+def _state16_numpy(q, k, v, P, n0, low_orders, window):
+    """Brute-force reading of the fp16 state with numpy's own roundings: tuples
+    by itertools, exact (fp64) prefix sums stored rounded, each step adds its
+    pending tokens exactly, reads out, and every window-th step stores rounded
+    (fp32 for orders below low_orders, fp16 above)."""
+    import itertools
+    n, d = q.shape[0], q.shape[1]
+    dv = v.shape[1]
+    feats = [(p, t) for p in range(P) for t in itertools.combinations_with_replacement(range(d), p)]
+
+    def mono(x, t):
+        return float(np.prod([float(x[i]) for i in t])) if t else 1.0
+
+    def weight(p, t):   # p!/alpha! / (p! d^(p/2)) = 1 / (alpha! d^(p/2))
+        alpha = np.prod([math.factorial(t.count(i)) for i in set(t)]) if t else 1
+        return 1.0 / (alpha * d ** (p / 2))
+
+    def rnd(p, x):
+        return float(np.float32(x)) if p < low_orders else float(np.float16(x))
+
+    vv = lambda s, c: float(v[s, c]) if c < dv else 1.0
+    S = [[rnd(p, sum(mono(k[s], t) * vv(s, c) for s in range(n0))) for c in range(dv + 1)] for p, t in feats]
+    out, first = [], n0
+    for s in range(n0, n):
+        store = s - first + 1 >= window
+        y = np.zeros(dv + 1)
+        for i, (p, t) in enumerate(feats):
+            mq = weight(p, t) * mono(q[s], t)
+            for c in range(dv + 1):
+                x = S[i][c] + sum(mono(k[u], t) * vv(u, c) for u in range(first, s + 1))
+                y[c] += mq * x
+                if store:
+                    S[i][c] = rnd(p, x)
+        if store:
+            first = s + 1
+        out.append(y[:dv] / y[dv])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("low_orders,window", [(0, 1), (1, 1), (2, 1), (2, 3)])
+def test_f16_state_matches_numpy_emulation(oracle, low_orders, window):
+    """O8 (fp16 with fp32 low orders) against the brute-force numpy reading on
+    a case whose sums fp16 cannot hold exactly (large v): equal to fp64
+    rounding; and the orders split differently give different results."""
+    rng = np.random.default_rng(21 + low_orders)
+    n, d, P, n0 = 14, 2, 3, 4
+    q = rng.normal(size=(1, n, d)).astype(np.float32)
+    k = rng.normal(size=(1, n, d)).astype(np.float32)
+    v = (rng.normal(size=(1, n, 2)) * 300).astype(np.float32)
+    a = oracle.f16_state_decode(q, k, v, P, n0, low_orders=low_orders, window=window)[0]
+    b = _state16_numpy(q[0], k[0], v[0], P, n0, low_orders, window)
+    assert np.max(np.abs(a - b)) <= 1e-9 * np.max(np.abs(b))
+    other = oracle.f16_state_decode(q, k, v, P, n0, low_orders=3 - low_orders if low_orders != 1 else 3,
+                                    window=window)[0]
+    assert np.max(np.abs(other - a)) > 1e-6 * np.max(np.abs(b))
