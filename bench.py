@@ -108,6 +108,18 @@ def decode_read_bytes(wl, state_elem: int = 4) -> float:
     return float(wl.batch * wl.heads * (state_elem * m * (wl.d_v + 1) + 4 * wl.d_k))
 
 
+def f16_low_features(wl) -> int:
+    """Features an fp16 state keeps in fp32: orders 0 and 1, rounded up to 8."""
+    return min(-(-(1 + wl.d_k) // 8) * 8, features(wl.d_k, wl.P))
+
+
+def decode_bytes_f16_main(wl) -> float:
+    """Algorithmic HBM bytes of one decode step's main kernel on an fp16 state:
+    the binary16 words (features from m_low on) read and written once."""
+    m = features(wl.d_k, wl.P) - f16_low_features(wl)
+    return float(wl.batch * wl.heads * 2 * 2 * m * (wl.d_v + 1))
+
+
 def decode_bytes(wl, state_elem: int = 4) -> float:
     """Algorithmic HBM bytes of one decode step: every head's state (fp32, or
     bf16 with state_elem = 2) read and written once, plus the token's fp32
@@ -214,7 +226,7 @@ def time_decode(sata, idx, st, wl, steps: int, warmup: int, seed: int):
     sata.sata_profile_enable(False)
     ms = e0.elapsed_time(e1) / steps
     kern = {}
-    for name in ("decode_stream", "decode_finish", "decode_read", "decode_fold"):
+    for name in ("decode_stream", "decode_finish", "decode_read", "decode_fold", "decode_low"):
         kms, kn = sata.sata_profile_query(name)
         if kn:
             kern[name] = (kms / kn, kn)
@@ -292,6 +304,14 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
     st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
     ms, kern = time_decode(sata, idx, st, wl, steps, warmup, wl.seed + 30)
     kern_ms, fin_ms = kern["decode_stream"][0], kern["decode_finish"][0]
+    sth = sata.State(idx, wl.batch, wl.heads, dtype=torch.float16)
+    sata.sata_state_convert(st, sth)
+    log("decode: the same state converted to fp16 storage (orders 0 and 1 in fp32)")
+    msh, kh = time_decode(sata, idx, sth, wl, steps, warmup, wl.seed + 30)
+    kernh, finh, lowh = kh["decode_stream"][0], kh["decode_finish"][0], kh["decode_low"][0]
+    sth.free()
+    nbytesh = decode_bytes_f16_main(wl)
+    achh = nbytesh / (kernh * 1e-3) / 1e9
     st16 = sata.State(idx, wl.batch, wl.heads, dtype=torch.bfloat16)
     sata.sata_state_convert(st, st16)
     st.free()
@@ -323,6 +343,18 @@ def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
         "finish_ms_per_step": fin_ms,
         "gbs_whole_step": nbytes / (ms * 1e-3) / 1e9,
         "torch_streams": None,
+        "f16_state": {
+            "accuracy": ("binary16 words for orders >= 2, fp32 for orders 0 and 1: every step of the 1024 after "
+                         "the prefix within 6e-4 of the exact Taylor output (tests: 2e-2 bar)"),
+            "value": wl.batch / (msh * 1e-3), "unit": "tokens/s", "ms_per_step": msh,
+            "roofline": {
+                "bound": "hbm", "achieved": achh, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achh / PEAK_HBM_GBS, "kernel": "decode_stream", "avg_launch_ms": kernh,
+                "bytes_per_launch": nbytesh, "traffic": traffic_for("decode_stream_f16", wl.name),
+            },
+            "low_orders_ms_per_step": lowh,
+            "finish_ms_per_step": finh,
+        },
         "bf16_state": {
             "accuracy": ("the state is rounded to bf16 after every update, and the output drifts from the exact "
                          "Taylor output past the 2e-2 bf16 bar within about 64 steps at d = 64: a bandwidth "
@@ -670,6 +702,7 @@ TRAFFIC_KERNELS = [
     (r"scan16_kernelILi16ELi128ELi1E", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_scan16.hip"),
     (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_rows_kernel<64, float, unsigned short, true>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_rows_kernel<64, float, _Float16, true>", "decode_stream_f16", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_fold_kernel<64, float, float, 3, false>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
@@ -708,6 +741,11 @@ def traffic_run():
     st = build_state(sata, idx, wl, wl.n, "f32", wl.seed)
     time_decode(sata, idx, st, wl, 2, 0, wl.seed + 30)
     log("traffic run: decode done")
+    sth = sata.State(idx, wl.batch, wl.heads, dtype=torch.float16)
+    sata.sata_state_convert(st, sth)
+    time_decode(sata, idx, sth, wl, 2, 0, wl.seed + 30)
+    log("traffic run: fp16-state decode done")
+    sth.free()
     st16 = sata.State(idx, wl.batch, wl.heads, dtype=torch.bfloat16)
     sata.sata_state_convert(st, st16)
     st.free()
@@ -839,6 +877,10 @@ def main():
         dec = decode_section(sata, dwl, args.decode_steps, 8, not args.no_flatness)
         log("decode: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak)"
             % (dec["ms_per_step"], dec["value"], dec["roofline"]["achieved"], 100 * dec["roofline"]["frac"]))
+        h16 = dec["f16_state"]
+        log("decode, fp16 state: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak), fp32 orders %.3f ms"
+            % (h16["ms_per_step"], h16["value"], h16["roofline"]["achieved"], 100 * h16["roofline"]["frac"],
+               h16["low_orders_ms_per_step"]))
         b16 = dec["bf16_state"]
         log("decode, bf16 state: %.3f ms/step, %.3e tok/s, stream %.0f GB/s (%.1f%% of peak)"
             % (b16["ms_per_step"], b16["value"], b16["roofline"]["achieved"], 100 * b16["roofline"]["frac"]))

@@ -75,6 +75,29 @@ template <int N> struct WordBf16 {
 };
 template <> struct Word<bf16_t, 8> : WordBf16<8> {};
 template <> struct Word<bf16_t, 4> : WordBf16<4> {};
+template <int N> struct WordF16 {
+    typedef uint32_t T __attribute__((ext_vector_type(N / 2)));
+    typedef _Float16 H2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ void widen(const T u, float (&x)[N]) {
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            // (the element goes through a scalar first: a bit cast applied to the indexed
+            // vector element directly compiles to a read of element 0 for every j)
+            const uint32_t e = u[j];
+            const H2 h = __builtin_bit_cast(H2, e);
+            x[2 * j] = (float)h[0];
+            x[2 * j + 1] = (float)h[1];
+        }
+    }
+    static __device__ __forceinline__ T narrow(const float (&x)[N]) {   // nearest even
+        T r;
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) r[j] = __builtin_bit_cast(uint32_t, H2{(_Float16)x[2 * j], (_Float16)x[2 * j + 1]});
+        return r;
+    }
+};
+template <> struct Word<f16_t, 8> : WordF16<8> {};
+template <> struct Word<f16_t, 4> : WordF16<4> {};
 
 // Wave-level reduce-scatter of DV (power of two) per-lane values followed by a
 // plain reduction across the remaining lane groups: afterwards lane l holds the
@@ -158,7 +181,7 @@ template <int DV, typename TIn, typename TS>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
                    int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
-                   const TIn *__restrict__ v, float *__restrict__ partial) {
+                   const TIn *__restrict__ v, float *__restrict__ partial, int64_t fbase) {
     constexpr int NC = DV + 1;
     constexpr int FPT = dec_fpt<TS>();
     constexpr int R = (NC + 1) / 2;                    // rows of the first load batch
@@ -167,8 +190,8 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
     __shared__ float red[kDecThreads / 64][NC];
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
-    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
-    const bool valid = f0 < m_pad;   // m_pad is a multiple of 64, so all FPT features are in range
+    const int64_t f0 = fbase + ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
+    const bool valid = f0 < m_pad;   // m_pad and fbase are multiples of 8 = FPT's largest value
     TS *Sb = state + (int64_t)bh * NC * m_pad + f0;
     auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
 
@@ -239,7 +262,7 @@ template <int DV, typename TIn, typename TS, bool UPDATE>
 __global__ __launch_bounds__(kDecThreads)
 void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef, TS *__restrict__ state,
                         int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
-                        const TIn *__restrict__ v, float *__restrict__ partial) {
+                        const TIn *__restrict__ v, float *__restrict__ partial, int64_t fbase) {
     constexpr int NC = DV + 1;
     constexpr int NR = rows_per_group<DV>();
     constexpr int FPT = dec_fpt<TS>();
@@ -250,8 +273,8 @@ void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restric
     const int tid = threadIdx.x;
     const int r0 = blockIdx.z * NR;
     const int nr = min(NR, NC - r0);                 // rows of this group (uniform)
-    const int64_t f0 = ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
-    const bool valid = f0 < m_pad;                   // m_pad is a multiple of 64
+    const int64_t f0 = fbase + ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
+    const bool valid = f0 < m_pad;                   // m_pad and fbase are multiples of 8
     TS *Sb = state + ((int64_t)bh * NC + r0) * m_pad + min<int64_t>(f0, m_pad - FPT);
     auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
 
@@ -334,7 +357,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
                         int64_t m_pad, int dk, const TIn *__restrict__ q, const TIn *__restrict__ k,
                         const TIn *__restrict__ v, const float *__restrict__ pend_k, const float *__restrict__ pend_v,
                         int npend, float *__restrict__ partial, const float *__restrict__ qs, int nq,
-                        float *__restrict__ bpartial) {
+                        float *__restrict__ bpartial, int64_t fbase) {
     constexpr int NC = DV + 1;
     constexpr int CT = (NC + 15) / 16;               // column tiles
     constexpr int T = kMaxDecodeWindow;
@@ -349,8 +372,13 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
     const bool readout = q != nullptr;
     const int ntok = npend + (k != nullptr ? 1 : 0);
     const int kt = (ntok + 3) / 4;                   // token groups of 4
-    const int64_t fw = ((int64_t)blockIdx.x * (kFoldThreads / 64) + wave) * 64;   // the wavefront's first feature
-    const bool active = fw < m_pad;                  // m_pad is a multiple of 64
+    const int64_t fw = fbase + ((int64_t)blockIdx.x * (kFoldThreads / 64) + wave) * 64;   // the wavefront's first feature
+    const bool active = fw < m_pad;
+    // the lane's state word of feature group g (features fw + 16 g + 4 lg .. + 3) lies inside
+    // the rows: m_pad is a multiple of 64 and fbase of 8, so a wavefront's 64 features may run
+    // past m_pad when fbase > 0, a word never straddles it
+    auto wok = [&](int g) { return fw + 16 * g + 4 * lg < m_pad; };
+    const uint32_t padt = (uint32_t)(dk + 1) * 0x01010101u;   // a tuple of monomial 0
     TS *Sb = state + (int64_t)bh * NC * m_pad;
 
     // the wavefront's state words: feature group g, column tile ct -> row ct*16 + l16,
@@ -362,7 +390,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             acc[g][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (active && c < NC) {
+            if (wok(g) && c < NC) {
                 float x[4];
                 Wd::widen(*reinterpret_cast<const typename Wd::T *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg), x);
                 acc[g][ct] = f32x4{x[0], x[1], x[2], x[3]};
@@ -390,7 +418,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
             for (int g = 0; g < 4; ++g) {
                 uint32_t tt[4];
                 float cc[4];
-                lane_tables<4>(active, tup, coef, active ? fw + 16 * g + 4 * lg : 0, tt, cc);
+                lane_tables<4>(wok(g), tup, coef, wok(g) ? fw + 16 * g + 4 * lg : 0, tt, cc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float a = cc[r] * monomial_n<NF>(tt[r], qrow, 1);
@@ -442,7 +470,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
         // A operand: lane holds feature fw + 16 g + l16 of token 4 kk + lg
         uint32_t ta[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) ta[g] = tup[fw + 16 * g + l16];
+        for (int g = 0; g < 4; ++g) ta[g] = fw + 16 * g + l16 < m_pad ? tup[fw + 16 * g + l16] : padt;
         for (int kk = 0; kk < kt; ++kk) {
             float a[4];
 #pragma unroll
@@ -461,7 +489,8 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const float x[4] = {acc[g][ct][0], acc[g][ct][1], acc[g][ct][2], acc[g][ct][3]};
-                    *reinterpret_cast<typename Wd::T *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg) = Wd::narrow(x);
+                    if (wok(g))
+                        *reinterpret_cast<typename Wd::T *>(Sb + (int64_t)c * m_pad + fw + 16 * g + 4 * lg) = Wd::narrow(x);
                 }
             }
         }
@@ -476,7 +505,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t f = fw + 16 * g + 4 * lg + r;
-            psq[g][r] = active ? coef[f] * monomial_n<NF>(tup[f], sq, 1) : 0.f;
+            psq[g][r] = wok(g) ? coef[f] * monomial_n<NF>(tup[f], sq, 1) : 0.f;
         }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -498,6 +527,122 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
     }
 }
 
+// fp16 states keep the features of orders 0 and 1 (f < m_low of every row, a multiple of 8)
+// in fp32 (sata_state::d_low); the main kernels start at feature m_low and leave them out.
+// This kernel, one workgroup per head on the same stream after the step's main kernel, adds
+// the tokens to fold in -- the npend deferred ones (pend_k / pend_v), then the step's own
+// (k, v) when given -- reads out with q when given, and adds the readout to the head's first
+// partial row (written by the main kernel) for the finish kernel.  Thread t takes the word
+// w = t % W (features 8w .. 8w+7, W = m_low / 8) of the rows t / W + j G (G = 256 / W): the
+// word's monomials are formed once per token for all its rows.  Tokens are staged in LDS 16
+// at a time; the readout goes through LDS so each row is summed over its words in order.
+constexpr int kLowThreads = 256;
+constexpr int kLowStage = 16;
+template <int DV, typename TIn, int NF>
+__global__ __launch_bounds__(kLowThreads) void decode_low_kernel(
+    const uint32_t *__restrict__ tup, const float *__restrict__ coef, float *__restrict__ low, int64_t m_low, int dk,
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v, const float *__restrict__ pend_k,
+    const float *__restrict__ pend_v, int npend, float *__restrict__ partial, int nblk) {
+    constexpr int NC = DV + 1;
+    constexpr int KST = tok_stage<DV>();
+    // rows per thread: W <= 9 words (d_K <= 64, G >= 28) or 17 (d_K = 128, G = 15)
+    constexpr int RPT = DV > 64 ? 9 : 3;
+    constexpr int WMAX = DV > 64 ? 17 : 9;
+    __shared__ float sk[kLowStage][KST], sv[kLowStage][NC], sq[KST];
+    __shared__ float red[NC * WMAX];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int W = (int)(m_low / 8), G = kLowThreads / W;
+    const int w = tid % W, g0 = tid / W;
+    const bool act = g0 < G;
+    float *L = low + (int64_t)bh * NC * m_low + 8 * w;
+    uint32_t tt[8];
+    float cc[8];
+    lane_tables<8>(act, tup, coef, 8 * w, tt, cc);
+    float x[RPT][8];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int c = g0 + j * G;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[j][e] = 0.f;
+        if (act && c < NC) {
+            const float4 a = *reinterpret_cast<const float4 *>(L + (int64_t)c * m_low);
+            const float4 b = *reinterpret_cast<const float4 *>(L + (int64_t)c * m_low + 4);
+            x[j][0] = a.x; x[j][1] = a.y; x[j][2] = a.z; x[j][3] = a.w;
+            x[j][4] = b.x; x[j][5] = b.y; x[j][6] = b.z; x[j][7] = b.w;
+        }
+    }
+    const int ntok = npend + (k != nullptr ? 1 : 0);
+    for (int t0 = 0; t0 < ntok; t0 += kLowStage) {
+        __syncthreads();   // the previous group has been used
+        for (int i = tid; i < kLowStage * KST; i += kLowThreads) {
+            const int t = i / KST, c = i % KST, tok = t0 + t;
+            float val = 0.f;
+            if (tok < ntok && c < dk)
+                val = tok < npend ? pend_k[((int64_t)bh * kMaxDecodeWindow + tok) * dk + c] : to_f32(k[(int64_t)bh * dk + c]);
+            else if (tok < ntok && c == dk)
+                val = 1.f;
+            sk[t][c] = val;
+        }
+        for (int i = tid; i < kLowStage * NC; i += kLowThreads) {
+            const int t = i / NC, c = i % NC, tok = t0 + t;
+            float val = 0.f;
+            if (tok < ntok)
+                val = c == DV ? 1.f
+                              : (tok < npend ? pend_v[((int64_t)bh * kMaxDecodeWindow + tok) * DV + c]
+                                             : to_f32(v[(int64_t)bh * DV + c]));
+            sv[t][c] = val;
+        }
+        __syncthreads();
+        const int nt = min(kLowStage, ntok - t0);
+        for (int t = 0; t < nt; ++t) {
+            float phk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) phk[e] = monomial_n<NF>(tt[e], sk[t], 1);
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) {
+                const int c = g0 + j * G;
+                if (act && c < NC) {
+                    const float vc = sv[t][c];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[j][e] += phk[e] * vc;
+                }
+            }
+        }
+    }
+    if (ntok > 0) {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const int c = g0 + j * G;
+            if (act && c < NC) {
+                *reinterpret_cast<float4 *>(L + (int64_t)c * m_low) = float4{x[j][0], x[j][1], x[j][2], x[j][3]};
+                *reinterpret_cast<float4 *>(L + (int64_t)c * m_low + 4) = float4{x[j][4], x[j][5], x[j][6], x[j][7]};
+            }
+        }
+    }
+    if (q == nullptr) return;
+    if (tid < KST) sq[tid] = tid < dk ? to_f32(q[(int64_t)bh * dk + tid]) : (tid == dk ? 1.f : 0.f);
+    __syncthreads();
+    float psq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) psq[e] = cc[e] * monomial_n<NF>(tt[e], sq, 1);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int c = g0 + j * G;
+        if (act && c < NC) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a += psq[e] * x[j][e];
+            red[c * W + w] = a;
+        }
+    }
+    __syncthreads();
+    if (tid < NC) {
+        float sum = 0.f;
+        for (int ww = 0; ww < W; ++ww) sum += red[tid * W + ww];
+        partial[(int64_t)bh * nblk * NC + tid] += sum;
+    }
+}
+
 // Readout of the state as it stands, without an update: the non-folding steps
 // of a deferred decode.  A pure read stream, so a workgroup walks tpw
 // consecutive feature tiles (256 * FPT features each) of its head and keeps
@@ -509,7 +654,7 @@ template <int DV, typename TIn, typename TS>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ coef,
                         const TS *__restrict__ state, int64_t m_pad, int dk, const TIn *__restrict__ q,
-                        float *__restrict__ partial, int tpw) {
+                        float *__restrict__ partial, int tpw, int64_t fbase) {
     constexpr int NC = DV + 1;
     constexpr int RA = (NC + 1) / 2;   // rows of the first half-tile
     constexpr int FPT = dec_fpt<TS>();
@@ -526,7 +671,7 @@ void decode_read_kernel(const uint32_t *__restrict__ tup, const float *__restric
     const TS *Sb = state + (int64_t)bh * NC * m_pad;
     // A lane past the last feature re-reads the last word (in bounds, weight 0),
     // so every load is unconditional.
-    auto fidx = [&](int i) { return (first + i) * TILE + (int64_t)tid * FPT; };
+    auto fidx = [&](int i) { return fbase + (first + i) * TILE + (int64_t)tid * FPT; };
     auto fclamp = [&](int i) { return min<int64_t>(fidx(i), m_pad - FPT); };
     auto row = [&](int64_t f, int r) { return reinterpret_cast<const WT *>(Sb + (int64_t)r * m_pad + f); };
     auto tables = [&](int i, uint32_t (&tt)[FPT], float (&cc)[FPT]) {
@@ -712,26 +857,28 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
     const int nblk = (int)grid.x;
     float *partial = static_cast<float *>(st->d_work);
     TS *S = static_cast<TS *>(st->d_state);
+    const int64_t fbase = st->m_low;   // fp16 states: the lowest orders are the low kernel's
     const TIn *qi = static_cast<const TIn *>(q), *ki = static_cast<const TIn *>(k), *vi = static_cast<const TIn *>(v);
     switch (mode) {
         case kDecodePlain: {
             ProfScope ps(kProfDecode, stream);
             if (groups > 1)
                 hipLaunchKernelGGL((decode_rows_kernel<DV, TIn, TS, true>), grid, dim3(kDecThreads), 0, stream,
-                                   idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
+                                   idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial, fbase);
             else if constexpr (DV <= 64)
                 hipLaunchKernelGGL((decode_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
-                                   idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial);
+                                   idx->d_coef, S, idx->m_pad, idx->dk, qi, ki, vi, partial, fbase);
             break;
         }
         case kDecodeRead: {
             ProfScope ps(kProfDecodeRead, stream);
             if (groups > 1)
                 hipLaunchKernelGGL((decode_rows_kernel<DV, TIn, TS, false>), grid, dim3(kDecThreads), 0, stream,
-                                   idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, nullptr, nullptr, partial);
+                                   idx->d_tup, idx->d_coef, S, idx->m_pad, idx->dk, qi, nullptr, nullptr, partial,
+                                   fbase);
             else if constexpr (DV <= 64)
                 hipLaunchKernelGGL((decode_read_kernel<DV, TIn, TS>), grid, dim3(kDecThreads), 0, stream, idx->d_tup,
-                                   idx->d_coef, S, idx->m_pad, idx->dk, qi, partial, tpw);
+                                   idx->d_coef, S, idx->m_pad, idx->dk, qi, partial, tpw, fbase);
             break;
         }
         case kDecodeFold:
@@ -741,12 +888,27 @@ static hipError_t launch_decode_t(const sata_index *idx, const sata_state *st, c
             auto fold = idx->P >= 5 ? decode_fold_kernel<DV, TIn, TS, 4> : decode_fold_kernel<DV, TIn, TS, 3>;
             hipLaunchKernelGGL(fold, grid, dim3(kFoldThreads), 0, stream, idx->d_tup, idx->d_coef, S, idx->m_pad,
                                idx->dk, step ? qi : nullptr, step ? ki : nullptr, step ? vi : nullptr, st->d_pend_k,
-                               st->d_pend_v, st->npend, partial, nullptr, 0, nullptr);
+                               st->d_pend_v, st->npend, partial, nullptr, 0, nullptr, fbase);
             break;
         }
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || mode == kDecodeFlush) return e;
+    if (e != hipSuccess) return e;
+    if (st->m_low > 0) {
+        // the fp32 words of the lowest orders: the same update (a read step adds nothing, a
+        // fold the deferred tokens and the step's own) and readout, into workgroup 0's row
+        ProfScope ps(kProfDecodeLow, stream);
+        const bool upd = mode != kDecodeRead, fold_in = mode == kDecodeFold || mode == kDecodeFlush;
+        const bool own = mode == kDecodePlain || mode == kDecodeFold;
+        auto lowk = idx->P >= 5 ? decode_low_kernel<DV, TIn, 4> : decode_low_kernel<DV, TIn, 3>;
+        hipLaunchKernelGGL(lowk, dim3((unsigned)bh), dim3(kLowThreads), 0, stream, idx->d_tup, idx->d_coef, st->d_low,
+                           st->m_low, idx->dk, mode == kDecodeFlush ? nullptr : qi, upd && own ? ki : nullptr,
+                           upd && own ? vi : nullptr, st->d_pend_k, st->d_pend_v, fold_in ? st->npend : 0, partial,
+                           nblk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (mode == kDecodeFlush) return hipSuccess;
     {
         ProfScope ps(kProfDecodeFinish, stream);
         const int direct = mode == kDecodeRead ? 1 : 0;
@@ -775,28 +937,53 @@ static hipError_t launch_decode_dv(const sata_index *idx, const sata_state *st, 
                                    const void *k, const void *v, void *out, sata_dtype in_dt,
                                    sata_dtype out_dt, DecodeMode mode, hipStream_t s) {
     if (st->dtype == SATA_BF16) return launch_decode_ts<DV, bf16_t>(idx, st, q, k, v, out, in_dt, out_dt, mode, s);
+    if (st->dtype == SATA_F16) return launch_decode_ts<DV, f16_t>(idx, st, q, k, v, out, in_dt, out_dt, mode, s);
     return launch_decode_ts<DV, float>(idx, st, q, k, v, out, in_dt, out_dt, mode, s);
 }
 
-// Element-wise state conversion between fp32 and bf16 (round to nearest even).
+// Element-wise state conversion between element types (to bf16 or fp16: round to nearest
+// even).  Element i is feature i % m_pad of row i / m_pad; in an fp16 state the features
+// below m_low are the fp32 values of its low array, and their fp16 slots are written as zero.
+template <typename TS> constexpr bool has_low() { return std::is_same<TS, f16_t>::value; }
 template <typename TSrc, typename TDst>
-__global__ __launch_bounds__(256) void convert_kernel(const TSrc *__restrict__ src, TDst *__restrict__ dst, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        dst[i] = from_f32<TDst>(to_f32(src[i]));
+__global__ __launch_bounds__(256) void convert_kernel(const TSrc *__restrict__ src, const float *__restrict__ src_low,
+                                                      int64_t src_m_low, TDst *__restrict__ dst,
+                                                      float *__restrict__ dst_low, int64_t dst_m_low, int64_t m_pad,
+                                                      int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / m_pad, f = i - r * m_pad;
+        const float x = has_low<TSrc>() && f < src_m_low ? src_low[r * src_m_low + f] : to_f32(src[i]);
+        if (has_low<TDst>() && f < dst_m_low) {
+            dst_low[r * dst_m_low + f] = x;
+            dst[i] = from_f32<TDst>(0.f);
+        } else {
+            dst[i] = from_f32<TDst>(x);
+        }
+    }
 }
 
 hipError_t launch_state_convert(const sata_state *src, sata_state *dst, hipStream_t stream) {
-    const int64_t n = (int64_t)src->batch * src->heads * (src->idx->dv + 1) * src->idx->m_pad;
-    const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 1 << 16);
-    if (src->dtype == SATA_F32 && dst->dtype == SATA_BF16)
-        hipLaunchKernelGGL((convert_kernel<float, bf16_t>), dim3(grid), dim3(256), 0, stream,
-                           static_cast<const float *>(src->d_state), static_cast<bf16_t *>(dst->d_state), n);
-    else if (src->dtype == SATA_BF16 && dst->dtype == SATA_F32)
-        hipLaunchKernelGGL((convert_kernel<bf16_t, float>), dim3(grid), dim3(256), 0, stream,
-                           static_cast<const bf16_t *>(src->d_state), static_cast<float *>(dst->d_state), n);
-    else
+    if (src->dtype == dst->dtype)
         return hipMemcpyAsync(dst->d_state, src->d_state, (size_t)src->state_bytes, hipMemcpyDeviceToDevice, stream);
-    return hipGetLastError();
+    const int64_t m_pad = src->idx->m_pad;
+    const int64_t n = (int64_t)src->batch * src->heads * (src->idx->dv + 1) * m_pad;
+    const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 1 << 16);
+    auto go = [&](auto s_t, auto d_t) {
+        using TSrc = decltype(s_t);
+        using TDst = decltype(d_t);
+        hipLaunchKernelGGL((convert_kernel<TSrc, TDst>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<const TSrc *>(src->d_state), src->d_low, src->m_low,
+                           static_cast<TDst *>(dst->d_state), dst->d_low, dst->m_low, m_pad, n);
+        return hipGetLastError();
+    };
+    auto to = [&](auto s_t) {
+        if (dst->dtype == SATA_BF16) return go(s_t, bf16_t{});
+        if (dst->dtype == SATA_F16) return go(s_t, f16_t{});
+        return go(s_t, float{});
+    };
+    if (src->dtype == SATA_BF16) return to(bf16_t{});
+    if (src->dtype == SATA_F16) return to(f16_t{});
+    return to(float{});
 }
 
 hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void *q, const void *k,
@@ -918,7 +1105,7 @@ static hipError_t block_prefill_t(const sata_index *idx, sata_state *st, const v
                                     : decode_fold_kernel<DV, float, float, 3, true>;
             hipLaunchKernelGGL(fold, dim3((unsigned)tiles, (unsigned)bh), dim3(kFoldThreads), 0, stream, idx->d_tup,
                                idx->d_coef, static_cast<float *>(st->d_state), idx->m_pad, idx->dk, nullptr, nullptr,
-                               nullptr, st->d_pend_k, st->d_pend_v, T, nullptr, qs, T, partial);
+                               nullptr, st->d_pend_k, st->d_pend_v, T, nullptr, qs, T, partial, (int64_t)0);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;

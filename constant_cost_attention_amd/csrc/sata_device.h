@@ -14,8 +14,11 @@ typedef uint16_t bf16_t;                                     // bfloat16 storage
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));   // MFMA operand, 8 x bf16
 typedef float f32x4 __attribute__((ext_vector_type(4)));     // MFMA accumulator, 16x16 tile
 
+typedef _Float16 f16_t;                                      // IEEE binary16 storage
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float to_f32(f16_t x) { return (float)x; }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
@@ -23,6 +26,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
     __bf16 b = (__bf16)x;                                    // round to nearest even
     return __builtin_bit_cast(bf16_t, b);
 }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (f16_t)x; }   // nearest even
 
 // Packed feature tuple (see sata_internal.h): four index slots, unused ones
 // pointing at the constant-1 slot.

@@ -47,9 +47,15 @@ constexpr int kMaxScan16Dim = 128;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-int64_t dtype_bytes(sata_dtype t) { return t == SATA_BF16 ? 2 : 4; }
+int64_t dtype_bytes(sata_dtype t) { return t == SATA_BF16 || t == SATA_F16 ? 2 : 4; }
 
-bool valid_dtype(int t) { return t == SATA_F32 || t == SATA_BF16; }
+bool valid_dtype(int t) { return t == SATA_F32 || t == SATA_BF16; }              // inputs and outputs
+bool valid_state_dtype(int t) { return t == SATA_F32 || t == SATA_BF16 || t == SATA_F16; }
+
+// An fp16 state keeps the features of orders 0 and 1 (the constant and the d_K linear ones,
+// which grow with every token) in fp32: the first 1 + d_K features, rounded up to whole
+// 8-feature words (all of them when P = 1).
+int64_t f16_low_features(const sata_index *idx) { return std::min<int64_t>(round_up(1 + idx->dk, 8), idx->m_pad); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -197,7 +203,7 @@ sata_status check_prefill_args(const sata_index *idx, sata_state *st, const void
         return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
     if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "prefill needs d_k == d_v");
     if (st->dtype != SATA_F32)
-        return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 state with sata_state_convert)");
+        return fail(SATA_ERR_UNSUPPORTED, "prefill needs an fp32 state (convert a bf16 or fp16 state with sata_state_convert)");
     s = take_state_error(st);
     if (s != SATA_OK) return s;
     *nothing = n == 0;
@@ -587,7 +593,7 @@ sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, 
     if (!idx) return fail(SATA_ERR_INVALID, "index is NULL");
     if (!out) return fail(SATA_ERR_INVALID, "out is NULL");
     if (batch < 1 || heads < 1) return fail(SATA_ERR_INVALID, "batch and heads must be >= 1 (%d, %d)", batch, heads);
-    if (!valid_dtype(state_dt)) return fail(SATA_ERR_INVALID, "unknown state dtype");
+    if (!valid_state_dtype(state_dt)) return fail(SATA_ERR_INVALID, "unknown state dtype");
     const int64_t bh = (int64_t)batch * heads;
     if (bh > 65535) return fail(SATA_ERR_UNSUPPORTED, "batch*heads <= 65535 supported (got %lld)", (long long)bh);
     DeviceGuard g(idx->device);
@@ -599,8 +605,11 @@ sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, 
     st->heads = heads;
     st->device = idx->device;
     st->dtype = state_dt;
-    // m_pad is a multiple of 64, so the byte size is a multiple of 4 for either dtype
-    st->state_bytes = bh * (idx->dv + 1) * idx->m_pad * dtype_bytes(state_dt);
+    // m_pad is a multiple of 64, so the main array's byte size is a multiple of 128 for any
+    // element type; an fp16 state's fp32 words of the lowest orders follow it
+    const int64_t main_bytes = bh * (idx->dv + 1) * idx->m_pad * dtype_bytes(state_dt);
+    st->m_low = state_dt == SATA_F16 ? f16_low_features(idx) : 0;
+    st->state_bytes = main_bytes + bh * (idx->dv + 1) * st->m_low * (int64_t)sizeof(float);
     hipError_t e = hipMalloc(&st->d_state, (size_t)st->state_bytes);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -608,6 +617,7 @@ sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, 
         delete st;
         return fail(SATA_ERR_OOM, "state allocation of %lld bytes failed", nbytes);
     }
+    if (st->m_low) st->d_low = reinterpret_cast<float *>(static_cast<char *>(st->d_state) + main_bytes);
     e = hipHostMalloc(reinterpret_cast<void **>(&st->h_err), sizeof(uint32_t),
                       hipHostMallocMapped | hipHostMallocCoherent);
     if (e == hipSuccess) {
@@ -995,7 +1005,7 @@ void prof_clear_locked() {
 }
 
 const char *const kProfNames[sata::kProfCount] = {"prefill_scan", "prefill_combine", "decode_stream",
-                                                   "decode_finish", "decode_read", "decode_fold"};
+                                                   "decode_finish", "decode_read", "decode_fold", "decode_low"};
 
 }  // namespace
 

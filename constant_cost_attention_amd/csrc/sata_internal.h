@@ -59,6 +59,11 @@ struct sata_state {
     sata_dtype dtype = SATA_F32; // element type of the state
     void *d_state = nullptr;     // [B*H][d_V+1][m_pad] of dtype
     int64_t state_bytes = 0;
+    // SATA_F16 states: features f < m_low (the lowest orders, a multiple of 8) are held in
+    // fp32 at d_low [B*H][d_V+1][m_low], right after the fp16 array (whose slots for them
+    // stay zero); 0 and NULL for the other types
+    int64_t m_low = 0;
+    float *d_low = nullptr;
     void *d_work = nullptr;      // prefill / decode partial sums (grown on demand)
     int64_t work_bytes = 0;
     int window = 1;              // decode steps per state update (1: every step)
@@ -176,7 +181,7 @@ hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const Pre
 // profiling is on, and does nothing otherwise.
 enum ProfKernel {
     kProfScan = 0, kProfCombine = 1, kProfDecode = 2, kProfDecodeFinish = 3, kProfDecodeRead = 4, kProfDecodeFold = 5,
-    kProfCount = 6
+    kProfDecodeLow = 6, kProfCount = 7
 };
 struct ProfScope {
     ProfScope(int kernel, hipStream_t stream);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libsata.so")
 
 SATA_OK, SATA_ERR_INVALID, SATA_ERR_UNSUPPORTED, SATA_ERR_OOM, SATA_ERR_HIP = range(5)
 SATA_NOALLOC_SCRATCH_BYTES = 128 << 20   # include/sata.h
-SATA_F32, SATA_BF16 = 0, 1
+SATA_F32, SATA_BF16, SATA_F16 = 0, 1, 2
 
 _EXPORTS = (
     "sata_build_index", "sata_index_free", "sata_index_features", "sata_index_info",
@@ -121,6 +121,7 @@ def _check(status: int, func: str):
 
 
 _DTYPES = {torch.float32: SATA_F32, torch.bfloat16: SATA_BF16}
+_STATE_DTYPES = {torch.float32: SATA_F32, torch.bfloat16: SATA_BF16, torch.float16: SATA_F16}
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -168,7 +169,8 @@ class Index:
 
 class State:
     """Handle of sata_state (fixed-size state of batch x heads heads); dtype is
-    torch.float32 (default) or torch.bfloat16 (decode only)."""
+    torch.float32 (default), torch.float16 or torch.bfloat16 (the last two
+    decode only; float16 keeps orders 0 and 1 in float32)."""
 
     def __init__(self, index: Index, batch: int, heads: int, stream=None, dtype=torch.float32):
         self.index = index
@@ -177,7 +179,7 @@ class State:
         if dtype == torch.float32:
             self.ptr = sata_state_alloc(index, batch, heads, stream)
         else:
-            self.ptr = sata_state_alloc_dtype(index, batch, heads, _DTYPES.get(dtype, -1), stream)
+            self.ptr = sata_state_alloc_dtype(index, batch, heads, _STATE_DTYPES.get(dtype, -1), stream)
 
     def free(self):
         if self.ptr:
@@ -306,8 +308,24 @@ def state_tensor(state: State) -> torch.Tensor:
     if state.dtype == torch.float32:
         assert nbytes == 4 * shape[0] * shape[1] * shape[2] * shape[3]
         return torch.as_tensor(_CudaArray(ptr, shape, "<f4"), device="cuda")
+    if state.dtype == torch.float16:   # the binary16 array; the fp32 orders: state_low_tensor
+        assert nbytes >= 2 * shape[0] * shape[1] * shape[2] * shape[3]
+        return torch.as_tensor(_CudaArray(ptr, shape, "<f2"), device="cuda")
     assert nbytes == 2 * shape[0] * shape[1] * shape[2] * shape[3]
     return torch.as_tensor(_CudaArray(ptr, shape, "<i2"), device="cuda").view(torch.bfloat16)
+
+
+def state_low_tensor(state: State) -> torch.Tensor:
+    """An fp16 state's fp32 words of orders 0 and 1: [B, H, d_V+1, m_low] (no copy)."""
+    if state.dtype != torch.float16:
+        raise ValueError("only float16 states keep an fp32 part")
+    ptr, nbytes = sata_state_data(state)
+    idx = state.index
+    rows = state.batch * state.heads * (idx.d_v + 1)
+    main = 2 * rows * idx.m_pad
+    m_low = (nbytes - main) // (4 * rows)
+    return torch.as_tensor(_CudaArray(ptr + main, (state.batch, state.heads, idx.d_v + 1, m_low), "<f4"),
+                           device="cuda")
 
 
 def _prefill_args(index: Index, state: State, q, k, v, out):
@@ -408,7 +426,7 @@ def sata_describe_features(d_k: int, P: int):
 
 
 PROFILE_KERNELS = {"prefill_scan": 0, "prefill_combine": 1, "decode_stream": 2, "decode_finish": 3,
-                   "decode_read": 4, "decode_fold": 5}
+                   "decode_read": 4, "decode_fold": 5, "decode_low": 6}
 
 
 def sata_profile_enable(on: bool):

@@ -65,7 +65,8 @@ typedef enum {
 
 typedef enum {
     SATA_F32 = 0,              /* IEEE float32 */
-    SATA_BF16 = 1              /* bfloat16 (upper half of a float32) */
+    SATA_BF16 = 1,             /* bfloat16 (upper half of a float32) */
+    SATA_F16 = 2               /* IEEE binary16: a decode state's element type only */
 } sata_dtype;
 
 /* Immutable, device-resident M_p tables and coefficients for one (d_K, d_V, P). */
@@ -111,7 +112,26 @@ sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *
                              sata_state **out);
 
 /* As sata_state_alloc, with the state's element type chosen: SATA_F32 (what
- * sata_state_alloc gives) or SATA_BF16, same layout, half the bytes.  A bf16
+ * sata_state_alloc gives), SATA_F16 or SATA_BF16.
+ *
+ * SATA_F16 [hotdry, "Hardware optimisation paths and current limits": Float16
+ * storage is enough at P = 4 and halves the state's bandwidth]: the same layout
+ * in binary16, except that the features of orders 0 and 1 -- the first
+ * m_low = min(round_up(1 + d_K, 8), m_pad) features of each row, whose sums
+ * grow with every token (the token count, the sums of k) and would stop
+ * growing in 16 bits -- live in an fp32 array [batch][heads][d_V + 1][m_low]
+ * that follows the binary16 one in the allocation (whose slots for them stay
+ * zero).  Each decode step widens the stored values to fp32, adds the token's
+ * term, reads out from the fp32 sums and stores them rounded to the nearest
+ * binary16 (ties to even); the state holds 2 (d_V+1)(m_pad + 2 m_low) bytes
+ * per head, 50.2% of the fp32 state at d_K = 64, P = 4.  At P = 4 the outputs
+ * stay within 2e-2 of the exact Taylor attention for at least 1024 decode
+ * steps after a conversion (measured: 6e-4 at d_K = 64, 2.2e-3 at d_K = 16).
+ * Values must stay inside binary16's range (|S| < 65504 for the orders >= 2,
+ * i.e. sums of monomials of k of degree >= 2 times v; unit-scale inputs stay
+ * far below it).
+ *
+ * SATA_BF16: same layout, half the bytes.  A bf16
  * state serves sata_decode_step only: each step widens the stored values to
  * fp32, adds the new token's term, reads out from the fp32 sums and stores them
  * rounded to the nearest bf16 (ties to even), so the step streams half the
@@ -123,14 +143,15 @@ sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *
  * exact Taylor attention, and the error keeps growing with the number of
  * steps (about 3e-2 after 64); fewer orders or smaller heads drift faster.
  * Use it for short decodes after a long prefill; the fp32 state is exact to
- * fp32 rounding at any length.  sata_prefill on it returns
+ * fp32 rounding at any length.  sata_prefill on a bf16 or fp16 state returns
  * SATA_ERR_UNSUPPORTED: prefill into an fp32 state and convert.  An unknown
  * state_dt returns SATA_ERR_INVALID. */
 sata_status sata_state_alloc_dtype(const sata_index *idx, int batch, int heads, sata_dtype state_dt,
                                    void *stream, sata_state **out);
 
-/* Copy src's content into dst, converting the element type (fp32 -> bf16
- * rounds to nearest even; bf16 -> fp32 is exact; equal types copy).  Both must
+/* Copy src's content into dst, converting the element type (to bf16 or fp16
+ * rounds to nearest even, except an fp16 state's fp32 orders; to fp32 is
+ * exact; equal types copy).  Both must
  * belong to the same index and have the same batch and heads; src != dst
  * (else SATA_ERR_INVALID, nothing enqueued).  src's deferred decode tokens
  * (sata_state_set_decode_window) are folded into src first; dst's are
@@ -336,8 +357,10 @@ sata_status sata_debug_scan_faults(int item_base, int spin_limit);
  * (0) stops recording and keeps them.  sata_profile_query waits for the
  * recorded events of one kernel and returns the summed duration (ms) and the
  * launch count.  Kernel ids: 0 prefill scan, 1 prefill combine, 2 decode
- * stream, 3 decode finish, 4 decode read (deferred steps), 5 decode fold
- * (names from sata_profile_kernel_name, NULL for an unknown id).  Host-thread safe; not meant to be left on in production. */
+ * stream, 3 decode finish, 4 decode read (deferred steps), 5 decode fold,
+ * 6 decode of an fp16 state's fp32 orders (names from
+ * sata_profile_kernel_name, NULL for an unknown id).  Host-thread safe; not
+ * meant to be left on in production. */
 sata_status sata_profile_enable(int on);
 sata_status sata_profile_query(int kernel, double *total_ms, int64_t *launches);
 const char *sata_profile_kernel_name(int kernel);
