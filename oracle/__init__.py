@@ -87,7 +87,7 @@ def _load():
     lib.orc_bf16_state_decode.restype = cint
     lib.orc_round_f16_array.argtypes = [f64p, f64p, i64]
     lib.orc_round_f16_array.restype = None
-    lib.orc_f16_state_decode.argtypes = [f32p, f32p, f32p, f64p, i64, i64, i64, cint, cint, cint, cint, cint]
+    lib.orc_f16_state_decode.argtypes = [f32p, f32p, f32p, f64p, i64, i64, i64, cint, cint, cint, i64, cint]
     lib.orc_f16_state_decode.restype = cint
     for name in ("orc_recurrent_attention", "orc_recurrent_attention_f32"):
         fn = getattr(lib, name)
@@ -268,21 +268,25 @@ def round_f16(x) -> np.ndarray:
     return out
 
 
-def f16_state_decode(q, k, v, P: int, n0: int, low_orders: int = 3, window: int = 1) -> np.ndarray:
+def f16_state_decode(q, k, v, P: int, n0: int, low_orders: int = 3, window: int = 1,
+                     low_features: int | None = None) -> np.ndarray:
     """O8 for an fp16-stored state [hotdry, "Hardware optimisation paths and
     current limits": Float16 storage at P = 4]: as bf16_state_decode, but the
-    features of orders below low_orders are stored in fp32 (round to nearest
+    first low_features features (numbered order by order; by default all those
+    of the orders below low_orders) are stored in fp32 (round to nearest
     binary32) and the others in fp16 (round to nearest binary16, ties to
     even).  Returns rows n0..n-1: [..., n - n0, d_V].  fp64; moderate inputs."""
     lead, bh, n, dk, dv = _heads(np.asarray(q), np.asarray(k), np.asarray(v))
     if not 0 <= n0 <= n:
         raise ValueError("need 0 <= n0 <= n")
+    if low_features is None:
+        low_features = cumulative_basis(dk, low_orders) if low_orders > 0 else 0
     q32, qp = _f32(q)
     k32, kp = _f32(k)
     v32, vp = _f32(v)
     out = np.empty((bh, n - n0, dv), dtype=np.float64)
     rc = _load().orc_f16_state_decode(qp, kp, vp, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                                      bh, int(n0), n, dk, dv, int(P), int(low_orders), int(window))
+                                      bh, int(n0), n, dk, dv, int(P), int(low_features), int(window))
     if rc:
         raise ValueError("orc_f16_state_decode rejected its arguments")
     return out.reshape(tuple(lead) + (n - n0, dv))

@@ -439,16 +439,15 @@ static void *prefix_worker(void *arg) {
 }
 
 static int state16_decode(const float *q, const float *k, const float *v, double *out, int64_t bh, int64_t n0,
-                          int64_t n, int dk, int dv, int P, int round_mode, int low_orders, int window) {
-    if (bh < 0 || n0 < 0 || n < n0 || dk <= 0 || dv <= 0 || P < 1 || P > 8 || window < 1 || low_orders < 0)
+                          int64_t n, int dk, int dv, int P, int round_mode, int64_t m_low, int window) {
+    if (bh < 0 || n0 < 0 || n < n0 || dk <= 0 || dv <= 0 || P < 1 || P > 8 || window < 1 || m_low < 0)
         return 1;
-    int64_t ng[8], off[8], m = 0, m_low = 0;
+    int64_t ng[8], off[8], m = 0;
     for (int p = 0; p < P; ++p) {
         ng[p] = orc_basis_bruteforce(dk, p, NULL, NULL, 0);
         if (ng[p] < 0) return 1;
         off[p] = m;
         m += ng[p];
-        if (p < low_orders) m_low = m;   /* features are numbered order by order */
     }
     int32_t *tup = (int32_t *)malloc(sizeof(int32_t) * (size_t)(m * (P > 1 ? P - 1 : 1)));
     double *qw = (double *)malloc(sizeof(double) * (size_t)m);     /* query-side weight per feature */
@@ -529,10 +528,11 @@ int orc_bf16_state_decode(const float *q, const float *k, const float *v, double
     return state16_decode(q, k, v, out, bh, n0, n, dk, dv, P, round_mode ? 1 : 0, 0, window);
 }
 
-/* O8 with the fp16 state: features of the orders below low_orders stored in
- * binary32, the rest in binary16 (the same reading of the 16-bit storage
- * otherwise: exact prefix rounded once, exact adds, rounding on every store). */
+/* O8 with the fp16 state: the first low_features features (numbered order by
+ * order, so the lowest orders) stored in binary32, the rest in binary16 (the
+ * same reading of the 16-bit storage otherwise: exact prefix rounded once,
+ * exact adds, rounding on every store). */
 int orc_f16_state_decode(const float *q, const float *k, const float *v, double *out, int64_t bh, int64_t n0,
-                         int64_t n, int dk, int dv, int P, int low_orders, int window) {
-    return state16_decode(q, k, v, out, bh, n0, n, dk, dv, P, 2, low_orders, window);
+                         int64_t n, int dk, int dv, int P, int64_t low_features, int window) {
+    return state16_decode(q, k, v, out, bh, n0, n, dk, dv, P, 2, low_features, window);
 }

@@ -559,11 +559,12 @@ def test_f16_state_all_fp32_is_fp32_close(oracle, d, P, n0):
     assert np.max(np.abs(a - b)) <= 1e-5 * np.max(np.abs(b))
 
 
-def _state16_numpy(q, k, v, P, n0, low_orders, window):
+def _state16_numpy(q, k, v, P, n0, low_features, window):
     """Brute-force reading of the fp16 state with numpy's own roundings: tuples
     by itertools, exact (fp64) prefix sums stored rounded, each step adds its
     pending tokens exactly, reads out, and every window-th step stores rounded
-    (fp32 for orders below low_orders, fp16 above)."""
+    (fp32 for the first low_features features, numbered order by order, fp16
+    for the rest)."""
     import itertools
     n, d = q.shape[0], q.shape[1]
     dv = v.shape[1]
@@ -576,11 +577,12 @@ def _state16_numpy(q, k, v, P, n0, low_orders, window):
         alpha = np.prod([math.factorial(t.count(i)) for i in set(t)]) if t else 1
         return 1.0 / (alpha * d ** (p / 2))
 
-    def rnd(p, x):
-        return float(np.float32(x)) if p < low_orders else float(np.float16(x))
+    def rnd(i, x):
+        return float(np.float32(x)) if i < low_features else float(np.float16(x))
 
     vv = lambda s, c: float(v[s, c]) if c < dv else 1.0
-    S = [[rnd(p, sum(mono(k[s], t) * vv(s, c) for s in range(n0))) for c in range(dv + 1)] for p, t in feats]
+    S = [[rnd(i, sum(mono(k[s], t) * vv(s, c) for s in range(n0))) for c in range(dv + 1)]
+         for i, (p, t) in enumerate(feats)]
     out, first = [], n0
     for s in range(n0, n):
         store = s - first + 1 >= window
@@ -591,26 +593,30 @@ def _state16_numpy(q, k, v, P, n0, low_orders, window):
                 x = S[i][c] + sum(mono(k[u], t) * vv(u, c) for u in range(first, s + 1))
                 y[c] += mq * x
                 if store:
-                    S[i][c] = rnd(p, x)
+                    S[i][c] = rnd(i, x)
         if store:
             first = s + 1
         out.append(y[:dv] / y[dv])
     return np.array(out)
 
 
-@pytest.mark.parametrize("low_orders,window", [(0, 1), (1, 1), (2, 1), (2, 3)])
-def test_f16_state_matches_numpy_emulation(oracle, low_orders, window):
+@pytest.mark.parametrize("low_orders,low_features,window", [(0, 0, 1), (1, 1, 1), (2, 3, 1), (2, 3, 3), (None, 5, 1)])
+def test_f16_state_matches_numpy_emulation(oracle, low_orders, low_features, window):
     """O8 (fp16 with fp32 low orders) against the brute-force numpy reading on
-    a case whose sums fp16 cannot hold exactly (large v): equal to fp64
-    rounding; and the orders split differently give different results."""
-    rng = np.random.default_rng(21 + low_orders)
+    a case whose sums fp16 cannot hold exactly (large v), d = 2, P = 3 (1 + 2 + 3
+    features): the orders below low_orders, or the first low_features features
+    (5 cuts inside order 2), in fp32.  Equal to fp64 rounding; and another cut
+    gives a different result."""
+    rng = np.random.default_rng(21 + low_features)
     n, d, P, n0 = 14, 2, 3, 4
     q = rng.normal(size=(1, n, d)).astype(np.float32)
     k = rng.normal(size=(1, n, d)).astype(np.float32)
     v = (rng.normal(size=(1, n, 2)) * 300).astype(np.float32)
-    a = oracle.f16_state_decode(q, k, v, P, n0, low_orders=low_orders, window=window)[0]
-    b = _state16_numpy(q[0], k[0], v[0], P, n0, low_orders, window)
+    if low_orders is None:
+        a = oracle.f16_state_decode(q, k, v, P, n0, window=window, low_features=low_features)[0]
+    else:
+        a = oracle.f16_state_decode(q, k, v, P, n0, low_orders=low_orders, window=window)[0]
+    b = _state16_numpy(q[0], k[0], v[0], P, n0, low_features, window)
     assert np.max(np.abs(a - b)) <= 1e-9 * np.max(np.abs(b))
-    other = oracle.f16_state_decode(q, k, v, P, n0, low_orders=3 - low_orders if low_orders != 1 else 3,
-                                    window=window)[0]
+    other = oracle.f16_state_decode(q, k, v, P, n0, window=window, low_features=6 if low_features < 3 else 0)[0]
     assert np.max(np.abs(other - a)) > 1e-6 * np.max(np.abs(b))
