@@ -191,7 +191,7 @@ void decode_kernel(const uint32_t *__restrict__ tup, const float *__restrict__ c
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int64_t f0 = fbase + ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
-    const bool valid = f0 < m_pad;   // m_pad and fbase are multiples of 8 = FPT's largest value
+    const bool valid = f0 < m_pad;   // m_pad and fbase are multiples of 64
     TS *Sb = state + (int64_t)bh * NC * m_pad + f0;
     auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
 
@@ -274,7 +274,7 @@ void decode_rows_kernel(const uint32_t *__restrict__ tup, const float *__restric
     const int r0 = blockIdx.z * NR;
     const int nr = min(NR, NC - r0);                 // rows of this group (uniform)
     const int64_t f0 = fbase + ((int64_t)blockIdx.x * kDecThreads + tid) * FPT;
-    const bool valid = f0 < m_pad;                   // m_pad and fbase are multiples of 8
+    const bool valid = f0 < m_pad;                   // m_pad and fbase are multiples of 64
     TS *Sb = state + ((int64_t)bh * NC + r0) * m_pad + min<int64_t>(f0, m_pad - FPT);
     auto row = [&](int r) { return reinterpret_cast<typename Wd::T *>(Sb + (int64_t)r * m_pad); };
 
@@ -375,8 +375,8 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
     const int64_t fw = fbase + ((int64_t)blockIdx.x * (kFoldThreads / 64) + wave) * 64;   // the wavefront's first feature
     const bool active = fw < m_pad;
     // the lane's state word of feature group g (features fw + 16 g + 4 lg .. + 3) lies inside
-    // the rows: m_pad is a multiple of 64 and fbase of 8, so a wavefront's 64 features may run
-    // past m_pad when fbase > 0, a word never straddles it
+    // the rows (m_pad and fbase are multiples of 64, so a wavefront's words are all inside or
+    // all past the end; the check per word keeps that from being an assumption)
     auto wok = [&](int g) { return fw + 16 * g + 4 * lg < m_pad; };
     const uint32_t padt = (uint32_t)(dk + 1) * 0x01010101u;   // a tuple of monomial 0
     TS *Sb = state + (int64_t)bh * NC * m_pad;
@@ -527,7 +527,7 @@ void decode_fold_kernel(const uint32_t *__restrict__ tup, const float *__restric
     }
 }
 
-// fp16 states keep the features of orders 0 and 1 (f < m_low of every row, a multiple of 8)
+// fp16 states keep the features of orders 0 and 1 (f < m_low of every row, a multiple of 64)
 // in fp32 (sata_state::d_low); the main kernels start at feature m_low and leave them out.
 // This kernel, one workgroup per head on the same stream after the step's main kernel, adds
 // the tokens to fold in -- the npend deferred ones (pend_k / pend_v), then the step's own
@@ -545,9 +545,10 @@ __global__ __launch_bounds__(kLowThreads) void decode_low_kernel(
     const float *__restrict__ pend_v, int npend, float *__restrict__ partial, int nblk) {
     constexpr int NC = DV + 1;
     constexpr int KST = tok_stage<DV>();
-    // rows per thread: W <= 9 words (d_K <= 64, G >= 28) or 17 (d_K = 128, G = 15)
-    constexpr int RPT = DV > 64 ? 9 : 3;
-    constexpr int WMAX = DV > 64 ? 17 : 9;
+    // rows per thread: W <= 16 words (d_K <= 64, m_low <= 128, G >= 16) or 24 (d_K = 128,
+    // m_low = 192, G = 10)
+    constexpr int RPT = DV > 64 ? 13 : 5;
+    constexpr int WMAX = DV > 64 ? 24 : 16;
     __shared__ float sk[kLowStage][KST], sv[kLowStage][NC], sq[KST];
     __shared__ float red[NC * WMAX];
     const int bh = blockIdx.x, tid = threadIdx.x;

@@ -53,9 +53,9 @@ bool valid_dtype(int t) { return t == SATA_F32 || t == SATA_BF16; }             
 bool valid_state_dtype(int t) { return t == SATA_F32 || t == SATA_BF16 || t == SATA_F16; }
 
 // An fp16 state keeps the features of orders 0 and 1 (the constant and the d_K linear ones,
-// which grow with every token) in fp32: the first 1 + d_K features, rounded up to whole
-// 8-feature words (all of them when P = 1).
-int64_t f16_low_features(const sata_index *idx) { return std::min<int64_t>(round_up(1 + idx->dk, 8), idx->m_pad); }
+// which grow with every token) in fp32: the first 1 + d_K features, rounded up to 64 (all of
+// them when P = 1), so that the fp16 words the decode kernels start from are 128-byte aligned.
+int64_t f16_low_features(const sata_index *idx) { return std::min<int64_t>(round_up(1 + idx->dk, 64), idx->m_pad); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -175,6 +175,7 @@ sata_status take_state_error(sata_state *st) {
 
 std::atomic<int> g_debug_item_base{0};
 std::atomic<int> g_debug_spin_limit{sata::kScanSpinLimit};
+std::atomic<int> g_debug_positions{0};
 
 }  // namespace
 
@@ -184,6 +185,7 @@ ScanDebug scan_debug() {
     ScanDebug d;
     d.item_base = g_debug_item_base.load(std::memory_order_relaxed);
     d.spin_limit = g_debug_spin_limit.load(std::memory_order_relaxed);
+    d.positions = g_debug_positions.load(std::memory_order_relaxed);
     return d;
 }
 }
@@ -906,6 +908,14 @@ sata_status sata_debug_scan_faults(int item_base, int spin_limit) {
     if (spin_limit < 0) return fail(SATA_ERR_INVALID, "spin_limit must be >= 0 (got %d)", spin_limit);
     g_debug_item_base.store(item_base, std::memory_order_relaxed);
     g_debug_spin_limit.store(spin_limit ? spin_limit : sata::kScanSpinLimit, std::memory_order_relaxed);
+    return SATA_OK;
+}
+
+sata_status sata_debug_prefill_positions(int mt) {
+    g_last_error.clear();
+    if (mt != 0 && mt != 1 && mt != 2 && mt != 3 && mt != 5)
+        return fail(SATA_ERR_INVALID, "positions per update wavefront must be 0, 1, 2, 3 or 5 (got %d)", mt);
+    g_debug_positions.store(mt, std::memory_order_relaxed);
     return SATA_OK;
 }
 

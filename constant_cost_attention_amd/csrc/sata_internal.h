@@ -59,7 +59,7 @@ struct sata_state {
     sata_dtype dtype = SATA_F32; // element type of the state
     void *d_state = nullptr;     // [B*H][d_V+1][m_pad] of dtype
     int64_t state_bytes = 0;
-    // SATA_F16 states: features f < m_low (the lowest orders, a multiple of 8) are held in
+    // SATA_F16 states: features f < m_low (the lowest orders, a multiple of 64) are held in
     // fp32 at d_low [B*H][d_V+1][m_low], right after the fp16 array (whose slots for them
     // stay zero); 0 and NULL for the other types
     int64_t m_low = 0;
@@ -203,6 +203,7 @@ constexpr int kScanSpinLimit = 1 << 24;
 // scans start taking work items at item_base instead of 0 (so the items before it never run
 // and their successors' waits time out), and give up after spin_limit polls.
 struct ScanDebug {
+    int positions = 0;   // forced positions per update wavefront of the fp16-operand scan (0: the rule)
     int item_base = 0;
     int spin_limit = kScanSpinLimit;
 };

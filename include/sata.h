@@ -117,14 +117,14 @@ sata_status sata_state_alloc(const sata_index *idx, int batch, int heads, void *
  * SATA_F16 [hotdry, "Hardware optimisation paths and current limits": Float16
  * storage is enough at P = 4 and halves the state's bandwidth]: the same layout
  * in binary16, except that the features of orders 0 and 1 -- the first
- * m_low = min(round_up(1 + d_K, 8), m_pad) features of each row, whose sums
+ * m_low = min(round_up(1 + d_K, 64), m_pad) features of each row, whose sums
  * grow with every token (the token count, the sums of k) and would stop
  * growing in 16 bits -- live in an fp32 array [batch][heads][d_V + 1][m_low]
  * that follows the binary16 one in the allocation (whose slots for them stay
  * zero).  Each decode step widens the stored values to fp32, adds the token's
  * term, reads out from the fp32 sums and stores them rounded to the nearest
  * binary16 (ties to even); the state holds 2 (d_V+1)(m_pad + 2 m_low) bytes
- * per head, 50.2% of the fp32 state at d_K = 64, P = 4.  At P = 4 the outputs
+ * per head, 50.3% of the fp32 state at d_K = 64, P = 4.  At P = 4 the outputs
  * stay within 2e-2 of the exact Taylor attention for at least 1024 decode
  * steps after a conversion (measured: 6e-4 at d_K = 64, 2.2e-3 at d_K = 16).
  * Values must stay inside binary16's range (|S| < 65504 for the orders >= 2,
@@ -209,8 +209,9 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
  * q, k: [batch][heads][n][d_K]; v, out: [batch][heads][n][d_V]; in_dt is the
  * dtype of q, k, v; out_dt that of out.  Token i attends to every earlier
  * token and to itself.  The sequence is processed in chunks of `chunk` tokens
- * (0 = default, 128 for d_K = 64 and 64 otherwise; supported: 64, 128; at
- * d_K = 128 the chunk is always 64 tokens):
+ * (0 = default: 128 for bf16 inputs with P <= 4 and d_K = d_V in {16, 32,
+ * 64}, and for d_K = 64; 64 otherwise; supported: 64, 128; at d_K = 128 the
+ * chunk is always 64 tokens):
  * within a chunk the Taylor weights are formed directly, across chunks the
  * orders' states are scanned and read out [hotdry, "Engineering realisation
  * of the constant compute cost"]; results do not depend on the chunk length
@@ -350,6 +351,15 @@ int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t 
  * waits and skipped items go unreported.  Negative arguments return
  * SATA_ERR_INVALID.  Not for production use. */
 sata_status sata_debug_scan_faults(int item_base, int spin_limit);
+
+/* Tile choice for measurement (process-wide, affects every later plan until
+ * reset with 0): the fp16-operand prefill scan holds mt positions (64 features
+ * each) of the state per update wavefront instead of the library's rule.
+ * mt must be 0 (the rule), 1, or the largest the head size holds (5, 3, 2, 1
+ * at d_K = 16, 32, 64, 128), else SATA_ERR_INVALID; a value the head size
+ * does not hold leaves the rule in force for that size.  The chunk length is
+ * sata_prefill's argument.  Not for production use. */
+sata_status sata_debug_prefill_positions(int mt);
 
 /* Kernel timing instrumentation.  While enabled, every launch of the
  * library's kernels is bracketed by a HIP event pair recorded on the stream

@@ -26,7 +26,9 @@ pytestmark = pytest.mark.gpu
 
 TOL_F16_STATE = 2e-4
 DRIFT_SHARE = 1e-2
-LOW_ORDERS = 2          # orders 0 and 1 stay in fp32
+def _m_low(sata, st):
+    """The state's fp32 features (orders 0 and 1, rounded up to 64)."""
+    return sata.state_low_tensor(st).shape[-1]
 
 
 @pytest.fixture(scope="module")
@@ -68,7 +70,7 @@ def test_f16_convert_keeps_low_orders_in_fp32(sata, d, P):
     main = sata.state_tensor(st16).clone()
     low = sata.state_low_tensor(st16).clone()
     m_low = low.shape[-1]
-    assert m_low == min(-(-(1 + d) // 8) * 8, idx.m_pad)
+    assert m_low == min(-(-(1 + d) // 64) * 64, idx.m_pad)
     assert torch.equal(low, s32[..., :m_low])
     assert torch.all(main[..., :m_low] == 0)
     assert torch.equal(main[..., m_low:].view(torch.int16), s32[..., m_low:].to(torch.float16).view(torch.int16))
@@ -97,7 +99,7 @@ def test_f16_state_decode_matches_emulation(sata, oracle, d, P, n0, T, heads):
     _, st = _f16_state_from_prefill(sata, idx, 1, heads, q[:, :, :n0].contiguous(), k[:, :, :n0].contiguous(),
                                     v[:, :, :n0].contiguous())
     o = _steps(idx, st, q, k, v, n0, n0 + T)
-    ref = oracle.f16_state_decode(x.q, x.k, x.v, P, n0, low_orders=LOW_ORDERS)
+    ref = oracle.f16_state_decode(x.q, x.k, x.v, P, n0, low_features=_m_low(sata, st))
     exact = oracle.taylor_attention(x.q, x.k, x.v, P)[:, :, n0:]
     err, drift, err_exact = rel_err(o, ref), rel_err(ref, exact), rel_err(o, exact)
     say("  err vs emulation %.3e, drift %.3e, err vs exact %.3e" % (err, drift, err_exact))
@@ -124,7 +126,8 @@ def test_f16_state_whole_tile_grid(sata, oracle, window):
     o = _steps(idx, st, q, k, v, n0, n0 + T)
     for b, h in ((0, 0), (B - 1, H - 1)):
         sub = lambda a: np.ascontiguousarray(a[b:b + 1, h:h + 1])
-        ref = oracle.f16_state_decode(sub(x.q), sub(x.k), sub(x.v), P, n0, low_orders=LOW_ORDERS, window=window)
+        ref = oracle.f16_state_decode(sub(x.q), sub(x.k), sub(x.v), P, n0, window=window,
+                                      low_features=_m_low(sata, st))
         exact = oracle.taylor_attention(sub(x.q), sub(x.k), sub(x.v), P)[:, :, n0:]
         err, drift = rel_err(o[b:b + 1, h:h + 1], ref), rel_err(ref, exact)
         say("  head (%d, %d): err vs emulation %.3e, drift %.3e" % (b, h, err, drift))
@@ -148,7 +151,7 @@ def test_f16_state_window_and_flush(sata, oracle):
     sata.sata_state_set_decode_window(st, 4)
     o = _steps(idx, st, q, k, v, n0, n0 + 12)
     ref = oracle.f16_state_decode(x.q[:, :, :n0 + 12], x.k[:, :, :n0 + 12], x.v[:, :, :n0 + 12], P, n0,
-                                  low_orders=LOW_ORDERS, window=4)
+                                  window=4, low_features=_m_low(sata, st))
     exact = oracle.taylor_attention(x.q, x.k, x.v, P)
     err, drift = rel_err(o, ref), rel_err(ref, exact[:, :, n0:n0 + 12])
     say("  window: err vs emulation %.3e, drift %.3e" % (err, drift))
@@ -177,7 +180,7 @@ def test_f16_state_d128(sata, oracle):
     _, st = _f16_state_from_prefill(sata, idx, 1, heads, q[:, :, :n0].contiguous(), k[:, :, :n0].contiguous(),
                                     v[:, :, :n0].contiguous())
     o = _steps(idx, st, q, k, v, n0, n0 + T)
-    ref = oracle.f16_state_decode(x.q, x.k, x.v, P, n0, low_orders=LOW_ORDERS)
+    ref = oracle.f16_state_decode(x.q, x.k, x.v, P, n0, low_features=_m_low(sata, st))
     exact = oracle.taylor_attention(x.q, x.k, x.v, P)[:, :, n0:]
     err, drift = rel_err(o, ref), rel_err(ref, exact)
     say("  err vs emulation %.3e, drift %.3e" % (err, drift))
