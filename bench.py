@@ -62,6 +62,8 @@ def parse_args():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="only: time every (chunk, positions per update wavefront) of the bf16 prefill workloads")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--traffic-run", action="store_true",
                     help="one launch of each timed kernel plus a 1 GiB copy, for rocprofv3 --pmc runs")
@@ -109,8 +111,8 @@ def decode_read_bytes(wl, state_elem: int = 4) -> float:
 
 
 def f16_low_features(wl) -> int:
-    """Features an fp16 state keeps in fp32: orders 0 and 1, rounded up to 8."""
-    return min(-(-(1 + wl.d_k) // 8) * 8, features(wl.d_k, wl.P))
+    """Features an fp16 state keeps in fp32: orders 0 and 1, rounded up to 64."""
+    return min(-(-(1 + wl.d_k) // 64) * 64, features(wl.d_k, wl.P))
 
 
 def decode_bytes_f16_main(wl) -> float:
@@ -295,6 +297,34 @@ def stream_ceiling(nbytes: float, reps: int = 10):
     out["method"] = ("reference rates (not upper bounds) of torch in-place mul_ and row sums of 4096 over a "
                      "%.2f GB fp32 tensor" % (nbytes / 1e9))
     return out
+
+
+TILE_SWEEP = (("prefill_d64_p4_bf16", (64, 128), 2), ("prefill_d32_p4_bf16", (64, 128), 3),
+              ("prefill_d16x64h_p4_bf16", (64, 128), 5), ("prefill_d128_p4_bf16", (64,), 1))
+
+
+def tile_sweep(sata):
+    """Whole-call ms of the fp16-operand scan's prefill for each chunk length and
+    positions per update wavefront (the rule's choice and the other), per workload."""
+    import dataclasses
+    import torch
+    import synth_inputs as si
+    rows = []
+    for name, chunks, mx in TILE_SWEEP:
+        wl = si.WORKLOADS[name]
+        q, k, v = si.draw_qkv_device((wl.batch, wl.heads), wl.n, wl.d_k, wl.d_v, wl.seed, wl.dtype)
+        for c in chunks:
+            for mt in sorted({1, mx}):
+                sata.sata_debug_prefill_positions(mt)
+                r = time_prefill(sata, dataclasses.replace(wl, chunk=c), q, k, v, 3, 1)
+                rows.append({"workload": name, "chunk": c, "positions": mt, "ms_per_call": r["ms_per_step"],
+                             "scan_ms": r["roofline"]["avg_launch_ms"]})
+                log("tile sweep %s chunk %d positions %d: %.3f ms per call (scan %.3f)"
+                    % (name, c, mt, r["ms_per_step"], r["roofline"]["avg_launch_ms"]))
+        sata.sata_debug_prefill_positions(0)
+        del q, k, v
+        torch.cuda.empty_cache()
+    return rows
 
 
 def decode_section(sata, wl, steps: int, warmup: int, flatness: bool):
@@ -829,6 +859,9 @@ def main():
     from constant_cost_attention_amd import sata
     sata.load()
     torch.cuda.set_device(0)
+    if args.tile_sweep:
+        print(json.dumps({"tile_sweep": tile_sweep(sata)}))
+        return
 
     wl = si.WORKLOADS["prefill_d64_p4_bf16"]
     log("drawing %s inputs" % wl.name)

@@ -1738,9 +1738,11 @@ bool scan16_covers(const sata_index *idx, sata_dtype in_dt) {
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt, int64_t work_cap,
                          bool fp16_operands) {
     PrefillPlan p;
-    p.chunk = chunk ? chunk : (idx->dk == 64 ? 128 : 64);
-    if (p.chunk != 64 && p.chunk != 128) return p;
     const bool s16 = fp16_operands && scan16_covers(idx, in_dt);
+    // default chunk: 128 tokens for the fp16-operand scan (measured faster than 64 at every
+    // head size it takes up to 64, by 18-26%) and for d_K = 64; 64 for the other scans
+    p.chunk = chunk ? chunk : (s16 || idx->dk == 64 ? 128 : 64);
+    if (p.chunk != 64 && p.chunk != 128) return p;
     if (idx->dk == 128) {
         if (!s16) return p;   // no chunked plan: the block prefill covers it
         p.chunk = 64;         // the operand image of a 128-token chunk does not fit beside the state copy

@@ -881,6 +881,8 @@ constexpr int scan16_mt_max(int dk) { return dk == 128 ? 1 : dk == 64 ? 2 : dk =
 
 int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus) {
     const int big = scan16_mt_max(dk);
+    const int forced = scan_debug().positions;   // a measurement's choice
+    if (forced == 1 || forced == big) return forced;
     const int64_t slices = (np16 + 4 * big - 1) / (4 * big);
     return bh * slices >= cus ? big : 1;
 }

@@ -220,3 +220,23 @@ def test_prefill_plan_head_size_128():
     assert p64["seg_chunks"] == 4096 // 64
     # partials (fp16) of every slice of every chunk fit the default workspace
     assert 8 * p64["slices"] * 4096 * 129 * 2 <= p64["work_bytes"] <= 16 << 30
+
+
+def test_forced_positions_change_the_plan():
+    """sata_debug_prefill_positions: one position per update wavefront at d_K = 64
+    doubles the slices of the rule's two; values other than 0, 1, 2, 3, 5 are
+    refused; 0 restores the rule."""
+    from constant_cost_attention_amd import sata
+    rule = sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16)["slices"]
+    try:
+        sata.sata_debug_prefill_positions(1)
+        one = sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16)["slices"]
+        sata.sata_debug_prefill_positions(5)   # not held at d_K = 64: the rule applies
+        five = sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16)["slices"]
+        for bad in (-1, 4, 6):
+            with pytest.raises(sata.SataError):
+                sata.sata_debug_prefill_positions(bad)
+    finally:
+        sata.sata_debug_prefill_positions(0)
+    assert one in (2 * rule - 1, 2 * rule) and five == rule
+    assert sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16)["slices"] == rule
