@@ -1000,14 +1000,15 @@ hipError_t launch_decode(const sata_index *idx, const sata_state *st, const void
     }
 }
 
-// ---- Prefill in blocks through the state in HBM (head sizes the scan kernels do not take) ----
+// ---- Prefill in blocks through the state in HBM (shapes the scan kernels do not take) ----
 // A sequence runs in blocks of up to kMaxDecodeWindow tokens.  The block's queries are read
-// out against the state as it stands before the block (one pass over the state for all of
-// them), each query adds the direct Taylor-weighted terms w(q.k_j / sqrt(d_K)) [v_j, 1] of the
-// block's tokens up to itself -- what those tokens contribute through the state's orders
-// [hotdry, "Core insight of symmetric tensor decomposition"] -- and the fold then adds the
-// block's tokens to the state.  Per block the state crosses HBM three times (a read, then the
-// fold's read and write), so this path is bound by HBM; it serves d_K = 128.
+// out against the state as it stands before the block, each query adds the direct
+// Taylor-weighted terms w(q.k_j / sqrt(d_K)) [v_j, 1] of the block's tokens up to itself --
+// what those tokens contribute through the state's orders [hotdry, "Core insight of
+// symmetric tensor decomposition"] -- and the fold then adds the block's tokens to the
+// state.  The readout runs inside the fold on the state words as loaded, so per block the
+// state crosses HBM twice (one read, one write) and the path is bound by HBM; it serves
+// d_K = 128 for fp32 inputs and five orders.
 
 // fp32 copies of a block's rows: q into qs, k and v into the pending-token buffers, each laid
 // out [bh][kMaxDecodeWindow][d] as the fold reads them.  Grid (T, B*H).
