@@ -726,13 +726,14 @@ def cpu_baseline(wl, x, budget_s: float):
 COPY_BYTES = 1 << 30
 # kernel-name pattern -> (kernel, workload, source file)
 TRAFFIC_KERNELS = [
-    # the fp16-operand scan (its names stay mangled in rocprofv3 output): D, C, positions per wave
+    # the fp16-operand scan and the fp16-state decode (their names stay mangled in rocprofv3
+    # output): D, C, positions per wave; head size, state type, storage type
     (r"scan16_kernelILi64ELi128ELi2E", "prefill_scan", "prefill_d64_p4_bf16", "sata_scan16.hip"),
     (r"scan16_kernelILi32ELi64ELi3E", "prefill_scan", "prefill_d32_p4_bf16", "sata_scan16.hip"),
     (r"scan16_kernelILi16ELi128ELi1E", "prefill_scan", "prefill_d16x64h_p4_bf16", "sata_scan16.hip"),
     (r"decode_kernel<64, float, float>", "decode_stream", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_rows_kernel<64, float, unsigned short, true>", "decode_stream_bf16", "decode_d64_p4_f32", "sata_decode.hip"),
-    (r"decode_rows_kernel<64, float, _Float16, true>", "decode_stream_f16", "decode_d64_p4_f32", "sata_decode.hip"),
+    (r"decode_rows_kernelILi64EfDF16_Lb1E", "decode_stream_f16", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_read_kernel<64, float, float>", "decode_read", "decode_d64_p4_f32", "sata_decode.hip"),
     (r"decode_fold_kernel<64, float, float, 3, false>", "decode_fold", "decode_d64_p4_f32", "sata_decode.hip"),
 ]
