@@ -63,28 +63,61 @@ __global__ __launch_bounds__(kBwThreads) void bw_reverse(const T *__restrict__ i
     }
 }
 
-// values of the dv pass: out[h][t][d] = g[h][n-1-t][d], d < D.
+// Largest |g| of the call into *bits (the bit pattern of a non-negative float, which orders like
+// an unsigned integer; *bits starts at 0).
+__global__ __launch_bounds__(kBwThreads) void bw_absmax(const float *__restrict__ g, int64_t total,
+                                                        unsigned *__restrict__ bits) {
+    __shared__ unsigned part[kBwThreads / 64];
+    unsigned m = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads)
+        m = max(m, __float_as_uint(fabsf(g[i])));
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kBwThreads / 64; ++w) m = max(m, part[w]);
+        atomicMax(bits, m);
+    }
+}
+
+// The power of two that the gradient-weighted values of the dv and dk passes are multiplied by
+// before they are rounded to the input type: it brings the largest |g| into [2^8, 2^9), so that
+// the fp16 operands of the fp16-operand scan hold them in their normal range (g = dout / z
+// shrinks with the token count).  Scaling by a power of two commutes with every rounding of the
+// passes; the results are multiplied back by the inverse.  1 when g is zero or not finite.
+constexpr int kBwValueExp = 9;
+__device__ __forceinline__ float bw_value_scale(const unsigned *bits, bool inverse) {
+    const float m = __uint_as_float(*bits);
+    if (!(m > 0.f) || !(m < INFINITY)) return 1.f;
+    const int e = __builtin_amdgcn_frexp_expf(m);   // m in [2^(e-1), 2^e)
+    return __builtin_amdgcn_ldexpf(1.f, inverse ? e - kBwValueExp : kBwValueExp - e);
+}
+
+// values of the dv pass: out[h][t][d] = g[h][n-1-t][d] (scaled), d < D.
 template <typename TIn>
-__global__ __launch_bounds__(kBwThreads) void bw_rev_g(const float *__restrict__ g, TIn *__restrict__ out, int64_t heads,
-                                                       int64_t n, int D) {
+__global__ __launch_bounds__(kBwThreads) void bw_rev_g(const float *__restrict__ g, const unsigned *__restrict__ gmax,
+                                                       TIn *__restrict__ out, int64_t heads, int64_t n, int D) {
     const int64_t total = heads * n * D;
+    const float vs = bw_value_scale(gmax, false);
     for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
         const int64_t d = i % D, t = (i / D) % n, h = i / (D * n);
-        out[i] = from_f32<TIn>(g[(h * n + (n - 1 - t)) * (D + 1) + d]);
+        out[i] = from_f32<TIn>(g[(h * n + (n - 1 - t)) * (D + 1) + d] * vs);
     }
 }
 
 // Inputs of one column group [c0, c0 + cg) of the dk pass (kdk = 1) or the dq
 // pass (kdk = 0), pseudo-head ph = h * cg + cc for column c = c0 + cc:
-//   dk: q' = rev(k), k' = rev(q), v'[t] = g[n-1-t][c] q[n-1-t]
+//   dk: q' = rev(k), k' = rev(q), v'[t] = g[n-1-t][c] q[n-1-t] (scaled)
 //   dq: q' = q,      k' = k,      v'[t] = [v, 1][t][c] k[t]
 template <typename TIn>
 __global__ __launch_bounds__(kBwThreads) void bw_group_inputs(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                               const TIn *__restrict__ v, const float *__restrict__ g,
+                                                              const unsigned *__restrict__ gmax,
                                                               TIn *__restrict__ qo, TIn *__restrict__ ko,
                                                               TIn *__restrict__ vo, int64_t heads, int64_t n, int D,
                                                               int c0, int cg, int kdk) {
     const int64_t total = heads * cg * n * D;
+    const float vs = bw_value_scale(gmax, false);
     for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
         const int64_t d = i % D, t = (i / D) % n, ph = i / (D * n);
         const int64_t h = ph / cg;
@@ -94,7 +127,7 @@ __global__ __launch_bounds__(kBwThreads) void bw_group_inputs(const TIn *__restr
         if (kdk) {
             qo[i] = k[src];
             ko[i] = q[src];
-            vo[i] = from_f32<TIn>(g[(h * n + ts) * (D + 1) + c] * to_f32(q[src]));
+            vo[i] = from_f32<TIn>(g[(h * n + ts) * (D + 1) + c] * vs * to_f32(q[src]));
         } else {
             qo[i] = q[src];
             ko[i] = k[src];
@@ -105,14 +138,15 @@ __global__ __launch_bounds__(kBwThreads) void bw_group_inputs(const TIn *__restr
 }
 
 // Contraction over a column group into the fp32 accumulator acc[h][t][d]:
-//   dk (kdk = 1): acc[h][j] += s sum_cc [v, 1][j][c] r[h*cg+cc][n-1-j]
+//   dk (kdk = 1): acc[h][j] += s sum_cc [v, 1][j][c] r[h*cg+cc][n-1-j]   (r unscaled here)
 //   dq (kdk = 0): acc[h][i] += s sum_cc g[i][c] r[h*cg+cc][i]
 template <typename TIn>
 __global__ __launch_bounds__(kBwThreads) void bw_contract(const float *__restrict__ r, const TIn *__restrict__ v,
-                                                          const float *__restrict__ g, float *__restrict__ acc,
-                                                          int64_t heads, int64_t n, int D, int c0, int cg, int kdk,
-                                                          float s) {
+                                                          const float *__restrict__ g, const unsigned *__restrict__ gmax,
+                                                          float *__restrict__ acc, int64_t heads, int64_t n, int D,
+                                                          int c0, int cg, int kdk, float s) {
     const int64_t total = heads * n * D;
+    if (kdk) s *= bw_value_scale(gmax, true);
     for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
         const int64_t d = i % D, t = (i / D) % n, h = i / (D * n);
         const int64_t tr = kdk ? n - 1 - t : t;                 // row of the pass's output
@@ -126,14 +160,15 @@ __global__ __launch_bounds__(kBwThreads) void bw_contract(const float *__restric
     }
 }
 
-// dv[h][j] = r[h][n-1-j] (the dv pass ran on reversed time).
+// dv[h][j] = r[h][n-1-j] (the dv pass ran on reversed time, on scaled values).
 template <typename TOut>
-__global__ __launch_bounds__(kBwThreads) void bw_finish_dv(const float *__restrict__ r, TOut *__restrict__ dv,
-                                                           int64_t heads, int64_t n, int D) {
+__global__ __launch_bounds__(kBwThreads) void bw_finish_dv(const float *__restrict__ r, const unsigned *__restrict__ gmax,
+                                                           TOut *__restrict__ dv, int64_t heads, int64_t n, int D) {
     const int64_t total = heads * n * D;
+    const float inv = bw_value_scale(gmax, true);
     for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
         const int64_t d = i % D, t = (i / D) % n, h = i / (D * n);
-        dv[i] = from_f32<TOut>(r[(h * n + (n - 1 - t)) * D + d]);
+        dv[i] = from_f32<TOut>(r[(h * n + (n - 1 - t)) * D + d] * inv);
     }
 }
 
@@ -167,7 +202,7 @@ struct TempState {
     int64_t max_heads = 0;
     hipError_t make(Arena &ar, const sata_index *idx, int64_t heads, int64_t n, int chunk, sata_dtype in_dt,
                     uint32_t *err) {
-        const PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt, kWorkCap, false);
+        const PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt, kWorkCap, scan16_covers(idx, in_dt));
         if (!plan.ok) return hipErrorInvalidValue;
         st.d_err = err;
         st.idx = idx;
@@ -186,13 +221,14 @@ struct TempState {
 hipError_t run_pass(TempState &ts, int64_t heads, const void *q, const void *k, const void *v, float *out, float *den,
                     int64_t n, int chunk, sata_dtype in_dt, bool raw, hipStream_t s) {
     const sata_index *idx = ts.st.idx;
-    // The passes' inputs are weighted by the gradient (g = dout / z, small for long sequences),
-    // below fp16's normal range: they plan without the fp16-operand scan.
-    PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt, kWorkCap, false);
+    // bf16 inputs run on the fp16-operand scan where it covers the index (the gradient-weighted
+    // values arrive scaled into fp16's normal range), like the forward prefill
+    const bool s16 = scan16_covers(idx, in_dt);
+    PrefillPlan plan = plan_prefill(idx, heads, n, chunk, in_dt, kWorkCap, s16);
     // fewer heads than the state was made for can fit more chunks under the default cap than
     // its workspace holds: plan again under the workspace it has (shorter segments)
     if (plan.ok && plan.work_bytes > ts.st.work_bytes)
-        plan = plan_prefill(idx, heads, n, chunk, in_dt, ts.st.work_bytes, false);
+        plan = plan_prefill(idx, heads, n, chunk, in_dt, ts.st.work_bytes, s16);
     if (!plan.ok || heads > ts.max_heads || plan.work_bytes > ts.st.work_bytes) return hipErrorInvalidValue;
     plan.raw = raw;
     plan.den_out = den;
@@ -219,10 +255,12 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     float *r = ar.get<float>(elems);
     TIn *rq = ar.get<TIn>(elems), *rk = ar.get<TIn>(elems), *rg = ar.get<TIn>(elems);
     if (ar.err != hipSuccess) return ar.err;
-    // error word of every pass's scan (a timed-out wait for a predecessor item), read back at the end
-    uint32_t *err = ar.get<uint32_t>(1);
+    // error word of every pass's scan (a timed-out wait for a predecessor item), read back at the
+    // end, and the largest |g| (bits of a float)
+    uint32_t *err = ar.get<uint32_t>(2);
     if (ar.err != hipSuccess) return ar.err;
-    hipError_t e = launch_zero(reinterpret_cast<float *>(err), 1, s);
+    uint32_t *gmax = err + 1;
+    hipError_t e = launch_zero(reinterpret_cast<float *>(err), 2, s);
     if (e != hipSuccess) return e;
     TempState top;
     t_bw_step = "state of the P-order passes";
@@ -233,16 +271,18 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     t_bw_step = "inputs of the dv pass";
     hipLaunchKernelGGL(bw_prep_g<TIn>, dim3(bw_grid(bh * n)), dim3(kBwThreads), 0, s,
                        static_cast<const TIn *>(doutv), o, z, g, bh * n, D);
+    hipLaunchKernelGGL(bw_absmax, dim3(std::min<unsigned>(bw_grid(bh * n * (D + 1)), 4096)), dim3(kBwThreads), 0, s, g,
+                       bh * n * (D + 1), gmax);
     // 2. dv: reversed time, queries k, keys q, values g[:d_V], P orders
     hipLaunchKernelGGL(bw_reverse<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, k, rq, bh, n, D);
     hipLaunchKernelGGL(bw_reverse<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, q, rk, bh, n, D);
-    hipLaunchKernelGGL(bw_rev_g<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, g, rg, bh, n, D);
+    hipLaunchKernelGGL(bw_rev_g<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, g, gmax, rg, bh, n, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     t_bw_step = "dv pass";
     if ((e = run_pass(top, bh, rq, rk, rg, r, nullptr, n, chunk, in_dt, true, s)) != hipSuccess) return e;
     t_bw_step = "dk and dq accumulators";
-    hipLaunchKernelGGL(bw_finish_dv<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, r, static_cast<TOut *>(dvv),
-                       bh, n, D);
+    hipLaunchKernelGGL(bw_finish_dv<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, r, gmax,
+                       static_cast<TOut *>(dvv), bh, n, D);
     // 3. dk and dq: P - 1 orders, one pseudo-head per column c in groups of cg
     float *acc_k = ar.get<float>(elems), *acc_q = ar.get<float>(elems);
     if (ar.err != hipSuccess) return ar.err;
@@ -266,13 +306,13 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
                 const int n_c = std::min(cg, D + 1 - c0);
                 t_bw_step = kdk ? "inputs of a dk pass" : "inputs of a dq pass";
                 hipLaunchKernelGGL(bw_group_inputs<TIn>, dim3(bw_grid(elems * n_c)), dim3(kBwThreads), 0, s, q, k, v,
-                                   g, gq, gk, gv, bh, n, D, c0, n_c, kdk);
+                                   g, gmax, gq, gk, gv, bh, n, D, c0, n_c, kdk);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 t_bw_step = kdk ? "dk pass" : "dq pass";
                 if ((e = run_pass(low, bh * n_c, gq, gk, gv, gr, nullptr, n, chunk, in_dt, true, s)) != hipSuccess)
                     return e;
                 t_bw_step = "contraction";
-                hipLaunchKernelGGL(bw_contract<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, gr, v, g,
+                hipLaunchKernelGGL(bw_contract<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, gr, v, g, gmax,
                                    kdk ? acc_k : acc_q, bh, n, D, c0, n_c, kdk, sc);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }

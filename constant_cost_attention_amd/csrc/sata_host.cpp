@@ -323,8 +323,13 @@ static void build_tables(int d_k, int P, std::vector<uint32_t> &tup, std::vector
 // prefixes.  Word w0: i1 | i2 << 8 | i0 << 16 | b << 24 | slot mask << 28; with
 // block_byte (views without three-index prefixes, P <= 4) b takes the i0 byte
 // instead: i1 | i2 << 8 | b << 16 | slot mask << 28, for d up to 1020.
+// pool: a group takes `streams` consecutive prefixes of the whole list instead
+// of those of one block a, and sweeps the blocks from that of its first prefix;
+// a prefix whose i2 lies above a block has no valid slot there.  With P = 3
+// there are only four prefixes per block a (five for a = 0), so a group of 16
+// per block would be three quarters padding.
 static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags,
-                        size_t streams = 4, bool block_byte = false) {
+                        size_t streams = 4, bool block_byte = false, bool pool = false) {
     std::map<std::vector<int>, int32_t> index;   // sorted tuple -> feature index
     {
         int32_t f = 0;
@@ -366,7 +371,8 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
         if (mask != 0xfu || q.coef[0] != q.coef[1] || q.coef[0] != q.coef[2] || q.coef[0] != q.coef[3]) nonuni = 1;
         return q;
     };
-    for (int a = 0; a < d / 4; ++a) {
+    // the prefixes whose last index lies in block a
+    auto block_prefixes = [&](int a) {
         std::vector<Prefix> prefixes;
         if (P >= 2 && a == 0) prefixes.push_back({none, none, none});
         for (int i2 = 4 * a; i2 < 4 * a + 4; ++i2) {
@@ -377,17 +383,40 @@ static void build_quads(int d, int P, std::vector<sata::QuadRec> &out, std::vect
                 for (int i1 = 0; i1 <= i2; ++i1) prefixes.push_back({none, i1, i2});
             if (P >= 3) prefixes.push_back({none, none, i2});
         }
-        for (size_t g = 0; g < prefixes.size(); g += streams) {
-            for (int b = a; b < d / 4; ++b) {
-                uint32_t nonuni = 0;
-                for (size_t s = 0; s < streams; ++s) {
-                    const bool have = g + s < prefixes.size();
-                    out.push_back(make(have ? prefixes[g + s] : Prefix{none, pad, pad}, b, nonuni));
-                }
-                flags.push_back(nonuni | (b == a ? 2u : 0u));
+        return prefixes;
+    };
+    // groups of up to `streams` prefixes, each sweeping the blocks a0 .. d/4-1
+    auto emit = [&](const std::vector<Prefix> &prefixes, size_t g, int a0) {
+        for (int b = a0; b < d / 4; ++b) {
+            uint32_t nonuni = 0;
+            for (size_t s = 0; s < streams; ++s) {
+                const bool have = g + s < prefixes.size();
+                out.push_back(make(have ? prefixes[g + s] : Prefix{none, pad, pad}, b, nonuni));
             }
+            flags.push_back(nonuni | (b == a0 ? 2u : 0u));
         }
+    };
+    if (pool) {
+        std::vector<Prefix> all;
+        std::vector<int> blk;   // block of each prefix's last index (0 for the empty prefix)
+        for (int a = 0; a < d / 4; ++a)
+            for (const Prefix &x : block_prefixes(a)) {
+                all.push_back(x);
+                blk.push_back(a);
+            }
+        for (size_t g = 0; g < all.size(); g += streams) emit(all, g, blk[g]);
+        return;
     }
+    for (int a = 0; a < d / 4; ++a) {
+        const std::vector<Prefix> prefixes = block_prefixes(a);
+        for (size_t g = 0; g < prefixes.size(); g += streams) emit(prefixes, g, a);
+    }
+}
+
+// The 16-stream view of the fp16-operand scan (P <= 4): blocks in the i0 byte, and groups
+// pooled across blocks when there are no two-index prefixes (P <= 3).
+static void build_quads16(int d, int P, std::vector<sata::QuadRec> &out, std::vector<uint32_t> &flags) {
+    build_quads(d, P, out, flags, 16, true, P <= 3);
 }
 
 static sata_status check_dims(int d_k, int d_v, int P) {
@@ -429,6 +458,26 @@ int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *
             for (int z = 0; z < 4; ++z) coef4[4 * i + z] = quads[(size_t)i].coef[z];
     }
     return nq;
+}
+
+int64_t sata_describe_quads16(int d_k, int P, uint32_t *w0, int32_t *cidx, float *coef4, uint32_t *flags,
+                              int64_t cap) {
+    g_last_error.clear();
+    if (check_dims(d_k, d_k, P) != SATA_OK) return -1;
+    std::vector<sata::QuadRec> quads;
+    std::vector<uint32_t> fl;
+    if (P <= 4 && d_k >= 16 && d_k <= kMaxScan16Dim) build_quads16(d_k, P, quads, fl);
+    const int64_t np = (int64_t)fl.size();
+    for (int64_t p = 0; p < np && p < cap; ++p) {
+        if (flags) flags[p] = fl[(size_t)p];
+        for (int64_t i = 16 * p; i < 16 * p + 16; ++i) {
+            if (w0) w0[i] = quads[(size_t)i].w0;
+            if (cidx) cidx[i] = quads[(size_t)i].cidx;
+            if (coef4)
+                for (int z = 0; z < 4; ++z) coef4[4 * i + z] = quads[(size_t)i].coef[z];
+        }
+    }
+    return np;
 }
 
 sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
@@ -474,7 +523,7 @@ sata_status sata_build_index(int d_k, int d_v, int P, sata_index **out) {
     std::vector<sata::QuadRec> quads16;
     std::vector<uint32_t> flags16;
     if (P <= 4 && d_k >= 16 && d_k <= kMaxScan16Dim) {
-        build_quads(d_k, P, quads16, flags16, 16, true);
+        build_quads16(d_k, P, quads16, flags16);
         idx->np16 = (int64_t)flags16.size();
         sata::QuadRec padq{};
         padq.w0 = (uint32_t)(d_k + 1) | ((uint32_t)(d_k + 1) << 8);
@@ -574,6 +623,7 @@ void sata_index_free(sata_index *idx) {
     if (idx->d_qflags) (void)hipFree(idx->d_qflags);
     for (void *p : {(void *)idx->d_p16_w0, (void *)idx->d_p16_cidx, (void *)idx->d_p16_coef, (void *)idx->d_p16_flags})
         if (p) (void)hipFree(p);
+    if (idx->lower) sata_index_free(idx->lower);
     delete idx;
 }
 
@@ -792,8 +842,12 @@ sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, c
     if (chunk != 0 && chunk != 64 && chunk != 128)
         return fail(SATA_ERR_UNSUPPORTED, "chunk must be 0 (default), 64 or 128 (got %d)", chunk);
     if (idx->dk != idx->dv) return fail(SATA_ERR_UNSUPPORTED, "the backward pass needs d_k == d_v");
-    if (idx->dk > kMaxPrefillDim)
-        return fail(SATA_ERR_UNSUPPORTED, "the backward pass supports d_k <= %d (got %d)", kMaxPrefillDim, idx->dk);
+    // above 64 every pass must run on the fp16-operand scan: bf16 inputs, and P - 1 orders that
+    // still have features beyond order 0
+    if (idx->dk > kMaxPrefillDim && !(sata::scan16_covers(idx, in_dt) && idx->P >= 3))
+        return fail(SATA_ERR_UNSUPPORTED,
+                    "the backward pass supports d_k <= %d, or d_k = %d with bf16 inputs and 3 <= P <= 4 "
+                    "(got d_k=%d, P=%d)", kMaxPrefillDim, kMaxScan16Dim, idx->dk, idx->P);
     const int64_t bh = (int64_t)batch * heads;
     if (bh > 65535) return fail(SATA_ERR_UNSUPPORTED, "batch*heads <= 65535 supported (got %lld)", (long long)bh);
     if (n == 0) return SATA_OK;
@@ -812,15 +866,20 @@ sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, c
     }
     DeviceGuard g(idx->device);
     if (!g.ok) return fail(SATA_ERR_HIP, "cannot select the index's device");
-    sata_index *lower = nullptr;
+    const sata_index *lower = nullptr;
     if (idx->P >= 2) {
-        sata_status s = sata_build_index(idx->dk, idx->dv, idx->P - 1, &lower);
-        if (s != SATA_OK) return s;
+        std::lock_guard<std::mutex> lock(idx->lower_mu);
+        if (!idx->lower) {
+            sata_index *built = nullptr;
+            sata_status s = sata_build_index(idx->dk, idx->dv, idx->P - 1, &built);
+            if (s != SATA_OK) return s;
+            idx->lower = built;
+        }
+        lower = idx->lower;
     }
     const int64_t kBudget = (int64_t)8 << 30;   // bytes of per-column temporaries per pass
     hipError_t e = sata::launch_backward(idx, lower, bh, q, k, v, dout, dq, dk, dv, n, chunk, in_dt, grad_dt, kBudget,
                                          (hipStream_t)stream);
-    if (lower) sata_index_free(lower);
     if (e == hipErrorMemoryAllocation || e == hipErrorOutOfMemory) {
         (void)hipGetLastError();
         return fail(SATA_ERR_OOM, "backward temporaries could not be allocated");
@@ -942,7 +1001,7 @@ int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t 
     if (P <= 4 && d_k >= 16) {
         std::vector<sata::QuadRec> q16;
         std::vector<uint32_t> f16;
-        build_quads(d_k, P, q16, f16, 16, true);
+        build_quads16(d_k, P, q16, f16);
         idx.np16 = (int64_t)f16.size();
     }
     const sata::PrefillPlan plan = sata::plan_prefill(&idx, batch_heads, n, chunk, (sata_dtype)in_dt, work_cap);

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/sata.h"
 
 // Largest decode window: deferred tokens held per head before a fold.
@@ -44,12 +46,16 @@ struct sata_index {
     // The same features in positions of 16 quads (16 streams sharing a block), for the
     // fp16-operand scan: np16 positions, each [16] quad words, state indices and [16][4]
     // weights, plus a flag word; kPos16Pad padding positions follow.  Built for P <= 4 and
-    // 16 <= d_K <= 64 (np16 = 0 otherwise).
+    // 16 <= d_K <= 128 (np16 = 0 otherwise).
     int64_t np16 = 0;
     uint32_t *d_p16_w0 = nullptr;
     int32_t *d_p16_cidx = nullptr;
     float *d_p16_coef = nullptr;
     uint32_t *d_p16_flags = nullptr;
+    // The index of the same head sizes with P - 1 orders (the backward's dk and dq passes),
+    // built by the first backward call that needs it and freed with this index.
+    mutable sata_index *lower = nullptr;
+    mutable std::mutex lower_mu;
 };
 
 struct sata_state {

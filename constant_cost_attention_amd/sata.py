@@ -29,6 +29,7 @@ _EXPORTS = (
     "sata_state_flush", "sata_state_check", "sata_state_reset", "sata_state_free",
     "sata_state_data",
     "sata_prefill", "sata_prefill_noalloc", "sata_prefill_backward", "sata_decode_step", "sata_expand_features", "sata_describe_features", "sata_describe_quads",
+    "sata_describe_quads16",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
     "sata_describe_prefill_plan", "sata_debug_scan_faults", "sata_debug_prefill_positions", "sata_measure_mfma_loop",
@@ -96,6 +97,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_describe_quads.argtypes = [cint, cint, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_float), i64]
     lib.sata_describe_quads.restype = i64
+    lib.sata_describe_quads16.argtypes = [cint, cint, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_uint32), i64]
+    lib.sata_describe_quads16.restype = i64
     lib.sata_status_string.argtypes = [cint]
     lib.sata_status_string.restype = ctypes.c_char_p
     lib.sata_last_error.argtypes = []
@@ -467,6 +471,26 @@ def sata_describe_quads(d_k: int, P: int):
                             cidx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                             coef.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), nq)
     return w0, cidx, coef
+
+
+def sata_describe_quads16(d_k: int, P: int):
+    """Host-only: (w0 uint32 [np, 16], cidx int32 [np, 16], coef float32 [np, 16, 4],
+    flags uint32 [np]) of the fp16-operand scan's positions (np = 0 outside its range)."""
+    import numpy as np
+    lib = load()
+    npos = lib.sata_describe_quads16(int(d_k), int(P), None, None, None, None, 0)
+    if npos < 0:
+        raise SataError(SATA_ERR_UNSUPPORTED if d_k > 0 and P >= 1 else SATA_ERR_INVALID, "sata_describe_quads16",
+                        lib.sata_last_error().decode())
+    w0 = np.zeros((npos, 16), dtype=np.uint32)
+    cidx = np.zeros((npos, 16), dtype=np.int32)
+    coef = np.zeros((npos, 16, 4), dtype=np.float32)
+    flags = np.zeros(npos, dtype=np.uint32)
+    lib.sata_describe_quads16(int(d_k), int(P), w0.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                              cidx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                              coef.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                              flags.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), npos)
+    return w0, cidx, coef, flags
 
 
 def status_string(status: int) -> str:

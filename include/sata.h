@@ -41,7 +41,8 @@
  *     1 <= P <= 5.  Prefill needs d_K == d_V; at d_K = 128 it runs the
  *     chunked scan for bf16 inputs with P <= 4, and otherwise (fp32 inputs,
  *     P = 5) blocks of 64 tokens through the state in HBM, which is much
- *     slower; the backward refuses d_K = 128.  Other values return
+ *     slower; the backward takes d_K = 128 for bf16 inputs with 3 <= P <= 4
+ *     and refuses it otherwise.  Other values return
  *     SATA_ERR_UNSUPPORTED.  The state grows as
  *     C(d_K+P-1, P-1) (d_V+1) fp32 values per head: at d_K = 64, 12.5 MB for
  *     P = 4 and 212 MB for P = 5; at d_K = 128 and P = 4, 189 MB.
@@ -271,8 +272,14 @@ sata_status sata_prefill_noalloc(const sata_index *idx, sata_state *st, const vo
  * a constant cost per token [hotdry, "Engineering realisation of the constant
  * compute cost"]: a forward pass for out and z, a pass of P orders for dv, and
  * passes of P - 1 orders over d_V + 1 pseudo-heads per head for dk and dq
- * (none when P == 1: dq = dk = 0).  Allocates its temporaries (hipMalloc, up
- * to a few GB) and synchronises `stream` before returning.  Gradients must
+ * (none when P == 1: dq = dk = 0).  With bf16 inputs every pass whose head
+ * size and order the fp16-operand prefill scan covers runs on it; the
+ * gradient-weighted values (g_i, and g_i[c] q_i) enter scaled by the power of
+ * two that brings the largest |g| into [2^8, 2^9), and the results are scaled
+ * back.  d_K = 128 needs bf16 inputs and 3 <= P <= 4 (SATA_ERR_UNSUPPORTED
+ * otherwise).  The (P - 1)-order index is built on the first call and kept
+ * with idx (freed by sata_index_free).  Allocates its temporaries (hipMalloc,
+ * up to a few GB) and synchronises `stream` before returning.  Gradients must
  * not overlap the inputs or each other; n = 0 is a no-op. */
 sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, const void *q, const void *k,
                                   const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n,
@@ -331,12 +338,28 @@ int64_t sata_describe_features(int d_k, int P, uint32_t *tuples, float *coef, in
  * number of quads, or -1 for arguments sata_build_index would reject. */
 int64_t sata_describe_quads(int d_k, int P, uint32_t *w0, int32_t *cidx, float *coef4, int64_t cap);
 
+/* Host-only, for tests: the same features in the fp16-operand scan's view
+ * (P <= 4, 16 <= d_K <= 128): positions of 16 quads sharing a block b, with
+ * w0 = i1 | i2 << 8 | b << 16 | slot mask << 28 (absent indices are d_K,
+ * padding quads d_K + 1), cidx and coef4 as above (16 per position), and per
+ * position flags: bit 0 = some quad has invalid slots or slots of different
+ * weights, bit 1 = the position starts a group (the 16 prefixes change; the
+ * following positions of the group take blocks b + 1, b + 2, ...).  For P <= 3
+ * a group takes 16 consecutive prefixes of the whole list, so some of its
+ * quads have no valid slot in its lower blocks.  Writes up to cap positions
+ * (16 cap quads, 64 cap weights; any pointer may be NULL) and returns the
+ * number of positions (0 outside that range), or -1 for arguments
+ * sata_build_index would reject. */
+int64_t sata_describe_quads16(int d_k, int P, uint32_t *w0, int32_t *cidx, float *coef4, uint32_t *flags,
+                              int64_t cap);
+
 /* Host-only: the chunked prefill's plan for batch_heads heads of n tokens of
  * (d_k = d_v, P) with in_dt inputs under a workspace cap of work_cap bytes
  * (sata_prefill starts at 16 GB): returns the workspace bytes and writes the
  * chunks per segment and the feature slices per head (either pointer may be
- * NULL); -1 for arguments the chunked prefill does not take (d_k > 64 runs in
- * blocks and has no such plan).  For tests and capacity planning. */
+ * NULL); -1 for arguments the chunked prefill does not take (d_k = 128 has a
+ * plan only for bf16 inputs with P <= 4; the rest runs in blocks).  For tests
+ * and capacity planning. */
 int64_t sata_describe_prefill_plan(int d_k, int P, int64_t batch_heads, int64_t n, int chunk, int in_dt,
                                    int64_t work_cap, int64_t *seg_chunks, int64_t *slices);
 

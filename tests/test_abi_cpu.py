@@ -22,7 +22,7 @@ def lib():
 def _declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sata_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sata_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -158,6 +158,84 @@ def test_quads_cover_every_feature_once(d, P):
             seen[f] += 1
     assert seen[0] == 0 and order[0] == 0
     assert np.all(seen[1:] == 1)
+
+
+def _positions16(d, P):
+    """Positions of the 16-stream view by its construction rule, counted without the library:
+    per block a the prefixes whose last index lies in it (order 3: i1 <= i2, order 2: i2
+    alone, and the empty prefix for a = 0); groups of 16 per block for P = 4, pooled over
+    the whole list for P <= 3; a group sweeps the blocks from its first prefix's to the last."""
+    per = []
+    for a in range(d // 4):
+        n = (1 if P >= 2 and a == 0 else 0) + (4 if P >= 3 else 0)
+        if P >= 4:
+            n += sum(i2 + 1 for i2 in range(4 * a, 4 * a + 4))
+        per.append(n)
+    if P <= 3:
+        blocks = [a for a in range(d // 4) for _ in range(per[a])]
+        return sum(d // 4 - blocks[g] for g in range(0, len(blocks), 16))
+    return sum(-(-per[a] // 16) * (d // 4 - a) for a in range(d // 4))
+
+
+@pytest.mark.parametrize("d,P", [(16, 2), (16, 3), (16, 4), (32, 3), (64, 3), (64, 4), (128, 3), (128, 4)])
+def test_quads16_cover_every_feature_once(d, P):
+    """The fp16-operand scan's view: every valid slot is the feature (i1, i2, 4b+z) at state
+    index cidx + (z - first valid slot) with the feature table's weight, and the valid slots
+    cover every feature but the constant one exactly once.  The 16 quads of a position share
+    the block b; flag bit 1 marks exactly the positions whose 16 prefixes differ from the
+    previous position's, and within a group b steps by one; a position without flag bit 0
+    has only full quads of one weight (and padding).  The position count follows the
+    grouping rule (P <= 3 pools the prefixes of all blocks: 44 positions at d = 64, against
+    136 with groups per block)."""
+    from constant_cost_attention_amd import sata
+    tup, coef = sata.sata_describe_features(d, P)
+    w0, cidx, qc, flags = sata.sata_describe_quads16(d, P)
+    assert len(w0) == _positions16(d, P)
+    if (d, P) == (64, 3):
+        assert len(w0) == 44
+    slots = np.stack([(tup >> (8 * r)) & 0xFF for r in range(4)], axis=1).astype(np.int64)
+    order = np.sum(slots < d, axis=1).astype(np.int64)
+    seen = np.zeros(len(tup), dtype=np.int64)
+    prev_pref, prev_b = None, None
+    for p in range(len(w0)):
+        i1 = (w0[p] & 0xFF).astype(np.int64)
+        i2 = ((w0[p] >> 8) & 0xFF).astype(np.int64)
+        b = ((w0[p] >> 16) & 0xFF).astype(np.int64)
+        mask = (w0[p] >> 28).astype(np.int64)
+        assert np.all(b == b[0])
+        pref = (tuple(i1), tuple(i2))
+        starts = prev_pref is None or pref != prev_pref
+        assert bool(flags[p] & 2) == starts, p
+        if not starts:
+            assert b[0] == prev_b + 1
+        prev_pref, prev_b = pref, int(b[0])
+        pad = (i1 == d + 1) & (i2 == d + 1)
+        mixed = False
+        for s in range(16):
+            if pad[s]:
+                assert mask[s] == 0 and cidx[p, s] == -1 and np.all(qc[p, s] == 0)
+                continue
+            if mask[s] != 0xF or len(set(qc[p, s].tolist())) != 1:
+                mixed = True
+            if not mask[s]:
+                assert cidx[p, s] == -1 and np.all(qc[p, s] == 0)
+                continue
+            z0 = (int(mask[s]) & -int(mask[s])).bit_length() - 1
+            for z in range(4):
+                if not (mask[s] >> z) & 1:
+                    assert qc[p, s, z] == 0
+                    continue
+                f = int(cidx[p, s]) + z - z0
+                idx = [int(i) for i in (i1[s], i2[s]) if i < d] + [4 * int(b[0]) + z]
+                assert idx == sorted(idx)
+                assert [int(x) for x in slots[f, :order[f]]] == idx, (p, s, z, idx)
+                assert abs(qc[p, s, z] / math.sqrt(d) ** len(idx) - coef[f]) <= 1e-6 * coef[f]
+                seen[f] += 1
+        assert bool(flags[p] & 1) == mixed, p
+    assert seen[0] == 0 and order[0] == 0
+    assert np.all(seen[1:] == 1)
+    assert sata.sata_describe_quads16(8, 4)[0].shape == (0, 16)
+
 
 
 def test_describe_errors_raise_sata_error():

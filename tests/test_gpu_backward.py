@@ -6,7 +6,8 @@ the head's whole gradient: single rows of dq or dk can be near zero).  Bars:
 TOL_GRAD_F32 for fp32 inputs (the passes run the fp32 prefill path; the
 gradients are sums of a few of its results, so a few times its 1e-5), and
 the bf16-input bar for bf16 inputs (the passes also round their values,
-g_i[c] q_i and [v_j, 1][c] k_j, to bf16).
+g_i[c] q_i and [v_j, 1][c] k_j, to bf16, and run on the fp16-operand scan
+where it covers the head size and order).
 """
 import numpy as np
 import pytest
@@ -117,10 +118,10 @@ def test_backward_d64_bf16_workload_heads(sata, oracle):
 def test_backward_d64_bf16_workload_full_size(sata):
     """The full d_K = 64 workload (1 x 8 heads x 65536 tokens, bf16), whose passes plan
     workspaces near the 16 GB cap, where O9 cannot run: properties that hold at any size.
-    Every pass is linear in dout, and the passes run on bf16 / fp32 operands whose exponent
-    range holds the gradient-weighted values, where scaling by two commutes with every
-    rounding: doubling dout doubles every gradient bit for bit.  The attention weights of each
-    query sum to one, so sum_j dv_j = sum_i dout_i (normwise within the bf16-input bar)."""
+    Every pass is linear in dout, and the gradient-weighted values enter the passes scaled by
+    a power of two chosen from the largest |g|, which doubling dout halves: the passes see the
+    same bits, and doubling dout doubles every gradient bit for bit.  The attention weights of
+    each query sum to one, so sum_j dv_j = sum_i dout_i (normwise within the bf16-input bar)."""
     wl = si.WORKLOADS["prefill_d64_p4_bf16"]
     say("backward full size %s" % wl.name)
     q, k, v = si.draw_qkv_device((wl.batch, wl.heads), wl.n, wl.d_k, wl.d_v, wl.seed, "bf16")

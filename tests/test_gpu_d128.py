@@ -4,7 +4,8 @@ kernel), the chunked fp16-operand prefill scan (bf16 inputs, P <= 4: 64-token
 chunks, one position per update wavefront) and the block prefill for the rest
 (fp32 inputs: blocks of up to 64 tokens read out against the state in HBM,
 direct terms inside the block, then folded in) against the oracle; the
-backward refuses d_K = 128."""
+backward for bf16 inputs and 3 <= P <= 4 (every pass on the fp16-operand
+scan) against the oracle's gradients, and its refusal otherwise."""
 import math
 
 import numpy as np
@@ -190,9 +191,41 @@ def test_prefill_d128_continued_by_decode_and_prefill(sata, oracle):
     idx.free()
 
 
-def test_d128_backward_refused(sata):
-    idx = sata.Index(D, D, 3)
-    q = torch.zeros((1, 1, 8, D), device="cuda")
+@pytest.mark.parametrize("P", [3, 4])
+def test_d128_backward_bf16(sata, oracle, P):
+    """dq, dk, dv of a ragged bf16 prefill (two 64-token chunks and 22) on two heads against
+    O9, normwise per head; a second call on the same index (its P - 1 order index is then
+    reused) gives the same bits."""
+    n, heads = 150, 2
+    x = si.draw_qkv((1, heads), n, D, D, 9500 + P, "bf16")
+    dout = np.random.default_rng(9510 + P).standard_normal((1, heads, n, D)).astype(np.float32)
+    idx = sata.Index(D, D, P)
+    q, k, v = dev_all(x)
+    do = torch.from_numpy(dout).cuda().to(torch.bfloat16)
+    say("backward d=128 P=%d bf16 n=%d" % (P, n))
+    runs = []
+    for _ in range(2):
+        g = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+        sata.sata_prefill_backward(idx, q, k, v, do, *g)
+        torch.cuda.synchronize()
+        runs.append(g)
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+    ref = oracle.taylor_attention_grad(x.q, x.k, x.v, do.float().cpu().numpy(), P)
+    for name, a, r in zip(("dq", "dk", "dv"), runs[0], ref):
+        a = a.cpu().numpy().astype(np.float64)
+        err = float((np.abs(a - r).reshape(heads, -1).max(1) / np.abs(r).reshape(heads, -1).max(1)).max())
+        say("  %s err %.3e" % (name, err))
+        assert err <= TOL_BF16, name
+    idx.free()
+
+
+@pytest.mark.parametrize("P,dtype", [(3, torch.float32), (2, torch.bfloat16)])
+def test_d128_backward_refused(sata, P, dtype):
+    """fp32 inputs (no chunked scan at this head size) and P = 2 (whose dk and dq passes have
+    order 0 alone, outside the fp16-operand scan) are refused before any work."""
+    idx = sata.Index(D, D, P)
+    q = torch.zeros((1, 1, 8, D), device="cuda", dtype=dtype)
     g = [torch.zeros_like(q) for _ in range(3)]
     with pytest.raises(sata.SataError) as e:
         sata.sata_prefill_backward(idx, q, q, q, q, g[0], g[1], g[2])
