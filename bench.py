@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 METRIC = "SATA tokens/sec (prefill, decode) at d_K=64 P=4; % of HBM / MFMA peak"
 METRIC_WORKLOAD = "prefill_d64_p4_bf16"   # the prefill the metric is quoted on
+BACKWARD_WORKLOADS = ("prefill_d64_p4_bf16", "prefill_d16_p4_f32", "prefill_d128_p4_bf16")
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix / vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
@@ -65,6 +66,8 @@ def parse_args():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="only: time every (chunk, positions per update wavefront) of the bf16 prefill workloads")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only: the backward calls of the backward section (for kernel traces)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--traffic-run", action="store_true",
                     help="one launch of each timed kernel plus a 1 GiB copy, for rocprofv3 --pmc runs")
@@ -864,6 +867,14 @@ def main():
     if args.tile_sweep:
         print(json.dumps({"tile_sweep": tile_sweep(sata)}))
         return
+    if args.backward_only:
+        out = []
+        for name in BACKWARD_WORKLOADS:
+            bw = time_backward(sata, si.WORKLOADS[name], args.steps)
+            log("backward %s: %.2f ms per call" % (name, bw["ms_per_call"]))
+            out.append(bw)
+        print(json.dumps({"backward": out}))
+        return
 
     wl = si.WORKLOADS[METRIC_WORKLOAD]
     log("drawing %s inputs" % wl.name)
@@ -968,7 +979,7 @@ def main():
 
     if not args.no_backward:
         bwd = []
-        for name in ("prefill_d64_p4_bf16", "prefill_d16_p4_f32", "prefill_d128_p4_bf16"):
+        for name in BACKWARD_WORKLOADS:
             bw = time_backward(sata, si.WORKLOADS[name], 2)
             if name == METRIC_WORKLOAD:
                 bw["vs_forward_call"] = bw["ms_per_call"] / result["ms_per_step"]

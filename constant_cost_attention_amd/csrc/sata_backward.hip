@@ -34,6 +34,13 @@ namespace {
 constexpr int kBwThreads = 256;
 
 inline unsigned bw_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + kBwThreads - 1) / kBwThreads, 1 << 20); }
+// Grid of the per-element kernels over [heads][n][D] (D a power of two): x strides one head's
+// n x D elements, y is the head, so element indices need shifts and masks, no division.
+inline dim3 bw_grid2(int64_t n, int D, int64_t heads) {
+    return dim3((unsigned)std::min<int64_t>((n * D + kBwThreads - 1) / kBwThreads, 4096), (unsigned)heads);
+}
+#define BW_ELEMENTS(j, n, lgD) \
+    for (int64_t j = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; j < ((n) << (lgD)); j += (int64_t)gridDim.x * kBwThreads)
 
 // g_i = [dO_i / z_i, -(dO_i . o_i) / z_i], one thread per token.
 template <typename TIn>
@@ -52,14 +59,14 @@ __global__ __launch_bounds__(kBwThreads) void bw_prep_g(const TIn *__restrict__ 
     }
 }
 
-// out[h][t][:] = in[h][n-1-t][:] (the time-reversed sequence of every head).
+// out[h][t][:] = in[h][n-1-t][:] (the time-reversed sequence of every head); grid bw_grid2.
 template <typename T>
-__global__ __launch_bounds__(kBwThreads) void bw_reverse(const T *__restrict__ in, T *__restrict__ out, int64_t heads,
-                                                         int64_t n, int D) {
-    const int64_t total = heads * n * D;
-    for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
-        const int64_t d = i % D, t = (i / D) % n, h = i / (D * n);
-        out[i] = in[(h * n + (n - 1 - t)) * D + d];
+__global__ __launch_bounds__(kBwThreads) void bw_reverse(const T *__restrict__ in, T *__restrict__ out, int64_t n,
+                                                         int lgD) {
+    const int64_t base = (int64_t)blockIdx.y * n << lgD;
+    BW_ELEMENTS(j, n, lgD) {
+        const int64_t t = j >> lgD, d = j & ((1 << lgD) - 1);
+        out[base + j] = in[base + ((n - 1 - t) << lgD) + d];
     }
 }
 
@@ -93,15 +100,16 @@ __device__ __forceinline__ float bw_value_scale(const unsigned *bits, bool inver
     return __builtin_amdgcn_ldexpf(1.f, inverse ? e - kBwValueExp : kBwValueExp - e);
 }
 
-// values of the dv pass: out[h][t][d] = g[h][n-1-t][d] (scaled), d < D.
-template <typename TIn>
+// values of the dv pass: out[h][t][d] = g[h][n-1-t][d] (scaled), d < D; TV is the input type,
+// or binary16 for a pass on the fp16-operand scan.
+template <typename TV>
 __global__ __launch_bounds__(kBwThreads) void bw_rev_g(const float *__restrict__ g, const unsigned *__restrict__ gmax,
-                                                       TIn *__restrict__ out, int64_t heads, int64_t n, int D) {
-    const int64_t total = heads * n * D;
+                                                       TV *__restrict__ out, int64_t n, int lgD) {
+    const int64_t h = blockIdx.y, D = 1 << lgD;
     const float vs = bw_value_scale(gmax, false);
-    for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
-        const int64_t d = i % D, t = (i / D) % n, h = i / (D * n);
-        out[i] = from_f32<TIn>(g[(h * n + (n - 1 - t)) * (D + 1) + d] * vs);
+    BW_ELEMENTS(j, n, lgD) {
+        const int64_t t = j >> lgD, d = j & (D - 1);
+        out[(h * n << lgD) + j] = from_f32<TV>(g[(h * n + (n - 1 - t)) * (D + 1) + d] * vs);
     }
 }
 
@@ -109,30 +117,38 @@ __global__ __launch_bounds__(kBwThreads) void bw_rev_g(const float *__restrict__
 // pass (kdk = 0), pseudo-head ph = h * cg + cc for column c = c0 + cc:
 //   dk: q' = rev(k), k' = rev(q), v'[t] = g[n-1-t][c] q[n-1-t] (scaled)
 //   dq: q' = q,      k' = k,      v'[t] = [v, 1][t][c] k[t]
-template <typename TIn>
+// q' and k' are written only when qo is given (a pass whose pseudo-heads read the head's
+// own q' and k' in place needs v' alone); v' is of TV (the input type, or binary16 for a pass
+// on the fp16-operand scan).
+template <typename TIn, typename TV>
 __global__ __launch_bounds__(kBwThreads) void bw_group_inputs(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                               const TIn *__restrict__ v, const float *__restrict__ g,
                                                               const unsigned *__restrict__ gmax,
                                                               TIn *__restrict__ qo, TIn *__restrict__ ko,
-                                                              TIn *__restrict__ vo, int64_t heads, int64_t n, int D,
-                                                              int c0, int cg, int kdk) {
-    const int64_t total = heads * cg * n * D;
+                                                              TV *__restrict__ vo, int64_t n, int lgD, int c0, int cg,
+                                                              int kdk) {
+    const int ph = blockIdx.y;                                  // grid bw_grid2 over the pseudo-heads
+    const int64_t h = ph / cg, D = 1 << lgD;
+    const int c = c0 + ph % cg;
     const float vs = bw_value_scale(gmax, false);
-    for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
-        const int64_t d = i % D, t = (i / D) % n, ph = i / (D * n);
-        const int64_t h = ph / cg;
-        const int c = c0 + (int)(ph % cg);
+    BW_ELEMENTS(j, n, lgD) {
+        const int64_t i = ((int64_t)ph * n << lgD) + j;
+        const int64_t t = j >> lgD, d = j & (D - 1);
         const int64_t ts = kdk ? n - 1 - t : t;                 // source token
         const int64_t src = (h * n + ts) * D + d;
         if (kdk) {
-            qo[i] = k[src];
-            ko[i] = q[src];
-            vo[i] = from_f32<TIn>(g[(h * n + ts) * (D + 1) + c] * vs * to_f32(q[src]));
+            if (qo) {
+                qo[i] = k[src];
+                ko[i] = q[src];
+            }
+            vo[i] = from_f32<TV>(g[(h * n + ts) * (D + 1) + c] * vs * to_f32(q[src]));
         } else {
-            qo[i] = q[src];
-            ko[i] = k[src];
+            if (qo) {
+                qo[i] = q[src];
+                ko[i] = k[src];
+            }
             const float vc = c < D ? to_f32(v[(h * n + ts) * D + c]) : 1.f;
-            vo[i] = from_f32<TIn>(vc * to_f32(k[src]));
+            vo[i] = from_f32<TV>(vc * to_f32(k[src]));
         }
     }
 }
@@ -143,12 +159,13 @@ __global__ __launch_bounds__(kBwThreads) void bw_group_inputs(const TIn *__restr
 template <typename TIn>
 __global__ __launch_bounds__(kBwThreads) void bw_contract(const float *__restrict__ r, const TIn *__restrict__ v,
                                                           const float *__restrict__ g, const unsigned *__restrict__ gmax,
-                                                          float *__restrict__ acc, int64_t heads, int64_t n, int D,
-                                                          int c0, int cg, int kdk, float s) {
-    const int64_t total = heads * n * D;
+                                                          float *__restrict__ acc, int64_t n, int lgD, int c0, int cg,
+                                                          int kdk, float s) {
+    const int64_t h = blockIdx.y, D = 1 << lgD;                 // grid bw_grid2 over the heads
     if (kdk) s *= bw_value_scale(gmax, true);
-    for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
-        const int64_t d = i % D, t = (i / D) % n, h = i / (D * n);
+    BW_ELEMENTS(j, n, lgD) {
+        const int64_t i = (h * n << lgD) + j;
+        const int64_t t = j >> lgD, d = j & (D - 1);
         const int64_t tr = kdk ? n - 1 - t : t;                 // row of the pass's output
         float sum = 0.f;
         for (int cc = 0; cc < cg; ++cc) {
@@ -163,12 +180,12 @@ __global__ __launch_bounds__(kBwThreads) void bw_contract(const float *__restric
 // dv[h][j] = r[h][n-1-j] (the dv pass ran on reversed time, on scaled values).
 template <typename TOut>
 __global__ __launch_bounds__(kBwThreads) void bw_finish_dv(const float *__restrict__ r, const unsigned *__restrict__ gmax,
-                                                           TOut *__restrict__ dv, int64_t heads, int64_t n, int D) {
-    const int64_t total = heads * n * D;
+                                                           TOut *__restrict__ dv, int64_t n, int lgD) {
+    const int64_t base = (int64_t)blockIdx.y * n << lgD;        // grid bw_grid2 over the heads
     const float inv = bw_value_scale(gmax, true);
-    for (int64_t i = (int64_t)blockIdx.x * kBwThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBwThreads) {
-        const int64_t d = i % D, t = (i / D) % n, h = i / (D * n);
-        dv[i] = from_f32<TOut>(r[(h * n + (n - 1 - t)) * D + d] * inv);
+    BW_ELEMENTS(j, n, lgD) {
+        const int64_t t = j >> lgD, d = j & ((1 << lgD) - 1);
+        dv[base + j] = from_f32<TOut>(r[base + ((n - 1 - t) << lgD) + d] * inv);
     }
 }
 
@@ -217,9 +234,11 @@ struct TempState {
     }
 };
 
-// One unnormalised (raw) or normalised prefill of `heads` heads from a zero state.
+// One unnormalised (raw) or normalised prefill of `heads` heads from a zero state; heads read
+// q and k of head h / qk_div (the fp16-operand scan only).
 hipError_t run_pass(TempState &ts, int64_t heads, const void *q, const void *k, const void *v, float *out, float *den,
-                    int64_t n, int chunk, sata_dtype in_dt, bool raw, hipStream_t s) {
+                    int64_t n, int chunk, sata_dtype in_dt, bool raw, hipStream_t s, int qk_div = 1,
+                    bool v_f16 = false) {
     const sata_index *idx = ts.st.idx;
     // bf16 inputs run on the fp16-operand scan where it covers the index (the gradient-weighted
     // values arrive scaled into fp16's normal range), like the forward prefill
@@ -230,8 +249,11 @@ hipError_t run_pass(TempState &ts, int64_t heads, const void *q, const void *k, 
     if (plan.ok && plan.work_bytes > ts.st.work_bytes)
         plan = plan_prefill(idx, heads, n, chunk, in_dt, ts.st.work_bytes, s16);
     if (!plan.ok || heads > ts.max_heads || plan.work_bytes > ts.st.work_bytes) return hipErrorInvalidValue;
+    if ((qk_div != 1 || v_f16) && !plan.s16) return hipErrorInvalidValue;
     plan.raw = raw;
     plan.den_out = den;
+    plan.qk_div = qk_div;
+    plan.v_f16 = v_f16;
     ts.st.heads = (int)heads;
     ts.st.state_bytes = heads * (idx->dv + 1) * idx->m_pad * (int64_t)sizeof(float);
     hipError_t e = launch_zero(static_cast<float *>(ts.st.d_state), ts.st.state_bytes / 4, s);
@@ -247,6 +269,7 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
                       const void *vv, const void *doutv, void *dqv, void *dkv, void *dvv, int64_t n, int chunk,
                       sata_dtype in_dt, int64_t mem_budget, hipStream_t s) {
     const int D = idx->dk;
+    const int lgD = __builtin_ctz((unsigned)D);   // head sizes are powers of two
     const TIn *q = static_cast<const TIn *>(qv), *k = static_cast<const TIn *>(kv), *v = static_cast<const TIn *>(vv);
     const int64_t elems = bh * n * D;
     t_bw_step = "temporaries";
@@ -274,26 +297,36 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     hipLaunchKernelGGL(bw_absmax, dim3(std::min<unsigned>(bw_grid(bh * n * (D + 1)), 4096)), dim3(kBwThreads), 0, s, g,
                        bh * n * (D + 1), gmax);
     // 2. dv: reversed time, queries k, keys q, values g[:d_V], P orders
-    hipLaunchKernelGGL(bw_reverse<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, k, rq, bh, n, D);
-    hipLaunchKernelGGL(bw_reverse<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, q, rk, bh, n, D);
-    hipLaunchKernelGGL(bw_rev_g<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, g, gmax, rg, bh, n, D);
+    hipLaunchKernelGGL(bw_reverse<TIn>, bw_grid2(n, D, bh), dim3(kBwThreads), 0, s, k, rq, n, lgD);
+    hipLaunchKernelGGL(bw_reverse<TIn>, bw_grid2(n, D, bh), dim3(kBwThreads), 0, s, q, rk, n, lgD);
+    // on the fp16-operand scan the gradient-weighted values go in as binary16 (rg has the width)
+    const bool top16 = scan16_covers(idx, in_dt);
+    if (top16)
+        hipLaunchKernelGGL(bw_rev_g<f16_t>, bw_grid2(n, D, bh), dim3(kBwThreads), 0, s, g, gmax,
+                           reinterpret_cast<f16_t *>(rg), n, lgD);
+    else
+        hipLaunchKernelGGL(bw_rev_g<TIn>, bw_grid2(n, D, bh), dim3(kBwThreads), 0, s, g, gmax, rg, n, lgD);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     t_bw_step = "dv pass";
-    if ((e = run_pass(top, bh, rq, rk, rg, r, nullptr, n, chunk, in_dt, true, s)) != hipSuccess) return e;
+    if ((e = run_pass(top, bh, rq, rk, rg, r, nullptr, n, chunk, in_dt, true, s, 1, top16)) != hipSuccess) return e;
     t_bw_step = "dk and dq accumulators";
-    hipLaunchKernelGGL(bw_finish_dv<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, r, gmax,
-                       static_cast<TOut *>(dvv), bh, n, D);
+    hipLaunchKernelGGL(bw_finish_dv<TOut>, bw_grid2(n, D, bh), dim3(kBwThreads), 0, s, r, gmax,
+                       static_cast<TOut *>(dvv), n, lgD);
     // 3. dk and dq: P - 1 orders, one pseudo-head per column c in groups of cg
     float *acc_k = ar.get<float>(elems), *acc_q = ar.get<float>(elems);
     if (ar.err != hipSuccess) return ar.err;
     if ((e = launch_zero(acc_k, elems, s)) != hipSuccess) return e;
     if ((e = launch_zero(acc_q, elems, s)) != hipSuccess) return e;
     if (lower) {
-        const int64_t per_col = elems * (3 * (int64_t)sizeof(TIn) + (int64_t)sizeof(float));
+        // on the fp16-operand scan the pseudo-heads of a head read its q' and k' in place (q and k
+        // for dq, the reversed copies of the dv pass for dk): only v' is written per column
+        const bool shared = scan16_covers(lower, in_dt);
+        const int64_t per_col = elems * ((shared ? 1 : 3) * (int64_t)sizeof(TIn) + (int64_t)sizeof(float));
         // columns per pass: within the memory budget, and bh * cg pseudo-heads within the grid's y limit
         const int cg = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)D + 1, mem_budget / std::max<int64_t>(per_col, 1),
                                                                    65535 / bh}));
-        TIn *gq = ar.get<TIn>(elems * cg), *gk = ar.get<TIn>(elems * cg), *gv = ar.get<TIn>(elems * cg);
+        TIn *gq = shared ? nullptr : ar.get<TIn>(elems * cg), *gk = shared ? nullptr : ar.get<TIn>(elems * cg);
+        TIn *gv = ar.get<TIn>(elems * cg);
         float *gr = ar.get<float>(elems * cg);
         if (ar.err != hipSuccess) return ar.err;
         TempState low;
@@ -305,15 +338,23 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
             for (int c0 = 0; c0 <= D; c0 += cg) {
                 const int n_c = std::min(cg, D + 1 - c0);
                 t_bw_step = kdk ? "inputs of a dk pass" : "inputs of a dq pass";
-                hipLaunchKernelGGL(bw_group_inputs<TIn>, dim3(bw_grid(elems * n_c)), dim3(kBwThreads), 0, s, q, k, v,
-                                   g, gmax, gq, gk, gv, bh, n, D, c0, n_c, kdk);
+                if (shared)
+                    hipLaunchKernelGGL((bw_group_inputs<TIn, f16_t>), bw_grid2(n, D, bh * n_c), dim3(kBwThreads), 0,
+                                       s, q, k, v, g, gmax, gq, gk, reinterpret_cast<f16_t *>(gv), n, lgD, c0, n_c,
+                                       kdk);
+                else
+                    hipLaunchKernelGGL((bw_group_inputs<TIn, TIn>), bw_grid2(n, D, bh * n_c), dim3(kBwThreads), 0, s,
+                                       q, k, v, g, gmax, gq, gk, gv, n, lgD, c0, n_c, kdk);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 t_bw_step = kdk ? "dk pass" : "dq pass";
-                if ((e = run_pass(low, bh * n_c, gq, gk, gv, gr, nullptr, n, chunk, in_dt, true, s)) != hipSuccess)
+                const void *pq = shared ? (kdk ? (const void *)rq : (const void *)q) : (const void *)gq;
+                const void *pk = shared ? (kdk ? (const void *)rk : (const void *)k) : (const void *)gk;
+                if ((e = run_pass(low, bh * n_c, pq, pk, gv, gr, nullptr, n, chunk, in_dt, true, s,
+                                  shared ? n_c : 1, shared)) != hipSuccess)
                     return e;
                 t_bw_step = "contraction";
-                hipLaunchKernelGGL(bw_contract<TIn>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, gr, v, g, gmax,
-                                   kdk ? acc_k : acc_q, bh, n, D, c0, n_c, kdk, sc);
+                hipLaunchKernelGGL(bw_contract<TIn>, bw_grid2(n, D, bh), dim3(kBwThreads), 0, s, gr, v, g, gmax,
+                                   kdk ? acc_k : acc_q, n, lgD, c0, n_c, kdk, sc);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
         }

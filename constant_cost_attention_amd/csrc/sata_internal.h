@@ -149,14 +149,20 @@ struct PrefillPlan {
     // normaliser y[d_V] of every token to den_out [B*H][n] (fp32)
     bool raw = false;
     float *den_out = nullptr;
+    // (s16 only) heads share q and k in groups of qk_div: head h reads q and k of head
+    // h / qk_div (the backward's pseudo-heads of one head differ only in v)
+    int qk_div = 1;
+    // (s16 only) v is binary16 rather than bf16: the backward's values (three more significand
+    // bits; they are scaled into fp16's normal range)
+    bool v_f16 = false;
 };
 // Largest prefill workspace planned by default (bytes; the device has 288 GB of HBM).  Longer
 // calls run in segments of whole chunks; when the allocation fails, sata_prefill plans again
 // under half the cap, down to one chunk per segment.
 constexpr int64_t kWorkCap = (int64_t)16 << 30;
 // fp16_operands: bf16 inputs may take the fp16-operand scan (exact for inputs inside fp16's
-// normal range once scaled; callers whose inputs can be far smaller, such as the backward's
-// gradient-weighted passes, plan without it).
+// normal range once scaled; the backward scales its gradient-weighted values into that range
+// first).
 PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk, sata_dtype in_dt,
                          int64_t work_cap = kWorkCap, bool fp16_operands = true);
 // Backward pass of a causal prefill from a zero state (sata_backward.hip);

@@ -1949,8 +1949,12 @@ static hipError_t run_prefill16(const sata_index *idx, const sata_state *st, con
     ta.raw = plan.raw ? 1 : 0;
     float *o0sums = reinterpret_cast<float *>(static_cast<char *>(st->d_work) + plan.o0_off);
     float *o0pre = o0sums + bh * nchunks * (D + 1);
-    hipLaunchKernelGGL((order0_sums_kernel<D, bf16_t>), dim3((unsigned)nchunks, (unsigned)bh), dim3(256), 0, stream,
-                       static_cast<const bf16_t *>(v), n, C, o0sums);
+    if (plan.v_f16)
+        hipLaunchKernelGGL((order0_sums_kernel<D, f16_t>), dim3((unsigned)nchunks, (unsigned)bh), dim3(256), 0, stream,
+                           static_cast<const f16_t *>(v), n, C, o0sums);
+    else
+        hipLaunchKernelGGL((order0_sums_kernel<D, bf16_t>), dim3((unsigned)nchunks, (unsigned)bh), dim3(256), 0, stream,
+                           static_cast<const bf16_t *>(v), n, C, o0sums);
     hipLaunchKernelGGL((order0_prefix_kernel<D>), dim3((unsigned)bh), dim3((D + 1 + 63) / 64 * 64), 0, stream, o0sums,
                        o0pre, nchunks, static_cast<float *>(st->d_state), idx->m_pad);   // a thread per column
     hipError_t e = hipGetLastError();
@@ -1966,6 +1970,8 @@ static hipError_t run_prefill16(const sata_index *idx, const sata_state *st, con
 hipError_t launch_prefill(const sata_index *idx, const sata_state *st, const PrefillPlan &plan,
                           const void *q, const void *k, const void *v, void *out, int64_t n,
                           sata_dtype in_dt, sata_dtype out_dt, hipStream_t stream) {
+    // shared q and k, binary16 values: the fp16-operand scan only
+    if (plan.qk_div < 1 || ((plan.qk_div != 1 || plan.v_f16) && !plan.s16)) return hipErrorInvalidValue;
     if (plan.s16) {
         if (in_dt != SATA_BF16) return hipErrorInvalidValue;   // never planned
         switch (idx->dk) {

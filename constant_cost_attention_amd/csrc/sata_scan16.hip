@@ -77,12 +77,30 @@ template <int D, int C> struct Img16 {
     static_assert(BYTES % 16 == 0 && (KS * 2) % 16 == 0, "16-byte units");
 };
 
+// The eight values of a 16-byte unit of v as fp16: bf16 words widen exactly and round to fp16
+// (exact inside its normal range); binary16 words are taken as they are.
+__device__ __forceinline__ void v_unit_f16(const uint4 &u, const bf16_t *, f16 (&out)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        out[2 * e] = (f16)__uint_as_float(w[e] << 16);
+        out[2 * e + 1] = (f16)__uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void v_unit_f16(const uint4 &u, const f16 *, f16 (&out)[8]) {
+    const f16x8 h = __builtin_bit_cast(f16x8, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = h[e];
+}
+
 // Prepass: grid (chunks of the segment, B*H), 256 threads.  Reads the chunk's
-// q, k, v (bf16) once and writes its image; k and v are transposed through LDS.
-template <int D, int C>
+// q, k (bf16) and v (bf16, or binary16 for internal callers) once and writes its image; k and v
+// are transposed through LDS.
+template <int D, int C, typename TV>
 __global__ __launch_bounds__(256) void scan16_prepass_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
-                                                             const bf16_t *__restrict__ v, int64_t n, int64_t tok0,
-                                                             int nchunk, float qscale, unsigned char *__restrict__ img) {
+                                                             const TV *__restrict__ v, int64_t n, int64_t tok0,
+                                                             int nchunk, float qscale, int qk_div,
+                                                             unsigned char *__restrict__ img) {
     using I = Img16<D, C>;
     constexpr int TS = C + 8;                         // LDS transpose row stride (halves)
     __shared__ __align__(16) f16 tk[D * TS];
@@ -96,7 +114,9 @@ __global__ __launch_bounds__(256) void scan16_prepass_kernel(const bf16_t *__res
     f16 *Kt = reinterpret_cast<f16 *>(dst + I::KT_OFF);
     f16 *Vt = reinterpret_cast<f16 *>(dst + I::V_OFF);
     f16 *Q = reinterpret_cast<f16 *>(dst + I::Q_OFF);
-    const bf16_t *qh = q + (bh * n + t0) * D, *kh = k + (bh * n + t0) * D, *vh = v + (bh * n + t0) * D;
+    const int64_t bqk = bh / qk_div;                  // the head whose q and k this head reads
+    const bf16_t *qh = q + (bqk * n + t0) * D, *kh = k + (bqk * n + t0) * D;
+    const TV *vh = v + (bh * n + t0) * D;
     // 16-byte units of 8 dims: unit i = token i / (D/8), dims 8 (i % (D/8)) ...
     constexpr int UPT = D / 8;
     for (int i = tid; i < C * UPT; i += 256) {
@@ -107,8 +127,9 @@ __global__ __launch_bounds__(256) void scan16_prepass_kernel(const bf16_t *__res
             uk = *reinterpret_cast<const uint4 *>(kh + (int64_t)t * D + d0);
             uv = *reinterpret_cast<const uint4 *>(vh + (int64_t)t * D + d0);
         }
-        const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w},
-                       wv[4] = {uv.x, uv.y, uv.z, uv.w};
+        const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w};
+        f16 hv[8];
+        v_unit_f16(uv, vh, hv);
         f16x2 hq[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -116,8 +137,8 @@ __global__ __launch_bounds__(256) void scan16_prepass_kernel(const bf16_t *__res
             hq[e] = f16x2{(f16)q0, (f16)q1};
             tk[(d0 + 2 * e) * TS + t] = (f16)(__uint_as_float(wk[e] << 16) * kKeyScale);
             tk[(d0 + 2 * e + 1) * TS + t] = (f16)(__uint_as_float(wk[e] & 0xffff0000u) * kKeyScale);
-            tv[(d0 + 2 * e) * TS + t] = (f16)__uint_as_float(wv[e] << 16);
-            tv[(d0 + 2 * e + 1) * TS + t] = (f16)__uint_as_float(wv[e] & 0xffff0000u);
+            tv[(d0 + 2 * e) * TS + t] = hv[2 * e];
+            tv[(d0 + 2 * e + 1) * TS + t] = hv[2 * e + 1];
         }
         // Q rows are I::QS halves (not a multiple of 8): two 8-byte stores
         uint2 *qd = reinterpret_cast<uint2 *>(Q + t * I::QS + d0);
@@ -769,7 +790,8 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
                                                             const bf16_t *__restrict__ k,
                                                             const unsigned char *__restrict__ img, TOut *__restrict__ out,
                                                             TaylorArgs ta, float *__restrict__ den_out,
-                                                            const float *__restrict__ o0pre, int64_t call_chunks) {
+                                                            const float *__restrict__ o0pre, int64_t call_chunks,
+                                                            int qk_div) {
     using I = Img16<D, C>;
     constexpr int NC = D + 1, TT = C / 16, NT = (NC + 15) / 16;
     constexpr int NV8 = TT * NC * 2;                // 16-byte loads (8 halves) per partial
@@ -839,7 +861,7 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
     __syncthreads();
     static_assert(TT % 2 == 0 && TT / 2 <= 4, "query tiles pair up over the four wavefronts");
     if (wave < TT / 2) {
-        const bf16_t *qh = q + bh * n * D, *kh = k + bh * n * D;
+        const bf16_t *qh = q + (bh / qk_div) * n * D, *kh = k + (bh / qk_div) * n * D;
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             const int qq = pass == 0 ? wave : TT - 1 - wave;
@@ -915,9 +937,14 @@ static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const 
     unsigned char *img = reinterpret_cast<unsigned char *>(work + plan.img_off);
     const int64_t call_chunks = (n + C - 1) / C;
     const int64_t chunk0 = tok0 / C;
-    hipLaunchKernelGGL((scan16_prepass_kernel<D, C>), dim3((unsigned)nseg, (unsigned)bh), dim3(256), 0, stream,
-                       static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), static_cast<const bf16_t *>(v),
-                       n, tok0, nseg, ta.scale * kQueryScale, img);
+    if (plan.v_f16)
+        hipLaunchKernelGGL((scan16_prepass_kernel<D, C, f16>), dim3((unsigned)nseg, (unsigned)bh), dim3(256), 0, stream,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), static_cast<const f16 *>(v),
+                           n, tok0, nseg, ta.scale * kQueryScale, plan.qk_div, img);
+    else
+        hipLaunchKernelGGL((scan16_prepass_kernel<D, C, bf16_t>), dim3((unsigned)nseg, (unsigned)bh), dim3(256), 0,
+                           stream, static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k),
+                           static_cast<const bf16_t *>(v), n, tok0, nseg, ta.scale * kQueryScale, plan.qk_div, img);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, st->device)) != hipSuccess) return e;
@@ -944,7 +971,7 @@ static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const 
         hipLaunchKernelGGL((scan16_reduce_kernel<D, C, TOut>), dim3((unsigned)nseg, (unsigned)bh), dim3(256), 0, stream,
                            partial, plan.slices, nseg, n, tok0, static_cast<const bf16_t *>(q),
                            static_cast<const bf16_t *>(k), img, static_cast<TOut *>(out), ta, plan.den_out, o0pre,
-                           call_chunks);
+                           call_chunks, plan.qk_div);
     }
     return hipGetLastError();
 }

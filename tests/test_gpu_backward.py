@@ -6,8 +6,8 @@ the head's whole gradient: single rows of dq or dk can be near zero).  Bars:
 TOL_GRAD_F32 for fp32 inputs (the passes run the fp32 prefill path; the
 gradients are sums of a few of its results, so a few times its 1e-5), and
 the bf16-input bar for bf16 inputs (the passes also round their values,
-g_i[c] q_i and [v_j, 1][c] k_j, to bf16, and run on the fp16-operand scan
-where it covers the head size and order).
+g_i[c] q_i and [v_j, 1][c] k_j: to binary16 on the fp16-operand scan, which
+takes every pass whose head size and order it covers, else to bf16).
 """
 import numpy as np
 import pytest
