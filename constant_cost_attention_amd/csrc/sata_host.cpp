@@ -176,6 +176,7 @@ sata_status take_state_error(sata_state *st) {
 std::atomic<int> g_debug_item_base{0};
 std::atomic<int> g_debug_spin_limit{sata::kScanSpinLimit};
 std::atomic<int> g_debug_positions{0};
+std::atomic<int> g_debug_refresh{0};
 
 }  // namespace
 
@@ -186,6 +187,7 @@ ScanDebug scan_debug() {
     d.item_base = g_debug_item_base.load(std::memory_order_relaxed);
     d.spin_limit = g_debug_spin_limit.load(std::memory_order_relaxed);
     d.positions = g_debug_positions.load(std::memory_order_relaxed);
+    d.refresh = g_debug_refresh.load(std::memory_order_relaxed);
     return d;
 }
 }
@@ -975,6 +977,14 @@ sata_status sata_debug_prefill_positions(int mt) {
     if (mt != 0 && mt != 1 && mt != 2 && mt != 3 && mt != 5)
         return fail(SATA_ERR_INVALID, "positions per update wavefront must be 0, 1, 2, 3 or 5 (got %d)", mt);
     g_debug_positions.store(mt, std::memory_order_relaxed);
+    return SATA_OK;
+}
+
+sata_status sata_debug_prefill_refresh(int chunks) {
+    g_last_error.clear();
+    if (chunks < 0 || chunks > 16)
+        return fail(SATA_ERR_INVALID, "chunks per state-copy refresh must be 0 (the rule) or 1 .. 16 (got %d)", chunks);
+    g_debug_refresh.store(chunks, std::memory_order_relaxed);
     return SATA_OK;
 }
 

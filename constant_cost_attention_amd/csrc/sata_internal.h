@@ -216,6 +216,7 @@ constexpr int kScanSpinLimit = 1 << 24;
 // and their successors' waits time out), and give up after spin_limit polls.
 struct ScanDebug {
     int positions = 0;   // forced positions per update wavefront of the fp16-operand scan (0: the rule)
+    int refresh = 0;     // forced chunks per state-copy refresh of the fp16-operand scan (0: the rule)
     int item_base = 0;
     int spin_limit = kScanSpinLimit;
 };

@@ -27,11 +27,16 @@
 //    q^ token-major, fp16) as one image that the scan copies into LDS.
 //  * Eight wavefronts, two per SIMD: four "update" wavefronts each keep MT
 //    positions of the slice's state in accumulators; four "readout"
-//    wavefronts each read 2C/32 token tiles... out against half of the slice's
-//    features from an fp16 copy of the state in LDS.  The readouts of the two
-//    halves are added in LDS (fp32) and stored as fp16 partials scaled by a
-//    power of two that follows the number of tokens seen (so they keep fp16's
-//    range), one per (chunk, slice); a reduce kernel adds the slices.
+//    wavefronts each read out a quarter of the chunk's tokens against every
+//    feature of the slice from an fp16 copy of the state in LDS, and store
+//    fp16 partials scaled by a power of two that follows the number of tokens
+//    seen (so they keep fp16's range), one per (chunk, slice); a reduce kernel
+//    adds the slices.
+//  * The copy is rewritten every R chunks only (R per head size): chunk c is
+//    read out against S^(g-1), g = c - c mod R, and the reduce kernel adds the
+//    keys of chunks g .. c as direct Taylor terms, exactly as it adds the
+//    intra-chunk term.  Both sums are the same quantity split at another
+//    token, so the result only differs in rounding.
 //
 //   [hotdry] blog.hotdry.top, "Symmetry-aware Taylor approximation attention:
 //            engineering a constant per-token cost" (2026-02-05).
@@ -259,6 +264,7 @@ struct S16Item {
     int64_t pstride;              // partial stride per chunk
     int64_t bh, ps0;
     int cbeg, cend;
+    int refresh;                  // chunks per refresh of the readout's state copy (cbeg is a multiple)
     uint32_t gstart, mixedm;
 };
 
@@ -283,6 +289,7 @@ __device__ __forceinline__ S16Item item_from_lds(const S16Item *s) {
     it.ps0 = rfl64(s->ps0);
     it.cbeg = __builtin_amdgcn_readfirstlane(s->cbeg);
     it.cend = __builtin_amdgcn_readfirstlane(s->cend);
+    it.refresh = __builtin_amdgcn_readfirstlane(s->refresh);
     it.gstart = (uint32_t)__builtin_amdgcn_readfirstlane((int)s->gstart);
     it.mixedm = (uint32_t)__builtin_amdgcn_readfirstlane((int)s->mixedm);
     return it;
@@ -407,6 +414,11 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
         for (int nt = 0; nt < NTF; ++nt) B[nt] = __builtin_bit_cast(f16x8, CP[(kk * NTF + nt) * 64 + lane]);
         B[NTF] = __builtin_bit_cast(f16x8, clast[kk * clast_step]);
     };
+    // first last index (4 x block) of each position of the slice, read once per item into scalar
+    // registers (an LDS read per K step would wait for the B prefetch in flight as well)
+    int xb[Cfg::NP];
+#pragma unroll
+    for (int p = 0; p < Cfg::NP; ++p) xb[p] = __builtin_amdgcn_readfirstlane(4 * qd16_b(W0[p * 16]));
     // A operand of K step kk for each token tile (LDS reads of the query image, and the prefix
     // factors regrouped where a position starts)
     auto formA = [&](int kk, f16x8 (&A)[TPW], auto first) {
@@ -415,7 +427,7 @@ __device__ __attribute__((noinline)) void scan16_readout(const S16Item *sit) {
             __asm__ volatile("" ::: "memory");
             regroup(p);
         }
-        const int xo = 4 * qd16_b(W0[p * 16]) + 2 * h;
+        const int xo = xb[p] + 2 * h;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const f16x2 x = *reinterpret_cast<const S16_LDS f16x2 *>(qrow[tt] + xo);
@@ -581,35 +593,58 @@ __device__ __attribute__((noinline)) void scan16_update(const S16Item *sit) {
     __syncthreads();   // Y: image of the first chunk and the first copy written
 
     const int vlast = li == 0 ? D : D + 1;    // the "+1" row for column D, zeros for the rest
-    for (int cc = it.cbeg; cc < it.cend; ++cc) {
-        // ---- phase A: S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1]
-#pragma unroll 1
-        for (int ks = 0; ks < UKS; ++ks) {
-            const int tb = 32 * ks + 8 * g;
-            f16x8 B[NT];
+    int until_refresh = it.refresh;           // chunks left before the copy is rewritten
+    // B operand of K step ks (32 tokens): the [V | 1] rows of the image
+    auto loadB = [&](int ks, f16x8 (&B)[NT]) {
+        const int tb = 32 * ks + 8 * g;
 #pragma unroll
-            for (int nt = 0; nt < NTF; ++nt) B[nt] = *reinterpret_cast<const S16_LDS f16x8 *>(Vt + (16 * nt + li) * KS + tb);
-            B[NTF] = *reinterpret_cast<const S16_LDS f16x8 *>(Vt + vlast * KS + tb);
-            f16x8 p2;
+        for (int nt = 0; nt < NTF; ++nt) B[nt] = *reinterpret_cast<const S16_LDS f16x8 *>(Vt + (16 * nt + li) * KS + tb);
+        B[NTF] = *reinterpret_cast<const S16_LDS f16x8 *>(Vt + vlast * KS + tb);
+    };
+    // one K step on operand B; the next step's B is read into Bn once this step's prefix reads
+    // are out (LDS reads complete in order, so the waits for this step's keys do not wait for it)
+    auto kstep = [&](int ks, const f16x8 (&B)[NT], f16x8 (&Bn)[NT]) {
+        const int tb = 32 * ks + 8 * g;
+        f16x8 p2;
 #pragma unroll
-            for (int j = 0; j < MT; ++j) {
-                if (j == 0 || ((newgrp >> j) & 1u)) {
-                    __asm__ volatile("" ::: "memory");
-                    const f16x8 a = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + qd_i1(wr[j]) * KS + tb);
-                    const f16x8 b = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + qd_i2(wr[j]) * KS + tb);
-                    p2 = a * b;
-                }
+        for (int j = 0; j < MT; ++j) {
+            if (j == 0 || ((newgrp >> j) & 1u)) {
+                __asm__ volatile("" ::: "memory");
+                const f16x8 a = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + qd_i1(wr[j]) * KS + tb);
+                const f16x8 b = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + qd_i2(wr[j]) * KS + tb);
+                p2 = a * b;
+            }
+            f16x8 k3[4];
 #pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    const f16x8 k3 = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + (4 * blk[j] + z) * KS + tb);
-                    const f16x8 A = p2 * k3;
+            for (int z = 0; z < 4; ++z) k3[z] = *reinterpret_cast<const S16_LDS f16x8 *>(Kt + (4 * blk[j] + z) * KS + tb);
+            if (j == MT - 1 && ks + 1 < UKS) loadB(ks + 1, Bn);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) S[j][z][nt] = mfma_f16(A, B[nt], S[j][z][nt]);
-                }
+            for (int z = 0; z < 4; ++z) {
+                const f16x8 A = p2 * k3[z];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) S[j][z][nt] = mfma_f16(A, B[nt], S[j][z][nt]);
             }
         }
+    };
+    static_assert(UKS % 2 == 0, "K steps pair up over the two B buffers");
+    for (int cc = it.cbeg; cc < it.cend; ++cc) {
+        // ---- phase A: S[slice, :] += phi(K_c)[:, slice]^T [V_c | 1], the K steps unrolled (their
+        // B buffers alternate; a rolled loop would carry them and copy the accumulators)
+        f16x8 Ba[NT], Bb[NT];
+        loadB(0, Ba);
+#pragma unroll
+        for (int ks = 0; ks < UKS; ks += 2) {
+            kstep(ks, Ba, Bb);
+            kstep(ks + 1, Bb, Ba);
+        }
         __syncthreads();   // X
-        write_copy();
+        // the copy the readout reads is S^(c-1) only after chunks whose index within the segment is a
+        // multiple of it.refresh; the readout of the chunks in between uses that older state, and the
+        // reduce kernel adds their keys since then as direct terms
+        if (--until_refresh == 0) {
+            until_refresh = it.refresh;
+            if (cc + 1 < it.cend) write_copy();
+        }
         __syncthreads();   // Y
     }
     // accumulators -> state slice (plain layout)
@@ -647,7 +682,7 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
                    const float4 *__restrict__ pcoef, const uint32_t *__restrict__ pflags,
                    float *__restrict__ state, int64_t m_pad, const unsigned char *__restrict__ img, int nchunk,
                    f16 *__restrict__ partial, const float *__restrict__ o0pre, int64_t call_chunks, int64_t chunk0,
-                   int nslices, int64_t nbh, int nsub, int sub_chunks, uint32_t *__restrict__ sync,
+                   int nslices, int64_t nbh, int nsub, int sub_chunks, int refresh, uint32_t *__restrict__ sync,
                    int item_base, int spin_limit, uint32_t *err) {
     using Cfg = S16Cfg<D, C, MT>;
     using I = typename Cfg::I;
@@ -693,6 +728,7 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
         const int slice = (int)(rem % nslices);
         it.cbeg = u * sub_chunks;
         it.cend = it.cbeg + sub_chunks < nchunk ? it.cbeg + sub_chunks : nchunk;
+        it.refresh = refresh;
         if (u > 0) {
             if (tid == 0) wait_predecessor(flags + rem, (uint32_t)u, spin_limit, err);
             __syncthreads();   // thread 0's acquire invalidated the caches every wave reads through
@@ -733,41 +769,44 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
     }
 }
 
-// Direct intra-chunk term for query tile qt (fp16 operands): Z (rows = queries
-// 4g + r, column li of each 16-column tile) receives sum_{key <= query}
-// w(q.k/sqrt d) [v, 1][key].  S^T = K Q^T is formed on bf16 MFMA from q and k as
-// given (exact products, fp32 sums); W = w(S^T) is packed to fp16 (w lies in
-// [1/3, e] for |x| <= 1) and multiplies [V | 1] from the chunk's image (fp16,
-// dimension-major) on fp16 MFMA.  The accumulator rows of S^T are the K slots
-// of the W [V | 1] product, so W never leaves the registers.
-template <int D, int NT, int KS>
+// Direct Taylor terms of query tile qt of the chunk starting at token tq0 (fp16 operands)
+// against the keys of one chunk starting at token tk0: Z (rows = queries 4g + r, column li of
+// each 16-column tile) receives sum_key w(q.k/sqrt d) [v, 1][key], over the keys up to the query
+// when the key chunk is the query's own (causal), over all C keys of an earlier chunk (full).
+// S^T = K Q^T is formed on bf16 MFMA from q and k as given (exact products, fp32 sums); W = w(S^T)
+// is packed to fp16 (w lies in [1/3, e] for |x| <= 1) and multiplies [V | 1] of the key chunk
+// (its image rows, fp16, dimension-major, in LDS) on fp16 MFMA.  The accumulator rows of S^T are
+// the K slots of the W [V | 1] product, so W never leaves the registers.
+template <int D, int NT, int KS, int C, bool full>
 __device__ __forceinline__ void intra_tile16(f32x4 (&Z)[NT], int qt, int g, int li, const bf16_t *qh, const bf16_t *kh,
-                                             int64_t t0, int nvalid, const f16 *Vt, const TaylorArgs &ta) {
+                                             int64_t tq0, int nvalid, int64_t tk0, const f16 *Vt,
+                                             const TaylorArgs &ta) {
     const int query = 16 * qt + li;
     constexpr int DS = D < 32 ? 1 : D / 32;
-    auto load8 = [&](const bf16_t *base, int tok, int d0) -> bf16x8 {
+    // rows at or past `lim` of the chunk read as zeros (a ragged last chunk)
+    auto load8 = [&](const bf16_t *base, int64_t t0, int tok, int lim, int d0) -> bf16x8 {
         uint4 u = {0u, 0u, 0u, 0u};
-        if (tok < nvalid && d0 < D) u = *reinterpret_cast<const uint4 *>(base + (t0 + tok) * D + d0);
+        if (tok < lim && d0 < D) u = *reinterpret_cast<const uint4 *>(base + (t0 + tok) * D + d0);
         return __builtin_bit_cast(bf16x8, u);
     };
     bf16x8 Bq[DS];
 #pragma unroll
-    for (int s = 0; s < DS; ++s) Bq[s] = load8(qh, query, 32 * s + 8 * g);
-    const int nks = qt / 2 + 1;
-    for (int ks = 0; ks < nks; ++ks) {
+    for (int s = 0; s < DS; ++s) Bq[s] = load8(qh, tq0, query, nvalid, 32 * s + 8 * g);
+    const int klim = full ? C : nvalid;           // an earlier chunk is whole
+    auto kstep = [&](int ks) {
         f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
         const int kA = 32 * ks + li, kB = kA + 16;
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-            sA = mfma_bf16(load8(kh, kA, 32 * s + 8 * g), Bq[s], sA);
-            sB = mfma_bf16(load8(kh, kB, 32 * s + 8 * g), Bq[s], sB);
+            sA = mfma_bf16(load8(kh, tk0, kA, klim, 32 * s + 8 * g), Bq[s], sA);
+            sB = mfma_bf16(load8(kh, tk0, kB, klim, 32 * s + 8 * g), Bq[s], sB);
         }
         f16 w8[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int keyA = 32 * ks + 4 * g + r, keyB = keyA + 16;
-            w8[r] = (f16)(keyA <= query ? taylor_w(sA[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.c4, ta.P) : 0.f);
-            w8[4 + r] = (f16)(keyB <= query ? taylor_w(sB[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.c4, ta.P) : 0.f);
+            w8[r] = (f16)(full || keyA <= query ? taylor_w(sA[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.c4, ta.P) : 0.f);
+            w8[4 + r] = (f16)(full || keyB <= query ? taylor_w(sB[r] * ta.scale, ta.c0, ta.c1, ta.c2, ta.c3, ta.c4, ta.P) : 0.f);
         }
         const f16x8 A = {w8[0], w8[1], w8[2], w8[3], w8[4], w8[5], w8[6], w8[7]};
 #pragma unroll
@@ -778,12 +817,20 @@ __device__ __forceinline__ void intra_tile16(f32x4 (&Z)[NT], int qt, int g, int 
             const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
             Z[nt] = mfma_f16(A, __builtin_bit_cast(f16x8, uint4{lo.x, lo.y, hi.x, hi.y}), Z[nt]);
         }
-    }
+    };
+    // (rolled loops: an unrolled whole key chunk holds all its key loads at once, and the registers
+    // that takes halve the kernel's occupancy)
+    const int nks = full ? C / 32 : qt / 2 + 1;
+#pragma unroll 1
+    for (int ks = 0; ks < nks; ++ks) kstep(ks);
 }
 
-// y = (direct intra-chunk term) + 2^e (sum over slices of the fp16 partials, fixed order)
-// + the chunk's order-0 prefix; o = y[:d_V] / y[d_V] (or y[:d_V] when ta.raw; y[d_V] also
-// goes to den_out when given).  Grid (chunks of the segment, B*H), 256 threads.
+// Chunk c of the segment was read out against S^(g-1), g = c - c % refresh (the scan rewrites the
+// readout's state copy every refresh chunks), so
+// y = (direct Taylor terms of the keys of chunks g .. c, causal in c) + 2^e (sum over slices of the
+// fp16 partials, fixed order) + the order-0 prefix before chunk g; o = y[:d_V] / y[d_V] (or
+// y[:d_V] when ta.raw; y[d_V] also goes to den_out when given).  Grid (chunks of the segment,
+// B*H), 256 threads.
 template <int D, int C, typename TOut>
 __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restrict__ partial, int nslices, int nchunk,
                                                             int64_t n, int64_t tok0, const bf16_t *__restrict__ q,
@@ -791,7 +838,7 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
                                                             const unsigned char *__restrict__ img, TOut *__restrict__ out,
                                                             TaylorArgs ta, float *__restrict__ den_out,
                                                             const float *__restrict__ o0pre, int64_t call_chunks,
-                                                            int qk_div) {
+                                                            int qk_div, int refresh) {
     using I = Img16<D, C>;
     constexpr int NC = D + 1, TT = C / 16, NT = (NC + 15) / 16;
     constexpr int NV8 = TT * NC * 2;                // 16-byte loads (8 halves) per partial
@@ -806,7 +853,9 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
     const int g = lane >> 4, li = lane & 15;
     const int64_t t0 = tok0 + (int64_t)cc * C;
     const int nvalid = n - t0 < C ? (int)(n - t0) : C;
+    const int gc = cc - cc % refresh;                                // first chunk of the direct window
     const float *pre = o0pre + (bh * call_chunks + t0 / C) * NC;   // this chunk's order-0 prefix
+    const float *pre_g = pre - (int64_t)(cc - gc) * NC;             // ... and the window's
     const float unscale = 1.0f / partial_scale(pre[D], C);
 
     const f16 *base = partial + (bh * nchunk + cc) * (int64_t)nslices * (TT * NC * 16);
@@ -852,30 +901,37 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
             d[1] = float4{acc[j][4] * unscale, acc[j][5] * unscale, acc[j][6] * unscale, acc[j][7] * unscale};
         }
     }
-    // [V | 1] of the chunk from its image
-    {
-        const uint4 *src = reinterpret_cast<const uint4 *>(img + (bh * nchunk + cc) * (int64_t)I::BYTES + I::V_OFF);
-        uint4 *dst = reinterpret_cast<uint4 *>(vt);
-        for (int i = tid; i < (D + 2) * I::KS / 8; i += 256) dst[i] = src[i];
-    }
-    __syncthreads();
+    // direct terms, one key chunk of the window at a time: its [V | 1] rows from its image, then
+    // every query tile against its keys (two tiles per wavefront, balanced over the causal triangle)
     static_assert(TT % 2 == 0 && TT / 2 <= 4, "query tiles pair up over the four wavefronts");
-    if (wave < TT / 2) {
-        const bf16_t *qh = q + (bh / qk_div) * n * D, *kh = k + (bh / qk_div) * n * D;
+    const bf16_t *qh = q + (bh / qk_div) * n * D, *kh = k + (bh / qk_div) * n * D;
+    for (int j = gc; j <= cc; ++j) {
+        if (j > gc) __syncthreads();   // the previous key chunk's rows are no longer read
+        {
+            const uint4 *src = reinterpret_cast<const uint4 *>(img + (bh * nchunk + j) * (int64_t)I::BYTES + I::V_OFF);
+            uint4 *dst = reinterpret_cast<uint4 *>(vt);
+            for (int i = tid; i < (D + 2) * I::KS / 8; i += 256) dst[i] = src[i];
+        }
+        __syncthreads();
+        if (wave < TT / 2) {
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int qq = pass == 0 ? wave : TT - 1 - wave;
-            f32x4 Z[NT];
+            for (int pass = 0; pass < 2; ++pass) {
+                const int qq = pass == 0 ? wave : TT - 1 - wave;
+                const int64_t tk0 = tok0 + (int64_t)j * C;
+                f32x4 Z[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            intra_tile16<D, NT, I::KS>(Z, qq, g, li, qh, kh, t0, nvalid, vt, ta);
+                for (int nt = 0; nt < NT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (j < cc) intra_tile16<D, NT, I::KS, C, true>(Z, qq, g, li, qh, kh, t0, nvalid, tk0, vt, ta);
+                else intra_tile16<D, NT, I::KS, C, false>(Z, qq, g, li, qh, kh, t0, nvalid, tk0, vt, ta);
+                // (each wavefront adds to its own query tiles' rows only)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int c = 16 * nt + li;
-                if (c < NC) {
-                    float4 *pp = reinterpret_cast<float4 *>(ys + (qq * NC + c) * 16 + 4 * g);
-                    const float4 o = *pp;
-                    *pp = float4{o.x + Z[nt][0], o.y + Z[nt][1], o.z + Z[nt][2], o.w + Z[nt][3]};
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int c = 16 * nt + li;
+                    if (c < NC) {
+                        float4 *pp = reinterpret_cast<float4 *>(ys + (qq * NC + c) * 16 + 4 * g);
+                        const float4 o = *pp;
+                        *pp = float4{o.x + Z[nt][0], o.y + Z[nt][1], o.z + Z[nt][2], o.w + Z[nt][3]};
+                    }
                 }
             }
         }
@@ -885,8 +941,8 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
         const int t = i / D, c = i - t * D;
         if (t < nvalid) {
             const int tt = t >> 4, t16 = t & 15;
-            const float y = ys[(tt * NC + c) * 16 + t16] + pre[c];
-            const float den = ys[(tt * NC + D) * 16 + t16] + pre[D];
+            const float y = ys[(tt * NC + c) * 16 + t16] + pre_g[c];
+            const float den = ys[(tt * NC + D) * 16 + t16] + pre_g[D];
             out[(bh * n + t0 + t) * D + c] = from_f32<TOut>(ta.raw ? y : y / den);
             if (den_out && c == 0) den_out[bh * n + t0 + t] = den;
         }
@@ -907,6 +963,17 @@ int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus) {
     if (forced == 1 || forced == big) return forced;
     const int64_t slices = (np16 + 4 * big - 1) / (4 * big);
     return bh * slices >= cus ? big : 1;
+}
+
+// Chunks per rewrite of the readout's state copy: the chunks in between are read out against the
+// older copy, and the reduce kernel takes their keys as direct terms instead.
+int scan16_refresh(int dk, int chunk) {
+    const int forced = scan_debug().refresh;   // a measurement's choice
+    if (forced > 0) return forced;
+    // measured whole-call optimum per head size (the scan gains less than the reduce kernel's
+    // wider direct window costs beyond it; at d_K = 16 the reduce kernel dominates from 2 on)
+    (void)chunk;
+    return dk == 16 ? 1 : dk == 64 ? 4 : 8;
 }
 
 int64_t scan16_image_bytes(int dk, int chunk) {
@@ -951,9 +1018,11 @@ static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const 
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan, Cfg::THREADS, Cfg::LDS)) != hipSuccess) return e;
     const int64_t resident = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     const int64_t items0 = bh * plan.slices;
-    // sub-segments of at least 16 chunks until there are about a dozen items per resident workgroup
+    const int refresh = scan16_refresh(D, C);
+    // sub-segments of at least 16 chunks until there are about a dozen items per resident workgroup;
+    // each a whole number of copy refresh intervals
     int nsub = items0 <= cus ? 1 : (int)std::min<int64_t>((12 * resident + items0 - 1) / items0, std::max(1, nseg / 16));
-    const int sub_chunks = (nseg + nsub - 1) / nsub;
+    const int sub_chunks = ((nseg + nsub - 1) / nsub + refresh - 1) / refresh * refresh;
     nsub = (nseg + sub_chunks - 1) / sub_chunks;
     const int64_t grid = std::min<int64_t>(items0 * nsub, resident);
     if ((e = launch_zero(reinterpret_cast<float *>(sync), plan.sync_words, stream)) != hipSuccess) return e;
@@ -963,7 +1032,8 @@ static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const 
         hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(Cfg::THREADS), Cfg::LDS, stream, idx->d_p16_w0,
                            idx->d_p16_cidx, reinterpret_cast<const float4 *>(idx->d_p16_coef), idx->d_p16_flags,
                            static_cast<float *>(st->d_state), idx->m_pad, img, nseg, partial, o0pre, call_chunks, chunk0,
-                           plan.slices, bh, nsub, sub_chunks, sync, dbg.item_base, dbg.spin_limit, st->d_err);
+                           plan.slices, bh, nsub, sub_chunks, refresh, sync, dbg.item_base, dbg.spin_limit,
+                           st->d_err);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
@@ -971,7 +1041,7 @@ static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const 
         hipLaunchKernelGGL((scan16_reduce_kernel<D, C, TOut>), dim3((unsigned)nseg, (unsigned)bh), dim3(256), 0, stream,
                            partial, plan.slices, nseg, n, tok0, static_cast<const bf16_t *>(q),
                            static_cast<const bf16_t *>(k), img, static_cast<TOut *>(out), ta, plan.den_out, o0pre,
-                           call_chunks, plan.qk_div);
+                           call_chunks, plan.qk_div, refresh);
     }
     return hipGetLastError();
 }

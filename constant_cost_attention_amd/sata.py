@@ -32,7 +32,8 @@ _EXPORTS = (
     "sata_describe_quads16",
     "sata_status_string", "sata_last_error",
     "sata_profile_enable", "sata_profile_query", "sata_profile_kernel_name",
-    "sata_describe_prefill_plan", "sata_debug_scan_faults", "sata_debug_prefill_positions", "sata_measure_mfma_loop",
+    "sata_describe_prefill_plan", "sata_debug_scan_faults", "sata_debug_prefill_positions", "sata_debug_prefill_refresh",
+    "sata_measure_mfma_loop",
 )
 
 _lib = None
@@ -79,6 +80,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_state_check.argtypes = [vp, vp]
     lib.sata_debug_scan_faults.argtypes = [cint, cint]
     lib.sata_debug_prefill_positions.argtypes = [cint]
+    lib.sata_debug_prefill_refresh.argtypes = [cint]
     lib.sata_describe_prefill_plan.argtypes = [cint, cint, i64, i64, cint, cint, i64, ctypes.POINTER(i64),
                                                ctypes.POINTER(i64)]
     lib.sata_describe_prefill_plan.restype = i64
@@ -112,7 +114,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sata_profile_kernel_name.restype = ctypes.c_char_p
     for name in ("sata_profile_enable", "sata_profile_query", "sata_build_index", "sata_index_info", "sata_state_alloc", "sata_state_alloc_dtype",
                  "sata_state_convert", "sata_state_set_decode_window", "sata_state_flush", "sata_state_check",
-                 "sata_debug_scan_faults", "sata_debug_prefill_positions", "sata_state_reset",
+                 "sata_debug_scan_faults", "sata_debug_prefill_positions", "sata_debug_prefill_refresh",
+                 "sata_state_reset",
                  "sata_state_data", "sata_prefill", "sata_prefill_noalloc", "sata_prefill_backward", "sata_decode_step",
                  "sata_expand_features"):
         getattr(lib, name).restype = cint
@@ -266,6 +269,11 @@ def sata_debug_scan_faults(item_base: int = 0, spin_limit: int = 0):
 def sata_debug_prefill_positions(mt: int = 0):
     """Force the fp16-operand scan's positions per update wavefront (measurement only; 0 = the rule)."""
     _check(load().sata_debug_prefill_positions(int(mt)), "sata_debug_prefill_positions")
+
+
+def sata_debug_prefill_refresh(chunks: int = 0):
+    """Force the fp16-operand scan's chunks per state-copy refresh (measurement only; 0 = the rule)."""
+    _check(load().sata_debug_prefill_refresh(int(chunks)), "sata_debug_prefill_refresh")
 
 
 def sata_describe_prefill_plan(d_k: int, P: int, batch_heads: int, n: int, chunk: int = 0, in_dt: int = SATA_BF16,

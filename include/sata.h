@@ -384,6 +384,16 @@ sata_status sata_debug_scan_faults(int item_base, int spin_limit);
  * sata_prefill's argument.  Not for production use. */
 sata_status sata_debug_prefill_positions(int mt);
 
+/* Copy refresh interval for measurement (process-wide, affects every later
+ * call until reset with 0): the fp16-operand prefill scan rewrites the fp16
+ * copy of the state that its readout reads every `chunks` chunks instead of
+ * at the library's rule.  Chunks in between are read out against the last
+ * copy, and the keys since that copy enter as direct Taylor terms (the
+ * weights of the intra-chunk term), so the result is the same up to
+ * rounding.  chunks must be 0 (the rule) or 1 .. 16, else SATA_ERR_INVALID.
+ * Not for production use. */
+sata_status sata_debug_prefill_refresh(int chunks);
+
 /* Kernel timing instrumentation.  While enabled, every launch of the
  * library's kernels is bracketed by a HIP event pair recorded on the stream
  * the kernel is launched on.  sata_profile_enable(1) clears earlier records;

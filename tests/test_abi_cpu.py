@@ -318,3 +318,21 @@ def test_forced_positions_change_the_plan():
         sata.sata_debug_prefill_positions(0)
     assert one in (2 * rule - 1, 2 * rule) and five == rule
     assert sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16)["slices"] == rule
+
+
+def test_forced_refresh_interval_checks():
+    """sata_debug_prefill_refresh takes 0 (the rule) or 1 .. 16 chunks and refuses
+    anything else with SATA_ERR_INVALID; it does not change the plan's slices or
+    workspace (the interval only moves terms between the scan and the reduce)."""
+    from constant_cost_attention_amd import sata
+    rule = sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16)
+    try:
+        for ok in (1, 3, 16):
+            sata.sata_debug_prefill_refresh(ok)
+            assert sata.sata_describe_prefill_plan(64, 4, 8, 65536, 128, sata.SATA_BF16) == rule
+        for bad in (-1, 17, 1000):
+            with pytest.raises(sata.SataError) as e:
+                sata.sata_debug_prefill_refresh(bad)
+            assert e.value.status == sata.SATA_ERR_INVALID
+    finally:
+        sata.sata_debug_prefill_refresh(0)

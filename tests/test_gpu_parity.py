@@ -161,6 +161,37 @@ def test_fp16_scan_both_slice_widths(sata, oracle, d, heads, slices):
     assert err <= TOL_BF16
 
 
+@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("refresh", [1, 2, 3, 5])
+def test_copy_refresh_intervals_every_row(sata, oracle, d, refresh):
+    """The fp16-operand scan rewrites the readout's state copy every `refresh`
+    chunks and the reduce kernel adds the keys since the last copy as direct
+    terms: every row of a two-call prefill (the second continuing the first's
+    state, so the order-0 prefix and the state both carry over) on a ragged
+    length matches the oracle at each forced interval, including intervals
+    that do not divide the chunk count."""
+    P, chunk, heads = 4, 128, 3
+    n1, n2 = 300, 6 * chunk + 45
+    n = n1 + n2
+    x = si.draw_qkv((1, heads), n, d, d, 8080 + d + refresh, "bf16")
+    ref = oracle.taylor_attention(x.q, x.k, x.v, P)
+    idx = sata.Index(d, d, P)
+    st = sata.State(idx, 1, heads)
+    q, k, v = dev_all(x)
+    say("prefill bf16 d=%d refresh %d: %d + %d tokens" % (d, refresh, n1, n2))
+    try:
+        sata.sata_debug_prefill_refresh(refresh)
+        part = lambda a, lo, hi: a[:, :, lo:hi].contiguous()
+        o1 = prefill(idx, st, part(q, 0, n1), part(k, 0, n1), part(v, 0, n1), chunk=chunk)
+        o2 = prefill(idx, st, part(q, n1, n), part(k, n1, n), part(v, n1, n), chunk=chunk)
+    finally:
+        sata.sata_debug_prefill_refresh(0)
+    o = torch.cat([o1, o2], dim=2).cpu().numpy()
+    err = rel_err(o, ref)
+    say("  err %.3e" % err)
+    assert err <= TOL_BF16
+
+
 def test_short_sequences_and_empty(sata, oracle):
     d, P = 16, 4
     idx = sata.Index(d, d, P)
