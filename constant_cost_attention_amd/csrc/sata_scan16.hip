@@ -1019,9 +1019,11 @@ static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const 
     const int64_t resident = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     const int64_t items0 = bh * plan.slices;
     const int refresh = scan16_refresh(D, C);
-    // sub-segments of at least 16 chunks until there are about a dozen items per resident workgroup;
-    // each a whole number of copy refresh intervals
-    int nsub = items0 <= cus ? 1 : (int)std::min<int64_t>((12 * resident + items0 - 1) / items0, std::max(1, nseg / 16));
+    // sub-segments of at least 64 chunks until there are about a dozen items per resident workgroup;
+    // each a whole number of copy refresh intervals.  (Measured: each item loads and stores its
+    // state slice and waits for its predecessor; 4 sub-segments per slice beat 8 at d_K = 32 by 6%
+    // and more than 4 lose at d_K = 64.)
+    int nsub = items0 <= cus ? 1 : (int)std::min<int64_t>((12 * resident + items0 - 1) / items0, std::max(1, nseg / 64));
     const int sub_chunks = ((nseg + nsub - 1) / nsub + refresh - 1) / refresh * refresh;
     nsub = (nseg + sub_chunks - 1) / sub_chunks;
     const int64_t grid = std::min<int64_t>(items0 * nsub, resident);

@@ -22,10 +22,11 @@ def sata():
 
 
 # Shapes with more work items than compute units, so each slice's chunks run as sub-segments
-# (2 at d = 16 fp32, 4 at d = 32 bf16) whose items wait for their predecessors.
-@pytest.mark.parametrize("d,dtype,chunk,nh", [(16, "f32", 128, 320), (32, "bf16", 64, 64)])
-def test_timed_out_wait_is_reported(sata, oracle, d, dtype, chunk, nh):
-    P, n = 4, 4096
+# (2 at d = 16 fp32 over 32 chunks; 4 at d = 32 bf16 over 256 chunks, the fp16-operand scan
+# taking sub-segments of at least 64 chunks) whose items wait for their predecessors.
+@pytest.mark.parametrize("d,dtype,chunk,nh,n", [(16, "f32", 128, 320, 4096), (32, "bf16", 64, 64, 16384)])
+def test_timed_out_wait_is_reported(sata, oracle, d, dtype, chunk, nh, n):
+    P = 4
     x = si.draw_qkv((1, nh), n, d, d, 5150 + d, dtype)
     idx = sata.Index(d, d, P)
     st = sata.State(idx, 1, nh)
@@ -53,7 +54,7 @@ def test_timed_out_wait_is_reported(sata, oracle, d, dtype, chunk, nh):
     o = prefill(idx, st, q, k, v, chunk=chunk)
     sata.sata_state_check(st)
     heads = [0, 1, 2, nh - 1]
-    rows = np.array([0, 1, 127, 2048, n - 1])
+    rows = np.array([0, 1, 127, 2048, n // 2 + 5, n - 1])
     sub = lambda a: np.ascontiguousarray(a[:, heads])
     ref = oracle.taylor_attention(sub(x.q), sub(x.k), sub(x.v), P, rows=rows)
     err = rel_err(o.float().cpu().numpy()[:, heads][:, :, rows], ref)
