@@ -967,13 +967,15 @@ int scan16_choose_mt(int dk, int64_t np16, int64_t bh, int cus) {
 
 // Chunks per rewrite of the readout's state copy: the chunks in between are read out against the
 // older copy, and the reduce kernel takes their keys as direct terms instead.
-int scan16_refresh(int dk, int chunk) {
+int scan16_refresh(int dk, int slices) {
     const int forced = scan_debug().refresh;   // a measurement's choice
     if (forced > 0) return forced;
-    // measured whole-call optimum per head size (the scan gains less than the reduce kernel's
-    // wider direct window costs beyond it; at d_K = 16 the reduce kernel dominates from 2 on)
-    (void)chunk;
-    return dk == 16 ? 1 : dk == 64 ? 4 : 8;
+    // The scan saves a copy phase per slice and chunk, the reduce kernel pays the wider direct
+    // window once per head and chunk: with few slices per head (d_K = 16 prefills, the backward's
+    // (P - 1)-order passes) the window costs more than it saves.  Otherwise the measured
+    // whole-call optimum per head size.
+    if (slices < 8) return 1;
+    return dk == 64 ? 4 : 8;
 }
 
 int64_t scan16_image_bytes(int dk, int chunk) {
@@ -1018,7 +1020,7 @@ static hipError_t run_scan16(const sata_index *idx, const sata_state *st, const 
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan, Cfg::THREADS, Cfg::LDS)) != hipSuccess) return e;
     const int64_t resident = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     const int64_t items0 = bh * plan.slices;
-    const int refresh = scan16_refresh(D, C);
+    const int refresh = scan16_refresh(D, plan.slices);
     // sub-segments of at least 64 chunks until there are about a dozen items per resident workgroup;
     // each a whole number of copy refresh intervals.  (Measured: each item loads and stores its
     // state slice and waits for its predecessor; 4 sub-segments per slice beat 8 at d_K = 32 by 6%
