@@ -216,7 +216,9 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
  * within a chunk the Taylor weights are formed directly, across chunks the
  * orders' states are scanned and read out [hotdry, "Engineering realisation
  * of the constant compute cost"]; results do not depend on the chunk length
- * beyond rounding.  For bf16 inputs with d_K = d_V in {16, 32, 64, 128} and
+ * beyond rounding.  (The fp16-operand scan below reads a chunk out against
+ * the state of up to 7 chunks earlier and forms the weights of the keys in
+ * between directly as well: the same terms, split at another token.)  For bf16 inputs with d_K = d_V in {16, 32, 64, 128} and
  * P <= 4 the scan's matrix operands are fp16: k / 4, 4 q / sqrt(d_K) and v
  * convert to fp16 exactly when their magnitudes lie in fp16's normal range
  * (6.1e-5 to 65504, or zero); smaller ones keep less precision and larger
