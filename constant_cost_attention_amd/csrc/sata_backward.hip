@@ -195,22 +195,55 @@ __global__ __launch_bounds__(kBwThreads) void bw_cast(const float *__restrict__ 
         out[i] = from_f32<TOut>(a[i]);
 }
 
-// Device buffers of one backward call, freed (after the stream drains) when
-// the call returns.
+// Device buffers of one backward call, taken in order from the index's pool: the calls on an
+// index request the same sequence of sizes for the same shapes, so after the first call nothing is
+// allocated.  (Allocating and freeing the tens of GB of a call each time slowed later calls down
+// to several times the first, and the device's free memory fell, once other indexes had come and
+// gone in the process.)  A request larger than its pool entry replaces the entry; when an
+// allocation fails, the entries this call has not reached yet are released and it is tried once
+// more.  The buffers stay in the pool when the call returns (its stream drained).
 struct Arena {
-    std::vector<void *> ptrs;
+    std::vector<std::pair<void *, size_t>> &pool;
+    size_t next = 0;
     hipError_t err = hipSuccess;
+    explicit Arena(std::vector<std::pair<void *, size_t>> &p) : pool(p) {}
     template <typename T> T *get(int64_t count) {
-        void *p = nullptr;
-        if (err == hipSuccess) err = hipMalloc(&p, (size_t)std::max<int64_t>(count, 1) * sizeof(T));
         if (err != hipSuccess) return nullptr;
-        ptrs.push_back(p);
+        const size_t bytes = (size_t)std::max<int64_t>(count, 1) * sizeof(T);
+        if (next < pool.size() && pool[next].first && pool[next].second >= bytes)
+            return static_cast<T *>(pool[next++].first);
+        if (next < pool.size() && pool[next].first) {
+            (void)hipFree(pool[next].first);
+            pool[next] = {nullptr, 0};
+        }
+        void *p = nullptr;
+        err = hipMalloc(&p, bytes);
+        if (err != hipSuccess) {
+            (void)hipGetLastError();
+            for (size_t i = next; i < pool.size(); ++i)
+                if (pool[i].first) {
+                    (void)hipFree(pool[i].first);
+                    pool[i] = {nullptr, 0};
+                }
+            err = hipMalloc(&p, bytes);
+            if (err != hipSuccess) return nullptr;
+        }
+        if (next < pool.size()) pool[next] = {p, bytes};
+        else pool.push_back({p, bytes});
+        ++next;
         return static_cast<T *>(p);
     }
-    ~Arena() {
-        for (void *p : ptrs) (void)hipFree(p);
-    }
 };
+
+}  // namespace
+
+void free_backward_pool(const sata_index *idx) {
+    for (auto &b : idx->bw_pool)
+        if (b.first) (void)hipFree(b.first);
+    idx->bw_pool.clear();
+}
+
+namespace {
 
 // A temporary state (and workspace) for up to `heads` heads of idx, reused by
 // every pass of one backward call and cleared before each.
@@ -270,10 +303,14 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
                       sata_dtype in_dt, int64_t mem_budget, hipStream_t s) {
     const int D = idx->dk;
     const int lgD = __builtin_ctz((unsigned)D);   // head sizes are powers of two
+    // The prefill's default chunk for fp32 inputs at d_K = 16 is 128 tokens (measured on the
+    // forward); the backward's passes, with d_V + 1 times the heads, measured faster at 64
+    // (1 x 8 x 4096: 3.8 ms per call against 4.8).
+    if (chunk == 0 && in_dt == SATA_F32 && D == 16) chunk = 64;
     const TIn *q = static_cast<const TIn *>(qv), *k = static_cast<const TIn *>(kv), *v = static_cast<const TIn *>(vv);
     const int64_t elems = bh * n * D;
     t_bw_step = "temporaries";
-    Arena ar;
+    Arena ar(idx->bw_pool);
     float *o = ar.get<float>(elems), *z = ar.get<float>(bh * n), *g = ar.get<float>(bh * n * (D + 1));
     float *r = ar.get<float>(elems);
     TIn *rq = ar.get<TIn>(elems), *rk = ar.get<TIn>(elems), *rg = ar.get<TIn>(elems);
@@ -363,7 +400,8 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
     hipLaunchKernelGGL(bw_cast<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, acc_k, static_cast<TOut *>(dkv), elems);
     hipLaunchKernelGGL(bw_cast<TOut>, dim3(bw_grid(elems)), dim3(kBwThreads), 0, s, acc_q, static_cast<TOut *>(dqv), elems);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // the temporaries are freed on return: let the stream drain first
+    // the temporaries go back to the pool on return, for a later call on any stream: let this
+    // stream drain first
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
     uint32_t bits = 0;
     if ((e = hipMemcpy(&bits, err, sizeof(bits), hipMemcpyDeviceToHost)) != hipSuccess) return e;

@@ -626,6 +626,7 @@ void sata_index_free(sata_index *idx) {
     for (void *p : {(void *)idx->d_p16_w0, (void *)idx->d_p16_cidx, (void *)idx->d_p16_coef, (void *)idx->d_p16_flags})
         if (p) (void)hipFree(p);
     if (idx->lower) sata_index_free(idx->lower);
+    sata::free_backward_pool(idx);
     delete idx;
 }
 
@@ -880,6 +881,7 @@ sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, c
         lower = idx->lower;
     }
     const int64_t kBudget = (int64_t)8 << 30;   // bytes of per-column temporaries per pass
+    std::lock_guard<std::mutex> pool_lock(idx->bw_mu);   // the index's pool of temporaries
     hipError_t e = sata::launch_backward(idx, lower, bh, q, k, v, dout, dq, dk, dv, n, chunk, in_dt, grad_dt, kBudget,
                                          (hipStream_t)stream);
     if (e == hipErrorMemoryAllocation || e == hipErrorOutOfMemory) {

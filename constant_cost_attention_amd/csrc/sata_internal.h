@@ -19,6 +19,8 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "../../include/sata.h"
 
@@ -56,6 +58,11 @@ struct sata_index {
     // built by the first backward call that needs it and freed with this index.
     mutable sata_index *lower = nullptr;
     mutable std::mutex lower_mu;
+    // Device temporaries of the backward calls on this index (pointer, bytes), kept between calls
+    // and freed with the index: request i of a call reuses buffer i when it is large enough, and a
+    // larger request replaces it.  bw_mu serialises the backward calls on the index.
+    mutable std::vector<std::pair<void *, size_t>> bw_pool;
+    mutable std::mutex bw_mu;
 };
 
 struct sata_state {
@@ -204,6 +211,8 @@ struct ProfScope {
 };
 
 hipError_t launch_zero(float *p, int64_t count, hipStream_t stream);
+// Frees the backward calls' temporaries kept with an index (sata_backward.hip).
+void free_backward_pool(const sata_index *idx);
 // Dense TFLOP/s of a plain 16x16x32 MFMA loop on the current device (sata_measure.hip).
 hipError_t measure_mfma_loop(bool bf16, double *tflops);
 

@@ -211,8 +211,8 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
  * dtype of q, k, v; out_dt that of out.  Token i attends to every earlier
  * token and to itself.  The sequence is processed in chunks of `chunk` tokens
  * (0 = default: 128 for bf16 inputs with P <= 4 and d_K = d_V in {16, 32,
- * 64}, and for d_K = 64; 64 otherwise; supported: 64, 128; at d_K = 128 the
- * chunk is always 64 tokens):
+ * 64}, for d_K = 64, and for fp32 inputs at d_K = 16; 64 otherwise;
+ * supported: 64, 128; at d_K = 128 the chunk is always 64 tokens):
  * within a chunk the Taylor weights are formed directly, across chunks the
  * orders' states are scanned and read out [hotdry, "Engineering realisation
  * of the constant compute cost"]; results do not depend on the chunk length
@@ -280,8 +280,11 @@ sata_status sata_prefill_noalloc(const sata_index *idx, sata_state *st, const vo
  * two that brings the largest |g| into [2^8, 2^9), and the results are scaled
  * back.  d_K = 128 needs bf16 inputs and 3 <= P <= 4 (SATA_ERR_UNSUPPORTED
  * otherwise).  The (P - 1)-order index is built on the first call and kept
- * with idx (freed by sata_index_free).  Allocates its temporaries (hipMalloc,
- * up to a few GB) and synchronises `stream` before returning.  Gradients must
+ * with idx (freed by sata_index_free).  Its device temporaries (tens of GB
+ * at d_K = 64, n = 65536) are allocated by the first call and kept with idx
+ * for later calls, grown when a call needs more, and freed by
+ * sata_index_free; backward calls on one index are serialised.  Synchronises
+ * `stream` before returning.  Gradients must
  * not overlap the inputs or each other; n = 0 is a no-op. */
 sata_status sata_prefill_backward(const sata_index *idx, int batch, int heads, const void *q, const void *k,
                                   const void *v, const void *dout, void *dq, void *dk, void *dv, int64_t n,

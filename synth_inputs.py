@@ -113,7 +113,7 @@ class Workload:
 # figures and the stated targets use them (d_K = d_V in every case).
 WORKLOADS = {
     "tiny_d8_p3": Workload("tiny_d8_p3", 1, 1, 256, 8, 8, 3, "f32", 64, SEED_BASE + 0),
-    "prefill_d16_p4_f32": Workload("prefill_d16_p4_f32", 1, 8, 4096, 16, 16, 4, "f32", 64, SEED_BASE + 1),
+    "prefill_d16_p4_f32": Workload("prefill_d16_p4_f32", 1, 8, 4096, 16, 16, 4, "f32", 128, SEED_BASE + 1),
     "prefill_d32_p4_bf16": Workload("prefill_d32_p4_bf16", 2, 16, 16384, 32, 32, 4, "bf16", 64, SEED_BASE + 2),
     "decode_d64_p4_f32": Workload("decode_d64_p4_f32", 32, 8, 8192, 64, 64, 4, "f32", 128, SEED_BASE + 3,
                                   decode_steps=1024),

@@ -160,3 +160,43 @@ def test_backward_error_paths(sata):
     with pytest.raises(sata.SataError) as e:
         sata.sata_prefill_backward(idx, q, q, q, q, g[0], g[0], g[2])  # dq aliases dk
     assert e.value.status == sata.SATA_ERR_INVALID
+
+
+def test_backward_temporaries_kept_with_the_index(sata):
+    """Backward calls on one index take their temporaries from a pool kept with
+    the index: after the first call the device's free memory stays put over
+    further calls, with another index created, used for a backward and freed
+    between them; the gradients repeat bit for bit; freeing the index returns
+    the pool's memory."""
+    d, P, n, heads = 64, 4, 1024, 2
+    x = si.draw_qkv((1, heads), n, d, d, 4321, "bf16")
+    q, k, v = dev(x, "q"), dev(x, "k"), dev(x, "v")
+    do = torch.from_numpy(np.random.default_rng(5).standard_normal((1, heads, n, d)).astype(np.float32)).cuda()
+    do = do.to(q.dtype)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+    xo = si.draw_qkv((1, 1), 200, 32, 32, 4322, "bf16")
+    qo, ko, vo = dev(xo, "q"), dev(xo, "k"), dev(xo, "v")
+    doo = torch.ones(qo.shape, dtype=qo.dtype, device="cuda")
+    go = [torch.empty(qo.shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+    idx = sata.Index(d, d, P)
+    say("backward pool: %d heads x %d tokens, d=%d" % (heads, n, d))
+    sata.sata_prefill_backward(idx, q, k, v, do, *grads)
+    torch.cuda.synchronize()
+    first = [g.cpu().numpy() for g in grads]
+    free_after_first = torch.cuda.mem_get_info()[0]
+    for _ in range(3):
+        other = sata.Index(32, 32, 4)
+        sata.sata_prefill_backward(other, qo, ko, vo, doo, *go)
+        other.free()
+        sata.sata_prefill_backward(idx, q, k, v, do, *grads)
+        torch.cuda.synchronize()
+        for a, b in zip(first, grads):
+            assert np.array_equal(a, b.cpu().numpy())
+        drop = free_after_first - torch.cuda.mem_get_info()[0]
+        say("  free memory below the first call's: %.1f MB" % (drop / 2**20))
+        assert drop < 64 << 20
+    idx.free()
+    torch.cuda.synchronize()
+    back = torch.cuda.mem_get_info()[0] - free_after_first
+    say("  freed with the index: %.1f MB" % (back / 2**20))
+    assert back > 0
