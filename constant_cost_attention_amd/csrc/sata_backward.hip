@@ -303,10 +303,6 @@ hipError_t backward_t(const sata_index *idx, const sata_index *lower, int64_t bh
                       sata_dtype in_dt, int64_t mem_budget, hipStream_t s) {
     const int D = idx->dk;
     const int lgD = __builtin_ctz((unsigned)D);   // head sizes are powers of two
-    // The prefill's default chunk for fp32 inputs at d_K = 16 is 128 tokens (measured on the
-    // forward); the backward's passes, with d_V + 1 times the heads, measured faster at 64
-    // (1 x 8 x 4096: 3.8 ms per call against 4.8).
-    if (chunk == 0 && in_dt == SATA_F32 && D == 16) chunk = 64;
     const TIn *q = static_cast<const TIn *>(qv), *k = static_cast<const TIn *>(kv), *v = static_cast<const TIn *>(vv);
     const int64_t elems = bh * n * D;
     t_bw_step = "temporaries";
