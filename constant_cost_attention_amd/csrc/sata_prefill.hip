@@ -1743,7 +1743,11 @@ PrefillPlan plan_prefill(const sata_index *idx, int64_t bh, int64_t n, int chunk
     // head size it takes up to 64, by 18-26%), for d_K = 64, and for fp32 inputs at d_K = 16
     // (1 x 8 x 4096: 0.437 ms per call against 0.482); 64 for the other scans
     p.chunk = chunk ? chunk : (s16 || idx->dk == 64 || (idx->dk == 16 && in_dt == SATA_F32) ? 128 : 64);
-    if (p.chunk != 64 && p.chunk != 128) return p;
+    // the fp16-operand scan at d_K = 16 by default takes 256-token chunks: its chunk steps are
+    // short, so twice the work per step amortises the per-step staging and barriers (1 x 64 x
+    // 131072: 3.35 ms per call against 3.52-3.64 at 128; scan 1.97 ms against 2.45-2.56)
+    if (!chunk && s16 && idx->dk == 16) p.chunk = 256;
+    if (p.chunk != 64 && p.chunk != 128 && !(p.chunk == 256 && s16 && idx->dk == 16)) return p;
     if (idx->dk == 128) {
         if (!s16) return p;   // no chunked plan: the block prefill covers it
         p.chunk = 64;         // the operand image of a 128-token chunk does not fit beside the state copy

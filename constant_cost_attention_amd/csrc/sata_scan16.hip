@@ -202,7 +202,7 @@ struct S16Cfg {
     static constexpr int UNITS = I::BYTES / 16;
     static constexpr int UPT = (UNITS + 64 * NR - 1) / (64 * NR);       // image units per readout thread
     static_assert(NC == 16 * NTF + 1, "the last column tile holds the normaliser alone");
-    static_assert(C % 64 == 0 && TT % NR == 0 && NKS % 2 == 0 && NKS >= 4, "64 or 128 tokens per chunk");
+    static_assert(C % 64 == 0 && TT % NR == 0 && NKS % 2 == 0 && NKS >= 4, "64, 128 or 256 tokens per chunk");
     static_assert(NP <= 32, "position flags fit a 32-bit mask");
     static_assert(LDS + 128 <= 160 * 1024, "LDS budget (the kernel adds its item record, 112 bytes)");
 };
@@ -776,11 +776,12 @@ void scan16_kernel(const uint32_t *__restrict__ pw0, const int32_t *__restrict__
 // S^T = K Q^T is formed on bf16 MFMA from q and k as given (exact products, fp32 sums); W = w(S^T)
 // is packed to fp16 (w lies in [1/3, e] for |x| <= 1) and multiplies [V | 1] of the key chunk
 // (its image rows, fp16, dimension-major, in LDS) on fp16 MFMA.  The accumulator rows of S^T are
-// the K slots of the W [V | 1] product, so W never leaves the registers.
-template <int D, int NT, int KS, int C, bool full>
+// the K slots of the W [V | 1] product, so W never leaves the registers.  With KL the key chunk's
+// rows come from LDS (kl: [C][D], zero past the valid keys) instead of global memory.
+template <int D, int NT, int KS, int C, bool full, bool KL>
 __device__ __forceinline__ void intra_tile16(f32x4 (&Z)[NT], int qt, int g, int li, const bf16_t *qh, const bf16_t *kh,
                                              int64_t tq0, int nvalid, int64_t tk0, const f16 *Vt,
-                                             const TaylorArgs &ta) {
+                                             const bf16_t *kl, const TaylorArgs &ta) {
     const int query = 16 * qt + li;
     constexpr int DS = D < 32 ? 1 : D / 32;
     // rows at or past `lim` of the chunk read as zeros (a ragged last chunk)
@@ -798,8 +799,17 @@ __device__ __forceinline__ void intra_tile16(f32x4 (&Z)[NT], int qt, int g, int 
         const int kA = 32 * ks + li, kB = kA + 16;
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-            sA = mfma_bf16(load8(kh, tk0, kA, klim, 32 * s + 8 * g), Bq[s], sA);
-            sB = mfma_bf16(load8(kh, tk0, kB, klim, 32 * s + 8 * g), Bq[s], sB);
+            if constexpr (KL) {
+                const int d0 = 32 * s + 8 * g;
+                const uint4 z = {0u, 0u, 0u, 0u};
+                const uint4 ua = d0 < D ? *reinterpret_cast<const uint4 *>(kl + kA * D + d0) : z;
+                const uint4 ub = d0 < D ? *reinterpret_cast<const uint4 *>(kl + kB * D + d0) : z;
+                sA = mfma_bf16(__builtin_bit_cast(bf16x8, ua), Bq[s], sA);
+                sB = mfma_bf16(__builtin_bit_cast(bf16x8, ub), Bq[s], sB);
+            } else {
+                sA = mfma_bf16(load8(kh, tk0, kA, klim, 32 * s + 8 * g), Bq[s], sA);
+                sB = mfma_bf16(load8(kh, tk0, kB, klim, 32 * s + 8 * g), Bq[s], sB);
+            }
         }
         f16 w8[8];
 #pragma unroll
@@ -846,6 +856,11 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
     constexpr int SU = 4;                           // slices per round
     __shared__ __align__(16) f16 vt[(D + 2) * I::KS];
     __shared__ __align__(16) float ys[TT * NC * 16];
+    // at d_K <= 32 each key chunk of the window is staged in LDS beside its [V | 1] rows (the causal
+    // term's key steps then wait on LDS rather than on global loads); at d_K = 64 and 128 the extra
+    // LDS would cost the occupancy that the partial sums need
+    constexpr bool KL = D <= 32;
+    __shared__ __align__(16) bf16_t kls[KL ? C * D : 8];
     const int cc = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -902,8 +917,9 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
         }
     }
     // direct terms, one key chunk of the window at a time: its [V | 1] rows from its image, then
-    // every query tile against its keys (two tiles per wavefront, balanced over the causal triangle)
-    static_assert(TT % 2 == 0 && TT / 2 <= 4, "query tiles pair up over the four wavefronts");
+    // every query tile against its keys (tiles t and TT - 1 - t together, balanced over the causal
+    // triangle; pairs dealt to the four wavefronts in turn)
+    static_assert(TT % 2 == 0 && (TT / 2 <= 4 || TT % 8 == 0), "query tile pairs deal evenly to the wavefronts");
     const bf16_t *qh = q + (bh / qk_div) * n * D, *kh = k + (bh / qk_div) * n * D;
     for (int j = gc; j <= cc; ++j) {
         if (j > gc) __syncthreads();   // the previous key chunk's rows are no longer read
@@ -912,17 +928,27 @@ __global__ __launch_bounds__(256) void scan16_reduce_kernel(const f16 *__restric
             uint4 *dst = reinterpret_cast<uint4 *>(vt);
             for (int i = tid; i < (D + 2) * I::KS / 8; i += 256) dst[i] = src[i];
         }
+        if constexpr (KL) {
+            const int klim = j < cc ? C : nvalid;   // keys past the last valid token read as zeros
+            const uint4 *src = reinterpret_cast<const uint4 *>(kh + (tok0 + (int64_t)j * C) * D);
+            uint4 *dst = reinterpret_cast<uint4 *>(kls);
+            for (int i = tid; i < C * D / 8; i += 256)
+                dst[i] = i / (D / 8) < klim ? src[i] : uint4{0u, 0u, 0u, 0u};
+        }
         __syncthreads();
-        if (wave < TT / 2) {
+#pragma unroll
+        for (int pr = 0; pr < (TT / 2 + 3) / 4; ++pr) {
+            const int pair = 4 * pr + wave;   // tiles pair and TT - 1 - pair
+            if (pair >= TT / 2) continue;
 #pragma unroll
             for (int pass = 0; pass < 2; ++pass) {
-                const int qq = pass == 0 ? wave : TT - 1 - wave;
+                const int qq = pass == 0 ? pair : TT - 1 - pair;
                 const int64_t tk0 = tok0 + (int64_t)j * C;
                 f32x4 Z[NT];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (j < cc) intra_tile16<D, NT, I::KS, C, true>(Z, qq, g, li, qh, kh, t0, nvalid, tk0, vt, ta);
-                else intra_tile16<D, NT, I::KS, C, false>(Z, qq, g, li, qh, kh, t0, nvalid, tk0, vt, ta);
+                if (j < cc) intra_tile16<D, NT, I::KS, C, true, KL>(Z, qq, g, li, qh, kh, t0, nvalid, tk0, vt, kls, ta);
+                else intra_tile16<D, NT, I::KS, C, false, KL>(Z, qq, g, li, qh, kh, t0, nvalid, tk0, vt, kls, ta);
                 // (each wavefront adds to its own query tiles' rows only)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
@@ -985,7 +1011,8 @@ int64_t scan16_image_bytes(int dk, int chunk) {
     using I64 = std::integral_constant<int, 64>;
     using C64 = std::integral_constant<int, 64>;
     using C128 = std::integral_constant<int, 128>;
-    if (dk == 16) return chunk == 64 ? b(I16{}, C64{}) : b(I16{}, C128{});
+    if (dk == 16) return chunk == 64 ? b(I16{}, C64{}) : chunk == 256 ? b(I16{}, std::integral_constant<int, 256>{})
+                                                                      : b(I16{}, C128{});
     if (dk == 32) return chunk == 64 ? b(I32{}, C64{}) : b(I32{}, C128{});
     if (dk == 128) return b(std::integral_constant<int, 128>{}, C64{});   // 64-token chunks only
     return chunk == 64 ? b(I64{}, C64{}) : b(I64{}, C128{});
@@ -1068,7 +1095,9 @@ hipError_t launch_scan16_segment(const sata_index *idx, const sata_state *st, co
     using C64 = std::integral_constant<int, 64>;
     using C128 = std::integral_constant<int, 128>;
     switch (idx->dk) {
-        case 16: return plan.chunk == 64 ? go(std::integral_constant<int, 16>{}, C64{}) : go(std::integral_constant<int, 16>{}, C128{});
+        case 16:
+            if (plan.chunk == 256) return go(std::integral_constant<int, 16>{}, std::integral_constant<int, 256>{});
+            return plan.chunk == 64 ? go(std::integral_constant<int, 16>{}, C64{}) : go(std::integral_constant<int, 16>{}, C128{});
         case 32: return plan.chunk == 64 ? go(std::integral_constant<int, 32>{}, C64{}) : go(std::integral_constant<int, 32>{}, C128{});
         case 64: return plan.chunk == 64 ? go(std::integral_constant<int, 64>{}, C64{}) : go(std::integral_constant<int, 64>{}, C128{});
         case 128: return plan.chunk == 64 ? go(std::integral_constant<int, 128>{}, C64{}) : hipErrorInvalidValue;

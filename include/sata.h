@@ -210,9 +210,10 @@ sata_status sata_state_data(const sata_state *st, void **dev_ptr, int64_t *bytes
  * q, k: [batch][heads][n][d_K]; v, out: [batch][heads][n][d_V]; in_dt is the
  * dtype of q, k, v; out_dt that of out.  Token i attends to every earlier
  * token and to itself.  The sequence is processed in chunks of `chunk` tokens
- * (0 = default: 128 for bf16 inputs with P <= 4 and d_K = d_V in {16, 32,
- * 64}, for d_K = 64, and for fp32 inputs at d_K = 16; 64 otherwise;
- * supported: 64, 128; at d_K = 128 the chunk is always 64 tokens):
+ * (0 = default: 256 for bf16 inputs with P <= 4 and d_K = d_V = 16; 128
+ * for bf16 inputs with P <= 4 and d_K = d_V in {32, 64}, for d_K = 64, and
+ * for fp32 inputs at d_K = 16; 64 otherwise; supported arguments: 0, 64,
+ * 128; at d_K = 128 the chunk is always 64 tokens):
  * within a chunk the Taylor weights are formed directly, across chunks the
  * orders' states are scanned and read out [hotdry, "Engineering realisation
  * of the constant compute cost"]; results do not depend on the chunk length
