@@ -161,24 +161,25 @@ def test_fp16_scan_both_slice_widths(sata, oracle, d, heads, slices):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("d,chunk", [(16, 128), (32, 128), (64, 128), (16, 0)])
 @pytest.mark.parametrize("refresh", [1, 2, 3, 5])
-def test_copy_refresh_intervals_every_row(sata, oracle, d, refresh):
+def test_copy_refresh_intervals_every_row(sata, oracle, d, chunk, refresh):
     """The fp16-operand scan rewrites the readout's state copy every `refresh`
     chunks and the reduce kernel adds the keys since the last copy as direct
     terms: every row of a two-call prefill (the second continuing the first's
     state, so the order-0 prefix and the state both carry over) on a ragged
     length matches the oracle at each forced interval, including intervals
-    that do not divide the chunk count."""
-    P, chunk, heads = 4, 128, 3
-    n1, n2 = 300, 6 * chunk + 45
+    that do not divide the chunk count; chunk 0 at d = 16 is the default
+    256-token chunk."""
+    P, heads = 4, 3
+    n1, n2 = 300, 6 * 128 + 45
     n = n1 + n2
     x = si.draw_qkv((1, heads), n, d, d, 8080 + d + refresh, "bf16")
     ref = oracle.taylor_attention(x.q, x.k, x.v, P)
     idx = sata.Index(d, d, P)
     st = sata.State(idx, 1, heads)
     q, k, v = dev_all(x)
-    say("prefill bf16 d=%d refresh %d: %d + %d tokens" % (d, refresh, n1, n2))
+    say("prefill bf16 d=%d chunk %d refresh %d: %d + %d tokens" % (d, chunk, refresh, n1, n2))
     try:
         sata.sata_debug_prefill_refresh(refresh)
         part = lambda a, lo, hi: a[:, :, lo:hi].contiguous()
@@ -369,7 +370,8 @@ def _prefill_workload(sata, oracle, wl, extra_rows):
     q, k, v = dev_all(x)
     o = prefill(idx, st, q, k, v, chunk=wl.chunk)
     torch.cuda.synchronize()
-    rows = None if extra_rows is None else sample_rows(wl.n, wl.chunk, extra_rows, wl.seed)
+    # (chunk 0, the default, is 256 tokens where it is used here: the d = 16 fp16-operand scan)
+    rows = None if extra_rows is None else sample_rows(wl.n, wl.chunk or 256, extra_rows, wl.seed)
     o = o.cpu().numpy()
     ref = oracle.taylor_attention(x.q, x.k, x.v, wl.P, rows=rows)
     got = o if rows is None else o[:, :, rows]
@@ -392,6 +394,17 @@ def test_workload_prefill_d64_bf16_sampled(sata, oracle):
 
 def test_workload_prefill_d16x64h_bf16_sampled(sata, oracle):
     assert _prefill_workload(sata, oracle, WL["prefill_d16x64h_p4_bf16"], 32) <= TOL_BF16
+
+
+def test_workload_prefill_d16x64h_default_chunk_sampled(sata, oracle):
+    """The same workload at the library's default chunk for this head size (256 tokens): 512
+    chunks per head in sub-segments, sampled rows of every head against the oracle."""
+    import dataclasses
+    wl = dataclasses.replace(WL["prefill_d16x64h_p4_bf16"], chunk=0)
+    plan = sata.sata_describe_prefill_plan(wl.d_k, wl.P, wl.batch * wl.heads, wl.n, 0, sata.SATA_BF16)
+    say("default chunk plan: %s" % plan)
+    assert plan["seg_chunks"] * 256 >= wl.n            # one segment of 256-token chunks
+    assert _prefill_workload(sata, oracle, wl, 32) <= TOL_BF16
 
 
 def test_workload_decode_d64_after_8192(sata, oracle):
